@@ -1,0 +1,160 @@
+"""Seeded synthetic workloads for the KV4 decode step.
+
+This module only draws inputs: query, key and value tensors and context
+lengths with the shapes of the KV4-RL workloads (Qwen3-4B/8B attention
+geometry: 32 query heads, 8 kv heads, head dim 128; 16-token pages).  It holds
+none of the method's arithmetic, so the fp64 oracle and the HIP path can both
+be fed from it.
+
+Recipe (the same for every config):
+  * values are drawn with numpy ``default_rng`` from a seed sequence
+    ``[config seed, layer, sequence or step, stream tag]`` as float32 N(0, 1),
+    then rounded to bfloat16 (round to nearest even) with torch on the CPU;
+  * "outlier" key channels are picked once per config, one per distinct
+    32-channel group, and their key values are multiplied (in float32, before
+    the bf16 rounding) by the config's factor, in every kv head;
+  * a sequence's sources cover positions [0, context + steps): the history
+    plus the token(s) appended by the decode step(s); "context" is the length
+    before the step's append, so a decode step attends over context + 1
+    positions;
+  * ragged lengths: lognormal with the stated median and sigma 0.8, rounded
+    and clipped; uniform lengths are integers drawn uniformly.
+Every sequence's sources depend only on (seed, layer, sequence), so any subset
+can be regenerated without drawing the rest.
+"""
+from __future__ import annotations
+
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+TAG_K, TAG_V, TAG_Q, TAG_CTX, TAG_OUTLIER = 1, 2, 3, 4, 5
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    layers: int
+    batch: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    page: int
+    group: int
+    sink: int
+    recent: int
+    seed: int
+    outliers: int
+    outlier_scale: float
+    ctx_kind: str                     # "fixed", "lognormal", "uniform"
+    ctx_fixed: Tuple[int, ...] = ()
+    ctx_median: float = 0.0
+    ctx_sigma: float = 0.8
+    ctx_lo: int = 0
+    ctx_hi: int = 0
+    steps: int = 1
+
+    @property
+    def gqa(self) -> int:
+        return self.q_heads // self.kv_heads
+
+
+CONFIGS = {
+    # 1 layer, batch 2, 8 q / 2 kv heads, contexts 300 and 512, S=4, R=64,
+    # 2 outlier K channels x8, seed 0.
+    "tiny": Config("tiny", 1, 2, 8, 2, 128, 16, 32, 4, 64, 0, 2, 8.0, "fixed", (300, 512)),
+    # Qwen3-4B-shaped layer, batch 64, lognormal median 2k clipped 256..8k, R=128,
+    # 4 outlier K channels x10, seed 1.
+    "q4b": Config("q4b", 1, 64, 32, 8, 128, 16, 32, 4, 128, 1, 4, 10.0, "lognormal",
+                  ctx_median=2048, ctx_lo=256, ctx_hi=8192),
+    # Qwen3-8B-shaped layer, batch 256, long-tail lognormal median 4k, max 16k,
+    # R=128, seed 2 (the benchmarked workload).
+    "q8b256": Config("q8b256", 1, 256, 32, 8, 128, 16, 32, 4, 128, 2, 4, 10.0, "lognormal",
+                     ctx_median=4096, ctx_lo=256, ctx_hi=16384),
+    # Long context: batch 16, every context 32768, R=256, seed 3.
+    "long": Config("long", 1, 16, 32, 8, 128, 16, 32, 4, 256, 3, 4, 10.0, "fixed",
+                   tuple([32768] * 16)),
+    # 36 layers, batch 128, contexts uniform 1k..12k, R=128, seed 4, 64 steps.
+    "full36": Config("full36", 36, 128, 32, 8, 128, 16, 32, 4, 128, 4, 4, 10.0, "uniform",
+                     ctx_lo=1024, ctx_hi=12288, steps=64),
+}
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in key]))
+
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest even) and return them as float32."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def contexts(cfg: Config) -> np.ndarray:
+    """Context lengths before the step's append, one per sequence."""
+    if cfg.ctx_kind == "fixed":
+        c = np.array(cfg.ctx_fixed, dtype=np.int64)
+        assert c.size == cfg.batch
+        return c
+    r = _rng(cfg.seed, TAG_CTX)
+    if cfg.ctx_kind == "lognormal":
+        v = r.lognormal(mean=np.log(cfg.ctx_median), sigma=cfg.ctx_sigma, size=cfg.batch)
+        return np.clip(np.round(v), cfg.ctx_lo, cfg.ctx_hi).astype(np.int64)
+    if cfg.ctx_kind == "uniform":
+        return r.integers(cfg.ctx_lo, cfg.ctx_hi + 1, size=cfg.batch).astype(np.int64)
+    raise ValueError(cfg.ctx_kind)
+
+
+def outlier_channels(cfg: Config, groups_of: int = 32) -> np.ndarray:
+    """Key channels scaled as outliers: one channel in each of ``outliers``
+    distinct ``groups_of``-channel groups."""
+    if cfg.outliers == 0:
+        return np.zeros(0, dtype=np.int64)
+    r = _rng(cfg.seed, TAG_OUTLIER)
+    ngroups = cfg.head_dim // groups_of
+    assert cfg.outliers <= ngroups
+    groups = r.choice(ngroups, size=cfg.outliers, replace=False)
+    return np.sort(groups * groups_of + r.integers(0, groups_of, size=cfg.outliers))
+
+
+def kv_sources(cfg: Config, layer: int, seq: int, n: int,
+               outliers: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Keys and values of positions [0, n) of one sequence: float32 arrays
+    [n, kv_heads, head_dim] holding bf16 values.
+
+    The draw for position p does not depend on n (rows are drawn in order), so a
+    shorter n gives a prefix of a longer one."""
+    if outliers is None:
+        outliers = outlier_channels(cfg)
+    shape = (n, cfg.kv_heads, cfg.head_dim)
+    k = _rng(cfg.seed, layer, seq, TAG_K).standard_normal(shape, dtype=np.float32)
+    v = _rng(cfg.seed, layer, seq, TAG_V).standard_normal(shape, dtype=np.float32)
+    if outliers.size:
+        k[:, :, outliers] *= np.float32(cfg.outlier_scale)
+    return to_bf16_values(k), to_bf16_values(v)
+
+
+def queries(cfg: Config, layer: int, step: int = 0) -> np.ndarray:
+    """Decode-step queries [batch, q_heads, head_dim] (bf16 values in float32)."""
+    q = _rng(cfg.seed, layer, step, TAG_Q).standard_normal(
+        (cfg.batch, cfg.q_heads, cfg.head_dim), dtype=np.float32)
+    return to_bf16_values(q)
+
+
+def all_kv_sources(cfg: Config, layer: int, lengths: Sequence[int],
+                   seqs: Optional[Sequence[int]] = None,
+                   threads: int = 8) -> Tuple[List[np.ndarray], List[np.ndarray]]:
+    """Sources of many sequences, drawn on a thread pool."""
+    seqs = list(range(len(lengths))) if seqs is None else list(seqs)
+    out = outlier_channels(cfg)
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        res = list(ex.map(lambda s: kv_sources(cfg, layer, s, int(lengths[s]), out), seqs))
+    return [r[0] for r in res], [r[1] for r in res]
+
+
+def scaled(cfg: Config, **changes) -> Config:
+    """A copy of a config with some fields replaced (for reduced test sizes)."""
+    return dataclasses.replace(cfg, **changes)

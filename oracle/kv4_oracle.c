@@ -1,0 +1,324 @@
+/*
+ * kv4_oracle.c -- plain, slow, fp64 CPU oracle for the KV4 decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header or table with the HIP
+ * kernels.
+ *
+ * What it computes, and where the method is stated (KV4-RL: "Unlocking Faster
+ * Asynchronous Rollouts for RLVR with INT4 KV Cache Quantization",
+ * arXiv 2610.14448):
+ *   - the b-bit affine quantizer x^ = Delta*c + m with c in {0..2^b-1}, Delta > 0
+ *     (Section 3, eq. 3.3), used with b = 4 and FP16 Delta and m per group of
+ *     channels of one token-head vector (Section 5.1; Appendix A.3, "Encoding
+ *     and allocation"; Appendix D.4, Fig. A4b for groups finer than a head);
+ *   - symmetric per-(token, head) INT8 side copies computed from the source
+ *     vector, not from its INT4 rounding (Appendix A.3);
+ *   - the protected set: the first s positions and the w most recent positions
+ *     (Section 5.2, "Bounded selective protection"), read from the INT8 copy,
+ *     all other positions read from INT4, disjointly (Section 5.3);
+ *   - exact softmax attention over the dequantized cache.  The paper's
+ *     regional merge (eq. A1) and context splits reach this same result; the
+ *     oracle therefore does not implement them.
+ *
+ * Readings of steps the pages leave open (the pages fix only "affine INT4 with
+ * FP16 scale and offset" and "symmetric INT8"):
+ *   Q-1  m = fp16_rne(min x); r = fp32(max x - m); Delta = fp16_rne(fp32(r/15));
+ *        Delta = 0 when r <= 0 or when it rounds to zero; stored zeros are +0.
+ *   Q-2  c = integer in [0,15] nearest to the exact real (x - m)/Delta, ties to
+ *        even; c = 0 when Delta = 0.
+ *   Q-4  s = fp16_rne(fp32(amax/127)); c = integer nearest to the exact x/s,
+ *        ties to even, clamped to [-127,127]; c = 0 when s = 0.
+ *   Q-5  protected = [0, min(S,n)) U [max(S, n-R), n); INT4 = the rest.
+ *   Q-6  q head j reads kv head j / (Hq/Hkv); the new token attends to itself.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * fp32 steps are ordinary C float arithmetic (SSE, FLT_EVAL_METHOD == 0),
+ * each correctly rounded to nearest-even.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs float expressions evaluated in float (FLT_EVAL_METHOD 0)"
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 conversion, written from the format's definition.           */
+/* ------------------------------------------------------------------------ */
+
+/* Round a binary32 value to the nearest binary16 value, ties to even.
+ * Values whose magnitude rounds to 65520 or more become infinity; NaN stays
+ * a quiet NaN.  Returns the binary16 bit pattern (sign kept, -0 stays -0). */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    uint16_t sign = (uint16_t)((bits >> 16) & 0x8000u);
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs((double)f);               /* exact */
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);                            /* a = mant * 2^e2, mant in [0.5,1) */
+    int E = e2 - 1;                           /* floor(log2 a) */
+    if (E < -14) E = -14;                     /* subnormal range shares one quantum */
+    double quantum = ldexp(1.0, E - 10);      /* spacing of binary16 values near a */
+    double N = nearbyint(a / quantum);        /* exact scaling, then round half even */
+    uint32_t Ni = (uint32_t)N;                /* 0 .. 2048 */
+    if (E == -14 && Ni < 1024u) return (uint16_t)(sign | Ni);   /* subnormal or zero */
+    if (Ni == 2048u) { Ni = 1024u; E += 1; }  /* mantissa carry into the exponent */
+    if (E > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)(((uint32_t)(E + 15) << 10) | (Ni - 1024u)));
+}
+
+/* Exact value of a binary16 bit pattern. */
+double orc_f16_to_f64(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int E = (h >> 10) & 31;
+    int M = h & 1023;
+    double v;
+    if (E == 0) v = ldexp((double)M, -24);
+    else if (E == 31) v = M ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + M), E - 25);
+    return s ? -v : v;
+}
+
+/* Convert many values at once (used by the conversion pin tests). */
+void orc_f32_to_f16_array(const float* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
+}
+
+void orc_f16_to_f64_array(const uint16_t* h, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f64(h[i]);
+}
+
+static uint16_t plus_zero(uint16_t h) { return h == 0x8000u ? (uint16_t)0 : h; }
+
+/* ------------------------------------------------------------------------ */
+/* Q-1 / Q-2: asymmetric INT4 with FP16 scale and offset per group.          */
+/* ------------------------------------------------------------------------ */
+
+/* One token-head vector x[d] (bf16 values carried exactly in float).
+ * codes[d] get values 0..15; delta[d/G], offs[d/G] get binary16 patterns. */
+void orc_quant_int4_vec(const float* x, int d, int G, uint8_t* codes,
+                        uint16_t* delta, uint16_t* offs)
+{
+    for (int g = 0; g < d / G; ++g) {
+        const float* xg = x + (size_t)g * G;
+        float lo = xg[0], hi = xg[0];
+        for (int i = 1; i < G; ++i) {
+            if (xg[i] < lo) lo = xg[i];
+            if (xg[i] > hi) hi = xg[i];
+        }
+        uint16_t mb = plus_zero(orc_f32_to_f16(lo));
+        float mf = (float)orc_f16_to_f64(mb);     /* exact: binary16 fits binary32 */
+        float r = hi - mf;                        /* one binary32 rounding */
+        uint16_t db = 0;
+        if (r > 0.0f) {
+            float qq = r / 15.0f;                 /* correctly rounded binary32 division */
+            db = plus_zero(orc_f32_to_f16(qq));
+        }
+        delta[g] = db;
+        offs[g] = mb;
+        double D = orc_f16_to_f64(db), M = orc_f16_to_f64(mb);
+        for (int i = 0; i < G; ++i) {
+            int c = 0;
+            if (db != 0) {
+                /* nearest grid point M + c*D; the midpoint between codes k and
+                 * k+1 is M + (k+1/2)*D, exact in binary64 because M and D are
+                 * binary16 values. At a midpoint, the even code wins. */
+                double xv = (double)xg[i];
+                for (int k = 0; k < 15; ++k) {
+                    double mid = M + ((double)k + 0.5) * D;
+                    if (xv > mid || (xv == mid && ((k + 1) % 2) == 0)) ++c;
+                }
+            }
+            codes[(size_t)g * G + i] = (uint8_t)c;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q-4: symmetric INT8 with an FP16 scale per token-head vector.             */
+/* ------------------------------------------------------------------------ */
+
+void orc_quant_int8_vec(const float* x, int d, int8_t* codes, uint16_t* scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < d; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    float qq = amax / 127.0f;                     /* correctly rounded binary32 division */
+    uint16_t sb = plus_zero(orc_f32_to_f16(qq));
+    *scale = sb;
+    double S = orc_f16_to_f64(sb);
+    for (int i = 0; i < d; ++i) {
+        int c = 0;
+        if (sb != 0) {
+            double a = fabs((double)x[i]);
+            /* nearest multiple c*S of the magnitude, c <= 127; midpoints
+             * (k+1/2)*S are exact in binary64; ties go to the even c. */
+            for (int k = 0; k < 127; ++k) {
+                double mid = ((double)k + 0.5) * S;
+                if (a > mid || (a == mid && ((k + 1) % 2) == 0)) ++c;
+            }
+            if (x[i] < 0.0f) c = -c;
+        }
+        codes[i] = (int8_t)c;
+    }
+}
+
+/* Batched forms over nvec consecutive vectors of d channels. */
+void orc_quant_int4(const float* x, int64_t nvec, int d, int G, uint8_t* codes,
+                    uint16_t* delta, uint16_t* offs)
+{
+    int ng = d / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < nvec; ++v)
+        orc_quant_int4_vec(x + v * d, d, G, codes + v * d, delta + v * ng, offs + v * ng);
+}
+
+void orc_quant_int8(const float* x, int64_t nvec, int d, int8_t* codes, uint16_t* scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < nvec; ++v)
+        orc_quant_int8_vec(x + v * d, d, codes + v * d, scale + v);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q-5: which copy a position is read from.                                  */
+/* ------------------------------------------------------------------------ */
+
+/* 1 if position p of an n-token context reads the INT8 side copy. */
+int orc_is_protected(int64_t p, int64_t n, int S, int R)
+{
+    int64_t sink_end = n < S ? n : S;
+    int64_t rec_start = n - R > S ? n - R : S;
+    return p < sink_end || (p >= rec_start && p < n);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q-6: softmax attention over the dequantized cache, in binary64.           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Mixed cache.  Positions of all B sequences are stored back to back; sequence
+ * b owns rows [pos_off[b], pos_off[b] + seq_lens[b]).  Per row r and kv head h:
+ *   k4[(r*Hkv+h)*d + c]      INT4 code of channel c (0..15)
+ *   k4d/k4m[(r*Hkv+h)*ng+g]  binary16 Delta / m of group g (ng = d/G)
+ *   k8[(r*Hkv+h)*d + c]      INT8 code, k8s[r*Hkv+h] binary16 scale
+ * and the same for V.  q is [B][Hq][d] (bf16 values in float); out [B][Hq][d].
+ */
+void orc_attend_mixed(int B, const int32_t* seq_lens, const int64_t* pos_off,
+                      int Hq, int Hkv, int d, int G, int S, int R, double sm_scale,
+                      const float* q,
+                      const uint8_t* k4, const uint16_t* k4d, const uint16_t* k4m,
+                      const uint8_t* v4, const uint16_t* v4d, const uint16_t* v4m,
+                      const int8_t* k8, const uint16_t* k8s,
+                      const int8_t* v8, const uint16_t* v8s,
+                      double* out)
+{
+    int ng = d / G;
+    int gqa = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bj = 0; bj < (int64_t)B * Hq; ++bj) {
+        int b = (int)(bj / Hq), j = (int)(bj % Hq);
+        int h = j / gqa;
+        int64_t n = seq_lens[b];
+        const float* qj = q + ((int64_t)b * Hq + j) * d;
+        double* o = out + ((int64_t)b * Hq + j) * d;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* vh = (double*)malloc(sizeof(double) * (size_t)d);
+        double smax = -INFINITY;
+        for (int64_t p = 0; p < n; ++p) {
+            int64_t row = (pos_off[b] + p) * Hkv + h;
+            int prot = orc_is_protected(p, n, S, R);
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double kh;
+                if (prot) kh = orc_f16_to_f64(k8s[row]) * (double)k8[row * d + c];
+                else kh = orc_f16_to_f64(k4d[row * ng + c / G]) * (double)k4[row * d + c]
+                          + orc_f16_to_f64(k4m[row * ng + c / G]);
+                dot += (double)qj[c] * kh;
+            }
+            s[p] = sm_scale * dot;
+            if (s[p] > smax) smax = s[p];
+        }
+        double den = 0.0;
+        for (int64_t p = 0; p < n; ++p) { s[p] = exp(s[p] - smax); den += s[p]; }
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t p = 0; p < n; ++p) {
+            int64_t row = (pos_off[b] + p) * Hkv + h;
+            int prot = orc_is_protected(p, n, S, R);
+            for (int c = 0; c < d; ++c) {
+                if (prot) vh[c] = orc_f16_to_f64(v8s[row]) * (double)v8[row * d + c];
+                else vh[c] = orc_f16_to_f64(v4d[row * ng + c / G]) * (double)v4[row * d + c]
+                             + orc_f16_to_f64(v4m[row * ng + c / G]);
+            }
+            double w = s[p] / den;
+            for (int c = 0; c < d; ++c) o[c] += w * vh[c];
+        }
+        free(vh);
+        free(s);
+    }
+}
+
+/* BF16 cache (the comparator): keys and values are the source values. */
+void orc_attend_dense(int B, const int32_t* seq_lens, const int64_t* pos_off,
+                      int Hq, int Hkv, int d, double sm_scale,
+                      const float* q, const float* k, const float* v, double* out)
+{
+    int gqa = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bj = 0; bj < (int64_t)B * Hq; ++bj) {
+        int b = (int)(bj / Hq), j = (int)(bj % Hq);
+        int h = j / gqa;
+        int64_t n = seq_lens[b];
+        const float* qj = q + ((int64_t)b * Hq + j) * d;
+        double* o = out + ((int64_t)b * Hq + j) * d;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double smax = -INFINITY;
+        for (int64_t p = 0; p < n; ++p) {
+            const float* kp = k + ((pos_off[b] + p) * Hkv + h) * d;
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) dot += (double)qj[c] * (double)kp[c];
+            s[p] = sm_scale * dot;
+            if (s[p] > smax) smax = s[p];
+        }
+        double den = 0.0;
+        for (int64_t p = 0; p < n; ++p) { s[p] = exp(s[p] - smax); den += s[p]; }
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t p = 0; p < n; ++p) {
+            const float* vp = v + ((pos_off[b] + p) * Hkv + h) * d;
+            double w = s[p] / den;
+            for (int c = 0; c < d; ++c) o[c] += w * (double)vp[c];
+        }
+        free(s);
+    }
+}
+
+/* Number of OpenMP threads a parallel region will use (for reporting). */
+int orc_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp master
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}
