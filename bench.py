@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV4 decode step on one MI355X.
+
+A step is one pass of the hot path over one batch: kv4_append of the batch's
+new token (INT4 pages + INT8 ring) followed by kv4_decode_attn (split-KV GQA
+attention over the ragged paged contexts + the log-sum-exp merge).  The
+workload is the Qwen3-8B-shaped layer (32 q / 8 kv heads, d = 128) at batch
+256 with long-tail lognormal contexts (median 4k, max 16k), 16-token pages,
+INT4 group 32, S = 4, R = 128.  Inputs are seeded synthetic data, resident in
+HBM before the timed region.  Every step re-appends the same token at the same
+position (idempotent) and decodes over the same contexts, so each timed step
+does the full work on identical state.
+
+Output: one JSON line (see the design doc for every field's definition).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="q8b256")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def region_counts(n, S, R):
+    sink_end = np.minimum(S, n)
+    rec_start = np.maximum(S, n - R)
+    n4 = np.maximum(rec_start - S, 0)
+    n8 = sink_end + np.maximum(n - rec_start, 0)
+    return n4, n8
+
+
+def decode_bytes_kv4(n, cfg):
+    """Algorithmic bytes of one kv4_decode_attn call: payload + metadata of both
+    regions, q, fp32 output, block-table entries of the INT4 pages."""
+    n4, n8 = region_counts(n, cfg.sink, cfg.recent)
+    ng = cfg.head_dim // cfg.group
+    per4 = cfg.head_dim + 2 * 2 * 2 * ng            # K+V codes (d/2 each) + K,V (Delta, m) fp16
+    per8 = 2 * cfg.head_dim + 2 * 2                 # K+V int8 + two fp16 scales
+    kv = int(np.sum(cfg.kv_heads * (per4 * n4 + per8 * n8)))
+    qb = len(n) * cfg.q_heads * cfg.head_dim * 2
+    ob = len(n) * cfg.q_heads * cfg.head_dim * 4
+    bt = int(np.sum(4 * np.ceil(n4 / 16)))
+    return kv + qb + ob + bt
+
+
+def decode_bytes_bf16(n, cfg):
+    kv = int(np.sum(cfg.kv_heads * 2 * cfg.head_dim * 2 * n))
+    return kv + len(n) * cfg.q_heads * cfg.head_dim * (2 + 4) + int(np.sum(4 * np.ceil(n / 16)))
+
+
+def append_bytes_kv4(n, cfg):
+    """Reads bf16 k, v of the new tokens; writes their INT4 entries and (every
+    new token is recent when R >= 1) their INT8 entries."""
+    B = len(n)
+    rd = B * cfg.kv_heads * cfg.head_dim * 2 * 2
+    ng = cfg.head_dim // cfg.group
+    wr = B * cfg.kv_heads * (cfg.head_dim + 8 * ng + (2 * cfg.head_dim + 4 if cfg.recent > 0 else 0))
+    return rd + wr
+
+
+def append_bytes_bf16(n, cfg):
+    return len(n) * cfg.kv_heads * cfg.head_dim * 2 * 2 * 2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the decode step shards by sequence or kv head with no "
+                                   "exchange inside the op; see DESIGN.md)"}))
+        sys.exit(2)
+
+    import torch
+    from int8_mixed_precision_amd import kv4
+    from int8_mixed_precision_amd import workloads as W
+    from tests import gpu_harness as H
+
+    cfg = W.CONFIGS[args.config]
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    B = cfg.batch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
+
+    kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
+                        seed=cfg.seed, device="cuda:0")
+    caches = [("kv4", kv4c)]
+    if not args.no_bf16:
+        bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
+                           kind=kv4.KV4_KIND_BF16, device="cuda:0")
+        caches.append(("bf16", bfc))
+    # build every cache from the same sources, sequence chunk by chunk
+    step_k, step_v = [], []
+    for lo in range(0, B, 32):
+        seqs = list(range(lo, min(B, lo + 32)))
+        ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
+        for _, c in caches:
+            H.append_chunks(c, 0, [ks[i][:int(ctx[s])] for i, s in enumerate(seqs)],
+                            [vs[i][:int(ctx[s])] for i, s in enumerate(seqs)], [0] * len(seqs),
+                            seqs, device="cuda:0")
+        for i, s in enumerate(seqs):
+            step_k.append(ks[i][int(ctx[s]):int(ctx[s]) + 1])
+            step_v.append(vs[i][int(ctx[s]):int(ctx[s]) + 1])
+        torch.cuda.synchronize()
+        log(f"built sequences {seqs[0]}..{seqs[-1]}")
+    knew = H.to_dev_bf16(np.concatenate(step_k, 0), "cuda:0")
+    vnew = H.to_dev_bf16(np.concatenate(step_v, 0), "cuda:0")
+    q = H.to_dev_bf16(W.queries(cfg, 0), "cuda:0")
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    ctx_d = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    n_d = torch.from_numpy(n.astype(np.int32)).to(dev)
+    max_ctx = int(n.max())
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+    log(f"caches built in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    results = {}
+    for name, c in caches:
+        out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+        ws = c.cache.workspace(B, max_ctx)
+        split_T, nsplit = kv4.kv4_decode_split_info(c.cache.handle, B, max_ctx)
+
+        def append():
+            kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B,
+                           B, stream)
+
+        def decode():
+            kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx,
+                                sm, out, kv4.KV4_OUT_F32, ws, stream)
+
+        for _ in range(args.warmup):
+            append()
+            decode()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            append()
+            ev[i][1].record(stream)
+            decode()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ta = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+        td = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+        assert torch.isfinite(out).all()
+        results[name] = dict(append_ms=float(ta.mean()), decode_ms=float(td.mean()),
+                             decode_ms_median=float(np.median(td)),
+                             decode_ms_p10=float(np.percentile(td, 10)),
+                             decode_ms_p90=float(np.percentile(td, 90)),
+                             wall_ms_per_step=wall * 1e3 / args.steps,
+                             split_tokens=split_T, nsplit=nsplit)
+        log(f"{name}: append {ta.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
+            f"(median {np.median(td) * 1e3:.1f}), split {split_T}")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies")
+
+    r = results["kv4"]
+    db = decode_bytes_kv4(n, cfg)
+    ab = append_bytes_kv4(n, cfg)
+    step_ms = r["append_ms"] + r["decode_ms"]
+    value = (db + ab) / (step_ms * 1e-3) / 1e9
+    achieved = db / (r["decode_ms"] * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("kernel_source_hash") == _kernel_hash():
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    line = {
+        "metric": "decode-attn KV GB/s (% of HBM peak) and tokens/s vs BF16-KV, Qwen3-8B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V, 4 outlier K channels x10)",
+        "config": {
+            "workload": "Qwen3-8B-shaped attention layer, batch 256 ragged decode step "
+                        "(lognormal contexts median 4k, max 16k), 32q/8kv heads, d=128, "
+                        "page 16, INT4 group 32, S=4, R=128",
+            "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
+            "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
+            "split_tokens": r["split_tokens"],
+        },
+        "decode_attn_gbs": round(achieved, 2),
+        "decode_attn_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
+        "decode_attn_us_median_p10_p90": [round(r["decode_ms_median"] * 1e3, 2),
+                                          round(r["decode_ms_p10"] * 1e3, 2),
+                                          round(r["decode_ms_p90"] * 1e3, 2)],
+        "append_us": round(r["append_ms"] * 1e3, 2),
+        "decode_alg_bytes": db,
+        "append_alg_bytes": ab,
+        "layer_tokens_per_s": round(B / (step_ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "kv4_decode_attn (decode_split_kv4 + merge_parts)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if "bf16" in results:
+        rb = results["bf16"]
+        bstep = rb["append_ms"] + rb["decode_ms"]
+        line["bf16_comparator"] = {
+            "decode_attn_us": round(rb["decode_ms"] * 1e3, 2),
+            "append_us": round(rb["append_ms"] * 1e3, 2),
+            "decode_attn_gbs": round(decode_bytes_bf16(n, cfg) / (rb["decode_ms"] * 1e-3) / 1e9, 2),
+            "layer_tokens_per_s": round(B / (bstep * 1e-3), 1),
+        }
+        line["speedup_vs_bf16_step"] = round(bstep / step_ms, 3)
+        line["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, ctx, n, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_hash():
+    import hashlib
+    from int8_mixed_precision_amd import build as hb
+    h = hashlib.sha256()
+    for f in hb.sources():
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(cfg, ctx, n, seconds):
+    """The fp64 oracle's decode step (quantize the new token, attend over the
+    dequantized cache) on a bounded sample of the same workload: the first
+    sequences of the batch, as many as take about `seconds` of CPU time."""
+    import oracle
+    from int8_mixed_precision_amd import workloads as W
+
+    q = W.queries(cfg, 0)
+
+    def run(k):
+        seqs = list(range(k))
+        ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
+        cache = oracle.MixedCache(ks, vs, cfg.group, protect=(cfg.sink, cfg.recent))
+        newk = np.stack([x[-1] for x in ks])
+        newv = np.stack([x[-1] for x in vs])
+        t0 = time.perf_counter()
+        # the step: quantize the new token into both representations ...
+        oracle.quant_int4(newk, cfg.group)
+        oracle.quant_int4(newv, cfg.group)
+        oracle.quant_int8(newk)
+        oracle.quant_int8(newv)
+        # ... and attend over the whole context (history + new token)
+        oracle.attend_mixed(q[seqs], cache, cfg.sink, cfg.recent, 1 / math.sqrt(cfg.head_dim))
+        return time.perf_counter() - t0
+
+    k = 2
+    elapsed = run(k)
+    k = int(min(cfg.batch, max(1, round(k * seconds / max(elapsed, 1e-3)))))
+    elapsed = run(k)
+    sub = n[:k]
+    nb = decode_bytes_kv4(sub, cfg) + append_bytes_kv4(sub, cfg)
+    return {"value": round(nb / elapsed / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {k} of {cfg.batch} sequences ({int(sub.sum())} context tokens), "
+                      f"one decode step (quantize new token + fp64 attention), {elapsed:.1f} s",
+            "seconds": round(elapsed, 2)}
+
+
+if __name__ == "__main__":
+    main()

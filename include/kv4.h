@@ -1,0 +1,204 @@
+/*
+ * kv4.h -- C ABI of the KV4 decode-step library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the decode step of a rollout engine whose KV cache is
+ * stored as calibration-free asymmetric INT4 with FP16 scale and offset per
+ * channel group, plus symmetric INT8 side copies of the attention-sink and
+ * recent positions (KV4-RL, arXiv 2610.14448: Section 3 eq. 3.3; Section 5.1;
+ * Section 5.2 "Bounded selective protection"; Section 5.3; Appendix A.2
+ * "Scheduling and attention" and "Phase memory management"; Appendix A.3).
+ * A BF16 cache kind with the same paging and the same split/merge structure is
+ * provided as the comparator (the paper's BF16 baseline, Section 6.1).
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers unless stated otherwise; the
+ *     library never allocates, frees or initialises device memory.  Pools and
+ *     workspaces are owned by the caller.
+ *   - Work is enqueued asynchronously on the given HIP stream; device-side
+ *     faults surface at the caller's next synchronisation with that stream.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and a KV4_ERR_* code is returned.  Device arrays
+ *     (lengths, slot ids, block tables) cannot be checked on the host: the
+ *     kernels clamp them into the declared ranges, so out-of-range values give
+ *     wrong results but never out-of-bounds accesses.
+ *   - A kv4_cache handle is not thread-safe; calls on one handle that overlap
+ *     in time on different streams race on the pools.
+ *
+ * Layout of the pools (all little-endian; "PB" = one (page, kv-head) block):
+ *   page pool, KV4 kind: [layer][page][kv_head] blocks of
+ *       K codes  16 tokens x head_dim/2 bytes, token-major; byte i of token t
+ *                holds channel 2i in bits 0-3 and channel 2i+1 in bits 4-7;
+ *       V codes  2 halves x head_dim 32-bit words; word (h, c) holds the codes
+ *                of tokens 8h..8h+7 at channel c, token 8h+e in bits 4e..4e+3;
+ *       K delta  [group][16 tokens] binary16;   K offset [group][16] binary16;
+ *       V delta  [group][16 tokens] binary16;   V offset [group][16] binary16;
+ *     i.e. 16 * (head_dim + 8 * head_dim / group_size) bytes per PB
+ *     (2,560 B at head_dim 128, group 32: 160 B per token and kv head).
+ *   page pool, BF16 kind: [layer][page][kv_head] blocks of K [16][head_dim]
+ *     bf16 then V [16][head_dim] bf16 (8,192 B at head_dim 128).
+ *   side pool (KV4 kind only): [layer][slot][kv_head] blocks of
+ *       K codes [S+R][head_dim] int8, V codes [S+R][head_dim] int8,
+ *       K scale [S+R] binary16, V scale [S+R] binary16, padded to 16 bytes.
+ *     Position p of a sequence lives in ring entry p when p < S and in entry
+ *     S + (p - S) mod R otherwise.
+ */
+#ifndef KV4_H
+#define KV4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define KV4_OK                0
+#define KV4_ERR_INVALID_ARG   1  /* null pointer, negative size, bad enum, shape mismatch */
+#define KV4_ERR_UNSUPPORTED   2  /* a valid request this build does not implement */
+#define KV4_ERR_CAPACITY      3  /* batch > max_slots, layer >= num_layers, pool too small */
+#define KV4_ERR_WORKSPACE     4  /* workspace pointer null or smaller than required */
+#define KV4_ERR_HIP           5  /* a HIP runtime call failed (launch error) */
+
+/* Cache kinds. */
+#define KV4_KIND_MIXED 0         /* INT4 pages + INT8 sink/recent side ring */
+#define KV4_KIND_BF16  1         /* BF16 pages, no protection (comparator) */
+
+/* Flags (kv4_cache_desc.flags). */
+#define KV4_FLAG_ROTATE_K 0x1    /* Hadamard rotation of K and q: not built yet,
+                                    returns KV4_ERR_UNSUPPORTED */
+
+/* Output dtypes of kv4_decode_attn. */
+#define KV4_OUT_F32  0
+#define KV4_OUT_BF16 1
+
+/* HIP stream handle, passed through untouched (hipStream_t). */
+typedef void* kv4_stream_t;
+
+typedef struct kv4_cache_desc {
+    int32_t num_layers;         /* >= 1 */
+    int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+    int32_t num_kv_heads;       /* Hkv; Hq / Hkv in {1, 2, 4, 8} */
+    int32_t head_dim;           /* d; this build supports 128 */
+    int32_t page_size;          /* tokens per page; this build supports 16 */
+    int32_t group_size;         /* G, INT4 channels per (Delta, m) pair: 32, 64 or 128 */
+    int32_t sink;               /* S >= 0: first S positions kept as INT8 */
+    int32_t recent;             /* R >= 0: last R positions kept as INT8 */
+    int32_t num_pages;          /* pages per layer in the page pool, >= 1 */
+    int32_t max_slots;          /* request slots (rows of the block table, side rings) */
+    int32_t max_pages_per_seq;  /* columns of the block table */
+    int32_t kind;               /* KV4_KIND_MIXED or KV4_KIND_BF16 */
+    int32_t flags;              /* KV4_FLAG_* */
+    int32_t split_tokens;       /* context-split length for decode; 0 = automatic,
+                                   else a positive multiple of 32 */
+} kv4_cache_desc;
+
+typedef struct kv4_cache kv4_cache;  /* opaque host-side handle */
+
+/*
+ * Bytes of device memory the caller must provide (KV4-RL Appendix A.2, "Phase
+ * memory management": the pool is provisioned as floor(M_q / b_q) pages, where
+ * b_q counts every byte of a 16-token page including metadata; side storage is
+ * reserved per request slot, Appendix A.3 "Encoding and allocation").
+ *   page_pool_bytes  num_layers * num_pages * num_kv_heads * PB bytes
+ *   side_pool_bytes  num_layers * max_slots * num_kv_heads * ring block bytes
+ *                    (0 for the BF16 kind, or when S + R = 0)
+ * page_bytes_per_layer (optional, may be NULL) receives b_q for one layer, so a
+ * caller can size num_pages = floor(M / (num_layers * b_q)).
+ * Host-only; never touches the GPU.
+ */
+int kv4_cache_required_bytes(const kv4_cache_desc* desc, size_t* page_pool_bytes,
+                             size_t* side_pool_bytes, size_t* page_bytes_per_layer);
+
+/*
+ * Create a handle over caller-owned pools.  page_pool / side_pool are device
+ * buffers of at least the sizes kv4_cache_required_bytes returns (side_pool
+ * may be NULL when that size is 0).  Pools need no initialisation: a position
+ * is only ever read after the append that wrote it.  *out receives a host
+ * object freed with kv4_cache_free.  No device work.
+ */
+int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_pool_bytes,
+                     void* side_pool, size_t side_pool_bytes, kv4_cache** out);
+
+/*
+ * Append new tokens' keys and values to layer `layer` (KV4-RL Section 5.3:
+ * both cache representations are produced directly from the source K/V
+ * vectors when each token is generated; Appendix A.3: prefill and carried-
+ * prefix reconstruction populate both representations).
+ *
+ *   k_bf16, v_bf16  [total_new][Hkv][d] bf16, keys after RoPE, sequence-major
+ *   cu_new          [batch+1] int32, prefix sums of new tokens per sequence
+ *                   (cu_new[0] = 0, cu_new[batch] = total_new)
+ *   ctx_before      [batch] int32, context length before this append; the new
+ *                   tokens of sequence b take positions ctx_before[b] ..
+ *                   ctx_before[b] + new_b - 1
+ *   slot_ids        [batch] int32, request slot of each sequence (distinct)
+ *   block_tables    [max_slots][max_pages_per_seq] int32, page ids per slot;
+ *                   every page covering a written position must be assigned
+ *
+ * KV4 kind: every new position gets its INT4 codes, Delta and m written into
+ * its page.  A new position also gets an INT8 entry in the slot's side ring
+ * when it is protected in the context as it stands after this append, i.e.
+ * p < S or p >= ctx_before + new_b - R.  A position that later leaves the
+ * recent window needs no further work (demotion moves only the region
+ * boundary; its INT4 entry already exists).  BF16 kind: the bf16 values are
+ * copied into the pages.
+ * Errors: KV4_ERR_INVALID_ARG (null pointers, batch < 1, total_new < 0),
+ * KV4_ERR_CAPACITY (layer out of range, batch > max_slots), KV4_ERR_HIP.
+ */
+int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf16,
+               const int32_t* cu_new, const int32_t* ctx_before, const int32_t* slot_ids,
+               const int32_t* block_tables, int batch, int total_new, kv4_stream_t stream);
+
+/*
+ * Workspace bytes kv4_decode_attn needs for `batch` sequences whose lengths
+ * (after the step's append) are at most max_ctx: the per-part outputs and
+ * log-normalisers of the split/merge.  Queries the current device's compute-
+ * unit count (the split plan depends on it); launches nothing.
+ */
+int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, size_t* bytes);
+
+/*
+ * GQA decode attention of one query token per sequence over its ragged, paged
+ * context (KV4-RL Section 5.3 and Appendix A.3 "Regional softmax merge",
+ * eq. A1): the INT4 region is processed in context splits and the protected
+ * region (sink + recent, read from the INT8 ring) as one more part; each part
+ * yields a locally normalised output and log-normaliser, and a merge kernel
+ * combines them by a stable log-sum-exp with zero weight for empty parts.
+ *
+ *   q_bf16      [batch][Hq][d] bf16 (after RoPE)
+ *   seq_lens    [batch] int32, n = context length after this step's append
+ *               (1 <= n <= max_ctx); the query attends over positions [0, n)
+ *   slot_ids    [batch] int32; block_tables as for kv4_append
+ *   max_ctx     host bound on every n; sizes the grid and the workspace
+ *   sm_scale    softmax scale applied to q.k (1/sqrt(d) is the usual choice)
+ *   out         [batch][Hq][d], float32 (KV4_OUT_F32) or bf16 (KV4_OUT_BF16)
+ *   workspace   device buffer of >= kv4_decode_workspace_bytes(cache, batch, max_ctx)
+ * q head j reads kv head j / (Hq / Hkv).  Protected positions of an n-token
+ * context are [0, min(S, n)) and [max(S, n - R), n); all others read INT4.
+ * Errors: KV4_ERR_INVALID_ARG, KV4_ERR_CAPACITY, KV4_ERR_WORKSPACE, KV4_ERR_HIP.
+ */
+int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                    const int32_t* slot_ids, const int32_t* block_tables, int batch,
+                    int max_ctx, float sm_scale, void* out, int out_dtype, void* workspace,
+                    size_t workspace_bytes, kv4_stream_t stream);
+
+/* Free the host handle (the pools stay with the caller). NULL is accepted. */
+int kv4_cache_free(kv4_cache* cache);
+
+/* Static, human-readable text for a return code. */
+const char* kv4_status_string(int status);
+
+/*
+ * Context-split length (tokens) kv4_decode_attn uses for this batch shape, and
+ * the number of splits reserved for the longest INT4 region.  For tests and
+ * for reporting; launches nothing.
+ */
+int kv4_decode_split_info(const kv4_cache* cache, int batch, int max_ctx,
+                          int* split_tokens, int* num_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KV4_H */

@@ -1,0 +1,287 @@
+// kv4.hip -- host side of the KV4 C ABI (include/kv4.h): argument validation,
+// pool sizing, work decomposition and kernel launches.  Nothing here allocates
+// device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "kv4_append.hpp"
+#include "kv4_common.hpp"
+#include "kv4_decode.hpp"
+
+struct kv4_cache {
+    kv4_cache_desc desc;
+    kv4::Geo geo;
+    uint8_t* pages;
+    size_t page_bytes;
+    uint8_t* side;
+    size_t side_bytes;
+    int num_cus;                 // queried lazily at the first launch
+};
+
+namespace {
+
+constexpr int kMaxSinkRecent = 1 << 16;
+
+int validate_desc(const kv4_cache_desc* d)
+{
+    if (d == nullptr) return KV4_ERR_INVALID_ARG;
+    if (d->num_layers < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1 || d->head_dim < 1 ||
+        d->page_size < 1 || d->group_size < 1 || d->sink < 0 || d->recent < 0 ||
+        d->num_pages < 1 || d->max_slots < 1 || d->max_pages_per_seq < 1 ||
+        d->split_tokens < 0)
+        return KV4_ERR_INVALID_ARG;
+    if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
+    if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16) return KV4_ERR_INVALID_ARG;
+    if (d->flags & ~KV4_FLAG_ROTATE_K) return KV4_ERR_INVALID_ARG;
+    if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
+    if (d->split_tokens % 32 != 0) return KV4_ERR_INVALID_ARG;
+    int gqa = d->num_q_heads / d->num_kv_heads;
+    if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
+    if (d->head_dim != kv4::kHeadDim || d->page_size != kv4::kPage) return KV4_ERR_UNSUPPORTED;
+    if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
+    if (d->flags & KV4_FLAG_ROTATE_K) return KV4_ERR_UNSUPPORTED;
+    if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
+    if ((int64_t)d->max_pages_per_seq * kv4::kPage > INT32_MAX / 2) return KV4_ERR_CAPACITY;
+    return KV4_OK;
+}
+
+void sizes(const kv4::Geo& g, size_t* page_pool, size_t* side_pool, size_t* per_layer_page)
+{
+    if (page_pool) *page_pool = (size_t)g.layer_pages * (size_t)g.num_layers;
+    if (side_pool) *side_pool = (size_t)g.layer_side * (size_t)g.num_layers;
+    if (per_layer_page) *per_layer_page = (size_t)g.pb * (size_t)g.Hkv;
+}
+
+int num_cus(kv4_cache* c)
+{
+    if (c->num_cus > 0) return c->num_cus;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        c->num_cus = n;
+    return c->num_cus > 0 ? c->num_cus : 256;
+}
+
+// Context-split length: explicit, or chosen so that a batch whose sequences
+// all reached max_ctx would give about 8 work items per compute unit, within
+// [256, 4096] tokens.
+void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split, int* nsplit)
+{
+    const kv4::Geo& g = c->geo;
+    int T = c->desc.split_tokens;
+    if (T == 0) {
+        double work = (double)batch * g.Hkv * (double)max_ctx;
+        double target = 8.0 * cus;
+        double t = work / target;
+        T = 256;
+        while (T < 4096 && T < t) T *= 2;
+    }
+    int len = g.kind == KV4_KIND_MIXED ? max(max_ctx - g.S, 0) : max_ctx;
+    *split = T;
+    *nsplit = max((len + T - 1) / T, 1);
+}
+
+size_t workspace_bytes(const kv4::Geo& g, int batch, int nsplit)
+{
+    return (size_t)batch * g.Hkv * (size_t)(nsplit + 1) * g.gqa * (g.d + kv4::kPartPad) * sizeof(float);
+}
+
+int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
+}
+
+template <int GQA>
+void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
+{
+    dim3 grid(a.nsplit + (a.g.kind == KV4_KIND_MIXED ? 1 : 0), a.g.Hkv, a.batch);
+    if (a.g.kind == KV4_KIND_MIXED)
+        hipLaunchKernelGGL(kv4::decode_split_kv4_kernel<GQA>, grid, dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL(kv4::decode_split_bf16_kernel<GQA>, grid, dim3(64), 0, s, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv4_cache_required_bytes(const kv4_cache_desc* desc, size_t* page_pool_bytes,
+                             size_t* side_pool_bytes, size_t* page_bytes_per_layer)
+{
+    int st = validate_desc(desc);
+    if (st != KV4_OK) return st;
+    if (page_pool_bytes == nullptr && side_pool_bytes == nullptr && page_bytes_per_layer == nullptr)
+        return KV4_ERR_INVALID_ARG;
+    sizes(kv4::make_geo(*desc), page_pool_bytes, side_pool_bytes, page_bytes_per_layer);
+    return KV4_OK;
+}
+
+int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_pool_bytes,
+                     void* side_pool, size_t side_pool_bytes, kv4_cache** out)
+{
+    if (out == nullptr) return KV4_ERR_INVALID_ARG;
+    *out = nullptr;
+    int st = validate_desc(desc);
+    if (st != KV4_OK) return st;
+    kv4::Geo g = kv4::make_geo(*desc);
+    size_t need_pages = 0, need_side = 0;
+    sizes(g, &need_pages, &need_side, nullptr);
+    if (page_pool == nullptr) return KV4_ERR_INVALID_ARG;
+    if (need_side > 0 && side_pool == nullptr) return KV4_ERR_INVALID_ARG;
+    if (page_pool_bytes < need_pages || side_pool_bytes < need_side) return KV4_ERR_CAPACITY;
+    kv4_cache* c = new (std::nothrow) kv4_cache;
+    if (c == nullptr) return KV4_ERR_CAPACITY;
+    c->desc = *desc;
+    c->geo = g;
+    c->pages = static_cast<uint8_t*>(page_pool);
+    c->page_bytes = page_pool_bytes;
+    c->side = static_cast<uint8_t*>(side_pool);
+    c->side_bytes = side_pool_bytes;
+    c->num_cus = 0;
+    *out = c;
+    return KV4_OK;
+}
+
+int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf16,
+               const int32_t* cu_new, const int32_t* ctx_before, const int32_t* slot_ids,
+               const int32_t* block_tables, int batch, int total_new, kv4_stream_t stream)
+{
+    if (cache == nullptr || batch < 0 || total_new < 0) return KV4_ERR_INVALID_ARG;
+    const kv4::Geo& g = cache->geo;
+    if (layer < 0 || layer >= g.num_layers) return KV4_ERR_CAPACITY;
+    if (batch > g.max_slots) return KV4_ERR_CAPACITY;
+    if (batch == 0 || total_new == 0) return KV4_OK;
+    if (k_bf16 == nullptr || v_bf16 == nullptr || cu_new == nullptr || ctx_before == nullptr ||
+        slot_ids == nullptr || block_tables == nullptr)
+        return KV4_ERR_INVALID_ARG;
+    kv4::AppendArgs a;
+    a.g = g;
+    a.layer = layer;
+    a.k = static_cast<const uint16_t*>(k_bf16);
+    a.v = static_cast<const uint16_t*>(v_bf16);
+    a.cu_new = cu_new;
+    a.ctx_before = ctx_before;
+    a.slot_ids = slot_ids;
+    a.block_tables = block_tables;
+    a.batch = batch;
+    a.total_new = total_new;
+    a.pages = cache->pages;
+    a.side = cache->side;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // parallelism along each sequence sized by the mean number of new tokens
+    int64_t mean_new = ((int64_t)total_new + batch - 1) / batch;
+    if (g.kind == KV4_KIND_MIXED) {
+        int gx = (int)std::min<int64_t>((mean_new + kv4::kHalf - 1) / kv4::kHalf + 1, 64);
+        if (mean_new <= 1) gx = 1;
+        dim3 grid(gx, g.Hkv, batch);
+        switch (g.G) {
+            case 32: hipLaunchKernelGGL(kv4::append_kv4_kernel<32>, grid, dim3(64), 0, s, a); break;
+            case 64: hipLaunchKernelGGL(kv4::append_kv4_kernel<64>, grid, dim3(64), 0, s, a); break;
+            default: hipLaunchKernelGGL(kv4::append_kv4_kernel<128>, grid, dim3(64), 0, s, a); break;
+        }
+    } else {
+        int gx = (int)std::min<int64_t>(mean_new, 256);
+        dim3 grid(gx, g.Hkv, batch);
+        hipLaunchKernelGGL(kv4::append_bf16_kernel, grid, dim3(64), 0, s, a);
+    }
+    return launch_status();
+}
+
+int kv4_decode_split_info(const kv4_cache* cache, int batch, int max_ctx, int* split_tokens,
+                          int* num_splits)
+{
+    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
+    int T, ns;
+    int cus = cache->num_cus > 0 ? cache->num_cus : 256;
+    split_plan(cache, batch, max_ctx, cus, &T, &ns);
+    if (split_tokens) *split_tokens = T;
+    if (num_splits) *num_splits = ns;
+    return KV4_OK;
+}
+
+int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, size_t* bytes)
+{
+    if (cache == nullptr || bytes == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
+    const kv4::Geo& g = cache->geo;
+    if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
+    int T, ns;
+    split_plan(cache, batch, max_ctx, num_cus(const_cast<kv4_cache*>(cache)), &T, &ns);
+    *bytes = workspace_bytes(g, batch, ns);
+    return KV4_OK;
+}
+
+int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                    const int32_t* slot_ids, const int32_t* block_tables, int batch, int max_ctx,
+                    float sm_scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes_,
+                    kv4_stream_t stream)
+{
+    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
+    const kv4::Geo& g = cache->geo;
+    if (layer < 0 || layer >= g.num_layers) return KV4_ERR_CAPACITY;
+    if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
+    if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale)) return KV4_ERR_INVALID_ARG;
+    if (batch == 0) return KV4_OK;
+    if (q_bf16 == nullptr || seq_lens == nullptr || slot_ids == nullptr || block_tables == nullptr ||
+        out == nullptr)
+        return KV4_ERR_INVALID_ARG;
+    int T, ns;
+    split_plan(cache, batch, max_ctx, num_cus(cache), &T, &ns);
+    size_t need = workspace_bytes(g, batch, ns);
+    if (workspace == nullptr || workspace_bytes_ < need) return KV4_ERR_WORKSPACE;
+    kv4::DecodeArgs a;
+    a.g = g;
+    a.layer = layer;
+    a.q = static_cast<const uint16_t*>(q_bf16);
+    a.seq_lens = seq_lens;
+    a.slot_ids = slot_ids;
+    a.block_tables = block_tables;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.split = T;
+    a.nsplit = ns;
+    a.scale2 = sm_scale * 1.4426950408889634f;
+    a.pages = cache->pages;
+    a.side = cache->side;
+    a.part = static_cast<float*>(workspace);
+    a.out = out;
+    a.out_dtype = out_dtype;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (g.gqa) {
+        case 1: launch_decode<1>(a, s); break;
+        case 2: launch_decode<2>(a, s); break;
+        case 4: launch_decode<4>(a, s); break;
+        default: launch_decode<8>(a, s); break;
+    }
+    int st = launch_status();
+    if (st != KV4_OK) return st;
+    int rows = batch * g.Hq;
+    hipLaunchKernelGGL(kv4::merge_parts_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+    return launch_status();
+}
+
+int kv4_cache_free(kv4_cache* cache)
+{
+    delete cache;
+    return KV4_OK;
+}
+
+const char* kv4_status_string(int status)
+{
+    switch (status) {
+        case KV4_OK: return "KV4_OK: success";
+        case KV4_ERR_INVALID_ARG: return "KV4_ERR_INVALID_ARG: invalid argument";
+        case KV4_ERR_UNSUPPORTED: return "KV4_ERR_UNSUPPORTED: valid request not supported by this build";
+        case KV4_ERR_CAPACITY: return "KV4_ERR_CAPACITY: exceeds a declared capacity";
+        case KV4_ERR_WORKSPACE: return "KV4_ERR_WORKSPACE: workspace missing or too small";
+        case KV4_ERR_HIP: return "KV4_ERR_HIP: HIP runtime error";
+        default: return "unknown kv4 status";
+    }
+}
+
+}  // extern "C"

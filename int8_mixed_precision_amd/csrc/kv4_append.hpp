@@ -1,0 +1,213 @@
+// kv4_append.hpp -- append kernels: quantize each new token's K and V into the
+// paged INT4 cache and, for protected positions, into the INT8 side ring.
+//
+// KV4-RL (arXiv 2610.14448): affine INT4 x^ = Delta*c + m with FP16 Delta and
+// m (Section 3 eq. 3.3; Section 5.1; Appendix A.3 "Encoding and allocation");
+// INT8 side entries with symmetric per-token/head scaling, computed from the
+// source vector (Appendix A.3); both produced when the token is generated, so
+// leaving the recent window needs no requantization (Section 5.3).
+//
+// Quantizer readings (the pages fix only the affine form and FP16 metadata):
+//   m = fp16(min x), r = fp32(max x - m), Delta = fp16(fp32(r / 15)), Delta = 0
+//   when r <= 0 or it rounds to 0; c = nearest integer in [0,15] to the exact
+//   (x - m)/Delta, ties to even.  INT8: s = fp16(fp32(amax / 127)),
+//   c = nearest integer to the exact x/s, ties to even, in [-127, 127].
+//   Stored zeros are +0.  Exactness: the code is first estimated in binary64
+//   and then checked against the exact binary64 midpoints m + (c +- 1/2)Delta
+//   (exact because m and Delta are binary16 values), so the result is the
+//   exact nearest code for every finite bf16 input.
+#pragma once
+
+#include "kv4_common.hpp"
+
+namespace kv4 {
+
+struct AppendArgs {
+    Geo g;
+    int layer;
+    const uint16_t* k;           // [total_new][Hkv][d] bf16
+    const uint16_t* v;
+    const int32_t* cu_new;       // [batch+1]
+    const int32_t* ctx_before;   // [batch]
+    const int32_t* slot_ids;     // [batch]
+    const int32_t* block_tables; // [max_slots][max_pages]
+    int batch, total_new;
+    uint8_t* pages;
+    uint8_t* side;
+};
+
+__device__ __forceinline__ uint16_t plus_zero16(uint16_t h) { return h == 0x8000u ? (uint16_t)0 : h; }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
+{
+    _Float16 h = (_Float16)f;     // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// INT4 parameters of a group whose values are spread over `lanes` consecutive
+// lanes (two channels per lane).  Returns Delta and m bit patterns.
+template <int LANES>
+__device__ __forceinline__ void int4_params(float x0, float x1, uint16_t& db, uint16_t& mb)
+{
+    float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
+#pragma unroll
+    for (int off = 1; off < LANES; off <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off));
+        hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    mb = plus_zero16(f32_to_f16_bits(lo));
+    float mf = half_bits_to_float(mb);
+    float r = hi - mf;
+    db = 0;
+    if (r > 0.0f) db = plus_zero16(f32_to_f16_bits(__fdiv_rn(r, 15.0f)));
+}
+
+__device__ __forceinline__ uint32_t int4_code(float x, double D, double M, uint16_t db)
+{
+    if (db == 0) return 0u;
+    double xv = (double)x;
+    int c = (int)rint((xv - M) / D);
+    c = clampi(c, 0, 15);
+    if (c > 0) {
+        double mid = M + ((double)c - 0.5) * D;
+        if (xv < mid || (xv == mid && (c & 1))) c -= 1;
+    }
+    if (c < 15) {
+        double mid = M + ((double)c + 0.5) * D;
+        if (xv > mid || (xv == mid && ((c + 1) & 1) == 0)) c += 1;
+    }
+    return (uint32_t)c;
+}
+
+__device__ __forceinline__ int int8_code(float x, double S, uint16_t sb)
+{
+    if (sb == 0) return 0;
+    double a = fabs((double)x);
+    int c = (int)rint(a / S);
+    c = clampi(c, 0, 127);
+    if (c > 0) {
+        double mid = ((double)c - 0.5) * S;
+        if (a < mid || (a == mid && (c & 1))) c -= 1;
+    }
+    if (c < 127) {
+        double mid = ((double)c + 0.5) * S;
+        if (a > mid || (a == mid && ((c + 1) & 1) == 0)) c += 1;
+    }
+    return x < 0.0f ? -c : c;
+}
+
+// Full-wave (64 lanes, 128 channels) INT8 scale.
+__device__ __forceinline__ uint16_t int8_scale(float x0, float x1)
+{
+    float a = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    return plus_zero16(f32_to_f16_bits(__fdiv_rn(a, 127.0f)));
+}
+
+// One wave per (sequence, kv head, 8-token half page) of new tokens; the wave
+// owns the half page's V code words, so read-modify-write of nibbles is
+// race-free.  Grid: (x, Hkv, batch); half pages are strided over x.
+template <int G>
+__global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
+{
+    const Geo& g = a.g;
+    const int b = blockIdx.z, h = blockIdx.y, lane = threadIdx.x;
+    int row0 = clampi(a.cu_new[b], 0, a.total_new);
+    int row1 = clampi(a.cu_new[b + 1], row0, a.total_new);
+    int p0 = max(a.ctx_before[b], 0);
+    int cap = g.max_pages * kPage;
+    int p1 = min(p0 + (row1 - row0), cap);
+    if (p1 <= p0) return;
+    int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    constexpr int LPG = G / 2;                 // lanes per group
+    const int grp = (2 * lane) / G;
+
+    uint8_t* ring = g.SR > 0 ? a.side + (int64_t)a.layer * g.layer_side +
+                                   ((int64_t)slot * g.Hkv + h) * g.rb
+                             : nullptr;
+
+    for (int hp = p0 / kHalf + blockIdx.x; hp <= (p1 - 1) / kHalf; hp += gridDim.x) {
+        int t_lo = max(hp * kHalf, p0), t_hi = min(hp * kHalf + kHalf, p1);
+        int page = clampi(bt[hp / 2], 0, g.num_pages - 1);
+        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
+        uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hp & 1) * g.d;
+        uint32_t w0 = vw[2 * lane], w1 = vw[2 * lane + 1];
+        for (int t = t_lo; t < t_hi; ++t) {
+            int64_t src = ((int64_t)(row0 + (t - p0)) * g.Hkv + h) * g.d;
+            uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
+            uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
+            float k0 = bf16_lo(kk), k1 = bf16_hi(kk), v0 = bf16_lo(vv), v1 = bf16_hi(vv);
+            int tp = t % kPage;
+            // ---- INT4, keys
+            uint16_t db, mb;
+            int4_params<LPG>(k0, k1, db, mb);
+            double D = (double)half_bits_to_float(db), M = (double)half_bits_to_float(mb);
+            uint32_t c0 = int4_code(k0, D, M, db), c1 = int4_code(k1, D, M, db);
+            pb[g.off_kc + tp * (g.d / 2) + lane] = (uint8_t)(c0 | (c1 << 4));
+            if ((lane % LPG) == 0) {
+                reinterpret_cast<uint16_t*>(pb + g.off_kd)[grp * kPage + tp] = db;
+                reinterpret_cast<uint16_t*>(pb + g.off_km)[grp * kPage + tp] = mb;
+            }
+            // ---- INT4, values
+            int4_params<LPG>(v0, v1, db, mb);
+            D = (double)half_bits_to_float(db);
+            M = (double)half_bits_to_float(mb);
+            c0 = int4_code(v0, D, M, db);
+            c1 = int4_code(v1, D, M, db);
+            int sh = 4 * (t % kHalf);
+            w0 = (w0 & ~(0xFu << sh)) | (c0 << sh);
+            w1 = (w1 & ~(0xFu << sh)) | (c1 << sh);
+            if ((lane % LPG) == 0) {
+                reinterpret_cast<uint16_t*>(pb + g.off_vd)[grp * kPage + tp] = db;
+                reinterpret_cast<uint16_t*>(pb + g.off_vm)[grp * kPage + tp] = mb;
+            }
+            // ---- INT8 side entry for positions protected at the new length
+            if (ring != nullptr && (t < g.S || t >= p1 - g.R)) {
+                int e = t < g.S ? t : g.S + (t - g.S) % g.R;
+                uint16_t sk = int8_scale(k0, k1), sv = int8_scale(v0, v1);
+                double Sk = (double)half_bits_to_float(sk), Sv = (double)half_bits_to_float(sv);
+                int a0 = int8_code(k0, Sk, sk), a1 = int8_code(k1, Sk, sk);
+                int b0 = int8_code(v0, Sv, sv), b1 = int8_code(v1, Sv, sv);
+                reinterpret_cast<uint16_t*>(ring + (int64_t)e * g.d)[lane] =
+                    (uint16_t)((a0 & 0xFF) | ((a1 & 0xFF) << 8));
+                reinterpret_cast<uint16_t*>(ring + (int64_t)(g.SR + e) * g.d)[lane] =
+                    (uint16_t)((b0 & 0xFF) | ((b1 & 0xFF) << 8));
+                if (lane == 0) {
+                    uint16_t* sc = reinterpret_cast<uint16_t*>(ring + (int64_t)2 * g.SR * g.d);
+                    sc[e] = sk;
+                    sc[g.SR + e] = sv;
+                }
+            }
+        }
+        vw[2 * lane] = w0;
+        vw[2 * lane + 1] = w1;
+    }
+}
+
+// BF16 comparator: copy the new tokens into bf16 pages.  Grid (x, Hkv, batch),
+// tokens strided over x.
+__global__ __launch_bounds__(64) void append_bf16_kernel(AppendArgs a)
+{
+    const Geo& g = a.g;
+    const int b = blockIdx.z, h = blockIdx.y, lane = threadIdx.x;
+    int row0 = clampi(a.cu_new[b], 0, a.total_new);
+    int row1 = clampi(a.cu_new[b + 1], row0, a.total_new);
+    int p0 = max(a.ctx_before[b], 0);
+    int p1 = min(p0 + (row1 - row0), g.max_pages * kPage);
+    int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    for (int t = p0 + blockIdx.x; t < p1; t += gridDim.x) {
+        int page = clampi(bt[t / kPage], 0, g.num_pages - 1);
+        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
+        int64_t src = ((int64_t)(row0 + (t - p0)) * g.Hkv + h) * g.d;
+        int tp = t % kPage;
+        uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
+        uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
+        reinterpret_cast<uint32_t*>(pb)[tp * (g.d / 2) + lane] = kk;
+        reinterpret_cast<uint32_t*>(pb + (int64_t)kPage * g.d * 2)[tp * (g.d / 2) + lane] = vv;
+    }
+}
+
+}  // namespace kv4

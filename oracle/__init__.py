@@ -158,7 +158,10 @@ class MixedCache:
     reads is decided by the position's region at attention time.
     """
 
-    def __init__(self, k_src, v_src, G: int):
+    def __init__(self, k_src, v_src, G: int, protect=None):
+        """``protect=(S, R)`` computes the INT8 copies only of positions that
+        are protected at the stored length (others stay zero); the default
+        computes them for every position, so any prefix can be attended."""
         self.G = G
         self.seq_lens = np.array([k.shape[0] for k in k_src], dtype=np.int32)
         self.pos_off = np.zeros(len(k_src), dtype=np.int64)
@@ -169,8 +172,21 @@ class MixedCache:
         self.Hkv, self.d = K.shape[1], K.shape[2]
         self.k4, self.k4d, self.k4m = quant_int4(K, G)
         self.v4, self.v4d, self.v4m = quant_int4(V, G)
-        self.k8, self.k8s = quant_int8(K)
-        self.v8, self.v8s = quant_int8(V)
+        if protect is None:
+            self.k8, self.k8s = quant_int8(K)
+            self.v8, self.v8s = quant_int8(V)
+        else:
+            S, R = protect
+            rows = np.concatenate([
+                o + np.nonzero([is_protected(p, n, S, R) for p in range(n)])[0]
+                for o, n in zip(self.pos_off, self.seq_lens)]).astype(np.int64)
+            self.k8 = np.zeros(K.shape, np.int8)
+            self.v8 = np.zeros(V.shape, np.int8)
+            self.k8s = np.zeros(K.shape[:2], np.uint16)
+            self.v8s = np.zeros(V.shape[:2], np.uint16)
+            if rows.size:
+                self.k8[rows], self.k8s[rows] = quant_int8(K[rows])
+                self.v8[rows], self.v8s[rows] = quant_int8(V[rows])
 
     def seq(self, b: int):
         """Row slice of sequence b."""

@@ -1,0 +1,104 @@
+"""Read the library's pools back into per-position arrays (test code only).
+
+Written from the pool layout stated in include/kv4.h, independently of the
+kernels, so that the GPU's bytes can be compared with the oracle's codes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 16
+
+
+def pb_bytes(d: int, G: int) -> int:
+    ng = d // G
+    return PAGE * d // 2 + PAGE * d // 2 + 4 * 2 * PAGE * ng
+
+
+def rb_bytes(d: int, SR: int) -> int:
+    return 0 if SR == 0 else -(-SR * (2 * d + 4) // 16) * 16
+
+
+def ring_entry(p: np.ndarray, S: int, R: int) -> np.ndarray:
+    p = np.asarray(p, dtype=np.int64)
+    return np.where(p < S, p, S + ((p - S) % R if R > 0 else 0))
+
+
+def gather_mixed(pages: np.ndarray, side, *, layer, num_pages, Hkv, d, G, S, R, max_slots,
+                 block_tables: np.ndarray, slot: int, n: int, protected_mask=None):
+    """Codes and metadata of positions [0, n) of the sequence in `slot`.
+
+    Returns a dict with k4, v4 (uint8 [n, Hkv, d]), k4d, k4m, v4d, v4m
+    (uint16 [n, Hkv, d/G]); and, for the positions where protected_mask is
+    true, k8, v8 (int8 [n, Hkv, d]) and k8s, v8s (uint16 [n, Hkv]) -- other
+    rows of those arrays are zero.
+    """
+    ng = d // G
+    PB = pb_bytes(d, G)
+    p = np.arange(n, dtype=np.int64)
+    page = block_tables[slot, p // PAGE].astype(np.int64)
+    tp = p % PAGE
+    h = np.arange(Hkv, dtype=np.int64)
+    base = ((layer * num_pages + page[:, None]) * Hkv + h[None, :]) * PB          # [n, Hkv]
+    # K codes: token-major bytes, channel 2i low nibble, 2i+1 high nibble
+    kb = pages[base[:, :, None] + (tp[:, None, None] * (d // 2)) + np.arange(d // 2)[None, None, :]]
+    k4 = np.empty((n, Hkv, d), dtype=np.uint8)
+    k4[:, :, 0::2] = kb & 0xF
+    k4[:, :, 1::2] = kb >> 4
+    # V codes: word (half, c) at offset 16*d/2 + 4*(half*d + c), token 8*half+e in bits 4e..
+    voff = PAGE * d // 2
+    widx = base[:, :, None] + voff + 4 * ((tp[:, None, None] // 8) * d + np.arange(d)[None, None, :])
+    words = (pages[widx].astype(np.uint32) | (pages[widx + 1].astype(np.uint32) << 8) |
+             (pages[widx + 2].astype(np.uint32) << 16) | (pages[widx + 3].astype(np.uint32) << 24))
+    v4 = ((words >> (4 * (tp[:, None, None] % 8)).astype(np.uint32)) & 0xF).astype(np.uint8)
+
+    def meta(off):
+        idx = base[:, :, None] + off + 2 * (np.arange(ng)[None, None, :] * PAGE + tp[:, None, None])
+        return (pages[idx].astype(np.uint16) | (pages[idx + 1].astype(np.uint16) << 8))
+
+    off_kd = PAGE * d
+    out = dict(k4=k4, v4=v4,
+               k4d=meta(off_kd), k4m=meta(off_kd + 2 * PAGE * ng),
+               v4d=meta(off_kd + 4 * PAGE * ng), v4m=meta(off_kd + 6 * PAGE * ng))
+    SR = S + R
+    k8 = np.zeros((n, Hkv, d), np.int8)
+    v8 = np.zeros((n, Hkv, d), np.int8)
+    k8s = np.zeros((n, Hkv), np.uint16)
+    v8s = np.zeros((n, Hkv), np.uint16)
+    if SR > 0 and protected_mask is not None and np.any(protected_mask):
+        RB = rb_bytes(d, SR)
+        pp = p[protected_mask]
+        e = ring_entry(pp, S, R)
+        rbase = ((layer * max_slots + slot) * Hkv + h[None, :]) * RB                  # [1, Hkv]
+        kk = side[rbase[:, :, None] + (e[:, None, None] * d) + np.arange(d)[None, None, :]]
+        vv = side[rbase[:, :, None] + ((SR + e)[:, None, None] * d) + np.arange(d)[None, None, :]]
+        k8[protected_mask] = kk.view(np.int8)
+        v8[protected_mask] = vv.view(np.int8)
+        sb = rbase + 2 * SR * d
+        ks = side[sb + 2 * e[:, None]].astype(np.uint16) | (side[sb + 2 * e[:, None] + 1].astype(np.uint16) << 8)
+        vs = side[sb + 2 * (SR + e)[:, None]].astype(np.uint16) | (
+            side[sb + 2 * (SR + e)[:, None] + 1].astype(np.uint16) << 8)
+        k8s[protected_mask] = ks
+        v8s[protected_mask] = vs
+    out.update(k8=k8, v8=v8, k8s=k8s, v8s=v8s)
+    return out
+
+
+def protected_mask(n: int, S: int, R: int) -> np.ndarray:
+    p = np.arange(n)
+    return (p < min(S, n)) | (p >= max(S, n - R))
+
+
+def gather_bf16(pages: np.ndarray, *, layer, num_pages, Hkv, d, block_tables, slot, n):
+    """K and V (float32 [n, Hkv, d]) of the BF16 kind's pages."""
+    PB = PAGE * d * 2 * 2
+    p = np.arange(n, dtype=np.int64)
+    page = block_tables[slot, p // PAGE].astype(np.int64)
+    tp = p % PAGE
+    h = np.arange(Hkv, dtype=np.int64)
+    base = ((layer * num_pages + page[:, None]) * Hkv + h[None, :]) * PB
+    idx = base[:, :, None] + 2 * (tp[:, None, None] * d + np.arange(d)[None, None, :])
+    k = (pages[idx].astype(np.uint32) | (pages[idx + 1].astype(np.uint32) << 8)) << 16
+    vi = idx + PAGE * d * 2
+    v = (pages[vi].astype(np.uint32) | (pages[vi + 1].astype(np.uint32) << 8)) << 16
+    return k.view(np.float32), v.view(np.float32)

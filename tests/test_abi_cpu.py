@@ -1,0 +1,177 @@
+"""CPU-only checks of the C ABI library: it loads, exports every function the
+header declares, sizes pools per the documented layout, and rejects invalid
+arguments before launching anything.  No compute call is made here.
+
+Storage figures pinned from the pages (tests/golden/storage.txt): KV4-RL
+Appendix D.4 gives 4.25 / 5.00 / 6.00 bits per element at group sizes
+128 / 32 / 16; Appendix B.3 gives kappa = 73,728 BF16 KV bytes per context
+position per GPU for Qwen3-4B/8B under TP2 (36 layers, 4 kv heads per GPU,
+d = 128); Appendix A.2 sizes pools in 16-token pages.
+"""
+import ctypes
+import os
+
+import pytest
+
+from int8_mixed_precision_amd import kv4
+from tests import layout as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "storage.txt")
+
+
+def _golden():
+    vals = {}
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = line.split("=")
+            vals[k.strip()] = float(v)
+    return vals
+
+
+def test_library_exports_every_declared_function():
+    names = kv4.declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(kv4.lib(), name), name
+    for name in ("kv4_cache_required_bytes", "kv4_cache_create", "kv4_append",
+                 "kv4_decode_workspace_bytes", "kv4_decode_attn", "kv4_cache_free",
+                 "kv4_status_string"):
+        assert name in names
+
+
+def test_storage_sizes_match_pages():
+    gold = _golden()
+    for G, key in ((128, "bits_per_elem_g128"), (32, "bits_per_elem_g32")):
+        d = kv4.make_desc(1, 32, 8, group_size=G, num_pages=1, max_slots=1, max_pages_per_seq=1)
+        pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
+        per_token_head = per_layer / (8 * 16)
+        assert per_token_head * 8 / 128 == gold[key] * 2          # K and V
+        assert per_layer == 8 * L.pb_bytes(128, G)
+    assert (L.pb_bytes(128, 32) / 16, L.pb_bytes(128, 128) / 16) == (160, 136)
+    # BF16 kind: kappa for 36 layers x 4 kv heads per GPU (TP2 of 8)
+    d = kv4.make_desc(36, 16, 4, kind=kv4.KV4_KIND_BF16, sink=0, recent=0, num_pages=1,
+                      max_slots=1, max_pages_per_seq=1)
+    pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
+    assert side == 0
+    assert pages / 16 == gold["kappa_bf16_bytes_per_position_tp2"]
+    # side ring: (S + R) entries of 2*d + 4 bytes per (slot, kv head)
+    d = kv4.make_desc(2, 32, 8, sink=4, recent=128, num_pages=7, max_slots=5, max_pages_per_seq=3)
+    pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
+    assert side == 2 * 5 * 8 * L.rb_bytes(128, 132) and L.rb_bytes(128, 132) == 132 * 260
+    assert pages == 2 * 7 * 8 * 2560
+
+
+def _err(fn, *a):
+    try:
+        fn(*a)
+    except kv4.KV4Error as e:
+        return e.code
+    return kv4.KV4_OK
+
+
+def test_invalid_descriptors():
+    base = dict(num_layers=1, num_q_heads=32, num_kv_heads=8, num_pages=4, max_slots=2,
+                max_pages_per_seq=4)
+    cases = [
+        (dict(num_layers=0), kv4.KV4_ERR_INVALID_ARG),
+        (dict(num_q_heads=30), kv4.KV4_ERR_INVALID_ARG),
+        (dict(group_size=48), kv4.KV4_ERR_INVALID_ARG),
+        (dict(group_size=16), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(head_dim=64, group_size=32), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(page_size=32), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(sink=-1), kv4.KV4_ERR_INVALID_ARG),
+        (dict(recent=-5), kv4.KV4_ERR_INVALID_ARG),
+        (dict(kind=7), kv4.KV4_ERR_INVALID_ARG),
+        (dict(flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(flags=0x10), kv4.KV4_ERR_INVALID_ARG),
+        (dict(split_tokens=48), kv4.KV4_ERR_INVALID_ARG),
+        (dict(num_q_heads=48, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
+    ]
+    for change, code in cases:
+        d = kv4.make_desc(**{**base, **change})
+        assert _err(kv4.kv4_cache_required_bytes, d) == code, change
+
+
+def _fake_handle(**kw):
+    base = dict(num_layers=2, num_q_heads=8, num_kv_heads=2, num_pages=4, max_slots=3,
+                max_pages_per_seq=4)
+    d = kv4.make_desc(**{**base, **kw})
+    pages, side, _ = kv4.kv4_cache_required_bytes(d)
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)                      # never dereferenced on the host
+    assert kv4.lib().kv4_cache_create(ctypes.byref(d), fake, pages, fake, side, ctypes.byref(h)) == 0
+    return h, d, pages, side
+
+
+def test_create_errors():
+    d = kv4.make_desc(1, 8, 2, num_pages=4, max_slots=3, max_pages_per_seq=4)
+    pages, side, _ = kv4.kv4_cache_required_bytes(d)
+    h = ctypes.c_void_p()
+    f = ctypes.c_void_p(1 << 20)
+    L_ = kv4.lib()
+    assert L_.kv4_cache_create(ctypes.byref(d), None, pages, f, side, ctypes.byref(h)) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_cache_create(ctypes.byref(d), f, pages - 1, f, side, ctypes.byref(h)) == kv4.KV4_ERR_CAPACITY
+    assert L_.kv4_cache_create(ctypes.byref(d), f, pages, f, side - 1, ctypes.byref(h)) == kv4.KV4_ERR_CAPACITY
+    assert L_.kv4_cache_create(ctypes.byref(d), f, pages, None, side, ctypes.byref(h)) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_cache_create(ctypes.byref(d), f, pages, f, side, None) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_cache_free(None) == kv4.KV4_OK
+
+
+def test_append_and_decode_validation_no_launch():
+    h, d, _, _ = _fake_handle()
+    L_ = kv4.lib()
+    f = ctypes.c_void_p(1 << 20)
+    # append
+    assert L_.kv4_append(None, 0, f, f, f, f, f, f, 1, 1, None) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_append(h, 2, f, f, f, f, f, f, 1, 1, None) == kv4.KV4_ERR_CAPACITY
+    assert L_.kv4_append(h, -1, f, f, f, f, f, f, 1, 1, None) == kv4.KV4_ERR_CAPACITY
+    assert L_.kv4_append(h, 0, f, f, f, f, f, f, 4, 4, None) == kv4.KV4_ERR_CAPACITY
+    assert L_.kv4_append(h, 0, None, f, f, f, f, f, 1, 1, None) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_append(h, 0, f, f, f, f, f, f, 1, -1, None) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_append(h, 0, None, None, None, None, None, None, 1, 0, None) == kv4.KV4_OK
+    # decode
+    ws = kv4.kv4_decode_workspace_bytes(h, 2, 64)
+    assert ws > 0
+    args = lambda **k: dict(dict(cache=h, layer=0, q=f, sl=f, slot=f, bt=f, batch=2, max_ctx=64,
+                                 scale=0.1, out=f, dt=kv4.KV4_OUT_F32, ws=f, wsb=ws), **k)
+
+    def call(**k):
+        a = args(**k)
+        return L_.kv4_decode_attn(a["cache"], a["layer"], a["q"], a["sl"], a["slot"], a["bt"],
+                                  a["batch"], a["max_ctx"], a["scale"], a["out"], a["dt"], a["ws"],
+                                  a["wsb"], None)
+
+    assert call(layer=5) == kv4.KV4_ERR_CAPACITY
+    assert call(batch=4) == kv4.KV4_ERR_CAPACITY
+    assert call(max_ctx=65) == kv4.KV4_ERR_CAPACITY           # 4 pages x 16
+    assert call(max_ctx=0) == kv4.KV4_ERR_INVALID_ARG
+    assert call(dt=9) == kv4.KV4_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == kv4.KV4_ERR_INVALID_ARG
+    assert call(q=None) == kv4.KV4_ERR_INVALID_ARG
+    assert call(out=None) == kv4.KV4_ERR_INVALID_ARG
+    assert call(ws=None) == kv4.KV4_ERR_WORKSPACE
+    assert call(wsb=ws - 1) == kv4.KV4_ERR_WORKSPACE
+    assert call(batch=0) == kv4.KV4_OK
+    kv4.kv4_cache_free(h)
+
+
+def test_split_plan_and_workspace():
+    h, d, _, _ = _fake_handle(split_tokens=64, max_pages_per_seq=64)
+    T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
+    assert T == 64 and ns == -(-(1024 - 4) // 64)
+    ws = kv4.kv4_decode_workspace_bytes(h, 3, 1024)
+    assert ws == 3 * 2 * (ns + 1) * 4 * (128 + 4) * 4
+    kv4.kv4_cache_free(h)
+    h, d, _, _ = _fake_handle(max_pages_per_seq=64)
+    T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
+    assert T % 32 == 0 and 256 <= T <= 4096 and ns * T >= 1024 - 4
+    kv4.kv4_cache_free(h)
+
+
+def test_status_strings():
+    for c in range(6):
+        s = kv4.kv4_status_string(c)
+        assert s.startswith("KV4_")
+    assert "unknown" in kv4.kv4_status_string(99)

@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar (KV4-RL decode step; tolerances fixed in advance):
+  * quantized bytes -- INT4 codes, Delta, m of every stored position and the
+    INT8 codes and scale of every protected position -- equal the oracle's
+    bit for bit;
+  * fp32 attention output: max |o - o*| <= 1e-3 and per-row
+    ||o - o*||_inf / max(||o*||_inf, 1e-6) <= 2e-3 against the oracle's fp64
+    attention over its own quantized cache.
+Pools are filled with 0xFF bytes (binary16 NaN patterns) before use, so any
+read of a position that was never written shows up as a mismatch or a NaN.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_mixed_precision_amd import kv4
+from int8_mixed_precision_amd import workloads as W
+from tests import gpu_harness as H
+from tests import layout as L
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-3, 2e-3
+
+
+def _fill_garbage(built):
+    built.cache.page_pool.fill_(0xFF)
+    if built.cache.side_pool is not None:
+        built.cache.side_pool.fill_(0xFF)
+
+
+def _compare_bytes(built, pages, side, layer, oc, S, R, seqs=None, n_of=None):
+    d, G, Hkv = 128, built.desc.group_size, built.desc.num_kv_heads
+    seqs = range(len(oc.seq_lens)) if seqs is None else seqs
+    for i, b in enumerate(seqs):
+        n = int(oc.seq_lens[i]) if n_of is None else int(n_of[i])
+        pm = L.protected_mask(n, S, R)
+        gm = L.gather_mixed(pages, side, layer=layer, num_pages=built.desc.num_pages, Hkv=Hkv,
+                            d=d, G=G, S=S, R=R, max_slots=built.desc.max_slots,
+                            block_tables=built.bt_host, slot=int(built.slots_host[b]), n=n,
+                            protected_mask=pm)
+        sl = oc.seq(i)
+        rows = slice(sl.start, sl.start + n)
+        for name in ("k4", "v4", "k4d", "k4m", "v4d", "v4m"):
+            want = getattr(oc, name)[rows]
+            got = gm[name]
+            if not np.array_equal(got, want):
+                bad = np.argwhere(got != want)[0]
+                raise AssertionError(f"seq {b} {name} mismatch at {tuple(bad)}: "
+                                     f"got {got[tuple(bad)]} want {want[tuple(bad)]}")
+        for name in ("k8", "v8", "k8s", "v8s"):
+            want = getattr(oc, name)[rows][pm]
+            got = gm[name][pm]
+            if not np.array_equal(got, want):
+                bad = np.argwhere(got != want)[0]
+                raise AssertionError(f"seq {b} {name} mismatch at protected row {tuple(bad)}")
+
+
+def _run_case(Hq, Hkv, G, S, R, ctx, seed, split=0, layers=1, layer=0, check_bytes=True,
+              garbage=True):
+    """Build a cache for contexts ctx (history + one step token), decode, and
+    compare with the oracle.  Returns (built, output, oracle cache)."""
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
+                   seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
+    n = np.asarray(ctx, np.int64) + 1
+    ks, vs = W.all_kv_sources(cfg, layer, n)
+    q = W.queries(cfg, layer)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, split=split, seed=seed)
+    if garbage:
+        _fill_garbage(built)
+    H.build_from_sources(built, layer, ks, vs, ctx)
+    out = H.decode(built, layer, q, n).cpu().numpy()
+    oc = oracle.MixedCache(ks, vs, G)
+    want = oracle.attend_mixed(q, oc, S, R, 1 / math.sqrt(128))
+    if check_bytes:
+        pages, side = H.pools_host(built)
+        _compare_bytes(built, pages, side, layer, oc, S, R)
+    H.check_output(out, want, ATOL, RTOL)
+    return built, out, oc, q, want
+
+
+def test_tiny_config():
+    c = W.CONFIGS["tiny"]
+    H.log("case tiny: B=2 8q/2kv ctx 300,512 G=32 S=4 R=64 seed 0")
+    ctx = W.contexts(c)
+    n = ctx + 1
+    ks, vs = W.all_kv_sources(c, 0, n)
+    q = W.queries(c, 0)
+    built = H.make_cache(c.q_heads, c.kv_heads, c.group, c.sink, c.recent, n, seed=c.seed)
+    _fill_garbage(built)
+    H.build_from_sources(built, 0, ks, vs, ctx)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    oc = oracle.MixedCache(ks, vs, c.group)
+    pages, side = H.pools_host(built)
+    _compare_bytes(built, pages, side, 0, oc, c.sink, c.recent)
+    want = oracle.attend_mixed(q, oc, c.sink, c.recent, 1 / math.sqrt(128))
+    err = H.check_output(out, want, ATOL, RTOL)
+    H.log(f"tiny: max abs {err[0]:.2e} rel {err[1]:.2e}")
+    # bf16 output is the fp32 result rounded to bf16
+    outb = H.decode(built, 0, q, n, out_dtype=kv4.KV4_OUT_BF16).float().cpu().numpy()
+    ref = torch.from_numpy(out).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(outb, ref)
+
+
+@pytest.mark.parametrize("G", [32, 128])
+@pytest.mark.parametrize("S", [0, 1, 4, 16])
+def test_edge_grid(G, S):
+    """n in [1, 40] x R in {0, 1, 3, 8, 64}: every case against the oracle."""
+    for R in (0, 1, 3, 8, 64):
+        H.log(f"case edge grid G={G} S={S} R={R} n=1..40")
+        ctx = np.arange(0, 40)
+        _run_case(8, 2, G, S, R, ctx, seed=S * 131 + R * 7 + G)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 2), (32, 8)])
+def test_gqa_ratios(Hq, Hkv):
+    H.log(f"case gqa Hq={Hq} Hkv={Hkv}")
+    _run_case(Hq, Hkv, 32, 4, 16, [0, 5, 19, 20, 21, 100, 257, 700], seed=Hq * 10 + Hkv)
+
+
+def test_group_64_and_multi_layer():
+    H.log("case G=64, 3 layers, layer 2")
+    _run_case(8, 2, 64, 4, 32, [33, 150, 401], seed=77, layers=3, layer=2)
+
+
+def test_split_invariance():
+    """Context splits merged by eq. A1 give the same output for any split size."""
+    ctx = [0, 3, 70, 300, 1000, 2500]
+    outs = {}
+    for split in (32, 64, 1024, 0, 8192):
+        H.log(f"case split={split}")
+        _, out, _, _, _ = _run_case(8, 2, 32, 4, 64, ctx, seed=5, split=split)
+        outs[split] = out
+    ref = outs[8192]          # one split covers every INT4 region here
+    for split, o in outs.items():
+        assert np.abs(o - ref).max() <= 1e-6, split
+
+
+def test_bulk_equals_token_by_token():
+    """Re-prefill path: a cache built in one bulk append equals the cache grown
+    one token per append (the quantization is per token)."""
+    Hq, Hkv, G, S, R = 8, 2, 32, 4, 16
+    n = np.array([1, 9, 40, 77])
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=9, batch=4, ctx_kind="fixed", ctx_fixed=tuple(n))
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    H.log("case bulk vs token-by-token")
+    a = H.make_cache(Hq, Hkv, G, S, R, n, seed=1, slot_perm=False)
+    b = H.make_cache(Hq, Hkv, G, S, R, n, seed=1, slot_perm=False)
+    _fill_garbage(a)
+    _fill_garbage(b)
+    H.append_chunks(a, 0, ks, vs, [0] * 4)
+    for t in range(int(n.max())):
+        seqs = [i for i in range(4) if n[i] > t]
+        H.append_chunks(b, 0, [ks[i][t:t + 1] for i in seqs], [vs[i][t:t + 1] for i in seqs],
+                        [t] * len(seqs), seqs)
+    pa, sa = H.pools_host(a)
+    pb, sb = H.pools_host(b)
+    assert np.array_equal(a.bt_host, b.bt_host) and np.array_equal(a.slots_host, b.slots_host)
+    for i in range(4):
+        kw = dict(layer=0, num_pages=a.desc.num_pages, Hkv=Hkv, d=128, G=G, S=S, R=R,
+                  max_slots=a.desc.max_slots, block_tables=a.bt_host, slot=int(a.slots_host[i]),
+                  n=int(n[i]), protected_mask=L.protected_mask(int(n[i]), S, R))
+        ga = L.gather_mixed(pa, sa, **kw)
+        gb = L.gather_mixed(pb, sb, **kw)
+        for k in ga:
+            assert np.array_equal(ga[k], gb[k]), (i, k)
+
+
+def test_decode_steps_cross_demotion_boundary():
+    """64 consecutive steps of (append, decode) starting at n = S+R-32, so the
+    cache goes from all-INT8 to mixed and positions are demoted every step;
+    INT4 bytes of a position never change after its append."""
+    Hq, Hkv, G, S, R = 8, 2, 32, 4, 64
+    steps = 64
+    start = S + R - 32
+    ctx0 = np.array([start, start + 5, start + 40, 300])
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=21, batch=4, ctx_kind="fixed", ctx_fixed=tuple(ctx0))
+    total = ctx0 + steps
+    ks, vs = W.all_kv_sources(cfg, 0, total)
+    built = H.make_cache(Hq, Hkv, G, S, R, total, seed=3)
+    _fill_garbage(built)
+    H.append_chunks(built, 0, [k[:c] for k, c in zip(ks, ctx0)], [v[:c] for v, c in zip(vs, ctx0)],
+                    [0] * 4)
+    oc = oracle.MixedCache(ks, vs, G)
+    first = None
+    for t in range(steps):
+        H.log(f"case demotion step {t}")
+        ctx = ctx0 + t
+        H.append_chunks(built, 0, [k[c:c + 1] for k, c in zip(ks, ctx)],
+                        [v[c:c + 1] for v, c in zip(vs, ctx)], list(ctx))
+        q = W.queries(cfg, 0, step=t)
+        out = H.decode(built, 0, q, ctx + 1).cpu().numpy()
+        want = oracle.attend_mixed(q, oc, S, R, 1 / math.sqrt(128), seq_lens=ctx + 1)
+        H.check_output(out, want, ATOL, RTOL)
+        if t in (0, 31, 63):
+            pages, side = H.pools_host(built)
+            _compare_bytes(built, pages, side, 0, oc, S, R, n_of=ctx + 1)
+            snap = pages.copy()
+            if first is None:
+                first = (snap, ctx + 1)
+            else:
+                # lifetime: INT4 bytes of positions present at step 0 are unchanged
+                n0 = first[1]
+                for i in range(4):
+                    kw = dict(layer=0, num_pages=built.desc.num_pages, Hkv=Hkv, d=128, G=G, S=S,
+                              R=R, max_slots=built.desc.max_slots, block_tables=built.bt_host,
+                              slot=int(built.slots_host[i]), n=int(n0[i]))
+                    g0 = L.gather_mixed(first[0], None, **kw)
+                    g1 = L.gather_mixed(snap, None, **kw)
+                    for k in ("k4", "v4", "k4d", "k4m", "v4d", "v4m"):
+                        assert np.array_equal(g0[k], g1[k]), (t, i, k)
+
+
+def test_bf16_comparator():
+    """BF16 kind: pages hold the bf16 values exactly; output matches the
+    oracle's dense attention."""
+    Hq, Hkv = 8, 2
+    ctx = np.array([0, 15, 16, 17, 300, 1000, 3000])
+    n = ctx + 1
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=31, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx))
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    q = W.queries(cfg, 0)
+    for split in (0, 64):
+        H.log(f"case bf16 comparator split={split}")
+        built = H.make_cache(Hq, Hkv, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, split=split, seed=4)
+        _fill_garbage(built)
+        H.build_from_sources(built, 0, ks, vs, ctx)
+        out = H.decode(built, 0, q, n).cpu().numpy()
+        pages, _ = H.pools_host(built)
+        for b in range(len(ctx)):
+            k, v = L.gather_bf16(pages, layer=0, num_pages=built.desc.num_pages, Hkv=Hkv, d=128,
+                                 block_tables=built.bt_host, slot=int(built.slots_host[b]), n=int(n[b]))
+            assert np.array_equal(k, ks[b]) and np.array_equal(v, vs[b])
+        want = oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128))
+        H.check_output(out, want, ATOL, RTOL)
