@@ -115,8 +115,8 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
     const int b = blockIdx.z, h = blockIdx.y, lane = threadIdx.x;
     int row0 = clampi(a.cu_new[b], 0, a.total_new);
     int row1 = clampi(a.cu_new[b + 1], row0, a.total_new);
-    int p0 = max(a.ctx_before[b], 0);
-    int cap = g.max_pages * kPage;
+    const int cap = g.max_pages * kPage;
+    int p0 = clampi(a.ctx_before[b], 0, cap);
     int p1 = min(p0 + (row1 - row0), cap);
     if (p1 <= p0) return;
     int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
@@ -194,8 +194,9 @@ __global__ __launch_bounds__(64) void append_bf16_kernel(AppendArgs a)
     const int b = blockIdx.z, h = blockIdx.y, lane = threadIdx.x;
     int row0 = clampi(a.cu_new[b], 0, a.total_new);
     int row1 = clampi(a.cu_new[b + 1], row0, a.total_new);
-    int p0 = max(a.ctx_before[b], 0);
-    int p1 = min(p0 + (row1 - row0), g.max_pages * kPage);
+    const int cap = g.max_pages * kPage;
+    int p0 = clampi(a.ctx_before[b], 0, cap);
+    int p1 = min(p0 + (row1 - row0), cap);
     int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
     const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
     for (int t = p0 + blockIdx.x; t < p1; t += gridDim.x) {
