@@ -66,8 +66,7 @@ __device__ __forceinline__ uint32_t int4_code(float x, double D, double M, uint1
 {
     if (db == 0) return 0u;
     double xv = (double)x;
-    int c = (int)rint((xv - M) / D);
-    c = clampi(c, 0, 15);
+    int c = (int)fmin(fmax(rint((xv - M) / D), 0.0), 15.0);
     if (c > 0) {
         double mid = M + ((double)c - 0.5) * D;
         if (xv < mid || (xv == mid && (c & 1))) c -= 1;
@@ -83,8 +82,7 @@ __device__ __forceinline__ int int8_code(float x, double S, uint16_t sb)
 {
     if (sb == 0) return 0;
     double a = fabs((double)x);
-    int c = (int)rint(a / S);
-    c = clampi(c, 0, 127);
+    int c = (int)fmin(fmax(rint(a / S), 0.0), 127.0);
     if (c > 0) {
         double mid = ((double)c - 0.5) * S;
         if (a < mid || (a == mid && (c & 1))) c -= 1;
