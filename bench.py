@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q8b256")
+    ap.add_argument("--split", type=int, default=0,
+                    help="context-split length in tokens (0 = the library's automatic choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -114,11 +116,11 @@ def main():
     log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
 
     kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                        seed=cfg.seed, device="cuda:0")
+                        seed=cfg.seed, split=args.split, device="cuda:0")
     caches = [("kv4", kv4c)]
     if not args.no_bf16:
         bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                           kind=kv4.KV4_KIND_BF16, device="cuda:0")
+                           kind=kv4.KV4_KIND_BF16, split=args.split, device="cuda:0")
         caches.append(("bf16", bfc))
     # build every cache from the same sources, sequence chunk by chunk
     step_k, step_v = [], []

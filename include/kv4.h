@@ -28,14 +28,16 @@
  *   page pool, KV4 kind: [layer][page][kv_head] blocks of
  *       K codes  16 tokens x head_dim/2 bytes, token-major; byte i of token t
  *                holds channel 2i in bits 0-3 and channel 2i+1 in bits 4-7;
- *       V codes  2 halves x head_dim 32-bit words; word (h, c) holds the codes
- *                of tokens 8h..8h+7 at channel c, token 8h+e in bits 4e..4e+3;
+ *       V codes  2 halves x head_dim 32-bit words; in half h, the word at index
+ *                64*(c/64) + 4*(c%16) + 2*((c/32)%2) + (c/16)%2 holds the codes of
+ *                tokens 8h..8h+7 at channel c, token 8h+e in bits 4e..4e+3;
  *       K delta  [group][16 tokens] binary16;   K offset [group][16] binary16;
  *       V delta  [group][16 tokens] binary16;   V offset [group][16] binary16;
  *     i.e. 16 * (head_dim + 8 * head_dim / group_size) bytes per PB
  *     (2,560 B at head_dim 128, group 32: 160 B per token and kv head).
  *   page pool, BF16 kind: [layer][page][kv_head] blocks of K [16][head_dim]
- *     bf16 then V [16][head_dim] bf16 (8,192 B at head_dim 128).
+ *     bf16 (token-major) then V [2 halves][head_dim][8 tokens] bf16 -- value
+ *     (t, c) at ((t/8)*head_dim + c)*8 + t%8 (8,192 B at head_dim 128).
  *   side pool (KV4 kind only): [layer][slot][kv_head] blocks of
  *       K codes [S+R][head_dim] int8, V codes [S+R][head_dim] int8,
  *       K scale [S+R] binary16, V scale [S+R] binary16, padded to 16 bytes.

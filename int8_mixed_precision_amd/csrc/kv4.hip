@@ -11,6 +11,7 @@
 #include "kv4_append.hpp"
 #include "kv4_common.hpp"
 #include "kv4_decode.hpp"
+#include "kv4_decode_mfma.hpp"
 
 struct kv4_cache {
     kv4_cache_desc desc;
@@ -80,9 +81,9 @@ void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split,
         T = 256;
         while (T < 4096 && T < t) T *= 2;
     }
-    int len = g.kind == KV4_KIND_MIXED ? max(max_ctx - g.S, 0) : max_ctx;
+    // split k covers absolute positions [k*T, (k+1)*T) of the INT4 region
     *split = T;
-    *nsplit = max((len + T - 1) / T, 1);
+    *nsplit = max((max_ctx + T - 1) / T, 1);
 }
 
 size_t workspace_bytes(const kv4::Geo& g, int batch, int nsplit)
@@ -96,14 +97,38 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
+// Vector-ALU kernels, used for GQA group sizes other than 4.
 template <int GQA>
-void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
+void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
     dim3 grid(a.nsplit + (a.g.kind == KV4_KIND_MIXED ? 1 : 0), a.g.Hkv, a.batch);
     if (a.g.kind == KV4_KIND_MIXED)
         hipLaunchKernelGGL(kv4::decode_split_kv4_kernel<GQA>, grid, dim3(64), 0, s, a);
     else
         hipLaunchKernelGGL(kv4::decode_split_bf16_kernel<GQA>, grid, dim3(64), 0, s, a);
+}
+
+// Work items of one decode launch (INT4 splits + protected parts).
+int64_t decode_items(const kv4::Geo& g, int batch, int nsplit)
+{
+    return (int64_t)(nsplit + (g.kind == KV4_KIND_MIXED ? 1 : 0)) * batch * g.Hkv;
+}
+
+void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
+{
+    if (a.g.gqa == 4) {
+        dim3 grid((unsigned)decode_items(a.g, a.batch, a.nsplit));
+        if (a.g.kind == KV4_KIND_MIXED)
+            hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel, grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL(kv4::decode_bf16_mfma_kernel, grid, dim3(64), 0, s, a);
+        return;
+    }
+    switch (a.g.gqa) {
+        case 1: launch_decode_valu<1>(a, s); break;
+        case 2: launch_decode_valu<2>(a, s); break;
+        default: launch_decode_valu<8>(a, s); break;
+    }
 }
 
 }  // namespace
@@ -232,6 +257,7 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
         return KV4_ERR_INVALID_ARG;
     int T, ns;
     split_plan(cache, batch, max_ctx, num_cus(cache), &T, &ns);
+    if (decode_items(g, batch, ns) > INT32_MAX) return KV4_ERR_CAPACITY;
     size_t need = workspace_bytes(g, batch, ns);
     if (workspace == nullptr || workspace_bytes_ < need) return KV4_ERR_WORKSPACE;
     kv4::DecodeArgs a;
@@ -252,12 +278,7 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
     a.out = out;
     a.out_dtype = out_dtype;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (g.gqa) {
-        case 1: launch_decode<1>(a, s); break;
-        case 2: launch_decode<2>(a, s); break;
-        case 4: launch_decode<4>(a, s); break;
-        default: launch_decode<8>(a, s); break;
-    }
+    launch_decode(a, s);
     int st = launch_status();
     if (st != KV4_OK) return st;
     int rows = batch * g.Hq;

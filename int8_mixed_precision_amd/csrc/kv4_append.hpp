@@ -131,7 +131,8 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
         int page = clampi(bt[hp / 2], 0, g.num_pages - 1);
         uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
         uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hp & 1) * g.d;
-        uint32_t w0 = vw[2 * lane], w1 = vw[2 * lane + 1];
+        const int q0 = vpos(2 * lane), q1 = vpos(2 * lane + 1);
+        uint32_t w0 = vw[q0], w1 = vw[q1];
         for (int t = t_lo; t < t_hi; ++t) {
             int64_t src = ((int64_t)(row0 + (t - p0)) * g.Hkv + h) * g.d;
             uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
@@ -179,8 +180,8 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
                 }
             }
         }
-        vw[2 * lane] = w0;
-        vw[2 * lane + 1] = w1;
+        vw[q0] = w0;
+        vw[q1] = w1;
     }
 }
 
@@ -205,7 +206,10 @@ __global__ __launch_bounds__(64) void append_bf16_kernel(AppendArgs a)
         uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
         uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
         reinterpret_cast<uint32_t*>(pb)[tp * (g.d / 2) + lane] = kk;
-        reinterpret_cast<uint32_t*>(pb + (int64_t)kPage * g.d * 2)[tp * (g.d / 2) + lane] = vv;
+        // V element (t, c) at [(t%16)/8][c][t%8]: 8 tokens of a channel are contiguous
+        uint16_t* vb = reinterpret_cast<uint16_t*>(pb + (int64_t)kPage * g.d * 2) + (tp / kHalf) * g.d * kHalf;
+        vb[(2 * lane) * kHalf + tp % kHalf] = (uint16_t)(vv & 0xFFFFu);
+        vb[(2 * lane + 1) * kHalf + tp % kHalf] = (uint16_t)(vv >> 16);
     }
 }
 

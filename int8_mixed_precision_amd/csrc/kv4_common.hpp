@@ -75,6 +75,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
 }
 
+// Index of channel c's code word inside one 8-token half of a page's V code
+// block (d = 128): the four words a lane loads with one 16-byte access belong
+// to four 16-channel column blocks of the PV product, and each column block
+// lies inside one 32-channel group.
+__host__ __device__ __forceinline__ int vpos(int c)
+{
+    return 64 * (c >> 6) + 4 * (c & 15) + 2 * ((c >> 5) & 1) + ((c >> 4) & 1);
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

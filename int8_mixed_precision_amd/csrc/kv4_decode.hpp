@@ -144,14 +144,14 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h, float 
 }
 
 // ---------------------------------------------------------------------------
-// Mixed cache: INT4 splits and the protected part.  Grid (nsplit+1, Hkv, batch),
-// one wave per work item; item nsplit is the protected part.
+// Mixed cache, vector-ALU path: one wave per work item (sequence b, kv head h,
+// item); items < nsplit are INT4 context splits, item nsplit is the protected
+// (sink + recent) part read from the INT8 ring.
 // ---------------------------------------------------------------------------
 template <int GQA>
-__global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
+__device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h, int item)
 {
     const Geo& g = a.g;
-    const int b = blockIdx.z, h = blockIdx.y, item = blockIdx.x;
     const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
     const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
     const Regions rg = regions_of(n, g.S, g.R);
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
     if (prot) {
         t_end = rg.n8;
     } else {
-        t_begin = g.S + item * a.split;
-        t_end = min(t_begin + a.split, rg.rec_start);
+        t_begin = max(item * a.split, g.S);
+        t_end = min((item + 1) * a.split, rg.rec_start);
     }
     if (t_end <= t_begin) return;
 
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
             __syncthreads();
             // ---- values
             const uint32_t* vw = reinterpret_cast<const uint32_t*>(pb + g.off_vc) + half * g.d;
-            uint32_t w0 = vw[2 * lane], w1 = vw[2 * lane + 1];
+            uint32_t w0 = vw[vpos(2 * lane)], w1 = vw[vpos(2 * lane + 1)];
             uint4 dv = *reinterpret_cast<const uint4*>(pb + g.off_vd + 2 * (gv * kPage + half * kHalf));
             uint4 mv = *reinterpret_cast<const uint4*>(pb + g.off_vm + 2 * (gv * kPage + half * kHalf));
             uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w}, mvw[4] = {mv.x, mv.y, mv.z, mv.w};
@@ -278,18 +278,24 @@ __global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
     write_partial<GQA>(a, st, b, h, item);
 }
 
+// Grid (nsplit+1, Hkv, batch).
+template <int GQA>
+__global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
+{
+    valu_item_kv4<GQA>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
-// BF16 comparator: the same split structure over bf16 pages (no protection).
+// BF16 comparator, vector-ALU path: the same split structure over bf16 pages.
 // ---------------------------------------------------------------------------
 template <int GQA>
-__global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
+__device__ __forceinline__ void valu_item_bf16(const DecodeArgs& a, int b, int h, int item)
 {
     const Geo& g = a.g;
-    const int b = blockIdx.z, h = blockIdx.y, item = blockIdx.x;
     const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
     const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
     const int t_begin = item * a.split;
-    const int t_end = min(t_begin + a.split, n);
+    const int t_end = min((item + 1) * a.split, n);
     if (t_end <= t_begin) return;
     const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
     const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
@@ -324,13 +330,17 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < GQA; ++j) { st.o[j][0] *= alpha[j]; st.o[j][1] *= alpha[j]; }
-        const uint32_t* vr = reinterpret_cast<const uint32_t*>(pb + (int64_t)kPage * g.d * 2);
+        const uint16_t* vr = reinterpret_cast<const uint16_t*>(pb + (int64_t)kPage * g.d * 2) +
+                             (hp & 1) * g.d * kHalf;
+        uint4 va = *reinterpret_cast<const uint4*>(vr + (2 * lane) * kHalf);
+        uint4 vb = *reinterpret_cast<const uint4*>(vr + (2 * lane + 1) * kHalf);
+        uint32_t vaw[4] = {va.x, va.y, va.z, va.w}, vbw[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
         for (int ee = 0; ee < kHalf; ++ee) {
             int t2 = hp * kHalf + ee;
             if (t2 < t_begin || t2 >= t_end) continue;
-            uint32_t vv = vr[(t2 % kPage) * (g.d / 2) + lane];
-            float x0 = bf16_lo(vv), x1 = bf16_hi(vv);
+            float x0 = (ee & 1) ? bf16_hi(vaw[ee >> 1]) : bf16_lo(vaw[ee >> 1]);
+            float x1 = (ee & 1) ? bf16_hi(vbw[ee >> 1]) : bf16_lo(vbw[ee >> 1]);
 #pragma unroll
             for (int j = 0; j < GQA; ++j) {
                 float p = P[ee][j];
@@ -341,6 +351,13 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
         __syncthreads();
     }
     write_partial<GQA>(a, st, b, h, item);
+}
+
+// Grid (nsplit, Hkv, batch).
+template <int GQA>
+__global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
+{
+    valu_item_bf16<GQA>(a, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -354,23 +371,25 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
     if (row >= a.batch * g.Hq) return;
     const int b = row / g.Hq, j = row % g.Hq, h = j / g.gqa, jj = j % g.gqa;
     const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
-    int nparts4, has8;
+    int k_lo, k_hi, has8;
     if (g.kind == KV4_KIND_MIXED) {
         Regions rg = regions_of(n, g.S, g.R);
-        nparts4 = (rg.n4 + a.split - 1) / a.split;
+        k_lo = g.S / a.split;
+        k_hi = rg.n4 > 0 ? (rg.rec_start + a.split - 1) / a.split : k_lo;
         has8 = rg.n8 > 0;
     } else {
-        nparts4 = (n + a.split - 1) / a.split;
+        k_lo = 0;
+        k_hi = (n + a.split - 1) / a.split;
         has8 = 0;
     }
-    nparts4 = min(nparts4, a.nsplit);
+    k_hi = min(k_hi, a.nsplit);
     float zmax = -INFINITY;
-    for (int i = 0; i < nparts4; ++i) zmax = fmaxf(zmax, part_ptr(a, b, h, i, jj)[g.d]);
+    for (int i = k_lo; i < k_hi; ++i) zmax = fmaxf(zmax, part_ptr(a, b, h, i, jj)[g.d]);
     if (has8) zmax = fmaxf(zmax, part_ptr(a, b, h, a.nsplit, jj)[g.d]);
     float W = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int i = 0; i <= nparts4; ++i) {
-        int item = i < nparts4 ? i : a.nsplit;
-        if (i == nparts4 && !has8) break;
+    for (int i = k_lo; i <= k_hi; ++i) {
+        int item = i < k_hi ? i : a.nsplit;
+        if (i == k_hi && !has8) break;
         const float* src = part_ptr(a, b, h, item, jj);
         float w = exp2f(src[g.d] - zmax);
         float2 v = *reinterpret_cast<const float2*>(src + 2 * lane);

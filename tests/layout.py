@@ -45,9 +45,12 @@ def gather_mixed(pages: np.ndarray, side, *, layer, num_pages, Hkv, d, G, S, R, 
     k4 = np.empty((n, Hkv, d), dtype=np.uint8)
     k4[:, :, 0::2] = kb & 0xF
     k4[:, :, 1::2] = kb >> 4
-    # V codes: word (half, c) at offset 16*d/2 + 4*(half*d + c), token 8*half+e in bits 4e..
+    # V codes: half h's word for channel c at index 64(c/64) + 4(c%16) + 2((c/32)%2) + (c/16)%2,
+    # token 8h+e in bits 4e..4e+3
     voff = PAGE * d // 2
-    widx = base[:, :, None] + voff + 4 * ((tp[:, None, None] // 8) * d + np.arange(d)[None, None, :])
+    c = np.arange(d)
+    vpos = 64 * (c // 64) + 4 * (c % 16) + 2 * ((c // 32) % 2) + (c // 16) % 2
+    widx = base[:, :, None] + voff + 4 * ((tp[:, None, None] // 8) * d + vpos[None, None, :])
     words = (pages[widx].astype(np.uint32) | (pages[widx + 1].astype(np.uint32) << 8) |
              (pages[widx + 2].astype(np.uint32) << 16) | (pages[widx + 3].astype(np.uint32) << 24))
     v4 = ((words >> (4 * (tp[:, None, None] % 8)).astype(np.uint32)) & 0xF).astype(np.uint8)
@@ -97,8 +100,10 @@ def gather_bf16(pages: np.ndarray, *, layer, num_pages, Hkv, d, block_tables, sl
     tp = p % PAGE
     h = np.arange(Hkv, dtype=np.int64)
     base = ((layer * num_pages + page[:, None]) * Hkv + h[None, :]) * PB
-    idx = base[:, :, None] + 2 * (tp[:, None, None] * d + np.arange(d)[None, None, :])
+    c = np.arange(d)[None, None, :]
+    idx = base[:, :, None] + 2 * (tp[:, None, None] * d + c)
     k = (pages[idx].astype(np.uint32) | (pages[idx + 1].astype(np.uint32) << 8)) << 16
-    vi = idx + PAGE * d * 2
+    # V value (t, c) at ((t/8)*d + c)*8 + t%8 after the K block
+    vi = base[:, :, None] + PAGE * d * 2 + 2 * (((tp[:, None, None] // 8) * d + c) * 8 + tp[:, None, None] % 8)
     v = (pages[vi].astype(np.uint32) | (pages[vi + 1].astype(np.uint32) << 8)) << 16
     return k.view(np.float32), v.view(np.float32)

@@ -160,13 +160,13 @@ def test_append_and_decode_validation_no_launch():
 def test_split_plan_and_workspace():
     h, d, _, _ = _fake_handle(split_tokens=64, max_pages_per_seq=64)
     T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
-    assert T == 64 and ns == -(-(1024 - 4) // 64)
+    assert T == 64 and ns == 1024 // 64
     ws = kv4.kv4_decode_workspace_bytes(h, 3, 1024)
     assert ws == 3 * 2 * (ns + 1) * 4 * (128 + 4) * 4
     kv4.kv4_cache_free(h)
     h, d, _, _ = _fake_handle(max_pages_per_seq=64)
     T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
-    assert T % 32 == 0 and 256 <= T <= 4096 and ns * T >= 1024 - 4
+    assert T % 32 == 0 and 256 <= T <= 4096 and ns * T >= 1024
     kv4.kv4_cache_free(h)
 
 

@@ -79,7 +79,8 @@ def _run_case(Hq, Hkv, G, S, R, ctx, seed, split=0, layers=1, layer=0, check_byt
     if check_bytes:
         pages, side = H.pools_host(built)
         _compare_bytes(built, pages, side, layer, oc, S, R)
-    H.check_output(out, want, ATOL, RTOL)
+    err = H.check_output(out, want, ATOL, RTOL)
+    H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
     return built, out, oc, q, want
 
 
@@ -127,6 +128,15 @@ def test_group_64_and_multi_layer():
     _run_case(8, 2, 64, 4, 32, [33, 150, 401], seed=77, layers=3, layer=2)
 
 
+# Self-agreement bound across split sizes.  The merge (eq. A1) is exact up to
+# rounding; what changes with the split is the fp32 rounding order.  The PV
+# accumulator sums w*(16 + c) (the +16 comes from widening 4-bit codes to bf16
+# exactly) over up to n/32 tile additions, so one path deviates from the exact
+# value by about sqrt(n/32) * 2^-24 * 31 * max(Delta_V) <= ~1e-5 at n = 2,500,
+# plus 2^-18 relative rounding of the bf16 hi+lo operand.  Two paths: 5e-5.
+SPLIT_SELF_TOL = 5e-5
+
+
 def test_split_invariance():
     """Context splits merged by eq. A1 give the same output for any split size."""
     ctx = [0, 3, 70, 300, 1000, 2500]
@@ -137,7 +147,7 @@ def test_split_invariance():
         outs[split] = out
     ref = outs[8192]          # one split covers every INT4 region here
     for split, o in outs.items():
-        assert np.abs(o - ref).max() <= 1e-6, split
+        assert np.abs(o - ref).max() <= SPLIT_SELF_TOL, (split, float(np.abs(o - ref).max()))
 
 
 def test_bulk_equals_token_by_token():
