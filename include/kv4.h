@@ -92,7 +92,8 @@ typedef struct kv4_cache_desc {
     int32_t kind;               /* KV4_KIND_MIXED or KV4_KIND_BF16 */
     int32_t flags;              /* KV4_FLAG_* */
     int32_t split_tokens;       /* context-split length for decode; 0 = automatic,
-                                   else a positive multiple of 32 */
+                                   else a positive multiple of 32 (values above
+                                   2048 act as 2048) */
 } kv4_cache_desc;
 
 typedef struct kv4_cache kv4_cache;  /* opaque host-side handle */

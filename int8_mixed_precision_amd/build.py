@@ -23,6 +23,9 @@ HIPFLAGS = [
     "-shared",
     # packed fp32 instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the decode loops then need no
+    # accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),

@@ -67,19 +67,18 @@ int num_cus(kv4_cache* c)
     return c->num_cus > 0 ? c->num_cus : 256;
 }
 
-// Context-split length: explicit, or chosen so that a batch whose sequences
-// all reached max_ctx would give about 8 work items per compute unit, within
-// [256, 4096] tokens.
+// Context-split length: explicit (capped at kMaxSplit), or chosen so that a
+// batch whose sequences all reached max_ctx would give about 8 work items per
+// compute unit, within [256, kMaxSplit] tokens.
 void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split, int* nsplit)
 {
-    const kv4::Geo& g = c->geo;
-    int T = c->desc.split_tokens;
+    int T = std::min(c->desc.split_tokens, kv4::kMaxSplit);
     if (T == 0) {
-        double work = (double)batch * g.Hkv * (double)max_ctx;
+        double work = (double)batch * c->geo.Hkv * (double)max_ctx;
         double target = 8.0 * cus;
         double t = work / target;
         T = 256;
-        while (T < 4096 && T < t) T *= 2;
+        while (T < kv4::kMaxSplit && T < t) T *= 2;
     }
     // split k covers absolute positions [k*T, (k+1)*T) of the INT4 region
     *split = T;

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/kv4.h"
+#include "kv4.h"
 
 namespace kv4 {
 

@@ -20,6 +20,7 @@
 namespace kv4 {
 
 constexpr int kPartPad = 4;      // floats after o[d] in a partial: z and padding
+constexpr int kMaxSplit = 2048;  // longest context split (tokens) a work item covers
 
 struct DecodeArgs {
     Geo g;

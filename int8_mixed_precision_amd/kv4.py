@@ -46,10 +46,10 @@ class KV4Error(RuntimeError):
         super().__init__(f"{where}: {kv4_status_string(code)} (code {code})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m int8_mixed_precision_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m int8_mixed_precision_amd.build`")
+    L = ctypes.CDLL(path)
     P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     pdesc = ctypes.POINTER(kv4_cache_desc)
     psz = ctypes.POINTER(sz)
