@@ -44,7 +44,16 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_kv4_mfma_kernel_qwen3-8b_b256_traffic.json"))
+    # summaries of rocprofv3 output (no GPU work): kernel durations from a
+    # --kernel-trace csv directory; HBM traffic from a FETCH_SIZE and a
+    # WRITE_SIZE --pmc csv directory of runs made with --copy-calibration
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summary-out", metavar="FILE")
+    ap.add_argument("--summary-cmd", default="", help="command that produced the profile")
+    ap.add_argument("--summary-bench", metavar="JSON",
+                    help="bench line printed by the profiled run (live event timings)")
     return ap.parse_args()
 
 
@@ -60,18 +69,25 @@ def region_counts(n, S, R):
     return n4, n8
 
 
-def decode_bytes_kv4(n, cfg):
-    """Algorithmic bytes of one kv4_decode_attn call: payload + metadata of both
-    regions, q, fp32 output, block-table entries of the INT4 pages."""
+def partial_bytes_kv4(n, cfg):
+    """Algorithmic bytes of the attention phase (kv4_decode_partials, one
+    kernel): payload + metadata of both regions, q, block-table entries of the
+    INT4 pages.  160 B per (INT4 token, kv head) and 260 B per (protected
+    token, kv head) at d = 128, G = 32."""
     n4, n8 = region_counts(n, cfg.sink, cfg.recent)
     ng = cfg.head_dim // cfg.group
     per4 = cfg.head_dim + 2 * 2 * 2 * ng            # K+V codes (d/2 each) + K,V (Delta, m) fp16
     per8 = 2 * cfg.head_dim + 2 * 2                 # K+V int8 + two fp16 scales
     kv = int(np.sum(cfg.kv_heads * (per4 * n4 + per8 * n8)))
     qb = len(n) * cfg.q_heads * cfg.head_dim * 2
-    ob = len(n) * cfg.q_heads * cfg.head_dim * 4
     bt = int(np.sum(4 * np.ceil(n4 / 16)))
-    return kv + qb + ob + bt
+    return kv + qb + bt
+
+
+def decode_bytes_kv4(n, cfg):
+    """Algorithmic bytes of one kv4_decode_attn call: the attention phase's
+    plus the fp32 output."""
+    return partial_bytes_kv4(n, cfg) + len(n) * cfg.q_heads * cfg.head_dim * 4
 
 
 def decode_bytes_bf16(n, cfg):
@@ -93,8 +109,96 @@ def append_bytes_bf16(n, cfg):
     return len(n) * cfg.kv_heads * cfg.head_dim * 2 * 2 * 2
 
 
+DOMINANT = "decode_kv4_mfma_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("kv4::", "")
+
+
+def summarize_trace(args):
+    """Per-kernel launch count and duration statistics from a kernel trace."""
+    rows = _csv_rows(args.summarize_trace, "kernel_trace.csv")
+    per = {}
+    for r in rows:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        per.setdefault(_short(r["Kernel_Name"]), []).append(dur)
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# rocprofv3 kernel trace summary: {args.summary_cmd}", "",
+             f"{'kernel':44s} {'calls':>6s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} "
+             f"{'max_us':>10s} {'total_%':>8s}"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        a = np.array(v) / 1e3
+        k = k if len(k) <= 44 else k[:41] + "..."
+        lines.append(f"{k:44s} {len(v):6d} {a.mean():10.2f} {np.median(a):10.2f} {a.min():10.2f} "
+                     f"{a.max():10.2f} {100 * a.sum() * 1e3 / total:8.2f}")
+    if args.summary_bench:
+        b = json.loads(open(args.summary_bench).read().strip().splitlines()[-1])
+        lines += ["", "live HIP-event timings of the same run (mean over the timed steps):",
+                  f"  kv4_decode_partials ({DOMINANT}): {b['decode_partials_us']} us",
+                  f"  kv4_decode_merge (merge_parts_kernel, incl. launch gap): {b['decode_merge_us']} us",
+                  f"  kv4_append (append_kv4_kernel<32>): {b['append_us']} us"]
+        if "bf16_comparator" in b:
+            lines.append(f"  BF16 comparator partials (decode_bf16_mfma_kernel): "
+                         f"{b['bf16_comparator']['decode_partials_us']} us")
+        lines.append("kernel counts include warm-up steps, the cache build's bulk appends and one "
+                     "kv4_decode_attn check call")
+    text = "\n".join(lines) + "\n"
+    if args.summary_out:
+        open(args.summary_out, "w").write(text)
+    print(text)
+
+
+def summarize_pmc(args):
+    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    1 GiB device-to-device copies that --copy-calibration issues."""
+    out = {}
+    for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_pmc):
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        dom = [float(r["Counter_Value"]) for r in rows if DOMINANT in r["Kernel_Name"]]
+        last_dom = max(int(r["Dispatch_Id"]) for r in rows if DOMINANT in r["Kernel_Name"])
+        # the calibration copies are the device copies issued after every decode
+        cal = [float(r["Counter_Value"]) for r in rows
+               if r["Kernel_Name"].startswith(COPY_KERNEL) and int(r["Dispatch_Id"]) > last_dom]
+        cal = [c for c in cal if cal and c >= 0.5 * max(cal)]     # the 1 GiB copies only
+        if not dom or not cal:
+            raise SystemExit(f"{counter}: {len(dom)} decode dispatches, {len(cal)} copy dispatches")
+        scale = COPY_BYTES / (np.median(cal) * 1024.0)
+        out[counter] = dict(kib_per_launch=float(np.mean(dom)), launches=len(dom),
+                            kib_spread=[float(np.min(dom)), float(np.max(dom))],
+                            copy_kib=float(np.median(cal)), copy_launches=len(cal), scale=scale,
+                            bytes_per_launch=float(np.mean(dom)) * 1024.0 * scale)
+    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    total = fetch["bytes_per_launch"] + write["bytes_per_launch"]
+    res = dict(kernel=DOMINANT, kernel_source_hash=_kernel_hash(), command=args.summary_cmd,
+               fetch=fetch, write=write, bytes_per_launch=int(round(total)))
+    if args.summary_out:
+        json.dump(res, open(args.summary_out, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the decode step shards by sequence or kv head with no "
@@ -146,6 +250,7 @@ def main():
     sm = 1.0 / math.sqrt(cfg.head_dim)
     log(f"caches built in {time.time() - t0:.1f}s")
 
+    # every launch goes to torch's current stream, which the events record on
     stream = torch.cuda.current_stream()
     results = {}
     for name, c in caches:
@@ -157,35 +262,51 @@ def main():
             kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B,
                            B, stream)
 
-        def decode():
-            kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx,
-                                sm, out, kv4.KV4_OUT_F32, ws, stream)
+        def partials():
+            kv4.kv4_decode_partials(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B,
+                                    max_ctx, sm, ws, stream)
+
+        def merge():
+            kv4.kv4_decode_merge(c.cache.handle, n_d, B, max_ctx, out, kv4.KV4_OUT_F32, ws, stream)
 
         for _ in range(args.warmup):
             append()
-            decode()
+            partials()
+            merge()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for i in range(args.steps):
             ev[i][0].record(stream)
             append()
             ev[i][1].record(stream)
-            decode()
+            partials()
             ev[i][2].record(stream)
+            merge()
+            ev[i][3].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        ta = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
-        td = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+        t = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)]
+                      for i in range(args.steps)])
+        ta, tp, tm = t[:, 0], t[:, 1], t[:, 2]
+        td = tp + tm
         assert torch.isfinite(out).all()
-        results[name] = dict(append_ms=float(ta.mean()), decode_ms=float(td.mean()),
+        # the two phases are kv4_decode_attn exactly
+        whole = torch.empty_like(out)
+        kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm,
+                            whole, kv4.KV4_OUT_F32, ws, stream)
+        torch.cuda.synchronize()
+        assert torch.equal(whole, out), "kv4_decode_attn differs from partials + merge"
+        results[name] = dict(append_ms=float(ta.mean()), partials_ms=float(tp.mean()),
+                             merge_ms=float(tm.mean()), decode_ms=float(td.mean()),
                              decode_ms_median=float(np.median(td)),
                              decode_ms_p10=float(np.percentile(td, 10)),
                              decode_ms_p90=float(np.percentile(td, 90)),
                              wall_ms_per_step=wall * 1e3 / args.steps,
                              split_tokens=split_T, nsplit=nsplit)
-        log(f"{name}: append {ta.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
+        log(f"{name}: append {ta.mean() * 1e3:.1f} us, partials {tp.mean() * 1e3:.1f} us, "
+            f"merge {tm.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
             f"(median {np.median(td) * 1e3:.1f}), split {split_T}")
 
     if args.copy_calibration:
@@ -198,10 +319,12 @@ def main():
 
     r = results["kv4"]
     db = decode_bytes_kv4(n, cfg)
+    pb = partial_bytes_kv4(n, cfg)
     ab = append_bytes_kv4(n, cfg)
     step_ms = r["append_ms"] + r["decode_ms"]
     value = (db + ab) / (step_ms * 1e-3) / 1e9
-    achieved = db / (r["decode_ms"] * 1e-3) / 1e9
+    decode_gbs = db / (r["decode_ms"] * 1e-3) / 1e9
+    achieved = pb / (r["partials_ms"] * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -231,25 +354,31 @@ def main():
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
             "split_tokens": r["split_tokens"],
         },
-        "decode_attn_gbs": round(achieved, 2),
-        "decode_attn_pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "decode_attn_gbs": round(decode_gbs, 2),
+        "decode_attn_pct_hbm_peak": round(100 * decode_gbs / HBM_PEAK_GBS, 2),
         "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
+        "decode_partials_us": round(r["partials_ms"] * 1e3, 2),
+        "decode_merge_us": round(r["merge_ms"] * 1e3, 2),
         "decode_attn_us_median_p10_p90": [round(r["decode_ms_median"] * 1e3, 2),
                                           round(r["decode_ms_p10"] * 1e3, 2),
                                           round(r["decode_ms_p90"] * 1e3, 2)],
         "append_us": round(r["append_ms"] * 1e3, 2),
         "decode_alg_bytes": db,
+        "partials_alg_bytes": pb,
         "append_alg_bytes": ab,
         "layer_tokens_per_s": round(B / (step_ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "kv4_decode_attn (decode_split_kv4 + merge_parts)",
+        "roofline": {"bound": "hbm", "kernel": "decode_kv4_mfma_kernel (kv4_decode_partials)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": pb,
+                     "launch_us": round(r["partials_ms"] * 1e3, 2)},
     }
     if "bf16" in results:
         rb = results["bf16"]
         bstep = rb["append_ms"] + rb["decode_ms"]
         line["bf16_comparator"] = {
             "decode_attn_us": round(rb["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(rb["partials_ms"] * 1e3, 2),
             "append_us": round(rb["append_ms"] * 1e3, 2),
             "decode_attn_gbs": round(decode_bytes_bf16(n, cfg) / (rb["decode_ms"] * 1e-3) / 1e9, 2),
             "layer_tokens_per_s": round(B / (bstep * 1e-3), 1),

@@ -186,6 +186,39 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
                     int max_ctx, float sm_scale, void* out, int out_dtype, void* workspace,
                     size_t workspace_bytes, kv4_stream_t stream);
 
+/*
+ * The two phases of kv4_decode_attn, with the same arguments and results:
+ * kv4_decode_attn is exactly kv4_decode_partials followed by kv4_decode_merge
+ * on one stream.  They are separate entry points for callers that time the
+ * attention and the merge apart, or that merge parts computed elsewhere (a
+ * context split over several devices yields parts of one (sequence, head)
+ * that combine by the same eq. A1 of KV4-RL Appendix A.3).
+ *
+ * kv4_decode_partials runs every work item of the step: the INT4 region of
+ * each (sequence b, kv head h) in context splits of T tokens, and the
+ * protected region as one more part.  It writes the workspace as float32
+ *     part[b][h][k][j][d + 4],  k in [0, nsplit],  j in [0, Hq/Hkv)
+ * (T, nsplit from kv4_decode_split_info): part k < nsplit covers absolute
+ * positions [kT, (k+1)T) of the INT4 region and part nsplit the protected
+ * region.  Floats [0, d) hold the part's softmax-normalised output of q head
+ * h*(Hq/Hkv)+j and float d its base-2 log-normaliser z = max + log2(sum) of
+ * the scores scaled by sm_scale*log2(e).  Parts with no positions are not
+ * written.
+ *
+ * kv4_decode_merge combines, per (b, q head), the non-empty parts of that
+ * workspace into out with weights 2^(z_k - max z) (zero for empty parts); its
+ * batch, max_ctx and seq_lens must be those of the kv4_decode_partials call
+ * that wrote the workspace.
+ * Errors: as kv4_decode_attn.
+ */
+int kv4_decode_partials(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                        const int32_t* slot_ids, const int32_t* block_tables, int batch,
+                        int max_ctx, float sm_scale, void* workspace, size_t workspace_bytes,
+                        kv4_stream_t stream);
+int kv4_decode_merge(kv4_cache* cache, const int32_t* seq_lens, int batch, int max_ctx,
+                     void* out, int out_dtype, const void* workspace, size_t workspace_bytes,
+                     kv4_stream_t stream);
+
 /* Free the host handle (the pools stay with the caller). NULL is accepted. */
 int kv4_cache_free(kv4_cache* cache);
 

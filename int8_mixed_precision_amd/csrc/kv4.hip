@@ -130,6 +130,51 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     }
 }
 
+// Validation and argument set-up shared by the decode phases.  `need_q` is
+// false for the merge, which reads only seq_lens and the workspace.
+int decode_args(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                const int32_t* slot_ids, const int32_t* block_tables, int batch, int max_ctx,
+                float sm_scale, const void* workspace, size_t ws_bytes, bool need_q,
+                kv4::DecodeArgs& a)
+{
+    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
+    const kv4::Geo& g = cache->geo;
+    if (need_q && (layer < 0 || layer >= g.num_layers)) return KV4_ERR_CAPACITY;
+    if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
+    if (!std::isfinite(sm_scale)) return KV4_ERR_INVALID_ARG;
+    if (batch > 0 && (seq_lens == nullptr ||
+                      (need_q && (q_bf16 == nullptr || slot_ids == nullptr || block_tables == nullptr))))
+        return KV4_ERR_INVALID_ARG;
+    int T, ns;
+    split_plan(cache, batch, max_ctx, num_cus(cache), &T, &ns);
+    if (decode_items(g, batch, ns) > INT32_MAX) return KV4_ERR_CAPACITY;
+    if (batch > 0 && (workspace == nullptr || ws_bytes < workspace_bytes(g, batch, ns)))
+        return KV4_ERR_WORKSPACE;
+    a.g = g;
+    a.layer = layer;
+    a.q = static_cast<const uint16_t*>(q_bf16);
+    a.seq_lens = seq_lens;
+    a.slot_ids = slot_ids;
+    a.block_tables = block_tables;
+    a.batch = batch;
+    a.max_ctx = max_ctx;
+    a.split = T;
+    a.nsplit = ns;
+    a.scale2 = sm_scale * 1.4426950408889634f;
+    a.pages = cache->pages;
+    a.side = cache->side;
+    a.part = static_cast<float*>(const_cast<void*>(workspace));
+    a.out = nullptr;
+    a.out_dtype = KV4_OUT_F32;
+    return KV4_OK;
+}
+
+void launch_merge(const kv4::DecodeArgs& a, hipStream_t s)
+{
+    int rows = a.batch * a.g.Hq;
+    hipLaunchKernelGGL(kv4::merge_parts_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,49 +284,53 @@ int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, s
     return KV4_OK;
 }
 
+int kv4_decode_partials(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                        const int32_t* slot_ids, const int32_t* block_tables, int batch,
+                        int max_ctx, float sm_scale, void* workspace, size_t workspace_bytes_,
+                        kv4_stream_t stream)
+{
+    kv4::DecodeArgs a;
+    int st = decode_args(cache, layer, q_bf16, seq_lens, slot_ids, block_tables, batch, max_ctx,
+                         sm_scale, workspace, workspace_bytes_, true, a);
+    if (st != KV4_OK || batch == 0) return st;
+    launch_decode(a, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int kv4_decode_merge(kv4_cache* cache, const int32_t* seq_lens, int batch, int max_ctx, void* out,
+                     int out_dtype, const void* workspace, size_t workspace_bytes_,
+                     kv4_stream_t stream)
+{
+    if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
+    kv4::DecodeArgs a;
+    int st = decode_args(cache, 0, nullptr, seq_lens, nullptr, nullptr, batch, max_ctx, 1.0f,
+                         workspace, workspace_bytes_, false, a);
+    if (st != KV4_OK || batch == 0) return st;
+    if (out == nullptr) return KV4_ERR_INVALID_ARG;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    launch_merge(a, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
                     const int32_t* slot_ids, const int32_t* block_tables, int batch, int max_ctx,
                     float sm_scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes_,
                     kv4_stream_t stream)
 {
-    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
-    const kv4::Geo& g = cache->geo;
-    if (layer < 0 || layer >= g.num_layers) return KV4_ERR_CAPACITY;
-    if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
     if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
-    if (!std::isfinite(sm_scale)) return KV4_ERR_INVALID_ARG;
-    if (batch == 0) return KV4_OK;
-    if (q_bf16 == nullptr || seq_lens == nullptr || slot_ids == nullptr || block_tables == nullptr ||
-        out == nullptr)
-        return KV4_ERR_INVALID_ARG;
-    int T, ns;
-    split_plan(cache, batch, max_ctx, num_cus(cache), &T, &ns);
-    if (decode_items(g, batch, ns) > INT32_MAX) return KV4_ERR_CAPACITY;
-    size_t need = workspace_bytes(g, batch, ns);
-    if (workspace == nullptr || workspace_bytes_ < need) return KV4_ERR_WORKSPACE;
     kv4::DecodeArgs a;
-    a.g = g;
-    a.layer = layer;
-    a.q = static_cast<const uint16_t*>(q_bf16);
-    a.seq_lens = seq_lens;
-    a.slot_ids = slot_ids;
-    a.block_tables = block_tables;
-    a.batch = batch;
-    a.max_ctx = max_ctx;
-    a.split = T;
-    a.nsplit = ns;
-    a.scale2 = sm_scale * 1.4426950408889634f;
-    a.pages = cache->pages;
-    a.side = cache->side;
-    a.part = static_cast<float*>(workspace);
+    int st = decode_args(cache, layer, q_bf16, seq_lens, slot_ids, block_tables, batch, max_ctx,
+                         sm_scale, workspace, workspace_bytes_, true, a);
+    if (st != KV4_OK || batch == 0) return st;
+    if (out == nullptr) return KV4_ERR_INVALID_ARG;
     a.out = out;
     a.out_dtype = out_dtype;
     hipStream_t s = static_cast<hipStream_t>(stream);
     launch_decode(a, s);
-    int st = launch_status();
+    st = launch_status();
     if (st != KV4_OK) return st;
-    int rows = batch * g.Hq;
-    hipLaunchKernelGGL(kv4::merge_parts_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+    launch_merge(a, s);
     return launch_status();
 }
 

@@ -154,6 +154,33 @@ def test_append_and_decode_validation_no_launch():
     assert call(ws=None) == kv4.KV4_ERR_WORKSPACE
     assert call(wsb=ws - 1) == kv4.KV4_ERR_WORKSPACE
     assert call(batch=0) == kv4.KV4_OK
+
+    # the two phases validate the same way
+    def partials(**k):
+        a = args(**k)
+        return L_.kv4_decode_partials(a["cache"], a["layer"], a["q"], a["sl"], a["slot"], a["bt"],
+                                      a["batch"], a["max_ctx"], a["scale"], a["ws"], a["wsb"], None)
+
+    def merge(**k):
+        a = args(**k)
+        return L_.kv4_decode_merge(a["cache"], a["sl"], a["batch"], a["max_ctx"], a["out"],
+                                   a["dt"], a["ws"], a["wsb"], None)
+
+    for fn in (partials, merge):
+        assert fn(cache=None) == kv4.KV4_ERR_INVALID_ARG
+        assert fn(batch=4) == kv4.KV4_ERR_CAPACITY
+        assert fn(max_ctx=65) == kv4.KV4_ERR_CAPACITY
+        assert fn(max_ctx=0) == kv4.KV4_ERR_INVALID_ARG
+        assert fn(sl=None) == kv4.KV4_ERR_INVALID_ARG
+        assert fn(ws=None) == kv4.KV4_ERR_WORKSPACE
+        assert fn(wsb=ws - 1) == kv4.KV4_ERR_WORKSPACE
+        assert fn(batch=0) == kv4.KV4_OK
+    assert partials(layer=2) == kv4.KV4_ERR_CAPACITY
+    assert partials(q=None) == kv4.KV4_ERR_INVALID_ARG
+    assert partials(bt=None) == kv4.KV4_ERR_INVALID_ARG
+    assert partials(scale=float("inf")) == kv4.KV4_ERR_INVALID_ARG
+    assert merge(out=None) == kv4.KV4_ERR_INVALID_ARG
+    assert merge(dt=3) == kv4.KV4_ERR_INVALID_ARG
     kv4.kv4_cache_free(h)
 
 
@@ -167,6 +194,10 @@ def test_split_plan_and_workspace():
     h, d, _, _ = _fake_handle(max_pages_per_seq=64)
     T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
     assert T % 32 == 0 and 256 <= T <= 2048 and ns * T >= 1024
+    kv4.kv4_cache_free(h)
+    # a work item spans at most 2048 tokens, whatever the descriptor asks for
+    h, d, _, _ = _fake_handle(split_tokens=8192, max_pages_per_seq=1024)
+    assert kv4.kv4_decode_split_info(h, 3, 16384) == (2048, 8)
     kv4.kv4_cache_free(h)
 
 

@@ -107,6 +107,63 @@ def test_tiny_config():
     assert np.array_equal(outb, ref)
 
 
+def test_decode_phases_and_workspace_layout():
+    """kv4_decode_partials followed by kv4_decode_merge equals kv4_decode_attn
+    bit for bit, and the workspace holds the parts its header documents: part
+    k < nsplit = INT4 positions [kT, (k+1)T), part nsplit = protected region,
+    float d = base-2 log-normaliser.  Merging the parts on the host by eq. A1
+    in fp64 reproduces the output, and the merged log-normaliser equals the
+    oracle's log2 sum of 2^(sm_scale log2(e) q.k^) over the whole context."""
+    Hq, Hkv, G, S, R = 8, 2, 32, 4, 64
+    ctx = [0, 3, 40, 67, 68, 69, 300, 1000, 2500]
+    H.log("case decode phases: 8q/2kv G=32 S=4 R=64 split 256")
+    built, out, oc, q, want = _run_case(Hq, Hkv, G, S, R, ctx, seed=11, split=256)
+    n = np.asarray(ctx) + 1
+    B, d, gqa = len(n), 128, Hq // Hkv
+    dev = torch.device("cuda")
+    qd = H.to_dev_bf16(q)
+    nd = torch.from_numpy(n.astype(np.int32)).to(dev)
+    max_ctx = int(n.max())
+    sm = 1 / math.sqrt(d)
+    ws = built.cache.workspace(B, max_ctx)
+    ws.fill_(0xFF)                       # parts that are never written stay NaN
+    kv4.kv4_decode_partials(built.cache.handle, 0, qd, nd, built.slots, built.block_tables, B,
+                            max_ctx, sm, ws)
+    o2 = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    kv4.kv4_decode_merge(built.cache.handle, nd, B, max_ctx, o2, kv4.KV4_OUT_F32, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.cpu().numpy(), out)
+    T, ns = kv4.kv4_decode_split_info(built.cache.handle, B, max_ctx)
+    assert T == 256
+    parts = ws[:B * Hkv * (ns + 1) * gqa * (d + 4) * 4].view(torch.float32).cpu().numpy()
+    parts = parts.reshape(B, Hkv, ns + 1, gqa, d + 4).astype(np.float64)
+    c2 = sm / math.log(2.0)
+    for b in range(B):
+        nb = int(n[b])
+        rec = max(S, nb - R)
+        used = [k for k in range(ns) if max(k * T, S) < min((k + 1) * T, rec)]
+        if min(S, nb) + max(nb - rec, 0) > 0:
+            used.append(ns)
+        sl = oc.seq(b)
+        prot = np.array([oracle.is_protected(p, nb, S, R) for p in range(nb)])
+        k_hat = np.where(prot[:, None, None],
+                         oracle.dequant_int8(oc.k8[sl][:nb], oc.k8s[sl][:nb]),
+                         oracle.dequant_int4(oc.k4[sl][:nb], oc.k4d[sl][:nb], oc.k4m[sl][:nb], G))
+        for h in range(Hkv):
+            for j in range(gqa):
+                z = parts[b, h, used, j, d]
+                o = parts[b, h, used, j, :d]
+                assert np.all(np.isfinite(z)) and np.all(np.isfinite(o))
+                w = np.exp2(z - z.max())
+                merged = (w[:, None] * o).sum(0) / w.sum()
+                assert np.abs(merged - out[b, h * gqa + j]).max() <= 1e-5
+                qq = H.to_dev_bf16(q[b, h * gqa + j]).float().cpu().numpy().astype(np.float64)
+                s = c2 * (k_hat[:, h, :] @ qq)
+                z_ref = s.max() + np.log2(np.exp2(s - s.max()).sum())
+                z_got = z.max() + np.log2(w.sum())
+                assert abs(z_got - z_ref) <= 1e-4 * max(1.0, abs(z_ref)), (b, h, j, z_got, z_ref)
+
+
 @pytest.mark.parametrize("G", [32, 128])
 @pytest.mark.parametrize("S", [0, 1, 4, 16])
 def test_edge_grid(G, S):
