@@ -26,13 +26,15 @@
  *
  * Layout of the pools (all little-endian; "PB" = one (page, kv-head) block):
  *   page pool, KV4 kind: [layer][page][kv_head] blocks of
- *       K codes  16 tokens x head_dim/2 bytes, token-major; byte i of token t
- *                holds channel 2i in bits 0-3 and channel 2i+1 in bits 4-7;
+ *       K codes  16 tokens x head_dim/2 bytes, token-major; a token's row is
+ *                16 32-bit words, word w holding channels 8n .. 8n+7 with
+ *                n = 4*(w%4) + w/4 (channel 8n+e in bits 4e..4e+3);
  *       V codes  2 halves x head_dim 32-bit words; in half h, the word at index
  *                64*(c/64) + 4*(c%16) + 2*((c/32)%2) + (c/16)%2 holds the codes of
  *                tokens 8h..8h+7 at channel c, token 8h+e in bits 4e..4e+3;
- *       K delta  [group][16 tokens] binary16;   K offset [group][16] binary16;
- *       V delta  [group][16 tokens] binary16;   V offset [group][16] binary16;
+ *       K meta   [16 tokens][group] pairs (delta, offset) of binary16;
+ *       V offset [16 tokens][group] binary16;
+ *       V delta  [group][16 tokens] binary16;
  *     i.e. 16 * (head_dim + 8 * head_dim / group_size) bytes per PB
  *     (2,560 B at head_dim 128, group 32: 160 B per token and kv head).
  *   page pool, BF16 kind: [layer][page][kv_head] blocks of K [16][head_dim]

@@ -117,9 +117,13 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
 {
     if (a.g.gqa == 4) {
         dim3 grid((unsigned)decode_items(a.g, a.batch, a.nsplit));
-        if (a.g.kind == KV4_KIND_MIXED)
-            hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel, grid, dim3(64), 0, s, a);
-        else
+        if (a.g.kind == KV4_KIND_MIXED) {
+            switch (a.g.G) {
+                case 32: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<32>, grid, dim3(64), 0, s, a); break;
+                case 64: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<64>, grid, dim3(64), 0, s, a); break;
+                default: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<128>, grid, dim3(64), 0, s, a); break;
+            }
+        } else
             hipLaunchKernelGGL(kv4::decode_bf16_mfma_kernel, grid, dim3(64), 0, s, a);
         return;
     }

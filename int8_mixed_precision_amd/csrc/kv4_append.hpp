@@ -144,10 +144,11 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             int4_params<LPG>(k0, k1, db, mb);
             double D = (double)half_bits_to_float(db), M = (double)half_bits_to_float(mb);
             uint32_t c0 = int4_code(k0, D, M, db), c1 = int4_code(k1, D, M, db);
-            pb[g.off_kc + tp * (g.d / 2) + lane] = (uint8_t)(c0 | (c1 << 4));
+            pb[g.off_kc + tp * (g.d / 2) + 4 * kpos(lane >> 2) + (lane & 3)] = (uint8_t)(c0 | (c1 << 4));
             if ((lane % LPG) == 0) {
-                reinterpret_cast<uint16_t*>(pb + g.off_kd)[grp * kPage + tp] = db;
-                reinterpret_cast<uint16_t*>(pb + g.off_km)[grp * kPage + tp] = mb;
+                uint16_t* kdm = reinterpret_cast<uint16_t*>(pb + g.off_kdm) + tp * 2 * g.ng + 2 * grp;
+                kdm[0] = db;
+                kdm[1] = mb;
             }
             // ---- INT4, values
             int4_params<LPG>(v0, v1, db, mb);
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             w1 = (w1 & ~(0xFu << sh)) | (c1 << sh);
             if ((lane % LPG) == 0) {
                 reinterpret_cast<uint16_t*>(pb + g.off_vd)[grp * kPage + tp] = db;
-                reinterpret_cast<uint16_t*>(pb + g.off_vm)[grp * kPage + tp] = mb;
+                reinterpret_cast<uint16_t*>(pb + g.off_vm)[tp * g.ng + grp] = mb;
             }
             // ---- INT8 side entry for positions protected at the new length
             if (ring != nullptr && (t < g.S || t >= p1 - g.R)) {

@@ -22,8 +22,9 @@ struct Geo {
     int64_t layer_pages;     // bytes of one layer of the page pool
     int64_t rb;              // bytes per (slot, kv head) ring block
     int64_t layer_side;      // bytes of one layer of the side pool
-    // offsets inside a KV4 (page, head) block
-    int off_kc, off_vc, off_kd, off_km, off_vd, off_vm;
+    // offsets inside a KV4 (page, head) block: K codes, V codes, K (Delta, m)
+    // token-major, V m token-major, V Delta group-major
+    int off_kc, off_vc, off_kdm, off_vm, off_vd;
 };
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -48,11 +49,10 @@ inline Geo make_geo(const kv4_cache_desc& c)
     if (c.kind == KV4_KIND_MIXED) {
         g.off_kc = 0;
         g.off_vc = kPage * g.d / 2;
-        g.off_kd = kPage * g.d;
-        g.off_km = g.off_kd + 2 * kPage * g.ng;
-        g.off_vd = g.off_km + 2 * kPage * g.ng;
-        g.off_vm = g.off_vd + 2 * kPage * g.ng;
-        g.pb = g.off_vm + 2 * kPage * g.ng;
+        g.off_kdm = kPage * g.d;
+        g.off_vm = g.off_kdm + 4 * kPage * g.ng;
+        g.off_vd = g.off_vm + 2 * kPage * g.ng;
+        g.pb = g.off_vd + 2 * kPage * g.ng;
         g.rb = g.SR > 0 ? round_up((int64_t)g.SR * (2 * g.d + 4), 16) : 0;
     } else {
         g.pb = (int64_t)kPage * g.d * 2 * 2;
@@ -82,6 +82,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h16)
 __host__ __device__ __forceinline__ int vpos(int c)
 {
     return 64 * (c >> 6) + 4 * (c & 15) + 2 * ((c >> 5) & 1) + ((c >> 4) & 1);
+}
+
+// Position of K code word n (channels 8n .. 8n+7, d = 128) inside a token's
+// 64-byte code row: word 4 kb + b holds channels 32 b + 8 kb .. +7, so the
+// words of the four 32-channel blocks that one lane feeds to the QK product
+// are one 16-byte access.
+__host__ __device__ __forceinline__ int kpos(int n)
+{
+    return 4 * (n & 3) + (n >> 2);
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -187,9 +187,12 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
             const bool valid = tok >= t_begin && tok < t_end;
             const int tp = tok % kPage;
             // ---- scores
-            uint2 kc = *reinterpret_cast<const uint2*>(pb + g.off_kc + tp * (g.d / 2) + 8 * sl);
-            float D = half_bits_to_float(reinterpret_cast<const uint16_t*>(pb + g.off_kd)[gk * kPage + tp]);
-            float M = half_bits_to_float(reinterpret_cast<const uint16_t*>(pb + g.off_km)[gk * kPage + tp]);
+            const uint8_t* krow = pb + g.off_kc + tp * (g.d / 2);
+            uint2 kc = make_uint2(*reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl)),
+                                  *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl + 1)));
+            const uint16_t* kdm = reinterpret_cast<const uint16_t*>(pb + g.off_kdm) + tp * 2 * g.ng + 2 * gk;
+            float D = half_bits_to_float(kdm[0]);
+            float M = half_bits_to_float(kdm[1]);
             float s[GQA];
 #pragma unroll
             for (int j = 0; j < GQA; ++j) {
@@ -208,8 +211,8 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
             const uint32_t* vw = reinterpret_cast<const uint32_t*>(pb + g.off_vc) + half * g.d;
             uint32_t w0 = vw[vpos(2 * lane)], w1 = vw[vpos(2 * lane + 1)];
             uint4 dv = *reinterpret_cast<const uint4*>(pb + g.off_vd + 2 * (gv * kPage + half * kHalf));
-            uint4 mv = *reinterpret_cast<const uint4*>(pb + g.off_vm + 2 * (gv * kPage + half * kHalf));
-            uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w}, mvw[4] = {mv.x, mv.y, mv.z, mv.w};
+            uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w};
+            const uint16_t* vmt = reinterpret_cast<const uint16_t*>(pb + g.off_vm) + half * kHalf * g.ng + gv;
 #pragma unroll
             for (int j = 0; j < GQA; ++j) { st.o[j][0] *= alpha[j]; st.o[j][1] *= alpha[j]; }
 #pragma unroll
@@ -217,7 +220,7 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
                 int t2 = hp * kHalf + ee;
                 if (t2 < t_begin || t2 >= t_end) continue;      // uniform across the wave
                 float Dv = half_bits_to_float((dvw[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
-                float Mv = half_bits_to_float((mvw[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
+                float Mv = half_bits_to_float(vmt[ee * g.ng]);
                 float x0 = fmaf(Dv, (float)((w0 >> (4 * ee)) & 0xFu), Mv);
                 float x1 = fmaf(Dv, (float)((w1 >> (4 * ee)) & 0xFu), Mv);
 #pragma unroll

@@ -92,6 +92,16 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o)
     return r;
 }
 
+// x where the lane's bit of `lanes` is set, else 0 (v_cndmask_b32).  Volatile:
+// the QK loop rebuilds its block-diagonal operand from 4 registers every tile
+// instead of keeping four 4-register copies, three of them zero, alive.
+__device__ __forceinline__ uint32_t keep_lanes(uint32_t x, uint64_t lanes)
+{
+    uint32_t r;
+    asm volatile("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(x), "s"(lanes));
+    return r;
+}
+
 // Eight 4-bit codes -> four bf16 pairs 16 + code (pair i = codes i, i+4).
 __device__ __forceinline__ u32x4_t widen(uint32_t w, uint32_t bias)
 {
@@ -128,163 +138,171 @@ __device__ __forceinline__ float h2f(uint32_t w, int k)
     return (float)__builtin_bit_cast(f16x2_t, w)[k];
 }
 
-// Online-softmax state of one INT4 work item.  The exponentials use a
-// reference maximum m_ref that is raised only when a tile's maximum exceeds it
-// by more than kSlack (base-2 units), so accumulators are rescaled rarely;
-// l_run uses the same reference, which keeps the result exact.  With p <=
-// 2^64, w (16 + c) <= 2^64 * 65504 * 31 and sums over any context stay far
-// below the fp32 range.
+// DPP move inside a 16-lane row (bound_ctrl: every source lane is in the row).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum and sum over the 16 lanes of a row (quad swaps, then row rotations).
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp<0xB1>(x));       // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));       // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x124>(x));      // row_ror 4
+    return fmaxf(x, dpp<0x128>(x));   // row_ror 8
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x124>(x);
+    return x + dpp<0x128>(x);
+}
+
+// The exponentials of an INT4 work item use a reference maximum m_ref that is
+// raised only when a tile's maximum exceeds it by more than kSlack (base-2
+// units), so accumulators are rescaled rarely; the running sum uses the same
+// reference, which keeps the result exact.  With p <= 2^64, w (16 + c) <=
+// 2^64 * 65504 * 31 and sums over any context stay far below the fp32 range.
 constexpr float kSlack = 64.0f;
 
-struct Kv4Acc {
-    f32x4_t O[8];       // PV accumulators (rows = (head kb, block r) of this lane)
-    f32x4_t W;          // sums over tokens of the PV A operand, per (head, block)
-    float m_ref, l_run, accm;
+// One lane's loads for one 32-token tile (pages P0 = tokens 0..15 and
+// P1 = tokens 16..31).
+template <int NG>
+struct Kv4Tile {
+    uint4 kc[2];              // K code words of token n16 of each page, channels 8 kb + 32 b (word b)
+    uint32_t kdm[2][NG];      // K (Delta, m) of each group of that token (Delta low half)
+    uint32_t vm[2][(NG + 1) / 2];   // V m of each group of that token (two per word)
+    uint4 vc0, vc1;           // V code words of channels 16 s + n16 for tokens 8 kb .. 8 kb + 7
+    uint4 vd;                 // V Delta of this lane's PV row group for the same tokens
 };
 
-// The 16-byte loads one lane makes for one 32-token tile: the K part (read by
-// QK) and the V part (read by PV), loaded separately so that each can be
-// refilled for the next tile as soon as the current one is consumed.
-struct Kv4K {
-    uint4 kc0, kc1;     // K codes of this lane's QK rows (tokens +0..3 and +4..7), its block
-    uint4 kd, km;       // K Delta, m of its (block, 8 tokens)
-};
-struct Kv4V {
-    uint4 vc0, vc1;     // V code words of its column blocks (tokens of its k-block)
-    uint4 vd, vm;       // V Delta, m of its (block, 8 tokens)
-};
+// Loads of one page block through a buffer descriptor: wave-uniform base in
+// SGPRs, 32-bit lane offset, and a range of exactly one page block (reads
+// past it return zero).
+typedef __amdgpu_buffer_rsrc_t Page;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void kv4_load_k(Kv4K& t, const uint8_t* PK, const uint8_t* PM,
-                                           const Geo& g, int kc_off0, int meta_off)
+__device__ __forceinline__ Page page_rsrc(const uint8_t* p, int bytes)
 {
-    t.kc0 = *reinterpret_cast<const uint4*>(PK + kc_off0);
-    t.kc1 = *reinterpret_cast<const uint4*>(PK + kc_off0 + 4 * (kHeadDim / 2));
-    t.kd = *reinterpret_cast<const uint4*>(PM + g.off_kd + meta_off);
-    t.km = *reinterpret_cast<const uint4*>(PM + g.off_km + meta_off);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void kv4_load_v(Kv4V& t, const uint8_t* PM, const Geo& g, int meta_off,
-                                           int vc_off)
+__device__ __forceinline__ uint4 ld16(Page r, uint32_t off)
 {
-    t.vc0 = *reinterpret_cast<const uint4*>(PM + vc_off);
-    t.vc1 = *reinterpret_cast<const uint4*>(PM + vc_off + 4 * 64);
-    t.vd = *reinterpret_cast<const uint4*>(PM + g.off_vd + meta_off);
-    t.vm = *reinterpret_cast<const uint4*>(PM + g.off_vm + meta_off);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Scores of one 32-token tile for head jq: sc[e] = log2-scaled q.k^ of token
-// tok0 + e (-inf outside [t_lo, t_hi) when the tile is partial).  Returns the
-// tile maximum of head jq (the same in every lane of that head).
-__device__ __forceinline__ float kv4_scores(float (&sc)[8], const Kv4K& t, const u32x4_t (&bq)[4],
-                                            float sq, float sq16, float c2, bool full, int tok0,
-                                            int t_lo, int t_hi)
+__device__ __forceinline__ uint2 ld8(Page r, uint32_t off)
 {
-    const uint32_t bias = 0x41804180u;
-    // QK: tokens tok0 + e, e = 0..3 in D0 and 4..7 in D1, column (jq, gq)
-    f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
-    D0 = mfma_bf16(widen(t.kc0.x, bias), bq[0], D0);
-    D1 = mfma_bf16(widen(t.kc1.x, bias), bq[0], D1);
-    D0 = mfma_bf16(widen(t.kc0.y, bias), bq[1], D0);
-    D1 = mfma_bf16(widen(t.kc1.y, bias), bq[1], D1);
-    D0 = mfma_bf16(widen(t.kc0.z, bias), bq[2], D0);
-    D1 = mfma_bf16(widen(t.kc1.z, bias), bq[2], D1);
-    D0 = mfma_bf16(widen(t.kc0.w, bias), bq[3], D0);
-    D1 = mfma_bf16(widen(t.kc1.w, bias), bq[3], D1);
-    const uint32_t kdw[4] = {t.kd.x, t.kd.y, t.kd.z, t.kd.w};
-    const uint32_t kmw[4] = {t.km.x, t.km.y, t.km.z, t.km.w};
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
+
+__device__ __forceinline__ uint32_t ld4(Page r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t ld2(Page r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Per-lane byte offsets of the loads inside a page block.
+struct Kv4Offs {
+    uint32_t kc, kdm, vm, vc, vd;
+};
+
+template <int NG>
+__device__ __forceinline__ void load_k_side(Kv4Tile<NG>& t, Page P0, Page P1, const Kv4Offs& o)
+{
+    const Page P[2] = {P0, P1};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float acc = e < 4 ? D0[e] : D1[e - 4];
-        // block partial of q.k^ = Delta (q.c) + m sum(q), summed over the 4 blocks
-        const float v = fmaf(h2f(kdw[e >> 1], e & 1), acc - sq16, h2f(kmw[e >> 1], e & 1) * sq);
-        sc[e] = quad_sum(v) * c2;
-    }
-    if (!full) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int tok = tok0 + e;
-            sc[e] = (tok >= t_lo && tok < t_hi) ? sc[e] : -INFINITY;
+    for (int hh = 0; hh < 2; ++hh) {
+        t.kc[hh] = ld16(P[hh], o.kc);
+        if constexpr (NG == 4) {
+            const uint4 u = ld16(P[hh], o.kdm);
+            t.kdm[hh][0] = u.x; t.kdm[hh][1] = u.y; t.kdm[hh][2] = u.z; t.kdm[hh][3] = u.w;
+        } else if constexpr (NG == 2) {
+            const uint2 u = ld8(P[hh], o.kdm);
+            t.kdm[hh][0] = u.x; t.kdm[hh][1] = u.y;
+        } else {
+            t.kdm[hh][0] = ld4(P[hh], o.kdm);
         }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    return rows_max(mx);
 }
 
-// PV part of one tile with the reference maximum m_ref of head jq.
-__device__ __forceinline__ void kv4_pv(Kv4Acc& st, const float (&sc)[8], const Kv4V& t, bool full,
-                                       int tok0, int t_lo, int t_hi)
+template <int NG>
+__device__ __forceinline__ void load_vm(Kv4Tile<NG>& t, Page P0, Page P1, const Kv4Offs& o)
 {
-    const uint32_t bias = 0x41804180u;
-    // A operand: w = p * Delta_V (exactly 0 outside the item), split hi + lo
-    const uint32_t vdw[4] = {t.vd.x, t.vd.y, t.vd.z, t.vd.w};
-    const uint32_t vmw[4] = {t.vm.x, t.vm.y, t.vm.z, t.vm.w};
-    float wv[8], pm[8];
+    const Page P[2] = {P0, P1};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sc[e] - st.m_ref);
-        wv[e] = fmaf(p, h2f(vdw[e >> 1], e & 1), 0.0f);
-        pm[e] = fmaf(p, h2f(vmw[e >> 1], e & 1), 0.0f);
-        st.l_run += p;
-    }
-    if (!full) {                          // metadata of slots outside the item may be NaN
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int tok = tok0 + e;
-            const bool ok = tok >= t_lo && tok < t_hi;
-            wv[e] = ok ? wv[e] : 0.0f;
-            pm[e] = ok ? pm[e] : 0.0f;
+    for (int hh = 0; hh < 2; ++hh) {
+        if constexpr (NG == 4) {
+            const uint2 u = ld8(P[hh], o.vm);
+            t.vm[hh][0] = u.x; t.vm[hh][1] = u.y;
+        } else if constexpr (NG == 2) {
+            t.vm[hh][0] = ld4(P[hh], o.vm);
+        } else {
+            t.vm[hh][0] = ld2(P[hh], o.vm);
         }
     }
-    st.accm += ((pm[0] + pm[1]) + (pm[2] + pm[3])) + ((pm[4] + pm[5]) + (pm[6] + pm[7]));
-    u32x4_t ahi, alo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t hw, lw;
-        split_bf16(wv[i], wv[i + 4], hw, lw);
-        ahi[i] = hw;
-        alo[i] = lw;
-    }
-    // column block s = channels 32 (s/2) + 16 (s%2) + n16
-    const uint32_t vcw[8] = {t.vc0.x, t.vc0.y, t.vc0.z, t.vc0.w, t.vc1.x, t.vc1.y, t.vc1.z, t.vc1.w};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const u32x4_t bv = widen(vcw[s], bias);
-        st.O[s] = mfma_bf16(ahi, bv, st.O[s]);
-        st.O[s] = mfma_bf16(alo, bv, st.O[s]);
-    }
-    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
-    st.W = mfma_bf16(ahi, ones, st.W);
-    st.W = mfma_bf16(alo, ones, st.W);
 }
 
-// Raise the reference maximum of every head whose tile maximum mx exceeds it
-// by more than kSlack, rescaling what was accumulated against the old one
-// (alpha = 1 for the other heads).
-__device__ __forceinline__ void kv4_raise(Kv4Acc& st, float mx)
+// PV-role loads: this lane's tokens 8 kb .. 8 kb + 7 lie in page kb / 2, so
+// lanes 0-31 read the first page and lanes 32-63 the second: an ordinary
+// per-lane address (a buffer descriptor would have to be wave-uniform).
+template <int NG>
+__device__ __forceinline__ void load_v_side(Kv4Tile<NG>& t, const uint8_t* PM, const Kv4Offs& o)
 {
-    const int kb = threadIdx.x >> 4;
-    const bool grow = mx > st.m_ref + kSlack;
-    const float m_new = grow ? mx : st.m_ref;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_ref - m_new) : 1.0f;
-    st.m_ref = m_new;
-    st.l_run *= alpha;
-    st.accm *= alpha;
-    const float alpha_d = __shfl(alpha, 4 * kb);      // head kb of the D rows held here
-#pragma unroll
-    for (int s = 0; s < 8; ++s) st.O[s][s >> 1] *= alpha_d;
-    st.W *= alpha_d;
+    t.vc0 = *reinterpret_cast<const uint4*>(PM + o.vc);
+    t.vc1 = *reinterpret_cast<const uint4*>(PM + o.vc + 4 * 64);
+    t.vd = *reinterpret_cast<const uint4*>(PM + o.vd);
+}
+
+// V m of group gg for token half hh.
+template <int NG>
+__device__ __forceinline__ float vm_of(const Kv4Tile<NG>& t, int hh, int gg)
+{
+    return h2f(t.vm[hh][gg >> 1], gg & 1);
 }
 
 // ---------------------------------------------------------------------------
-// INT4 context split of the mixed cache.
+// INT4 context split of the mixed cache, GQA group 4.  Lane roles
+// (n16 = lane % 16, kb = lane / 16):
+//   QK, transposed: A = q, block-diagonal, row n16 = (head n16/4, block n16%4)
+//     holding q of that head on that 32-channel block, k = the 32 channels of
+//     block b (so only b = n16%4 is non-zero); B = K codes of block b widened
+//     to 16 + c, column = token n16 of a page, k = channels 32 b + 8 kb ...
+//     The four blocks accumulate into one D started at -16 sum(q), so lane l
+//     holds q_{kb,r} . c over block r of token n16 in D[r], for head kb.  The
+//     affine identity q.k^ = sum_g Delta_g (q_g . c_g) + m_g sum(q_g)
+//     (KV4-RL eq. 5.1, applied per group) then gives the score in-lane.
+//   PV: A = w = p Delta_V, row n16 = (head n16/4, block n16%4), k = tile
+//     tokens 8 kb .. 8 kb + 7, split into bf16 hi + lo; B = V codes widened to
+//     16 + c, column = channel 16 s + n16.  D row (head kb, block r), so lane
+//     l accumulates head kb's output for channel 16 s + n16 in O[s][s/2];
+//     the +16 bias is removed with the sum of exactly the A operand used
+//     (one more MFMA against a column of ones) and the m_V term sum p m is
+//     accumulated on the vector ALU in the QK layout.
+//   Probabilities move from the QK layout to the PV layout through LDS.
+// Masking: tokens outside the work item (and never-written slots of a page)
+// get score -inf, probability 0 and weight exactly 0 by selection, so garbage
+// bytes never reach the result.
 // ---------------------------------------------------------------------------
+template <int G>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int split)
 {
+    constexpr int NG = kHeadDim / G;
     const Geo& g = a.g;
     const int lane = threadIdx.x;
-    const int n16 = lane & 15, kb = lane >> 4;   // MFMA column (or A row) and k-block
-    const int jq = n16 >> 2, gq = n16 & 3;       // (head, 32-channel block) of that row/column
+    const int n16 = lane & 15, kb = lane >> 4;
+    const int jq = n16 >> 2, gq = n16 & 3;       // A row (head, block) of this lane
     const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
     const Regions rg = regions_of(n, g.S, g.R);
     const int t_lo = max(split * a.split, g.S);
@@ -295,114 +313,207 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
     const uint8_t* hbase = a.pages + (int64_t)a.layer * g.layer_pages + (int64_t)h * g.pb;
     const int64_t page_stride = (int64_t)g.Hkv * g.pb;
-    const int mg = (32 * gq) / g.G;              // metadata group of block gq
 
-    // ---- q operands: lane (column (jq, gq), k-block kb) holds q_jq on block gq
-    const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-    u32x4_t bq[4];
-    float sq = 0.f;
+    // ---- q: block-diagonal A operands and block sums
+    u32x4_t aqv;                                 // q of head jq on block gq (k-slot pairs)
+    float sq_part;
     {
-        const uint4* q4 = reinterpret_cast<const uint4*>(qrow + 32 * gq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 u = q4[i];
-            sq += bf16_lo(u.x) + bf16_hi(u.x) + bf16_lo(u.y) + bf16_hi(u.y) +
-                  bf16_lo(u.z) + bf16_hi(u.z) + bf16_lo(u.w) + bf16_hi(u.w);
-            // k-slot pairs (c, c+4) of channels 32 gq + 8 i + c
-            u32x4_t v;
-            v[0] = (u.x & 0xFFFFu) | (u.z << 16);
-            v[1] = (u.x >> 16) | (u.z & 0xFFFF0000u);
-            v[2] = (u.y & 0xFFFFu) | (u.w << 16);
-            v[3] = (u.y >> 16) | (u.w & 0xFFFF0000u);
-            u32x4_t z = {0u, 0u, 0u, 0u};
-            bq[i] = (gq == kb) ? v : z;
-        }
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
+        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
+        sq_part = ((bf16_lo(u.x) + bf16_hi(u.x)) + (bf16_lo(u.y) + bf16_hi(u.y))) +
+                  ((bf16_lo(u.z) + bf16_hi(u.z)) + (bf16_lo(u.w) + bf16_hi(u.w)));
+        // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen() pairs codes
+        aqv[0] = (u.x & 0xFFFFu) | (u.z << 16);
+        aqv[1] = (u.x >> 16) | (u.z & 0xFFFF0000u);
+        aqv[2] = (u.y & 0xFFFFu) | (u.w << 16);
+        aqv[3] = (u.y >> 16) | (u.w & 0xFFFF0000u);
     }
-    const float sq16 = 16.0f * sq;
+    // sum of q over block gq of head jq (the four lanes of A row n16), then
+    // the sums of head kb over each block r, for this lane's D rows
+    const float sq_blk = rows_sum(sq_part);
+    float sqr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sqr[r] = __shfl(sq_blk, 4 * kb + r);
+    const f32x4_t c16 = {-16.0f * sqr[0], -16.0f * sqr[1], -16.0f * sqr[2], -16.0f * sqr[3]};
+    float sqm[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+        sqm[gg] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if ((32 * r) / G == gg) sqm[gg] += sqr[r];
+    }
     const float c2 = a.scale2;
 
-    Kv4Acc st;
+    f32x4_t O[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) st.O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.W = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.m_ref = -INFINITY;
-    st.l_run = 0.f;
-    st.accm = 0.f;
+    for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
+    float accm[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) accm[gg] = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
 
-    // fixed per-lane offsets inside a 32-token tile
-    const int rq = n16 >> 2, rr = n16 & 3;       // QK row n16 -> tokens 8 rq + rr (+4)
-    const int kc_off0 = g.off_kc + (8 * (rq & 1) + rr) * (g.d / 2) + 16 * kb;
-    const int meta_off = 2 * (mg * kPage + 8 * (kb & 1));
-    const int vc_off = g.off_vc + 4 * ((kb & 1) * g.d + 4 * n16);
+    // fixed per-lane offsets inside a page block
+    Kv4Offs o;
+    o.kc = (uint32_t)(g.off_kc + n16 * (kHeadDim / 2) + 16 * kb);
+    o.kdm = (uint32_t)(g.off_kdm + n16 * 4 * NG);
+    o.vm = (uint32_t)(g.off_vm + n16 * 2 * NG);
+    o.vc = (uint32_t)(g.off_vc + 4 * ((kb & 1) * g.d + 4 * n16));
+    o.vd = (uint32_t)(g.off_vd + 2 * (((32 * gq) / G) * kPage + 8 * (kb & 1)));
 
-    // Page ids of the item's tiles, two per lane: lane l holds the pages of
-    // relative index l and l + 64 from the item's first page.  Context splits
-    // are at most kMaxSplit = 2048 tokens (64 tiles), so this covers the item.
-    int tbase = t_lo / 32;
-    int pid_a = 0, pid_b = 0;
-    auto load_pids = [&](int tb) {
-        tbase = tb;
-        const int pi = 2 * tb + lane;
-        pid_a = clampi(bt[min(pi, g.max_pages - 1)], 0, g.num_pages - 1);
-        pid_b = clampi(bt[min(pi + 64, g.max_pages - 1)], 0, g.num_pages - 1);
-    };
-    auto page_ptrs = [&](int tl, const uint8_t*& PK, const uint8_t*& PM) {
-        const int rel = 2 * (tl - tbase);            // < 128: an item spans <= 64 tiles
-        const int p0 = rel < 64 ? __builtin_amdgcn_readlane(pid_a, rel)
-                                : __builtin_amdgcn_readlane(pid_b, rel - 64);
-        const int p1 = rel + 1 < 64 ? __builtin_amdgcn_readlane(pid_a, rel + 1)
-                                    : __builtin_amdgcn_readlane(pid_b, rel + 1 - 64);
-        const uint8_t* P0 = hbase + p0 * page_stride;
-        const uint8_t* P1 = hbase + p1 * page_stride;
-        PK = (rq >> 1) ? P1 : P0;                // page of this lane's QK rows
-        PM = (kb >> 1) ? P1 : P0;                // page of this lane's k-block tokens
-    };
+    // Page ids come through the scalar cache (the block table is read-only
+    // during the kernel), two tiles ahead of their use.
     const int tile_first = t_lo / 32, tile_end = (t_hi + 31) / 32;
-    load_pids(tile_first);
-    // Software pipeline over tiles, in registers: the K part of tile t+1 is
-    // requested as soon as QK(t) has read the K part of tile t, and the V part
-    // as soon as PV(t) has read the V part, so each load overlaps about half a
-    // tile of compute without a second register set.
-    Kv4K kt;
-    Kv4V vt;
-    {
-        const uint8_t *PK, *PM;
-        page_ptrs(tile_first, PK, PM);
-        kv4_load_k(kt, PK, PM, g, kc_off0, meta_off);
-        kv4_load_v(vt, PM, g, meta_off, vc_off);
-    }
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    const const_i32 btc = (const_i32)bt;
+    const int pb_bytes = (int)g.pb;
+    auto page = [&](int pi) -> const uint8_t* {
+        const int p = clampi(btc[min(pi, g.max_pages - 1)], 0, g.num_pages - 1);
+        return hbase + (int64_t)p * page_stride;
+    };
+    const bool upper = kb >> 1;                          // PV-role tokens in the second page
+
+    __shared__ __attribute__((aligned(16))) float pbuf[4][32];
+    Kv4Tile<NG> t;
+    const uint8_t* C0 = page(2 * tile_first);           // pages of the tile loaded next
+    const uint8_t* C1 = page(2 * tile_first + 1);
+    load_k_side<NG>(t, page_rsrc(C0, pb_bytes), page_rsrc(C1, pb_bytes), o);
+    load_vm<NG>(t, page_rsrc(C0, pb_bytes), page_rsrc(C1, pb_bytes), o);
+    load_v_side<NG>(t, upper ? C1 : C0, o);
+    C0 = page(2 * tile_first + 2);
+    C1 = page(2 * tile_first + 3);
+    const uint8_t* T0 = nullptr;                        // pages of the current tile
+    const uint8_t* T1 = nullptr;
     for (int tl = tile_first; tl < tile_end; ++tl) {
         const bool full = 32 * tl >= t_lo && 32 * tl + 32 <= t_hi;
-        const int tok0 = 32 * tl + 8 * kb;
         const bool more = tl + 1 < tile_end;
-        const uint8_t *PK = nullptr, *PM = nullptr;
-        if (more) page_ptrs(tl + 1, PK, PM);
-        float sc[8];
-        const float mx = kv4_scores(sc, kt, bq, sq, sq16, c2, full, tok0, t_lo, t_hi);
-        if (more) kv4_load_k(kt, PK, PM, g, kc_off0, meta_off);
-        kv4_raise(st, mx);
-        kv4_pv(st, sc, vt, full, tok0, t_lo, t_hi);
-        if (more) kv4_load_v(vt, PM, g, meta_off, vc_off);
+        T0 = tl == tile_first ? page(2 * tl) : T0;
+        T1 = tl == tile_first ? page(2 * tl + 1) : T1;
+        // pages of tile tl + 1; after the last tile the loads below re-read
+        // the current pages (cache hits), so every load is unconditional
+        const uint8_t* N0 = more ? C0 : T0;
+        const uint8_t* N1 = more ? C1 : T1;
+        const Page R0 = page_rsrc(N0, pb_bytes), R1 = page_rsrc(N1, pb_bytes);
+        T0 = N0;
+        T1 = N1;
+        C0 = page(2 * tl + 4);
+        C1 = page(2 * tl + 5);
+
+        // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
+        f32x4_t D0 = c16, D1 = c16;
+        const uint32_t k0w[4] = {t.kc[0].x, t.kc[0].y, t.kc[0].z, t.kc[0].w};
+        const uint32_t k1w[4] = {t.kc[1].x, t.kc[1].y, t.kc[1].z, t.kc[1].w};
+        const uint32_t bias = 0x41804180u;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            // block-diagonal A: only rows of block bb (lanes with lane % 4 == bb) carry q
+            const uint64_t rows = 0x1111111111111111ull << bb;
+            const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
+                               keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
+            D0 = mfma_bf16(A, widen(k0w[bb], bias), D0);
+            D1 = mfma_bf16(A, widen(k1w[bb], bias), D1);
+        }
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int gg = (32 * r) / G;
+            x0 = fmaf(h2f(t.kdm[0][gg], 0), D0[r], x0);
+            x1 = fmaf(h2f(t.kdm[1][gg], 0), D1[r], x1);
+        }
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            x0 = fmaf(h2f(t.kdm[0][gg], 1), sqm[gg], x0);
+            x1 = fmaf(h2f(t.kdm[1][gg], 1), sqm[gg], x1);
+        }
+        load_k_side<NG>(t, R0, R1, o);
+        float s0 = x0 * c2, s1 = x1 * c2;
+        const int tok0 = 32 * tl + n16;
+        const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
+        const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
+        s0 = ok0 ? s0 : -INFINITY;
+        s1 = ok1 ? s1 : -INFINITY;
+        const float mx = row16_max(fmaxf(s0, s1));
+
+        // ---- raise the reference maximum of head kb when the tile exceeds it
+        // by more than kSlack (alpha = 1 otherwise; branch-free, so the
+        // accumulators stay in place)
+        {
+            const bool grow = mx > m_ref + kSlack;
+            const float m_new = grow ? mx : m_ref;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+            m_ref = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) O[s][s >> 1] *= alpha;
+            W *= alpha;
+        }
+
+        // ---- probabilities of head kb for tokens n16 and 16 + n16
+        const float p0 = __builtin_amdgcn_exp2f(s0 - m_ref);
+        const float p1 = __builtin_amdgcn_exp2f(s1 - m_ref);
+        l_run += p0 + p1;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            const float v0 = ok0 ? vm_of<NG>(t, 0, gg) : 0.f;   // never-written slots may hold NaN
+            const float v1 = ok1 ? vm_of<NG>(t, 1, gg) : 0.f;
+            accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+        }
+        load_vm<NG>(t, R0, R1, o);
+        pbuf[kb][n16] = p0;
+        pbuf[kb][16 + n16] = p1;
+        __syncthreads();
+        const float4 pa = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb]);
+        const float4 pb = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb + 4]);
+
+        // ---- PV: A = w = p Delta_V of head jq, block gq, tokens 8 kb + e
+        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        const uint32_t vdw[4] = {t.vd.x, t.vd.y, t.vd.z, t.vd.w};
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = fmaf(pr[e], h2f(vdw[e >> 1], e & 1), 0.0f);
+        if (!full) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tok = 32 * tl + 8 * kb + e;
+                wv[e] = (tok >= t_lo && tok < t_hi) ? wv[e] : 0.0f;
+            }
+        }
+        u32x4_t ahi, alo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hw, lw;
+            split_bf16(wv[i], wv[i + 4], hw, lw);
+            ahi[i] = hw;
+            alo[i] = lw;
+        }
+        const uint32_t vcw[8] = {t.vc0.x, t.vc0.y, t.vc0.z, t.vc0.w, t.vc1.x, t.vc1.y, t.vc1.z, t.vc1.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t bv = widen(vcw[s], bias);
+            O[s] = mfma_bf16(ahi, bv, O[s]);
+            O[s] = mfma_bf16(alo, bv, O[s]);
+        }
+        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
+        W = mfma_bf16(ahi, ones, W);
+        W = mfma_bf16(alo, ones, W);
+        load_v_side<NG>(t, upper ? N1 : N0, o);
     }
 
-    // ---- reduce the per-k-block partial sums and hand them to the output lanes
-    const float l_run = rows_sum(st.l_run);
-    const float accm = rows_sum(st.accm);
-    __shared__ float sh_c[16], sh_l[4], sh_m[4];
-    if (kb == 0) {
-        sh_c[n16] = accm;
-        if (gq == 0) { sh_l[jq] = l_run; sh_m[jq] = st.m_ref; }
-    }
-    __syncthreads();
-    const float lj = sh_l[kb];
-    const float inv = 1.0f / lj;
+    // ---- epilogue: lane l holds head kb, channels 16 s + n16
+    const float l = row16_sum(l_run);
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
+    const float inv = 1.0f / l;
     float* dst = part_ptr(a, b, h, split, kb);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int c = 32 * (s >> 1) + 16 * (s & 1) + n16;
-        dst[c] = (st.O[s][s >> 1] - 16.0f * st.W[s >> 1] + sh_c[4 * kb + (s >> 1)]) * inv;
+        const int r = s >> 1;
+        dst[16 * s + n16] = (O[s][r] - 16.0f * W[r] + accm[(32 * r) / G]) * inv;
     }
-    if (n16 == 0) dst[g.d] = sh_m[kb] + log2f(lj);
+    if (n16 == 0) dst[g.d] = m_ref + log2f(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -524,16 +635,18 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
     if (n16 == 0) dst[g.d] = sh_m[kb] + log2f(lj);
 }
 
-// One 1-D grid over work items, split-major: all first splits of every
-// (sequence, kv head), then all second splits, ..., and the protected parts
-// last, where their short runs fill the tail of the grid.
+// One 1-D grid over work items: the protected parts of every (sequence, kv
+// head) first, then split-major: all first INT4 splits, all second splits, ...
+// so that the vector-ALU protected parts overlap the INT4 work instead of
+// forming a tail.
+template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
     const int nbh = a.batch * a.g.Hkv;
-    const int split = blockIdx.x / nbh, bh = blockIdx.x % nbh;
+    const int unit = blockIdx.x / nbh, bh = blockIdx.x % nbh;
     const int b = bh / a.g.Hkv, h = bh % a.g.Hkv;
-    if (split < a.nsplit) mfma_item_kv4(a, b, h, split);
-    else valu_item_kv4<4>(a, b, h, a.nsplit);
+    if (unit == 0) valu_item_kv4<4>(a, b, h, a.nsplit);
+    else mfma_item_kv4<G>(a, b, h, unit - 1);
 }
 
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)

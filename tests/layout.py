@@ -41,7 +41,10 @@ def gather_mixed(pages: np.ndarray, side, *, layer, num_pages, Hkv, d, G, S, R, 
     h = np.arange(Hkv, dtype=np.int64)
     base = ((layer * num_pages + page[:, None]) * Hkv + h[None, :]) * PB          # [n, Hkv]
     # K codes: token-major bytes, channel 2i low nibble, 2i+1 high nibble
-    kb = pages[base[:, :, None] + (tp[:, None, None] * (d // 2)) + np.arange(d // 2)[None, None, :]]
+    # natural byte i (channels 2i, 2i+1) of word i/4 sits in word 4 (w % 4) + w / 4 of the row
+    i = np.arange(d // 2)
+    kbyte = 4 * (4 * ((i // 4) % 4) + (i // 4) // 4) + i % 4
+    kb = pages[base[:, :, None] + (tp[:, None, None] * (d // 2)) + kbyte[None, None, :]]
     k4 = np.empty((n, Hkv, d), dtype=np.uint8)
     k4[:, :, 0::2] = kb & 0xF
     k4[:, :, 1::2] = kb >> 4
@@ -55,14 +58,17 @@ def gather_mixed(pages: np.ndarray, side, *, layer, num_pages, Hkv, d, G, S, R, 
              (pages[widx + 2].astype(np.uint32) << 16) | (pages[widx + 3].astype(np.uint32) << 24))
     v4 = ((words >> (4 * (tp[:, None, None] % 8)).astype(np.uint32)) & 0xF).astype(np.uint8)
 
-    def meta(off):
-        idx = base[:, :, None] + off + 2 * (np.arange(ng)[None, None, :] * PAGE + tp[:, None, None])
-        return (pages[idx].astype(np.uint16) | (pages[idx + 1].astype(np.uint16) << 8))
+    def u16(idx):
+        return pages[idx].astype(np.uint16) | (pages[idx + 1].astype(np.uint16) << 8)
 
-    off_kd = PAGE * d
-    out = dict(k4=k4, v4=v4,
-               k4d=meta(off_kd), k4m=meta(off_kd + 2 * PAGE * ng),
-               v4d=meta(off_kd + 4 * PAGE * ng), v4m=meta(off_kd + 6 * PAGE * ng))
+    grp = np.arange(ng)[None, None, :]
+    off_kdm = PAGE * d                      # K (Delta, m) token-major: [token][group][2]
+    off_vm = off_kdm + 4 * PAGE * ng        # V m token-major: [token][group]
+    off_vd = off_vm + 2 * PAGE * ng         # V Delta group-major: [group][token]
+    kdm = base[:, :, None] + off_kdm + tp[:, None, None] * 4 * ng + 4 * grp
+    out = dict(k4=k4, v4=v4, k4d=u16(kdm), k4m=u16(kdm + 2),
+               v4d=u16(base[:, :, None] + off_vd + 2 * (grp * PAGE + tp[:, None, None])),
+               v4m=u16(base[:, :, None] + off_vm + tp[:, None, None] * 2 * ng + 2 * grp))
     SR = S + R
     k8 = np.zeros((n, Hkv, d), np.int8)
     v8 = np.zeros((n, Hkv, d), np.int8)
