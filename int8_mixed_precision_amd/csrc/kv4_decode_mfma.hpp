@@ -30,6 +30,10 @@
 
 #include "kv4_decode.hpp"
 
+#ifndef KV4_DECODE_DEPTH
+#define KV4_DECODE_DEPTH 1
+#endif
+
 namespace kv4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -170,21 +174,22 @@ __device__ __forceinline__ float row16_sum(float x)
 constexpr float kSlack = 64.0f;
 
 // One lane's loads for one 32-token tile (pages P0 = tokens 0..15 and
-// P1 = tokens 16..31).
-template <int NG>
+// P1 = tokens 16..31).  The tile's metadata (K (Delta, m), V m, V Delta of
+// both pages: 2 x 128 NG bytes) is loaded once, 16 bytes per lane, and
+// shared through LDS, instead of each lane loading the copies it needs.
+// The registers are only the landing zone of the loads: at the start of the
+// tile they belong to they are copied to a per-wave LDS stage and refilled
+// with the next tile at once, so every load has a whole tile to arrive.
 struct Kv4Tile {
     uint4 kc[2];              // K code words of token n16 of each page, channels 8 kb + 32 b (word b)
-    uint32_t kdm[2][NG];      // K (Delta, m) of each group of that token (Delta low half)
-    uint32_t vm[2][(NG + 1) / 2];   // V m of each group of that token (two per word)
     uint4 vc0, vc1;           // V code words of channels 16 s + n16 for tokens 8 kb .. 8 kb + 7
-    uint4 vd;                 // V Delta of this lane's PV row group for the same tokens
+    uint4 meta;               // 16-byte chunk lane % 32 of the metadata of page lane / 32
 };
 
 // Loads of one page block through a buffer descriptor: wave-uniform base in
 // SGPRs, 32-bit lane offset, and a range of exactly one page block (reads
 // past it return zero).
 typedef __amdgpu_buffer_rsrc_t Page;
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ Page page_rsrc(const uint8_t* p, int bytes)
 {
@@ -197,79 +202,29 @@ __device__ __forceinline__ uint4 ld16(Page r, uint32_t off)
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ uint2 ld8(Page r, uint32_t off)
-{
-    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    return make_uint2(v[0], v[1]);
-}
-
-__device__ __forceinline__ uint32_t ld4(Page r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t ld2(Page r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-
 // Per-lane byte offsets of the loads inside a page block.
 struct Kv4Offs {
-    uint32_t kc, kdm, vm, vc, vd;
+    uint32_t kc, vc, meta;
 };
 
-template <int NG>
-__device__ __forceinline__ void load_k_side(Kv4Tile<NG>& t, Page P0, Page P1, const Kv4Offs& o)
+__device__ __forceinline__ void load_k_codes(Kv4Tile& t, Page P0, Page P1, const Kv4Offs& o)
 {
-    const Page P[2] = {P0, P1};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        t.kc[hh] = ld16(P[hh], o.kc);
-        if constexpr (NG == 4) {
-            const uint4 u = ld16(P[hh], o.kdm);
-            t.kdm[hh][0] = u.x; t.kdm[hh][1] = u.y; t.kdm[hh][2] = u.z; t.kdm[hh][3] = u.w;
-        } else if constexpr (NG == 2) {
-            const uint2 u = ld8(P[hh], o.kdm);
-            t.kdm[hh][0] = u.x; t.kdm[hh][1] = u.y;
-        } else {
-            t.kdm[hh][0] = ld4(P[hh], o.kdm);
-        }
-    }
+    t.kc[0] = ld16(P0, o.kc);
+    t.kc[1] = ld16(P1, o.kc);
 }
 
-template <int NG>
-__device__ __forceinline__ void load_vm(Kv4Tile<NG>& t, Page P0, Page P1, const Kv4Offs& o)
-{
-    const Page P[2] = {P0, P1};
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        if constexpr (NG == 4) {
-            const uint2 u = ld8(P[hh], o.vm);
-            t.vm[hh][0] = u.x; t.vm[hh][1] = u.y;
-        } else if constexpr (NG == 2) {
-            t.vm[hh][0] = ld4(P[hh], o.vm);
-        } else {
-            t.vm[hh][0] = ld2(P[hh], o.vm);
-        }
-    }
-}
-
-// PV-role loads: this lane's tokens 8 kb .. 8 kb + 7 lie in page kb / 2, so
-// lanes 0-31 read the first page and lanes 32-63 the second: an ordinary
-// per-lane address (a buffer descriptor would have to be wave-uniform).
-template <int NG>
-__device__ __forceinline__ void load_v_side(Kv4Tile<NG>& t, const uint8_t* PM, const Kv4Offs& o)
+// Per-lane pages (an ordinary per-lane address: a buffer descriptor would
+// have to be wave-uniform): PV-role V codes of page kb / 2, metadata chunk
+// of page lane / 32.
+__device__ __forceinline__ void load_v_codes(Kv4Tile& t, const uint8_t* PM, const Kv4Offs& o)
 {
     t.vc0 = *reinterpret_cast<const uint4*>(PM + o.vc);
     t.vc1 = *reinterpret_cast<const uint4*>(PM + o.vc + 4 * 64);
-    t.vd = *reinterpret_cast<const uint4*>(PM + o.vd);
 }
 
-// V m of group gg for token half hh.
-template <int NG>
-__device__ __forceinline__ float vm_of(const Kv4Tile<NG>& t, int hh, int gg)
+__device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const Kv4Offs& o)
 {
-    return h2f(t.vm[hh][gg >> 1], gg & 1);
+    t.meta = *reinterpret_cast<const uint4*>(PH + o.meta);
 }
 
 // ---------------------------------------------------------------------------
@@ -295,7 +250,7 @@ __device__ __forceinline__ float vm_of(const Kv4Tile<NG>& t, int hh, int gg)
 // get score -inf, probability 0 and weight exactly 0 by selection, so garbage
 // bytes never reach the result.
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, int DEPTH>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int split)
 {
     constexpr int NG = kHeadDim / G;
@@ -355,15 +310,20 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     float m_ref = -INFINITY, l_run = 0.f;
 
     // fixed per-lane offsets inside a page block
+    constexpr int MB = 128 * NG;                 // metadata bytes per page
     Kv4Offs o;
     o.kc = (uint32_t)(g.off_kc + n16 * (kHeadDim / 2) + 16 * kb);
-    o.kdm = (uint32_t)(g.off_kdm + n16 * 4 * NG);
-    o.vm = (uint32_t)(g.off_vm + n16 * 2 * NG);
     o.vc = (uint32_t)(g.off_vc + 4 * ((kb & 1) * g.d + 4 * n16));
-    o.vd = (uint32_t)(g.off_vd + 2 * (((32 * gq) / G) * kPage + 8 * (kb & 1)));
+    const int chunk = lane & 31;                 // metadata chunk of this lane
+    const bool chunk_ok = 16 * chunk < MB;
+    o.meta = (uint32_t)(g.off_kdm + 16 * (chunk_ok ? chunk : 0));
+    // byte offsets of this lane's metadata inside the LDS copy of a page's
+    const int m_kdm = n16 * 4 * NG;                              // K (Delta, m) of token n16
+    const int m_vm = 64 * NG + n16 * 2 * NG;                     // V m of token n16
+    const int m_vd = (kb >> 1) * MB + 96 * NG + 2 * (((32 * gq) / G) * kPage + 8 * (kb & 1));
 
     // Page ids come through the scalar cache (the block table is read-only
-    // during the kernel), two tiles ahead of their use.
+    // during the kernel), ahead of their use.
     const int tile_first = t_lo / 32, tile_end = (t_hi + 31) / 32;
     typedef const __attribute__((address_space(4))) int32_t* const_i32;
     const const_i32 btc = (const_i32)bt;
@@ -372,38 +332,51 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const int p = clampi(btc[min(pi, g.max_pages - 1)], 0, g.num_pages - 1);
         return hbase + (int64_t)p * page_stride;
     };
-    const bool upper = kb >> 1;                          // PV-role tokens in the second page
+    const bool upper = kb >> 1;                  // lanes 32-63: PV tokens and metadata chunk in page 2
 
     __shared__ __attribute__((aligned(16))) float pbuf[4][32];
-    Kv4Tile<NG> t;
-    const uint8_t* C0 = page(2 * tile_first);           // pages of the tile loaded next
-    const uint8_t* C1 = page(2 * tile_first + 1);
-    load_k_side<NG>(t, page_rsrc(C0, pb_bytes), page_rsrc(C1, pb_bytes), o);
-    load_vm<NG>(t, page_rsrc(C0, pb_bytes), page_rsrc(C1, pb_bytes), o);
-    load_v_side<NG>(t, upper ? C1 : C0, o);
-    C0 = page(2 * tile_first + 2);
-    C1 = page(2 * tile_first + 3);
-    const uint8_t* T0 = nullptr;                        // pages of the current tile
-    const uint8_t* T1 = nullptr;
-    for (int tl = tile_first; tl < tile_end; ++tl) {
+    __shared__ __attribute__((aligned(16))) uint8_t mbuf[2 * 512];
+    __shared__ uint4 stage[4][64];               // K codes of both pages, V codes, per lane
+
+    auto load_tile = [&](Kv4Tile& t, const uint8_t* N0, const uint8_t* N1) {
+        load_k_codes(t, page_rsrc(N0, pb_bytes), page_rsrc(N1, pb_bytes), o);
+        const uint8_t* PM = upper ? N1 : N0;
+        load_v_codes(t, PM, o);
+        load_meta(t, PM, o);
+    };
+
+    // One tile: stage tile tl from the landing registers t into LDS, refill t
+    // from pages (N0, N1), then compute from the stage.
+    auto step = [&](Kv4Tile& t, int tl, const uint8_t* N0, const uint8_t* N1) {
         const bool full = 32 * tl >= t_lo && 32 * tl + 32 <= t_hi;
-        const bool more = tl + 1 < tile_end;
-        T0 = tl == tile_first ? page(2 * tl) : T0;
-        T1 = tl == tile_first ? page(2 * tl + 1) : T1;
-        // pages of tile tl + 1; after the last tile the loads below re-read
-        // the current pages (cache hits), so every load is unconditional
-        const uint8_t* N0 = more ? C0 : T0;
-        const uint8_t* N1 = more ? C1 : T1;
-        const Page R0 = page_rsrc(N0, pb_bytes), R1 = page_rsrc(N1, pb_bytes);
-        T0 = N0;
-        T1 = N1;
-        C0 = page(2 * tl + 4);
-        C1 = page(2 * tl + 5);
+        // ---- this tile's data to LDS, then refill the landing registers
+        stage[0][lane] = t.kc[0];
+        stage[1][lane] = t.kc[1];
+        stage[2][lane] = t.vc0;
+        stage[3][lane] = t.vc1;
+        if (chunk_ok) *reinterpret_cast<uint4*>(&mbuf[(lane >> 5) * MB + 16 * chunk]) = t.meta;
+        __builtin_amdgcn_wave_barrier();
+        load_tile(t, N0, N1);
+        const uint4 kc0 = stage[0][lane], kc1 = stage[1][lane];
+        uint32_t kdm[2][NG];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint8_t* src = &mbuf[hh * MB + m_kdm];
+            if constexpr (NG == 4) {
+                const uint4 u = *reinterpret_cast<const uint4*>(src);
+                kdm[hh][0] = u.x; kdm[hh][1] = u.y; kdm[hh][2] = u.z; kdm[hh][3] = u.w;
+            } else if constexpr (NG == 2) {
+                const uint2 u = *reinterpret_cast<const uint2*>(src);
+                kdm[hh][0] = u.x; kdm[hh][1] = u.y;
+            } else {
+                kdm[hh][0] = *reinterpret_cast<const uint32_t*>(src);
+            }
+        }
 
         // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
         f32x4_t D0 = c16, D1 = c16;
-        const uint32_t k0w[4] = {t.kc[0].x, t.kc[0].y, t.kc[0].z, t.kc[0].w};
-        const uint32_t k1w[4] = {t.kc[1].x, t.kc[1].y, t.kc[1].z, t.kc[1].w};
+        const uint32_t k0w[4] = {kc0.x, kc0.y, kc0.z, kc0.w};
+        const uint32_t k1w[4] = {kc1.x, kc1.y, kc1.z, kc1.w};
         const uint32_t bias = 0x41804180u;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
@@ -418,15 +391,14 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int gg = (32 * r) / G;
-            x0 = fmaf(h2f(t.kdm[0][gg], 0), D0[r], x0);
-            x1 = fmaf(h2f(t.kdm[1][gg], 0), D1[r], x1);
+            x0 = fmaf(h2f(kdm[0][gg], 0), D0[r], x0);
+            x1 = fmaf(h2f(kdm[1][gg], 0), D1[r], x1);
         }
 #pragma unroll
         for (int gg = 0; gg < NG; ++gg) {
-            x0 = fmaf(h2f(t.kdm[0][gg], 1), sqm[gg], x0);
-            x1 = fmaf(h2f(t.kdm[1][gg], 1), sqm[gg], x1);
+            x0 = fmaf(h2f(kdm[0][gg], 1), sqm[gg], x0);
+            x1 = fmaf(h2f(kdm[1][gg], 1), sqm[gg], x1);
         }
-        load_k_side<NG>(t, R0, R1, o);
         float s0 = x0 * c2, s1 = x1 * c2;
         const int tok0 = 32 * tl + n16;
         const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
@@ -455,22 +427,39 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const float p0 = __builtin_amdgcn_exp2f(s0 - m_ref);
         const float p1 = __builtin_amdgcn_exp2f(s1 - m_ref);
         l_run += p0 + p1;
+        {
+            const uint8_t* v0p = &mbuf[m_vm];
+            const uint8_t* v1p = &mbuf[MB + m_vm];
+            uint32_t vm0[(NG + 1) / 2], vm1[(NG + 1) / 2];
+            if constexpr (NG == 4) {
+                const uint2 u0 = *reinterpret_cast<const uint2*>(v0p);
+                const uint2 u1 = *reinterpret_cast<const uint2*>(v1p);
+                vm0[0] = u0.x; vm0[1] = u0.y; vm1[0] = u1.x; vm1[1] = u1.y;
+            } else if constexpr (NG == 2) {
+                vm0[0] = *reinterpret_cast<const uint32_t*>(v0p);
+                vm1[0] = *reinterpret_cast<const uint32_t*>(v1p);
+            } else {
+                vm0[0] = *reinterpret_cast<const uint16_t*>(v0p);
+                vm1[0] = *reinterpret_cast<const uint16_t*>(v1p);
+            }
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-            const float v0 = ok0 ? vm_of<NG>(t, 0, gg) : 0.f;   // never-written slots may hold NaN
-            const float v1 = ok1 ? vm_of<NG>(t, 1, gg) : 0.f;
-            accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+            for (int gg = 0; gg < NG; ++gg) {
+                // never-written slots may hold NaN: select, do not multiply
+                const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
+                const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
+                accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+            }
         }
-        load_vm<NG>(t, R0, R1, o);
         pbuf[kb][n16] = p0;
         pbuf[kb][16 + n16] = p1;
         __syncthreads();
         const float4 pa = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb]);
         const float4 pb = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb + 4]);
+        const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vd]);
 
         // ---- PV: A = w = p Delta_V of head jq, block gq, tokens 8 kb + e
         const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t vdw[4] = {t.vd.x, t.vd.y, t.vd.z, t.vd.w};
+        const uint32_t vdw[4] = {vd.x, vd.y, vd.z, vd.w};
         float wv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) wv[e] = fmaf(pr[e], h2f(vdw[e >> 1], e & 1), 0.0f);
@@ -489,7 +478,8 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             ahi[i] = hw;
             alo[i] = lw;
         }
-        const uint32_t vcw[8] = {t.vc0.x, t.vc0.y, t.vc0.z, t.vc0.w, t.vc1.x, t.vc1.y, t.vc1.z, t.vc1.w};
+        const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
+        const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const u32x4_t bv = widen(vcw[s], bias);
@@ -499,7 +489,66 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
         W = mfma_bf16(ahi, ones, W);
         W = mfma_bf16(alo, ones, W);
-        load_v_side<NG>(t, upper ? N1 : N0, o);
+    };
+
+    // Software pipeline over tiles in registers: DEPTH buffers, each refilled
+    // with the tile DEPTH ahead while it is consumed.  Refills past the last
+    // tile re-read the buffer's own pages (cache hits), so every load is
+    // unconditional; page ids are read one refill ahead.
+    if constexpr (DEPTH == 1) {
+        Kv4Tile t;
+        const uint8_t* T0 = page(2 * tile_first);       // pages of the tile in t
+        const uint8_t* T1 = page(2 * tile_first + 1);
+        load_tile(t, T0, T1);
+        const uint8_t* C0 = page(2 * tile_first + 2);   // pages of the next tile
+        const uint8_t* C1 = page(2 * tile_first + 3);
+        for (int tl = tile_first; tl < tile_end; ++tl) {
+            const bool more = tl + 1 < tile_end;
+            const uint8_t* N0 = more ? C0 : T0;
+            const uint8_t* N1 = more ? C1 : T1;
+            C0 = page(2 * tl + 4);
+            C1 = page(2 * tl + 5);
+            step(t, tl, N0, N1);
+            T0 = N0;
+            T1 = N1;
+        }
+    } else {
+        Kv4Tile tA, tB;
+        const bool two = tile_first + 1 < tile_end;
+        const uint8_t* A0 = page(2 * tile_first);       // pages of the tile in tA / tB
+        const uint8_t* A1 = page(2 * tile_first + 1);
+        const uint8_t* B0 = two ? page(2 * tile_first + 2) : A0;
+        const uint8_t* B1 = two ? page(2 * tile_first + 3) : A1;
+        load_tile(tA, A0, A1);
+        load_tile(tB, B0, B1);
+        const uint8_t* CA0 = page(2 * tile_first + 4);  // pages two tiles ahead of tA / tB
+        const uint8_t* CA1 = page(2 * tile_first + 5);
+        const uint8_t* CB0 = page(2 * tile_first + 6);
+        const uint8_t* CB1 = page(2 * tile_first + 7);
+        int tl = tile_first;
+        for (; tl + 1 < tile_end; tl += 2) {
+            {
+                const bool more = tl + 2 < tile_end;
+                const uint8_t* N0 = more ? CA0 : A0;
+                const uint8_t* N1 = more ? CA1 : A1;
+                CA0 = page(2 * tl + 8);
+                CA1 = page(2 * tl + 9);
+                step(tA, tl, N0, N1);
+                A0 = N0;
+                A1 = N1;
+            }
+            {
+                const bool more = tl + 3 < tile_end;
+                const uint8_t* N0 = more ? CB0 : B0;
+                const uint8_t* N1 = more ? CB1 : B1;
+                CB0 = page(2 * tl + 10);
+                CB1 = page(2 * tl + 11);
+                step(tB, tl + 1, N0, N1);
+                B0 = N0;
+                B1 = N1;
+            }
+        }
+        if (tl < tile_end) step(tA, tl, A0, A1);
     }
 
     // ---- epilogue: lane l holds head kb, channels 16 s + n16
@@ -640,13 +689,13 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
 // so that the vector-ALU protected parts overlap the INT4 work instead of
 // forming a tail.
 template <int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KV4_DECODE_DEPTH == 1 ? 4 : 3))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
     const int nbh = a.batch * a.g.Hkv;
     const int unit = blockIdx.x / nbh, bh = blockIdx.x % nbh;
     const int b = bh / a.g.Hkv, h = bh % a.g.Hkv;
     if (unit == 0) valu_item_kv4<4>(a, b, h, a.nsplit);
-    else mfma_item_kv4<G>(a, b, h, unit - 1);
+    else mfma_item_kv4<G, KV4_DECODE_DEPTH>(a, b, h, unit - 1);
 }
 
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)
