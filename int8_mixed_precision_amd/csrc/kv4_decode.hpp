@@ -367,6 +367,17 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------
 // Merge (eq. A1): one wave per (sequence, q head); 256-thread blocks.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// One wave per (sequence, q head): the stable base-2 log-sum-exp merge of the
+// non-empty parts (eq. A1).  The log-normalisers are read lane-parallel, 64
+// parts per pass; the outputs (2 channels per lane) with four independent
+// loads in flight.
 __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
 {
     const Geo& g = a.g;
@@ -387,21 +398,36 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
         has8 = 0;
     }
     k_hi = min(k_hi, a.nsplit);
+    const int n4p = max(k_hi - k_lo, 0);
+    const int np = n4p + has8;                   // parts to merge: splits k_lo.., then the protected part
+    auto part_of = [&](int i) { return part_ptr(a, b, h, i < n4p ? k_lo + i : a.nsplit, jj); };
+
     float zmax = -INFINITY;
-    for (int i = k_lo; i < k_hi; ++i) zmax = fmaxf(zmax, part_ptr(a, b, h, i, jj)[g.d]);
-    if (has8) zmax = fmaxf(zmax, part_ptr(a, b, h, a.nsplit, jj)[g.d]);
+    for (int c = 0; c < np; c += 64)
+        if (c + lane < np) zmax = fmaxf(zmax, part_of(c + lane)[g.d]);
+    zmax = wave_max(zmax);
     float W = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int i = k_lo; i <= k_hi; ++i) {
-        int item = i < k_hi ? i : a.nsplit;
-        if (i == k_hi && !has8) break;
-        const float* src = part_ptr(a, b, h, item, jj);
-        float w = exp2f(src[g.d] - zmax);
-        float2 v = *reinterpret_cast<const float2*>(src + 2 * lane);
-        W += w;
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
+    for (int c = 0; c < np; c += 64) {
+        const float w = c + lane < np ? exp2f(part_of(c + lane)[g.d] - zmax) : 0.f;
+        W += wave_sum(w);
+        const int m = min(64, np - c);
+        for (int i = 0; i < m; i += 4) {
+            float2 v[4];
+            float wi[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ii = min(i + u, m - 1);
+                wi[u] = i + u < m ? __shfl(w, ii) : 0.f;
+                v[u] = *reinterpret_cast<const float2*>(part_of(c + ii) + 2 * lane);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                o0 = fmaf(wi[u], v[u].x, o0);
+                o1 = fmaf(wi[u], v[u].y, o1);
+            }
+        }
     }
-    float inv = W > 0.f ? 1.0f / W : 0.f;      // n = 0 (clamped input) gives zeros
+    const float inv = W > 0.f ? 1.0f / W : 0.f;  // n = 0 (clamped input) gives zeros
     o0 *= inv;
     o1 *= inv;
     int64_t off = ((int64_t)b * g.Hq + j) * g.d + 2 * lane;

@@ -30,10 +30,6 @@
 
 #include "kv4_decode.hpp"
 
-#ifndef KV4_DECODE_DEPTH
-#define KV4_DECODE_DEPTH 1
-#endif
-
 namespace kv4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -250,7 +246,7 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 // get score -inf, probability 0 and weight exactly 0 by selection, so garbage
 // bytes never reach the result.
 // ---------------------------------------------------------------------------
-template <int G, int DEPTH>
+template <int G>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int split)
 {
     constexpr int NG = kHeadDim / G;
@@ -491,11 +487,10 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         W = mfma_bf16(alo, ones, W);
     };
 
-    // Software pipeline over tiles in registers: DEPTH buffers, each refilled
-    // with the tile DEPTH ahead while it is consumed.  Refills past the last
-    // tile re-read the buffer's own pages (cache hits), so every load is
-    // unconditional; page ids are read one refill ahead.
-    if constexpr (DEPTH == 1) {
+    // Tiles in order; the landing registers always hold the next tile.
+    // Refills past the last tile re-read the current pages (cache hits), so
+    // every load is unconditional; page ids are read one tile ahead.
+    {
         Kv4Tile t;
         const uint8_t* T0 = page(2 * tile_first);       // pages of the tile in t
         const uint8_t* T1 = page(2 * tile_first + 1);
@@ -512,43 +507,6 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             T0 = N0;
             T1 = N1;
         }
-    } else {
-        Kv4Tile tA, tB;
-        const bool two = tile_first + 1 < tile_end;
-        const uint8_t* A0 = page(2 * tile_first);       // pages of the tile in tA / tB
-        const uint8_t* A1 = page(2 * tile_first + 1);
-        const uint8_t* B0 = two ? page(2 * tile_first + 2) : A0;
-        const uint8_t* B1 = two ? page(2 * tile_first + 3) : A1;
-        load_tile(tA, A0, A1);
-        load_tile(tB, B0, B1);
-        const uint8_t* CA0 = page(2 * tile_first + 4);  // pages two tiles ahead of tA / tB
-        const uint8_t* CA1 = page(2 * tile_first + 5);
-        const uint8_t* CB0 = page(2 * tile_first + 6);
-        const uint8_t* CB1 = page(2 * tile_first + 7);
-        int tl = tile_first;
-        for (; tl + 1 < tile_end; tl += 2) {
-            {
-                const bool more = tl + 2 < tile_end;
-                const uint8_t* N0 = more ? CA0 : A0;
-                const uint8_t* N1 = more ? CA1 : A1;
-                CA0 = page(2 * tl + 8);
-                CA1 = page(2 * tl + 9);
-                step(tA, tl, N0, N1);
-                A0 = N0;
-                A1 = N1;
-            }
-            {
-                const bool more = tl + 3 < tile_end;
-                const uint8_t* N0 = more ? CB0 : B0;
-                const uint8_t* N1 = more ? CB1 : B1;
-                CB0 = page(2 * tl + 10);
-                CB1 = page(2 * tl + 11);
-                step(tB, tl + 1, N0, N1);
-                B0 = N0;
-                B1 = N1;
-            }
-        }
-        if (tl < tile_end) step(tA, tl, A0, A1);
     }
 
     // ---- epilogue: lane l holds head kb, channels 16 s + n16
@@ -689,13 +647,13 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
 // so that the vector-ALU protected parts overlap the INT4 work instead of
 // forming a tail.
 template <int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KV4_DECODE_DEPTH == 1 ? 4 : 3))) void decode_kv4_mfma_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
     const int nbh = a.batch * a.g.Hkv;
     const int unit = blockIdx.x / nbh, bh = blockIdx.x % nbh;
     const int b = bh / a.g.Hkv, h = bh % a.g.Hkv;
     if (unit == 0) valu_item_kv4<4>(a, b, h, a.nsplit);
-    else mfma_item_kv4<G, KV4_DECODE_DEPTH>(a, b, h, unit - 1);
+    else mfma_item_kv4<G>(a, b, h, unit - 1);
 }
 
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)

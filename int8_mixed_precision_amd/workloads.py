@@ -20,7 +20,9 @@ Recipe (the same for every config):
   * ragged lengths: lognormal with the stated median and sigma 0.8, rounded
     and clipped; uniform lengths are integers drawn uniformly.
 Every sequence's sources depend only on (seed, layer, sequence), so any subset
-can be regenerated without drawing the rest.
+can be regenerated without drawing the rest.  The 36-layer multi-step workload
+is drawn on the device instead (kv_sources_device), same recipe, seeded per
+(layer, sequence).
 """
 from __future__ import annotations
 
@@ -153,6 +155,43 @@ def all_kv_sources(cfg: Config, layer: int, lengths: Sequence[int],
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         res = list(ex.map(lambda s: kv_sources(cfg, layer, s, int(lengths[s]), out), seqs))
     return [r[0] for r in res], [r[1] for r in res]
+
+
+def device_seed(*key: int) -> int:
+    """63-bit seed of a device generator, mixed from integer keys."""
+    st = np.random.SeedSequence([int(k) for k in key]).generate_state(2, dtype=np.uint32)
+    return int((int(st[0]) << 31) ^ int(st[1])) & ((1 << 63) - 1)
+
+
+def kv_sources_device(cfg: Config, layer: int, seq: int, n: int, device,
+                      outliers: Optional[np.ndarray] = None):
+    """Keys and values of positions [0, n) of one sequence drawn on `device`
+    with a seeded counter-based generator: bf16 tensors [n, kv_heads,
+    head_dim].  Same recipe as kv_sources (N(0, 1) in float32, outlier key
+    channels scaled before rounding), different stream: for the workloads too
+    large to draw on the host.  A draw is reproducible for the same (n,
+    device) only, so callers always pass a sequence's full length."""
+    if outliers is None:
+        outliers = outlier_channels(cfg)
+    shape = (n, cfg.kv_heads, cfg.head_dim)
+    out = []
+    for tag in (TAG_K, TAG_V):
+        gen = torch.Generator(device=device)
+        gen.manual_seed(device_seed(cfg.seed, layer, seq, tag))
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if tag == TAG_K and outliers.size:
+            x[:, :, torch.as_tensor(outliers, device=device)] *= cfg.outlier_scale
+        out.append(x.to(torch.bfloat16))
+    return out[0], out[1]
+
+
+def queries_device(cfg: Config, layer: int, step: int, device):
+    """Decode-step queries [batch, q_heads, head_dim] as bf16 on `device`."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(device_seed(cfg.seed, layer, step, TAG_Q))
+    q = torch.randn((cfg.batch, cfg.q_heads, cfg.head_dim), generator=gen, device=device,
+                    dtype=torch.float32)
+    return q.to(torch.bfloat16)
 
 
 def scaled(cfg: Config, **changes) -> Config:

@@ -9,7 +9,13 @@ max_ctx = the longest sequence).
   * Qwen3-8B shape, batch 256 (lognormal median 4k, max 16k): bytes and output
     of sampled sequences (shortest, longest, median and random ones) computed
     one by one by the oracle; for every other row, properties that hold at any
-    size (finite output inside the hull of the dequantized values).
+    size (finite output inside the hull of the dequantized values);
+  * 36 layers x 64 decode steps, batch 128 (contexts uniform 1k..12k): every
+    step appends one token per sequence and layer and decodes; the output of
+    every sequence against the oracle at layers {0, 17, 35} x steps {0, 31,
+    63}; bytes of sampled sequences after the last step; and, at every step,
+    the pages that were full before the first step unchanged at the sampled
+    layers (a position's INT4 bytes are written once, when it is appended).
 """
 import math
 
@@ -72,3 +78,111 @@ def test_qwen3_8b_batch256_sampled():
     # every row: a convex combination of dequantized values stays inside their
     # per-channel range; |o| is bounded by the largest |v^| (<= ~6 for N(0,1))
     assert np.abs(out).max() < 16.0
+
+
+def test_full36_decode_steps():
+    from tests import layout as L
+    from int8_mixed_precision_amd import kv4
+    cfg = W.CONFIGS["full36"]
+    dev = torch.device("cuda")
+    ctx = W.contexts(cfg)
+    B, steps, Lyr = cfg.batch, cfg.steps, cfg.layers
+    total = ctx + steps                          # positions each sequence ends with
+    H.log(f"case full36: {Lyr} layers x {steps} steps, B={B}, sum(ctx)={int(ctx.sum())}")
+    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, total,
+                         layers=Lyr, seed=cfg.seed)
+    c = built.cache
+    out_ch = W.outlier_channels(cfg)
+    sample_layers, sample_steps = (0, 17, 35), (0, 31, 63)
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    # ---- history of every layer, and the step tokens kept on the device
+    step_k = torch.empty((Lyr, steps, B, cfg.kv_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    step_v = torch.empty_like(step_k)
+    for layer in range(Lyr):
+        for lo in range(0, B, 16):
+            seqs = list(range(lo, min(B, lo + 16)))
+            ks, vs = [], []
+            for b in seqs:
+                k, v = W.kv_sources_device(cfg, layer, b, int(total[b]), dev, out_ch)
+                ks.append(k[:int(ctx[b])])
+                vs.append(v[:int(ctx[b])])
+                step_k[layer, :, b] = k[int(ctx[b]):]
+                step_v[layer, :, b] = v[int(ctx[b]):]
+            cnt = np.array([int(ctx[b]) for b in seqs])
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).to(dev)
+            kv4.kv4_append(c.handle, layer, torch.cat(ks).contiguous(), torch.cat(vs).contiguous(),
+                           cu, torch.zeros(len(seqs), dtype=torch.int32, device=dev),
+                           built.slots[lo:lo + len(seqs)].contiguous(), built.block_tables,
+                           len(seqs), int(cnt.sum()))
+        torch.cuda.synchronize()
+        if layer % 6 == 5:
+            H.log(f"  built layer {layer}")
+    # ---- snapshot of the pages that are full before the first step
+    pages4 = c.page_pool.view(Lyr, built.desc.num_pages, -1)
+    full_ids = np.concatenate([built.bt_host[built.slots_host[b], :int(ctx[b]) // 16] for b in range(B)])
+    full_ids = torch.from_numpy(full_ids.astype(np.int64)).to(dev)
+    snap = {layer: pages4[layer].index_select(0, full_ids).clone() for layer in sample_layers}
+    # ---- decode steps: append + decode on every layer
+    outs = {}
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+    for step in range(steps):
+        before = torch.from_numpy((ctx + step).astype(np.int32)).to(dev)
+        n_d = before + 1
+        max_ctx = int(ctx.max()) + step + 1
+        for layer in range(Lyr):
+            kv4.kv4_append(c.handle, layer, step_k[layer, step].contiguous(),
+                           step_v[layer, step].contiguous(), cu1, before, built.slots,
+                           built.block_tables, B, B)
+            q = W.queries_device(cfg, layer, step, dev)
+            o = c.decode(layer, q, n_d, built.slots, built.block_tables, max_ctx, sm)
+            if layer in sample_layers and step in sample_steps:
+                outs[(layer, step)] = (q.float().cpu().numpy(), o.cpu().numpy())
+        for layer in sample_layers:
+            assert torch.equal(pages4[layer].index_select(0, full_ids), snap[layer]), \
+                f"full pages of layer {layer} changed at step {step}"
+        if step % 16 == 15:
+            H.log(f"  step {step} done")
+    torch.cuda.synchronize()
+    # ---- oracle: every sequence at the sampled (layer, step) pairs; bytes of
+    # four sequences per sampled layer after the last step
+    order = np.argsort(ctx)
+    byte_seqs = {int(order[0]), int(order[-1]), int(order[B // 2]), 7}
+    side4 = c.side_pool.view(Lyr, built.desc.max_slots, -1)
+    worst = 0.0
+    for layer in sample_layers:
+        reps = []
+        for b in range(B):
+            k, v = W.kv_sources_device(cfg, layer, b, int(total[b]), dev, out_ch)
+            kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+            k4, k4d, k4m = oracle.quant_int4(kf, cfg.group)
+            v4, v4d, v4m = oracle.quant_int4(vf, cfg.group)
+            k8, k8s = oracle.quant_int8(kf)
+            v8, v8s = oracle.quant_int8(vf)
+            reps.append((k4, k4d, k4m, v4, v4d, v4m, k8, k8s, v8, v8s))
+            if b in byte_seqs:
+                nb = int(total[b])
+                npg = -(-nb // 16)
+                ids = built.bt_host[built.slots_host[b], :npg].astype(np.int64)
+                pg = pages4[layer].index_select(0, torch.from_numpy(ids).to(dev)).cpu().numpy().ravel()
+                sd = side4[layer, int(built.slots_host[b])].cpu().numpy().ravel()
+                pm = L.protected_mask(nb, cfg.sink, cfg.recent)
+                gm = L.gather_mixed(pg, sd, layer=0, num_pages=npg, Hkv=cfg.kv_heads, d=cfg.head_dim,
+                                    G=cfg.group, S=cfg.sink, R=cfg.recent, max_slots=1,
+                                    block_tables=np.arange(npg, dtype=np.int32)[None], slot=0, n=nb,
+                                    protected_mask=pm)
+                for name, want in zip(("k4", "k4d", "k4m", "v4", "v4d", "v4m"), reps[-1][:6]):
+                    assert np.array_equal(gm[name], want), f"layer {layer} seq {b}: {name} differs"
+                for name, want in zip(("k8", "k8s", "v8", "v8s"), reps[-1][6:]):
+                    assert np.array_equal(gm[name][pm], want[pm]), f"layer {layer} seq {b}: {name} differs"
+        for step in sample_steps:
+            q, got = outs[(layer, step)]
+            want = np.empty(got.shape, np.float64)
+            for b in range(B):
+                nb = int(ctx[b]) + step + 1
+                r = [x[:nb] for x in reps[b]]
+                want[b] = oracle.attend_mixed_raw(q[b:b + 1], [nb], [0], cfg.kv_heads, cfg.group,
+                                                  cfg.sink, cfg.recent, sm, *r)[0]
+            err = H.check_output(got, want, ATOL, RTOL)
+            worst = max(worst, err[0])
+            H.log(f"  layer {layer} step {step}: max abs {err[0]:.2e} row rel {err[1]:.2e}")
+    H.log(f"full36: worst max abs {worst:.2e}")
