@@ -28,6 +28,8 @@
 // never reach the result.
 #pragma once
 
+#include <type_traits>
+
 #include "kv4_decode.hpp"
 
 namespace kv4 {
@@ -146,13 +148,22 @@ __device__ __forceinline__ float dpp(float x)
 }
 
 // Maximum and sum over the 16 lanes of a row (quad swaps, then row rotations).
+// The maximum is one v_max_f32 with a DPP source per step (a separate DPP move
+// would need an extra canonicalising max); s_nop 1 covers the VALU-write to
+// DPP-read hazard.  Inputs are finite or -inf.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ float row16_max(float x)
 {
-    x = fmaxf(x, dpp<0xB1>(x));       // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4E>(x));       // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x124>(x));      // row_ror 4
-    return fmaxf(x, dpp<0x128>(x));   // row_ror 8
+    asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+                 "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+                 "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+                 "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+                 "s_nop 1"
+                 : "+v"(x));
+    return x;
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ float row16_sum(float x)
 {
@@ -343,8 +354,8 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 
     // One tile: stage tile tl from the landing registers t into LDS, refill t
     // from pages (N0, N1), then compute from the stage.
-    auto step = [&](Kv4Tile& t, int tl, const uint8_t* N0, const uint8_t* N1) {
-        const bool full = 32 * tl >= t_lo && 32 * tl + 32 <= t_hi;
+    auto step = [&](Kv4Tile& t, int tl, const uint8_t* N0, const uint8_t* N1, auto full_tag) {
+        constexpr bool full = decltype(full_tag)::value;
         // ---- this tile's data to LDS, then refill the landing registers
         stage[0][lane] = t.kc[0];
         stage[1][lane] = t.kc[1];
@@ -399,8 +410,10 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const int tok0 = 32 * tl + n16;
         const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
         const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
-        s0 = ok0 ? s0 : -INFINITY;
-        s1 = ok1 ? s1 : -INFINITY;
+        if constexpr (!full) {
+            s0 = ok0 ? s0 : -INFINITY;
+            s1 = ok1 ? s1 : -INFINITY;
+        }
         const float mx = row16_max(fmaxf(s0, s1));
 
         // ---- raise the reference maximum of head kb when the tile exceeds it
@@ -440,10 +453,14 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             }
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
-                // never-written slots may hold NaN: select, do not multiply
-                const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
-                const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
-                accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+                if constexpr (full) {
+                    accm[gg] = fmaf(p0, h2f(vm0[gg >> 1], gg & 1), fmaf(p1, h2f(vm1[gg >> 1], gg & 1), accm[gg]));
+                } else {
+                    // never-written slots may hold NaN: select, do not multiply
+                    const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
+                    const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
+                    accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+                }
             }
         }
         pbuf[kb][n16] = p0;
@@ -459,7 +476,7 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         float wv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) wv[e] = fmaf(pr[e], h2f(vdw[e >> 1], e & 1), 0.0f);
-        if (!full) {
+        if constexpr (!full) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int tok = 32 * tl + 8 * kb + e;
@@ -497,16 +514,23 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         load_tile(t, T0, T1);
         const uint8_t* C0 = page(2 * tile_first + 2);   // pages of the next tile
         const uint8_t* C1 = page(2 * tile_first + 3);
-        for (int tl = tile_first; tl < tile_end; ++tl) {
+        // one tile: refill pointers, then the step (full tiles need no masks)
+        auto advance = [&](int tl, auto full_tag) {
             const bool more = tl + 1 < tile_end;
             const uint8_t* N0 = more ? C0 : T0;
             const uint8_t* N1 = more ? C1 : T1;
             C0 = page(2 * tl + 4);
             C1 = page(2 * tl + 5);
-            step(t, tl, N0, N1);
+            step(t, tl, N0, N1, full_tag);
             T0 = N0;
             T1 = N1;
-        }
+        };
+        // only the first and the last tile of an item can be partial
+        int tl = tile_first;
+        if (32 * tl < t_lo || 32 * tl + 32 > t_hi) advance(tl++, std::false_type{});
+        const int full_end = t_hi / 32;          // tiles [tl, full_end) are full
+        for (; tl < full_end; ++tl) advance(tl, std::true_type{});
+        if (tl < tile_end) advance(tl, std::false_type{});
     }
 
     // ---- epilogue: lane l holds head kb, channels 16 s + n16
