@@ -69,7 +69,8 @@ int num_cus(kv4_cache* c)
 
 // Context-split length: explicit (capped at kMaxSplit), or chosen so that a
 // batch whose sequences all reached max_ctx would give about 8 work items per
-// compute unit, within [256, kMaxSplit] tokens.
+// compute unit, within [256, kAutoSplit] tokens (longer items leave too few
+// of them for the MI355X's 1,024 SIMDs on ragged batches).
 void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split, int* nsplit)
 {
     int T = std::min(c->desc.split_tokens, kv4::kMaxSplit);
@@ -78,7 +79,7 @@ void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split,
         double target = 8.0 * cus;
         double t = work / target;
         T = 256;
-        while (T < kv4::kMaxSplit && T < t) T *= 2;
+        while (T < kv4::kAutoSplit && T < t) T *= 2;
     }
     // split k covers absolute positions [k*T, (k+1)*T) of the INT4 region
     *split = T;

@@ -21,6 +21,7 @@ namespace kv4 {
 
 constexpr int kPartPad = 4;      // floats after o[d] in a partial: z and padding
 constexpr int kMaxSplit = 2048;  // longest context split (tokens) a work item covers
+constexpr int kAutoSplit = 1024; // longest split the automatic choice picks
 
 struct DecodeArgs {
     Geo g;

@@ -463,9 +463,12 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
                 }
             }
         }
+        // A work item is one wave (64-thread workgroup) and one wave's LDS
+        // accesses execute in issue order, so the reads below see these
+        // writes; the barrier only keeps the compiler from reordering them.
         pbuf[kb][n16] = p0;
         pbuf[kb][16 + n16] = p1;
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
         const float4 pa = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb]);
         const float4 pb = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb + 4]);
         const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vd]);
