@@ -2,26 +2,27 @@
 //
 // One wave per work item (sequence, kv head, context split); the split is
 // walked in 32-token tiles (two pages).  Both contractions of a tile run on
-// v_mfma_f32_16x16x32_bf16 (A rows x 32 k-slots x 16 columns, fp32 accumulate):
+// 16x16x32 MFMAs with fp32 accumulation:
 //
-//   QK (INT4 keys): rows = 16 tokens, k = 32 channels of one 32-channel block,
-//     columns = (q head j, channel block g).  The B operand holds q_j only in
-//     the k-slots of block g, so one tile of four MFMAs yields, per token, the
-//     partial products q_{j,g} . c_{t,g} of every block separately; the affine
-//     identity q.k^ = Delta (q.c) + m sum(q) (KV4-RL eq. 5.1, applied per group)
-//     then turns them into scores.
-//   PV (INT4 values): rows = (q head j, channel block g), k = 32 tokens,
-//     columns = 16 channels of one block.  Row (j, g) carries p_{j,t} Delta_{t,g}
-//     so that the per-token, per-group scale of eq. 3.3 is applied exactly
-//     before the token sum; the offset term sum_t p m is accumulated on the
-//     vector ALU.
+//   QK (INT4 keys, v_mfma_f32_16x16x32_f16): rows = (q head j, 32-channel
+//     block g), k = the 32 channels of one block, columns = 16 tokens.  Row
+//     (j, g) carries q_j only when g is the block of the k-slots, so four
+//     MFMAs leave every per-block product q_{j,g} . c_{t,g} in one
+//     accumulator, and the affine identity q.k^ = sum_g Delta_g (q_g . c_g) +
+//     m_g sum(q_g) (KV4-RL eq. 5.1, applied per group) gives the scores in-lane.
+//   PV (INT4 values, v_mfma_f32_16x16x32_bf16): rows = (q head j, block g),
+//     k = 32 tokens, columns = 16 channels of one block.  Row (j, g) carries
+//     p_{j,t} Delta_{t,g}, so the per-token, per-group scale of eq. 3.3 is
+//     applied exactly before the token sum; the offset term sum_t p m is
+//     accumulated on the vector ALU.
 //
-// Exactness: 4-bit codes are widened to the bf16 values 16 + c (exact; one
-// shift and one and-or per pair), q is used at its bf16 value, and the bf16 A
-// operand of PV is split as hi + lo (both rounded to nearest), which carries
-// p*Delta to about 2^-18 relative; accumulation is fp32 throughout.  The +16
-// bias is removed with sum(q) on the QK side and, on the PV side, with the sum
-// of exactly the A operand used (one more MFMA against a column of ones).
+// Exactness: codes enter the matrix core as subnormal numbers whose mantissa
+// is the code (K: fp16, code * 2^-24 or 16 code * 2^-24; V: bf16, code *
+// 2^-133), so widening is a mask (and one shift per two pairs) and needs no
+// bias.  q is scaled by a power of two per head and is exact in fp16; the
+// bf16 A operand of PV is split as hi + lo (both rounded to nearest), which
+// carries p*Delta to about 2^-18 relative.  The power-of-two scales are
+// undone in the score factor and in the epilogue.
 //
 // Masking: tokens outside the work item (and never-written slots of a page)
 // get score -inf and weight exactly 0 by selection, so garbage bytes can
@@ -44,20 +45,44 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c)
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Eight 4-bit codes (code e in bits 4e..4e+3) -> four bf16 pairs holding the
-// exact values 16 + code; pair i = (code i, code i+4).
-__device__ __forceinline__ u32x4_t widen_codes(uint32_t w)
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c)
 {
-    const uint32_t M = 0x00780078u, B16 = 0x41804180u;
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight 4-bit K codes (code e in bits 4e..4e+3) -> four fp16 pairs whose bit
+// patterns are subnormal numbers, exact multiples of 2^-24: pair 0 = codes
+// (0, 4) and pair 2 = codes (2, 6) hold code * 2^-24, pairs 1 = (1, 5) and
+// 3 = (3, 7) hold 16 code * 2^-24 (the nibble sits in mantissa bits 4..7).
+// The A operand carries q / 16 in the k-slots of pairs 1 and 3.  One shift and
+// four ands per word; the matrix core keeps fp16 subnormal inputs.
+__device__ __forceinline__ u32x4_t widen_k16(uint32_t w)
+{
+    const uint32_t w8 = w >> 8;
     u32x4_t r;
-    r[0] = ((w << 3) & M) | B16;
-    r[1] = ((w >> 1) & M) | B16;
-    r[2] = ((w >> 5) & M) | B16;
-    r[3] = ((w >> 9) & M) | B16;
+    r[0] = w & 0x000F000Fu;
+    r[1] = w & 0x00F000F0u;
+    r[2] = w8 & 0x000F000Fu;
+    r[3] = w8 & 0x00F000F0u;
     return r;
 }
 
-__device__ __forceinline__ float dpp_f(float x, int ctrl);
+// Eight 4-bit V codes -> four bf16 pairs holding code * 2^-133 exactly (bf16
+// subnormals, mantissa = code); pair i = (code i, code i+4).  The A operand is
+// pre-scaled so that the products are normal fp32 numbers.
+__device__ __forceinline__ u32x4_t widen_v(uint32_t w)
+{
+    const uint32_t M = 0x000F000Fu;
+    u32x4_t r;
+    r[0] = w & M;
+    r[1] = (w >> 4) & M;
+    r[2] = (w >> 8) & M;
+    r[3] = (w >> 12) & M;
+    return r;
+}
 
 // Sum over the 4 lanes of a quad (lanes 4k..4k+3).
 __device__ __forceinline__ float quad_sum(float x)
@@ -67,15 +92,20 @@ __device__ __forceinline__ float quad_sum(float x)
     return x;
 }
 
-__device__ __forceinline__ float half_of(uint32_t w, int hi) { return half_bits_to_float(hi ? (w >> 16) : (w & 0xFFFFu)); }
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float x, float y)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
+}
+
+// Two fp32 values -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16(float x, float y)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, f16x2_t));
 }
 
 // Split (x, y) into bf16 high parts (nearest) and bf16 remainders (nearest):
@@ -86,14 +116,6 @@ __device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint3
     lo = pack_bf16(x - __uint_as_float(hi << 16), y - __uint_as_float(hi & 0xFFFF0000u));
 }
 
-// (x & m) | o in one VOP3 instruction (the constants live in registers).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
-    return r;
-}
-
 // x where the lane's bit of `lanes` is set, else 0 (v_cndmask_b32).  Volatile:
 // the QK loop rebuilds its block-diagonal operand from 4 registers every tile
 // instead of keeping four 4-register copies, three of them zero, alive.
@@ -101,18 +123,6 @@ __device__ __forceinline__ uint32_t keep_lanes(uint32_t x, uint64_t lanes)
 {
     uint32_t r;
     asm volatile("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(x), "s"(lanes));
-    return r;
-}
-
-// Eight 4-bit codes -> four bf16 pairs 16 + code (pair i = codes i, i+4).
-__device__ __forceinline__ u32x4_t widen(uint32_t w, uint32_t bias)
-{
-    const uint32_t M = 0x00780078u;
-    u32x4_t r;
-    r[0] = and_or(w << 3, M, bias);
-    r[1] = and_or(w >> 1, M, bias);
-    r[2] = and_or(w >> 5, M, bias);
-    r[3] = and_or(w >> 9, M, bias);
     return r;
 }
 
@@ -132,8 +142,6 @@ __device__ __forceinline__ float rows_sum(float x)
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float h2f(uint32_t w, int k)
 {
@@ -176,9 +184,13 @@ __device__ __forceinline__ float row16_sum(float x)
 // The exponentials of an INT4 work item use a reference maximum m_ref that is
 // raised only when a tile's maximum exceeds it by more than kSlack (base-2
 // units), so accumulators are rescaled rarely; the running sum uses the same
-// reference, which keeps the result exact.  With p <= 2^64, w (16 + c) <=
-// 2^64 * 65504 * 31 and sums over any context stay far below the fp32 range.
-constexpr float kSlack = 64.0f;
+// reference, which keeps the result exact.  The weights are also carried
+// scaled by 2^kPScale (p' = 2^(s - m_ref + kPScale) <= 2^64), so that the
+// products p' Delta code 2^-133 of the value contraction are normal fp32
+// numbers whenever p Delta code >= 2^-41; p' Delta <= 2^80 stays inside bf16
+// and every sum over 2^24 tokens inside fp32.
+constexpr float kSlack = 16.0f;
+constexpr float kPScale = 48.0f;
 
 // One lane's loads for one 32-token tile (pages P0 = tokens 0..15 and
 // P1 = tokens 16..31).  The tile's metadata (K (Delta, m), V m, V Delta of
@@ -237,21 +249,18 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 // ---------------------------------------------------------------------------
 // INT4 context split of the mixed cache, GQA group 4.  Lane roles
 // (n16 = lane % 16, kb = lane / 16):
-//   QK, transposed: A = q, block-diagonal, row n16 = (head n16/4, block n16%4)
-//     holding q of that head on that 32-channel block, k = the 32 channels of
-//     block b (so only b = n16%4 is non-zero); B = K codes of block b widened
-//     to 16 + c, column = token n16 of a page, k = channels 32 b + 8 kb ...
-//     The four blocks accumulate into one D started at -16 sum(q), so lane l
-//     holds q_{kb,r} . c over block r of token n16 in D[r], for head kb.  The
-//     affine identity q.k^ = sum_g Delta_g (q_g . c_g) + m_g sum(q_g)
-//     (KV4-RL eq. 5.1, applied per group) then gives the score in-lane.
-//   PV: A = w = p Delta_V, row n16 = (head n16/4, block n16%4), k = tile
-//     tokens 8 kb .. 8 kb + 7, split into bf16 hi + lo; B = V codes widened to
-//     16 + c, column = channel 16 s + n16.  D row (head kb, block r), so lane
-//     l accumulates head kb's output for channel 16 s + n16 in O[s][s/2];
-//     the +16 bias is removed with the sum of exactly the A operand used
-//     (one more MFMA against a column of ones) and the m_V term sum p m is
-//     accumulated on the vector ALU in the QK layout.
+//   QK, transposed: A = scaled q in fp16, block-diagonal, row n16 = (head
+//     n16/4, block n16%4) holding q of that head on that 32-channel block,
+//     k = the 32 channels of block b (so only b = n16%4 is non-zero); B = K
+//     codes of block b as fp16 subnormals, column = token n16 of a page,
+//     k = channels 32 b + 8 kb ...  The four blocks accumulate into one D, so
+//     lane l holds q_{kb,r} . c over block r of token n16 in D[r], for head
+//     kb, and the score follows in-lane.
+//   PV: A = w = p' Delta_V, row n16 = (head n16/4, block n16%4), k = tile
+//     tokens 8 kb .. 8 kb + 7, split into bf16 hi + lo; B = V codes as bf16
+//     subnormals, column = channel 16 s + n16.  D row (head kb, block r), so
+//     lane l accumulates head kb's output for channel 16 s + n16 in O[s][s/2];
+//     the m_V term sum p' m is accumulated on the vector ALU in the QK layout.
 //   Probabilities move from the QK layout to the PV layout through LDS.
 // Masking: tokens outside the work item (and never-written slots of a page)
 // get score -inf, probability 0 and weight exactly 0 by selection, so garbage
@@ -277,18 +286,30 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     const int64_t page_stride = (int64_t)g.Hkv * g.pb;
 
     // ---- q: block-diagonal A operands and block sums
-    u32x4_t aqv;                                 // q of head jq on block gq (k-slot pairs)
+    // A carries q_j scaled by 2^sc_j, with sc_j chosen so that max |q_j| * 2^sc_j
+    // lies in [2^14, 2^15): every bf16 element of q above 2^-31 max |q_j| is then
+    // exact in fp16 (a power-of-two scale), and the k-slots facing codes
+    // stored at 16 times their value get a further 2^-4.
+    u32x4_t aqv;                                 // scaled q of head jq on block gq (k-slot pairs)
     float sq_part;
+    int sc;                                      // scale exponent of head jq
     {
         const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
         const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
-        sq_part = ((bf16_lo(u.x) + bf16_hi(u.x)) + (bf16_lo(u.y) + bf16_hi(u.y))) +
-                  ((bf16_lo(u.z) + bf16_hi(u.z)) + (bf16_lo(u.w) + bf16_hi(u.w)));
-        // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen() pairs codes
-        aqv[0] = (u.x & 0xFFFFu) | (u.z << 16);
-        aqv[1] = (u.x >> 16) | (u.z & 0xFFFF0000u);
-        aqv[2] = (u.y & 0xFFFFu) | (u.w << 16);
-        aqv[3] = (u.y >> 16) | (u.w & 0xFFFF0000u);
+        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        sq_part = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
+        amax = fmaxf(amax, dpp<0xB1>(amax));                 // over the quad (blocks) ...
+        amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));       // ... and the rows: head jq
+        sc = 15 - __builtin_amdgcn_frexp_expf(amax);
+        // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen_k16() pairs codes
+        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
+        aqv[1] = pack_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
+        aqv[2] = pack_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
+        aqv[3] = pack_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
     }
     // sum of q over block gq of head jq (the four lanes of A row n16), then
     // the sums of head kb over each block r, for this lane's D rows
@@ -296,7 +317,10 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     float sqr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sqr[r] = __shfl(sq_blk, 4 * kb + r);
-    const f32x4_t c16 = {-16.0f * sqr[0], -16.0f * sqr[1], -16.0f * sqr[2], -16.0f * sqr[3]};
+    // D rows of this lane belong to head kb: its products come scaled by
+    // 2^(sc_kb - 24); the offset term is scaled alike and the score factor
+    // undoes it.
+    const int sc_d = __shfl(sc, 4 * kb) - 24;
     float sqm[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) {
@@ -304,17 +328,17 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if ((32 * r) / G == gg) sqm[gg] += sqr[r];
+        sqm[gg] = ldexpf(sqm[gg], sc_d);
     }
-    const float c2 = a.scale2;
+    const float c2 = ldexpf(a.scale2, -sc_d);
 
     f32x4_t O[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
     float accm[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) accm[gg] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+    float m_sh = -INFINITY, l_run = 0.f;        // m_sh = m_ref - kPScale
 
     // fixed per-lane offsets inside a page block
     constexpr int MB = 128 * NG;                 // metadata bytes per page
@@ -381,18 +405,17 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         }
 
         // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
-        f32x4_t D0 = c16, D1 = c16;
+        f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
         const uint32_t k0w[4] = {kc0.x, kc0.y, kc0.z, kc0.w};
         const uint32_t k1w[4] = {kc1.x, kc1.y, kc1.z, kc1.w};
-        const uint32_t bias = 0x41804180u;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
             // block-diagonal A: only rows of block bb (lanes with lane % 4 == bb) carry q
             const uint64_t rows = 0x1111111111111111ull << bb;
             const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
                                keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-            D0 = mfma_bf16(A, widen(k0w[bb], bias), D0);
-            D1 = mfma_bf16(A, widen(k1w[bb], bias), D1);
+            D0 = mfma_f16(A, widen_k16(k0w[bb]), D0);
+            D1 = mfma_f16(A, widen_k16(k1w[bb]), D1);
         }
         float x0 = 0.f, x1 = 0.f;
 #pragma unroll
@@ -417,24 +440,25 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const float mx = row16_max(fmaxf(s0, s1));
 
         // ---- raise the reference maximum of head kb when the tile exceeds it
-        // by more than kSlack (alpha = 1 otherwise; branch-free, so the
-        // accumulators stay in place)
+        // by more than kSlack.  The branch is wave-uniform and rarely taken;
+        // lanes that do not grow scale by exactly 1.
         {
-            const bool grow = mx > m_ref + kSlack;
-            const float m_new = grow ? mx : m_ref;
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-            m_ref = m_new;
-            l_run *= alpha;
+            const bool grow = mx > m_sh + (kPScale + kSlack);
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? mx - kPScale : m_sh;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
+                m_sh = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
+                for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) O[s][s >> 1] *= alpha;
-            W *= alpha;
+                for (int s = 0; s < 8; ++s) O[s][s >> 1] *= alpha;
+            }
         }
 
         // ---- probabilities of head kb for tokens n16 and 16 + n16
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_ref);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_ref);
+        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
+        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
         l_run += p0 + p1;
         {
             const uint8_t* v0p = &mbuf[m_vm];
@@ -498,13 +522,10 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const u32x4_t bv = widen(vcw[s], bias);
+            const u32x4_t bv = widen_v(vcw[s]);
             O[s] = mfma_bf16(ahi, bv, O[s]);
             O[s] = mfma_bf16(alo, bv, O[s]);
         }
-        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
-        W = mfma_bf16(ahi, ones, W);
-        W = mfma_bf16(alo, ones, W);
     };
 
     // Tiles in order; the landing registers always hold the next tile.
@@ -545,9 +566,9 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int r = s >> 1;
-        dst[16 * s + n16] = (O[s][r] - 16.0f * W[r] + accm[(32 * r) / G]) * inv;
+        dst[16 * s + n16] = (ldexpf(O[s][r], 133) + accm[(32 * r) / G]) * inv;
     }
-    if (n16 == 0) dst[g.d] = m_ref + log2f(l);
+    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
 // ---------------------------------------------------------------------------
