@@ -282,6 +282,36 @@ def test_decode_steps_cross_demotion_boundary():
                         assert np.array_equal(g0[k], g1[k]), (t, i, k)
 
 
+@pytest.mark.parametrize("vscale", [1.0, 300.0, 1e-3])
+def test_extreme_scales(vscale):
+    """Inputs far from N(0, 1): per-head q magnitudes from 1e-30 to 100
+    (one head all zero), keys x 10 and values x vscale.  The matrix-core path
+    scales q by a power of two per head and carries codes and weights as
+    subnormal / power-of-two-scaled numbers; the errors scale with the
+    values, so the absolute bar is 1e-3 * max(vscale, 1)."""
+    Hq, Hkv, G, S, R = 32, 8, 32, 4, 64
+    ctx = [70, 333, 1200, 2500]
+    H.log(f"case extreme scales: vscale {vscale} ctx {ctx}")
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
+                   seed=11, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx))
+    n = np.asarray(ctx, np.int64) + 1
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    ks = [W.to_bf16_values(k * 10.0) for k in ks]
+    vs = [W.to_bf16_values(v * vscale) for v in vs]
+    q = W.queries(cfg, 0).astype(np.float64)
+    head_scale = np.array([1e-30, 1e-6, 1e-2, 1.0, 3.0, 10.0, 100.0, 0.0] * (Hq // 8))
+    q = W.to_bf16_values((q * head_scale[None, :, None]).astype(np.float32))
+    built = H.make_cache(Hq, Hkv, G, S, R, n, seed=11)
+    _fill_garbage(built)
+    H.build_from_sources(built, 0, ks, vs, ctx)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    oc = oracle.MixedCache(ks, vs, G)
+    want = oracle.attend_mixed(q, oc, S, R, 1 / math.sqrt(128))
+    assert np.isfinite(out).all()
+    err = H.check_output(out, want, ATOL * max(vscale, 1.0), RTOL)
+    H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
+
+
 def test_bf16_comparator():
     """BF16 kind: pages hold the bf16 values exactly; output matches the
     oracle's dense attention."""
