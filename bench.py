@@ -2,8 +2,9 @@
 """Benchmark of the KV4 decode step on one MI355X.
 
 A step is one pass of the hot path over one batch: kv4_append of the batch's
-new token (INT4 pages + INT8 ring) followed by kv4_decode_attn (split-KV GQA
-attention over the ragged paged contexts + the log-sum-exp merge).  The
+new token (INT4 pages + INT8 ring) followed by kv4_decode_attn (GQA attention
+over the ragged paged contexts, cut by a balanced partition over the GPU's
+waves, + the log-sum-exp merge).  The
 workload is the Qwen3-8B-shaped layer (32 q / 8 kv heads, d = 128) at batch
 256 with long-tail lognormal contexts (median 4k, max 16k), 16-token pages,
 INT4 group 32, S = 4, R = 128.  Inputs are seeded synthetic data, resident in
@@ -36,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q8b256")
-    ap.add_argument("--split", type=int, default=0,
-                    help="context-split length in tokens (0 = the library's automatic choice)")
+    ap.add_argument("--waves", type=int, default=0,
+                    help="waves of the decode partition (0 = the library's choice, 16 per CU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -220,11 +221,11 @@ def main():
     log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
 
     kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                        seed=cfg.seed, split=args.split, device="cuda:0")
+                        seed=cfg.seed, waves=args.waves, device="cuda:0")
     caches = [("kv4", kv4c)]
     if not args.no_bf16:
         bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                           kind=kv4.KV4_KIND_BF16, split=args.split, device="cuda:0")
+                           kind=kv4.KV4_KIND_BF16, waves=args.waves, device="cuda:0")
         caches.append(("bf16", bfc))
     # build every cache from the same sources, sequence chunk by chunk
     step_k, step_v = [], []
@@ -256,7 +257,7 @@ def main():
     for name, c in caches:
         out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
         ws = c.cache.workspace(B, max_ctx)
-        split_T, nsplit = kv4.kv4_decode_split_info(c.cache.handle, B, max_ctx)
+        waves = kv4.kv4_decode_waves(c.cache.handle)
 
         def append():
             kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B,
@@ -304,10 +305,10 @@ def main():
                              decode_ms_p10=float(np.percentile(td, 10)),
                              decode_ms_p90=float(np.percentile(td, 90)),
                              wall_ms_per_step=wall * 1e3 / args.steps,
-                             split_tokens=split_T, nsplit=nsplit)
+                             waves=waves)
         log(f"{name}: append {ta.mean() * 1e3:.1f} us, partials {tp.mean() * 1e3:.1f} us, "
             f"merge {tm.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
-            f"(median {np.median(td) * 1e3:.1f}), split {split_T}")
+            f"(median {np.median(td) * 1e3:.1f}), waves {waves}")
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -352,7 +353,7 @@ def main():
                         "page 16, INT4 group 32, S=4, R=128",
             "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
-            "split_tokens": r["split_tokens"],
+            "waves": r["waves"],
         },
         "decode_attn_gbs": round(decode_gbs, 2),
         "decode_attn_pct_hbm_peak": round(100 * decode_gbs / HBM_PEAK_GBS, 2),

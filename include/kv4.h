@@ -7,8 +7,8 @@
  * recent positions (KV4-RL, arXiv 2610.14448: Section 3 eq. 3.3; Section 5.1;
  * Section 5.2 "Bounded selective protection"; Section 5.3; Appendix A.2
  * "Scheduling and attention" and "Phase memory management"; Appendix A.3).
- * A BF16 cache kind with the same paging and the same split/merge structure is
- * provided as the comparator (the paper's BF16 baseline, Section 6.1).
+ * A BF16 cache kind with the same paging and the same partition/merge structure
+ * is provided as the comparator (the paper's BF16 baseline, Section 6.1).
  *
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers unless stated otherwise; the
@@ -40,11 +40,15 @@
  *   page pool, BF16 kind: [layer][page][kv_head] blocks of K [16][head_dim]
  *     bf16 (token-major) then V [2 halves][head_dim][8 tokens] bf16 -- value
  *     (t, c) at ((t/8)*head_dim + c)*8 + t%8 (8,192 B at head_dim 128).
- *   side pool (KV4 kind only): [layer][slot][kv_head] blocks of
- *       K codes [S+R][head_dim] int8, V codes [S+R][head_dim] int8,
- *       K scale [S+R] binary16, V scale [S+R] binary16, padded to 16 bytes.
- *     Position p of a sequence lives in ring entry p when p < S and in entry
- *     S + (p - S) mod R otherwise.
+ *   side pool (KV4 kind only): [layer][slot][kv_head] blocks of E = S + R
+ *     ring entries padded to a multiple of 32:
+ *       K codes [E][head_dim] int8 (entry-major);
+ *       V codes [E/8] blocks of 8 entries x head_dim int8, channel-major:
+ *                entry e, channel c at (e/8)*8*head_dim + ((c%16)*8 + c/16)*8 + e%8;
+ *       K scale [E] binary16, then V scale [E] binary16;
+ *     i.e. E * (2*head_dim + 4) bytes.  Position p of a sequence lives in ring
+ *     entry p when p < S and in entry S + (p - S) mod R otherwise, so the
+ *     protected positions of an n-token context are entries [0, min(n, S+R)).
  */
 #ifndef KV4_H
 #define KV4_H
@@ -93,9 +97,9 @@ typedef struct kv4_cache_desc {
     int32_t max_pages_per_seq;  /* columns of the block table */
     int32_t kind;               /* KV4_KIND_MIXED or KV4_KIND_BF16 */
     int32_t flags;              /* KV4_FLAG_* */
-    int32_t split_tokens;       /* context-split length for decode; 0 = automatic,
-                                   else a positive multiple of 32 (values above
-                                   2048 act as 2048) */
+    int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
+                                   partition; 0 = 16 per compute unit of the
+                                   current device, else 1 .. 65536 */
 } kv4_cache_desc;
 
 typedef struct kv4_cache kv4_cache;  /* opaque host-side handle */
@@ -156,32 +160,38 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
                const int32_t* block_tables, int batch, int total_new, kv4_stream_t stream);
 
 /*
- * Workspace bytes kv4_decode_attn needs for `batch` sequences whose lengths
- * (after the step's append) are at most max_ctx: the per-part outputs and
- * log-normalisers of the split/merge.  Queries the current device's compute-
- * unit count (the split plan depends on it); launches nothing.
+ * Workspace bytes kv4_decode_attn needs for `batch` sequences (validated
+ * against max_ctx, which does not change the size): the per-part outputs and
+ * log-normalisers of the partition/merge, ((2*batch*Hkv + W) * (Hq/Hkv) *
+ * (d + 4)) float32 plus batch*Hkv int32 pairs, W = kv4_decode_waves.  Queries
+ * the current device's compute-unit count; launches nothing.
  */
 int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, size_t* bytes);
 
 /*
  * GQA decode attention of one query token per sequence over its ragged, paged
  * context (KV4-RL Section 5.3 and Appendix A.3 "Regional softmax merge",
- * eq. A1): the INT4 region is processed in context splits and the protected
- * region (sink + recent, read from the INT8 ring) as one more part; each part
- * yields a locally normalised output and log-normaliser, and a merge kernel
- * combines them by a stable log-sum-exp with zero weight for empty parts.
+ * eq. A1): the INT4 region is cut into runs of 32-token tiles and the
+ * protected region (sink + recent, read from the INT8 ring) is one more part;
+ * each part yields a locally normalised output and log-normaliser, and a merge
+ * kernel combines them by a stable log-sum-exp with zero weight for empty
+ * parts.  The cut is a balanced partition of the whole batch's work over W
+ * waves (see kv4_decode_partials), so every wave gets the same number of tiles
+ * whatever the length mix.
  *
  *   q_bf16      [batch][Hq][d] bf16 (after RoPE)
  *   seq_lens    [batch] int32, n = context length after this step's append
  *               (1 <= n <= max_ctx); the query attends over positions [0, n)
  *   slot_ids    [batch] int32; block_tables as for kv4_append
- *   max_ctx     host bound on every n; sizes the grid and the workspace
+ *   max_ctx     host bound on every n (lengths are clamped to it)
  *   sm_scale    softmax scale applied to q.k (1/sqrt(d) is the usual choice)
  *   out         [batch][Hq][d], float32 (KV4_OUT_F32) or bf16 (KV4_OUT_BF16)
  *   workspace   device buffer of >= kv4_decode_workspace_bytes(cache, batch, max_ctx)
  * q head j reads kv head j / (Hq / Hkv).  Protected positions of an n-token
  * context are [0, min(S, n)) and [max(S, n - R), n); all others read INT4.
- * Errors: KV4_ERR_INVALID_ARG, KV4_ERR_CAPACITY, KV4_ERR_WORKSPACE, KV4_ERR_HIP.
+ * Errors: KV4_ERR_INVALID_ARG, KV4_ERR_CAPACITY (also when batch * Hkv *
+ * (ceil(max_ctx / 32) + 1 + ceil((S + R) / 32)) >= 2^30, the bound of the
+ * partition's 32-bit counts), KV4_ERR_WORKSPACE, KV4_ERR_HIP.
  */
 int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
                     const int32_t* slot_ids, const int32_t* block_tables, int batch,
@@ -196,21 +206,35 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
  * context split over several devices yields parts of one (sequence, head)
  * that combine by the same eq. A1 of KV4-RL Appendix A.3).
  *
- * kv4_decode_partials runs every work item of the step: the INT4 region of
- * each (sequence b, kv head h) in context splits of T tokens, and the
- * protected region as one more part.  It writes the workspace as float32
- *     part[b][h][k][j][d + 4],  k in [0, nsplit],  j in [0, Hq/Hkv)
- * (T, nsplit from kv4_decode_split_info): part k < nsplit covers absolute
- * positions [kT, (k+1)T) of the INT4 region and part nsplit the protected
- * region.  Floats [0, d) hold the part's softmax-normalised output of q head
- * h*(Hq/Hkv)+j and float d its base-2 log-normaliser z = max + log2(sum) of
- * the scores scaled by sm_scale*log2(e).  Parts with no positions are not
- * written.
+ * kv4_decode_partials runs the whole step's work as one sequence of units:
+ * for each (sequence b, kv head h), bh = b*Hkv + h in increasing order, its
+ * protected part (if non-empty; one indivisible unit of weight U8 =
+ * ceil((S + R) / 32), its 32-entry tiles) and then the
+ * 32-token tiles of its INT4 region [S, max(S, n - R)) (tile t covers positions
+ * [32t, 32t + 32) clipped to the region).  With U units in total and
+ * P protected parts, T4 tiles, weight U = T4 + U8 * P and W' = min(W,
+ * ceil(U / 8)) waves in use, wave w runs protected parts [floor(w P / W'),
+ * floor((w+1) P / W')) and tiles [t(w), t(w+1)) of the tile sequence, t(w) =
+ * floor(w U / W') - U8 * floor(w P / W') (every wave the same weight); when
+ * that is not increasing in w, t(w) = floor(min(w, W4) T4 / W4) with W4 =
+ * max(1, min(W', T4)) instead.  Each maximal run of tiles of one bh in a
+ * wave's range is one part.  Workspace, float32
+ * records of (Hq/Hkv) rows of d + 4 floats (row j: floats [0, d) the
+ * softmax-normalised output of q head h*(Hq/Hkv) + j over the part, float d its
+ * base-2 log-normaliser z = max + log2(sum) of the scores scaled by
+ * sm_scale*log2(e)):
+ *     run records        [batch*Hkv + W]  the run of bh by wave w at bh + w
+ *     protected records  [batch*Hkv]      the protected part of bh at bh
+ *     header             [batch*Hkv][2] int32: first and last wave running
+ *                        tiles of bh (written when bh has INT4 tiles)
+ * so the runs of bh are the records bh + first .. bh + last.  Parts with no
+ * positions are not written.  The BF16 kind has no protected parts and tiles
+ * its whole context.
  *
  * kv4_decode_merge combines, per (b, q head), the non-empty parts of that
  * workspace into out with weights 2^(z_k - max z) (zero for empty parts); its
  * batch, max_ctx and seq_lens must be those of the kv4_decode_partials call
- * that wrote the workspace.
+ * that wrote the workspace.  The workspace must be 16-byte aligned.
  * Errors: as kv4_decode_attn.
  */
 int kv4_decode_partials(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
@@ -228,12 +252,11 @@ int kv4_cache_free(kv4_cache* cache);
 const char* kv4_status_string(int status);
 
 /*
- * Context-split length (tokens) kv4_decode_attn uses for this batch shape, and
- * the number of splits reserved for the longest INT4 region.  For tests and
- * for reporting; launches nothing.
+ * W, the number of waves of the decode partition (desc.num_waves, or 16 per
+ * compute unit of the current device).  For tests and reporting; launches
+ * nothing.
  */
-int kv4_decode_split_info(const kv4_cache* cache, int batch, int max_ctx,
-                          int* split_tokens, int* num_splits);
+int kv4_decode_waves(const kv4_cache* cache, int* waves);
 
 #ifdef __cplusplus
 }

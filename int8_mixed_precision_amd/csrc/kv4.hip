@@ -33,13 +33,12 @@ int validate_desc(const kv4_cache_desc* d)
     if (d->num_layers < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1 || d->head_dim < 1 ||
         d->page_size < 1 || d->group_size < 1 || d->sink < 0 || d->recent < 0 ||
         d->num_pages < 1 || d->max_slots < 1 || d->max_pages_per_seq < 1 ||
-        d->split_tokens < 0)
+        d->num_waves < 0 || d->num_waves > kv4::kMaxWaves)
         return KV4_ERR_INVALID_ARG;
     if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
     if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16) return KV4_ERR_INVALID_ARG;
     if (d->flags & ~KV4_FLAG_ROTATE_K) return KV4_ERR_INVALID_ARG;
     if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
-    if (d->split_tokens % 32 != 0) return KV4_ERR_INVALID_ARG;
     int gqa = d->num_q_heads / d->num_kv_heads;
     if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
     if (d->head_dim != kv4::kHeadDim || d->page_size != kv4::kPage) return KV4_ERR_UNSUPPORTED;
@@ -67,28 +66,36 @@ int num_cus(kv4_cache* c)
     return c->num_cus > 0 ? c->num_cus : 256;
 }
 
-// Context-split length: explicit (capped at kMaxSplit), or chosen so that a
-// batch whose sequences all reached max_ctx would give about 8 work items per
-// compute unit, within [256, kAutoSplit] tokens (longer items leave too few
-// of them for the MI355X's 1,024 SIMDs on ragged batches).
-void split_plan(const kv4_cache* c, int batch, int max_ctx, int cus, int* split, int* nsplit)
+// Waves of the balanced decode partition: explicit, or 16 per compute unit
+// (4 one-wave workgroups per SIMD, the occupancy the decode kernel is built
+// for), so that every wave of the grid is resident at once.
+int decode_waves(const kv4_cache* c, int cus)
 {
-    int T = std::min(c->desc.split_tokens, kv4::kMaxSplit);
-    if (T == 0) {
-        double work = (double)batch * c->geo.Hkv * (double)max_ctx;
-        double target = 8.0 * cus;
-        double t = work / target;
-        T = 256;
-        while (T < kv4::kAutoSplit && T < t) T *= 2;
-    }
-    // split k covers absolute positions [k*T, (k+1)*T) of the INT4 region
-    *split = T;
-    *nsplit = max((max_ctx + T - 1) / T, 1);
+    return c->desc.num_waves > 0 ? c->desc.num_waves : 16 * cus;
 }
 
-size_t workspace_bytes(const kv4::Geo& g, int batch, int nsplit)
+// Weight of a protected part in the partition: its 32-entry tiles.
+int prot_units(const kv4::Geo& g)
 {
-    return (size_t)batch * g.Hkv * (size_t)(nsplit + 1) * g.gqa * (g.d + kv4::kPartPad) * sizeof(float);
+    return g.kind == KV4_KIND_MIXED && g.SR > 0 ? (g.SR + kv4::kTile - 1) / kv4::kTile : 0;
+}
+
+// Upper bound of the partition's total weight for a batch shape.
+int64_t partition_weight(const kv4::Geo& g, int batch, int max_ctx)
+{
+    return (int64_t)batch * g.Hkv * ((max_ctx + kv4::kTile - 1) / kv4::kTile + 1 + prot_units(g));
+}
+
+// Records of the INT4 / BF16 runs, protected records, then the (first, last)
+// wave header of every (sequence, kv head).
+size_t records_floats(const kv4::Geo& g, int batch, int waves)
+{
+    return ((size_t)2 * batch * g.Hkv + (size_t)waves) * g.gqa * (g.d + kv4::kPartPad);
+}
+
+size_t workspace_bytes(const kv4::Geo& g, int batch, int waves)
+{
+    return records_floats(g, batch, waves) * sizeof(float) + (size_t)batch * g.Hkv * 2 * sizeof(int32_t);
 }
 
 int launch_status()
@@ -101,23 +108,17 @@ int launch_status()
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
-    dim3 grid(a.nsplit + (a.g.kind == KV4_KIND_MIXED ? 1 : 0), a.g.Hkv, a.batch);
+    dim3 grid((unsigned)a.waves);
     if (a.g.kind == KV4_KIND_MIXED)
-        hipLaunchKernelGGL(kv4::decode_split_kv4_kernel<GQA>, grid, dim3(64), 0, s, a);
+        hipLaunchKernelGGL(kv4::decode_valu_kv4_kernel<GQA>, grid, dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL(kv4::decode_split_bf16_kernel<GQA>, grid, dim3(64), 0, s, a);
-}
-
-// Work items of one decode launch (INT4 splits + protected parts).
-int64_t decode_items(const kv4::Geo& g, int batch, int nsplit)
-{
-    return (int64_t)(nsplit + (g.kind == KV4_KIND_MIXED ? 1 : 0)) * batch * g.Hkv;
+        hipLaunchKernelGGL(kv4::decode_valu_bf16_kernel<GQA>, grid, dim3(64), 0, s, a);
 }
 
 void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
 {
     if (a.g.gqa == 4) {
-        dim3 grid((unsigned)decode_items(a.g, a.batch, a.nsplit));
+        dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {
             switch (a.g.G) {
                 case 32: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<32>, grid, dim3(64), 0, s, a); break;
@@ -150,11 +151,12 @@ int decode_args(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* 
     if (batch > 0 && (seq_lens == nullptr ||
                       (need_q && (q_bf16 == nullptr || slot_ids == nullptr || block_tables == nullptr))))
         return KV4_ERR_INVALID_ARG;
-    int T, ns;
-    split_plan(cache, batch, max_ctx, num_cus(cache), &T, &ns);
-    if (decode_items(g, batch, ns) > INT32_MAX) return KV4_ERR_CAPACITY;
-    if (batch > 0 && (workspace == nullptr || ws_bytes < workspace_bytes(g, batch, ns)))
+    // the partition counts tiles and protected parts in 32-bit arithmetic
+    if (partition_weight(g, batch, max_ctx) >= (int64_t)1 << 30) return KV4_ERR_CAPACITY;
+    const int waves = decode_waves(cache, num_cus(cache));
+    if (batch > 0 && (workspace == nullptr || ws_bytes < workspace_bytes(g, batch, waves)))
         return KV4_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KV4_ERR_INVALID_ARG;
     a.g = g;
     a.layer = layer;
     a.q = static_cast<const uint16_t*>(q_bf16);
@@ -163,12 +165,13 @@ int decode_args(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* 
     a.block_tables = block_tables;
     a.batch = batch;
     a.max_ctx = max_ctx;
-    a.split = T;
-    a.nsplit = ns;
+    a.waves = waves;
+    a.prot_units = prot_units(g);
     a.scale2 = sm_scale * 1.4426950408889634f;
     a.pages = cache->pages;
     a.side = cache->side;
     a.part = static_cast<float*>(const_cast<void*>(workspace));
+    a.hdr = reinterpret_cast<int2*>(a.part + records_floats(g, batch, waves));
     a.out = nullptr;
     a.out_dtype = KV4_OUT_F32;
     return KV4_OK;
@@ -266,15 +269,10 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     return launch_status();
 }
 
-int kv4_decode_split_info(const kv4_cache* cache, int batch, int max_ctx, int* split_tokens,
-                          int* num_splits)
+int kv4_decode_waves(const kv4_cache* cache, int* waves)
 {
-    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
-    int T, ns;
-    int cus = cache->num_cus > 0 ? cache->num_cus : 256;
-    split_plan(cache, batch, max_ctx, cus, &T, &ns);
-    if (split_tokens) *split_tokens = T;
-    if (num_splits) *num_splits = ns;
+    if (cache == nullptr || waves == nullptr) return KV4_ERR_INVALID_ARG;
+    *waves = decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache)));
     return KV4_OK;
 }
 
@@ -283,9 +281,8 @@ int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, s
     if (cache == nullptr || bytes == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
     const kv4::Geo& g = cache->geo;
     if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
-    int T, ns;
-    split_plan(cache, batch, max_ctx, num_cus(const_cast<kv4_cache*>(cache)), &T, &ns);
-    *bytes = workspace_bytes(g, batch, ns);
+    if (partition_weight(g, batch, max_ctx) >= (int64_t)1 << 30) return KV4_ERR_CAPACITY;
+    *bytes = workspace_bytes(g, batch, decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache))));
     return KV4_OK;
 }
 

@@ -172,12 +172,13 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
                 int b0 = int8_code(v0, Sv, sv), b1 = int8_code(v1, Sv, sv);
                 reinterpret_cast<uint16_t*>(ring + (int64_t)e * g.d)[lane] =
                     (uint16_t)((a0 & 0xFF) | ((a1 & 0xFF) << 8));
-                reinterpret_cast<uint16_t*>(ring + (int64_t)(g.SR + e) * g.d)[lane] =
-                    (uint16_t)((b0 & 0xFF) | ((b1 & 0xFF) << 8));
+                uint8_t* vr = ring + (int64_t)g.SR32 * g.d;
+                vr[ring_vbyte(e, 2 * lane)] = (uint8_t)b0;
+                vr[ring_vbyte(e, 2 * lane + 1)] = (uint8_t)b1;
                 if (lane == 0) {
-                    uint16_t* sc = reinterpret_cast<uint16_t*>(ring + (int64_t)2 * g.SR * g.d);
+                    uint16_t* sc = reinterpret_cast<uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
                     sc[e] = sk;
-                    sc[g.SR + e] = sv;
+                    sc[g.SR32 + e] = sv;
                 }
             }
         }

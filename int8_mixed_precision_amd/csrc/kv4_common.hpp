@@ -21,6 +21,7 @@ struct Geo {
     int64_t pb;              // bytes per (page, kv head) block
     int64_t layer_pages;     // bytes of one layer of the page pool
     int64_t rb;              // bytes per (slot, kv head) ring block
+    int SR32;                // ring entries, padded to a multiple of 32
     int64_t layer_side;      // bytes of one layer of the side pool
     // offsets inside a KV4 (page, head) block: K codes, V codes, K (Delta, m)
     // token-major, V m token-major, V Delta group-major
@@ -53,10 +54,12 @@ inline Geo make_geo(const kv4_cache_desc& c)
         g.off_vm = g.off_kdm + 4 * kPage * g.ng;
         g.off_vd = g.off_vm + 2 * kPage * g.ng;
         g.pb = g.off_vd + 2 * kPage * g.ng;
-        g.rb = g.SR > 0 ? round_up((int64_t)g.SR * (2 * g.d + 4), 16) : 0;
+        g.SR32 = (int)round_up(g.SR, 32);
+        g.rb = g.SR > 0 ? (int64_t)g.SR32 * (2 * g.d + 4) : 0;
     } else {
         g.pb = (int64_t)kPage * g.d * 2 * 2;
         g.rb = 0;
+        g.SR32 = 0;
     }
     g.layer_pages = (int64_t)g.num_pages * g.Hkv * g.pb;
     g.layer_side = (int64_t)g.max_slots * g.Hkv * g.rb;
@@ -91,6 +94,15 @@ __host__ __device__ __forceinline__ int vpos(int c)
 __host__ __device__ __forceinline__ int kpos(int n)
 {
     return 4 * (n & 3) + (n >> 2);
+}
+
+// Byte of channel c of ring entry e inside the V code region of a ring block:
+// entries in blocks of 8, channel-major, channels ordered c%16 then c/16, so
+// one lane's eight channels 16 s + n (s = 0..7) of 8 entries are 64
+// contiguous bytes.
+__host__ __device__ __forceinline__ int ring_vbyte(int e, int c)
+{
+    return (e >> 3) * (8 * kHeadDim) + ((c & 15) * 8 + (c >> 4)) * 8 + (e & 7);
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -6,7 +6,19 @@
 // each part yields a locally normalised output o_r and log-normaliser z_r and
 // the parts are merged with z = log sum_r e^{z_r}, o = sum_r e^{z_r - z} o_r
 // (eq. A1), with zero weight for empty parts; the same identity merges the
-// context splits inside a region.
+// pieces into which the partition below cuts a region.
+//
+// Work partition (balanced, persistent): the work of a launch is a sequence of
+// units -- for each (sequence b, kv head h) in order, first its protected part
+// (one indivisible unit weighing as many tiles as it has 32-entry tiles) and
+// then the 32-token tiles of
+// its INT4 region (one unit each).  W waves take equal contiguous ranges of
+// that sequence; a wave runs every protected part that starts in its range and
+// every run of tiles of one (b, h) inside it, writing one record per run.  A
+// run of (b, h) by wave w writes record b*Hkv + h + w, which is unique because
+// along the sequence either the head index or the wave index grows at every
+// cut.  The wave that runs the first tile of (b, h) stores the first and the
+// last wave of (b, h) in a header for the merge.
 //
 // Arithmetic: q stays at its bf16 value; keys and values are reconstructed in
 // fp32 registers as Delta*c + m (INT4, eq. 3.3) or s*c (INT8); scores, the
@@ -20,8 +32,9 @@
 namespace kv4 {
 
 constexpr int kPartPad = 4;      // floats after o[d] in a partial: z and padding
-constexpr int kMaxSplit = 2048;  // longest context split (tokens) a work item covers
-constexpr int kAutoSplit = 1024; // longest split the automatic choice picks
+constexpr int kTile = 32;        // tokens per INT4 / BF16 unit
+constexpr int kMinUnits = 8;     // least weight a wave is given (fewer waves otherwise)
+constexpr int kMaxWaves = 1 << 16;
 
 struct DecodeArgs {
     Geo g;
@@ -31,12 +44,14 @@ struct DecodeArgs {
     const int32_t* slot_ids;
     const int32_t* block_tables;
     int batch, max_ctx;
-    int split;                    // tokens per context split (multiple of 32)
-    int nsplit;                   // INT4 splits reserved per (sequence, kv head)
+    int waves;                    // W: waves of the partition (= the grid)
+    int prot_units;               // weight of a protected part in tiles: its 32-entry tiles
     float scale2;                 // sm_scale * log2(e)
     const uint8_t* pages;
     const uint8_t* side;
-    float* part;                  // [batch][Hkv][nsplit+1][gqa][d + kPartPad]
+    float* part;                  // records [batch*Hkv + W][gqa][d + kPartPad], then the
+                                  // protected records [batch*Hkv][gqa][d + kPartPad]
+    int2* hdr;                    // [batch*Hkv]: first and last wave of the INT4 records
     void* out;
     int out_dtype;
 };
@@ -56,10 +71,224 @@ __device__ __forceinline__ Regions regions_of(int n, int S, int R)
     return r;
 }
 
-__device__ __forceinline__ float* part_ptr(const DecodeArgs& a, int b, int h, int item, int j)
+// Record `slot` (INT4 / BF16 runs) and the protected record of (b, h).
+__device__ __forceinline__ float* rec_ptr(const DecodeArgs& a, int64_t slot)
 {
-    return a.part + ((((int64_t)b * a.g.Hkv + h) * (a.nsplit + 1) + item) * a.g.gqa + j) *
-                        (int64_t)(a.g.d + kPartPad);
+    return a.part + slot * a.g.gqa * (int64_t)(a.g.d + kPartPad);
+}
+
+__device__ __forceinline__ float* prot_ptr(const DecodeArgs& a, int bh)
+{
+    return rec_ptr(a, (int64_t)a.batch * a.g.Hkv + a.waves + bh);
+}
+
+// Tile range of the INT4 (mixed cache) or BF16 region of a sequence of n
+// tokens, and whether it has a protected part.
+struct Units {
+    int tok_lo, tok_hi;           // token range of the tiled region
+    int tile_lo, ntile;           // its tiles
+    int prot;                     // 1 if the sequence has a protected part
+};
+
+__device__ __forceinline__ Units units_of(const DecodeArgs& a, int n)
+{
+    Units u;
+    if (a.g.kind == KV4_KIND_MIXED) {
+        const Regions rg = regions_of(n, a.g.S, a.g.R);
+        u.tok_lo = a.g.S;
+        u.tok_hi = rg.rec_start;
+        u.prot = rg.n8 > 0;
+    } else {
+        u.tok_lo = 0;
+        u.tok_hi = n;
+        u.prot = 0;
+    }
+    u.tile_lo = u.tok_lo / kTile;
+    u.ntile = u.tok_hi > u.tok_lo ? (u.tok_hi + kTile - 1) / kTile - u.tile_lo : 0;
+    return u;
+}
+
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b)
+{
+    return clampi(a.seq_lens[b], 0, a.max_ctx);
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    return __builtin_amdgcn_readfirstlane(x);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_scan_i32(int x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// floor(w X / W) for w <= W <= 2^16 without 64-bit division.
+__device__ __forceinline__ uint32_t share(uint32_t w, uint32_t X, uint32_t W)
+{
+    const uint32_t q = X / W, r = X - q * W;
+    return w * q + (w * r) / W;
+}
+
+// The partition of one launch.  Units: T4 tiles in (b, h, tile) order and P
+// protected parts in (b, h) order, of weight U8 tiles each.  Wave w
+// runs protected parts [pbeg(w), pbeg(w+1)) with pbeg(w) = floor(w P / W) and
+// tiles [tbeg(w), tbeg(w+1)) with tbeg(w) = floor(w (T4 + U8 P) / W)
+// - U8 pbeg(w), so that every wave's total weight is the same (and
+// every wave gets at least one tile).  When tiles are too few for that, they
+// are split evenly over the first min(W, T4) waves instead.  Either way the
+// waves running tiles of one (b, h) are consecutive and each runs some of
+// them.  The host bounds T4 + U8 P below 2^30.
+struct Plan {
+    uint32_t T4;                  // INT4 / BF16 tiles
+    uint32_t P;                   // protected parts
+    uint32_t U8;                  // weight of a protected part
+    uint32_t W;                   // waves in use
+    uint32_t Wt;                  // waves running tiles when not balanced
+    bool balanced;
+    __device__ uint32_t pbeg(uint32_t w) const { return share(w, P, W); }
+    __device__ uint32_t tbeg(uint32_t w) const
+    {
+        return balanced ? share(w, T4 + U8 * P, W) - U8 * pbeg(w)
+                        : share(min(w, Wt), T4, Wt);
+    }
+    // the wave whose tile range holds tile x (tbeg(w_lo) <= x < T4)
+    __device__ uint32_t wave_of_tile(uint32_t x, uint32_t w_lo) const
+    {
+        uint32_t lo = w_lo, hi = W - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (tbeg(mid) <= x) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+};
+
+__device__ __forceinline__ Plan make_plan(const DecodeArgs& a)
+{
+    const int lane = threadIdx.x & 63;
+    int t = 0, p = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+        const int b = b0 + lane;
+        if (b < a.batch) {
+            const Units u = units_of(a, seq_len(a, b));
+            t += u.ntile;
+            p += u.prot;
+        }
+    }
+    Plan pl;
+    pl.T4 = (uint32_t)wave_sum_i32(t) * a.g.Hkv;
+    pl.P = (uint32_t)wave_sum_i32(p) * a.g.Hkv;
+    pl.U8 = (uint32_t)a.prot_units;
+    const uint32_t weight = pl.T4 + pl.U8 * pl.P;
+    pl.W = min((uint32_t)a.waves, max(1u, (weight + kMinUnits - 1) / kMinUnits));
+    // monotone iff every wave's share covers its protected parts
+    const uint32_t pmax = (pl.P + pl.W - 1) / pl.W;
+    pl.balanced = weight / pl.W >= pl.U8 * pmax + 1;
+    pl.Wt = max(1u, min(pl.W, pl.T4));
+    return pl;
+}
+
+// First sequence b whose cumulative count (of `field` times Hkv) exceeds x:
+// returns b and the count before it in C.
+template <class F>
+__device__ __forceinline__ int locate_seq(const DecodeArgs& a, uint32_t x, F&& field, uint32_t& C)
+{
+    const int lane = threadIdx.x & 63;
+    C = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+        const int bb = b0 + lane;
+        const int s = bb < a.batch ? a.g.Hkv * field(units_of(a, seq_len(a, bb))) : 0;
+        const int incl = wave_scan_i32(s);
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        if (C + tot > x) {
+            const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(C + (uint32_t)incl > x)));
+            C += __builtin_amdgcn_readlane(incl - s, l);
+            return b0 + l;
+        }
+        C += tot;
+    }
+    return a.batch;
+}
+
+// Wave w's protected parts: prot(b, h) for each.
+template <class Prot>
+__device__ __forceinline__ void walk_prot(const DecodeArgs& a, const Plan& pl, uint32_t w, Prot&& prot)
+{
+    uint32_t p = pl.pbeg(w);
+    const uint32_t pe = pl.pbeg(w + 1);
+    if (p >= pe) return;
+    uint32_t C;
+    int b = locate_seq(a, p, [](const Units& u) { return u.prot; }, C);
+    int h = (int)(p - C);
+    for (; p < pe; ++p) {
+        prot(b, h);
+        if (++h == a.g.Hkv) {                   // next sequence with a protected part
+            h = 0;
+            do {
+                if (++b >= a.batch) return;
+            } while (!units_of(a, seq_len(a, b)).prot);
+        }
+    }
+}
+
+// Wave w's tiles: run(b, h, tok_lo, tok_hi, rec) for each maximal run of tiles
+// of one (b, h) in its range (token range clipped to the region; rec = record
+// b*Hkv + h + w).  The wave running the first tile of (b, h) stores the first
+// and last wave of (b, h) in the header.
+template <class Run>
+__device__ __forceinline__ void walk_tiles(const DecodeArgs& a, const Plan& pl, uint32_t w, Run&& run)
+{
+    const int lane = threadIdx.x & 63;
+    const int Hkv = a.g.Hkv;
+    uint32_t x = pl.tbeg(w);
+    const uint32_t xe = pl.tbeg(w + 1);
+    if (x >= xe) return;
+    uint32_t C;
+    int b = locate_seq(a, x, [](const Units& u) { return u.ntile; }, C);
+    Units u = units_of(a, seq_len(a, b));
+    while (x < xe) {
+        const uint32_t r = x - C;
+        const int h = (int)(r / (uint32_t)u.ntile);
+        const int t0 = (int)(r - (uint32_t)h * u.ntile);
+        const uint32_t base = C + (uint32_t)h * u.ntile;
+        const int t1 = (int)min((uint32_t)u.ntile, xe - base);
+        const int bh = b * Hkv + h;
+        if (t0 == 0 && lane == 0) a.hdr[bh] = make_int2((int)w, (int)pl.wave_of_tile(base + u.ntile - 1, w));
+        run(b, h, max(kTile * (u.tile_lo + t0), u.tok_lo), min(kTile * (u.tile_lo + t1), u.tok_hi),
+            rec_ptr(a, (int64_t)bh + w));
+        x = base + t1;
+        if (x >= C + (uint32_t)Hkv * u.ntile) {  // next sequence with tiles
+            C += (uint32_t)Hkv * u.ntile;
+            do {
+                if (++b >= a.batch) return;
+                u = units_of(a, seq_len(a, b));
+            } while (u.ntile == 0);
+        }
+    }
+}
+
+// The whole partition for wave w = blockIdx.x: its protected parts, then its
+// tiles (two separate loops, so that the vector-ALU and the matrix-core parts
+// never share a loop body's registers).
+template <class Prot, class Run>
+__device__ __forceinline__ void walk_units(const DecodeArgs& a, Prot&& prot, Run&& run)
+{
+    const Plan pl = make_plan(a);
+    const uint32_t w = blockIdx.x;
+    if (w >= pl.W) return;
+    walk_prot(a, pl, w, prot);
+    walk_tiles(a, pl, w, run);
 }
 
 __device__ __forceinline__ float wave_sum(float x)
@@ -108,15 +337,14 @@ __device__ __forceinline__ void softmax_chunk(Online<GQA>& st, float (&s)[GQA], 
 }
 
 template <int GQA>
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, Online<GQA>& st, int b, int h,
-                                              int item)
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, Online<GQA>& st, float* rec)
 {
     const int lane = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < GQA; ++j) {
         float l = wave_sum(st.l[j]);
         float inv = 1.0f / l;
-        float* dst = part_ptr(a, b, h, item, j);
+        float* dst = rec + j * (a.g.d + kPartPad);
         *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(st.o[j][0] * inv, st.o[j][1] * inv);
         if (lane == 0) dst[a.g.d] = st.m[j] + log2f(l);
     }
@@ -146,24 +374,21 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h, float 
 }
 
 // ---------------------------------------------------------------------------
-// Mixed cache, vector-ALU path: one wave per work item (sequence b, kv head h,
-// item); items < nsplit are INT4 context splits, item nsplit is the protected
-// (sink + recent) part read from the INT8 ring.
+// Mixed cache, vector-ALU path: one wave runs INT4 positions [t_begin, t_end)
+// of (sequence b, kv head h) (prot = false), or the protected (sink + recent)
+// part read from the INT8 ring (prot = true), into record `rec`.
 // ---------------------------------------------------------------------------
 template <int GQA>
-__device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h, int item)
+__device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h, bool prot,
+                                              int t_begin, int t_end, float* rec)
 {
     const Geo& g = a.g;
     const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
-    const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
+    const int n = seq_len(a, b);
     const Regions rg = regions_of(n, g.S, g.R);
-    const bool prot = item == a.nsplit;
-    int t_begin = 0, t_end = 0;
     if (prot) {
+        t_begin = 0;
         t_end = rg.n8;
-    } else {
-        t_begin = max(item * a.split, g.S);
-        t_end = min((item + 1) * a.split, rg.rec_start);
     }
     if (t_end <= t_begin) return;
 
@@ -234,16 +459,22 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
             __syncthreads();
         }
     } else {
+        // The protected positions of an n-token context occupy ring entries
+        // [0, n8) (sinks, then the recent window in ring order); attention is
+        // over the set, so the entries are walked in ring order.
         const uint8_t* ring = a.side + (int64_t)a.layer * g.layer_side + ((int64_t)slot * g.Hkv + h) * g.rb;
-        const uint16_t* scales = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR * g.d);
+        const uint8_t* vr = ring + (int64_t)g.SR32 * g.d;
+        const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
+        const uint16_t* vsc = ksc + g.SR32;
         for (int c0 = 0; c0 < t_end; c0 += kHalf) {
-            const int i = c0 + e;
-            const bool valid = i < t_end;
-            const int pos = i < rg.sink_end ? i : rg.rec_start + (i - rg.sink_end);
-            const int ent = pos < g.S ? pos : g.S + (g.R > 0 ? (pos - g.S) % g.R : 0);
-            const int entc = clampi(ent, 0, g.SR - 1);
-            uint4 kc = *reinterpret_cast<const uint4*>(ring + (int64_t)entc * g.d + 16 * sl);
-            float sk = half_bits_to_float(scales[entc]);
+            const int ent = c0 + e;                  // < SR32: the ring is padded to 32 entries
+            const bool valid = ent < t_end;
+            uint4 kc = *reinterpret_cast<const uint4*>(ring + (int64_t)ent * g.d + 16 * sl);
+            float sk = half_bits_to_float(ksc[ent]);
+            // the chunk's value codes (8 entries of this lane's two channels) and scales
+            const uint2 va = *reinterpret_cast<const uint2*>(vr + ring_vbyte(c0, 2 * lane));
+            const uint2 vb = *reinterpret_cast<const uint2*>(vr + ring_vbyte(c0, 2 * lane + 1));
+            const uint4 svw = *reinterpret_cast<const uint4*>(vsc + c0);
             uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
             float s[GQA];
 #pragma unroll
@@ -260,16 +491,15 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < GQA; ++j) { st.o[j][0] *= alpha[j]; st.o[j][1] *= alpha[j]; }
+            const uint32_t svs[4] = {svw.x, svw.y, svw.z, svw.w};
+#pragma unroll
             for (int ee = 0; ee < kHalf; ++ee) {
-                int i2 = c0 + ee;
-                if (i2 >= t_end) break;
-                int pos2 = i2 < rg.sink_end ? i2 : rg.rec_start + (i2 - rg.sink_end);
-                int ent2 = pos2 < g.S ? pos2 : g.S + (g.R > 0 ? (pos2 - g.S) % g.R : 0);
-                ent2 = clampi(ent2, 0, g.SR - 1);
-                uint32_t vv = reinterpret_cast<const uint16_t*>(ring + (int64_t)(g.SR + ent2) * g.d)[lane];
-                float sv = half_bits_to_float(scales[g.SR + ent2]);
-                float x0 = sv * (float)(int)(int8_t)(vv & 0xFFu);
-                float x1 = sv * (float)(int)(int8_t)(vv >> 8);
+                // entries past the end hold garbage: select, do not multiply
+                const bool ok = c0 + ee < t_end;
+                const float sv = half_bits_to_float((svs[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
+                const uint32_t wa = ee < 4 ? va.x : va.y, wb = ee < 4 ? vb.x : vb.y;
+                const float x0 = ok ? sv * (float)(int)(int8_t)((wa >> (8 * (ee & 3))) & 0xFFu) : 0.f;
+                const float x1 = ok ? sv * (float)(int)(int8_t)((wb >> (8 * (ee & 3))) & 0xFFu) : 0.f;
 #pragma unroll
                 for (int j = 0; j < GQA; ++j) {
                     float p = P[ee][j];
@@ -280,27 +510,26 @@ __device__ __forceinline__ void valu_item_kv4(const DecodeArgs& a, int b, int h,
             __syncthreads();
         }
     }
-    write_partial<GQA>(a, st, b, h, item);
+    write_partial<GQA>(a, st, rec);
 }
 
-// Grid (nsplit+1, Hkv, batch).
+// One wave per workgroup; grid = W.
 template <int GQA>
-__global__ __launch_bounds__(64) void decode_split_kv4_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64) void decode_valu_kv4_kernel(DecodeArgs a)
 {
-    valu_item_kv4<GQA>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+    walk_units(a, [&](int b, int h) { valu_item_kv4<GQA>(a, b, h, true, 0, 0, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec) { valu_item_kv4<GQA>(a, b, h, false, lo, hi, rec); });
 }
 
 // ---------------------------------------------------------------------------
 // BF16 comparator, vector-ALU path: the same split structure over bf16 pages.
 // ---------------------------------------------------------------------------
 template <int GQA>
-__device__ __forceinline__ void valu_item_bf16(const DecodeArgs& a, int b, int h, int item)
+__device__ __forceinline__ void valu_item_bf16(const DecodeArgs& a, int b, int h, int t_begin,
+                                               int t_end, float* rec)
 {
     const Geo& g = a.g;
     const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
-    const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
-    const int t_begin = item * a.split;
-    const int t_end = min((item + 1) * a.split, n);
     if (t_end <= t_begin) return;
     const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
     const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
@@ -355,14 +584,14 @@ __device__ __forceinline__ void valu_item_bf16(const DecodeArgs& a, int b, int h
         }
         __syncthreads();
     }
-    write_partial<GQA>(a, st, b, h, item);
+    write_partial<GQA>(a, st, rec);
 }
 
-// Grid (nsplit, Hkv, batch).
 template <int GQA>
-__global__ __launch_bounds__(64) void decode_split_bf16_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64) void decode_valu_bf16_kernel(DecodeArgs a)
 {
-    valu_item_bf16<GQA>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+    walk_units(a, [&](int, int) {},
+               [&](int b, int h, int lo, int hi, float* rec) { valu_item_bf16<GQA>(a, b, h, lo, hi, rec); });
 }
 
 // ---------------------------------------------------------------------------
@@ -386,22 +615,19 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
     const int lane = threadIdx.x & 63;
     if (row >= a.batch * g.Hq) return;
     const int b = row / g.Hq, j = row % g.Hq, h = j / g.gqa, jj = j % g.gqa;
-    const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
-    int k_lo, k_hi, has8;
-    if (g.kind == KV4_KIND_MIXED) {
-        Regions rg = regions_of(n, g.S, g.R);
-        k_lo = g.S / a.split;
-        k_hi = rg.n4 > 0 ? (rg.rec_start + a.split - 1) / a.split : k_lo;
-        has8 = rg.n8 > 0;
-    } else {
-        k_lo = 0;
-        k_hi = (n + a.split - 1) / a.split;
-        has8 = 0;
+    const int bh = b * g.Hkv + h;
+    const Units u = units_of(a, seq_len(a, b));
+    int n4p = 0, w0 = 0;
+    if (u.ntile > 0) {
+        const int2 hd = a.hdr[bh];
+        w0 = clampi(hd.x, 0, a.waves - 1);
+        n4p = clampi(hd.y, w0, a.waves - 1) - w0 + 1;
     }
-    k_hi = min(k_hi, a.nsplit);
-    const int n4p = max(k_hi - k_lo, 0);
-    const int np = n4p + has8;                   // parts to merge: splits k_lo.., then the protected part
-    auto part_of = [&](int i) { return part_ptr(a, b, h, i < n4p ? k_lo + i : a.nsplit, jj); };
+    const int np = n4p + (u.prot > 0);           // the runs of (b, h), then its protected part
+    const int stride = g.d + kPartPad;
+    auto part_of = [&](int i) {
+        return (i < n4p ? rec_ptr(a, (int64_t)bh + w0 + i) : prot_ptr(a, bh)) + jj * stride;
+    };
 
     float zmax = -INFINITY;
     for (int c = 0; c < np; c += 64)

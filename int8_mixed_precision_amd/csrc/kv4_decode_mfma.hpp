@@ -267,17 +267,14 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 // bytes never reach the result.
 // ---------------------------------------------------------------------------
 template <int G>
-__device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int split)
+__device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
+                                              float* rec)
 {
     constexpr int NG = kHeadDim / G;
     const Geo& g = a.g;
     const int lane = threadIdx.x;
     const int n16 = lane & 15, kb = lane >> 4;
     const int jq = n16 >> 2, gq = n16 & 3;       // A row (head, block) of this lane
-    const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
-    const Regions rg = regions_of(n, g.S, g.R);
-    const int t_lo = max(split * a.split, g.S);
-    const int t_hi = min((split + 1) * a.split, rg.rec_start);
     if (t_hi <= t_lo) return;
 
     const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
@@ -562,12 +559,195 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
     const float inv = 1.0f / l;
-    float* dst = part_ptr(a, b, h, split, kb);
+    float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         const int r = s >> 1;
         dst[16 * s + n16] = (ldexpf(O[s][r], 133) + accm[(32 * r) / G]) * inv;
     }
+    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
+}
+
+// Four int8 codes per word (byte i = code i) -> bf16 or fp16 pairs whose bit
+// patterns are the subnormal numbers (code + 128) * 2^-133 (bf16) or
+// (code + 128) * 2^-24 (fp16): pair 0 = codes (0, 2), pair 1 = (1, 3) of w0,
+// pairs 2, 3 the same of w1.  The +128 bias is removed with the sum of the
+// operand it multiplies.
+__device__ __forceinline__ u32x4_t widen_i8(uint32_t w0, uint32_t w1)
+{
+    const uint32_t M = 0x00FF00FFu;
+    const uint32_t x0 = w0 ^ 0x80808080u, x1 = w1 ^ 0x80808080u;
+    u32x4_t r;
+    r[0] = x0 & M;
+    r[1] = (x0 >> 8) & M;
+    r[2] = x1 & M;
+    r[3] = (x1 >> 8) & M;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Protected part of the mixed cache (sink + recent positions, INT8 with one
+// fp16 scale per entry and kv head, KV4-RL Section 5.2), GQA group 4, on the
+// matrix core.  The protected positions occupy ring entries [0, n8); they are
+// walked in tiles of 32 entries (the ring is padded to a multiple of 32).
+//   QK, transposed as for INT4: A = scaled q in fp16, block-diagonal, row n16 =
+//     (head n16/4, block n16%4); MFMA b covers channels 32 kb + 8 b + i of
+//     k-slot (kb, i), so a lane's K operand for all four MFMAs is the 32
+//     contiguous bytes [32 kb, 32 kb + 32) of its token's row.  The score is
+//     s_K * sum_b D[b] (one scale per token, no groups).
+//   PV: A = w = p' s_V (the same for every block row), k = tile entries 8 kb ..
+//     8 kb + 7, split into bf16 hi + lo; B = V codes (ring blocks of 8 entries,
+//     channel-major), column = channel 16 s + n16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h, float* rec)
+{
+    const Geo& g = a.g;
+    const int lane = threadIdx.x;
+    const int n16 = lane & 15, kb = lane >> 4;
+    const int jq = n16 >> 2, gq = n16 & 3;
+    const int n8 = regions_of(seq_len(a, b), g.S, g.R).n8;
+    if (n8 <= 0) return;
+    const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const uint8_t* ring = a.side + (int64_t)a.layer * g.layer_side + ((int64_t)slot * g.Hkv + h) * g.rb;
+    const uint8_t* vreg = ring + (int64_t)g.SR32 * g.d;
+    const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
+    const uint16_t* vsc = ksc + g.SR32;
+
+    // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
+    u32x4_t aqv;
+    float qpart;
+    int sc;
+    {
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
+        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
+        amax = fmaxf(amax, dpp<0xB1>(amax));
+        amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
+        sc = 15 - __builtin_amdgcn_frexp_expf(amax);
+        // k-slot pairs as widen_i8 pairs codes: (0, 2), (1, 3), (4, 6), (5, 7)
+        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[2], sc));
+        aqv[1] = pack_f16(ldexpf(q[1], sc), ldexpf(q[3], sc));
+        aqv[2] = pack_f16(ldexpf(q[4], sc), ldexpf(q[6], sc));
+        aqv[3] = pack_f16(ldexpf(q[5], sc), ldexpf(q[7], sc));
+        qpart = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
+    }
+    // sum of the operand over MFMA block gq's 32 k-slots (row n16), then per D
+    // row (head kb, block r): D starts at -128 * 2^-24 * that sum
+    const float qblk = rows_sum(qpart);
+    f32x4_t dinit;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dinit[r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
+    const float c2 = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
+
+    f32x4_t O[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
+    float m_sh = -INFINITY, l_run = 0.f;
+    __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
+
+    for (int e0 = 0; e0 < n8; e0 += 32) {
+        // ---- loads: K rows of entries e0 + n16, e0 + 16 + n16 (bytes 32 kb ..),
+        // V codes of entries e0 + 8 kb .. + 7 (this lane's 8 channels), scales
+        const uint8_t* kr = ring + (int64_t)(e0 + n16) * g.d + 32 * kb;
+        const uint4 k00 = *reinterpret_cast<const uint4*>(kr);
+        const uint4 k01 = *reinterpret_cast<const uint4*>(kr + 16);
+        const uint4 k10 = *reinterpret_cast<const uint4*>(kr + 16 * g.d);
+        const uint4 k11 = *reinterpret_cast<const uint4*>(kr + 16 * g.d + 16);
+        const uint8_t* vb = vreg + (int64_t)((e0 >> 3) + kb) * (8 * kHeadDim) + 64 * n16;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(vb);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(vb + 16);
+        const uint4 v2 = *reinterpret_cast<const uint4*>(vb + 32);
+        const uint4 v3 = *reinterpret_cast<const uint4*>(vb + 48);
+        const float sk0 = half_bits_to_float(ksc[e0 + n16]);
+        const float sk1 = half_bits_to_float(ksc[e0 + 16 + n16]);
+        const uint4 svp = *reinterpret_cast<const uint4*>(vsc + e0 + 8 * kb);
+
+        // ---- QK
+        f32x4_t D0 = dinit, D1 = dinit;
+        const uint32_t kw0[8] = {k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w};
+        const uint32_t kw1[8] = {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w};
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const uint64_t rows = 0x1111111111111111ull << bb;
+            const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
+                               keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
+            D0 = mfma_f16(A, widen_i8(kw0[2 * bb], kw0[2 * bb + 1]), D0);
+            D1 = mfma_f16(A, widen_i8(kw1[2 * bb], kw1[2 * bb + 1]), D1);
+        }
+        const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
+        float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
+        float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2;
+        s0 = ok0 ? s0 : -INFINITY;
+        s1 = ok1 ? s1 : -INFINITY;
+        const float mx = row16_max(fmaxf(s0, s1));
+        {
+            const bool grow = mx > m_sh + (kPScale + kSlack);
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? mx - kPScale : m_sh;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
+                m_sh = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) O[s][0] *= alpha;
+                W *= alpha;
+            }
+        }
+        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
+        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
+        l_run += p0 + p1;
+        pbuf8[kb][n16] = p0;
+        pbuf8[kb][16 + n16] = p1;
+        __builtin_amdgcn_wave_barrier();
+        const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb]);
+        const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb + 4]);
+
+        // ---- PV: w = p' s_V of head jq, entries e0 + 8 kb + e
+        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // entries past the end may hold garbage scales: select, do not multiply
+            const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
+            wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
+        }
+        u32x4_t ahi, alo;
+        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hw, lw;
+            split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
+            ahi[i] = hw;
+            alo[i] = lw;
+        }
+        const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4_t bv = widen_i8(vw[2 * s], vw[2 * s + 1]);
+            O[s] = mfma_bf16(ahi, bv, O[s]);
+            O[s] = mfma_bf16(alo, bv, O[s]);
+        }
+        W = mfma_bf16(ahi, ones, W);
+        W = mfma_bf16(alo, ones, W);
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- epilogue: lane l holds head kb, channels 16 s + n16 (every block row
+    // of D carries the same value; row 0 is used)
+    const float l = row16_sum(l_run);
+    const float inv = 1.0f / l;
+    float* dst = rec + kb * (g.d + kPartPad);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (ldexpf(O[s][0], 133) - 128.0f * W[0]) * inv;
     if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
@@ -579,15 +759,13 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 //       parts 2-3 zero;
 //       columns = channels 16 s + n16; k = tokens 8 kb .. 8 kb + 7 in order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h, int split)
+__device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
+                                               float* rec)
 {
     const Geo& g = a.g;
     const int lane = threadIdx.x;
     const int n16 = lane & 15, kb = lane >> 4;
     const int jq = n16 >> 2, gq = n16 & 3;
-    const int n = clampi(a.seq_lens[b], 0, a.max_ctx);
-    const int t_lo = split * a.split;
-    const int t_hi = min((split + 1) * a.split, n);
     if (t_hi <= t_lo) return;
     const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
     const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
@@ -684,31 +862,26 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
     __syncthreads();
     const float lj = sh_l[kb];
     const float inv = 1.0f / lj;
-    float* dst = part_ptr(a, b, h, split, kb);
+    float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (O[s][0] + O[s][1]) * inv;
     if (n16 == 0) dst[g.d] = sh_m[kb] + log2f(lj);
 }
 
-// One 1-D grid over work items: the protected parts of every (sequence, kv
-// head) first, then split-major: all first INT4 splits, all second splits, ...
-// so that the vector-ALU protected parts overlap the INT4 work instead of
-// forming a tail.
+// Grid = W one-wave workgroups, each walking its range of the balanced unit
+// partition: protected parts on the vector ALU, runs of INT4 tiles on the
+// matrix core.
 template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
-    const int nbh = a.batch * a.g.Hkv;
-    const int unit = blockIdx.x / nbh, bh = blockIdx.x % nbh;
-    const int b = bh / a.g.Hkv, h = bh % a.g.Hkv;
-    if (unit == 0) valu_item_kv4<4>(a, b, h, a.nsplit);
-    else mfma_item_kv4<G>(a, b, h, unit - 1);
+    walk_units(a, [&](int b, int h) { mfma_prot_kv4(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec) { mfma_item_kv4<G>(a, b, h, lo, hi, rec); });
 }
 
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)
 {
-    const int nbh = a.batch * a.g.Hkv;
-    const int split = blockIdx.x / nbh, bh = blockIdx.x % nbh;
-    mfma_item_bf16(a, bh / a.g.Hkv, bh % a.g.Hkv, split);
+    walk_units(a, [&](int, int) {},
+               [&](int b, int h, int lo, int hi, float* rec) { mfma_item_bf16(a, b, h, lo, hi, rec); });
 }
 
 }  // namespace kv4

@@ -15,8 +15,21 @@ def pb_bytes(d: int, G: int) -> int:
     return PAGE * d // 2 + PAGE * d // 2 + 4 * 2 * PAGE * ng
 
 
+def sr32(SR: int) -> int:
+    """Ring entries, padded to a multiple of 32."""
+    return -(-SR // 32) * 32
+
+
 def rb_bytes(d: int, SR: int) -> int:
-    return 0 if SR == 0 else -(-SR * (2 * d + 4) // 16) * 16
+    return 0 if SR == 0 else sr32(SR) * (2 * d + 4)
+
+
+def ring_vbyte(e, c, d: int = 128):
+    """Byte of channel c of ring entry e in the V code region: blocks of 8
+    entries, channel-major, channels ordered c % 16 then c // 16."""
+    e = np.asarray(e, np.int64)
+    c = np.asarray(c, np.int64)
+    return (e // 8) * (8 * d) + ((c % 16) * 8 + c // 16) * 8 + e % 8
 
 
 def ring_entry(p: np.ndarray, S: int, R: int) -> np.ndarray:
@@ -79,14 +92,15 @@ def gather_mixed(pages: np.ndarray, side, *, layer, num_pages, Hkv, d, G, S, R, 
         pp = p[protected_mask]
         e = ring_entry(pp, S, R)
         rbase = ((layer * max_slots + slot) * Hkv + h[None, :]) * RB                  # [1, Hkv]
+        E = sr32(SR)
         kk = side[rbase[:, :, None] + (e[:, None, None] * d) + np.arange(d)[None, None, :]]
-        vv = side[rbase[:, :, None] + ((SR + e)[:, None, None] * d) + np.arange(d)[None, None, :]]
+        vv = side[rbase[:, :, None] + E * d + ring_vbyte(e[:, None, None], np.arange(d)[None, None, :], d)]
         k8[protected_mask] = kk.view(np.int8)
         v8[protected_mask] = vv.view(np.int8)
-        sb = rbase + 2 * SR * d
+        sb = rbase + 2 * E * d
         ks = side[sb + 2 * e[:, None]].astype(np.uint16) | (side[sb + 2 * e[:, None] + 1].astype(np.uint16) << 8)
-        vs = side[sb + 2 * (SR + e)[:, None]].astype(np.uint16) | (
-            side[sb + 2 * (SR + e)[:, None] + 1].astype(np.uint16) << 8)
+        vs = side[sb + 2 * (E + e)[:, None]].astype(np.uint16) | (
+            side[sb + 2 * (E + e)[:, None] + 1].astype(np.uint16) << 8)
         k8s[protected_mask] = ks
         v8s[protected_mask] = vs
     out.update(k8=k8, v8=v8, k8s=k8s, v8s=v8s)

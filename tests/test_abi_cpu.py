@@ -58,7 +58,7 @@ def test_storage_sizes_match_pages():
     # side ring: (S + R) entries of 2*d + 4 bytes per (slot, kv head)
     d = kv4.make_desc(2, 32, 8, sink=4, recent=128, num_pages=7, max_slots=5, max_pages_per_seq=3)
     pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
-    assert side == 2 * 5 * 8 * L.rb_bytes(128, 132) and L.rb_bytes(128, 132) == 132 * 260
+    assert side == 2 * 5 * 8 * L.rb_bytes(128, 132) and L.rb_bytes(128, 132) == 160 * 260
     assert pages == 2 * 7 * 8 * 2560
 
 
@@ -85,7 +85,8 @@ def test_invalid_descriptors():
         (dict(kind=7), kv4.KV4_ERR_INVALID_ARG),
         (dict(flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
         (dict(flags=0x10), kv4.KV4_ERR_INVALID_ARG),
-        (dict(split_tokens=48), kv4.KV4_ERR_INVALID_ARG),
+        (dict(num_waves=-1), kv4.KV4_ERR_INVALID_ARG),
+        (dict(num_waves=(1 << 16) + 1), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_q_heads=48, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
     ]
@@ -153,6 +154,7 @@ def test_append_and_decode_validation_no_launch():
     assert call(out=None) == kv4.KV4_ERR_INVALID_ARG
     assert call(ws=None) == kv4.KV4_ERR_WORKSPACE
     assert call(wsb=ws - 1) == kv4.KV4_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 8)) == kv4.KV4_ERR_INVALID_ARG   # not 16-aligned
     assert call(batch=0) == kv4.KV4_OK
 
     # the two phases validate the same way
@@ -184,20 +186,38 @@ def test_append_and_decode_validation_no_launch():
     kv4.kv4_cache_free(h)
 
 
-def test_split_plan_and_workspace():
-    h, d, _, _ = _fake_handle(split_tokens=64, max_pages_per_seq=64)
-    T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
-    assert T == 64 and ns == 1024 // 64
-    ws = kv4.kv4_decode_workspace_bytes(h, 3, 1024)
-    assert ws == 3 * 2 * (ns + 1) * 4 * (128 + 4) * 4
+def test_wave_plan_and_workspace():
+    # explicit wave count: run records for batch*Hkv + W, protected records for
+    # batch*Hkv, and a (first, last) int32 pair per (sequence, kv head)
+    h, d, _, _ = _fake_handle(num_waves=64, max_pages_per_seq=64)
+    assert kv4.kv4_decode_waves(h) == 64
+    B, Hkv, gqa = 3, 2, 4
+    ws = kv4.kv4_decode_workspace_bytes(h, B, 1024)
+    assert ws == (2 * B * Hkv + 64) * gqa * (128 + 4) * 4 + B * Hkv * 8
+    assert kv4.kv4_decode_workspace_bytes(h, B, 16) == ws       # independent of max_ctx
     kv4.kv4_cache_free(h)
+    # automatic: 16 waves per compute unit (256 assumed without a device)
     h, d, _, _ = _fake_handle(max_pages_per_seq=64)
-    T, ns = kv4.kv4_decode_split_info(h, 3, 1024)
-    assert T % 32 == 0 and 256 <= T <= 1024 and ns * T >= 1024
+    w = kv4.kv4_decode_waves(h)
+    assert w % 16 == 0 and w >= 16
     kv4.kv4_cache_free(h)
-    # a work item spans at most 2048 tokens, whatever the descriptor asks for
-    h, d, _, _ = _fake_handle(split_tokens=8192, max_pages_per_seq=1024)
-    assert kv4.kv4_decode_split_info(h, 3, 16384) == (2048, 8)
+
+
+def test_partition_capacity_bound():
+    """batch * Hkv * (ceil(max_ctx / 32) + 1 + ceil((S + R) / 32)) must stay
+    below 2^30 (the partition's 32-bit counts)."""
+    base = dict(num_layers=1, num_q_heads=8, num_kv_heads=2, num_pages=4, max_slots=4096,
+                max_pages_per_seq=1 << 22)
+    d = kv4.make_desc(**base)
+    pages, side, _ = kv4.kv4_cache_required_bytes(d)
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)
+    assert kv4.lib().kv4_cache_create(ctypes.byref(d), fake, pages, fake, side, ctypes.byref(h)) == 0
+    n = ctypes.c_size_t()
+    ok = kv4.lib().kv4_decode_workspace_bytes(h, 4096, 1 << 16, ctypes.byref(n))
+    assert ok == kv4.KV4_OK                     # 4096 * 2 * (2048 + 6) < 2^30
+    big = kv4.lib().kv4_decode_workspace_bytes(h, 4096, 1 << 22, ctypes.byref(n))
+    assert big == kv4.KV4_ERR_CAPACITY          # 4096 * 2 * (131072 + 6) >= 2^30
     kv4.kv4_cache_free(h)
 
 

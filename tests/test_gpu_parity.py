@@ -60,7 +60,7 @@ def _compare_bytes(built, pages, side, layer, oc, S, R, seqs=None, n_of=None):
                 raise AssertionError(f"seq {b} {name} mismatch at protected row {tuple(bad)}")
 
 
-def _run_case(Hq, Hkv, G, S, R, ctx, seed, split=0, layers=1, layer=0, check_bytes=True,
+def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_bytes=True,
               garbage=True):
     """Build a cache for contexts ctx (history + one step token), decode, and
     compare with the oracle.  Returns (built, output, oracle cache)."""
@@ -69,7 +69,7 @@ def _run_case(Hq, Hkv, G, S, R, ctx, seed, split=0, layers=1, layer=0, check_byt
     n = np.asarray(ctx, np.int64) + 1
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
-    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, split=split, seed=seed)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, seed=seed)
     if garbage:
         _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
@@ -107,17 +107,50 @@ def test_tiny_config():
     assert np.array_equal(outb, ref)
 
 
-def test_decode_phases_and_workspace_layout():
+def _partition(n, S, R, Hkv, W, min_units=8):
+    """The documented partition of one decode launch, written out on the host:
+    per (b, h) its tile count and the (first, last) wave running its tiles."""
+    tiles, prot = [], []
+    for nb in n:
+        rec = max(S, nb - R)
+        tiles.append(-(-rec // 32) - S // 32 if rec > S else 0)
+        prot.append(1 if min(S, nb) + max(nb - rec, 0) > 0 else 0)
+    prot_units = -(-(S + R) // 32)
+    T4, P = sum(tiles) * Hkv, sum(prot) * Hkv
+    weight = T4 + prot_units * P
+    Wn = min(W, max(1, -(-weight // min_units)))
+    balanced = weight // Wn >= prot_units * (-(-P // Wn)) + 1
+    Wt = max(1, min(Wn, T4))
+    def tbeg(w):
+        return w * weight // Wn - prot_units * (w * P // Wn) if balanced else min(w, Wt) * T4 // Wt
+    starts = [tbeg(w) for w in range(Wn + 1)]
+    assert starts == sorted(starts) and starts[0] == 0 and starts[-1] == T4
+    def wave_of(x):
+        w = max(w for w in range(Wn) if starts[w] <= x)
+        assert starts[w] < starts[w + 1]          # the wave holding x runs it
+        return w
+    out, x = {}, 0
+    for b, nb in enumerate(n):
+        for h in range(Hkv):
+            if tiles[b]:
+                out[(b, h)] = (wave_of(x), wave_of(x + tiles[b] - 1))
+            x += tiles[b]
+    return out, tiles, prot
+
+
+@pytest.mark.parametrize("waves", [7, 0])
+def test_decode_phases_and_workspace_layout(waves):
     """kv4_decode_partials followed by kv4_decode_merge equals kv4_decode_attn
-    bit for bit, and the workspace holds the parts its header documents: part
-    k < nsplit = INT4 positions [kT, (k+1)T), part nsplit = protected region,
-    float d = base-2 log-normaliser.  Merging the parts on the host by eq. A1
-    in fp64 reproduces the output, and the merged log-normaliser equals the
-    oracle's log2 sum of 2^(sm_scale log2(e) q.k^) over the whole context."""
+    bit for bit, and the workspace holds what its header documents: the runs of
+    (b, h) at records b*Hkv + h + w for w = first .. last (as the documented
+    partition gives them), the protected part at its own record, float d the
+    base-2 log-normaliser.  Merging the parts on the host by eq. A1 in fp64
+    reproduces the output, and the merged log-normaliser equals the oracle's
+    log2 sum of 2^(sm_scale log2(e) q.k^) over the whole context."""
     Hq, Hkv, G, S, R = 8, 2, 32, 4, 64
     ctx = [0, 3, 40, 67, 68, 69, 300, 1000, 2500]
-    H.log("case decode phases: 8q/2kv G=32 S=4 R=64 split 256")
-    built, out, oc, q, want = _run_case(Hq, Hkv, G, S, R, ctx, seed=11, split=256)
+    H.log(f"case decode phases: 8q/2kv G=32 S=4 R=64 waves {waves}")
+    built, out, oc, q, want = _run_case(Hq, Hkv, G, S, R, ctx, seed=11, waves=waves)
     n = np.asarray(ctx) + 1
     B, d, gqa = len(n), 128, Hq // Hkv
     dev = torch.device("cuda")
@@ -133,26 +166,35 @@ def test_decode_phases_and_workspace_layout():
     kv4.kv4_decode_merge(built.cache.handle, nd, B, max_ctx, o2, kv4.KV4_OUT_F32, ws)
     torch.cuda.synchronize()
     assert np.array_equal(o2.cpu().numpy(), out)
-    T, ns = kv4.kv4_decode_split_info(built.cache.handle, B, max_ctx)
-    assert T == 256
-    parts = ws[:B * Hkv * (ns + 1) * gqa * (d + 4) * 4].view(torch.float32).cpu().numpy()
-    parts = parts.reshape(B, Hkv, ns + 1, gqa, d + 4).astype(np.float64)
+    W = kv4.kv4_decode_waves(built.cache.handle)
+    if waves:
+        assert W == waves
+    nrec = 2 * B * Hkv + W
+    rec = ws[:nrec * gqa * (d + 4) * 4].view(torch.float32).cpu().numpy()
+    rec = rec.reshape(nrec, gqa, d + 4).astype(np.float64)
+    hdr = ws[nrec * gqa * (d + 4) * 4:nrec * gqa * (d + 4) * 4 + B * Hkv * 8].view(torch.int32)
+    hdr = hdr.cpu().numpy().reshape(B * Hkv, 2)
+    want_hdr, tiles, prot = _partition(n, S, R, Hkv, W)
     c2 = sm / math.log(2.0)
     for b in range(B):
         nb = int(n[b])
-        rec = max(S, nb - R)
-        used = [k for k in range(ns) if max(k * T, S) < min((k + 1) * T, rec)]
-        if min(S, nb) + max(nb - rec, 0) > 0:
-            used.append(ns)
         sl = oc.seq(b)
-        prot = np.array([oracle.is_protected(p, nb, S, R) for p in range(nb)])
-        k_hat = np.where(prot[:, None, None],
+        prot_mask = np.array([oracle.is_protected(p, nb, S, R) for p in range(nb)])
+        k_hat = np.where(prot_mask[:, None, None],
                          oracle.dequant_int8(oc.k8[sl][:nb], oc.k8s[sl][:nb]),
                          oracle.dequant_int4(oc.k4[sl][:nb], oc.k4d[sl][:nb], oc.k4m[sl][:nb], G))
         for h in range(Hkv):
+            bh = b * Hkv + h
+            used = []
+            if tiles[b]:
+                first, last = (int(v) for v in hdr[bh])
+                assert (first, last) == want_hdr[(b, h)], (b, h, first, last, want_hdr[(b, h)])
+                used += [bh + w for w in range(first, last + 1)]
+            if prot[b]:
+                used.append(B * Hkv + W + bh)
             for j in range(gqa):
-                z = parts[b, h, used, j, d]
-                o = parts[b, h, used, j, :d]
+                z = rec[used, j, d]
+                o = rec[used, j, :d]
                 assert np.all(np.isfinite(z)) and np.all(np.isfinite(o))
                 w = np.exp2(z - z.max())
                 merged = (w[:, None] * o).sum(0) / w.sum()
@@ -185,26 +227,27 @@ def test_group_64_and_multi_layer():
     _run_case(8, 2, 64, 4, 32, [33, 150, 401], seed=77, layers=3, layer=2)
 
 
-# Self-agreement bound across split sizes.  The merge (eq. A1) is exact up to
-# rounding; what changes with the split is the fp32 rounding order.  The PV
-# accumulator sums w*(16 + c) (the +16 comes from widening 4-bit codes to bf16
-# exactly) over up to n/32 tile additions, so one path deviates from the exact
-# value by about sqrt(n/32) * 2^-24 * 31 * max(Delta_V) <= ~1e-5 at n = 2,500,
-# plus 2^-18 relative rounding of the bf16 hi+lo operand.  Two paths: 5e-5.
+# Self-agreement bound across wave counts.  The merge (eq. A1) is exact up to
+# rounding; what changes with the cut is the fp32 rounding order.  The PV
+# accumulator sums w * code (codes enter the matrix core exactly) over up to
+# n/32 tile additions, so one path deviates from the exact value by about
+# sqrt(n/32) * 2^-24 * 15 * max(Delta_V) <= ~1e-5 at n = 2,500, plus 2^-18
+# relative rounding of the bf16 hi+lo operand.  Two paths: 5e-5.
 SPLIT_SELF_TOL = 5e-5
 
 
-def test_split_invariance():
-    """Context splits merged by eq. A1 give the same output for any split size."""
+def test_wave_invariance():
+    """The partition's pieces merged by eq. A1 give the same output for any
+    number of waves (one wave running everything, to more waves than units)."""
     ctx = [0, 3, 70, 300, 1000, 2500]
     outs = {}
-    for split in (32, 64, 1024, 0, 8192):
-        H.log(f"case split={split}")
-        _, out, _, _, _ = _run_case(8, 2, 32, 4, 64, ctx, seed=5, split=split)
-        outs[split] = out
-    ref = outs[8192]          # one split covers every INT4 region here
-    for split, o in outs.items():
-        assert np.abs(o - ref).max() <= SPLIT_SELF_TOL, (split, float(np.abs(o - ref).max()))
+    for waves in (1, 2, 7, 64, 0, 5000):
+        H.log(f"case waves={waves}")
+        _, out, _, _, _ = _run_case(8, 2, 32, 4, 64, ctx, seed=5, waves=waves)
+        outs[waves] = out
+    ref = outs[1]             # one wave: one run per (sequence, kv head)
+    for waves, o in outs.items():
+        assert np.abs(o - ref).max() <= SPLIT_SELF_TOL, (waves, float(np.abs(o - ref).max()))
 
 
 def test_bulk_equals_token_by_token():
@@ -321,9 +364,9 @@ def test_bf16_comparator():
     cfg = W.scaled(W.CONFIGS["tiny"], seed=31, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx))
     ks, vs = W.all_kv_sources(cfg, 0, n)
     q = W.queries(cfg, 0)
-    for split in (0, 64):
-        H.log(f"case bf16 comparator split={split}")
-        built = H.make_cache(Hq, Hkv, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, split=split, seed=4)
+    for waves in (0, 3):
+        H.log(f"case bf16 comparator waves={waves}")
+        built = H.make_cache(Hq, Hkv, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, waves=waves, seed=4)
         _fill_garbage(built)
         H.build_from_sources(built, 0, ks, vs, ctx)
         out = H.decode(built, 0, q, n).cpu().numpy()

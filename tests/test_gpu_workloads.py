@@ -1,5 +1,5 @@
 """GPU parity on the full-size synthetic workloads (KV4-RL Qwen3-shaped decode
-states), in the launch configuration the benchmark times (automatic split,
+states), in the launch configuration the benchmark times (automatic wave count,
 max_ctx = the longest sequence).
 
   * Qwen3-4B shape, batch 64 (lognormal median 2k): every sequence, bytes and
