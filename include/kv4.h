@@ -190,8 +190,8 @@ int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, s
  * q head j reads kv head j / (Hq / Hkv).  Protected positions of an n-token
  * context are [0, min(S, n)) and [max(S, n - R), n); all others read INT4.
  * Errors: KV4_ERR_INVALID_ARG, KV4_ERR_CAPACITY (also when batch * Hkv *
- * (ceil(max_ctx / 32) + 1 + ceil((S + R) / 32)) >= 2^30, the bound of the
- * partition's 32-bit counts), KV4_ERR_WORKSPACE, KV4_ERR_HIP.
+ * (ceil(max_ctx / 32) + 1 + U8) >= 2^30, the bound of the partition's 32-bit
+ * counts), KV4_ERR_WORKSPACE, KV4_ERR_HIP.
  */
 int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
                     const int32_t* slot_ids, const int32_t* block_tables, int batch,
@@ -209,7 +209,8 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
  * kv4_decode_partials runs the whole step's work as one sequence of units:
  * for each (sequence b, kv head h), bh = b*Hkv + h in increasing order, its
  * protected part (if non-empty; one indivisible unit of weight U8 =
- * ceil((S + R) / 32), its 32-entry tiles) and then the
+ * (5 * ceil((S + R) / 32) + 1) / 2 tiles, the measured cost of its 32-entry
+ * INT8 tiles) and then the
  * 32-token tiles of its INT4 region [S, max(S, n - R)) (tile t covers positions
  * [32t, 32t + 32) clipped to the region).  With U units in total and
  * P protected parts, T4 tiles, weight U = T4 + U8 * P and W' = min(W,

@@ -115,7 +115,7 @@ def _partition(n, S, R, Hkv, W, min_units=8):
         rec = max(S, nb - R)
         tiles.append(-(-rec // 32) - S // 32 if rec > S else 0)
         prot.append(1 if min(S, nb) + max(nb - rec, 0) > 0 else 0)
-    prot_units = -(-(S + R) // 32)
+    prot_units = (5 * -(-(S + R) // 32) + 1) // 2 if S + R > 0 else 0
     T4, P = sum(tiles) * Hkv, sum(prot) * Hkv
     weight = T4 + prot_units * P
     Wn = min(W, max(1, -(-weight // min_units)))
