@@ -258,8 +258,11 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 //     kb, and the score follows in-lane.
 //   PV: A = w = p' Delta_V, row n16 = (head n16/4, block n16%4), k = tile
 //     tokens 8 kb .. 8 kb + 7, split into bf16 hi + lo; B = V codes as bf16
-//     subnormals, column = channel 16 s + n16.  D row (head kb, block r), so
-//     lane l accumulates head kb's output for channel 16 s + n16 in O[s][s/2];
+//     subnormals.  Only D row (head, block r) of the accumulator for channels
+//     32 r + 16 h + n16 is wanted, so each of the four blocks keeps the A rows
+//     of its own block (the rest are zeroed) and two accumulators E[0], E[1]
+//     cover all 128 channels: lane l holds head kb, channel 32 r + 16 h + n16
+//     in E[h][r];
 //     the m_V term sum p' m is accumulated on the vector ALU in the QK layout.
 //   Probabilities move from the QK layout to the PV layout through LDS.
 // Masking: tokens outside the work item (and never-written slots of a page)
@@ -329,9 +332,8 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     }
     const float c2 = ldexpf(a.scale2, -sc_d);
 
-    f32x4_t O[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // E[h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
+    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     float accm[NG];
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) accm[gg] = 0.f;
@@ -449,7 +451,7 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
                 for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) O[s][s >> 1] *= alpha;
+                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
             }
         }
 
@@ -518,10 +520,18 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
         const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const u32x4_t bv = widen_v(vcw[s]);
-            O[s] = mfma_bf16(ahi, bv, O[s]);
-            O[s] = mfma_bf16(alo, bv, O[s]);
+        for (int blk = 0; blk < 4; ++blk) {
+            // rows of block blk only: each accumulator row gathers its own block
+            const uint64_t rows = 0x1111111111111111ull << blk;
+            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+            const u32x4_t b0 = widen_v(vcw[2 * blk]), b1 = widen_v(vcw[2 * blk + 1]);
+            E[0] = mfma_bf16(bh, b0, E[0]);
+            E[1] = mfma_bf16(bh, b1, E[1]);
+            E[0] = mfma_bf16(bl, b0, E[0]);
+            E[1] = mfma_bf16(bl, b1, E[1]);
         }
     };
 
@@ -554,16 +564,16 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         if (tl < tile_end) advance(tl, std::false_type{});
     }
 
-    // ---- epilogue: lane l holds head kb, channels 16 s + n16
+    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
     const float l = row16_sum(l_run);
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
     const float inv = 1.0f / l;
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int r = s >> 1;
-        dst[16 * s + n16] = (ldexpf(O[s][r], 133) + accm[(32 * r) / G]) * inv;
+    for (int r = 0; r < 4; ++r) {
+        dst[32 * r + n16] = (ldexpf(E[0][r], 133) + accm[(32 * r) / G]) * inv;
+        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) + accm[(32 * r) / G]) * inv;
     }
     if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
@@ -597,7 +607,9 @@ __device__ __forceinline__ u32x4_t widen_i8(uint32_t w0, uint32_t w1)
 //     s_K * sum_b D[b] (one scale per token, no groups).
 //   PV: A = w = p' s_V (the same for every block row), k = tile entries 8 kb ..
 //     8 kb + 7, split into bf16 hi + lo; B = V codes (ring blocks of 8 entries,
-//     channel-major), column = channel 16 s + n16.
+//     channel-major).  The accumulators are compacted as in the INT4 item:
+//     block r's MFMAs keep the A rows of block r and cover channels 32 r +
+//     16 h + n16 in E[h][r].
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h, float* rec)
 {
@@ -645,9 +657,8 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
     for (int r = 0; r < 4; ++r) dinit[r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
     const float c2 = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
 
-    f32x4_t O[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // E[h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
+    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
     f32x4_t W = {0.f, 0.f, 0.f, 0.f};
     float m_sh = -INFINITY, l_run = 0.f;
     __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
@@ -696,7 +707,7 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
                 m_sh = m_new;
                 l_run *= alpha;
 #pragma unroll
-                for (int s = 0; s < 8; ++s) O[s][0] *= alpha;
+                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
                 W *= alpha;
             }
         }
@@ -731,23 +742,34 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
         const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
                                  v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const u32x4_t bv = widen_i8(vw[2 * s], vw[2 * s + 1]);
-            O[s] = mfma_bf16(ahi, bv, O[s]);
-            O[s] = mfma_bf16(alo, bv, O[s]);
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint64_t rows = 0x1111111111111111ull << blk;
+            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+            const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
+            const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
+            E[0] = mfma_bf16(bh, b0, E[0]);
+            E[1] = mfma_bf16(bh, b1, E[1]);
+            E[0] = mfma_bf16(bl, b0, E[0]);
+            E[1] = mfma_bf16(bl, b1, E[1]);
         }
         W = mfma_bf16(ahi, ones, W);
         W = mfma_bf16(alo, ones, W);
         __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- epilogue: lane l holds head kb, channels 16 s + n16 (every block row
-    // of D carries the same value; row 0 is used)
+    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
+    // (every block row of W carries the same sum; row 0 is used)
     const float l = row16_sum(l_run);
     const float inv = 1.0f / l;
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (ldexpf(O[s][0], 133) - 128.0f * W[0]) * inv;
+    for (int r = 0; r < 4; ++r) {
+        dst[32 * r + n16] = (ldexpf(E[0][r], 133) - 128.0f * W[0]) * inv;
+        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) - 128.0f * W[0]) * inv;
+    }
     if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
