@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--config", default="q8b256")
     ap.add_argument("--waves", type=int, default=0,
                     help="waves of the decode partition (0 = the library's choice, 16 per CU)")
+    ap.add_argument("--pool-chunks", type=int, default=0,
+                    help="most chunks of the decode's dynamic pool (0 = none, the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -221,11 +223,13 @@ def main():
     log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
 
     kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                        seed=cfg.seed, waves=args.waves, device="cuda:0")
+                        seed=cfg.seed, waves=args.waves, pool_chunks=args.pool_chunks,
+                        device="cuda:0")
     caches = [("kv4", kv4c)]
     if not args.no_bf16:
         bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                           kind=kv4.KV4_KIND_BF16, waves=args.waves, device="cuda:0")
+                           kind=kv4.KV4_KIND_BF16, waves=args.waves,
+                           pool_chunks=args.pool_chunks, device="cuda:0")
         caches.append(("bf16", bfc))
     # build every cache from the same sources, sequence chunk by chunk
     step_k, step_v = [], []
@@ -257,7 +261,7 @@ def main():
     for name, c in caches:
         out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
         ws = c.cache.workspace(B, max_ctx)
-        waves = kv4.kv4_decode_waves(c.cache.handle)
+        waves, chunks = kv4.kv4_decode_partition(c.cache.handle)
 
         def append():
             kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B,
@@ -305,10 +309,10 @@ def main():
                              decode_ms_p10=float(np.percentile(td, 10)),
                              decode_ms_p90=float(np.percentile(td, 90)),
                              wall_ms_per_step=wall * 1e3 / args.steps,
-                             waves=waves)
+                             waves=waves, pool_chunks=chunks)
         log(f"{name}: append {ta.mean() * 1e3:.1f} us, partials {tp.mean() * 1e3:.1f} us, "
             f"merge {tm.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
-            f"(median {np.median(td) * 1e3:.1f}), waves {waves}")
+            f"(median {np.median(td) * 1e3:.1f}), waves {waves}, pool chunks {chunks}")
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -353,7 +357,7 @@ def main():
                         "page 16, INT4 group 32, S=4, R=128",
             "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
-            "waves": r["waves"],
+            "waves": r["waves"], "pool_chunks": r["pool_chunks"],
         },
         "decode_attn_gbs": round(decode_gbs, 2),
         "decode_attn_pct_hbm_peak": round(100 * decode_gbs / HBM_PEAK_GBS, 2),

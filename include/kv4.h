@@ -100,6 +100,9 @@ typedef struct kv4_cache_desc {
     int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
                                    partition; 0 = 16 per compute unit of the
                                    current device, else 1 .. 65536 */
+    int32_t pool_chunks;        /* most chunks of the decode's dynamic pool: 0 = no
+                                   pool (the default), else a power of two in
+                                   8 .. 65536 */
 } kv4_cache_desc;
 
 typedef struct kv4_cache kv4_cache;  /* opaque host-side handle */
@@ -162,8 +165,9 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
 /*
  * Workspace bytes kv4_decode_attn needs for `batch` sequences (validated
  * against max_ctx, which does not change the size): the per-part outputs and
- * log-normalisers of the partition/merge, ((2*batch*Hkv + W) * (Hq/Hkv) *
- * (d + 4)) float32 plus batch*Hkv int32 pairs, W = kv4_decode_waves.  Queries
+ * log-normalisers of the partition/merge, ((2*batch*Hkv + W + C) * (Hq/Hkv) *
+ * (d + 4)) float32 plus batch*Hkv int32 pairs, rounded up to 256 bytes, plus
+ * 2 KiB of pool counters (W, C as kv4_decode_partition gives them).  Queries
  * the current device's compute-unit count; launches nothing.
  */
 int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, size_t* bytes);
@@ -175,9 +179,9 @@ int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, s
  * protected region (sink + recent, read from the INT8 ring) is one more part;
  * each part yields a locally normalised output and log-normaliser, and a merge
  * kernel combines them by a stable log-sum-exp with zero weight for empty
- * parts.  The cut is a balanced partition of the whole batch's work over W
- * waves (see kv4_decode_partials), so every wave gets the same number of tiles
- * whatever the length mix.
+ * parts.  The cut is a partition of the whole batch's work over W waves (see
+ * kv4_decode_partials): balanced static shares, optionally followed by a
+ * pool of chunks that the waves take as they finish.
  *
  *   q_bf16      [batch][Hq][d] bf16 (after RoPE)
  *   seq_lens    [batch] int32, n = context length after this step's append
@@ -206,31 +210,44 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
  * context split over several devices yields parts of one (sequence, head)
  * that combine by the same eq. A1 of KV4-RL Appendix A.3).
  *
- * kv4_decode_partials runs the whole step's work as one sequence of units:
+ * kv4_decode_partials runs the whole step's work over W waves.  The work is,
  * for each (sequence b, kv head h), bh = b*Hkv + h in increasing order, its
- * protected part (if non-empty; one indivisible unit of weight U8 =
+ * protected part (if non-empty; indivisible, of weight U8 =
  * (5 * ceil((S + R) / 32) + 1) / 2 tiles, the measured cost of its 32-entry
- * INT8 tiles) and then the
- * 32-token tiles of its INT4 region [S, max(S, n - R)) (tile t covers positions
- * [32t, 32t + 32) clipped to the region).  With U units in total and
- * P protected parts, T4 tiles, weight U = T4 + U8 * P and W' = min(W,
- * ceil(U / 8)) waves in use, wave w runs protected parts [floor(w P / W'),
- * floor((w+1) P / W')) and tiles [t(w), t(w+1)) of the tile sequence, t(w) =
- * floor(w U / W') - U8 * floor(w P / W') (every wave the same weight); when
- * that is not increasing in w, t(w) = floor(min(w, W4) T4 / W4) with W4 =
- * max(1, min(W', T4)) instead.  Each maximal run of tiles of one bh in a
- * wave's range is one part.  Workspace, float32
- * records of (Hq/Hkv) rows of d + 4 floats (row j: floats [0, d) the
- * softmax-normalised output of q head h*(Hq/Hkv) + j over the part, float d its
- * base-2 log-normaliser z = max + log2(sum) of the scores scaled by
- * sm_scale*log2(e)):
- *     run records        [batch*Hkv + W]  the run of bh by wave w at bh + w
+ * INT8 tiles) and the 32-token tiles of its INT4 region [S, max(S, n - R))
+ * (tile t covers positions [32t, 32t + 32) clipped to the region); T4 tiles
+ * and P protected parts in all, W' = min(W, ceil((T4 + U8 P) / 8)) waves in
+ * use.  The tile sequence is cut into shares:
+ *   - a pool of the last Tp = floor(3 T4 / 16) tiles in Cd chunks, Cd the
+ *     largest power of two <= the cache's pool chunk count with 2 Cd <= Tp
+ *     (no pool, Tp = 0, when that is below 8); with A = Tp - Cd, chunk c is
+ *     pool tiles [g(c), g(c+1)), g(c) = c + A - floor(A (Cd - c)^2 / Cd^2);
+ *   - static shares over the first Ts = T4 - Tp tiles: wave w runs protected
+ *     parts [floor(w P / W'), floor((w+1) P / W')) and tiles [t(w), t(w+1)),
+ *     t(w) = floor(w (Ts + U8 P) / W') - U8 floor(w P / W') (every wave the same
+ *     weight); when that is not increasing in w, t(w) = floor(min(w, W4) Ts /
+ *     W4) with W4 = max(1, min(W', Ts)) instead;
+ *   - share s < S0 (S0 = W', or W4 in the second case) is static share s,
+ *     share S0 + c is chunk c.  A wave runs its static share, then takes chunks
+ *     (chunk c is ticket c / 8 of atomic counter c % 8 in the workspace) until
+ *     none is left.
+ * Each maximal run of tiles of one bh in a share is one part.  Which wave runs
+ * a share changes nothing in its results, so the output is the same from run
+ * to run.  Workspace (16-byte aligned), float32 records of (Hq/Hkv) rows of
+ * d + 4 floats (row j: floats [0, d) the softmax-normalised output of q head
+ * h*(Hq/Hkv) + j over the part, float d its base-2 log-normaliser z = max +
+ * log2(sum) of the scores scaled by sm_scale*log2(e)):
+ *     run records        [batch*Hkv + W + C]  the run of bh in share s at bh + s
+ *                        (C = kv4_decode_partition's pool chunk count)
  *     protected records  [batch*Hkv]      the protected part of bh at bh
- *     header             [batch*Hkv][2] int32: first and last wave running
+ *     header             [batch*Hkv][2] int32: first and last share running
  *                        tiles of bh (written when bh has INT4 tiles)
+ *     counters           8 uint32 at the next multiple of 256 bytes, 256 bytes
+ *                        apart; kv4_decode_partials zeroes them before its
+ *                        attention kernel, on the same stream
  * so the runs of bh are the records bh + first .. bh + last.  Parts with no
  * positions are not written.  The BF16 kind has no protected parts and tiles
- * its whole context.
+ * its whole context.  Two calls in flight at once must not share a workspace.
  *
  * kv4_decode_merge combines, per (b, q head), the non-empty parts of that
  * workspace into out with weights 2^(z_k - max z) (zero for empty parts); its
@@ -254,10 +271,11 @@ const char* kv4_status_string(int status);
 
 /*
  * W, the number of waves of the decode partition (desc.num_waves, or 16 per
- * compute unit of the current device).  For tests and reporting; launches
- * nothing.
+ * compute unit of the current device), and C, the most chunks of its dynamic
+ * pool (desc.pool_chunks, 0 for none); either pointer may be NULL, not both.
+ * For tests and reporting; launches nothing.
  */
-int kv4_decode_waves(const kv4_cache* cache, int* waves);
+int kv4_decode_partition(const kv4_cache* cache, int* waves, int* pool_chunks);
 
 #ifdef __cplusplus
 }

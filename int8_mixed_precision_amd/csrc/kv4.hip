@@ -35,6 +35,10 @@ int validate_desc(const kv4_cache_desc* d)
         d->num_pages < 1 || d->max_slots < 1 || d->max_pages_per_seq < 1 ||
         d->num_waves < 0 || d->num_waves > kv4::kMaxWaves)
         return KV4_ERR_INVALID_ARG;
+    if (d->pool_chunks < 0 || d->pool_chunks > kv4::kPoolMaxChunks ||
+        (d->pool_chunks > 0 && (d->pool_chunks < kv4::kPoolMinChunks ||
+                                (d->pool_chunks & (d->pool_chunks - 1)) != 0)))
+        return KV4_ERR_INVALID_ARG;
     if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
     if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16) return KV4_ERR_INVALID_ARG;
     if (d->flags & ~KV4_FLAG_ROTATE_K) return KV4_ERR_INVALID_ARG;
@@ -74,6 +78,16 @@ int decode_waves(const kv4_cache* c, int cus)
     return c->desc.num_waves > 0 ? c->desc.num_waves : 16 * cus;
 }
 
+// Most chunks of the dynamic pool (0: none, the default).  Measured at the
+// batch-256 and 16 x 32k decode shapes, the pool is slower than the static
+// shares alone: a chunk's atomic ticket takes 6-25 us under full HBM load and
+// its extra records slow the merge.
+int decode_pool_chunks(const kv4_cache* c, int waves)
+{
+    (void)waves;
+    return c->desc.pool_chunks;
+}
+
 // Weight of a protected part in the partition, in INT4 tiles: an INT8 tile of
 // 32 entries moves 9.7 KB against 5 KB and runs with its load latency exposed;
 // measured at S + R = 132 and 260, it costs about 2.5 INT4 tiles.
@@ -89,16 +103,25 @@ int64_t partition_weight(const kv4::Geo& g, int batch, int max_ctx)
     return (int64_t)batch * g.Hkv * ((max_ctx + kv4::kTile - 1) / kv4::kTile + 1 + prot_units(g));
 }
 
-// Records of the INT4 / BF16 runs, protected records, then the (first, last)
-// wave header of every (sequence, kv head).
-size_t records_floats(const kv4::Geo& g, int batch, int waves)
+// Records of the INT4 / BF16 runs (one per (sequence, kv head) and share),
+// protected records, the (first, last) share header of every (sequence, kv
+// head), then the pool counters at the next multiple of 256 bytes.
+size_t records_floats(const kv4::Geo& g, int batch, int waves, int chunks)
 {
-    return ((size_t)2 * batch * g.Hkv + (size_t)waves) * g.gqa * (g.d + kv4::kPartPad);
+    return ((size_t)2 * batch * g.Hkv + (size_t)waves + (size_t)chunks) * g.gqa * (g.d + kv4::kPartPad);
 }
 
-size_t workspace_bytes(const kv4::Geo& g, int batch, int waves)
+size_t counters_offset(const kv4::Geo& g, int batch, int waves, int chunks)
 {
-    return records_floats(g, batch, waves) * sizeof(float) + (size_t)batch * g.Hkv * 2 * sizeof(int32_t);
+    const size_t end = records_floats(g, batch, waves, chunks) * sizeof(float) +
+                       (size_t)batch * g.Hkv * 2 * sizeof(int32_t);
+    return (end + 255) / 256 * 256;
+}
+
+size_t workspace_bytes(const kv4::Geo& g, int batch, int waves, int chunks)
+{
+    return counters_offset(g, batch, waves, chunks) +
+           (size_t)kv4::kPoolCounters * kv4::kPoolStride * sizeof(uint32_t);
 }
 
 int launch_status()
@@ -120,6 +143,9 @@ void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 
 void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
 {
+    // the pool counters start every launch at zero (a kernel, not a memset, so
+    // that the launch sequence can be captured in a graph)
+    if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
     if (a.g.gqa == 4) {
         dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {
@@ -157,7 +183,8 @@ int decode_args(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* 
     // the partition counts tiles and protected parts in 32-bit arithmetic
     if (partition_weight(g, batch, max_ctx) >= (int64_t)1 << 30) return KV4_ERR_CAPACITY;
     const int waves = decode_waves(cache, num_cus(cache));
-    if (batch > 0 && (workspace == nullptr || ws_bytes < workspace_bytes(g, batch, waves)))
+    const int chunks = decode_pool_chunks(cache, waves);
+    if (batch > 0 && (workspace == nullptr || ws_bytes < workspace_bytes(g, batch, waves, chunks)))
         return KV4_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KV4_ERR_INVALID_ARG;
     a.g = g;
@@ -170,11 +197,14 @@ int decode_args(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* 
     a.max_ctx = max_ctx;
     a.waves = waves;
     a.prot_units = prot_units(g);
+    a.pool_chunks = chunks;
     a.scale2 = sm_scale * 1.4426950408889634f;
     a.pages = cache->pages;
     a.side = cache->side;
     a.part = static_cast<float*>(const_cast<void*>(workspace));
-    a.hdr = reinterpret_cast<int2*>(a.part + records_floats(g, batch, waves));
+    a.hdr = reinterpret_cast<int2*>(a.part + records_floats(g, batch, waves, chunks));
+    a.ctr = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(const_cast<void*>(workspace)) +
+                                        counters_offset(g, batch, waves, chunks));
     a.out = nullptr;
     a.out_dtype = KV4_OUT_F32;
     return KV4_OK;
@@ -272,10 +302,12 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     return launch_status();
 }
 
-int kv4_decode_waves(const kv4_cache* cache, int* waves)
+int kv4_decode_partition(const kv4_cache* cache, int* waves, int* pool_chunks)
 {
-    if (cache == nullptr || waves == nullptr) return KV4_ERR_INVALID_ARG;
-    *waves = decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache)));
+    if (cache == nullptr || (waves == nullptr && pool_chunks == nullptr)) return KV4_ERR_INVALID_ARG;
+    const int w = decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache)));
+    if (waves) *waves = w;
+    if (pool_chunks) *pool_chunks = decode_pool_chunks(cache, w);
     return KV4_OK;
 }
 
@@ -285,7 +317,8 @@ int kv4_decode_workspace_bytes(const kv4_cache* cache, int batch, int max_ctx, s
     const kv4::Geo& g = cache->geo;
     if (batch > g.max_slots || max_ctx > g.max_pages * kv4::kPage) return KV4_ERR_CAPACITY;
     if (partition_weight(g, batch, max_ctx) >= (int64_t)1 << 30) return KV4_ERR_CAPACITY;
-    *bytes = workspace_bytes(g, batch, decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache))));
+    const int waves = decode_waves(cache, num_cus(const_cast<kv4_cache*>(cache)));
+    *bytes = workspace_bytes(g, batch, waves, decode_pool_chunks(cache, waves));
     return KV4_OK;
 }
 

@@ -8,17 +8,19 @@
 // (eq. A1), with zero weight for empty parts; the same identity merges the
 // pieces into which the partition below cuts a region.
 //
-// Work partition (balanced, persistent): the work of a launch is a sequence of
-// units -- for each (sequence b, kv head h) in order, first its protected part
-// (one indivisible unit weighing as many tiles as it has 32-entry tiles) and
-// then the 32-token tiles of
-// its INT4 region (one unit each).  W waves take equal contiguous ranges of
-// that sequence; a wave runs every protected part that starts in its range and
-// every run of tiles of one (b, h) inside it, writing one record per run.  A
-// run of (b, h) by wave w writes record b*Hkv + h + w, which is unique because
-// along the sequence either the head index or the wave index grows at every
-// cut.  The wave that runs the first tile of (b, h) stores the first and the
-// last wave of (b, h) in a header for the merge.
+// Work partition (balanced, persistent, with a dynamic tail): the work of a
+// launch is the protected parts of every (sequence b, kv head h) and the
+// 32-token tiles of their INT4 regions, in (b, h) order.  The tiles are cut
+// into shares: W static shares over the first Ts tiles, balanced together with
+// the protected parts so that every wave starts with the same weight, then a
+// pool of chunks over the remaining tiles, of decreasing size, that waves take
+// from a few atomic counters as they finish, so that waves that run faster
+// (older waves on a SIMD, less loaded XCDs) take more.  The run of (b, h) in
+// share s writes record b*Hkv + h + s, which is unique because along the tile
+// sequence either the head index or the share index grows at every cut; which
+// wave runs a share does not change its record.  The runner of the first tile
+// of (b, h) stores the first and the last share of (b, h) in a header for the
+// merge.
 //
 // Arithmetic: q stays at its bf16 value; keys and values are reconstructed in
 // fp32 registers as Delta*c + m (INT4, eq. 3.3) or s*c (INT8); scores, the
@@ -35,6 +37,11 @@ constexpr int kPartPad = 4;      // floats after o[d] in a partial: z and paddin
 constexpr int kTile = 32;        // tokens per INT4 / BF16 unit
 constexpr int kMinUnits = 8;     // least weight a wave is given (fewer waves otherwise)
 constexpr int kMaxWaves = 1 << 16;
+constexpr int kPoolCounters = 8;         // atomic counters of the pool
+constexpr int kPoolStride = 64;          // uint32 between counters (256 bytes)
+constexpr int kPoolMinChunks = 8;
+constexpr int kPoolMaxChunks = 1 << 16;
+constexpr uint32_t kPoolSixteenths = 3;  // share of the tiles left to the pool, in 1/16
 
 struct DecodeArgs {
     Geo g;
@@ -46,12 +53,14 @@ struct DecodeArgs {
     int batch, max_ctx;
     int waves;                    // W: waves of the partition (= the grid)
     int prot_units;               // weight of a protected part in tiles: its 32-entry tiles
+    int pool_chunks;              // most chunks of the pool (a power of two >= 8), 0 = no pool
     float scale2;                 // sm_scale * log2(e)
     const uint8_t* pages;
     const uint8_t* side;
-    float* part;                  // records [batch*Hkv + W][gqa][d + kPartPad], then the
-                                  // protected records [batch*Hkv][gqa][d + kPartPad]
-    int2* hdr;                    // [batch*Hkv]: first and last wave of the INT4 records
+    float* part;                  // records [batch*Hkv + W + pool_chunks][gqa][d + kPartPad],
+                                  // then the protected records [batch*Hkv][gqa][d + kPartPad]
+    int2* hdr;                    // [batch*Hkv]: first and last share of the INT4 records
+    uint32_t* ctr;                // pool counters, kPoolStride apart (zero at launch)
     void* out;
     int out_dtype;
 };
@@ -79,7 +88,7 @@ __device__ __forceinline__ float* rec_ptr(const DecodeArgs& a, int64_t slot)
 
 __device__ __forceinline__ float* prot_ptr(const DecodeArgs& a, int bh)
 {
-    return rec_ptr(a, (int64_t)a.batch * a.g.Hkv + a.waves + bh);
+    return rec_ptr(a, (int64_t)a.batch * a.g.Hkv + a.waves + a.pool_chunks + bh);
 }
 
 // Tile range of the INT4 (mixed cache) or BF16 region of a sequence of n
@@ -139,15 +148,59 @@ __device__ __forceinline__ uint32_t share(uint32_t w, uint32_t X, uint32_t W)
     return w * q + (w * r) / W;
 }
 
-// The partition of one launch.  Units: T4 tiles in (b, h, tile) order and P
-// protected parts in (b, h) order, of weight U8 tiles each.  Wave w
-// runs protected parts [pbeg(w), pbeg(w+1)) with pbeg(w) = floor(w P / W) and
-// tiles [tbeg(w), tbeg(w+1)) with tbeg(w) = floor(w (T4 + U8 P) / W)
-// - U8 pbeg(w), so that every wave's total weight is the same (and
-// every wave gets at least one tile).  When tiles are too few for that, they
-// are split evenly over the first min(W, T4) waves instead.  Either way the
-// waves running tiles of one (b, h) are consecutive and each runs some of
-// them.  The host bounds T4 + U8 P below 2^30.
+// s_setprio takes its level as an immediate.
+__device__ __forceinline__ void set_wave_prio(int p)
+{
+    if (p <= 0) __builtin_amdgcn_s_setprio(0);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(3);
+}
+
+// Wave priority by progress through the static share.  The instruction
+// arbiter of a SIMD favours older waves, so at equal priority the waves
+// dispatched first run ahead (about 20% faster with four per SIMD) and finish
+// early, while the youngest set the end of the launch.  A wave therefore runs
+// at a priority that falls as its share drains: 3 while more than half of it
+// is left, 2 above a quarter, 1 above an eighth, then 0 (and 0 in pool
+// chunks).  A wave that falls behind keeps the higher level until it catches
+// up, so the waves of a SIMD finish close together.  Priority only orders
+// instruction issue; results do not depend on it.
+struct Pace {
+    int share_len;                // tiles of the wave's static share (0: a pool chunk)
+    int rem_after;                // tiles of the share after the current run
+    int level;                    // current priority
+    // at the start of a tile with `left` tiles of the run to go (this one included)
+    __device__ __forceinline__ void tile(int left)
+    {
+        const int rem = rem_after + left;
+        const int lv = share_len <= 0 ? 0
+                     : 2 * rem > share_len ? 3 : 4 * rem > share_len ? 2 : 8 * rem > share_len ? 1 : 0;
+        if (lv != level) {
+            set_wave_prio(lv);
+            level = lv;
+        }
+    }
+};
+
+// The partition of one launch.  T4 tiles in (b, h, tile) order and P
+// protected parts in (b, h) order, of weight U8 tiles each; W waves.
+//  - Pool: Tp = floor(3 T4 / 16) tiles in Cd chunks, Cd the largest power of
+//    two <= pool_chunks with 2 Cd <= Tp (no pool when that is below 8).  With
+//    A = Tp - Cd, chunk c covers pool tiles [g(c), g(c+1)), g(c) = c + A -
+//    floor(A (Cd - c)^2 / Cd^2): at least one tile each, sizes falling
+//    linearly from about 2 Tp / Cd to 1.
+//  - Static shares over the other Ts = T4 - Tp tiles: wave w runs protected
+//    parts [pbeg(w), pbeg(w+1)), pbeg(w) = floor(w P / W), and tiles [tbeg(w),
+//    tbeg(w+1)), tbeg(w) = floor(w (Ts + U8 P) / W) - U8 pbeg(w), so that every
+//    wave starts with the same weight and at least one tile.  When tiles are
+//    too few for that, they are split evenly over the first Wt = min(W, Ts)
+//    waves instead.
+//  - Shares: s < S0 (S0 = W, or Wt) is static share s; s = S0 + c is chunk c,
+//    tiles [Ts + g(c), Ts + g(c+1)).  Consecutive shares cover consecutive
+//    tiles and none is empty, so the shares running tiles of one (b, h) are
+//    consecutive and each runs some of them.
+// The host bounds T4 + U8 P below 2^30.
 struct Plan {
     uint32_t T4;                  // INT4 / BF16 tiles
     uint32_t P;                   // protected parts
@@ -155,19 +208,31 @@ struct Plan {
     uint32_t W;                   // waves in use
     uint32_t Wt;                  // waves running tiles when not balanced
     bool balanced;
+    uint32_t Ts;                  // tiles of the static shares
+    uint32_t Cd;                  // pool chunks (0 = no pool)
+    uint32_t A;                   // pool tiles - Cd
+    uint32_t lg2;                 // 2 log2(Cd)
+    uint32_t S0;                  // static shares
     __device__ uint32_t pbeg(uint32_t w) const { return share(w, P, W); }
     __device__ uint32_t tbeg(uint32_t w) const
     {
-        return balanced ? share(w, T4 + U8 * P, W) - U8 * pbeg(w)
-                        : share(min(w, Wt), T4, Wt);
+        return balanced ? share(w, Ts + U8 * P, W) - U8 * pbeg(w)
+                        : share(min(w, Wt), Ts, Wt);
     }
-    // the wave whose tile range holds tile x (tbeg(w_lo) <= x < T4)
-    __device__ uint32_t wave_of_tile(uint32_t x, uint32_t w_lo) const
+    __device__ uint32_t cbeg(uint32_t c) const
     {
-        uint32_t lo = w_lo, hi = W - 1;
+        const uint64_t r = Cd - c;
+        return Ts + c + A - (uint32_t)(((uint64_t)A * r * r) >> lg2);
+    }
+    __device__ uint32_t shares() const { return S0 + Cd; }
+    __device__ uint32_t sbeg(uint32_t s) const { return s <= S0 ? tbeg(s) : cbeg(s - S0); }
+    // the share holding tile x (sbeg(s_lo) <= x < T4)
+    __device__ uint32_t share_of_tile(uint32_t x, uint32_t s_lo) const
+    {
+        uint32_t lo = s_lo, hi = shares() - 1;
         while (lo < hi) {
             const uint32_t mid = (lo + hi + 1) >> 1;
-            if (tbeg(mid) <= x) lo = mid;
+            if (sbeg(mid) <= x) lo = mid;
             else hi = mid - 1;
         }
         return lo;
@@ -192,10 +257,20 @@ __device__ __forceinline__ Plan make_plan(const DecodeArgs& a)
     pl.U8 = (uint32_t)a.prot_units;
     const uint32_t weight = pl.T4 + pl.U8 * pl.P;
     pl.W = min((uint32_t)a.waves, max(1u, (weight + kMinUnits - 1) / kMinUnits));
+    // pool: the largest power of two <= pool_chunks with two tiles per chunk
+    const uint32_t tp = (pl.T4 >> 4) * kPoolSixteenths + (((pl.T4 & 15u) * kPoolSixteenths) >> 4);
+    uint32_t cd = (uint32_t)a.pool_chunks;
+    if (cd > 0 && 2 * cd > tp) cd = tp >= 2 ? 1u << (31 - __builtin_clz(tp / 2)) : 0u;
+    if (cd < (uint32_t)kPoolMinChunks) cd = 0;
+    pl.Cd = cd;
+    pl.A = cd ? tp - cd : 0;
+    pl.lg2 = cd ? 2 * (uint32_t)__builtin_ctz(cd) : 0;
+    pl.Ts = pl.T4 - (cd ? tp : 0);
     // monotone iff every wave's share covers its protected parts
     const uint32_t pmax = (pl.P + pl.W - 1) / pl.W;
-    pl.balanced = weight / pl.W >= pl.U8 * pmax + 1;
-    pl.Wt = max(1u, min(pl.W, pl.T4));
+    pl.balanced = (pl.Ts + pl.U8 * pl.P) / pl.W >= pl.U8 * pmax + 1;
+    pl.Wt = max(1u, min(pl.W, pl.Ts));
+    pl.S0 = pl.balanced ? pl.W : pl.Wt;
     return pl;
 }
 
@@ -242,53 +317,96 @@ __device__ __forceinline__ void walk_prot(const DecodeArgs& a, const Plan& pl, u
     }
 }
 
-// Wave w's tiles: run(b, h, tok_lo, tok_hi, rec) for each maximal run of tiles
-// of one (b, h) in its range (token range clipped to the region; rec = record
-// b*Hkv + h + w).  The wave running the first tile of (b, h) stores the first
-// and last wave of (b, h) in the header.
-template <class Run>
-__device__ __forceinline__ void walk_tiles(const DecodeArgs& a, const Plan& pl, uint32_t w, Run&& run)
+// The next pool chunk for this wave, as a share index (shares() when the pool
+// is used up).  Chunk c belongs to counter c % 8 and is its ticket c / 8, so
+// each counter hands out its chunks largest first.  A wave draws on its own
+// counter j; when that one is used up it reads all eight at once and moves on
+// to the next open one after j.  A counter that returned a ticket past its
+// chunks is used up for good, so a wave leaves after at most eight misses, and
+// a chunk is never left untaken while a wave still looks for work.
+__device__ __forceinline__ uint32_t take_chunk(const DecodeArgs& a, const Plan& pl, uint32_t& j)
 {
+    if (pl.Cd == 0) return pl.shares();
     const int lane = threadIdx.x & 63;
-    const int Hkv = a.g.Hkv;
-    uint32_t x = pl.tbeg(w);
-    const uint32_t xe = pl.tbeg(w + 1);
-    if (x >= xe) return;
-    uint32_t C;
-    int b = locate_seq(a, x, [](const Units& u) { return u.ntile; }, C);
-    Units u = units_of(a, seq_len(a, b));
-    while (x < xe) {
-        const uint32_t r = x - C;
-        const int h = (int)(r / (uint32_t)u.ntile);
-        const int t0 = (int)(r - (uint32_t)h * u.ntile);
-        const uint32_t base = C + (uint32_t)h * u.ntile;
-        const int t1 = (int)min((uint32_t)u.ntile, xe - base);
-        const int bh = b * Hkv + h;
-        if (t0 == 0 && lane == 0) a.hdr[bh] = make_int2((int)w, (int)pl.wave_of_tile(base + u.ntile - 1, w));
-        run(b, h, max(kTile * (u.tile_lo + t0), u.tok_lo), min(kTile * (u.tile_lo + t1), u.tok_hi),
-            rec_ptr(a, (int64_t)bh + w));
-        x = base + t1;
-        if (x >= C + (uint32_t)Hkv * u.ntile) {  // next sequence with tiles
-            C += (uint32_t)Hkv * u.ntile;
-            do {
-                if (++b >= a.batch) return;
-                u = units_of(a, seq_len(a, b));
-            } while (u.ntile == 0);
-        }
+    const uint32_t per = pl.Cd / kPoolCounters;
+    uint32_t dead = 0;
+    for (;;) {
+        uint32_t n = 0;
+        if (lane == 0) n = atomicAdd(a.ctr + kPoolStride * j, 1u);
+        n = __builtin_amdgcn_readfirstlane(n);
+        if (n < per) return pl.S0 + j + kPoolCounters * n;
+        dead |= 1u << j;
+        const uint32_t v = lane < kPoolCounters
+            ? __hip_atomic_load(a.ctr + kPoolStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : per;
+        const uint32_t open = (uint32_t)__ballot(v < per) & ~dead & 0xFFu;
+        if (open == 0) return pl.shares();
+        const uint32_t k = (j + 1) & 7u;
+        const uint32_t rot = ((open >> k) | (open << (8u - k))) & 0xFFu;
+        j = (k + (uint32_t)__builtin_ctz(rot)) & 7u;
     }
 }
 
-// The whole partition for wave w = blockIdx.x: its protected parts, then its
-// tiles (two separate loops, so that the vector-ALU and the matrix-core parts
-// never share a loop body's registers).
+// Wave w's tiles: its static share, then pool chunks while there are any.
+// run(b, h, tok_lo, tok_hi, rec, pace) for each maximal run of tiles of one
+// (b, h) in a share s (token range clipped to the region; rec = record
+// b*Hkv + h + s; pace set for the run).
+// The runner of the first tile of (b, h) stores the first and the last share
+// of (b, h) in the header.
+template <class Run>
+__device__ __forceinline__ void walk_tiles(const DecodeArgs& a, const Plan& pl, uint32_t w, Pace& pace,
+                                           Run&& run)
+{
+    const int lane = threadIdx.x & 63;
+    const int Hkv = a.g.Hkv;
+    uint32_t j = w % kPoolCounters;
+    uint32_t s = w < pl.S0 ? w : take_chunk(a, pl, j);
+    while (s < pl.shares()) {
+        uint32_t x = pl.sbeg(s);
+        const uint32_t xe = pl.sbeg(s + 1);
+        pace.share_len = s < pl.S0 ? (int)(xe - x) : 0;
+        uint32_t C;
+        int b = locate_seq(a, x, [](const Units& u) { return u.ntile; }, C);
+        Units u = units_of(a, seq_len(a, b));
+        while (x < xe) {
+            const uint32_t r = x - C;
+            const int h = (int)(r / (uint32_t)u.ntile);
+            const int t0 = (int)(r - (uint32_t)h * u.ntile);
+            const uint32_t base = C + (uint32_t)h * u.ntile;
+            const int t1 = (int)min((uint32_t)u.ntile, xe - base);
+            const int bh = b * Hkv + h;
+            if (t0 == 0 && lane == 0) a.hdr[bh] = make_int2((int)s, (int)pl.share_of_tile(base + u.ntile - 1, s));
+            pace.rem_after = (int)(xe - (base + t1));
+            run(b, h, max(kTile * (u.tile_lo + t0), u.tok_lo), min(kTile * (u.tile_lo + t1), u.tok_hi),
+                rec_ptr(a, (int64_t)bh + s), pace);
+            x = base + t1;
+            if (x < xe && x >= C + (uint32_t)Hkv * u.ntile) {  // next sequence with tiles
+                C += (uint32_t)Hkv * u.ntile;
+                do {
+                    if (++b >= a.batch) break;
+                    u = units_of(a, seq_len(a, b));
+                } while (u.ntile == 0);
+                if (b >= a.batch) break;
+            }
+        }
+        s = take_chunk(a, pl, j);
+    }
+}
+
+// The whole partition for wave w = blockIdx.x: its protected parts (at the
+// top priority: they come first in a share), then its tiles (two separate
+// loops, so that the vector-ALU and the matrix-core parts never share a loop
+// body's registers).
 template <class Prot, class Run>
 __device__ __forceinline__ void walk_units(const DecodeArgs& a, Prot&& prot, Run&& run)
 {
     const Plan pl = make_plan(a);
     const uint32_t w = blockIdx.x;
     if (w >= pl.W) return;
+    Pace pace{0, 0, 3};
+    set_wave_prio(3);
     walk_prot(a, pl, w, prot);
-    walk_tiles(a, pl, w, run);
+    walk_tiles(a, pl, w, pace, run);
 }
 
 __device__ __forceinline__ float wave_sum(float x)
@@ -518,7 +636,10 @@ template <int GQA>
 __global__ __launch_bounds__(64) void decode_valu_kv4_kernel(DecodeArgs a)
 {
     walk_units(a, [&](int b, int h) { valu_item_kv4<GQA>(a, b, h, true, 0, 0, prot_ptr(a, b * a.g.Hkv + h)); },
-               [&](int b, int h, int lo, int hi, float* rec) { valu_item_kv4<GQA>(a, b, h, false, lo, hi, rec); });
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   pace.tile((hi + kTile - 1) / kTile - lo / kTile);
+                   valu_item_kv4<GQA>(a, b, h, false, lo, hi, rec);
+               });
 }
 
 // ---------------------------------------------------------------------------
@@ -591,7 +712,10 @@ template <int GQA>
 __global__ __launch_bounds__(64) void decode_valu_bf16_kernel(DecodeArgs a)
 {
     walk_units(a, [&](int, int) {},
-               [&](int b, int h, int lo, int hi, float* rec) { valu_item_bf16<GQA>(a, b, h, lo, hi, rec); });
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   pace.tile((hi + kTile - 1) / kTile - lo / kTile);
+                   valu_item_bf16<GQA>(a, b, h, lo, hi, rec);
+               });
 }
 
 // ---------------------------------------------------------------------------
@@ -602,6 +726,12 @@ __device__ __forceinline__ float wave_max(float x)
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
     return x;
+}
+
+// Zeroes the pool counters before a decode launch.
+__global__ __launch_bounds__(64) void pool_reset_kernel(uint32_t* ctr)
+{
+    if (threadIdx.x < kPoolCounters) ctr[kPoolStride * threadIdx.x] = 0u;
 }
 
 // One wave per (sequence, q head): the stable base-2 log-sum-exp merge of the
@@ -620,8 +750,9 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
     int n4p = 0, w0 = 0;
     if (u.ntile > 0) {
         const int2 hd = a.hdr[bh];
-        w0 = clampi(hd.x, 0, a.waves - 1);
-        n4p = clampi(hd.y, w0, a.waves - 1) - w0 + 1;
+        const int smax = a.waves + a.pool_chunks - 1;
+        w0 = clampi(hd.x, 0, smax);
+        n4p = clampi(hd.y, w0, smax) - w0 + 1;
     }
     const int np = n4p + (u.prot > 0);           // the runs of (b, h), then its protected part
     const int stride = g.d + kPartPad;

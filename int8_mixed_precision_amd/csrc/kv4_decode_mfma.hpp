@@ -271,7 +271,7 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
-                                              float* rec)
+                                              float* rec, Pace& pace)
 {
     constexpr int NG = kHeadDim / G;
     const Geo& g = a.g;
@@ -547,6 +547,7 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         const uint8_t* C1 = page(2 * tile_first + 3);
         // one tile: refill pointers, then the step (full tiles need no masks)
         auto advance = [&](int tl, auto full_tag) {
+            pace.tile(tile_end - tl);
             const bool more = tl + 1 < tile_end;
             const uint8_t* N0 = more ? C0 : T0;
             const uint8_t* N1 = more ? C1 : T1;
@@ -782,7 +783,7 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
 //       columns = channels 16 s + n16; k = tokens 8 kb .. 8 kb + 7 in order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
-                                               float* rec)
+                                               float* rec, Pace& pace)
 {
     const Geo& g = a.g;
     const int lane = threadIdx.x;
@@ -813,6 +814,7 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
     const int v_off = kPage * g.d * 2 + 2 * (((kb & 1) * g.d + n16) * kHalf);
 
     for (int ts = (t_lo / 32) * 32; ts < t_hi; ts += 32) {
+        pace.tile((t_hi + 31) / 32 - ts / 32);
         const int pi = ts / kPage;
         const int p0 = clampi(bt[min(pi, g.max_pages - 1)], 0, g.num_pages - 1);
         const int p1 = clampi(bt[min(pi + 1, g.max_pages - 1)], 0, g.num_pages - 1);
@@ -897,13 +899,17 @@ template <int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
     walk_units(a, [&](int b, int h) { mfma_prot_kv4(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
-               [&](int b, int h, int lo, int hi, float* rec) { mfma_item_kv4<G>(a, b, h, lo, hi, rec); });
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_kv4<G>(a, b, h, lo, hi, rec, pace);
+               });
 }
 
 __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)
 {
     walk_units(a, [&](int, int) {},
-               [&](int b, int h, int lo, int hi, float* rec) { mfma_item_bf16(a, b, h, lo, hi, rec); });
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_bf16(a, b, h, lo, hi, rec, pace);
+               });
 }
 
 }  // namespace kv4

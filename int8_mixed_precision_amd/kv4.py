@@ -37,7 +37,7 @@ class kv4_cache_desc(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "num_layers", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "group_size",
         "sink", "recent", "num_pages", "max_slots", "max_pages_per_seq", "kind", "flags",
-        "num_waves")]
+        "num_waves", "pool_chunks")]
 
 
 class KV4Error(RuntimeError):
@@ -64,10 +64,10 @@ def _load(path: str = LIB_PATH):
     L.kv4_cache_free.argtypes = [P]
     L.kv4_status_string.argtypes = [i32]
     L.kv4_status_string.restype = ctypes.c_char_p
-    L.kv4_decode_waves.argtypes = [P, pi32]
+    L.kv4_decode_partition.argtypes = [P, pi32, pi32]
     for f in ("kv4_cache_required_bytes", "kv4_cache_create", "kv4_append",
               "kv4_decode_workspace_bytes", "kv4_decode_attn", "kv4_decode_partials",
-              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_waves"):
+              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition"):
         getattr(L, f).restype = i32
     return L
 
@@ -114,10 +114,10 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
 
 def make_desc(num_layers, num_q_heads, num_kv_heads, head_dim=128, page_size=16, group_size=32,
               sink=4, recent=128, num_pages=1, max_slots=1, max_pages_per_seq=1,
-              kind=KV4_KIND_MIXED, flags=0, num_waves=0) -> kv4_cache_desc:
+              kind=KV4_KIND_MIXED, flags=0, num_waves=0, pool_chunks=0) -> kv4_cache_desc:
     return kv4_cache_desc(num_layers, num_q_heads, num_kv_heads, head_dim, page_size, group_size,
                           sink, recent, num_pages, max_slots, max_pages_per_seq, kind, flags,
-                          num_waves)
+                          num_waves, pool_chunks)
 
 
 # ---------------------------------------------------------------------------
@@ -173,11 +173,11 @@ def kv4_decode_workspace_bytes(cache, batch: int, max_ctx: int) -> int:
     return n.value
 
 
-def kv4_decode_waves(cache) -> int:
-    """Waves W of the decode partition (desc.num_waves, or 16 per compute unit)."""
-    w = ctypes.c_int32()
-    _check(_lib.kv4_decode_waves(cache, ctypes.byref(w)), "kv4_decode_waves")
-    return w.value
+def kv4_decode_partition(cache) -> tuple:
+    """(W, C): waves of the decode partition and most chunks of its pool."""
+    w, c = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.kv4_decode_partition(cache, ctypes.byref(w), ctypes.byref(c)), "kv4_decode_partition")
+    return w.value, c.value
 
 
 def kv4_decode_attn(cache, layer: int, q: torch.Tensor, seq_lens: torch.Tensor,

@@ -87,6 +87,10 @@ def test_invalid_descriptors():
         (dict(flags=0x10), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_waves=-1), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_waves=(1 << 16) + 1), kv4.KV4_ERR_INVALID_ARG),
+        (dict(pool_chunks=-1), kv4.KV4_ERR_INVALID_ARG),
+        (dict(pool_chunks=4), kv4.KV4_ERR_INVALID_ARG),        # below 8
+        (dict(pool_chunks=24), kv4.KV4_ERR_INVALID_ARG),       # not a power of two
+        (dict(pool_chunks=1 << 17), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_q_heads=48, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
     ]
@@ -186,20 +190,31 @@ def test_append_and_decode_validation_no_launch():
     kv4.kv4_cache_free(h)
 
 
+def _ws_bytes(B, Hkv, gqa, W, C):
+    # run records for batch*Hkv + W + C, protected records for batch*Hkv, a
+    # (first, last) int32 pair per (sequence, kv head), then 8 pool counters
+    # 256 bytes apart from the next multiple of 256 bytes
+    end = (2 * B * Hkv + W + C) * gqa * (128 + 4) * 4 + B * Hkv * 8
+    return -(-end // 256) * 256 + 8 * 256
+
+
 def test_wave_plan_and_workspace():
-    # explicit wave count: run records for batch*Hkv + W, protected records for
-    # batch*Hkv, and a (first, last) int32 pair per (sequence, kv head)
     h, d, _, _ = _fake_handle(num_waves=64, max_pages_per_seq=64)
-    assert kv4.kv4_decode_waves(h) == 64
+    assert kv4.kv4_decode_partition(h) == (64, 0)    # no pool by default
     B, Hkv, gqa = 3, 2, 4
     ws = kv4.kv4_decode_workspace_bytes(h, B, 1024)
-    assert ws == (2 * B * Hkv + 64) * gqa * (128 + 4) * 4 + B * Hkv * 8
+    assert ws == _ws_bytes(B, Hkv, gqa, 64, 0)
     assert kv4.kv4_decode_workspace_bytes(h, B, 16) == ws       # independent of max_ctx
     kv4.kv4_cache_free(h)
+    for waves, pool, want in ((100, 0, 0), (5, 8, 8), (64, 8, 8), (100, 128, 128), (7, 1 << 16, 1 << 16)):
+        h, d, _, _ = _fake_handle(num_waves=waves, pool_chunks=pool, max_pages_per_seq=64)
+        assert kv4.kv4_decode_partition(h) == (waves, want)
+        assert kv4.kv4_decode_workspace_bytes(h, B, 1024) == _ws_bytes(B, Hkv, gqa, waves, want)
+        kv4.kv4_cache_free(h)
     # automatic: 16 waves per compute unit (256 assumed without a device)
     h, d, _, _ = _fake_handle(max_pages_per_seq=64)
-    w = kv4.kv4_decode_waves(h)
-    assert w % 16 == 0 and w >= 16
+    w, c = kv4.kv4_decode_partition(h)
+    assert w % 16 == 0 and w >= 16 and c == 0
     kv4.kv4_cache_free(h)
 
 
@@ -226,3 +241,35 @@ def test_status_strings():
         s = kv4.kv4_status_string(c)
         assert s.startswith("KV4_")
     assert "unknown" in kv4.kv4_status_string(99)
+
+
+def test_partition_closed_forms():
+    """The documented shares cover the tile sequence in order, none empty; the
+    pool's chunks shrink and sum to its tiles; the static shares carry equal
+    weight when balanced.  Many shapes, plain integers."""
+    import random
+    from tests.partition import plan
+    rng = random.Random(3)
+    cases = [(T4, P, U8, W, C) for T4 in (1, 7, 64, 200, 1000, 4097, 343008)
+             for P, U8 in ((0, 0), (3, 13), (2048, 13)) for W in (1, 7, 64, 4096)
+             for C in (0, 8, 64, 4096, 1 << 16)]
+    cases += [(rng.randrange(1, 1 << 20), rng.randrange(0, 5000), rng.choice((0, 5, 13, 23)),
+               rng.randrange(1, 1 << 16), rng.choice((0, 8, 256, 8192))) for _ in range(300)]
+    for T4, P, U8, W, C in cases:
+        if T4 + U8 * P >= 1 << 30:
+            continue
+        pl = plan(T4, P, U8, W, C)
+        sb = pl["sbeg"]
+        assert sb[0] == 0 and sb[-1] == T4, (T4, P, U8, W, C)
+        assert all(a < b for a, b in zip(sb, sb[1:])), (T4, P, U8, W, C)
+        cd = pl["Cd"]
+        if cd:
+            assert cd & (cd - 1) == 0 and cd >= 8 and 2 * cd <= pl["Tp"]
+            sizes = [b - a for a, b in zip(sb[pl["S0"]:], sb[pl["S0"] + 1:])]
+            assert len(sizes) == cd and sum(sizes) == pl["Tp"] and min(sizes) >= 1
+            A = pl["Tp"] - cd                  # sizes fall linearly (up to rounding)
+            assert all(abs(z - 1 - A * (2 * (cd - c) - 1) / cd ** 2) < 1 for c, z in enumerate(sizes))
+        if pl["balanced"]:
+            Wn, pb = pl["W"], pl["pbeg"]
+            wt = [sb[w + 1] - sb[w] + U8 * (pb[w + 1] - pb[w]) for w in range(Wn)]
+            assert max(wt) - min(wt) <= 1, (T4, P, U8, W, C)

@@ -21,6 +21,7 @@ from int8_mixed_precision_amd import kv4
 from int8_mixed_precision_amd import workloads as W
 from tests import gpu_harness as H
 from tests import layout as L
+from tests import partition as PT
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +62,7 @@ def _compare_bytes(built, pages, side, layer, oc, S, R, seqs=None, n_of=None):
 
 
 def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_bytes=True,
-              garbage=True):
+              garbage=True, pool_chunks=0):
     """Build a cache for contexts ctx (history + one step token), decode, and
     compare with the oracle.  Returns (built, output, oracle cache)."""
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
@@ -69,7 +70,8 @@ def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_byt
     n = np.asarray(ctx, np.int64) + 1
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
-    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, seed=seed)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, pool_chunks=pool_chunks,
+                         seed=seed)
     if garbage:
         _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
@@ -107,50 +109,21 @@ def test_tiny_config():
     assert np.array_equal(outb, ref)
 
 
-def _partition(n, S, R, Hkv, W, min_units=8):
-    """The documented partition of one decode launch, written out on the host:
-    per (b, h) its tile count and the (first, last) wave running its tiles."""
-    tiles, prot = [], []
-    for nb in n:
-        rec = max(S, nb - R)
-        tiles.append(-(-rec // 32) - S // 32 if rec > S else 0)
-        prot.append(1 if min(S, nb) + max(nb - rec, 0) > 0 else 0)
-    prot_units = (5 * -(-(S + R) // 32) + 1) // 2 if S + R > 0 else 0
-    T4, P = sum(tiles) * Hkv, sum(prot) * Hkv
-    weight = T4 + prot_units * P
-    Wn = min(W, max(1, -(-weight // min_units)))
-    balanced = weight // Wn >= prot_units * (-(-P // Wn)) + 1
-    Wt = max(1, min(Wn, T4))
-    def tbeg(w):
-        return w * weight // Wn - prot_units * (w * P // Wn) if balanced else min(w, Wt) * T4 // Wt
-    starts = [tbeg(w) for w in range(Wn + 1)]
-    assert starts == sorted(starts) and starts[0] == 0 and starts[-1] == T4
-    def wave_of(x):
-        w = max(w for w in range(Wn) if starts[w] <= x)
-        assert starts[w] < starts[w + 1]          # the wave holding x runs it
-        return w
-    out, x = {}, 0
-    for b, nb in enumerate(n):
-        for h in range(Hkv):
-            if tiles[b]:
-                out[(b, h)] = (wave_of(x), wave_of(x + tiles[b] - 1))
-            x += tiles[b]
-    return out, tiles, prot
-
-
-@pytest.mark.parametrize("waves", [7, 0])
-def test_decode_phases_and_workspace_layout(waves):
+@pytest.mark.parametrize("waves,pool", [(7, 0), (7, 8), (0, 0), (0, 16), (64, 16)])
+def test_decode_phases_and_workspace_layout(waves, pool):
     """kv4_decode_partials followed by kv4_decode_merge equals kv4_decode_attn
     bit for bit, and the workspace holds what its header documents: the runs of
-    (b, h) at records b*Hkv + h + w for w = first .. last (as the documented
-    partition gives them), the protected part at its own record, float d the
-    base-2 log-normaliser.  Merging the parts on the host by eq. A1 in fp64
-    reproduces the output, and the merged log-normaliser equals the oracle's
-    log2 sum of 2^(sm_scale log2(e) q.k^) over the whole context."""
+    (b, h) at records b*Hkv + h + s for the shares s = first .. last (as the
+    documented partition gives them, static shares and pool chunks), the
+    protected part at its own record, float d the base-2 log-normaliser.
+    Merging the parts on the host by eq. A1 in fp64 reproduces the output, and
+    the merged log-normaliser equals the oracle's log2 sum of 2^(sm_scale
+    log2(e) q.k^) over the whole context."""
     Hq, Hkv, G, S, R = 8, 2, 32, 4, 64
     ctx = [0, 3, 40, 67, 68, 69, 300, 1000, 2500]
-    H.log(f"case decode phases: 8q/2kv G=32 S=4 R=64 waves {waves}")
-    built, out, oc, q, want = _run_case(Hq, Hkv, G, S, R, ctx, seed=11, waves=waves)
+    H.log(f"case decode phases: 8q/2kv G=32 S=4 R=64 waves {waves} pool {pool}")
+    built, out, oc, q, want = _run_case(Hq, Hkv, G, S, R, ctx, seed=11, waves=waves,
+                                        pool_chunks=pool)
     n = np.asarray(ctx) + 1
     B, d, gqa = len(n), 128, Hq // Hkv
     dev = torch.device("cuda")
@@ -166,15 +139,17 @@ def test_decode_phases_and_workspace_layout(waves):
     kv4.kv4_decode_merge(built.cache.handle, nd, B, max_ctx, o2, kv4.KV4_OUT_F32, ws)
     torch.cuda.synchronize()
     assert np.array_equal(o2.cpu().numpy(), out)
-    W = kv4.kv4_decode_waves(built.cache.handle)
+    W, C = kv4.kv4_decode_partition(built.cache.handle)
     if waves:
         assert W == waves
-    nrec = 2 * B * Hkv + W
+    nrec = 2 * B * Hkv + W + C
     rec = ws[:nrec * gqa * (d + 4) * 4].view(torch.float32).cpu().numpy()
     rec = rec.reshape(nrec, gqa, d + 4).astype(np.float64)
     hdr = ws[nrec * gqa * (d + 4) * 4:nrec * gqa * (d + 4) * 4 + B * Hkv * 8].view(torch.int32)
     hdr = hdr.cpu().numpy().reshape(B * Hkv, 2)
-    want_hdr, tiles, prot = _partition(n, S, R, Hkv, W)
+    want_hdr, tiles, prot, pl = PT.header(n, S, R, Hkv, W, C)
+    if pool > 0:
+        assert pl["Cd"] > 0          # the case exercises the pool
     c2 = sm / math.log(2.0)
     for b in range(B):
         nb = int(n[b])
@@ -191,7 +166,7 @@ def test_decode_phases_and_workspace_layout(waves):
                 assert (first, last) == want_hdr[(b, h)], (b, h, first, last, want_hdr[(b, h)])
                 used += [bh + w for w in range(first, last + 1)]
             if prot[b]:
-                used.append(B * Hkv + W + bh)
+                used.append(B * Hkv + W + C + bh)
             for j in range(gqa):
                 z = rec[used, j, d]
                 o = rec[used, j, :d]
@@ -241,11 +216,12 @@ def test_wave_invariance():
     number of waves (one wave running everything, to more waves than units)."""
     ctx = [0, 3, 70, 300, 1000, 2500]
     outs = {}
-    for waves in (1, 2, 7, 64, 0, 5000):
-        H.log(f"case waves={waves}")
-        _, out, _, _, _ = _run_case(8, 2, 32, 4, 64, ctx, seed=5, waves=waves)
-        outs[waves] = out
-    ref = outs[1]             # one wave: one run per (sequence, kv head)
+    for waves, pool in ((1, 0), (1, 8), (2, 0), (7, 0), (7, 8), (64, 0), (64, 16), (0, 0),
+                        (0, 4096), (5000, 0)):
+        H.log(f"case waves={waves} pool={pool}")
+        _, out, _, _, _ = _run_case(8, 2, 32, 4, 64, ctx, seed=5, waves=waves, pool_chunks=pool)
+        outs[(waves, pool)] = out
+    ref = outs[(1, 0)]        # one wave, no pool: one run per (sequence, kv head)
     for waves, o in outs.items():
         assert np.abs(o - ref).max() <= SPLIT_SELF_TOL, (waves, float(np.abs(o - ref).max()))
 
