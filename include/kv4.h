@@ -213,7 +213,7 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
  * kv4_decode_partials runs the whole step's work over W waves.  The work is,
  * for each (sequence b, kv head h), bh = b*Hkv + h in increasing order, its
  * protected part (if non-empty; indivisible, of weight U8 =
- * (5 * ceil((S + R) / 32) + 1) / 2 tiles, the measured cost of its 32-entry
+ * 3 * ceil((S + R) / 32) tiles, the measured cost of its 32-entry
  * INT8 tiles) and the 32-token tiles of its INT4 region [S, max(S, n - R))
  * (tile t covers positions [32t, 32t + 32) clipped to the region); T4 tiles
  * and P protected parts in all, W' = min(W, ceil((T4 + U8 P) / 8)) waves in

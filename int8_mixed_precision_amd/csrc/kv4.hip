@@ -90,11 +90,12 @@ int decode_pool_chunks(const kv4_cache* c, int waves)
 
 // Weight of a protected part in the partition, in INT4 tiles: an INT8 tile of
 // 32 entries moves 9.7 KB against 5 KB and runs with its load latency exposed;
-// measured at S + R = 132 and 260, it costs about 2.5 INT4 tiles.
+// measured at S + R = 132 and 260 (with the waves paced by progress), it
+// costs about 3 INT4 tiles.
 int prot_units(const kv4::Geo& g)
 {
     if (g.kind != KV4_KIND_MIXED || g.SR == 0) return 0;
-    return (5 * ((g.SR + kv4::kTile - 1) / kv4::kTile) + 1) / 2;
+    return 3 * ((g.SR + kv4::kTile - 1) / kv4::kTile);
 }
 
 // Upper bound of the partition's total weight for a batch shape.

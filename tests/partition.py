@@ -8,7 +8,7 @@ POOL_SIXTEENTHS = 3
 
 
 def prot_units(S, R):
-    return (5 * -(-(S + R) // 32) + 1) // 2 if S + R > 0 else 0
+    return 3 * -(-(S + R) // 32) if S + R > 0 else 0
 
 
 def plan(T4, P, U8, waves, pool_chunks):

@@ -220,7 +220,7 @@ def test_wave_plan_and_workspace():
 
 def test_partition_capacity_bound():
     """batch * Hkv * (ceil(max_ctx / 32) + 1 + U8) must stay below 2^30 (the
-    partition's 32-bit counts; U8 = 13 at S + R = 132)."""
+    partition's 32-bit counts; U8 = 15 at S + R = 132)."""
     base = dict(num_layers=1, num_q_heads=8, num_kv_heads=2, num_pages=4, max_slots=4096,
                 max_pages_per_seq=1 << 22)
     d = kv4.make_desc(**base)
@@ -230,9 +230,9 @@ def test_partition_capacity_bound():
     assert kv4.lib().kv4_cache_create(ctypes.byref(d), fake, pages, fake, side, ctypes.byref(h)) == 0
     n = ctypes.c_size_t()
     ok = kv4.lib().kv4_decode_workspace_bytes(h, 4096, 1 << 16, ctypes.byref(n))
-    assert ok == kv4.KV4_OK                     # 4096 * 2 * (2048 + 14) < 2^30
+    assert ok == kv4.KV4_OK                     # 4096 * 2 * (2048 + 16) < 2^30
     big = kv4.lib().kv4_decode_workspace_bytes(h, 4096, 1 << 22, ctypes.byref(n))
-    assert big == kv4.KV4_ERR_CAPACITY          # 4096 * 2 * (131072 + 14) >= 2^30
+    assert big == kv4.KV4_ERR_CAPACITY          # 4096 * 2 * (131072 + 16) >= 2^30
     kv4.kv4_cache_free(h)
 
 
