@@ -243,12 +243,21 @@ __device__ __forceinline__ Plan make_plan(const DecodeArgs& a)
 {
     const int lane = threadIdx.x & 63;
     int t = 0, p = 0;
-    for (int b0 = 0; b0 < a.batch; b0 += 64) {
-        const int b = b0 + lane;
-        if (b < a.batch) {
-            const Units u = units_of(a, seq_len(a, b));
-            t += u.ntile;
-            p += u.prot;
+    // the lengths of 256 sequences per pass, their loads issued together
+    for (int b0 = 0; b0 < a.batch; b0 += 4 * 64) {
+        int n[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = b0 + 64 * k + lane;
+            n[k] = b < a.batch ? seq_len(a, b) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (b0 + 64 * k + lane < a.batch) {
+                const Units u = units_of(a, n[k]);
+                t += u.ntile;
+                p += u.prot;
+            }
         }
     }
     Plan pl;
@@ -281,17 +290,27 @@ __device__ __forceinline__ int locate_seq(const DecodeArgs& a, uint32_t x, F&& f
 {
     const int lane = threadIdx.x & 63;
     C = 0;
-    for (int b0 = 0; b0 < a.batch; b0 += 64) {
-        const int bb = b0 + lane;
-        const int s = bb < a.batch ? a.g.Hkv * field(units_of(a, seq_len(a, bb))) : 0;
-        const int incl = wave_scan_i32(s);
-        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-        if (C + tot > x) {
-            const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(C + (uint32_t)incl > x)));
-            C += __builtin_amdgcn_readlane(incl - s, l);
-            return b0 + l;
+    // 256 sequences per pass, their lengths loaded together
+    for (int b0 = 0; b0 < a.batch; b0 += 4 * 64) {
+        int n[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int bb = b0 + 64 * k + lane;
+            n[k] = bb < a.batch ? seq_len(a, bb) : 0;
         }
-        C += tot;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int bb = b0 + 64 * k + lane;
+            const int s = bb < a.batch ? a.g.Hkv * field(units_of(a, n[k])) : 0;
+            const int incl = wave_scan_i32(s);
+            const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+            if (C + tot > x) {
+                const int l = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(C + (uint32_t)incl > x)));
+                C += __builtin_amdgcn_readlane(incl - s, l);
+                return b0 + 64 * k + l;
+            }
+            C += tot;
+        }
     }
     return a.batch;
 }
@@ -735,9 +754,11 @@ __global__ __launch_bounds__(64) void pool_reset_kernel(uint32_t* ctr)
 }
 
 // One wave per (sequence, q head): the stable base-2 log-sum-exp merge of the
-// non-empty parts (eq. A1).  The log-normalisers are read lane-parallel, 64
-// parts per pass; the outputs (2 channels per lane) with four independent
-// loads in flight.
+// non-empty parts (eq. A1).  The length and the header are loaded together;
+// with up to 8 parts, every part's log-normaliser (one per lane) and output
+// (2 channels per lane) are then loaded at once, so a row costs two memory
+// round trips.  More parts: log-normalisers lane-parallel, 64 parts per pass,
+// and the outputs with four independent loads in flight.
 __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
 {
     const Geo& g = a.g;
@@ -746,10 +767,11 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
     if (row >= a.batch * g.Hq) return;
     const int b = row / g.Hq, j = row % g.Hq, h = j / g.gqa, jj = j % g.gqa;
     const int bh = b * g.Hkv + h;
-    const Units u = units_of(a, seq_len(a, b));
+    const int n_b = seq_len(a, b);
+    const int2 hd = a.hdr[bh];                   // read with the length; used only when bh has tiles
+    const Units u = units_of(a, n_b);
     int n4p = 0, w0 = 0;
     if (u.ntile > 0) {
-        const int2 hd = a.hdr[bh];
         const int smax = a.waves + a.pool_chunks - 1;
         w0 = clampi(hd.x, 0, smax);
         n4p = clampi(hd.y, w0, smax) - w0 + 1;
@@ -760,12 +782,29 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
         return (i < n4p ? rec_ptr(a, (int64_t)bh + w0 + i) : prot_ptr(a, bh)) + jj * stride;
     };
 
+    constexpr int kFew = 8;
+    float W = 0.f, o0 = 0.f, o1 = 0.f;
+    if (np <= kFew) {
+        const float z = lane < np ? part_of(lane)[g.d] : -INFINITY;
+        float2 v[kFew];
+#pragma unroll
+        for (int i = 0; i < kFew; ++i)
+            v[i] = i < np ? *reinterpret_cast<const float2*>(part_of(i) + 2 * lane) : make_float2(0.f, 0.f);
+        const float zm = wave_max(z);
+        const float w = lane < np ? exp2f(z - zm) : 0.f;
+        W = wave_sum(w);
+#pragma unroll
+        for (int i = 0; i < kFew; ++i) {
+            const float wi = __shfl(w, i);
+            o0 = fmaf(wi, v[i].x, o0);
+            o1 = fmaf(wi, v[i].y, o1);
+        }
+    }
     float zmax = -INFINITY;
-    for (int c = 0; c < np; c += 64)
+    for (int c = 0; np > kFew && c < np; c += 64)
         if (c + lane < np) zmax = fmaxf(zmax, part_of(c + lane)[g.d]);
     zmax = wave_max(zmax);
-    float W = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int c = 0; c < np; c += 64) {
+    for (int c = 0; np > kFew && c < np; c += 64) {
         const float w = c + lane < np ? exp2f(part_of(c + lane)[g.d] - zmax) : 0.f;
         W += wave_sum(w);
         const int m = min(64, np - c);
