@@ -757,8 +757,8 @@ __global__ __launch_bounds__(64) void pool_reset_kernel(uint32_t* ctr)
 // non-empty parts (eq. A1).  The length and the header are loaded together;
 // with up to 8 parts, every part's log-normaliser (one per lane) and output
 // (2 channels per lane) are then loaded at once, so a row costs two memory
-// round trips.  More parts: log-normalisers lane-parallel, 64 parts per pass,
-// and the outputs with four independent loads in flight.
+// round trips.  Up to 128 parts: the log-normalisers in two loads per lane and
+// the outputs 16 parts at a time; beyond that, 64 log-normalisers per pass.
 __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
 {
     const Geo& g = a.g;
@@ -782,8 +782,24 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
         return (i < n4p ? rec_ptr(a, (int64_t)bh + w0 + i) : prot_ptr(a, bh)) + jj * stride;
     };
 
-    constexpr int kFew = 8;
+    constexpr int kFew = 8, kBatch = 16;
     float W = 0.f, o0 = 0.f, o1 = 0.f;
+    // outputs of parts [i, i + kBatch) weighted by wsel(part), loads issued together
+    auto gather = [&](int i, int end, auto&& wsel) {
+        float2 v[kBatch];
+        float wi[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int ii = min(i + u, end - 1);
+            wi[u] = i + u < end ? wsel(ii) : 0.f;
+            v[u] = *reinterpret_cast<const float2*>(part_of(ii) + 2 * lane);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            o0 = fmaf(wi[u], v[u].x, o0);
+            o1 = fmaf(wi[u], v[u].y, o1);
+        }
+    };
     if (np <= kFew) {
         const float z = lane < np ? part_of(lane)[g.d] : -INFINITY;
         float2 v[kFew];
@@ -799,29 +815,28 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
             o0 = fmaf(wi, v[i].x, o0);
             o1 = fmaf(wi, v[i].y, o1);
         }
-    }
-    float zmax = -INFINITY;
-    for (int c = 0; np > kFew && c < np; c += 64)
-        if (c + lane < np) zmax = fmaxf(zmax, part_of(c + lane)[g.d]);
-    zmax = wave_max(zmax);
-    for (int c = 0; np > kFew && c < np; c += 64) {
-        const float w = c + lane < np ? exp2f(part_of(c + lane)[g.d] - zmax) : 0.f;
-        W += wave_sum(w);
-        const int m = min(64, np - c);
-        for (int i = 0; i < m; i += 4) {
-            float2 v[4];
-            float wi[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int ii = min(i + u, m - 1);
-                wi[u] = i + u < m ? __shfl(w, ii) : 0.f;
-                v[u] = *reinterpret_cast<const float2*>(part_of(c + ii) + 2 * lane);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                o0 = fmaf(wi[u], v[u].x, o0);
-                o1 = fmaf(wi[u], v[u].y, o1);
-            }
+    } else if (np <= 128) {
+        // log-normalisers of up to 128 parts in two registers, then the outputs
+        // in batches of 16 loads
+        const float z0 = lane < np ? part_of(lane)[g.d] : -INFINITY;
+        const float z1 = 64 + lane < np ? part_of(64 + lane)[g.d] : -INFINITY;
+        const float zm = wave_max(fmaxf(z0, z1));
+        const float w0 = lane < np ? exp2f(z0 - zm) : 0.f;
+        const float w1 = 64 + lane < np ? exp2f(z1 - zm) : 0.f;
+        W = wave_sum(w0 + w1);
+        for (int i = 0; i < np; i += kBatch)
+            gather(i, np, [&](int ii) { return ii < 64 ? __shfl(w0, ii) : __shfl(w1, ii - 64); });
+    } else {
+        float zmax = -INFINITY;
+        for (int c = 0; c < np; c += 64)
+            if (c + lane < np) zmax = fmaxf(zmax, part_of(c + lane)[g.d]);
+        zmax = wave_max(zmax);
+        for (int c = 0; c < np; c += 64) {
+            const float w = c + lane < np ? exp2f(part_of(c + lane)[g.d] - zmax) : 0.f;
+            W += wave_sum(w);
+            const int m = min(64, np - c);
+            for (int i = 0; i < m; i += kBatch)
+                gather(c + i, c + m, [&](int ii) { return __shfl(w, ii - c); });
         }
     }
     const float inv = W > 0.f ? 1.0f / W : 0.f;  // n = 0 (clamped input) gives zeros
