@@ -59,6 +59,9 @@ def lib():
         L.orc_f16_to_f64_array.argtypes = [P, P, i64]
         L.orc_quant_int4.argtypes = [P, i64, i32, i32, P, P, P]
         L.orc_quant_int8.argtypes = [P, i64, i32, P, P]
+        L.orc_wht_f32.argtypes = [P, i64, i32, P]
+        L.orc_wht_scale.argtypes = [i32]
+        L.orc_wht_scale.restype = ctypes.c_float
         L.orc_is_protected.argtypes = [i64, i64, i32, i32]
         L.orc_is_protected.restype = i32
         L.orc_attend_mixed.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P,
@@ -141,6 +144,23 @@ def dequant_int8(codes, scale) -> np.ndarray:
     return f16_bits_to_f64(scale)[..., None] * codes.astype(np.float64)
 
 
+def wht(x) -> np.ndarray:
+    """The fixed normalized Hadamard transform y = x H / sqrt(d) of vectors
+    x[..., d] (KV4-RL Section 5.1; Appendix A.3), in binary32 in the order of
+    reading R-15: butterfly stages of span 1, 2, ..., d/2, then one product
+    with the binary32 value nearest 1/sqrt(d)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    d = x.shape[-1]
+    assert d & (d - 1) == 0 and d <= 1024
+    y = np.empty_like(x)
+    lib().orc_wht_f32(_ptr(x), x.size // d, d, _ptr(y))
+    return y
+
+
+def wht_scale(d: int) -> float:
+    return float(lib().orc_wht_scale(d))
+
+
 def is_protected(p: int, n: int, S: int, R: int) -> bool:
     return bool(lib().orc_is_protected(p, n, S, R))
 
@@ -158,10 +178,12 @@ class MixedCache:
     reads is decided by the position's region at attention time.
     """
 
-    def __init__(self, k_src, v_src, G: int, protect=None):
+    def __init__(self, k_src, v_src, G: int, protect=None, rotate: bool = False):
         """``protect=(S, R)`` computes the INT8 copies only of positions that
         are protected at the stored length (others stay zero); the default
-        computes them for every position, so any prefix can be attended."""
+        computes them for every position, so any prefix can be attended.
+        ``rotate`` stores the keys in the rotated basis (R-15): both the INT4
+        and the INT8 copy are computed from wht(k); values stay as they are."""
         self.G = G
         self.seq_lens = np.array([k.shape[0] for k in k_src], dtype=np.int32)
         self.pos_off = np.zeros(len(k_src), dtype=np.int64)
@@ -170,6 +192,9 @@ class MixedCache:
         K = np.ascontiguousarray(np.concatenate([np.asarray(k, np.float32) for k in k_src], 0))
         V = np.ascontiguousarray(np.concatenate([np.asarray(v, np.float32) for v in v_src], 0))
         self.Hkv, self.d = K.shape[1], K.shape[2]
+        self.rotate = rotate
+        if rotate:
+            K = wht(K)
         self.k4, self.k4d, self.k4m = quant_int4(K, G)
         self.v4, self.v4d, self.v4m = quant_int4(V, G)
         if protect is None:

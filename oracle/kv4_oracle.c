@@ -195,6 +195,40 @@ void orc_quant_int8(const float* x, int64_t nvec, int d, int8_t* codes, uint16_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* R-15: the fixed normalized Hadamard transform of keys (after RoPE, before */
+/* quantization) and of queries (before attention), KV4-RL Section 5.1 and   */
+/* Appendix A.3 "Encoding and allocation"; scores are kept because HH^T = I  */
+/* (eq. 3.4).                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* y = x H / sqrt(d) for the Sylvester Hadamard matrix H of order d (a power
+ * of two, H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]), in binary32 and in one
+ * fixed order (the pages fix no order; bit-exact stored codes need one):
+ * stages of span h = 1, 2, 4, ..., d/2, each replacing every pair
+ * (z[c], z[c+h]) with c & h == 0 by (z[c] + z[c+h], z[c] - z[c+h]), each sum one
+ * binary32 rounding; then every element times the binary32 value nearest
+ * 1/sqrt(d), one more rounding. */
+void orc_wht_f32(const float* x, int64_t nvec, int d, float* y)
+{
+    const float s = (float)(1.0 / sqrt((double)d));
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < nvec; ++v) {
+        float z[1024];
+        for (int c = 0; c < d && c < 1024; ++c) z[c] = x[v * d + c];
+        for (int h = 1; h < d && d <= 1024; h <<= 1)
+            for (int c = 0; c < d; ++c)
+                if ((c & h) == 0) {
+                    const float a = z[c], b = z[c + h];
+                    z[c] = a + b;
+                    z[c + h] = a - b;
+                }
+        for (int c = 0; c < d && c < 1024; ++c) y[v * d + c] = z[c] * s;
+    }
+}
+
+float orc_wht_scale(int d) { return (float)(1.0 / sqrt((double)d)); }
+
+/* ------------------------------------------------------------------------ */
 /* Q-5: which copy a position is read from.                                  */
 /* ------------------------------------------------------------------------ */
 
