@@ -73,8 +73,18 @@ extern "C" {
 #define KV4_KIND_BF16  1         /* BF16 pages, no protection (comparator) */
 
 /* Flags (kv4_cache_desc.flags). */
-#define KV4_FLAG_ROTATE_K 0x1    /* Hadamard rotation of K and q: not built yet,
-                                    returns KV4_ERR_UNSUPPORTED */
+/* KV4_FLAG_ROTATE_K: keys are stored in a rotated basis (KV4-RL Section 5.1,
+ * Appendix A.3 "Encoding and allocation"): kv4_append replaces each new key
+ * k (post-RoPE, bf16) by y = k H / sqrt(128), H the Sylvester Hadamard matrix,
+ * before both the INT4 and the INT8 encoding, and the decode transforms each
+ * query the same way before attention, so unquantized scores are unchanged
+ * (eq. 3.4); values are not rotated.  y is computed in binary32 in one fixed
+ * order: butterfly stages of span 1, 2, 4, ..., 64, each replacing every
+ * channel pair (c, c + h), c & h == 0, by (y_c + y_{c+h}, y_c - y_{c+h}), then
+ * every channel times the binary32 value nearest 1/sqrt(128) (0x3DB504F3).
+ * Mixed kind only (KV4_ERR_UNSUPPORTED with KV4_KIND_BF16); rotated keys must
+ * stay within the binary16 range. */
+#define KV4_FLAG_ROTATE_K 0x1
 
 /* Output dtypes of kv4_decode_attn. */
 #define KV4_OUT_F32  0

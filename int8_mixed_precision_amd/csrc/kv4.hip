@@ -47,7 +47,8 @@ int validate_desc(const kv4_cache_desc* d)
     if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
     if (d->head_dim != kv4::kHeadDim || d->page_size != kv4::kPage) return KV4_ERR_UNSUPPORTED;
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
-    if (d->flags & KV4_FLAG_ROTATE_K) return KV4_ERR_UNSUPPORTED;
+    // the rotation belongs to the quantized keys: the BF16 comparator has none
+    if ((d->flags & KV4_FLAG_ROTATE_K) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
     if ((int64_t)d->max_pages_per_seq * kv4::kPage > INT32_MAX / 2) return KV4_ERR_CAPACITY;
     return KV4_OK;
@@ -151,9 +152,18 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
         dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {
             switch (a.g.G) {
-                case 32: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<32>, grid, dim3(64), 0, s, a); break;
-                case 64: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<64>, grid, dim3(64), 0, s, a); break;
-                default: hipLaunchKernelGGL(kv4::decode_kv4_mfma_kernel<128>, grid, dim3(64), 0, s, a); break;
+                case 32:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<32, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<32, false>), grid, dim3(64), 0, s, a);
+                    break;
+                case 64:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<64, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<64, false>), grid, dim3(64), 0, s, a);
+                    break;
+                default:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<128, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<128, false>), grid, dim3(64), 0, s, a);
+                    break;
             }
         } else
             hipLaunchKernelGGL(kv4::decode_bf16_mfma_kernel, grid, dim3(64), 0, s, a);

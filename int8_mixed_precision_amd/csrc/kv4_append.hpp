@@ -138,6 +138,16 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
             uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
             float k0 = bf16_lo(kk), k1 = bf16_hi(kk), v0 = bf16_lo(vv), v1 = bf16_hi(vv);
+            if (g.rot) {
+                // keys in the rotated basis; lane l holds channels 2l, 2l + 1
+                float kr[2] = {k0, k1};
+                wht_local(kr);
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) wht_lanes(kr, m);
+                wht_scale(kr);
+                k0 = kr[0];
+                k1 = kr[1];
+            }
             int tp = t % kPage;
             // ---- INT4, keys
             uint16_t db, mb;

@@ -18,6 +18,7 @@ struct Geo {
     int Hq, Hkv, gqa, d, G, ng, S, R, SR;
     int num_layers, num_pages, max_slots, max_pages;
     int kind;
+    int rot;                 // 1: keys stored, and queries attended, in the rotated basis
     int64_t pb;              // bytes per (page, kv head) block
     int64_t layer_pages;     // bytes of one layer of the page pool
     int64_t rb;              // bytes per (slot, kv head) ring block
@@ -30,6 +31,50 @@ struct Geo {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// The fixed normalized Hadamard transform y = x H / sqrt(128) of a 128-channel
+// key or query (Sylvester H; KV4-RL Section 5.1, Appendix A.3 "Encoding and
+// allocation"; eq. 3.4 keeps the unquantized scores), in one fixed binary32
+// order that every kernel follows so that the stored codes are reproducible:
+// butterfly stages of span h = 1, 2, 4, ..., 64, each replacing every channel
+// pair (c, c + h), c & h == 0, by (z_c + z_{c+h}, z_c - z_{c+h}), then every
+// channel times the binary32 value nearest 1/sqrt(128).  Channels are spread
+// over registers and lanes in each kernel's own layout: wht_local runs the
+// stages over the channel bits held in one lane's N registers (the low bits),
+// wht_lanes one stage whose channel bit is the lane bit `mask`.
+constexpr float kWhtScale = 0x1.6a09e6p-4f;
+
+template <int N>
+__device__ __forceinline__ void wht_local(float (&v)[N])
+{
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+}
+
+template <int N>
+__device__ __forceinline__ void wht_lanes(float (&v)[N], int mask)
+{
+    const bool upper = (threadIdx.x & mask) != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float p = __shfl_xor(v[i], mask);
+        v[i] = upper ? p - v[i] : v[i] + p;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wht_scale(float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] *= kWhtScale;
+}
+
 inline Geo make_geo(const kv4_cache_desc& c)
 {
     Geo g{};
@@ -40,6 +85,7 @@ inline Geo make_geo(const kv4_cache_desc& c)
     g.G = c.group_size;
     g.ng = c.head_dim / c.group_size;
     g.kind = c.kind;
+    g.rot = (c.flags & KV4_FLAG_ROTATE_K) != 0;
     g.S = c.kind == KV4_KIND_MIXED ? c.sink : 0;
     g.R = c.kind == KV4_KIND_MIXED ? c.recent : 0;
     g.SR = g.S + g.R;

@@ -499,13 +499,22 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int h, float 
         uint4 u0 = *reinterpret_cast<const uint4*>(qr);
         uint4 u1 = *reinterpret_cast<const uint4*>(qr + 8);
         uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        float s = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             qk[j][2 * i] = bf16_lo(w[i]);
             qk[j][2 * i + 1] = bf16_hi(w[i]);
-            s += qk[j][2 * i] + qk[j][2 * i + 1];
         }
+        if (a.g.rot) {
+            // query into the keys' basis; channel bits 4-6 are lane bits 0-2
+            wht_local(qk[j]);
+            wht_lanes(qk[j], 1);
+            wht_lanes(qk[j], 2);
+            wht_lanes(qk[j], 4);
+            wht_scale(qk[j]);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += qk[j][2 * i] + qk[j][2 * i + 1];
         sq[j] = s;
     }
 }

@@ -19,7 +19,8 @@
 // Exactness: codes enter the matrix core as subnormal numbers whose mantissa
 // is the code (K: fp16, code * 2^-24 or 16 code * 2^-24; V: bf16, code *
 // 2^-133), so widening is a mask (and one shift per two pairs) and needs no
-// bias.  q is scaled by a power of two per head and is exact in fp16; the
+// bias.  q is scaled by a power of two per head and is exact in fp16 (a query
+// rotated into the keys' basis is a binary32 value, rounded to fp16); the
 // bf16 A operand of PV is split as hi + lo (both rounded to nearest), which
 // carries p*Delta to about 2^-18 relative.  The power-of-two scales are
 // undone in the score factor and in the epilogue.
@@ -269,7 +270,16 @@ __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const K
 // get score -inf, probability 0 and weight exactly 0 by selection, so garbage
 // bytes never reach the result.
 // ---------------------------------------------------------------------------
-template <int G>
+// A rotated query (ROT) is a binary32 value; its fp16 operand is then split
+// into hi + lo (both rounded to nearest, ~22 significant bits together) and
+// QK runs both halves, since one fp16 rounding costs ~3e-4 of a score.
+__device__ __forceinline__ uint2 split_f16(float x, float y)
+{
+    const uint32_t hi = pack_f16(x, y);
+    return make_uint2(hi, pack_f16(x - h2f(hi, 0), y - h2f(hi, 1)));
+}
+
+template <int G, bool ROT>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                               float* rec, Pace& pace)
 {
@@ -288,17 +298,28 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     // ---- q: block-diagonal A operands and block sums
     // A carries q_j scaled by 2^sc_j, with sc_j chosen so that max |q_j| * 2^sc_j
     // lies in [2^14, 2^15): every bf16 element of q above 2^-31 max |q_j| is then
-    // exact in fp16 (a power-of-two scale), and the k-slots facing codes
-    // stored at 16 times their value get a further 2^-4.
+    // exact in fp16 (a power-of-two scale; a rotated query is rounded to its
+    // 11 significant bits), and the k-slots facing codes stored at 16 times
+    // their value get a further 2^-4.
     u32x4_t aqv;                                 // scaled q of head jq on block gq (k-slot pairs)
+    u32x4_t aql = {0u, 0u, 0u, 0u};              // its low half (rotated queries only)
     float sq_part;
     int sc;                                      // scale exponent of head jq
     {
         const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
         const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
-        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-        sq_part = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        if constexpr (ROT) {
+            // query into the keys' basis: channel bits 3-4 are lane bits 4-5
+            // (kb), bits 5-6 lane bits 0-1 (gq)
+            wht_local(q);
+            wht_lanes(q, 16);
+            wht_lanes(q, 32);
+            wht_lanes(q, 1);
+            wht_lanes(q, 2);
+            wht_scale(q);
+        }
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
@@ -306,10 +327,30 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));       // ... and the rows: head jq
         sc = 15 - __builtin_amdgcn_frexp_expf(amax);
         // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen_k16() pairs codes
-        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
-        aqv[1] = pack_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
-        aqv[2] = pack_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
-        aqv[3] = pack_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+        if constexpr (ROT) {
+            const uint2 s0 = split_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
+            const uint2 s1 = split_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
+            const uint2 s2 = split_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
+            const uint2 s3 = split_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+            aqv = u32x4_t{s0.x, s1.x, s2.x, s3.x};
+            aql = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+        } else {
+            aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
+            aqv[1] = pack_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
+            aqv[2] = pack_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
+            aqv[3] = pack_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+        }
+        // the sum of q as the matrix core sees it, so that the offset term
+        // m sum(q) matches the products
+        auto opsum = [&](const u32x4_t& o, int i, int j) {
+            return (h2f(o[i], 0) + h2f(o[i], 1)) + (h2f(o[j], 0) + h2f(o[j], 1));
+        };
+        float e0 = opsum(aqv, 0, 2), e1 = opsum(aqv, 1, 3);
+        if constexpr (ROT) {
+            e0 += opsum(aql, 0, 2);
+            e1 += opsum(aql, 1, 3);
+        }
+        sq_part = ldexpf(fmaf(16.0f, e1, e0), -sc);
     }
     // sum of q over block gq of head jq (the four lanes of A row n16), then
     // the sums of head kb over each block r, for this lane's D rows
@@ -413,8 +454,15 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             const uint64_t rows = 0x1111111111111111ull << bb;
             const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
                                keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-            D0 = mfma_f16(A, widen_k16(k0w[bb]), D0);
-            D1 = mfma_f16(A, widen_k16(k1w[bb]), D1);
+            const u32x4_t B0 = widen_k16(k0w[bb]), B1 = widen_k16(k1w[bb]);
+            D0 = mfma_f16(A, B0, D0);
+            D1 = mfma_f16(A, B1, D1);
+            if constexpr (ROT) {
+                const u32x4_t Al = {keep_lanes(aql[0], rows), keep_lanes(aql[1], rows),
+                                    keep_lanes(aql[2], rows), keep_lanes(aql[3], rows)};
+                D0 = mfma_f16(Al, B0, D0);
+                D1 = mfma_f16(Al, B1, D1);
+            }
         }
         float x0 = 0.f, x1 = 0.f;
 #pragma unroll
@@ -612,6 +660,7 @@ __device__ __forceinline__ u32x4_t widen_i8(uint32_t w0, uint32_t w1)
 //     block r's MFMAs keep the A rows of block r and cover channels 32 r +
 //     16 h + n16 in E[h][r].
 // ---------------------------------------------------------------------------
+template <bool ROT>
 __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h, float* rec)
 {
     const Geo& g = a.g;
@@ -628,13 +677,22 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
 
     // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
     u32x4_t aqv;
-    float qpart;
+    u32x4_t aql = {0u, 0u, 0u, 0u};              // low half of a rotated query
     int sc;
     {
         const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
         const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
-        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        if constexpr (ROT) {
+            // channel bits 3-4 are lane bits 0-1 (gq), bits 5-6 lane bits 4-5 (kb)
+            wht_local(q);
+            wht_lanes(q, 1);
+            wht_lanes(q, 2);
+            wht_lanes(q, 16);
+            wht_lanes(q, 32);
+            wht_scale(q);
+        }
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
@@ -642,13 +700,23 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
         amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
         sc = 15 - __builtin_amdgcn_frexp_expf(amax);
         // k-slot pairs as widen_i8 pairs codes: (0, 2), (1, 3), (4, 6), (5, 7)
-        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[2], sc));
-        aqv[1] = pack_f16(ldexpf(q[1], sc), ldexpf(q[3], sc));
-        aqv[2] = pack_f16(ldexpf(q[4], sc), ldexpf(q[6], sc));
-        aqv[3] = pack_f16(ldexpf(q[5], sc), ldexpf(q[7], sc));
-        qpart = 0.f;
+        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (ROT) {
+                const uint2 hl = split_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
+                aqv[i] = hl.x;
+                aql[i] = hl.y;
+            } else {
+                aqv[i] = pack_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
+            }
+        }
+    }
+    float qpart = 0.f;                           // the sum of exactly the operand used
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
+        if constexpr (ROT) qpart += h2f(aql[i], 0) + h2f(aql[i], 1);
     }
     // sum of the operand over MFMA block gq's 32 k-slots (row n16), then per D
     // row (head kb, block r): D starts at -128 * 2^-24 * that sum
@@ -691,8 +759,16 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
             const uint64_t rows = 0x1111111111111111ull << bb;
             const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
                                keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-            D0 = mfma_f16(A, widen_i8(kw0[2 * bb], kw0[2 * bb + 1]), D0);
-            D1 = mfma_f16(A, widen_i8(kw1[2 * bb], kw1[2 * bb + 1]), D1);
+            const u32x4_t B0 = widen_i8(kw0[2 * bb], kw0[2 * bb + 1]);
+            const u32x4_t B1 = widen_i8(kw1[2 * bb], kw1[2 * bb + 1]);
+            D0 = mfma_f16(A, B0, D0);
+            D1 = mfma_f16(A, B1, D1);
+            if constexpr (ROT) {
+                const u32x4_t Al = {keep_lanes(aql[0], rows), keep_lanes(aql[1], rows),
+                                    keep_lanes(aql[2], rows), keep_lanes(aql[3], rows)};
+                D0 = mfma_f16(Al, B0, D0);
+                D1 = mfma_f16(Al, B1, D1);
+            }
         }
         const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
         float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
@@ -895,12 +971,13 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
 // Grid = W one-wave workgroups, each walking its range of the balanced unit
 // partition: protected parts on the vector ALU, runs of INT4 tiles on the
 // matrix core.
-template <int G>
+// ROT: keys stored in the rotated basis (the query is rotated at load).
+template <int G, bool ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv4_mfma_kernel(DecodeArgs a)
 {
-    walk_units(a, [&](int b, int h) { mfma_prot_kv4(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+    walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
-                   mfma_item_kv4<G>(a, b, h, lo, hi, rec, pace);
+                   mfma_item_kv4<G, ROT>(a, b, h, lo, hi, rec, pace);
                });
 }
 

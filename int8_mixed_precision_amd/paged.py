@@ -46,7 +46,7 @@ def page_tables(lengths, max_pages, rng, num_pages=None, shuffle=True):
 
 
 def make_cache(Hq, Hkv, G, S, R, lengths, *, layers=1, kind=kv4.KV4_KIND_MIXED, waves=0,
-               pool_chunks=0, seed=0, max_pages=None, extra_pages=3, slot_perm=True, device="cuda"):
+               pool_chunks=0, flags=0, seed=0, max_pages=None, extra_pages=3, slot_perm=True, device="cuda"):
     rng = np.random.default_rng(seed + 1000)
     B = len(lengths)
     if max_pages is None:
@@ -59,7 +59,7 @@ def make_cache(Hq, Hkv, G, S, R, lengths, *, layers=1, kind=kv4.KV4_KIND_MIXED, 
     bt = np.zeros((max_slots, max_pages), dtype=np.int32)
     bt[slots] = bt_seq
     desc = kv4.make_desc(layers, Hq, Hkv, 128, PAGE, G, S, R, num_pages, max_slots, max_pages,
-                         kind, 0, waves, pool_chunks)
+                         kind, flags, waves, pool_chunks)
     cache = kv4.Cache(desc, device)
     dev = torch.device(device)
     return Built(cache, desc, torch.from_numpy(bt).to(dev), bt,

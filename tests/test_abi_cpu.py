@@ -83,7 +83,7 @@ def test_invalid_descriptors():
         (dict(sink=-1), kv4.KV4_ERR_INVALID_ARG),
         (dict(recent=-5), kv4.KV4_ERR_INVALID_ARG),
         (dict(kind=7), kv4.KV4_ERR_INVALID_ARG),
-        (dict(flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(flags=kv4.KV4_FLAG_ROTATE_K, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
         (dict(flags=0x10), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_waves=-1), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_waves=(1 << 16) + 1), kv4.KV4_ERR_INVALID_ARG),
@@ -97,6 +97,9 @@ def test_invalid_descriptors():
     for change, code in cases:
         d = kv4.make_desc(**{**base, **change})
         assert _err(kv4.kv4_cache_required_bytes, d) == code, change
+    # the rotation is a property of the quantized (mixed) cache; sizes do not change
+    rot = kv4.kv4_cache_required_bytes(kv4.make_desc(**base, flags=kv4.KV4_FLAG_ROTATE_K))
+    assert rot == kv4.kv4_cache_required_bytes(kv4.make_desc(**base))
 
 
 def _fake_handle(**kw):

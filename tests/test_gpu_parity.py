@@ -62,22 +62,24 @@ def _compare_bytes(built, pages, side, layer, oc, S, R, seqs=None, n_of=None):
 
 
 def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_bytes=True,
-              garbage=True, pool_chunks=0):
+              garbage=True, pool_chunks=0, rotate=False):
     """Build a cache for contexts ctx (history + one step token), decode, and
-    compare with the oracle.  Returns (built, output, oracle cache)."""
+    compare with the oracle.  Returns (built, output, oracle cache).  With
+    ``rotate`` the cache stores keys in the rotated basis (KV4_FLAG_ROTATE_K)
+    and the oracle quantizes wht(k) and attends with wht(q)."""
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
                    seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
     n = np.asarray(ctx, np.int64) + 1
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
     built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, pool_chunks=pool_chunks,
-                         seed=seed)
+                         flags=kv4.KV4_FLAG_ROTATE_K if rotate else 0, seed=seed)
     if garbage:
         _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
     out = H.decode(built, layer, q, n).cpu().numpy()
-    oc = oracle.MixedCache(ks, vs, G)
-    want = oracle.attend_mixed(q, oc, S, R, 1 / math.sqrt(128))
+    oc = oracle.MixedCache(ks, vs, G, rotate=rotate)
+    want = oracle.attend_mixed(oracle.wht(q) if rotate else q, oc, S, R, 1 / math.sqrt(128))
     if check_bytes:
         pages, side = H.pools_host(built)
         _compare_bytes(built, pages, side, layer, oc, S, R)
@@ -353,3 +355,28 @@ def test_bf16_comparator():
             assert np.array_equal(k, ks[b]) and np.array_equal(v, vs[b])
         want = oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128))
         H.check_output(out, want, ATOL, RTOL)
+
+
+# ---------------------------------------------------------------------------
+# Keys stored in the rotated basis (KV4-RL Section 5.1, Appendix A.3): the
+# append rotates k before both quantizers, the decode rotates q; bytes are
+# compared with the oracle's quantization of wht(k), outputs with its fp64
+# attention of wht(q) over that cache.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Hq,Hkv,G", [(8, 2, 32), (8, 2, 128), (16, 4, 64), (4, 4, 32), (16, 2, 32),
+                                      (32, 8, 32)])
+def test_rotated_keys(Hq, Hkv, G):
+    H.log(f"case rotated keys Hq={Hq} Hkv={Hkv} G={G}")
+    _run_case(Hq, Hkv, G, 4, 64, [0, 3, 40, 67, 68, 69, 300, 1000, 2500], seed=Hq + 3 * G + Hkv,
+              rotate=True)
+
+
+def test_rotated_keys_edges_and_layers():
+    for S, R in ((0, 0), (0, 8), (16, 3), (4, 128)):
+        H.log(f"case rotated keys edges S={S} R={R}")
+        _run_case(8, 2, 32, S, R, list(range(0, 40, 3)) + [S + R, S + R + 1, 600], seed=71 + S + R,
+                  rotate=True)
+    H.log("case rotated keys, 3 layers, layer 1, waves 7")
+    _run_case(8, 2, 32, 4, 32, [33, 150, 401, 1200], seed=72, layers=3, layer=1, waves=7, rotate=True)
+
