@@ -43,6 +43,8 @@ def parse():
                     help="most chunks of the decode's dynamic pool (0 = none, the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--rotate", action="store_true",
+                    help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -224,7 +226,7 @@ def main():
 
     kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
                         seed=cfg.seed, waves=args.waves, pool_chunks=args.pool_chunks,
-                        device="cuda:0")
+                        flags=kv4.KV4_FLAG_ROTATE_K if args.rotate else 0, device="cuda:0")
     caches = [("kv4", kv4c)]
     if not args.no_bf16:
         bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
@@ -331,7 +333,7 @@ def main():
     decode_gbs = db / (r["decode_ms"] * 1e-3) / 1e9
     achieved = pb / (r["partials_ms"] * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(args.traffic_json):
+    if os.path.exists(args.traffic_json) and not args.rotate:   # counters of the unrotated kernel
         try:
             tj = json.load(open(args.traffic_json))
             if tj.get("kernel_source_hash") == _kernel_hash():
@@ -357,7 +359,7 @@ def main():
                         "page 16, INT4 group 32, S=4, R=128",
             "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
-            "waves": r["waves"], "pool_chunks": r["pool_chunks"],
+            "waves": r["waves"], "pool_chunks": r["pool_chunks"], "rotate_k": bool(args.rotate),
         },
         "decode_attn_gbs": round(decode_gbs, 2),
         "decode_attn_pct_hbm_peak": round(100 * decode_gbs / HBM_PEAK_GBS, 2),
