@@ -43,6 +43,8 @@ def parse():
                     help="most chunks of the decode's dynamic pool (0 = none, the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-kv8", action="store_true",
+                    help="skip the KV8 comparator (INT8 pages for every position)")
     ap.add_argument("--rotate", action="store_true",
                     help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -98,6 +100,13 @@ def decode_bytes_kv4(n, cfg):
 def decode_bytes_bf16(n, cfg):
     kv = int(np.sum(cfg.kv_heads * 2 * cfg.head_dim * 2 * n))
     return kv + len(n) * cfg.q_heads * cfg.head_dim * (2 + 4) + int(np.sum(4 * np.ceil(n / 16)))
+
+
+def partial_bytes_kv8(n, cfg):
+    """KV8 kind: 2 d int8 codes + two fp16 scales per (token, kv head), q,
+    block-table entries."""
+    kv = int(np.sum(cfg.kv_heads * (2 * cfg.head_dim + 4) * n))
+    return kv + len(n) * cfg.q_heads * cfg.head_dim * 2 + int(np.sum(4 * np.ceil(n / 16)))
 
 
 def append_bytes_kv4(n, cfg):
@@ -160,6 +169,9 @@ def summarize_trace(args):
         if "bf16_comparator" in b:
             lines.append(f"  BF16 comparator partials (decode_bf16_mfma_kernel): "
                          f"{b['bf16_comparator']['decode_partials_us']} us")
+        if "kv8_comparator" in b:
+            lines.append(f"  KV8 comparator partials (decode_kv8_mfma_kernel): "
+                         f"{b['kv8_comparator']['decode_partials_us']} us")
         lines.append("kernel counts include warm-up steps, the cache build's bulk appends and one "
                      "kv4_decode_attn check call")
     text = "\n".join(lines) + "\n"
@@ -233,6 +245,11 @@ def main():
                            kind=kv4.KV4_KIND_BF16, waves=args.waves,
                            pool_chunks=args.pool_chunks, device="cuda:0")
         caches.append(("bf16", bfc))
+    if not args.no_kv8:
+        k8c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
+                           kind=kv4.KV4_KIND_KV8, waves=args.waves,
+                           pool_chunks=args.pool_chunks, device="cuda:0")
+        caches.append(("kv8", k8c))
     # build every cache from the same sources, sequence chunk by chunk
     step_k, step_v = [], []
     for lo in range(0, B, 32):
@@ -392,6 +409,20 @@ def main():
         }
         line["speedup_vs_bf16_step"] = round(bstep / step_ms, 3)
         line["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
+
+    if "kv8" in results:
+        r8 = results["kv8"]
+        p8 = partial_bytes_kv8(n, cfg)
+        line["kv8_comparator"] = {
+            "decode_attn_us": round(r8["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(r8["partials_ms"] * 1e3, 2),
+            "append_us": round(r8["append_ms"] * 1e3, 2),
+            "partials_alg_bytes": p8,
+            "partials_gbs": round(p8 / (r8["partials_ms"] * 1e-3) / 1e9, 2),
+            "partials_frac_hbm_peak": round(p8 / (r8["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "layer_tokens_per_s": round(B / ((r8["append_ms"] + r8["decode_ms"]) * 1e-3), 1),
+        }
+        line["speedup_vs_kv8_decode"] = round(r8["decode_ms"] / r["decode_ms"], 3)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, ctx, n, args.cpu_seconds)

@@ -37,6 +37,13 @@
  *       V delta  [group][16 tokens] binary16;
  *     i.e. 16 * (head_dim + 8 * head_dim / group_size) bytes per PB
  *     (2,560 B at head_dim 128, group 32: 160 B per token and kv head).
+ *   page pool, KV8 kind: [layer][page][kv_head] blocks of
+ *       K codes  [16 tokens][head_dim] int8, token-major;
+ *       V codes  2 blocks of 8 tokens x head_dim int8, channel-major: token t,
+ *                channel c at (t/8)*8*head_dim + ((c%16)*8 + c/16)*8 + t%8
+ *                (the side ring's V layout);
+ *       K scale  [16] binary16, then V scale [16] binary16;
+ *     i.e. 16 * (2*head_dim + 4) bytes per PB (4,160 B at head_dim 128).
  *   page pool, BF16 kind: [layer][page][kv_head] blocks of K [16][head_dim]
  *     bf16 (token-major) then V [2 halves][head_dim][8 tokens] bf16 -- value
  *     (t, c) at ((t/8)*head_dim + c)*8 + t%8 (8,192 B at head_dim 128).
@@ -71,6 +78,12 @@ extern "C" {
 /* Cache kinds. */
 #define KV4_KIND_MIXED 0         /* INT4 pages + INT8 sink/recent side ring */
 #define KV4_KIND_BF16  1         /* BF16 pages, no protection (comparator) */
+#define KV4_KIND_KV8   2         /* INT8 pages for every position, symmetric per
+                                    token and kv head with a binary16 scale (the
+                                    side entries' encoding, KV4-RL Appendix A.3);
+                                    the paper's KV8 comparison point (Fig. 3b,
+                                    Fig. 4a); sink and recent are unused; decode
+                                    needs Hq/Hkv = 4 */
 
 /* Flags (kv4_cache_desc.flags). */
 /* KV4_FLAG_ROTATE_K: keys are stored in a rotated basis (KV4-RL Section 5.1,
@@ -105,7 +118,7 @@ typedef struct kv4_cache_desc {
     int32_t num_pages;          /* pages per layer in the page pool, >= 1 */
     int32_t max_slots;          /* request slots (rows of the block table, side rings) */
     int32_t max_pages_per_seq;  /* columns of the block table */
-    int32_t kind;               /* KV4_KIND_MIXED or KV4_KIND_BF16 */
+    int32_t kind;               /* KV4_KIND_MIXED, KV4_KIND_BF16 or KV4_KIND_KV8 */
     int32_t flags;              /* KV4_FLAG_* */
     int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
                                    partition; 0 = 16 per compute unit of the
@@ -164,7 +177,9 @@ int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_po
  * p < S or p >= ctx_before + new_b - R.  A position that later leaves the
  * recent window needs no further work (demotion moves only the region
  * boundary; its INT4 entry already exists).  BF16 kind: the bf16 values are
- * copied into the pages.
+ * copied into the pages.  KV8 kind: every new position gets its INT8 K and V
+ * codes and scales (s = fp16(fp32(amax / 127)), codes the nearest integers to
+ * x / s, ties to even, in [-127, 127]) written into its page.
  * Errors: KV4_ERR_INVALID_ARG (null pointers, batch < 1, total_new < 0),
  * KV4_ERR_CAPACITY (layer out of range, batch > max_slots), KV4_ERR_HIP.
  */

@@ -40,7 +40,8 @@ int validate_desc(const kv4_cache_desc* d)
                                 (d->pool_chunks & (d->pool_chunks - 1)) != 0)))
         return KV4_ERR_INVALID_ARG;
     if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
-    if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16) return KV4_ERR_INVALID_ARG;
+    if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16 && d->kind != KV4_KIND_KV8)
+        return KV4_ERR_INVALID_ARG;
     if (d->flags & ~KV4_FLAG_ROTATE_K) return KV4_ERR_INVALID_ARG;
     if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
     int gqa = d->num_q_heads / d->num_kv_heads;
@@ -49,6 +50,7 @@ int validate_desc(const kv4_cache_desc* d)
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
     // the rotation belongs to the quantized keys: the BF16 comparator has none
     if ((d->flags & KV4_FLAG_ROTATE_K) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
+    if (d->kind == KV4_KIND_KV8 && d->num_q_heads != 4 * d->num_kv_heads) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
     if ((int64_t)d->max_pages_per_seq * kv4::kPage > INT32_MAX / 2) return KV4_ERR_CAPACITY;
     return KV4_OK;
@@ -165,8 +167,11 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
                     else hipLaunchKernelGGL((kv4::decode_kv4_mfma_kernel<128, false>), grid, dim3(64), 0, s, a);
                     break;
             }
-        } else
+        } else if (a.g.kind == KV4_KIND_KV8) {
+            hipLaunchKernelGGL(kv4::decode_kv8_mfma_kernel, grid, dim3(64), 0, s, a);
+        } else {
             hipLaunchKernelGGL(kv4::decode_bf16_mfma_kernel, grid, dim3(64), 0, s, a);
+        }
         return;
     }
     switch (a.g.gqa) {
@@ -308,7 +313,10 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     } else {
         int gx = (int)std::min<int64_t>(mean_new, 256);
         dim3 grid(gx, g.Hkv, batch);
-        hipLaunchKernelGGL(kv4::append_bf16_kernel, grid, dim3(64), 0, s, a);
+        if (g.kind == KV4_KIND_KV8)
+            hipLaunchKernelGGL(kv4::append_kv8_kernel, grid, dim3(64), 0, s, a);
+        else
+            hipLaunchKernelGGL(kv4::append_bf16_kernel, grid, dim3(64), 0, s, a);
     }
     return launch_status();
 }

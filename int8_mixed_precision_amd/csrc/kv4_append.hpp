@@ -197,6 +197,45 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
     }
 }
 
+// KV8 kind: INT8 codes and binary16 scales of every new token's K and V (the
+// side entries' encoding, KV4-RL Appendix A.3) into its page.  Grid (x, Hkv,
+// batch), tokens strided over x; lane l holds channels 2l and 2l + 1.  Every
+// byte written belongs to one token, so tokens never race.
+__global__ __launch_bounds__(64) void append_kv8_kernel(AppendArgs a)
+{
+    const Geo& g = a.g;
+    const int b = blockIdx.z, h = blockIdx.y, lane = threadIdx.x;
+    int row0 = clampi(a.cu_new[b], 0, a.total_new);
+    int row1 = clampi(a.cu_new[b + 1], row0, a.total_new);
+    const int cap = g.max_pages * kPage;
+    int p0 = clampi(a.ctx_before[b], 0, cap);
+    int p1 = min(p0 + (row1 - row0), cap);
+    int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    for (int t = p0 + blockIdx.x; t < p1; t += gridDim.x) {
+        int page = clampi(bt[t / kPage], 0, g.num_pages - 1);
+        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
+        int64_t src = ((int64_t)(row0 + (t - p0)) * g.Hkv + h) * g.d;
+        const int tp = t % kPage;
+        uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
+        uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
+        const float k0 = bf16_lo(kk), k1 = bf16_hi(kk), v0 = bf16_lo(vv), v1 = bf16_hi(vv);
+        const uint16_t sk = int8_scale(k0, k1), sv = int8_scale(v0, v1);
+        const double Sk = (double)half_bits_to_float(sk), Sv = (double)half_bits_to_float(sv);
+        const int a0 = int8_code(k0, Sk, sk), a1 = int8_code(k1, Sk, sk);
+        const int b0 = int8_code(v0, Sv, sv), b1 = int8_code(v1, Sv, sv);
+        reinterpret_cast<uint16_t*>(pb + g.off_kc + (int64_t)tp * g.d)[lane] =
+            (uint16_t)((a0 & 0xFF) | ((a1 & 0xFF) << 8));
+        uint8_t* vr = pb + g.off_vc;
+        vr[ring_vbyte(tp, 2 * lane)] = (uint8_t)b0;
+        vr[ring_vbyte(tp, 2 * lane + 1)] = (uint8_t)b1;
+        if (lane == 0) {
+            reinterpret_cast<uint16_t*>(pb + g.off_kdm)[tp] = sk;
+            reinterpret_cast<uint16_t*>(pb + g.off_vm)[tp] = sv;
+        }
+    }
+}
+
 // BF16 comparator: copy the new tokens into bf16 pages.  Grid (x, Hkv, batch),
 // tokens strided over x.
 __global__ __launch_bounds__(64) void append_bf16_kernel(AppendArgs a)

@@ -102,6 +102,15 @@ inline Geo make_geo(const kv4_cache_desc& c)
         g.pb = g.off_vd + 2 * kPage * g.ng;
         g.SR32 = (int)round_up(g.SR, 32);
         g.rb = g.SR > 0 ? (int64_t)g.SR32 * (2 * g.d + 4) : 0;
+    } else if (c.kind == KV4_KIND_KV8) {
+        g.off_kc = 0;                            // K int8 [16][d]
+        g.off_vc = kPage * g.d;                  // V int8, 2 channel-major blocks of 8 tokens
+        g.off_kdm = 2 * kPage * g.d;             // K scales [16] fp16
+        g.off_vm = g.off_kdm + 2 * kPage;        // V scales [16] fp16
+        g.off_vd = g.off_vm + 2 * kPage;
+        g.pb = g.off_vd;
+        g.rb = 0;
+        g.SR32 = 0;
     } else {
         g.pb = (int64_t)kPage * g.d * 2 * 2;
         g.rb = 0;

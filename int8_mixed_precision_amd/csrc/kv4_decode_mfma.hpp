@@ -851,6 +851,221 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
 }
 
 // ---------------------------------------------------------------------------
+// KV8 kind: positions [t_lo, t_hi) of (b, h) from INT8 pages, in 32-token
+// tiles (pages 2t and 2t + 1), with the protected part's matrix-core compute:
+// fp16 QK on (code + 128) subnormals with D started at -128 2^-24 sum(q),
+// score s_K sum D; bf16 PV with w = p' s_V on (code + 128) subnormals and the
+// +128 removed by a ones-column product.  A lane's loads for a tile land in
+// registers and move to a per-wave LDS stage at the start of the tile, so the
+// next tile's loads are in flight during the compute.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
+                                              float* rec, Pace& pace)
+{
+    const Geo& g = a.g;
+    const int lane = threadIdx.x;
+    const int n16 = lane & 15, kb = lane >> 4;
+    const int jq = n16 >> 2, gq = n16 & 3;
+    if (t_hi <= t_lo) return;
+    const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    const uint8_t* hbase = a.pages + (int64_t)a.layer * g.layer_pages + (int64_t)h * g.pb;
+    const int64_t page_stride = (int64_t)g.Hkv * g.pb;
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    const const_i32 btc = (const_i32)bt;
+    auto page = [&](int pi) -> const uint8_t* {
+        const int p = clampi(btc[min(pi, g.max_pages - 1)], 0, g.num_pages - 1);
+        return hbase + (int64_t)p * page_stride;
+    };
+
+    // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
+    u32x4_t aqv;
+    int sc;
+    {
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
+        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
+        amax = fmaxf(amax, dpp<0xB1>(amax));
+        amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
+        sc = 15 - __builtin_amdgcn_frexp_expf(amax);
+        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[2], sc));
+        aqv[1] = pack_f16(ldexpf(q[1], sc), ldexpf(q[3], sc));
+        aqv[2] = pack_f16(ldexpf(q[4], sc), ldexpf(q[6], sc));
+        aqv[3] = pack_f16(ldexpf(q[5], sc), ldexpf(q[7], sc));
+    }
+    float qpart = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
+    const float qblk = rows_sum(qpart);
+    f32x4_t dinit;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dinit[r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
+    const float c2 = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
+
+    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
+    float m_sh = -INFINITY, l_run = 0.f;
+    __shared__ uint4 stage8[8][64];
+    __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
+
+    // landing registers of one tile
+    uint4 lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3, lsv;
+    uint32_t lsk0, lsk1;
+    const uint32_t kofs = (uint32_t)(g.off_kc + n16 * g.d + 32 * kb);
+    const uint32_t vofs = (uint32_t)(g.off_vc + (kb & 1) * 8 * g.d + 64 * n16);
+    const uint32_t svofs = (uint32_t)(g.off_vm + 16 * (kb & 1));
+    auto load = [&](const uint8_t* P0, const uint8_t* P1) {
+        lk0 = *reinterpret_cast<const uint4*>(P0 + kofs);
+        lk1 = *reinterpret_cast<const uint4*>(P0 + kofs + 16);
+        lk2 = *reinterpret_cast<const uint4*>(P1 + kofs);
+        lk3 = *reinterpret_cast<const uint4*>(P1 + kofs + 16);
+        const uint8_t* PV = (kb >> 1) ? P1 : P0;
+        lv0 = *reinterpret_cast<const uint4*>(PV + vofs);
+        lv1 = *reinterpret_cast<const uint4*>(PV + vofs + 16);
+        lv2 = *reinterpret_cast<const uint4*>(PV + vofs + 32);
+        lv3 = *reinterpret_cast<const uint4*>(PV + vofs + 48);
+        lsk0 = reinterpret_cast<const uint16_t*>(P0 + g.off_kdm)[n16];
+        lsk1 = reinterpret_cast<const uint16_t*>(P1 + g.off_kdm)[n16];
+        lsv = *reinterpret_cast<const uint4*>(PV + svofs);
+    };
+
+    const int tile_first = t_lo / 32, tile_end = (t_hi + 31) / 32;
+    const uint8_t* T0 = page(2 * tile_first);
+    const uint8_t* T1 = page(2 * tile_first + 1);
+    load(T0, T1);
+    const uint8_t* C0 = page(2 * tile_first + 2);
+    const uint8_t* C1 = page(2 * tile_first + 3);
+    for (int tl = tile_first; tl < tile_end; ++tl) {
+        pace.tile(tile_end - tl);
+        // ---- this tile to the stage, then the next tile's loads (the last
+        // tile re-reads its own pages: cache hits)
+        stage8[0][lane] = lk0;
+        stage8[1][lane] = lk1;
+        stage8[2][lane] = lk2;
+        stage8[3][lane] = lk3;
+        stage8[4][lane] = lv0;
+        stage8[5][lane] = lv1;
+        stage8[6][lane] = lv2;
+        stage8[7][lane] = lv3;
+        const float sk0 = half_bits_to_float((uint16_t)lsk0);
+        const float sk1 = half_bits_to_float((uint16_t)lsk1);
+        const uint4 svp = lsv;
+        __builtin_amdgcn_wave_barrier();
+        const bool more = tl + 1 < tile_end;
+        const uint8_t* N0 = more ? C0 : T0;
+        const uint8_t* N1 = more ? C1 : T1;
+        C0 = page(2 * tl + 4);
+        C1 = page(2 * tl + 5);
+        load(N0, N1);
+        T0 = N0;
+        T1 = N1;
+
+        // ---- QK
+        f32x4_t D0 = dinit, D1 = dinit;
+        {
+            const uint4 k00 = stage8[0][lane], k01 = stage8[1][lane];
+            const uint4 k10 = stage8[2][lane], k11 = stage8[3][lane];
+            const uint32_t kw0[8] = {k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w};
+            const uint32_t kw1[8] = {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w};
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint64_t rows = 0x1111111111111111ull << bb;
+                const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
+                                   keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
+                D0 = mfma_f16(A, widen_i8(kw0[2 * bb], kw0[2 * bb + 1]), D0);
+                D1 = mfma_f16(A, widen_i8(kw1[2 * bb], kw1[2 * bb + 1]), D1);
+            }
+        }
+        const int tok0 = 32 * tl + n16;
+        const bool ok0 = tok0 >= t_lo && tok0 < t_hi;
+        const bool ok1 = tok0 + 16 >= t_lo && tok0 + 16 < t_hi;
+        float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
+        float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2;
+        s0 = ok0 ? s0 : -INFINITY;
+        s1 = ok1 ? s1 : -INFINITY;
+        const float mx = row16_max(fmaxf(s0, s1));
+        {
+            const bool grow = mx > m_sh + (kPScale + kSlack);
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? mx - kPScale : m_sh;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
+                m_sh = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
+                W *= alpha;
+            }
+        }
+        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
+        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
+        l_run += p0 + p1;
+        pbuf8[kb][n16] = p0;
+        pbuf8[kb][16 + n16] = p1;
+        __builtin_amdgcn_wave_barrier();
+        const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb]);
+        const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb + 4]);
+
+        // ---- PV: w = p' s_V of head jq, tokens 32 tl + 8 kb + e
+        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // tokens outside the run may have garbage scales: select, do not multiply
+            const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
+            const int tok = 32 * tl + 8 * kb + e;
+            wv[e] = tok >= t_lo && tok < t_hi ? w : 0.0f;
+        }
+        u32x4_t ahi, alo;
+        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hw, lw;
+            split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
+            ahi[i] = hw;
+            alo[i] = lw;
+        }
+        const uint4 v0 = stage8[4][lane], v1 = stage8[5][lane];
+        const uint4 v2 = stage8[6][lane], v3 = stage8[7][lane];
+        const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const uint64_t rows = 0x1111111111111111ull << blk;
+            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+            const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
+            const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
+            E[0] = mfma_bf16(bh, b0, E[0]);
+            E[1] = mfma_bf16(bh, b1, E[1]);
+            E[0] = mfma_bf16(bl, b0, E[0]);
+            E[1] = mfma_bf16(bl, b1, E[1]);
+        }
+        W = mfma_bf16(ahi, ones, W);
+        W = mfma_bf16(alo, ones, W);
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
+    const float l = row16_sum(l_run);
+    const float inv = 1.0f / l;
+    float* dst = rec + kb * (g.d + kPartPad);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        dst[32 * r + n16] = (ldexpf(E[0][r], 133) - 128.0f * W[0]) * inv;
+        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) - 128.0f * W[0]) * inv;
+    }
+    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
+}
+
+// ---------------------------------------------------------------------------
 // BF16 comparator split (same tiling; keys and values used as stored).
 //   QK: rows = 16 tokens, k = 8 consecutive channels per k-block, columns =
 //       (head j, 0): only column block 0 of each head is non-zero.
@@ -978,6 +1193,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_kv4<G, ROT>(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// KV8 kind: every position from INT8 pages (no protected parts).
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_kv8_mfma_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int, int) {},
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_kv8(a, b, h, lo, hi, rec, pace);
                });
 }
 

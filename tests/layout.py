@@ -112,6 +112,31 @@ def protected_mask(n: int, S: int, R: int) -> np.ndarray:
     return (p < min(S, n)) | (p >= max(S, n - R))
 
 
+def pb_kv8_bytes(d: int) -> int:
+    return PAGE * (2 * d + 4)
+
+
+def gather_kv8(pages: np.ndarray, *, layer, num_pages, Hkv, d, block_tables, slot, n):
+    """KV8 kind: k8, v8 (int8 [n, Hkv, d]) and k8s, v8s (uint16 [n, Hkv]) of
+    positions [0, n) of the sequence in `slot`."""
+    PB = pb_kv8_bytes(d)
+    p = np.arange(n, dtype=np.int64)
+    page = block_tables[slot, p // PAGE].astype(np.int64)
+    tp = p % PAGE
+    h = np.arange(Hkv, dtype=np.int64)
+    base = ((layer * num_pages + page[:, None]) * Hkv + h[None, :]) * PB          # [n, Hkv]
+    c = np.arange(d)[None, None, :]
+    k8 = pages[base[:, :, None] + tp[:, None, None] * d + c].view(np.int8)
+    v8 = pages[base[:, :, None] + PAGE * d + ring_vbyte(tp[:, None, None], c, d)].view(np.int8)
+
+    def u16(idx):
+        return pages[idx].astype(np.uint16) | (pages[idx + 1].astype(np.uint16) << 8)
+
+    k8s = u16(base + 2 * PAGE * d + 2 * tp[:, None])
+    v8s = u16(base + 2 * PAGE * d + 2 * PAGE + 2 * tp[:, None])
+    return dict(k8=k8, v8=v8, k8s=k8s, v8s=v8s)
+
+
 def gather_bf16(pages: np.ndarray, *, layer, num_pages, Hkv, d, block_tables, slot, n):
     """K and V (float32 [n, Hkv, d]) of the BF16 kind's pages."""
     PB = PAGE * d * 2 * 2

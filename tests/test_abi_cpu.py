@@ -60,6 +60,11 @@ def test_storage_sizes_match_pages():
     pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
     assert side == 2 * 5 * 8 * L.rb_bytes(128, 132) and L.rb_bytes(128, 132) == 160 * 260
     assert pages == 2 * 7 * 8 * 2560
+    # KV8 kind: 16 tokens x (2*d int8 codes + 2 binary16 scales) per PB, no side pool
+    d = kv4.make_desc(3, 16, 4, kind=kv4.KV4_KIND_KV8, num_pages=5, max_slots=2, max_pages_per_seq=3)
+    pages, side, per_layer = kv4.kv4_cache_required_bytes(d)
+    assert side == 0 and L.pb_kv8_bytes(128) == 4160
+    assert per_layer == 4 * 4160 and pages == 3 * 5 * per_layer
 
 
 def _err(fn, *a):
@@ -93,6 +98,10 @@ def test_invalid_descriptors():
         (dict(pool_chunks=1 << 17), kv4.KV4_ERR_INVALID_ARG),
         (dict(num_q_heads=48, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
+        (dict(kind=kv4.KV4_KIND_KV8), kv4.KV4_OK),
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_ERR_UNSUPPORTED),     # GQA 2
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=64), kv4.KV4_ERR_UNSUPPORTED),     # GQA 8
+        (dict(kind=kv4.KV4_KIND_KV8, flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
     ]
     for change, code in cases:
         d = kv4.make_desc(**{**base, **change})

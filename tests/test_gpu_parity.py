@@ -358,6 +358,60 @@ def test_bf16_comparator():
 
 
 # ---------------------------------------------------------------------------
+# KV8 kind (KV4-RL Fig. 3b / Fig. 4a comparison point): every position holds
+# the side entries' INT8 encoding; bytes are compared with the oracle's INT8
+# copies of every position, outputs with its fp64 attention when every
+# position is protected (S = 0, R >= n).
+# ---------------------------------------------------------------------------
+
+def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0):
+    Hq = 4 * Hkv
+    n = np.asarray(ctx, np.int64) + 1
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, seed=seed, batch=len(ctx),
+                   ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
+    ks, vs = W.all_kv_sources(cfg, layer, n)
+    q = W.queries(cfg, layer)
+    built = H.make_cache(Hq, Hkv, 32, 0, 0, n, layers=layers, kind=kv4.KV4_KIND_KV8, waves=waves,
+                         seed=seed)
+    _fill_garbage(built)
+    H.build_from_sources(built, layer, ks, vs, ctx)
+    out = H.decode(built, layer, q, n).cpu().numpy()
+    oc = oracle.MixedCache(ks, vs, 32)
+    pages, _ = H.pools_host(built)
+    for b in range(len(ctx)):
+        got = L.gather_kv8(pages, layer=layer, num_pages=built.desc.num_pages, Hkv=Hkv, d=128,
+                           block_tables=built.bt_host, slot=int(built.slots_host[b]), n=int(n[b]))
+        sl = oc.seq(b)
+        for name in ("k8", "v8", "k8s", "v8s"):
+            want = getattr(oc, name)[sl]
+            if not np.array_equal(got[name], want):
+                bad = np.argwhere(got[name] != want)[0]
+                raise AssertionError(f"seq {b} {name} mismatch at {tuple(bad)}")
+    want = oracle.attend_mixed(q, oc, 0, int(n.max()), 1 / math.sqrt(128))
+    err = H.check_output(out, want, ATOL, RTOL)
+    H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
+    return out
+
+
+@pytest.mark.parametrize("Hkv", [1, 2, 8])
+def test_kv8_kind(Hkv):
+    ctx = [0, 14, 15, 16, 30, 31, 32, 33, 63, 64, 300, 1000, 2500]
+    H.log(f"case kv8 Hkv={Hkv}")
+    out = _kv8_case(Hkv, ctx, seed=80 + Hkv)
+    for waves in (1, 5):
+        H.log(f"case kv8 Hkv={Hkv} waves={waves}")
+        o2 = _kv8_case(Hkv, ctx, seed=80 + Hkv, waves=waves)
+        assert np.abs(o2 - out).max() <= 5e-5
+
+
+def test_kv8_layers_and_long_context():
+    H.log("case kv8, 3 layers, layer 2, waves 7")
+    _kv8_case(2, [33, 150, 401, 1200], seed=91, layers=3, layer=2, waves=7)
+    H.log("case kv8 long 9000 + short")
+    _kv8_case(4, [9000, 1, 47], seed=92)
+
+
+# ---------------------------------------------------------------------------
 # Keys stored in the rotated basis (KV4-RL Section 5.1, Appendix A.3): the
 # append rotates k before both quantizers, the decode rotates q; bytes are
 # compared with the oracle's quantization of wht(k), outputs with its fp64
