@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-kv8", action="store_true",
                     help="skip the KV8 comparator (INT8 pages for every position)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="INT4 group size of the KV4 cache (0 = the config's, 32)")
+    ap.add_argument("--populate-reps", type=int, default=5,
+                    help="timed bulk appends of the first 32 sequences' histories (0 = skip)")
     ap.add_argument("--rotate", action="store_true",
                     help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -117,6 +121,18 @@ def append_bytes_kv4(n, cfg):
     ng = cfg.head_dim // cfg.group
     wr = B * cfg.kv_heads * (cfg.head_dim + 8 * ng + (2 * cfg.head_dim + 4 if cfg.recent > 0 else 0))
     return rd + wr
+
+
+def populate_bytes_kv4(hist, cfg):
+    """Bulk append of whole histories (prefill populate): reads bf16 k, v;
+    writes every position's INT4 entry and the INT8 entries of the positions
+    protected at the new length."""
+    T = int(np.sum(hist))
+    ng = cfg.head_dim // cfg.group
+    rd = T * cfg.kv_heads * cfg.head_dim * 2 * 2
+    wr4 = T * cfg.kv_heads * (cfg.head_dim + 8 * ng)
+    wr8 = int(np.sum(np.minimum(hist, cfg.sink + cfg.recent))) * cfg.kv_heads * (2 * cfg.head_dim + 4)
+    return rd + wr4 + wr8
 
 
 def append_bytes_bf16(n, cfg):
@@ -228,6 +244,8 @@ def main():
     from tests import gpu_harness as H
 
     cfg = W.CONFIGS[args.config]
+    if args.group:
+        cfg = W.scaled(cfg, group=args.group)
     ctx = W.contexts(cfg)
     n = ctx + 1
     B = cfg.batch
@@ -252,9 +270,21 @@ def main():
         caches.append(("kv8", k8c))
     # build every cache from the same sources, sequence chunk by chunk
     step_k, step_v = [], []
+    pop = None
     for lo in range(0, B, 32):
         seqs = list(range(lo, min(B, lo + 32)))
         ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
+        if lo == 0 and args.populate_reps > 0:
+            # the first chunk's histories, kept on the device for the populate timing
+            hist = np.array([int(ctx[s]) for s in seqs])
+            pcu = np.zeros(len(seqs) + 1, np.int32)
+            pcu[1:] = np.cumsum(hist)
+            pop = dict(hist=hist,
+                       k=H.to_dev_bf16(np.concatenate([ks[i][:hist[i]] for i in range(len(seqs))], 0), "cuda:0"),
+                       v=H.to_dev_bf16(np.concatenate([vs[i][:hist[i]] for i in range(len(seqs))], 0), "cuda:0"),
+                       cu=torch.from_numpy(pcu).to(dev),
+                       ctx0=torch.zeros(len(seqs), dtype=torch.int32, device=dev),
+                       slots=torch.from_numpy(kv4c.slots_host[seqs]).to(dev))
         for _, c in caches:
             H.append_chunks(c, 0, [ks[i][:int(ctx[s])] for i, s in enumerate(seqs)],
                             [vs[i][:int(ctx[s])] for i, s in enumerate(seqs)], [0] * len(seqs),
@@ -333,6 +363,35 @@ def main():
             f"merge {tm.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
             f"(median {np.median(td) * 1e3:.1f}), waves {waves}, pool chunks {chunks}")
 
+    # bulk populate: the first 32 sequences' histories re-appended whole (after
+    # every decode timing: it rewrites ring entries the step token owns)
+    populate = None
+    if pop is not None:
+        c = kv4c
+        T = int(pop["hist"].sum())
+
+        def bulk():
+            kv4.kv4_append(c.cache.handle, 0, pop["k"], pop["v"], pop["cu"], pop["ctx0"],
+                           pop["slots"], c.block_tables, len(pop["hist"]), T, stream)
+
+        bulk()
+        torch.cuda.synchronize()
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.populate_reps)]
+        for e0, e1 in pe:
+            e0.record(stream)
+            bulk()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
+        pbytes = populate_bytes_kv4(pop["hist"], cfg)
+        populate = {"sequences": len(pop["hist"]), "tokens": T, "us": round(pms * 1e3, 2),
+                    "alg_bytes": pbytes, "gbs": round(pbytes / (pms * 1e-3) / 1e9, 2),
+                    "frac_hbm_peak": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": round(T / (pms * 1e-3), 1)}
+        log(f"populate: {T} tokens in {pms * 1e3:.1f} us ({populate['gbs']} GB/s)")
+        del pop
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -350,7 +409,8 @@ def main():
     decode_gbs = db / (r["decode_ms"] * 1e-3) / 1e9
     achieved = pb / (r["partials_ms"] * 1e-3) / 1e9
     traffic = None
-    if os.path.exists(args.traffic_json) and not args.rotate:   # counters of the unrotated kernel
+    # the stored counters are those of the default workload (unrotated, group 32)
+    if os.path.exists(args.traffic_json) and not args.rotate and cfg.group == 32:
         try:
             tj = json.load(open(args.traffic_json))
             if tj.get("kernel_source_hash") == _kernel_hash():
@@ -373,7 +433,7 @@ def main():
         "config": {
             "workload": "Qwen3-8B-shaped attention layer, batch 256 ragged decode step "
                         "(lognormal contexts median 4k, max 16k), 32q/8kv heads, d=128, "
-                        "page 16, INT4 group 32, S=4, R=128",
+                        f"page 16, INT4 group {cfg.group}, S=4, R=128",
             "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
             "waves": r["waves"], "pool_chunks": r["pool_chunks"], "rotate_k": bool(args.rotate),
@@ -410,6 +470,8 @@ def main():
         line["speedup_vs_bf16_step"] = round(bstep / step_ms, 3)
         line["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
 
+    if populate is not None:
+        line["populate"] = populate
     if "kv8" in results:
         r8 = results["kv8"]
         p8 = partial_bytes_kv8(n, cfg)
