@@ -302,7 +302,7 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     // parallelism along each sequence sized by the mean number of new tokens
     int64_t mean_new = ((int64_t)total_new + batch - 1) / batch;
     if (g.kind == KV4_KIND_MIXED) {
-        int gx = (int)std::min<int64_t>((mean_new + kv4::kHalf - 1) / kv4::kHalf + 1, 64);
+        int gx = (int)std::min<int64_t>((mean_new + kv4::kHalf - 1) / kv4::kHalf + 1, 256);
         if (mean_new <= 1) gx = 1;
         dim3 grid(gx, g.Hkv, batch);
         switch (g.G) {

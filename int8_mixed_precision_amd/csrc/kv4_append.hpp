@@ -133,10 +133,22 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
         uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hp & 1) * g.d;
         const int q0 = vpos(2 * lane), q1 = vpos(2 * lane + 1);
         uint32_t w0 = vw[q0], w1 = vw[q1];
-        for (int t = t_lo; t < t_hi; ++t) {
-            int64_t src = ((int64_t)(row0 + (t - p0)) * g.Hkv + h) * g.d;
-            uint32_t kk = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
-            uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
+        // every token of the half page is loaded before the first is quantized
+        // (one load latency per half page in a bulk append)
+        uint32_t kkr[kHalf], vvr[kHalf];
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) {
+            if (t_lo + i < t_hi) {
+                const int64_t src = ((int64_t)(row0 + (t_lo + i - p0)) * g.Hkv + h) * g.d;
+                kkr[i] = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
+                vvr[i] = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kHalf; ++i) {
+            const int t = t_lo + i;
+            if (t >= t_hi) break;
+            const uint32_t kk = kkr[i], vv = vvr[i];
             float k0 = bf16_lo(kk), k1 = bf16_hi(kk), v0 = bf16_lo(vv), v1 = bf16_hi(vv);
             if (g.rot) {
                 // keys in the rotated basis; lane l holds channels 2l, 2l + 1
