@@ -44,17 +44,49 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// DPP move inside a 16-lane row (every lane active, every source in the row).
+template <int CTRL>
+__device__ __forceinline__ float row_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Minimum and maximum over aligned groups of LANES (16, 32 or 64) lanes: quad
+// swaps and row rotations inside each 16-lane row, then the row swaps of
+// v_permlane16_swap / v_permlane32_swap.  Exact for any order.
+template <int LANES>
+__device__ __forceinline__ void group_minmax(float& lo, float& hi)
+{
+    static_assert(LANES == 16 || LANES == 32 || LANES == 64, "group of 16, 32 or 64 lanes");
+    lo = fminf(lo, row_mov<0xB1>(lo));          // quad_perm [1,0,3,2]
+    hi = fmaxf(hi, row_mov<0xB1>(hi));
+    lo = fminf(lo, row_mov<0x4E>(lo));          // quad_perm [2,3,0,1]
+    hi = fmaxf(hi, row_mov<0x4E>(hi));
+    lo = fminf(lo, row_mov<0x124>(lo));         // row_ror 4
+    hi = fmaxf(hi, row_mov<0x124>(hi));
+    lo = fminf(lo, row_mov<0x128>(lo));         // row_ror 8
+    hi = fmaxf(hi, row_mov<0x128>(hi));
+    if constexpr (LANES >= 32) {
+        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+        lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+        hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+    if constexpr (LANES == 64) {
+        auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+        lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+        hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+}
+
 // INT4 parameters of a group whose values are spread over `lanes` consecutive
 // lanes (two channels per lane).  Returns Delta and m bit patterns.
 template <int LANES>
 __device__ __forceinline__ void int4_params(float x0, float x1, uint16_t& db, uint16_t& mb)
 {
     float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
-#pragma unroll
-    for (int off = 1; off < LANES; off <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, off));
-        hi = fmaxf(hi, __shfl_xor(hi, off));
-    }
+    group_minmax<LANES>(lo, hi);
     mb = plus_zero16(f32_to_f16_bits(lo));
     float mf = half_bits_to_float(mb);
     float r = hi - mf;
@@ -62,7 +94,7 @@ __device__ __forceinline__ void int4_params(float x0, float x1, uint16_t& db, ui
     if (r > 0.0f) db = plus_zero16(f32_to_f16_bits(__fdiv_rn(r, 15.0f)));
 }
 
-__device__ __forceinline__ uint32_t int4_code(float x, double D, double M, uint16_t db)
+__device__ __forceinline__ uint32_t int4_code_exact(float x, double D, double M, uint16_t db)
 {
     if (db == 0) return 0u;
     double xv = (double)x;
@@ -78,7 +110,7 @@ __device__ __forceinline__ uint32_t int4_code(float x, double D, double M, uint1
     return (uint32_t)c;
 }
 
-__device__ __forceinline__ int int8_code(float x, double S, uint16_t sb)
+__device__ __forceinline__ int int8_code_exact(float x, double S, uint16_t sb)
 {
     if (sb == 0) return 0;
     double a = fabs((double)x);
@@ -94,12 +126,41 @@ __device__ __forceinline__ int int8_code(float x, double S, uint16_t sb)
     return x < 0.0f ? -c : c;
 }
 
+// Binary32 fast paths of the two code decisions, with the same results.  With
+// x, m and Delta (or s) exact binary32 values, u = fl(x - m) * rcp(Delta) has a
+// relative error below 2^-22 (one rounding in the difference, 1 ulp in
+// v_rcp_f32, one in the product), i.e. below 4e-6 for |u| < 16 and below 3.1e-5
+// for |u| < 128.  Away from a midpoint between two admissible codes by more than
+// 2^-14 (INT4) or 2^-11 (INT8) the nearest integer to u is therefore the exact
+// nearest code; near a midpoint, or for non-finite operands, the binary64 test
+// above decides.
+__device__ __forceinline__ uint32_t int4_code(float x, float Df, float Mf, uint16_t db)
+{
+    if (db == 0) return 0u;
+    const float u = (x - Mf) * __builtin_amdgcn_rcpf(Df);
+    const float fl = floorf(u);
+    const bool near = fabsf(u - fl - 0.5f) < 0x1p-14f && fl >= 0.0f && fl <= 14.0f;
+    if (near || !(fabsf(u) < 64.0f) || !(Df < 65536.0f))
+        return int4_code_exact(x, (double)Df, (double)Mf, db);
+    return (uint32_t)fminf(fmaxf(rintf(u), 0.0f), 15.0f);
+}
+
+__device__ __forceinline__ int int8_code(float x, float Sf, uint16_t sb)
+{
+    if (sb == 0) return 0;
+    const float u = fabsf(x) * __builtin_amdgcn_rcpf(Sf);
+    const float fl = floorf(u);
+    const bool near = fabsf(u - fl - 0.5f) < 0x1p-11f && fl <= 126.0f;
+    if (near || !(u < 256.0f) || !(Sf < 65536.0f)) return int8_code_exact(x, (double)Sf, sb);
+    const int c = (int)fminf(rintf(u), 127.0f);
+    return x < 0.0f ? -c : c;
+}
+
 // Full-wave (64 lanes, 128 channels) INT8 scale.
 __device__ __forceinline__ uint16_t int8_scale(float x0, float x1)
 {
-    float a = fmaxf(fabsf(x0), fabsf(x1));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+    float a = fmaxf(fabsf(x0), fabsf(x1)), unused = a;
+    group_minmax<64>(unused, a);
     return plus_zero16(f32_to_f16_bits(__fdiv_rn(a, 127.0f)));
 }
 
@@ -164,7 +225,7 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             // ---- INT4, keys
             uint16_t db, mb;
             int4_params<LPG>(k0, k1, db, mb);
-            double D = (double)half_bits_to_float(db), M = (double)half_bits_to_float(mb);
+            float D = half_bits_to_float(db), M = half_bits_to_float(mb);
             uint32_t c0 = int4_code(k0, D, M, db), c1 = int4_code(k1, D, M, db);
             pb[g.off_kc + tp * (g.d / 2) + 4 * kpos(lane >> 2) + (lane & 3)] = (uint8_t)(c0 | (c1 << 4));
             if ((lane % LPG) == 0) {
@@ -174,8 +235,8 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             }
             // ---- INT4, values
             int4_params<LPG>(v0, v1, db, mb);
-            D = (double)half_bits_to_float(db);
-            M = (double)half_bits_to_float(mb);
+            D = half_bits_to_float(db);
+            M = half_bits_to_float(mb);
             c0 = int4_code(v0, D, M, db);
             c1 = int4_code(v1, D, M, db);
             int sh = 4 * (t % kHalf);
@@ -189,7 +250,7 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
             if (ring != nullptr && (t < g.S || t >= p1 - g.R)) {
                 int e = t < g.S ? t : g.S + (t - g.S) % g.R;
                 uint16_t sk = int8_scale(k0, k1), sv = int8_scale(v0, v1);
-                double Sk = (double)half_bits_to_float(sk), Sv = (double)half_bits_to_float(sv);
+                const float Sk = half_bits_to_float(sk), Sv = half_bits_to_float(sv);
                 int a0 = int8_code(k0, Sk, sk), a1 = int8_code(k1, Sk, sk);
                 int b0 = int8_code(v0, Sv, sv), b1 = int8_code(v1, Sv, sv);
                 reinterpret_cast<uint16_t*>(ring + (int64_t)e * g.d)[lane] =
@@ -233,7 +294,7 @@ __global__ __launch_bounds__(64) void append_kv8_kernel(AppendArgs a)
         uint32_t vv = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
         const float k0 = bf16_lo(kk), k1 = bf16_hi(kk), v0 = bf16_lo(vv), v1 = bf16_hi(vv);
         const uint16_t sk = int8_scale(k0, k1), sv = int8_scale(v0, v1);
-        const double Sk = (double)half_bits_to_float(sk), Sv = (double)half_bits_to_float(sv);
+        const float Sk = half_bits_to_float(sk), Sv = half_bits_to_float(sv);
         const int a0 = int8_code(k0, Sk, sk), a1 = int8_code(k1, Sk, sk);
         const int b0 = int8_code(v0, Sv, sv), b1 = int8_code(v1, Sv, sv);
         reinterpret_cast<uint16_t*>(pb + g.off_kc + (int64_t)tp * g.d)[lane] =
