@@ -46,8 +46,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
+        build(force=False)                      # (re)builds when missing or older than the source
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
@@ -67,6 +66,8 @@ def lib():
         L.orc_attend_mixed.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P,
                                        P, P, P, P, P, P, P, P, P, P, P]
         L.orc_attend_dense.argtypes = [i32, P, P, i32, i32, i32, dbl, P, P, P, P]
+        L.orc_attend_int.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P,
+                                     P, P, P, P, P, P, P, P, P, P, dbl, P, P]
         L.orc_num_threads.restype = i32
         _lib = L
     return _lib
@@ -239,6 +240,31 @@ def attend_mixed(q, cache: MixedCache, S: int, R: int, sm_scale: float,
                            _ptr(c.k8), _ptr(c.k8s), _ptr(c.v8), _ptr(c.v8s),
                            _ptr(out))
     return out
+
+
+def attend_int(q, cache: MixedCache, S: int, R: int, sm_scale: float, eps: float = 2.0 ** -6,
+               seq_lens=None):
+    """The integer decode path (KV4-RL Appendix A.3; readings I-1 .. I-6 in
+    kv4_oracle.c): INT8 q per (sequence, q head), integer QK with the affine
+    fold, binary64 softmax, an 8-bit probability operand per (8-position block,
+    value group, q head) for the INT4 values, full-precision PV for the
+    protected ones.  Returns (out, bound), both float64 [B, Hq, d]; bound is the
+    largest change of out if every code within eps of a rounding tie moved by
+    one.  q must already be in the keys' basis when the cache is rotated."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
+    B, Hq, d = q.shape
+    sl = cache.seq_lens if seq_lens is None else np.ascontiguousarray(np.asarray(seq_lens, np.int32))
+    assert np.all(sl <= cache.seq_lens)
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    bound = np.empty((B, Hq, d), dtype=np.float64)
+    c = cache
+    lib().orc_attend_int(B, _ptr(sl), _ptr(c.pos_off), Hq, c.Hkv, d, c.G, S, R,
+                         float(sm_scale), _ptr(q),
+                         _ptr(c.k4), _ptr(c.k4d), _ptr(c.k4m),
+                         _ptr(c.v4), _ptr(c.v4d), _ptr(c.v4m),
+                         _ptr(c.k8), _ptr(c.k8s), _ptr(c.v8), _ptr(c.v8s),
+                         float(eps), _ptr(out), _ptr(bound))
+    return out, bound
 
 
 def attend_mixed_raw(q, seq_lens, pos_off, Hkv, G, S, R, sm_scale,

@@ -340,6 +340,131 @@ void orc_attend_dense(int B, const int32_t* seq_lens, const int64_t* pos_off,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* The integer decode path (KV4-RL Appendix A.3, "Integer decode path" and   */
+/* "Protected path and reconstruction"; Section 5.3), in binary64.           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages state the steps (INT8 query; integer QK on widened INT4 codes with
+ * the scales and offsets applied to the integer sums; FP32 softmax; an 8-bit
+ * probability operand carrying the value scales for an integer PV with an
+ * affine correction; integer QK and higher-precision PV for the protected
+ * positions) but not the operand scales.  Readings:
+ *   I-1 q (already in the keys' basis when keys are rotated) is quantized per
+ *       (sequence, q head) with Q-4: scale s_q, codes qi.
+ *   I-2 INT4 position t: score = sm_scale * s_q * sum_g (Delta_g I_g + m_g Q_g),
+ *       I_g = sum_{c in g} qi_c k4_c and Q_g = sum_{c in g} qi_c (integers).
+ *   I-3 protected position t: score = sm_scale * s_q * s_k * sum_c qi_c k8_c.
+ *   I-4 p_t = exp(score_t - max) over the whole context; the normalizer is
+ *       sum_t p_t of the unquantized probabilities.
+ *   I-5 8-bit probability operand: INT4 positions are cut into blocks
+ *       [8k, 8k + 8) (a half page, the unit of the stored V codes); per block
+ *       B, value group g and q head, w_t = p_t Delta^v_{t,g},
+ *       sigma = max_{t in B} w_t / 255 and u_t = the integer nearest to
+ *       w_t / sigma (ties to even; 0 when sigma = 0).
+ *   I-6 numerator of channel c: over INT4 positions
+ *       sum_B sigma_B sum_t u_t v4_{t,c} + sum_t p_t m^v_{t,g(c)}; over protected
+ *       positions sum_t p_t s_v v8_{t,c} (no probability quantization).
+ * The pages merge the two regions' outputs by their log-normalizers (eq. A1);
+ * the codes u do not depend on the reference maximum, so that merge reaches
+ * this single-softmax result in exact arithmetic.
+ *
+ * bound[c] is the change of out[c] if every code u whose w/sigma lies within
+ * eps of a half-integer moved by one: sum of sigma_B v4_{t,c} over those codes,
+ * divided by the normalizer.  (An implementation computing p in lower
+ * precision may round exactly those codes the other way.)
+ */
+void orc_attend_int(int B, const int32_t* seq_lens, const int64_t* pos_off,
+                    int Hq, int Hkv, int d, int G, int S, int R, double sm_scale,
+                    const float* q,
+                    const uint8_t* k4, const uint16_t* k4d, const uint16_t* k4m,
+                    const uint8_t* v4, const uint16_t* v4d, const uint16_t* v4m,
+                    const int8_t* k8, const uint16_t* k8s,
+                    const int8_t* v8, const uint16_t* v8s,
+                    double eps, double* out, double* bound)
+{
+    int ng = d / G;
+    int gqa = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bj = 0; bj < (int64_t)B * Hq; ++bj) {
+        int b = (int)(bj / Hq), j = (int)(bj % Hq);
+        int h = j / gqa;
+        int64_t n = seq_lens[b];
+        const float* qj = q + ((int64_t)b * Hq + j) * d;
+        double* o = out + ((int64_t)b * Hq + j) * d;
+        double* bd = bound + ((int64_t)b * Hq + j) * d;
+        int8_t* qi = (int8_t*)malloc((size_t)d);
+        uint16_t sqb;
+        orc_quant_int8_vec(qj, d, qi, &sqb);                       /* I-1 */
+        double sq = orc_f16_to_f64(sqb);
+        double* p = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t row = (pos_off[b] + t) * Hkv + h;
+            double acc = 0.0;
+            if (orc_is_protected(t, n, S, R)) {                    /* I-3 */
+                int64_t I = 0;
+                for (int c = 0; c < d; ++c) I += (int64_t)qi[c] * (int64_t)k8[row * d + c];
+                acc = orc_f16_to_f64(k8s[row]) * (double)I;
+            } else {                                               /* I-2 */
+                for (int g = 0; g < ng; ++g) {
+                    int64_t I = 0, Q = 0;
+                    for (int c = g * G; c < (g + 1) * G; ++c) {
+                        I += (int64_t)qi[c] * (int64_t)k4[row * d + c];
+                        Q += qi[c];
+                    }
+                    acc += orc_f16_to_f64(k4d[row * ng + g]) * (double)I +
+                           orc_f16_to_f64(k4m[row * ng + g]) * (double)Q;
+                }
+            }
+            p[t] = sm_scale * sq * acc;
+            if (p[t] > smax) smax = p[t];
+        }
+        double den = 0.0;                                          /* I-4 */
+        for (int64_t t = 0; t < n; ++t) { p[t] = exp(p[t] - smax); den += p[t]; }
+        for (int c = 0; c < d; ++c) { o[c] = 0.0; bd[c] = 0.0; }
+        for (int64_t t = 0; t < n; ++t) {                          /* I-6, protected */
+            if (!orc_is_protected(t, n, S, R)) continue;
+            int64_t row = (pos_off[b] + t) * Hkv + h;
+            double sv = orc_f16_to_f64(v8s[row]);
+            for (int c = 0; c < d; ++c) o[c] += p[t] * (sv * (double)v8[row * d + c]);
+        }
+        for (int64_t t0 = 0; t0 < n; t0 += 8) {                    /* I-5, I-6, INT4 blocks */
+            int64_t t1 = t0 + 8 < n ? t0 + 8 : n;
+            for (int g = 0; g < ng; ++g) {
+                double wmax = 0.0;
+                for (int64_t t = t0; t < t1; ++t) {
+                    if (orc_is_protected(t, n, S, R)) continue;
+                    int64_t row = (pos_off[b] + t) * Hkv + h;
+                    double w = p[t] * orc_f16_to_f64(v4d[row * ng + g]);
+                    if (w > wmax) wmax = w;
+                }
+                double sigma = wmax / 255.0;
+                for (int64_t t = t0; t < t1; ++t) {
+                    if (orc_is_protected(t, n, S, R)) continue;
+                    int64_t row = (pos_off[b] + t) * Hkv + h;
+                    double u = 0.0;
+                    int near = 0;
+                    if (sigma > 0.0) {
+                        double x = p[t] * orc_f16_to_f64(v4d[row * ng + g]) / sigma;
+                        u = rint(x);
+                        near = fabs(x - floor(x) - 0.5) < eps;
+                    }
+                    double mv = orc_f16_to_f64(v4m[row * ng + g]);
+                    for (int c = g * G; c < (g + 1) * G; ++c) {
+                        o[c] += sigma * u * (double)v4[row * d + c] + p[t] * mv;
+                        if (near) bd[c] += sigma * (double)v4[row * d + c];
+                    }
+                }
+            }
+        }
+        for (int c = 0; c < d; ++c) { o[c] /= den; bd[c] /= den; }
+        free(p);
+        free(qi);
+    }
+}
+
 /* Number of OpenMP threads a parallel region will use (for reporting). */
 int orc_num_threads(void)
 {
