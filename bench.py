@@ -49,6 +49,8 @@ def parse():
                     help="INT4 group size of the KV4 cache (0 = the config's, 32)")
     ap.add_argument("--populate-reps", type=int, default=5,
                     help="timed bulk appends of the first 32 sequences' histories (0 = skip)")
+    ap.add_argument("--no-int-path", action="store_true",
+                    help="skip the integer decode path (KV4_FLAG_INT_PATH) over the same KV4 bytes")
     ap.add_argument("--rotate", action="store_true",
                     help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -263,6 +265,12 @@ def main():
                            kind=kv4.KV4_KIND_BF16, waves=args.waves,
                            pool_chunks=args.pool_chunks, device="cuda:0")
         caches.append(("bf16", bfc))
+    if not args.no_int_path:
+        ipc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
+                           seed=cfg.seed, waves=args.waves, pool_chunks=args.pool_chunks,
+                           flags=kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if args.rotate else 0),
+                           device="cuda:0")
+        caches.append(("int", ipc))
     if not args.no_kv8:
         k8c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
                            kind=kv4.KV4_KIND_KV8, waves=args.waves,
@@ -472,6 +480,15 @@ def main():
 
     if populate is not None:
         line["populate"] = populate
+    if "int" in results:
+        ri = results["int"]
+        line["int_path"] = {
+            "kernel": "decode_int_kv4_kernel (KV4_FLAG_INT_PATH, same KV4 bytes)",
+            "decode_attn_us": round(ri["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(ri["partials_ms"] * 1e3, 2),
+            "partials_gbs": round(pb / (ri["partials_ms"] * 1e-3) / 1e9, 2),
+            "partials_frac_hbm_peak": round(pb / (ri["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
     if "kv8" in results:
         r8 = results["kv8"]
         p8 = partial_bytes_kv8(n, cfg)

@@ -98,6 +98,24 @@ extern "C" {
  * Mixed kind only (KV4_ERR_UNSUPPORTED with KV4_KIND_BF16); rotated keys must
  * stay within the binary16 range. */
 #define KV4_FLAG_ROTATE_K 0x1
+/* KV4_FLAG_INT_PATH: the decode takes the integer path of KV4-RL Appendix A.3
+ * ("Integer decode path"; "Protected path and reconstruction") instead of the
+ * bf16-query, fp32-probability path.  Per (sequence, q head) the query (in the
+ * keys' basis when KV4_FLAG_ROTATE_K is set) is quantized to INT8 with the side
+ * entries' encoding (scale s_q = fp16(fp32(amax/127)), nearest codes, ties to
+ * even).  INT4 position: score = sm_scale * s_q * sum over groups g of
+ * (Delta_g * I_g + m_g * Q_g), with I_g the integer dot product of the query
+ * codes and the position's 4-bit key codes over the group and Q_g the sum of
+ * the query codes.  Protected position: score = sm_scale * s_q * s_k * (integer
+ * dot product with the INT8 key codes).  Softmax in binary32.  INT4 values: per
+ * block of the 8 positions [8k, 8k + 8) that share a V code word, value group
+ * and q head, w_t = p_t * Delta^v_t is carried as an 8-bit code
+ * u_t = rint(255 w_t / max w) with scale max w / 255, and the block adds
+ * scale * (integer dot product of u with the value codes) + sum_t p_t m^v_t.
+ * Protected values: binary32 products with the dequantized INT8 values (no
+ * probability quantization).  Mixed kind only (KV4_ERR_UNSUPPORTED otherwise);
+ * any q/kv head ratio of 1, 2, 4 or 8; the cache's bytes do not change. */
+#define KV4_FLAG_INT_PATH 0x2
 
 /* Output dtypes of kv4_decode_attn. */
 #define KV4_OUT_F32  0

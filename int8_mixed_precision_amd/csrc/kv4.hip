@@ -42,7 +42,7 @@ int validate_desc(const kv4_cache_desc* d)
     if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
     if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16 && d->kind != KV4_KIND_KV8)
         return KV4_ERR_INVALID_ARG;
-    if (d->flags & ~KV4_FLAG_ROTATE_K) return KV4_ERR_INVALID_ARG;
+    if (d->flags & ~(KV4_FLAG_ROTATE_K | KV4_FLAG_INT_PATH)) return KV4_ERR_INVALID_ARG;
     if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
     int gqa = d->num_q_heads / d->num_kv_heads;
     if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
@@ -50,6 +50,8 @@ int validate_desc(const kv4_cache_desc* d)
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
     // the rotation belongs to the quantized keys: the BF16 comparator has none
     if ((d->flags & KV4_FLAG_ROTATE_K) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
+    // the integer path reads the INT4 pages and the INT8 ring
+    if ((d->flags & KV4_FLAG_INT_PATH) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
     if (d->kind == KV4_KIND_KV8 && d->num_q_heads != 4 * d->num_kv_heads) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
     if ((int64_t)d->max_pages_per_seq * kv4::kPage > INT32_MAX / 2) return KV4_ERR_CAPACITY;
@@ -150,6 +152,16 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     // the pool counters start every launch at zero (a kernel, not a memset, so
     // that the launch sequence can be captured in a graph)
     if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
+    if (a.g.intp) {
+        dim3 grid((unsigned)a.waves);
+        switch (a.g.gqa) {
+            case 1: hipLaunchKernelGGL(kv4::decode_int_kv4_kernel<1>, grid, dim3(64), 0, s, a); break;
+            case 2: hipLaunchKernelGGL(kv4::decode_int_kv4_kernel<2>, grid, dim3(64), 0, s, a); break;
+            case 4: hipLaunchKernelGGL(kv4::decode_int_kv4_kernel<4>, grid, dim3(64), 0, s, a); break;
+            default: hipLaunchKernelGGL(kv4::decode_int_kv4_kernel<8>, grid, dim3(64), 0, s, a); break;
+        }
+        return;
+    }
     if (a.g.gqa == 4) {
         dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {

@@ -36,14 +36,6 @@ struct AppendArgs {
     uint8_t* side;
 };
 
-__device__ __forceinline__ uint16_t plus_zero16(uint16_t h) { return h == 0x8000u ? (uint16_t)0 : h; }
-
-__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
-{
-    _Float16 h = (_Float16)f;     // v_cvt_f16_f32: round to nearest even
-    return __builtin_bit_cast(uint16_t, h);
-}
-
 // DPP move inside a 16-lane row (every lane active, every source in the row).
 template <int CTRL>
 __device__ __forceinline__ float row_mov(float x)
@@ -110,23 +102,8 @@ __device__ __forceinline__ uint32_t int4_code_exact(float x, double D, double M,
     return (uint32_t)c;
 }
 
-__device__ __forceinline__ int int8_code_exact(float x, double S, uint16_t sb)
-{
-    if (sb == 0) return 0;
-    double a = fabs((double)x);
-    int c = (int)fmin(fmax(rint(a / S), 0.0), 127.0);
-    if (c > 0) {
-        double mid = ((double)c - 0.5) * S;
-        if (a < mid || (a == mid && (c & 1))) c -= 1;
-    }
-    if (c < 127) {
-        double mid = ((double)c + 0.5) * S;
-        if (a > mid || (a == mid && ((c + 1) & 1) == 0)) c += 1;
-    }
-    return x < 0.0f ? -c : c;
-}
-
-// Binary32 fast paths of the two code decisions, with the same results.  With
+// Binary32 fast path of the INT4 code decision, with the same results (the
+// INT8 one, int8_code, is in kv4_common.hpp).  With
 // x, m and Delta (or s) exact binary32 values, u = fl(x - m) * rcp(Delta) has a
 // relative error below 2^-22 (one rounding in the difference, 1 ulp in
 // v_rcp_f32, one in the product), i.e. below 4e-6 for |u| < 16 and below 3.1e-5
@@ -143,17 +120,6 @@ __device__ __forceinline__ uint32_t int4_code(float x, float Df, float Mf, uint1
     if (near || !(fabsf(u) < 64.0f) || !(Df < 65536.0f))
         return int4_code_exact(x, (double)Df, (double)Mf, db);
     return (uint32_t)fminf(fmaxf(rintf(u), 0.0f), 15.0f);
-}
-
-__device__ __forceinline__ int int8_code(float x, float Sf, uint16_t sb)
-{
-    if (sb == 0) return 0;
-    const float u = fabsf(x) * __builtin_amdgcn_rcpf(Sf);
-    const float fl = floorf(u);
-    const bool near = fabsf(u - fl - 0.5f) < 0x1p-11f && fl <= 126.0f;
-    if (near || !(u < 256.0f) || !(Sf < 65536.0f)) return int8_code_exact(x, (double)Sf, sb);
-    const int c = (int)fminf(rintf(u), 127.0f);
-    return x < 0.0f ? -c : c;
 }
 
 // Full-wave (64 lanes, 128 channels) INT8 scale.

@@ -19,6 +19,7 @@ struct Geo {
     int num_layers, num_pages, max_slots, max_pages;
     int kind;
     int rot;                 // 1: keys stored, and queries attended, in the rotated basis
+    int intp;                // 1: decode takes the integer path (INT8 q, 8-bit P operand)
     int64_t pb;              // bytes per (page, kv head) block
     int64_t layer_pages;     // bytes of one layer of the page pool
     int64_t rb;              // bytes per (slot, kv head) ring block
@@ -86,6 +87,7 @@ inline Geo make_geo(const kv4_cache_desc& c)
     g.ng = c.head_dim / c.group_size;
     g.kind = c.kind;
     g.rot = (c.flags & KV4_FLAG_ROTATE_K) != 0;
+    g.intp = (c.flags & KV4_FLAG_INT_PATH) != 0;
     g.S = c.kind == KV4_KIND_MIXED ? c.sink : 0;
     g.R = c.kind == KV4_KIND_MIXED ? c.recent : 0;
     g.SR = g.S + g.R;
@@ -161,6 +163,50 @@ __host__ __device__ __forceinline__ int ring_vbyte(int e, int c)
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// ---- binary16 rounding and the INT8 code decision (side entries, KV8 pages
+// and the integer path's query).  s = fp16(fp32(amax / 127)); the code is the
+// integer in [-127, 127] nearest to the exact x / s, ties to even.
+__device__ __forceinline__ uint16_t plus_zero16(uint16_t h) { return h == 0x8000u ? (uint16_t)0 : h; }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
+{
+    _Float16 h = (_Float16)f;     // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Exact decision: a binary64 estimate corrected by the exact binary64
+// midpoints (c +- 1/2) s (exact because s is a binary16 value).
+__device__ __forceinline__ int int8_code_exact(float x, double S, uint16_t sb)
+{
+    if (sb == 0) return 0;
+    double a = fabs((double)x);
+    int c = (int)fmin(fmax(rint(a / S), 0.0), 127.0);
+    if (c > 0) {
+        double mid = ((double)c - 0.5) * S;
+        if (a < mid || (a == mid && (c & 1))) c -= 1;
+    }
+    if (c < 127) {
+        double mid = ((double)c + 0.5) * S;
+        if (a > mid || (a == mid && ((c + 1) & 1) == 0)) c += 1;
+    }
+    return x < 0.0f ? -c : c;
+}
+
+// Binary32 fast path: u = |x| rcp(s) has a relative error below 2^-22, so
+// farther than 2^-11 from a midpoint (|u| < 128) its nearest integer is the
+// exact code; near a midpoint, or for non-finite operands, the exact test decides.
+__device__ __forceinline__ int int8_code(float x, float Sf, uint16_t sb)
+{
+    if (sb == 0) return 0;
+    const float u = fabsf(x) * __builtin_amdgcn_rcpf(Sf);
+    const float fl = floorf(u);
+    const bool near = fabsf(u - fl - 0.5f) < 0x1p-11f && fl <= 126.0f;
+    if (near || !(u < 256.0f) || !(Sf < 65536.0f)) return int8_code_exact(x, (double)Sf, sb);
+    const int c = (int)fminf(rintf(u), 127.0f);
+    return x < 0.0f ? -c : c;
+}
+
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)

@@ -671,6 +671,226 @@ __global__ __launch_bounds__(64) void decode_valu_kv4_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Integer decode path (KV4_FLAG_INT_PATH; KV4-RL Appendix A.3, "Integer
+// decode path" and "Protected path and reconstruction").  The layout of
+// valu_item_kv4: for the scores lanes (e = lane/8, sl = lane%8) hold token e of
+// an 8-token chunk and channels 16 sl .. 16 sl + 15; for the values lane l
+// holds channels 2l and 2l + 1 of every token of the chunk.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
+{
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)(d & 0xFF) << 24);
+}
+
+// INT8 query of GQA heads in this lane's 16-channel slice: codes four per word
+// in channel order (qn, against INT8 key bytes) and as the even and odd
+// channels of each 8-channel half (qe, qo, against the low and high nibbles of
+// the INT4 key bytes); the slice's code sum and the head's scale.
+template <int GQA>
+struct QInt {
+    uint32_t qn[GQA][4], qe[GQA][2], qo[GQA][2];
+    int qsum[GQA];
+    float sq[GQA];
+};
+
+template <int GQA>
+__device__ __forceinline__ void load_q_int(const DecodeArgs& a, int b, int h, QInt<GQA>& Q)
+{
+    float qk[GQA][16], unused[GQA];
+    load_q<GQA>(a, b, h, qk, unused);            // bf16 values, rotated when keys are
+#pragma unroll
+    for (int j = 0; j < GQA; ++j) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qk[j][i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));  // the head's 8 slices
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const uint16_t sb = plus_zero16(f32_to_f16_bits(__fdiv_rn(amax, 127.0f)));
+        const float S = half_bits_to_float(sb);
+        int c[16], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            c[i] = int8_code(qk[j][i], S, sb);
+            sum += c[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Q.qn[j][k] = pack_i8x4(c[4 * k], c[4 * k + 1], c[4 * k + 2], c[4 * k + 3]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            Q.qe[j][k] = pack_i8x4(c[8 * k], c[8 * k + 2], c[8 * k + 4], c[8 * k + 6]);
+            Q.qo[j][k] = pack_i8x4(c[8 * k + 1], c[8 * k + 3], c[8 * k + 5], c[8 * k + 7]);
+        }
+        Q.qsum[j] = sum;
+        Q.sq[j] = S;
+    }
+}
+
+// One wave runs INT4 positions [t_begin, t_end) of (sequence b, kv head h)
+// (prot = false), or the protected part read from the INT8 ring (prot = true),
+// into record `rec`.
+template <int GQA>
+__device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, bool prot,
+                                             int t_begin, int t_end, float* rec)
+{
+    const Geo& g = a.g;
+    const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
+    const int n = seq_len(a, b);
+    const Regions rg = regions_of(n, g.S, g.R);
+    if (prot) {
+        t_begin = 0;
+        t_end = rg.n8;
+    }
+    if (t_end <= t_begin) return;
+
+    const int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
+    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    __shared__ float P[8][GQA];
+    QInt<GQA> Q;
+    load_q_int<GQA>(a, b, h, Q);
+    Online<GQA> st;
+    st.init();
+    float alpha[GQA];
+
+    if (!prot) {
+        const uint8_t* lbase = a.pages + (int64_t)a.layer * g.layer_pages;
+        const int gk = (16 * sl) / g.G;          // K group of this lane's slice
+        const int gv = (2 * lane) / g.G;         // V group of this lane's channels
+        for (int hp = t_begin / kHalf; hp <= (t_end - 1) / kHalf; ++hp) {
+            const int page = clampi(bt[hp / 2], 0, g.num_pages - 1);
+            const uint8_t* pb = lbase + ((int64_t)page * g.Hkv + h) * g.pb;
+            const int half = hp & 1;
+            const int tok = hp * kHalf + e;
+            const bool valid = tok >= t_begin && tok < t_end;
+            const int tp = tok % kPage;
+            // ---- scores: integer dot products of the query codes with the
+            // widened nibbles, then the group's Delta and m
+            const uint8_t* krow = pb + g.off_kc + tp * (g.d / 2);
+            const uint32_t kx = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl));
+            const uint32_t ky = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl + 1));
+            const uint32_t kxl = kx & 0x0F0F0F0Fu, kxh = (kx >> 4) & 0x0F0F0F0Fu;
+            const uint32_t kyl = ky & 0x0F0F0F0Fu, kyh = (ky >> 4) & 0x0F0F0F0Fu;
+            const uint16_t* kdm = reinterpret_cast<const uint16_t*>(pb + g.off_kdm) + tp * 2 * g.ng + 2 * gk;
+            const float D = half_bits_to_float(kdm[0]);
+            const float M = half_bits_to_float(kdm[1]);
+            float s[GQA];
+#pragma unroll
+            for (int j = 0; j < GQA; ++j) {
+                int I = __builtin_amdgcn_sdot4((int)Q.qe[j][0], (int)kxl, 0, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qo[j][0], (int)kxh, I, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qe[j][1], (int)kyl, I, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qo[j][1], (int)kyh, I, false);
+                s[j] = fmaf(D, (float)I, M * (float)Q.qsum[j]) * Q.sq[j];
+            }
+            softmax_chunk<GQA>(st, s, valid, a.scale2, P, alpha);
+            __syncthreads();
+            // ---- values: per head, the 8-bit operand of w = p Delta^v over the
+            // chunk's tokens, an integer dot product with the value codes, and
+            // the offsets' term
+            const uint32_t* vw = reinterpret_cast<const uint32_t*>(pb + g.off_vc) + half * g.d;
+            const uint32_t w0 = vw[vpos(2 * lane)], w1 = vw[vpos(2 * lane + 1)];
+            const uint32_t w0l = w0 & 0x0F0F0F0Fu, w0h = (w0 >> 4) & 0x0F0F0F0Fu;   // tokens 0,2,4,6 / 1,3,5,7
+            const uint32_t w1l = w1 & 0x0F0F0F0Fu, w1h = (w1 >> 4) & 0x0F0F0F0Fu;
+            const uint4 dv = *reinterpret_cast<const uint4*>(pb + g.off_vd + 2 * (gv * kPage + half * kHalf));
+            const uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w};
+            const uint16_t* vmt = reinterpret_cast<const uint16_t*>(pb + g.off_vm) + half * kHalf * g.ng + gv;
+            float Dv[kHalf], Mv[kHalf];
+            bool ok[kHalf];
+#pragma unroll
+            for (int ee = 0; ee < kHalf; ++ee) {
+                const int t2 = hp * kHalf + ee;
+                ok[ee] = t2 >= t_begin && t2 < t_end;
+                Dv[ee] = half_bits_to_float((dvw[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
+                Mv[ee] = half_bits_to_float(vmt[ee * g.ng]);
+            }
+#pragma unroll
+            for (int j = 0; j < GQA; ++j) {
+                // tokens outside the run may hold garbage metadata: select
+                float w[kHalf], wmax = 0.f, off = 0.f;
+#pragma unroll
+                for (int ee = 0; ee < kHalf; ++ee) {
+                    const float p = P[ee][j];
+                    w[ee] = ok[ee] ? p * Dv[ee] : 0.f;
+                    wmax = fmaxf(wmax, w[ee]);
+                    off += ok[ee] ? p * Mv[ee] : 0.f;
+                }
+                int u[kHalf];
+                const float r = wmax > 0.f ? __fdiv_rn(255.0f, wmax) : 0.f;
+#pragma unroll
+                for (int ee = 0; ee < kHalf; ++ee) u[ee] = (int)fminf(rintf(w[ee] * r), 255.0f);
+                const uint32_t ue = pack_i8x4(u[0], u[2], u[4], u[6]);
+                const uint32_t uo = pack_i8x4(u[1], u[3], u[5], u[7]);
+                const float sigma = wmax * (1.0f / 255.0f);
+                const uint32_t i0 = __builtin_amdgcn_udot4(uo, w0h, __builtin_amdgcn_udot4(ue, w0l, 0u, false), false);
+                const uint32_t i1 = __builtin_amdgcn_udot4(uo, w1h, __builtin_amdgcn_udot4(ue, w1l, 0u, false), false);
+                st.o[j][0] = fmaf(st.o[j][0], alpha[j], fmaf(sigma, (float)i0, off));
+                st.o[j][1] = fmaf(st.o[j][1], alpha[j], fmaf(sigma, (float)i1, off));
+            }
+            __syncthreads();
+        }
+    } else {
+        // protected positions: ring entries [0, n8) in ring order; integer QK
+        // against the INT8 keys, binary32 PV with the dequantized INT8 values
+        const uint8_t* ring = a.side + (int64_t)a.layer * g.layer_side + ((int64_t)slot * g.Hkv + h) * g.rb;
+        const uint8_t* vr = ring + (int64_t)g.SR32 * g.d;
+        const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
+        const uint16_t* vsc = ksc + g.SR32;
+        for (int c0 = 0; c0 < t_end; c0 += kHalf) {
+            const int ent = c0 + e;                  // < SR32: the ring is padded to 32 entries
+            const bool valid = ent < t_end;
+            const uint4 kc = *reinterpret_cast<const uint4*>(ring + (int64_t)ent * g.d + 16 * sl);
+            const float sk = half_bits_to_float(ksc[ent]);
+            const uint2 va = *reinterpret_cast<const uint2*>(vr + ring_vbyte(c0, 2 * lane));
+            const uint2 vb = *reinterpret_cast<const uint2*>(vr + ring_vbyte(c0, 2 * lane + 1));
+            const uint4 svw = *reinterpret_cast<const uint4*>(vsc + c0);
+            float s[GQA];
+#pragma unroll
+            for (int j = 0; j < GQA; ++j) {
+                int I = __builtin_amdgcn_sdot4((int)Q.qn[j][0], (int)kc.x, 0, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qn[j][1], (int)kc.y, I, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qn[j][2], (int)kc.z, I, false);
+                I = __builtin_amdgcn_sdot4((int)Q.qn[j][3], (int)kc.w, I, false);
+                s[j] = sk * (float)I * Q.sq[j];
+            }
+            softmax_chunk<GQA>(st, s, valid, a.scale2, P, alpha);
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < GQA; ++j) { st.o[j][0] *= alpha[j]; st.o[j][1] *= alpha[j]; }
+            const uint32_t svs[4] = {svw.x, svw.y, svw.z, svw.w};
+#pragma unroll
+            for (int ee = 0; ee < kHalf; ++ee) {
+                // entries past the end hold garbage: select, do not multiply
+                const bool okk = c0 + ee < t_end;
+                const float sv = half_bits_to_float((svs[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
+                const uint32_t wa = ee < 4 ? va.x : va.y, wb = ee < 4 ? vb.x : vb.y;
+                const float x0 = okk ? sv * (float)(int)(int8_t)((wa >> (8 * (ee & 3))) & 0xFFu) : 0.f;
+                const float x1 = okk ? sv * (float)(int)(int8_t)((wb >> (8 * (ee & 3))) & 0xFFu) : 0.f;
+#pragma unroll
+                for (int j = 0; j < GQA; ++j) {
+                    const float p = P[ee][j];
+                    st.o[j][0] = fmaf(p, x0, st.o[j][0]);
+                    st.o[j][1] = fmaf(p, x1, st.o[j][1]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    write_partial<GQA>(a, st, rec);
+}
+
+template <int GQA>
+__global__ __launch_bounds__(64) void decode_int_kv4_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int b, int h) { int_item_kv4<GQA>(a, b, h, true, 0, 0, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   pace.tile((hi + kTile - 1) / kTile - lo / kTile);
+                   int_item_kv4<GQA>(a, b, h, false, lo, hi, rec);
+               });
+}
+
+// ---------------------------------------------------------------------------
 // BF16 comparator, vector-ALU path: the same split structure over bf16 pages.
 // ---------------------------------------------------------------------------
 template <int GQA>

@@ -30,6 +30,7 @@ KV4_KIND_MIXED = 0
 KV4_KIND_BF16 = 1
 KV4_KIND_KV8 = 2
 KV4_FLAG_ROTATE_K = 0x1
+KV4_FLAG_INT_PATH = 0x2
 KV4_OUT_F32 = 0
 KV4_OUT_BF16 = 1
 

@@ -102,6 +102,11 @@ def test_invalid_descriptors():
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_ERR_UNSUPPORTED),     # GQA 2
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=64), kv4.KV4_ERR_UNSUPPORTED),     # GQA 8
         (dict(kind=kv4.KV4_KIND_KV8, flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),
+        (dict(flags=kv4.KV4_FLAG_INT_PATH | kv4.KV4_FLAG_ROTATE_K), kv4.KV4_OK),
+        (dict(flags=kv4.KV4_FLAG_INT_PATH, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(flags=kv4.KV4_FLAG_INT_PATH, kind=kv4.KV4_KIND_KV8), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(flags=0x4), kv4.KV4_ERR_INVALID_ARG),
     ]
     for change, code in cases:
         d = kv4.make_desc(**{**base, **change})
@@ -109,6 +114,9 @@ def test_invalid_descriptors():
     # the rotation is a property of the quantized (mixed) cache; sizes do not change
     rot = kv4.kv4_cache_required_bytes(kv4.make_desc(**base, flags=kv4.KV4_FLAG_ROTATE_K))
     assert rot == kv4.kv4_cache_required_bytes(kv4.make_desc(**base))
+    # so is the integer decode path: it reads the same pages and ring
+    ip = kv4.kv4_cache_required_bytes(kv4.make_desc(**base, flags=kv4.KV4_FLAG_INT_PATH))
+    assert ip == kv4.kv4_cache_required_bytes(kv4.make_desc(**base))
 
 
 def _fake_handle(**kw):

@@ -412,6 +412,65 @@ def test_kv8_layers_and_long_context():
 
 
 # ---------------------------------------------------------------------------
+# Integer decode path (KV4_FLAG_INT_PATH; KV4-RL Appendix A.3), against the
+# oracle's integer path.  Where the kernel's binary32 probabilities and the
+# oracle's binary64 ones lie on two sides of a rounding tie of the 8-bit
+# operand, either code is a correct reading: the oracle's bound (every code
+# within 2^-6 of a tie moved by one) covers those; all else agrees to 1e-4.
+# And the kernel is much closer to the integer oracle than the integer path is
+# to the exact attention over the same cache (no systematic deviation).
+# ---------------------------------------------------------------------------
+
+INT_ATOL = 1e-4
+
+
+def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0):
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
+                   seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
+    n = np.asarray(ctx, np.int64) + 1
+    ks, vs = W.all_kv_sources(cfg, layer, n)
+    q = W.queries(cfg, layer)
+    flags = kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if rotate else 0)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, flags=flags, seed=seed)
+    _fill_garbage(built)
+    H.build_from_sources(built, layer, ks, vs, ctx)
+    out = H.decode(built, layer, q, n).cpu().numpy().astype(np.float64)
+    assert np.isfinite(out).all()
+    oc = oracle.MixedCache(ks, vs, G, rotate=rotate)
+    qq = oracle.wht(q) if rotate else q
+    want, bound = oracle.attend_int(qq, oc, S, R, 1 / math.sqrt(128))
+    exact = oracle.attend_mixed(qq, oc, S, R, 1 / math.sqrt(128))
+    err = np.abs(out - want)
+    excess = err - (INT_ATOL + bound)
+    assert excess.max() <= 0, (f"|o - o_int| exceeds 1e-4 + bound by {excess.max():.3e} at "
+                               f"{np.unravel_index(excess.argmax(), excess.shape)}")
+    own = float(np.sqrt(np.mean((want - exact) ** 2)))
+    dev = float(np.sqrt(np.mean((out - want) ** 2)))
+    H.log(f"  max |o - o_int| {err.max():.2e}, rms {dev:.2e}; integer path vs exact: "
+          f"rms {own:.2e}, max {np.abs(want - exact).max():.2e}")
+    assert dev <= 0.1 * own + 1e-6
+    return out
+
+
+@pytest.mark.parametrize("Hq,Hkv,G", [(8, 2, 32), (32, 8, 32), (8, 8, 32), (16, 8, 64), (16, 2, 128)])
+def test_integer_path(Hq, Hkv, G):
+    H.log(f"case integer path Hq={Hq} Hkv={Hkv} G={G}")
+    _int_case(Hq, Hkv, G, 4, 64, [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500], seed=110 + Hq + G)
+
+
+def test_integer_path_edges_rotation_layers():
+    for S, R in ((0, 0), (0, 8), (16, 3), (4, 128)):
+        H.log(f"case integer path edges S={S} R={R}")
+        _int_case(8, 2, 32, S, R, list(range(0, 40, 3)) + [S + R, S + R + 1, 600], seed=120 + S + R)
+    H.log("case integer path, rotated keys")
+    _int_case(8, 2, 32, 4, 64, [0, 40, 67, 300, 1000, 2500], seed=131, rotate=True)
+    H.log("case integer path, 3 layers, layer 1, waves 7")
+    _int_case(8, 2, 32, 4, 32, [33, 150, 401, 1200], seed=132, layers=3, layer=1, waves=7)
+    H.log("case integer path, 32q/8kv long")
+    _int_case(32, 8, 32, 4, 128, [9000, 17, 4000], seed=133)
+
+
+# ---------------------------------------------------------------------------
 # Keys stored in the rotated basis (KV4-RL Section 5.1, Appendix A.3): the
 # append rotates k before both quantizers, the decode rotates q; bytes are
 # compared with the oracle's quantization of wht(k), outputs with its fp64
