@@ -3,6 +3,7 @@
 // device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -78,9 +79,39 @@ int num_cus(kv4_cache* c)
 // Waves of the balanced decode partition: explicit, or 16 per compute unit
 // (4 one-wave workgroups per SIMD, the occupancy the decode kernel is built
 // for), so that every wave of the grid is resident at once.
+// The integer path's vector-ALU kernels hold more registers than the
+// matrix-core ones: as many waves per compute unit as the kernel keeps
+// resident (at most 16), so that the partition's waves still run at once.
+// 16 when the runtime cannot tell (no device).
+int int_path_waves_per_cu(int gqa)
+{
+    static std::atomic<int> known[9];
+    const int k = gqa == 1 ? 1 : gqa == 2 ? 2 : gqa == 4 ? 4 : 8;
+    int w = known[k].load(std::memory_order_relaxed);
+    if (w > 0) return w;
+    int nb = 0;
+    hipError_t e;
+    switch (k) {
+        case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<1>, 64, 0); break;
+        case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<2>, 64, 0); break;
+        case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<4>, 64, 0); break;
+        default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<8>, 64, 0); break;
+    }
+    if (e != hipSuccess || nb <= 0) {
+        (void)hipGetLastError();
+        return 16;
+    }
+    w = std::min(nb, 16);
+    known[k].store(w, std::memory_order_relaxed);
+    return w;
+}
+
 int decode_waves(const kv4_cache* c, int cus)
 {
-    return c->desc.num_waves > 0 ? c->desc.num_waves : 16 * cus;
+    if (c->desc.num_waves > 0) return c->desc.num_waves;
+    if (c->desc.flags & KV4_FLAG_INT_PATH)
+        return int_path_waves_per_cu(c->desc.num_q_heads / c->desc.num_kv_heads) * cus;
+    return 16 * cus;
 }
 
 // Most chunks of the dynamic pool (0: none, the default).  Measured at the

@@ -446,6 +446,35 @@ struct Online {
     }
 };
 
+// DPP move inside a 16-lane row (every lane active, every source in the row).
+template <int CTRL>
+__device__ __forceinline__ float lane_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 8 lanes 8k .. 8k+7: the quad swaps, then the half-row mirror
+// (lane i reads lane 7 - i), which after the quad steps adds the other quad's
+// sum -- the same additions in the same order as a butterfly over lane bits
+// 0, 1, 2.
+__device__ __forceinline__ float lanes8_sum(float x)
+{
+    x += lane_mov<0xB1>(x);                      // quad_perm [1,0,3,2]
+    x += lane_mov<0x4E>(x);                      // quad_perm [2,3,0,1]
+    return x + lane_mov<0x141>(x);               // row_half_mirror
+}
+
+// Maximum over the 8 lanes l, l ^ 8, ..., l ^ 56 (row rotation by 8, then the
+// row swaps of v_permlane16_swap and v_permlane32_swap).
+__device__ __forceinline__ float lanes_e_max(float x)
+{
+    x = fmaxf(x, lane_mov<0x128>(x));            // row_ror 8
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Chunk step shared by all paths: lanes (e = lane/8, sl = lane%8) hold the
 // partial score of token e over their 16-channel slice.  Reduces the scores,
 // updates the running max/sum and publishes the probabilities P[e][j] in LDS.
@@ -456,14 +485,9 @@ __device__ __forceinline__ void softmax_chunk(Online<GQA>& st, float (&s)[GQA], 
     const int lane = threadIdx.x, e = lane >> 3, sl = lane & 7;
 #pragma unroll
     for (int j = 0; j < GQA; ++j) {
-        float x = s[j];
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
-        x += __shfl_xor(x, 4);
+        float x = lanes8_sum(s[j]);
         x = valid ? x * scale2 : -INFINITY;
-        float mx = fmaxf(x, __shfl_xor(x, 8));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float mx = lanes_e_max(x);
         float mn = fmaxf(st.m[j], mx);            // finite: the chunk has a valid token
         alpha[j] = exp2f(st.m[j] - mn);
         float p = exp2f(x - mn);
@@ -758,23 +782,45 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
         const uint8_t* lbase = a.pages + (int64_t)a.layer * g.layer_pages;
         const int gk = (16 * sl) / g.G;          // K group of this lane's slice
         const int gv = (2 * lane) / g.G;         // V group of this lane's channels
-        for (int hp = t_begin / kHalf; hp <= (t_end - 1) / kHalf; ++hp) {
+        // one chunk's loads (token e's K codes and (Delta, m) for the scores;
+        // channels 2 lane, 2 lane + 1 of all 8 tokens for the values), issued a
+        // chunk ahead of their use
+        struct Ld {
+            uint32_t kx, ky, kdm, w0, w1;
+            uint4 dv;
+            uint32_t vm[kHalf];
+        };
+        auto load = [&](int hp) {
+            Ld L;
             const int page = clampi(bt[hp / 2], 0, g.num_pages - 1);
             const uint8_t* pb = lbase + ((int64_t)page * g.Hkv + h) * g.pb;
             const int half = hp & 1;
+            const int tp = (hp * kHalf + e) % kPage;
+            const uint8_t* krow = pb + g.off_kc + tp * (g.d / 2);
+            L.kx = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl));
+            L.ky = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl + 1));
+            L.kdm = *reinterpret_cast<const uint32_t*>(pb + g.off_kdm + 4 * (tp * g.ng + gk));
+            const uint32_t* vw = reinterpret_cast<const uint32_t*>(pb + g.off_vc) + half * g.d;
+            L.w0 = vw[vpos(2 * lane)];
+            L.w1 = vw[vpos(2 * lane + 1)];
+            L.dv = *reinterpret_cast<const uint4*>(pb + g.off_vd + 2 * (gv * kPage + half * kHalf));
+            const uint16_t* vmt = reinterpret_cast<const uint16_t*>(pb + g.off_vm) + half * kHalf * g.ng + gv;
+#pragma unroll
+            for (int ee = 0; ee < kHalf; ++ee) L.vm[ee] = vmt[ee * g.ng];
+            return L;
+        };
+        const int hp_last = (t_end - 1) / kHalf;
+        Ld cur = load(t_begin / kHalf);
+        for (int hp = t_begin / kHalf; hp <= hp_last; ++hp) {
+            const Ld nxt = load(min(hp + 1, hp_last));      // the last chunk reloads itself (cache hits)
             const int tok = hp * kHalf + e;
             const bool valid = tok >= t_begin && tok < t_end;
-            const int tp = tok % kPage;
             // ---- scores: integer dot products of the query codes with the
             // widened nibbles, then the group's Delta and m
-            const uint8_t* krow = pb + g.off_kc + tp * (g.d / 2);
-            const uint32_t kx = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl));
-            const uint32_t ky = *reinterpret_cast<const uint32_t*>(krow + 4 * kpos(2 * sl + 1));
-            const uint32_t kxl = kx & 0x0F0F0F0Fu, kxh = (kx >> 4) & 0x0F0F0F0Fu;
-            const uint32_t kyl = ky & 0x0F0F0F0Fu, kyh = (ky >> 4) & 0x0F0F0F0Fu;
-            const uint16_t* kdm = reinterpret_cast<const uint16_t*>(pb + g.off_kdm) + tp * 2 * g.ng + 2 * gk;
-            const float D = half_bits_to_float(kdm[0]);
-            const float M = half_bits_to_float(kdm[1]);
+            const uint32_t kxl = cur.kx & 0x0F0F0F0Fu, kxh = (cur.kx >> 4) & 0x0F0F0F0Fu;
+            const uint32_t kyl = cur.ky & 0x0F0F0F0Fu, kyh = (cur.ky >> 4) & 0x0F0F0F0Fu;
+            const float D = half_bits_to_float(cur.kdm & 0xFFFFu);
+            const float M = half_bits_to_float(cur.kdm >> 16);
             float s[GQA];
 #pragma unroll
             for (int j = 0; j < GQA; ++j) {
@@ -784,18 +830,17 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                 I = __builtin_amdgcn_sdot4((int)Q.qo[j][1], (int)kyh, I, false);
                 s[j] = fmaf(D, (float)I, M * (float)Q.qsum[j]) * Q.sq[j];
             }
+            // one-wave workgroup: LDS operations of the wave run in order, so the
+            // probability exchange needs no memory fence (which would also wait
+            // for the prefetched loads)
             softmax_chunk<GQA>(st, s, valid, a.scale2, P, alpha);
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
             // ---- values: per head, the 8-bit operand of w = p Delta^v over the
             // chunk's tokens, an integer dot product with the value codes, and
             // the offsets' term
-            const uint32_t* vw = reinterpret_cast<const uint32_t*>(pb + g.off_vc) + half * g.d;
-            const uint32_t w0 = vw[vpos(2 * lane)], w1 = vw[vpos(2 * lane + 1)];
-            const uint32_t w0l = w0 & 0x0F0F0F0Fu, w0h = (w0 >> 4) & 0x0F0F0F0Fu;   // tokens 0,2,4,6 / 1,3,5,7
-            const uint32_t w1l = w1 & 0x0F0F0F0Fu, w1h = (w1 >> 4) & 0x0F0F0F0Fu;
-            const uint4 dv = *reinterpret_cast<const uint4*>(pb + g.off_vd + 2 * (gv * kPage + half * kHalf));
-            const uint32_t dvw[4] = {dv.x, dv.y, dv.z, dv.w};
-            const uint16_t* vmt = reinterpret_cast<const uint16_t*>(pb + g.off_vm) + half * kHalf * g.ng + gv;
+            const uint32_t w0l = cur.w0 & 0x0F0F0F0Fu, w0h = (cur.w0 >> 4) & 0x0F0F0F0Fu;   // tokens 0,2,4,6 / 1,3,5,7
+            const uint32_t w1l = cur.w1 & 0x0F0F0F0Fu, w1h = (cur.w1 >> 4) & 0x0F0F0F0Fu;
+            const uint32_t dvw[4] = {cur.dv.x, cur.dv.y, cur.dv.z, cur.dv.w};
             float Dv[kHalf], Mv[kHalf];
             bool ok[kHalf];
 #pragma unroll
@@ -803,7 +848,7 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                 const int t2 = hp * kHalf + ee;
                 ok[ee] = t2 >= t_begin && t2 < t_end;
                 Dv[ee] = half_bits_to_float((dvw[ee >> 1] >> (16 * (ee & 1))) & 0xFFFFu);
-                Mv[ee] = half_bits_to_float(vmt[ee * g.ng]);
+                Mv[ee] = half_bits_to_float(cur.vm[ee]);
             }
 #pragma unroll
             for (int j = 0; j < GQA; ++j) {
@@ -828,7 +873,8 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                 st.o[j][0] = fmaf(st.o[j][0], alpha[j], fmaf(sigma, (float)i0, off));
                 st.o[j][1] = fmaf(st.o[j][1], alpha[j], fmaf(sigma, (float)i1, off));
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
+            cur = nxt;
         }
     } else {
         // protected positions: ring entries [0, n8) in ring order; integer QK
@@ -855,7 +901,7 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                 s[j] = sk * (float)I * Q.sq[j];
             }
             softmax_chunk<GQA>(st, s, valid, a.scale2, P, alpha);
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int j = 0; j < GQA; ++j) { st.o[j][0] *= alpha[j]; st.o[j][1] *= alpha[j]; }
             const uint32_t svs[4] = {svw.x, svw.y, svw.z, svw.w};
@@ -874,7 +920,7 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                     st.o[j][1] = fmaf(p, x1, st.o[j][1]);
                 }
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
         }
     }
     write_partial<GQA>(a, st, rec);
