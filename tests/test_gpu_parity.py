@@ -452,7 +452,8 @@ def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, laye
     return out
 
 
-@pytest.mark.parametrize("Hq,Hkv,G", [(8, 2, 32), (32, 8, 32), (8, 8, 32), (16, 8, 64), (16, 2, 128)])
+@pytest.mark.parametrize("Hq,Hkv,G", [(8, 2, 32), (32, 8, 32), (16, 4, 64), (8, 2, 128), (8, 8, 32),
+                                      (16, 8, 64), (16, 2, 128)])
 def test_integer_path(Hq, Hkv, G):
     H.log(f"case integer path Hq={Hq} Hkv={Hkv} G={G}")
     _int_case(Hq, Hkv, G, 4, 64, [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500], seed=110 + Hq + G)
@@ -462,8 +463,11 @@ def test_integer_path_edges_rotation_layers():
     for S, R in ((0, 0), (0, 8), (16, 3), (4, 128)):
         H.log(f"case integer path edges S={S} R={R}")
         _int_case(8, 2, 32, S, R, list(range(0, 40, 3)) + [S + R, S + R + 1, 600], seed=120 + S + R)
-    H.log("case integer path, rotated keys")
+    H.log("case integer path, rotated keys (vector-ALU kernel)")
     _int_case(8, 2, 32, 4, 64, [0, 40, 67, 300, 1000, 2500], seed=131, rotate=True)
+    H.log("case integer path, rotated keys, GQA 2 and 8")
+    _int_case(8, 4, 32, 4, 64, [0, 67, 1000], seed=134, rotate=True)
+    _int_case(16, 2, 64, 4, 64, [5, 300], seed=135, rotate=True)
     H.log("case integer path, 3 layers, layer 1, waves 7")
     _int_case(8, 2, 32, 4, 32, [33, 150, 401, 1200], seed=132, layers=3, layer=1, waves=7)
     H.log("case integer path, 32q/8kv long")
