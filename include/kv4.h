@@ -140,9 +140,10 @@ typedef struct kv4_cache_desc {
     int32_t flags;              /* KV4_FLAG_* */
     int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
                                    partition; 0 = 16 per compute unit of the
-                                   current device (with KV4_FLAG_INT_PATH: as many
-                                   per compute unit as its kernel keeps resident,
-                                   at most 16), else 1 .. 65536 */
+                                   current device (with KV4_FLAG_INT_PATH and a
+                                   q/kv head ratio other than 4: as many per
+                                   compute unit as its vector-ALU kernel keeps
+                                   resident, at most 16), else 1 .. 65536 */
     int32_t pool_chunks;        /* most chunks of the decode's dynamic pool: 0 = no
                                    pool (the default), else a power of two in
                                    8 .. 65536 */

@@ -109,10 +109,9 @@ int int_path_waves_per_cu(int gqa)
 int decode_waves(const kv4_cache* c, int cus)
 {
     if (c->desc.num_waves > 0) return c->desc.num_waves;
-    // (the matrix-core integer kernel, GQA 4 without rotation, keeps 16 resident)
+    // (the matrix-core integer kernels of GQA 4 keep 16 resident)
     const int gqa = c->desc.num_q_heads / c->desc.num_kv_heads;
-    if ((c->desc.flags & KV4_FLAG_INT_PATH) && !(gqa == 4 && !(c->desc.flags & KV4_FLAG_ROTATE_K)))
-        return int_path_waves_per_cu(gqa) * cus;
+    if ((c->desc.flags & KV4_FLAG_INT_PATH) && gqa != 4) return int_path_waves_per_cu(gqa) * cus;
     return 16 * cus;
 }
 
@@ -187,11 +186,20 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
     if (a.g.intp) {
         dim3 grid((unsigned)a.waves);
-        if (a.g.gqa == 4 && !a.g.rot) {
+        if (a.g.gqa == 4) {
             switch (a.g.G) {
-                case 32: hipLaunchKernelGGL(kv4::decode_int_mfma_kernel<32>, grid, dim3(64), 0, s, a); break;
-                case 64: hipLaunchKernelGGL(kv4::decode_int_mfma_kernel<64>, grid, dim3(64), 0, s, a); break;
-                default: hipLaunchKernelGGL(kv4::decode_int_mfma_kernel<128>, grid, dim3(64), 0, s, a); break;
+                case 32:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<32, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<32, false>), grid, dim3(64), 0, s, a);
+                    break;
+                case 64:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<64, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<64, false>), grid, dim3(64), 0, s, a);
+                    break;
+                default:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<128, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<128, false>), grid, dim3(64), 0, s, a);
+                    break;
             }
             return;
         }

@@ -1197,8 +1197,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
 }
 
 // ---------------------------------------------------------------------------
-// Integer path on the matrix core (KV4_FLAG_INT_PATH, GQA 4, keys stored as
-// they are): the tiles, loads, LDS stage and partition of mfma_item_kv4 with
+// Integer path on the matrix core (KV4_FLAG_INT_PATH, GQA 4): the tiles, loads, LDS stage and partition of mfma_item_kv4 with
 // integer products.  Lane roles (n16 = lane % 16, kb = lane / 16):
 //   QK: v_mfma_i32_16x16x64_i8.  A = the INT8 query codes, block-diagonal:
 //     row n16 = (head n16/4, 32-channel block n16%4); the lane's 16 k-slots
@@ -1258,7 +1257,7 @@ __device__ __forceinline__ QCodes quant_q8(const float (&q)[8], float S, uint16_
     return r;
 }
 
-template <int G>
+template <int G, bool ROT>
 __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                               float* rec, Pace& pace)
 {
@@ -1281,8 +1280,18 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
     {
         const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
         const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
-        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        if constexpr (ROT) {
+            // into the keys' basis in the fixed span order 1, 2, ..., 64: channel
+            // bits 3-4 are lane bits 4-5 (kb), bits 5-6 lane bits 0-1 (gq)
+            wht_local(q);
+            wht_lanes(q, 16);
+            wht_lanes(q, 32);
+            wht_lanes(q, 1);
+            wht_lanes(q, 2);
+            wht_scale(q);
+        }
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
@@ -1549,6 +1558,7 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
 // product that covers those bytes only; B = 16 key bytes of entry n16), then
 // the PV of mfma_prot_kv4: binary32-accurate products with the dequantized
 // INT8 values, no probability quantization.
+template <bool ROT>
 __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h, float* rec)
 {
     const Geo& g = a.g;
@@ -1568,8 +1578,17 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
     {
         const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
         const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
-        const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                            bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+        if constexpr (ROT) {
+            // channel bits 3-4 are lane bits 0-1 (gq), bits 5-6 lane bits 4-5 (kb)
+            wht_local(q);
+            wht_lanes(q, 1);
+            wht_lanes(q, 2);
+            wht_lanes(q, 16);
+            wht_lanes(q, 32);
+            wht_scale(q);
+        }
         float amax = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
@@ -1696,13 +1715,13 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
     if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
-// Integer path, GQA 4, keys stored as they are.
-template <int G>
+// Integer path, GQA 4.
+template <int G, bool ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_int_mfma_kernel(DecodeArgs a)
 {
-    walk_units(a, [&](int b, int h) { mfma_prot_int(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+    walk_units(a, [&](int b, int h) { mfma_prot_int<ROT>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
-                   mfma_item_int<G>(a, b, h, lo, hi, rec, pace);
+                   mfma_item_int<G, ROT>(a, b, h, lo, hi, rec, pace);
                });
 }
 

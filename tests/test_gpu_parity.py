@@ -463,9 +463,10 @@ def test_integer_path_edges_rotation_layers():
     for S, R in ((0, 0), (0, 8), (16, 3), (4, 128)):
         H.log(f"case integer path edges S={S} R={R}")
         _int_case(8, 2, 32, S, R, list(range(0, 40, 3)) + [S + R, S + R + 1, 600], seed=120 + S + R)
-    H.log("case integer path, rotated keys (vector-ALU kernel)")
+    H.log("case integer path, rotated keys, GQA 4 (matrix core)")
     _int_case(8, 2, 32, 4, 64, [0, 40, 67, 300, 1000, 2500], seed=131, rotate=True)
-    H.log("case integer path, rotated keys, GQA 2 and 8")
+    _int_case(16, 4, 128, 16, 8, [3, 200, 1500], seed=136, rotate=True)
+    H.log("case integer path, rotated keys, GQA 2 and 8 (vector ALU)")
     _int_case(8, 4, 32, 4, 64, [0, 67, 1000], seed=134, rotate=True)
     _int_case(16, 2, 64, 4, 64, [5, 300], seed=135, rotate=True)
     H.log("case integer path, 3 layers, layer 1, waves 7")
