@@ -187,6 +187,9 @@ def summarize_trace(args):
         if "bf16_comparator" in b:
             lines.append(f"  BF16 comparator partials (decode_bf16_mfma_kernel): "
                          f"{b['bf16_comparator']['decode_partials_us']} us")
+        if "int_path" in b:
+            lines.append(f"  integer path partials (decode_int_mfma_kernel): "
+                         f"{b['int_path']['decode_partials_us']} us")
         if "kv8_comparator" in b:
             lines.append(f"  KV8 comparator partials (decode_kv8_mfma_kernel): "
                          f"{b['kv8_comparator']['decode_partials_us']} us")
@@ -483,7 +486,7 @@ def main():
     if "int" in results:
         ri = results["int"]
         line["int_path"] = {
-            "kernel": "decode_int_kv4_kernel (KV4_FLAG_INT_PATH, same KV4 bytes)",
+            "kernel": "decode_int_mfma_kernel (KV4_FLAG_INT_PATH at GQA 4, same KV4 bytes)",
             "decode_attn_us": round(ri["decode_ms"] * 1e3, 2),
             "decode_partials_us": round(ri["partials_ms"] * 1e3, 2),
             "partials_gbs": round(pb / (ri["partials_ms"] * 1e-3) / 1e9, 2),
