@@ -142,6 +142,7 @@ def append_bytes_bf16(n, cfg):
 
 
 DOMINANT = "decode_kv4_mfma_kernel"
+TP_NOTE = {"q8b256tp2": " (one GPU's share under two-way tensor parallelism)"}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
@@ -421,7 +422,8 @@ def main():
     achieved = pb / (r["partials_ms"] * 1e-3) / 1e9
     traffic = None
     # the stored counters are those of the default workload (unrotated, group 32)
-    if os.path.exists(args.traffic_json) and not args.rotate and cfg.group == 32:
+    if (os.path.exists(args.traffic_json) and not args.rotate and cfg.group == 32
+            and cfg.name == "q8b256"):
         try:
             tj = json.load(open(args.traffic_json))
             if tj.get("kernel_source_hash") == _kernel_hash():
@@ -442,9 +444,11 @@ def main():
         "dtype": "fp32",
         "data": "synthetic (seeded N(0,1) bf16 q/K/V, 4 outlier K channels x10)",
         "config": {
-            "workload": "Qwen3-8B-shaped attention layer, batch 256 ragged decode step "
-                        "(lognormal contexts median 4k, max 16k), 32q/8kv heads, d=128, "
-                        f"page 16, INT4 group {cfg.group}, S=4, R=128",
+            "workload": (f"Qwen3-8B-shaped attention layer{TP_NOTE.get(cfg.name, '')}, "
+                         f"batch {B} ragged decode step (lognormal contexts median 4k, max 16k), "
+                         f"{cfg.q_heads}q/{cfg.kv_heads}kv heads, d=128, "
+                         f"page 16, INT4 group {cfg.group}, S={cfg.sink}, R={cfg.recent}")
+            if cfg.ctx_kind == "lognormal" else f"workload {cfg.name}",
             "global_batch": B, "seq_len_mean": float(n.mean()), "seq_len_max": int(n.max()),
             "tokens_in_context": int(n.sum()), "parallelism": "single GPU",
             "waves": r["waves"], "pool_chunks": r["pool_chunks"], "rotate_k": bool(args.rotate),

@@ -79,6 +79,10 @@ CONFIGS = {
     # Long context: batch 16, every context 32768, R=256, seed 3.
     "long": Config("long", 1, 16, 32, 8, 128, 16, 32, 4, 256, 3, 4, 10.0, "fixed",
                    tuple([32768] * 16)),
+    # One GPU's share of the Qwen3-8B layer under two-way tensor parallelism:
+    # config q8b256's batch and contexts with 16 q / 4 kv heads, seed 2.
+    "q8b256tp2": Config("q8b256tp2", 1, 256, 16, 4, 128, 16, 32, 4, 128, 2, 4, 10.0, "lognormal",
+                        ctx_median=4096, ctx_lo=256, ctx_hi=16384),
     # 36 layers, batch 128, contexts uniform 1k..12k, R=128, seed 4, 64 steps.
     "full36": Config("full36", 36, 128, 32, 8, 128, 16, 32, 4, 128, 4, 4, 10.0, "uniform",
                      ctx_lo=1024, ctx_hi=12288, steps=64),
