@@ -10,6 +10,8 @@ max_ctx = the longest sequence).
     of sampled sequences (shortest, longest, median and random ones) computed
     one by one by the oracle; for every other row, properties that hold at any
     size (finite output inside the hull of the dequantized values);
+  * the integer decode path on the Qwen3-8B shape, batch 256: sampled
+    sequences against the oracle's integer path;
   * 36 layers x 64 decode steps, batch 128 (contexts uniform 1k..12k): every
     step appends one token per sequence and layer and decodes; the output of
     every sequence against the oracle at layers {0, 17, 35} x steps {0, 31,
@@ -57,6 +59,47 @@ def _run(cfg_name, sample=None, byte_sample=None):
     sub = oracle.MixedCache([ks[i] for i in idx], [vs[i] for i in idx], cfg.group)
     _compare_bytes(built, pages, side, 0, sub, cfg.sink, cfg.recent, seqs=bs)
     return out, built
+
+
+def _run_int(cfg_name, sample):
+    """Integer decode path (KV4_FLAG_INT_PATH) on a full workload, sampled
+    sequences against the oracle's integer path: within 1e-4 plus the tie-flip
+    bound, and an rms far below the path's own error."""
+    from int8_mixed_precision_amd import kv4
+    from tests.test_gpu_parity import INT_ATOL
+    cfg = W.CONFIGS[cfg_name]
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    H.log(f"case {cfg_name} integer path: B={cfg.batch} sum(n)={int(n.sum())}")
+    sample = sorted(set(sample))
+    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
+                         seed=cfg.seed, flags=kv4.KV4_FLAG_INT_PATH)
+    _fill_garbage(built)
+    kept = H.build_streaming(built, cfg, 0, ctx, keep=sample)
+    q = W.queries(cfg, 0)
+    out = H.decode(built, 0, q, n).cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out))
+    oc = oracle.MixedCache([kept[s][0] for s in sample], [kept[s][1] for s in sample], cfg.group)
+    want, bound = oracle.attend_int(q[sample], oc, cfg.sink, cfg.recent, 1 / math.sqrt(cfg.head_dim))
+    exact = oracle.attend_mixed(q[sample], oc, cfg.sink, cfg.recent, 1 / math.sqrt(cfg.head_dim))
+    err = np.abs(out[sample] - want)
+    assert (err - (INT_ATOL + bound)).max() <= 0
+    dev = float(np.sqrt(np.mean((out[sample] - want) ** 2)))
+    own = float(np.sqrt(np.mean((want - exact) ** 2)))
+    H.log(f"{cfg_name} integer path: {len(sample)} sequences, max |o - o_int| {err.max():.2e}, "
+          f"rms {dev:.2e}; path vs exact rms {own:.2e}")
+    assert dev <= 0.1 * own + 1e-6
+    return out
+
+
+def test_qwen3_8b_batch256_integer_path_sampled():
+    cfg = W.CONFIGS["q8b256"]
+    ctx = W.contexts(cfg)
+    order = np.argsort(ctx)
+    rng = np.random.default_rng(124)
+    sample = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
+    sample += [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]
+    _run_int("q8b256", sample)
 
 
 def test_qwen3_4b_shape_full():
