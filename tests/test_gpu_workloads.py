@@ -12,6 +12,7 @@ max_ctx = the longest sequence).
     size (finite output inside the hull of the dequantized values);
   * the integer decode path on the Qwen3-8B shape, batch 256: sampled
     sequences against the oracle's integer path;
+  * the KV8 mode on the same batch: bytes and outputs of sampled sequences;
   * 36 layers x 64 decode steps, batch 128 (contexts uniform 1k..12k): every
     step appends one token per sequence and layer and decodes; the output of
     every sequence against the oracle at layers {0, 17, 35} x steps {0, 31,
@@ -100,6 +101,40 @@ def test_qwen3_8b_batch256_integer_path_sampled():
     sample = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
     sample += [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]
     _run_int("q8b256", sample)
+
+
+def test_qwen3_8b_batch256_kv8_sampled():
+    """KV8 mode on config 3's batch: bytes and outputs of sampled sequences
+    against the oracle's INT8 copies and its attention with every position
+    protected."""
+    from int8_mixed_precision_amd import kv4
+    from tests import layout as L
+    cfg = W.CONFIGS["q8b256"]
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    order = np.argsort(ctx)
+    rng = np.random.default_rng(125)
+    sample = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                        [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]))
+    H.log(f"case q8b256 KV8: B={cfg.batch} sum(n)={int(n.sum())}")
+    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
+                         kind=kv4.KV4_KIND_KV8)
+    _fill_garbage(built)
+    kept = H.build_streaming(built, cfg, 0, ctx, keep=sample)
+    q = W.queries(cfg, 0)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    oc = oracle.MixedCache([kept[s][0] for s in sample], [kept[s][1] for s in sample], cfg.group)
+    want = oracle.attend_mixed(q[sample], oc, 0, int(n.max()), 1 / math.sqrt(cfg.head_dim))
+    err = H.check_output(out[sample], want, ATOL, RTOL)
+    H.log(f"q8b256 KV8: {len(sample)} sequences, max abs {err[0]:.2e} rel {err[1]:.2e}")
+    pages, _ = H.pools_host(built)
+    for i, b in enumerate(sample):
+        got = L.gather_kv8(pages, layer=0, num_pages=built.desc.num_pages, Hkv=cfg.kv_heads,
+                           d=cfg.head_dim, block_tables=built.bt_host, slot=int(built.slots_host[b]),
+                           n=int(n[b]))
+        for name in ("k8", "v8", "k8s", "v8s"):
+            assert np.array_equal(got[name], getattr(oc, name)[oc.seq(i)]), (b, name)
 
 
 def test_qwen3_4b_shape_full():
