@@ -12,7 +12,10 @@ HBM before the timed region.  Every step re-appends the same token at the same
 position (idempotent) and decodes over the same contexts, so each timed step
 does the full work on identical state.
 
-Output: one JSON line (see the design doc for every field's definition).
+Output: one JSON line: the metric and its value (algorithmic bytes of the step
+per second), the step time, the dominant kernel's roofline (achieved vs peak HBM
+bandwidth, measured traffic), the comparators, the populate rate and the oracle's
+CPU baseline.
 """
 from __future__ import annotations
 
@@ -241,7 +244,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the decode step shards by sequence or kv head with no "
-                                   "exchange inside the op; see DESIGN.md)"}))
+                                   "exchange inside the op)"}))
         sys.exit(2)
 
     import torch
