@@ -242,7 +242,7 @@ def main():
     if args.summarize_pmc:
         return summarize_pmc(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 "
                                    "(the decode step shards by sequence or kv head with no "
                                    "exchange inside the op)"}))
         sys.exit(2)

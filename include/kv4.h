@@ -70,7 +70,7 @@ extern "C" {
 /* Return codes. */
 #define KV4_OK                0
 #define KV4_ERR_INVALID_ARG   1  /* null pointer, negative size, bad enum, shape mismatch */
-#define KV4_ERR_UNSUPPORTED   2  /* a valid request this build does not implement */
+#define KV4_ERR_UNSUPPORTED   2  /* a valid request the library does not implement */
 #define KV4_ERR_CAPACITY      3  /* batch > max_slots, layer >= num_layers, pool too small */
 #define KV4_ERR_WORKSPACE     4  /* workspace pointer null or smaller than required */
 #define KV4_ERR_HIP           5  /* a HIP runtime call failed (launch error) */
@@ -128,8 +128,8 @@ typedef struct kv4_cache_desc {
     int32_t num_layers;         /* >= 1 */
     int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
     int32_t num_kv_heads;       /* Hkv; Hq / Hkv in {1, 2, 4, 8} */
-    int32_t head_dim;           /* d; this build supports 128 */
-    int32_t page_size;          /* tokens per page; this build supports 16 */
+    int32_t head_dim;           /* d; the library supports 128 */
+    int32_t page_size;          /* tokens per page; the library supports 16 */
     int32_t group_size;         /* G, INT4 channels per (Delta, m) pair: 32, 64 or 128 */
     int32_t sink;               /* S >= 0: first S positions kept as INT8 */
     int32_t recent;             /* R >= 0: last R positions kept as INT8 */

@@ -463,7 +463,7 @@ const char* kv4_status_string(int status)
     switch (status) {
         case KV4_OK: return "KV4_OK: success";
         case KV4_ERR_INVALID_ARG: return "KV4_ERR_INVALID_ARG: invalid argument";
-        case KV4_ERR_UNSUPPORTED: return "KV4_ERR_UNSUPPORTED: valid request not supported by this build";
+        case KV4_ERR_UNSUPPORTED: return "KV4_ERR_UNSUPPORTED: valid request not supported by the library";
         case KV4_ERR_CAPACITY: return "KV4_ERR_CAPACITY: exceeds a declared capacity";
         case KV4_ERR_WORKSPACE: return "KV4_ERR_WORKSPACE: workspace missing or too small";
         case KV4_ERR_HIP: return "KV4_ERR_HIP: HIP runtime error";

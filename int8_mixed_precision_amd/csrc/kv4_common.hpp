@@ -11,7 +11,7 @@ namespace kv4 {
 
 constexpr int kPage = 16;        // tokens per page
 constexpr int kHalf = 8;         // tokens per V code word
-constexpr int kHeadDim = 128;    // head dimension this build supports
+constexpr int kHeadDim = 128;    // head dimension the library supports
 
 // Byte geometry of one cache, derived once on the host and passed by value.
 struct Geo {
