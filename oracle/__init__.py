@@ -66,6 +66,7 @@ def lib():
         L.orc_attend_mixed.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P,
                                        P, P, P, P, P, P, P, P, P, P, P]
         L.orc_attend_dense.argtypes = [i32, P, P, i32, i32, i32, dbl, P, P, P, P]
+        L.orc_prefill_attn.argtypes = [i32, P, i32, i32, i32, dbl, P, P, P, P]
         L.orc_attend_int.argtypes = [i32, P, P, i32, i32, i32, i32, i32, i32, dbl, P,
                                      P, P, P, P, P, P, P, P, P, P, dbl, P, P]
         L.orc_num_threads.restype = i32
@@ -265,6 +266,22 @@ def attend_int(q, cache: MixedCache, S: int, R: int, sm_scale: float, eps: float
                          _ptr(c.k8), _ptr(c.k8s), _ptr(c.v8), _ptr(c.v8s),
                          float(eps), _ptr(out), _ptr(bound))
     return out, bound
+
+
+def prefill_attn(q, k, v, cu, sm_scale: float) -> np.ndarray:
+    """Causal fp64 attention of every packed position over its sequence's
+    prefix (reading P-1 in kv4_oracle.c): q [T, Hq, d], k, v [T, Hkv, d] (bf16
+    values in float32), cu [B + 1] row offsets.  Returns float64 [T, Hq, d]."""
+    q = np.ascontiguousarray(np.asarray(q, np.float32))
+    k = np.ascontiguousarray(np.asarray(k, np.float32))
+    v = np.ascontiguousarray(np.asarray(v, np.float32))
+    cu = np.ascontiguousarray(np.asarray(cu, np.int32))
+    T, Hq, d = q.shape
+    assert int(cu[-1]) == T and k.shape == v.shape and k.shape[0] == T
+    out = np.empty((T, Hq, d), dtype=np.float64)
+    lib().orc_prefill_attn(len(cu) - 1, _ptr(cu), Hq, k.shape[1], d, float(sm_scale),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(out))
+    return out
 
 
 def attend_mixed_raw(q, seq_lens, pos_off, Hkv, G, S, R, sm_scale,

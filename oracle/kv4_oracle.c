@@ -465,6 +465,55 @@ void orc_attend_int(int B, const int32_t* seq_lens, const int64_t* pos_off,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Prefill attention (KV4-RL Appendix A.3, "Protected path and              */
+/* reconstruction": prefill and carried-prefix reconstruction run BF16      */
+/* attention over the newly computed K/V), in binary64.                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Reading P-1: causal softmax attention of every position i of a sequence over
+ * the positions [0, i] of the same sequence, on the bf16 source values (no
+ * quantization).  Sequences are packed: sequence b owns rows [cu[b], cu[b+1])
+ * of q [T][Hq][d] and of k, v [T][Hkv][d]; q head j reads kv head j/(Hq/Hkv);
+ * out is [T][Hq][d].
+ */
+void orc_prefill_attn(int B, const int32_t* cu, int Hq, int Hkv, int d, double sm_scale,
+                      const float* q, const float* k, const float* v, double* out)
+{
+    int gqa = Hq / Hkv;
+    int64_t T = cu[B];
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t tj = 0; tj < T * Hq; ++tj) {
+        int64_t t = tj / Hq;
+        int j = (int)(tj % Hq), h = j / gqa;
+        int b = 0;
+        while (cu[b + 1] <= t) ++b;
+        int64_t t0 = cu[b];
+        const float* qt = q + (t * Hq + j) * d;
+        double* o = out + (t * Hq + j) * d;
+        int64_t m = t - t0 + 1;                       /* positions [t0, t] */
+        double* s = (double*)malloc(sizeof(double) * (size_t)m);
+        double smax = -INFINITY;
+        for (int64_t p = 0; p < m; ++p) {
+            const float* kp = k + ((t0 + p) * Hkv + h) * d;
+            double dot = 0.0;
+            for (int c = 0; c < d; ++c) dot += (double)qt[c] * (double)kp[c];
+            s[p] = sm_scale * dot;
+            if (s[p] > smax) smax = s[p];
+        }
+        double den = 0.0;
+        for (int64_t p = 0; p < m; ++p) { s[p] = exp(s[p] - smax); den += s[p]; }
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t p = 0; p < m; ++p) {
+            const float* vp = v + ((t0 + p) * Hkv + h) * d;
+            double w = s[p] / den;
+            for (int c = 0; c < d; ++c) o[c] += w * (double)vp[c];
+        }
+        free(s);
+    }
+}
+
 /* Number of OpenMP threads a parallel region will use (for reporting). */
 int orc_num_threads(void)
 {
