@@ -309,6 +309,29 @@ int kv4_decode_merge(kv4_cache* cache, const int32_t* seq_lens, int batch, int m
                      void* out, int out_dtype, const void* workspace, size_t workspace_bytes,
                      kv4_stream_t stream);
 
+/*
+ * Prefill attention (KV4-RL Appendix A.3, "Protected path and reconstruction":
+ * prefill and carried-prefix reconstruction run BF16 attention over the newly
+ * computed K/V, whose cache entries kv4_append then writes): causal softmax
+ * attention of every packed position t of sequence b over the positions
+ * [cu_seqlens[b], t] of the same sequence, on the bf16 values as given (no
+ * quantization), with binary32 accumulation.  Uses the cache only for its
+ * geometry (Hq, Hkv, head_dim); reads and writes no pool.
+ *   q_bf16       [total][Hq][d] bf16 (after RoPE); k_bf16, v_bf16 [total][Hkv][d]
+ *   cu_seqlens   [batch + 1] int32 device array, row offsets: cu[0] = 0,
+ *                nondecreasing, cu[batch] = total
+ *   max_seqlen   host bound on every length (longer sequences are cut to it)
+ *   out          [total][Hq][d], float32 (KV4_OUT_F32) or bf16 (KV4_OUT_BF16)
+ * q head j reads kv head j / (Hq / Hkv).  Offsets are clamped to [0, total].
+ * Errors: KV4_ERR_INVALID_ARG (null pointers, batch < 1, total < 0,
+ * max_seqlen < 1, non-finite sm_scale, bad out_dtype), KV4_ERR_CAPACITY
+ * (max_seqlen above 2^24), KV4_ERR_HIP.  total = 0 launches nothing.
+ */
+int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_bf16,
+                     const void* v_bf16, const int32_t* cu_seqlens, int batch, int total,
+                     int max_seqlen, float sm_scale, void* out, int out_dtype,
+                     kv4_stream_t stream);
+
 /* Free the host handle (the pools stay with the caller). NULL is accepted. */
 int kv4_cache_free(kv4_cache* cache);
 

@@ -13,6 +13,7 @@
 #include "kv4_common.hpp"
 #include "kv4_decode.hpp"
 #include "kv4_decode_mfma.hpp"
+#include "kv4_prefill.hpp"
 
 struct kv4_cache {
     kv4_cache_desc desc;
@@ -449,6 +450,37 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
     st = launch_status();
     if (st != KV4_OK) return st;
     launch_merge(a, s);
+    return launch_status();
+}
+
+int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_bf16,
+                     const void* v_bf16, const int32_t* cu_seqlens, int batch, int total,
+                     int max_seqlen, float sm_scale, void* out, int out_dtype, kv4_stream_t stream)
+{
+    if (cache == nullptr || q_bf16 == nullptr || k_bf16 == nullptr || v_bf16 == nullptr ||
+        cu_seqlens == nullptr || out == nullptr)
+        return KV4_ERR_INVALID_ARG;
+    if (batch < 1 || total < 0 || max_seqlen < 1 || !std::isfinite(sm_scale)) return KV4_ERR_INVALID_ARG;
+    if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
+    if (max_seqlen > (1 << 24)) return KV4_ERR_CAPACITY;
+    if (total == 0) return KV4_OK;
+    const kv4_cache_desc& d = cache->desc;
+    kv4::PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(q_bf16);
+    a.k = static_cast<const uint16_t*>(k_bf16);
+    a.v = static_cast<const uint16_t*>(v_bf16);
+    a.cu = cu_seqlens;
+    a.out = out;
+    a.out_bf16 = out_dtype == KV4_OUT_BF16;
+    a.batch = batch;
+    a.total = total;
+    a.max_len = max_seqlen;
+    a.Hq = d.num_q_heads;
+    a.Hkv = d.num_kv_heads;
+    a.gqa = d.num_q_heads / d.num_kv_heads;
+    a.scale2 = sm_scale * 1.4426950408889634f;
+    dim3 grid((unsigned)((max_seqlen + 15) / 16), (unsigned)a.Hq, (unsigned)batch);
+    hipLaunchKernelGGL(kv4::prefill_attn_kernel, grid, dim3(64), 0, static_cast<hipStream_t>(stream), a);
     return launch_status();
 }
 

@@ -67,9 +67,10 @@ def _load(path: str = LIB_PATH):
     L.kv4_status_string.argtypes = [i32]
     L.kv4_status_string.restype = ctypes.c_char_p
     L.kv4_decode_partition.argtypes = [P, pi32, pi32]
+    L.kv4_prefill_attn.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.c_float, P, i32, P]
     for f in ("kv4_cache_required_bytes", "kv4_cache_create", "kv4_append",
               "kv4_decode_workspace_bytes", "kv4_decode_attn", "kv4_decode_partials",
-              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition"):
+              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition", "kv4_prefill_attn"):
         getattr(L, f).restype = i32
     return L
 
@@ -198,6 +199,23 @@ def kv4_decode_attn(cache, layer: int, q: torch.Tensor, seq_lens: torch.Tensor,
                                 _ptr(block_tables), int(batch), int(max_ctx), float(sm_scale),
                                 _ptr(out), int(out_dtype), _ptr(workspace), workspace.numel(),
                                 _stream(stream)), "kv4_decode_attn")
+
+
+def kv4_prefill_attn(cache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     cu_seqlens: torch.Tensor, batch: int, max_seqlen: int, sm_scale: float,
+                     out: torch.Tensor, out_dtype: int = KV4_OUT_F32, stream=None) -> None:
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _need(out, "out", torch.float32 if out_dtype == KV4_OUT_F32 else torch.bfloat16, dev)
+    if q.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] or out.shape != q.shape:
+        raise ValueError("q, out [total, Hq, d]; k, v [total, Hkv, d]")
+    if cu_seqlens.numel() != batch + 1:
+        raise ValueError("cu_seqlens must have batch + 1 entries")
+    _check(_lib.kv4_prefill_attn(cache, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), int(batch),
+                                 int(q.shape[0]), int(max_seqlen), float(sm_scale), _ptr(out),
+                                 int(out_dtype), _stream(stream)), "kv4_prefill_attn")
 
 
 def kv4_decode_partials(cache, layer: int, q: torch.Tensor, seq_lens: torch.Tensor,

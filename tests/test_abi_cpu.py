@@ -218,6 +218,28 @@ def _ws_bytes(B, Hkv, gqa, W, C):
     return -(-end // 256) * 256 + 8 * 256
 
 
+def test_prefill_validation_no_launch():
+    h, d, _, _ = _fake_handle()
+    L_ = kv4.lib()
+    f = ctypes.c_void_p(1 << 20)
+
+    def call(cache=h, q=f, k=f, v=f, cu=f, batch=1, total=16, max_len=16, scale=0.1, out=f,
+             dt=kv4.KV4_OUT_F32):
+        return L_.kv4_prefill_attn(cache, q, k, v, cu, batch, total, max_len, scale, out, dt, None)
+
+    assert call(cache=None) == kv4.KV4_ERR_INVALID_ARG
+    for name in ("q", "k", "v", "cu", "out"):
+        assert call(**{name: None}) == kv4.KV4_ERR_INVALID_ARG, name
+    assert call(batch=0) == kv4.KV4_ERR_INVALID_ARG
+    assert call(total=-1) == kv4.KV4_ERR_INVALID_ARG
+    assert call(max_len=0) == kv4.KV4_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == kv4.KV4_ERR_INVALID_ARG
+    assert call(dt=5) == kv4.KV4_ERR_INVALID_ARG
+    assert call(max_len=(1 << 24) + 1) == kv4.KV4_ERR_CAPACITY
+    assert call(total=0) == kv4.KV4_OK                         # nothing to launch
+    kv4.kv4_cache_free(h)
+
+
 def test_wave_plan_and_workspace():
     h, d, _, _ = _fake_handle(num_waves=64, max_pages_per_seq=64)
     assert kv4.kv4_decode_partition(h) == (64, 0)    # no pool by default
