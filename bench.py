@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0             # dense bf16 matrix-core peak of MI355X
 
 
 def parse():
@@ -54,6 +55,8 @@ def parse():
                     help="timed bulk appends of the first 32 sequences' histories (0 = skip)")
     ap.add_argument("--no-int-path", action="store_true",
                     help="skip the integer decode path (KV4_FLAG_INT_PATH) over the same KV4 bytes")
+    ap.add_argument("--prefill-reps", type=int, default=3,
+                    help="timed prefill attentions over the populate histories (0 = skip)")
     ap.add_argument("--rotate", action="store_true",
                     help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -138,6 +141,13 @@ def populate_bytes_kv4(hist, cfg):
     wr4 = T * cfg.kv_heads * (cfg.head_dim + 8 * ng)
     wr8 = int(np.sum(np.minimum(hist, cfg.sink + cfg.recent))) * cfg.kv_heads * (2 * cfg.head_dim + 4)
     return rd + wr4 + wr8
+
+
+def prefill_flops(lens, cfg):
+    """Causal attention of every prompt position over its prefix: 2 d flops per
+    (query, key, q head) for the scores and as many for the values."""
+    lens = np.asarray(lens, np.float64)
+    return float(np.sum(cfg.q_heads * 2 * cfg.head_dim * lens * (lens + 1)))
 
 
 def append_bytes_bf16(n, cfg):
@@ -380,7 +390,7 @@ def main():
 
     # bulk populate: the first 32 sequences' histories re-appended whole (after
     # every decode timing: it rewrites ring entries the step token owns)
-    populate = None
+    populate = prefill = None
     if pop is not None:
         c = kv4c
         T = int(pop["hist"].sum())
@@ -405,6 +415,35 @@ def main():
                     "frac_hbm_peak": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "tokens_per_s": round(T / (pms * 1e-3), 1)}
         log(f"populate: {T} tokens in {pms * 1e3:.1f} us ({populate['gbs']} GB/s)")
+        if args.prefill_reps > 0:
+            # the same histories as prompts: causal BF16 attention (synthetic queries)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(cfg.seed)
+            qp = torch.randn((T, cfg.q_heads, cfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+            po = torch.empty((T, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+
+            def pre():
+                kv4.kv4_prefill_attn(c.cache.handle, qp, pop["k"], pop["v"], pop["cu"],
+                                     len(pop["hist"]), int(pop["hist"].max()), sm, po, kv4.KV4_OUT_F32,
+                                     stream)
+
+            pre()
+            torch.cuda.synchronize()
+            fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.prefill_reps)]
+            for e0, e1 in fe:
+                e0.record(stream)
+                pre()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            fms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe]))
+            fl = prefill_flops(pop["hist"], cfg)
+            prefill = {"sequences": len(pop["hist"]), "tokens": T, "us": round(fms * 1e3, 2),
+                       "alg_flops": fl, "tflops": round(fl / (fms * 1e-3) / 1e12, 2),
+                       "frac_mfma_bf16_peak": round(fl / (fms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "tokens_per_s": round(T / (fms * 1e-3), 1)}
+            log(f"prefill: {T} tokens in {fms * 1e3:.1f} us ({prefill['tflops']} TFLOP/s)")
+            del qp, po
         del pop
 
     if args.copy_calibration:
@@ -490,6 +529,8 @@ def main():
 
     if populate is not None:
         line["populate"] = populate
+    if prefill is not None:
+        line["prefill"] = prefill
     if "int" in results:
         ri = results["int"]
         line["int_path"] = {
