@@ -34,14 +34,17 @@ struct PrefillArgs {
 //     keys 8 kb + e).  Lane l holds queries 4 kb + r, channel 16 m + n16 in
 //     O[m][r]: the rows of the scores, so the online-softmax rescale is in-lane.
 constexpr int kPreQ = 64;        // queries per workgroup
-constexpr int kPreK = 32;        // keys per tile
-// LDS row strides, padded so that the 16 lanes of a row read at most two
-// lanes per bank (rows stay 16-byte aligned): K rows of 136 halfs, V^T rows
-// of 40 halfs, probability rows of 36 floats.
-constexpr int kKs = kHeadDim + 8, kVt = kPreK + 8, kPs = kPreK + 4;
+// Keys per tile: 32 (152 VGPRs and 53 KB of LDS at 64 keys leave 3 waves per
+// SIMD instead of 4, and measured 4% slower).
+constexpr int kPrefillKeys = 32;
 
+// KT keys per tile (32 or 64).  LDS row strides are padded so that the 16
+// lanes of a row read at most two lanes per bank (rows stay 16-byte aligned).
+template <int KT>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
 {
+    constexpr int kPreK = KT, NC = KT / 16, NL = KT / 32;      // key blocks, 16-byte loads per thread / 2
+    constexpr int kKs = kHeadDim + 8, kVt = KT + 8, kPs = KT + 4;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, kb = lane >> 4;
     const int b = blockIdx.z, j = blockIdx.y, qb = blockIdx.x;
@@ -77,40 +80,45 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t VT[d][kVt];
     __shared__ __attribute__((aligned(16))) float P[4][16][kPs];
 
-    // cooperative tile loads, two 16-byte chunks of K and two of V per thread:
-    // K chunk (key idx / 16, channels 8 (idx % 16) ..), V keys 2 kp, 2 kp + 1
-    // (kp = tid % 16) at channels 8 (tid / 16) .., so that each V^T store is one
-    // 32-bit word holding a key pair
+    // cooperative tile loads, 2 NL 16-byte chunks of K and of V per thread:
+    // K chunk (key idx / 16, channels 8 (idx % 16) ..); V keys 2 kp, 2 kp + 1 of
+    // each 32-key half (kp = tid % 16) at channels 8 (tid / 16) .., so that each
+    // V^T store is one 32-bit word holding a key pair
     const int kp = tid & 15, vch = 8 * (tid >> 4);
-    auto load = [&](int kt, uint4 (&kr)[2], uint4 (&vr)[2]) {
+    auto load = [&](int kt, uint4 (&kr)[2 * NL], uint4 (&vr)[2 * NL]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 * NL; ++i) {
             const int idx = tid + 256 * i, key = idx >> 4, ch = 8 * (idx & 15);
             const int ki = min(kPreK * kt + key, L - 1);
             kr[i] = *reinterpret_cast<const uint4*>(a.k + ((int64_t)(t0 + ki) * a.Hkv + h) * d + ch);
-            const int vi = min(kPreK * kt + 2 * kp + i, L - 1);
+            const int vi = min(kPreK * kt + 32 * (i >> 1) + 2 * kp + (i & 1), L - 1);
             vr[i] = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + vi) * a.Hkv + h) * d + vch);
         }
     };
-    auto store = [&](const uint4 (&kr)[2], const uint4 (&vr)[2]) {
+    auto store = [&](const uint4 (&kr)[2 * NL], const uint4 (&vr)[2 * NL]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < 2 * NL; ++i) {
             const int idx = tid + 256 * i, key = idx >> 4, ch = 8 * (idx & 15);
             *reinterpret_cast<uint4*>(&Ks[key][ch]) = kr[i];
         }
-        const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};   // key 2 kp
-        const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};   // key 2 kp + 1
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e][2 * kp]) = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-            *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e + 1][2 * kp]) = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+        for (int hh = 0; hh < NL; ++hh) {
+            const uint4 a0 = vr[2 * hh], a1 = vr[2 * hh + 1];
+            const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w};   // key 32 hh + 2 kp
+            const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w};   // key 32 hh + 2 kp + 1
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e][32 * hh + 2 * kp]) = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+                *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e + 1][32 * hh + 2 * kp]) =
+                    (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
+            }
         }
     };
 
     const int q_last_b = min(kPreQ * qb + kPreQ - 1, L - 1);   // last query of the block
     const int q_last_w = min(qw + 15, L - 1);                  // ... and of this wave
     const int kt_end = q_last_b / kPreK + 1;
-    uint4 kr[2], vr[2];
+    uint4 kr[2 * NL], vr[2 * NL];
     load(0, kr, vr);
     store(kr, vr);
     __syncthreads();
@@ -119,9 +127,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
         if (more) load(kt + 1, kr, vr);                       // in flight during the compute
         if (kPreK * kt <= q_last_w) {                         // uniform per wave
             // ---- scores
-            float x[2][4];
+            float x[NC][4];
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
@@ -132,45 +140,74 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int qpos = min(qw + 4 * kb + r, L - 1);
-                    x[c][r] = key <= qpos ? S[r] * a.scale2 : -INFINITY;
+                    // tiles wholly at or below the wave's first query need no mask
+                    x[c][r] = (kPreK * kt + kPreK - 1 <= qw || key <= qpos) ? S[r] * a.scale2 : -INFINITY;
                 }
             }
-            // ---- online softmax per query row (every row has key 0 in the first tile)
-            float alpha[4];
+            // ---- online softmax per query row against a reference maximum m_r that
+            // is raised only when a row exceeds it by more than kSlack (then
+            // p <= 2^kSlack; the result is exact for any reference).  Every row
+            // has key 0 in the first tile, so m_r is finite from then on.
+            float mx[4];
+            bool grow_any = false;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float mx = row16_max(fmaxf(x[0][r], x[1][r]));
-                const float mn = fmaxf(m_r[r], mx);
-                alpha[r] = __builtin_amdgcn_exp2f(m_r[r] - mn);
-                m_r[r] = mn;
-                const float p0 = __builtin_amdgcn_exp2f(x[0][r] - mn);
-                const float p1 = __builtin_amdgcn_exp2f(x[1][r] - mn);
-                l_r[r] = l_r[r] * alpha[r] + (p0 + p1);
-                P[w][4 * kb + r][n16] = p0;
-                P[w][4 * kb + r][16 + n16] = p1;
+                float xm = x[0][r];
+#pragma unroll
+                for (int c = 1; c < NC; ++c) xm = fmaxf(xm, x[c][r]);
+                mx[r] = row16_max(xm);
+                grow_any |= mx[r] > m_r[r] + kSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool grow = mx[r] > m_r[r] + kSlack;
+                    const float mn = grow ? mx[r] : m_r[r];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_r[r] - mn) : 1.0f;
+                    m_r[r] = mn;
+                    l_r[r] *= alpha;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) O[m][r] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float ps = 0.f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const float pc = __builtin_amdgcn_exp2f(x[c][r] - m_r[r]);
+                    ps += pc;
+                    P[w][4 * kb + r][16 * c + n16] = pc;
+                }
+                l_r[r] += ps;
             }
             // the wave's own LDS rows: its LDS accesses run in order
             __builtin_amdgcn_wave_barrier();
-            const float4 pa = *reinterpret_cast<const float4*>(&P[w][n16][8 * kb]);
-            const float4 pb = *reinterpret_cast<const float4*>(&P[w][n16][8 * kb + 4]);
-            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-            u32x4_t ahi, alo;
+            // A operands of the value products: keys 32 hh + 8 kb + e
+            u32x4_t ahi[NL], alo[NL];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t hw, lw;
-                split_bf16(pr[2 * e], pr[2 * e + 1], hw, lw);
-                ahi[e] = hw;
-                alo[e] = lw;
+            for (int hh = 0; hh < NL; ++hh) {
+                const float4 pa = *reinterpret_cast<const float4*>(&P[w][n16][32 * hh + 8 * kb]);
+                const float4 pb = *reinterpret_cast<const float4*>(&P[w][n16][32 * hh + 8 * kb + 4]);
+                const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t hw, lw;
+                    split_bf16(pr[2 * e], pr[2 * e + 1], hw, lw);
+                    ahi[hh][e] = hw;
+                    alo[hh][e] = lw;
+                }
             }
             // ---- PV
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const uint4 bv = *reinterpret_cast<const uint4*>(&VT[16 * m + n16][8 * kb]);
-                const u32x4_t B = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) O[m][r] *= alpha[r];
-                O[m] = mfma_bf16(ahi, B, O[m]);
-                O[m] = mfma_bf16(alo, B, O[m]);
+                for (int hh = 0; hh < NL; ++hh) {
+                    const uint4 bv = *reinterpret_cast<const uint4*>(&VT[16 * m + n16][32 * hh + 8 * kb]);
+                    const u32x4_t B = {bv.x, bv.y, bv.z, bv.w};
+                    O[m] = mfma_bf16(ahi[hh], B, O[m]);
+                    O[m] = mfma_bf16(alo[hh], B, O[m]);
+                }
             }
         }
         __syncthreads();                                      // the tile is consumed
