@@ -480,7 +480,7 @@ int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_b
     a.gqa = d.num_q_heads / d.num_kv_heads;
     a.scale2 = sm_scale * 1.4426950408889634f;
     dim3 grid((unsigned)((max_seqlen + kv4::kPreQ - 1) / kv4::kPreQ), (unsigned)a.Hq, (unsigned)batch);
-    hipLaunchKernelGGL(kv4::prefill_attn_kernel<kv4::kPrefillKeys>, grid, dim3(256), 0,
+    hipLaunchKernelGGL((kv4::prefill_attn_kernel<kv4::kPrefillKeys, kv4::kPrefillRows>), grid, dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
     return launch_status();
 }

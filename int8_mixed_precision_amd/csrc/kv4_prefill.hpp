@@ -33,52 +33,61 @@ struct PrefillArgs {
 //     in bf16 hi + lo through the wave's LDS rows, B = V^T (channel 16 m + n16,
 //     keys 8 kb + e).  Lane l holds queries 4 kb + r, channel 16 m + n16 in
 //     O[m][r]: the rows of the scores, so the online-softmax rescale is in-lane.
-constexpr int kPreQ = 64;        // queries per workgroup
 // Keys per tile: 32 (152 VGPRs and 53 KB of LDS at 64 keys leave 3 waves per
 // SIMD instead of 4, and measured 4% slower).
 constexpr int kPrefillKeys = 32;
+// 16-query row blocks per wave: RB blocks share every K and V operand the wave
+// reads from LDS.
+constexpr int kPrefillRows = 2;                  // 198 VGPRs, 2 waves per SIMD: 28.8 -> 26.4 ms
+constexpr int kPreQ = 4 * 16 * kPrefillRows;   // queries per workgroup
 
-// KT keys per tile (32 or 64).  LDS row strides are padded so that the 16
-// lanes of a row read at most two lanes per bank (rows stay 16-byte aligned).
-template <int KT>
+// KT keys per tile (32 or 64), RB row blocks per wave.  LDS row strides are
+// padded so that the 16 lanes of a row read at most two lanes per bank (rows
+// stay 16-byte aligned).
+template <int KT, int RB>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
 {
     constexpr int kPreK = KT, NC = KT / 16, NL = KT / 32;      // key blocks, 16-byte loads per thread / 2
     constexpr int kKs = kHeadDim + 8, kVt = KT + 8, kPs = KT + 4;
+    constexpr int QB = 4 * 16 * RB;                            // queries per workgroup
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, kb = lane >> 4;
     const int b = blockIdx.z, j = blockIdx.y, qb = blockIdx.x;
     const int t0 = clampi(a.cu[b], 0, a.total);
     const int L = min(clampi(a.cu[b + 1], t0, a.total) - t0, a.max_len);
-    if (kPreQ * qb >= L) return;                          // uniform over the workgroup
+    if (QB * qb >= L) return;                             // uniform over the workgroup
     const int h = j / a.gqa;
     constexpr int d = kHeadDim;
-    const int qw = kPreQ * qb + 16 * w;                   // first query of this wave
+    const int qw = QB * qb + 16 * RB * w;                 // first query of this wave
 
-    // ---- q rows of the wave (rows past the end read the last row: discarded)
-    u32x4_t aq[4];
-    {
-        const int qi = min(qw + n16, L - 1);
+    // ---- q rows of the wave's blocks (rows past the end read the last row: discarded)
+    u32x4_t aq[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int qi = min(qw + 16 * rb + n16, L - 1);
         const uint16_t* qr = a.q + ((int64_t)(t0 + qi) * a.Hq + j) * d;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
             const uint4 u = *reinterpret_cast<const uint4*>(qr + 32 * bb + 8 * kb);
-            aq[bb] = u32x4_t{u.x, u.y, u.z, u.w};
+            aq[rb][bb] = u32x4_t{u.x, u.y, u.z, u.w};
         }
     }
 
-    f32x4_t O[8];
+    f32x4_t O[RB][8];
+    float m_r[RB][4], l_r[RB][4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) O[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_r[4], l_r[4];
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m_r[r] = -INFINITY;
-        l_r[r] = 0.f;
+        for (int m = 0; m < 8; ++m) O[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            m_r[rb][r] = -INFINITY;
+            l_r[rb][r] = 0.f;
+        }
     }
     __shared__ __attribute__((aligned(16))) uint16_t Ks[kPreK][kKs];
     __shared__ __attribute__((aligned(16))) uint16_t VT[d][kVt];
-    __shared__ __attribute__((aligned(16))) float P[4][16][kPs];
+    __shared__ __attribute__((aligned(16))) float P[4][RB][16][kPs];
 
     // cooperative tile loads, 2 NL 16-byte chunks of K and of V per thread:
     // K chunk (key idx / 16, channels 8 (idx % 16) ..); V keys 2 kp, 2 kp + 1 of
@@ -115,8 +124,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
         }
     };
 
-    const int q_last_b = min(kPreQ * qb + kPreQ - 1, L - 1);   // last query of the block
-    const int q_last_w = min(qw + 15, L - 1);                  // ... and of this wave
+    const int q_last_b = min(QB * qb + QB - 1, L - 1);         // last query of the block
+    const int q_last_w = min(qw + 16 * RB - 1, L - 1);         // ... and of this wave
     const int kt_end = q_last_b / kPreK + 1;
     uint4 kr[2 * NL], vr[2 * NL];
     load(0, kr, vr);
@@ -126,89 +135,102 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
         const bool more = kt + 1 < kt_end;
         if (more) load(kt + 1, kr, vr);                       // in flight during the compute
         if (kPreK * kt <= q_last_w) {                         // uniform per wave
-            // ---- scores
-            float x[NC][4];
+            // ---- scores: every K operand read once for the RB row blocks
+            f32x4_t S[RB][NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) S[rb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
                     const uint4 kc = *reinterpret_cast<const uint4*>(&Ks[16 * c + n16][32 * bb + 8 * kb]);
-                    S = mfma_bf16(aq[bb], u32x4_t{kc.x, kc.y, kc.z, kc.w}, S);
+                    const u32x4_t B = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) S[rb][c] = mfma_bf16(aq[rb][bb], B, S[rb][c]);
                 }
-                const int key = kPreK * kt + 16 * c + n16;
+            u32x4_t ahi[RB][NL], alo[RB][NL];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qpos = min(qw + 4 * kb + r, L - 1);
-                    // tiles wholly at or below the wave's first query need no mask
-                    x[c][r] = (kPreK * kt + kPreK - 1 <= qw || key <= qpos) ? S[r] * a.scale2 : -INFINITY;
-                }
-            }
-            // ---- online softmax per query row against a reference maximum m_r that
-            // is raised only when a row exceeds it by more than kSlack (then
-            // p <= 2^kSlack; the result is exact for any reference).  Every row
-            // has key 0 in the first tile, so m_r is finite from then on.
-            float mx[4];
-            bool grow_any = false;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float xm = x[0][r];
-#pragma unroll
-                for (int c = 1; c < NC; ++c) xm = fmaxf(xm, x[c][r]);
-                mx[r] = row16_max(xm);
-                grow_any |= mx[r] > m_r[r] + kSlack;
-            }
-            if (__builtin_amdgcn_ballot_w64(grow_any)) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool grow = mx[r] > m_r[r] + kSlack;
-                    const float mn = grow ? mx[r] : m_r[r];
-                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_r[r] - mn) : 1.0f;
-                    m_r[r] = mn;
-                    l_r[r] *= alpha;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) O[m][r] *= alpha;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float ps = 0.f;
+            for (int rb = 0; rb < RB; ++rb) {
+                const int qf = qw + 16 * rb;                  // first query of the block
+                float x[NC][4];
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const float pc = __builtin_amdgcn_exp2f(x[c][r] - m_r[r]);
-                    ps += pc;
-                    P[w][4 * kb + r][16 * c + n16] = pc;
+                    const int key = kPreK * kt + 16 * c + n16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int qpos = min(qf + 4 * kb + r, L - 1);
+                        // tiles wholly at or below the block's first query need no mask
+                        x[c][r] = (kPreK * kt + kPreK - 1 <= qf || key <= qpos) ? S[rb][c][r] * a.scale2
+                                                                                : -INFINITY;
+                    }
                 }
-                l_r[r] += ps;
-            }
-            // the wave's own LDS rows: its LDS accesses run in order
-            __builtin_amdgcn_wave_barrier();
-            // A operands of the value products: keys 32 hh + 8 kb + e
-            u32x4_t ahi[NL], alo[NL];
+                // online softmax per query row against a reference maximum raised
+                // only when a row exceeds it by more than kSlack (exact for any
+                // reference; every row has key 0 in the first tile)
+                float mx[4];
+                bool grow_any = false;
 #pragma unroll
-            for (int hh = 0; hh < NL; ++hh) {
-                const float4 pa = *reinterpret_cast<const float4*>(&P[w][n16][32 * hh + 8 * kb]);
-                const float4 pb = *reinterpret_cast<const float4*>(&P[w][n16][32 * hh + 8 * kb + 4]);
-                const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                for (int r = 0; r < 4; ++r) {
+                    float xm = x[0][r];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t hw, lw;
-                    split_bf16(pr[2 * e], pr[2 * e + 1], hw, lw);
-                    ahi[hh][e] = hw;
-                    alo[hh][e] = lw;
+                    for (int c = 1; c < NC; ++c) xm = fmaxf(xm, x[c][r]);
+                    mx[r] = row16_max(xm);
+                    grow_any |= mx[r] > m_r[rb][r] + kSlack;
+                }
+                if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool grow = mx[r] > m_r[rb][r] + kSlack;
+                        const float mn = grow ? mx[r] : m_r[rb][r];
+                        const float alpha = grow ? __builtin_amdgcn_exp2f(m_r[rb][r] - mn) : 1.0f;
+                        m_r[rb][r] = mn;
+                        l_r[rb][r] *= alpha;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) O[rb][m][r] *= alpha;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ps = 0.f;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const float pc = __builtin_amdgcn_exp2f(x[c][r] - m_r[rb][r]);
+                        ps += pc;
+                        P[w][rb][4 * kb + r][16 * c + n16] = pc;
+                    }
+                    l_r[rb][r] += ps;
+                }
+                // the wave's own LDS rows: its LDS accesses run in order
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int hh = 0; hh < NL; ++hh) {
+                    const float4 pa = *reinterpret_cast<const float4*>(&P[w][rb][n16][32 * hh + 8 * kb]);
+                    const float4 pb = *reinterpret_cast<const float4*>(&P[w][rb][n16][32 * hh + 8 * kb + 4]);
+                    const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint32_t hw, lw;
+                        split_bf16(pr[2 * e], pr[2 * e + 1], hw, lw);
+                        ahi[rb][hh][e] = hw;
+                        alo[rb][hh][e] = lw;
+                    }
                 }
             }
-            // ---- PV
+            // ---- PV: every V operand read once for the RB row blocks
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int hh = 0; hh < NL; ++hh) {
                     const uint4 bv = *reinterpret_cast<const uint4*>(&VT[16 * m + n16][32 * hh + 8 * kb]);
                     const u32x4_t B = {bv.x, bv.y, bv.z, bv.w};
-                    O[m] = mfma_bf16(ahi[hh], B, O[m]);
-                    O[m] = mfma_bf16(alo[hh], B, O[m]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        O[rb][m] = mfma_bf16(ahi[rb][hh], B, O[rb][m]);
+                        O[rb][m] = mfma_bf16(alo[rb][hh], B, O[rb][m]);
+                    }
                 }
-            }
         }
         __syncthreads();                                      // the tile is consumed
         if (more) {
@@ -217,23 +239,25 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
         }
     }
 
-    // ---- epilogue: queries 4 kb + r of the wave, channels 16 m + n16
+    // ---- epilogue: queries 16 rb + 4 kb + r of the wave, channels 16 m + n16
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int qi = qw + 4 * kb + r;
-        const float l = row16_sum(l_r[r]);
-        if (qi >= L) continue;
-        const float inv = 1.0f / l;
-        const int64_t o = ((int64_t)(t0 + qi) * a.Hq + j) * d;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const float val = O[m][r] * inv;
-            if (a.out_bf16)
-                reinterpret_cast<uint16_t*>(a.out)[o + 16 * m + n16] = (uint16_t)f32_to_bf16_rne(val);
-            else
-                reinterpret_cast<float*>(a.out)[o + 16 * m + n16] = val;
+        for (int r = 0; r < 4; ++r) {
+            const int qi = qw + 16 * rb + 4 * kb + r;
+            const float l = row16_sum(l_r[rb][r]);
+            if (qi >= L) continue;
+            const float inv = 1.0f / l;
+            const int64_t o = ((int64_t)(t0 + qi) * a.Hq + j) * d;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float val = O[rb][m][r] * inv;
+                if (a.out_bf16)
+                    reinterpret_cast<uint16_t*>(a.out)[o + 16 * m + n16] = (uint16_t)f32_to_bf16_rne(val);
+                else
+                    reinterpret_cast<float*>(a.out)[o + 16 * m + n16] = val;
+            }
         }
-    }
 }
 
 }  // namespace kv4
