@@ -364,7 +364,7 @@ def test_bf16_comparator():
 # position is protected (S = 0, R >= n).
 # ---------------------------------------------------------------------------
 
-def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0):
+def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0, pool_chunks=0):
     Hq = 4 * Hkv
     n = np.asarray(ctx, np.int64) + 1
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, seed=seed, batch=len(ctx),
@@ -372,7 +372,7 @@ def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0):
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
     built = H.make_cache(Hq, Hkv, 32, 0, 0, n, layers=layers, kind=kv4.KV4_KIND_KV8, waves=waves,
-                         seed=seed)
+                         seed=seed, pool_chunks=pool_chunks)
     _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
     out = H.decode(built, layer, q, n).cpu().numpy()
@@ -409,6 +409,8 @@ def test_kv8_layers_and_long_context():
     _kv8_case(2, [33, 150, 401, 1200], seed=91, layers=3, layer=2, waves=7)
     H.log("case kv8 long 9000 + short")
     _kv8_case(4, [9000, 1, 47], seed=92)
+    H.log("case kv8, dynamic pool of 16 chunks, 64 waves")
+    _kv8_case(2, [1000, 2500, 40, 3000], seed=93, waves=64, pool_chunks=16)
 
 
 # ---------------------------------------------------------------------------
@@ -424,14 +426,15 @@ def test_kv8_layers_and_long_context():
 INT_ATOL = 1e-4
 
 
-def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0):
+def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0, pool_chunks=0):
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
                    seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
     n = np.asarray(ctx, np.int64) + 1
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
     flags = kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if rotate else 0)
-    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, flags=flags, seed=seed)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, flags=flags, seed=seed,
+                         pool_chunks=pool_chunks)
     _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
     out = H.decode(built, layer, q, n).cpu().numpy().astype(np.float64)
@@ -473,6 +476,8 @@ def test_integer_path_edges_rotation_layers():
     _int_case(8, 2, 32, 4, 32, [33, 150, 401, 1200], seed=132, layers=3, layer=1, waves=7)
     H.log("case integer path, 32q/8kv long")
     _int_case(32, 8, 32, 4, 128, [9000, 17, 4000], seed=133)
+    H.log("case integer path, dynamic pool of 16 chunks, 64 waves")
+    _int_case(8, 2, 32, 4, 64, [1000, 2500, 40, 3000], seed=137, waves=64, pool_chunks=16)
 
 
 # ---------------------------------------------------------------------------
