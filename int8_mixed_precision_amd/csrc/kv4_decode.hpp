@@ -702,6 +702,12 @@ __global__ __launch_bounds__(64) void decode_valu_kv4_kernel(DecodeArgs a)
 // holds channels 2l and 2l + 1 of every token of the chunk.
 // ---------------------------------------------------------------------------
 
+// Blocks whose largest w = p Delta_V is at most 2^-100 carry all-zero 8-bit
+// codes: their weight is below 2^-100 of the block holding the maximum
+// probability (p = 1, or 2^48 with the matrix-core item's scaling), and
+// 255 / w would leave the binary32 range.
+constexpr float kTinyW = 0x1p-100f;
+
 __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
 {
     return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
@@ -862,7 +868,7 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                     off += ok[ee] ? p * Mv[ee] : 0.f;
                 }
                 int u[kHalf];
-                const float r = wmax > 0.f ? __fdiv_rn(255.0f, wmax) : 0.f;
+                const float r = wmax > kTinyW ? __fdiv_rn(255.0f, wmax) : 0.f;
 #pragma unroll
                 for (int ee = 0; ee < kHalf; ++ee) u[ee] = (int)fminf(rintf(w[ee] * r), 255.0f);
                 const uint32_t ue = pack_i8x4(u[0], u[2], u[4], u[6]);

@@ -426,12 +426,15 @@ def test_kv8_layers_and_long_context():
 INT_ATOL = 1e-4
 
 
-def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0, pool_chunks=0):
+def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0, pool_chunks=0,
+              qscale=1.0):
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
                    seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
     n = np.asarray(ctx, np.int64) + 1
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
+    if qscale != 1.0:
+        q = W.to_bf16_values((q * qscale).astype(np.float32))
     flags = kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if rotate else 0)
     built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, flags=flags, seed=seed,
                          pool_chunks=pool_chunks)
@@ -476,6 +479,9 @@ def test_integer_path_edges_rotation_layers():
     _int_case(8, 2, 32, 4, 32, [33, 150, 401, 1200], seed=132, layers=3, layer=1, waves=7)
     H.log("case integer path, 32q/8kv long")
     _int_case(32, 8, 32, 4, 128, [9000, 17, 4000], seed=133)
+    H.log("case integer path, queries x30 (peaked softmax, vanishing blocks), GQA 4 and 2")
+    _int_case(8, 2, 32, 4, 64, [300, 1000, 2500], seed=138, qscale=30.0)
+    _int_case(8, 4, 32, 4, 64, [300, 1000, 2500], seed=139, qscale=30.0)
     H.log("case integer path, dynamic pool of 16 chunks, 64 waves")
     _int_case(8, 2, 32, 4, 64, [1000, 2500, 40, 3000], seed=137, waves=64, pool_chunks=16)
 
