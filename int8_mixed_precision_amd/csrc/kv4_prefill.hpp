@@ -85,8 +85,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             l_r[rb][r] = 0.f;
         }
     }
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kPreK][kKs];
-    __shared__ __attribute__((aligned(16))) uint16_t VT[d][kVt];
+    // two buffers of each tile: the tile after next is stored while this one is read
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kPreK][kKs];
+    __shared__ __attribute__((aligned(16))) uint16_t VT[2][d][kVt];
     __shared__ __attribute__((aligned(16))) float P[4][RB][16][kPs];
 
     // cooperative tile loads, 2 NL 16-byte chunks of K and of V per thread:
@@ -104,11 +105,11 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             vr[i] = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + vi) * a.Hkv + h) * d + vch);
         }
     };
-    auto store = [&](const uint4 (&kr)[2 * NL], const uint4 (&vr)[2 * NL]) {
+    auto store = [&](int buf, const uint4 (&kr)[2 * NL], const uint4 (&vr)[2 * NL]) {
 #pragma unroll
         for (int i = 0; i < 2 * NL; ++i) {
             const int idx = tid + 256 * i, key = idx >> 4, ch = 8 * (idx & 15);
-            *reinterpret_cast<uint4*>(&Ks[key][ch]) = kr[i];
+            *reinterpret_cast<uint4*>(&Ks[buf][key][ch]) = kr[i];
         }
 #pragma unroll
         for (int hh = 0; hh < NL; ++hh) {
@@ -117,8 +118,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w};   // key 32 hh + 2 kp + 1
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e][32 * hh + 2 * kp]) = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-                *reinterpret_cast<uint32_t*>(&VT[vch + 2 * e + 1][32 * hh + 2 * kp]) =
+                *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e][32 * hh + 2 * kp]) = (w0[e] & 0xFFFFu) | (w1[e] << 16);
+                *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e + 1][32 * hh + 2 * kp]) =
                     (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
             }
         }
@@ -127,13 +128,18 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
     const int q_last_b = min(QB * qb + QB - 1, L - 1);         // last query of the block
     const int q_last_w = min(qw + 16 * RB - 1, L - 1);         // ... and of this wave
     const int kt_end = q_last_b / kPreK + 1;
+    // Tile kt is read from buffer kt % 2 while tile kt + 1 (in registers since
+    // the previous step) is stored to the other buffer and tile kt + 2 is
+    // loaded.  One barrier per tile: every wave has passed the barrier that
+    // ended tile kt - 1, i.e. finished reading the buffer that tile kt + 1
+    // overwrites.
     uint4 kr[2 * NL], vr[2 * NL];
     load(0, kr, vr);
-    store(kr, vr);
+    store(0, kr, vr);
+    if (kt_end > 1) load(1, kr, vr);
     __syncthreads();
     for (int kt = 0; kt < kt_end; ++kt) {
-        const bool more = kt + 1 < kt_end;
-        if (more) load(kt + 1, kr, vr);                       // in flight during the compute
+        const int buf = kt & 1;
         if (kPreK * kt <= q_last_w) {                         // uniform per wave
             // ---- scores: every K operand read once for the RB row blocks
             f32x4_t S[RB][NC];
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
-                    const uint4 kc = *reinterpret_cast<const uint4*>(&Ks[16 * c + n16][32 * bb + 8 * kb]);
+                    const uint4 kc = *reinterpret_cast<const uint4*>(&Ks[buf][16 * c + n16][32 * bb + 8 * kb]);
                     const u32x4_t B = {kc.x, kc.y, kc.z, kc.w};
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) S[rb][c] = mfma_bf16(aq[rb][bb], B, S[rb][c]);
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int hh = 0; hh < NL; ++hh) {
-                    const uint4 bv = *reinterpret_cast<const uint4*>(&VT[16 * m + n16][32 * hh + 8 * kb]);
+                    const uint4 bv = *reinterpret_cast<const uint4*>(&VT[buf][16 * m + n16][32 * hh + 8 * kb]);
                     const u32x4_t B = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
@@ -232,11 +238,11 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
                     }
                 }
         }
-        __syncthreads();                                      // the tile is consumed
-        if (more) {
-            store(kr, vr);
-            __syncthreads();
+        if (kt + 1 < kt_end) {
+            store(buf ^ 1, kr, vr);
+            if (kt + 2 < kt_end) load(kt + 2, kr, vr);        // in flight during the next tile
         }
+        __syncthreads();
     }
 
     // ---- epilogue: queries 16 rb + 4 kb + r of the wave, channels 16 m + n16
