@@ -216,9 +216,26 @@ __device__ __forceinline__ Page page_rsrc(const uint8_t* p, int bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, bytes, 0x00020000);
 }
 
+// The INT4 tiles' bytes are read once per step, so their loads carry the
+// nontemporal policy (the nt bit, cache-policy immediate 2 on gfx950): random
+// 2.5 KB page blocks then stream at about 6.6-6.8 TB/s on MI355X, against
+// about 5.7 TB/s with the default policy.  Each of those loads covers whole
+// 128-byte lines.  The INT8 parts (protected ring, KV8 pages) keep the default
+// policy: a lane there reads 32 contiguous bytes in two 16-byte loads, each of
+// which covers half of every line it touches, and with the nontemporal policy
+// that pattern measured much slower (KV8 decode 522 -> 682 us).
+constexpr int kStreamPolicy = 2;
+
 __device__ __forceinline__ uint4 ld16(Page r, uint32_t off)
 {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// A 16-byte global load of cache bytes with the nontemporal policy.
+__device__ __forceinline__ uint4 ldg_stream(const void* p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -238,13 +255,13 @@ __device__ __forceinline__ void load_k_codes(Kv4Tile& t, Page P0, Page P1, const
 // of page lane / 32.
 __device__ __forceinline__ void load_v_codes(Kv4Tile& t, const uint8_t* PM, const Kv4Offs& o)
 {
-    t.vc0 = *reinterpret_cast<const uint4*>(PM + o.vc);
-    t.vc1 = *reinterpret_cast<const uint4*>(PM + o.vc + 4 * 64);
+    t.vc0 = ldg_stream(PM + o.vc);
+    t.vc1 = ldg_stream(PM + o.vc + 4 * 64);
 }
 
 __device__ __forceinline__ void load_meta(Kv4Tile& t, const uint8_t* PH, const Kv4Offs& o)
 {
-    t.meta = *reinterpret_cast<const uint4*>(PH + o.meta);
+    t.meta = ldg_stream(PH + o.meta);
 }
 
 // ---------------------------------------------------------------------------
@@ -1164,7 +1181,8 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
             vmask[i] = (valid[2 * i] ? 0x0000FFFFu : 0u) | (valid[2 * i + 1] ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            uint4 v = *reinterpret_cast<const uint4*>(PM + v_off + 2 * 16 * s * kHalf);
+            // 16 lanes read 256 contiguous bytes: whole lines, streamed
+            uint4 v = ldg_stream(PM + v_off + 2 * 16 * s * kHalf);
             u32x4_t bv = {v.x, v.y, v.z, v.w};
             if (!full) bv &= vmask;
             O[s] = mfma_bf16(ap, bv, O[s]);
