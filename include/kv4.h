@@ -112,6 +112,16 @@ extern "C" {
  * and q head, w_t = p_t * Delta^v_t is carried as an 8-bit code
  * u_t = rint(255 w_t / max w) with scale max w / 255, and the block adds
  * scale * (integer dot product of u with the value codes) + sum_t p_t m^v_t.
+ * Exception: a block whose largest w is at most 2^-100 gets u = 0 for all its
+ * positions (its term sum_t p_t m^v_t stays).  w is measured in each kernel's
+ * own units: with p_t = 2^(score_t - m_ref) against the running maximum m_ref
+ * of the scores in the vector-ALU form (q/kv ratios 1, 2, 8), and with
+ * p_t = 2^(score_t - m_ref + 48) against a reference that trails the running
+ * maximum by at most 16 in the matrix-core form (ratio 4), scores in base 2.
+ * Either way the dropped terms sum to at most 8 * 15 * max w <= 120 * 2^-100
+ * against a normaliser of at least 1 (vector ALU) or 2^32 (matrix core), so
+ * every output differs from the rint rule by less than 2^-90; 255 / max w
+ * would overflow binary32 there.
  * Protected values: binary32 products with the dequantized INT8 values (no
  * probability quantization).  Mixed kind only (KV4_ERR_UNSUPPORTED otherwise);
  * any q/kv head ratio of 1, 2, 4 or 8; the cache's bytes do not change. */
@@ -201,8 +211,12 @@ int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_po
  * copied into the pages.  KV8 kind: every new position gets its INT8 K and V
  * codes and scales (s = fp16(fp32(amax / 127)), codes the nearest integers to
  * x / s, ties to even, in [-127, 127]) written into its page.
- * Errors: KV4_ERR_INVALID_ARG (null pointers, batch < 1, total_new < 0),
- * KV4_ERR_CAPACITY (layer out of range, batch > max_slots), KV4_ERR_HIP.
+ * batch == 0 or total_new == 0 is a no-op that returns KV4_OK once the cache,
+ * the sizes and the layer are valid, before the pointers are checked (they may
+ * then be NULL).
+ * Errors: KV4_ERR_INVALID_ARG (cache NULL, batch < 0, total_new < 0, or a NULL
+ * pointer when there is work), KV4_ERR_CAPACITY (layer out of range, batch >
+ * max_slots), KV4_ERR_HIP.
  */
 int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf16,
                const int32_t* cu_new, const int32_t* ctx_before, const int32_t* slot_ids,

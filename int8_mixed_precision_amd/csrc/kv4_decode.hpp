@@ -383,6 +383,10 @@ __device__ __forceinline__ void walk_tiles(const DecodeArgs& a, const Plan& pl, 
     while (s < pl.shares()) {
         uint32_t x = pl.sbeg(s);
         const uint32_t xe = pl.sbeg(s + 1);
+        if (x >= xe) {                          // an empty share (no INT4 tiles at all):
+            s = take_chunk(a, pl, j);           // nothing to locate, and no sequence index
+            continue;                           // past the batch is ever formed
+        }
         pace.share_len = s < pl.S0 ? (int)(xe - x) : 0;
         uint32_t C;
         int b = locate_seq(a, x, [](const Units& u) { return u.ntile; }, C);

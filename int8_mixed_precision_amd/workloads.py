@@ -201,3 +201,72 @@ def queries_device(cfg: Config, layer: int, step: int, device):
 def scaled(cfg: Config, **changes) -> Config:
     """A copy of a config with some fields replaced (for reduced test sizes)."""
     return dataclasses.replace(cfg, **changes)
+
+
+# Group kinds of extreme_kv_sources, in the order they cycle.
+EXTREME_KINDS = ("normal", "tiny", "f32_subnormal", "constant", "near_max", "int4_ties",
+                 "scaled", "two_values")
+
+
+def extreme_kv_sources(seed: int, n: int, kv_heads: int, head_dim: int, group: int,
+                       int8_tie_rows: Sequence[int] = ()) -> Tuple[np.ndarray, np.ndarray]:
+    """Keys and values [n, kv_heads, head_dim] (bf16 values in float32) whose
+    channel groups of ``group`` channels cycle through the EXTREME_KINDS value
+    patterns, all inside |x| <= 65280 (the largest bf16 value below the binary16
+    limit 65504):
+      normal        N(0, 1);
+      tiny          N(0, 1) * 1e-6 (offset and step fall in the binary16
+                    subnormal range);
+      f32_subnormal half the group 1e-39 (below binary32's normal range), the
+                    rest N(0, 1);
+      constant      one repeated value (0, -0, 3.140625, -1e-30, 65280 or -2^-20);
+      near_max      values spread over [-65280, 65280], including both ends;
+      int4_ties     the integers 0..15 followed by half-integers (a step of 1
+                    and offset 0 put those exactly between two codes);
+      scaled        N(0, 1) times 10^k, k in [-6, 3];
+      two_values    a random mix of -1.5 and 2.25.
+    Rows listed in ``int8_tie_rows`` hold, in every kv head, 127 followed by
+    half-integers (exact ties of a symmetric 8-bit code with scale 1).
+    Seeded by ``seed`` only."""
+    r = _rng(seed, TAG_K, 777)
+    shape = (n, kv_heads, head_dim)
+    ng = head_dim // group
+    consts = np.array([0.0, -0.0, 3.140625, -1e-30, 65280.0, -2.0 ** -20], np.float32)
+    halves = np.array([2.5, 3.5, 4.5, 0.5, 14.5, 7.5, 8.5, 1.5, 0.25, 0.75, 13.5, 9.0, 10.0,
+                       11.0, 12.0, 5.5], np.float32)
+    out = []
+    for tensor in range(2):
+        x = np.empty(shape, np.float32)
+        for t in range(n):
+            for h in range(kv_heads):
+                for g in range(ng):
+                    kind = EXTREME_KINDS[(t * kv_heads * ng + h * ng + g + 3 * tensor) % len(EXTREME_KINDS)]
+                    if kind == "normal":
+                        v = r.standard_normal(group)
+                    elif kind == "tiny":
+                        v = r.standard_normal(group) * 1e-6
+                    elif kind == "f32_subnormal":
+                        v = r.standard_normal(group)
+                        v[r.permutation(group)[: group // 2]] = 1e-39
+                    elif kind == "constant":
+                        v = np.full(group, consts[r.integers(consts.size)])
+                    elif kind == "near_max":
+                        v = r.uniform(-65280.0, 65280.0, group)
+                        v[0], v[-1] = 65280.0, -65280.0
+                    elif kind == "int4_ties":
+                        base = np.concatenate([np.arange(16, dtype=np.float32), halves])
+                        v = np.resize(base, group)
+                    elif kind == "scaled":
+                        v = r.standard_normal(group) * 10.0 ** int(r.integers(-6, 4))
+                    else:
+                        v = r.choice(np.array([-1.5, 2.25]), size=group)
+                    x[t, h, g * group:(g + 1) * group] = v
+        for t in int8_tie_rows:
+            row = np.zeros(head_dim, np.float32)
+            row[0] = 127.0
+            ties = np.array([0.5, 1.5, 2.5, -2.5, -3.5, 100.5, 101.5, -126.5], np.float32)
+            row[1:1 + ties.size] = ties
+            row[1 + ties.size:] = r.integers(-120, 121, head_dim - 1 - ties.size)
+            x[t, :, :] = row
+        out.append(to_bf16_values(np.clip(x, -65280.0, 65280.0)))
+    return out[0], out[1]

@@ -73,3 +73,40 @@ def header(n, S, R, Hkv, waves, pool_chunks, mixed=True):
                 out[(b, h)] = (share_of(x), share_of(x + tiles[b] - 1))
             x += tiles[b]
     return out, tiles, prot, pl
+
+
+def walk_share(tiles, Hkv, x, xe, touch):
+    """The tile walk of one share [x, xe) as the decode kernels run it: locate
+    the sequence holding tile x, then cut the share into maximal runs of one
+    (b, h).  Calls touch(b) for every sequence index read and returns the runs
+    (b, h, first tile, end tile).  An empty share reads nothing."""
+    runs = []
+    if x >= xe:
+        return runs
+    B = len(tiles)
+    C, b = 0, 0
+    while True:                                   # locate: first b whose count passes x
+        touch(b)
+        if C + Hkv * tiles[b] > x:
+            break
+        C += Hkv * tiles[b]
+        b += 1
+    while x < xe:
+        touch(b)
+        nt = tiles[b]
+        r = x - C
+        h, t0 = r // nt, r % nt
+        base = C + h * nt
+        t1 = min(nt, xe - base)
+        runs.append((b, h, t0, t1))
+        x = base + t1
+        if x < xe and x >= C + Hkv * nt:          # next sequence with tiles
+            C += Hkv * nt
+            while True:
+                b += 1
+                if b >= B:
+                    return runs
+                touch(b)
+                if tiles[b]:
+                    break
+    return runs

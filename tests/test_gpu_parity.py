@@ -327,10 +327,82 @@ def test_extreme_scales(vscale):
     H.build_from_sources(built, 0, ks, vs, ctx)
     out = H.decode(built, 0, q, n).cpu().numpy()
     oc = oracle.MixedCache(ks, vs, G)
+    pages, side = H.pools_host(built)
+    _compare_bytes(built, pages, side, 0, oc, S, R)
     want = oracle.attend_mixed(q, oc, S, R, 1 / math.sqrt(128))
     assert np.isfinite(out).all()
     err = H.check_output(out, want, ATOL * max(vscale, 1.0), RTOL)
     H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_append_extreme_values(G):
+    """Quantizer edge cases through the HIP append, bytes against the oracle
+    bit for bit (KV4-RL eq. 3.3 and Appendix A.3; readings Q-1 .. Q-4): groups
+    of magnitude 1e-6 (offset and step binary16 subnormals), bf16 values below
+    binary32's normal range mixed with N(0, 1), constant groups (step 0),
+    values out to +-65280, INT4 groups whose values sit exactly between two
+    codes, whole kv-head vectors whose INT8 codes are exact ties, and groups
+    scaled by 10^-6 .. 10^3.  These are the cases where the append's binary32
+    code decision hands over to its exact binary64 test.  Most positions are
+    protected (S = 4, R = 24), so both encodings are compared.
+
+    The attention over this cache is then checked against the oracle with a
+    bar derived from binary32 score arithmetic: keys near 65280 give scores of
+    1e4 .. 1e5 nats, where one binary32 ulp is already 2^-24 of that, so the
+    workloads' fixed 2e-3 cannot hold.  With every partial sum of a score
+    bounded by A = sm_scale * max_t sum_c |q_c k^_{t,c}| and at most 16
+    roundings of 2^-24 each, every score is within delta = 2^-20 A, every
+    normalised weight within a factor e^(2 delta), and every output within
+    (e^(2 delta) - 1) * 2 max|v^| of the oracle's, plus the value path's
+    1e-3 * max|v^|.  The queries are scaled by 2^-12 so that this bar stays
+    near 3e-3 * max|v^| (it is checked per row)."""
+    Hq, Hkv, S, R = 8, 2, 4, 24
+    ctx = [0, 5, 27, 28, 29, 90, 200]
+    n = np.asarray(ctx, np.int64) + 1
+    H.log(f"case append extreme values G={G} ctx {ctx}")
+    ks, vs = [], []
+    for b, nb in enumerate(n):
+        k, v = W.extreme_kv_sources(1000 + 10 * G + b, int(nb), Hkv, 128, G,
+                                    int8_tie_rows=(0, int(nb) - 1))
+        ks.append(k)
+        vs.append(v)
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
+                   seed=1000 + G, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx))
+    q = W.to_bf16_values(W.queries(cfg, 0) * np.float32(2.0 ** -12))
+    built = H.make_cache(Hq, Hkv, G, S, R, n, seed=1000 + G)
+    _fill_garbage(built)
+    H.build_from_sources(built, 0, ks, vs, ctx)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    oc = oracle.MixedCache(ks, vs, G)
+    pages, side = H.pools_host(built)
+    _compare_bytes(built, pages, side, 0, oc, S, R)
+    # the cases are really present in the oracle's bytes
+    d16 = oracle.f16_bits_to_f64(oc.k4d)
+    assert np.any((d16 > 0) & (d16 < 2.0 ** -14))          # subnormal steps
+    assert np.any(oc.k4d == 0)                              # constant groups
+    assert np.any(oc.k8s == 0x3C00)                         # INT8 scale 1 (the tie rows)
+    assert np.isfinite(out).all()
+    sm = 1 / math.sqrt(128)
+    want = oracle.attend_mixed(q, oc, S, R, sm)
+    worst = 0.0
+    for b in range(len(ctx)):
+        nb = int(n[b])
+        sl = oc.seq(b)
+        prot = np.array([oracle.is_protected(p, nb, S, R) for p in range(nb)])
+        khat = np.where(prot[:, None, None], oracle.dequant_int8(oc.k8[sl][:nb], oc.k8s[sl][:nb]),
+                        oracle.dequant_int4(oc.k4[sl][:nb], oc.k4d[sl][:nb], oc.k4m[sl][:nb], G))
+        vhat = np.where(prot[:, None, None], oracle.dequant_int8(oc.v8[sl][:nb], oc.v8s[sl][:nb]),
+                        oracle.dequant_int4(oc.v4[sl][:nb], oc.v4d[sl][:nb], oc.v4m[sl][:nb], G))
+        for j in range(Hq):
+            h = j // (Hq // Hkv)
+            A = sm * float((np.abs(khat[:, h, :]) @ np.abs(q[b, j].astype(np.float64))).max())
+            vmax = float(np.abs(vhat[:, h, :]).max())
+            tol = ATOL * max(vmax, 1.0) + math.expm1(2 * 2.0 ** -20 * A) * 2 * vmax
+            e = float(np.abs(out[b, j] - want[b, j]).max())
+            assert e <= tol, (b, j, e, tol, A)
+            worst = max(worst, e / max(vmax, 1.0))
+    H.log(f"  bytes bit-exact; outputs within the derived bar, worst error {worst:.2e} of max|v^|")
 
 
 def test_bf16_comparator():

@@ -55,3 +55,44 @@ def test_prefill_long_prompt_and_bf16_output():
     outb, _ = _case(32, 8, [2048, 5], seed=210, out_dtype=kv4.KV4_OUT_BF16)
     ref = torch.from_numpy(out32).to(torch.bfloat16).float().numpy()
     assert np.array_equal(outb, ref)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_16k_prompt_sampled_rows():
+    """Prompts as long as the benchmark's (16,384 tokens, packed with a 3,000-
+    and a 7-token one): sampled rows -- the first and last of each prompt, tile
+    and block boundaries, random ones -- against the oracle's fp64 dense
+    attention of that row's query over its prefix [0, t] (row t of a causal
+    prefill is exactly that)."""
+    Hq, Hkv = 32, 8
+    lens = [16384, 3000, 7]
+    H.log(f"case prefill 16k prompt: lens {lens}, sampled rows")
+    rng = np.random.default_rng(220)
+    T = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = W.to_bf16_values(rng.standard_normal((T, Hq, 128)).astype(np.float32) * 2)
+    k = W.to_bf16_values(rng.standard_normal((T, Hkv, 128)).astype(np.float32))
+    v = W.to_bf16_values(rng.standard_normal((T, Hkv, 128)).astype(np.float32))
+    built = H.make_cache(Hq, Hkv, 32, 4, 16, [16], seed=220)
+    dev = torch.device("cuda")
+    out = torch.empty((T, Hq, 128), dtype=torch.float32, device=dev)
+    kv4.kv4_prefill_attn(built.cache.handle, H.to_dev_bf16(q), H.to_dev_bf16(k), H.to_dev_bf16(v),
+                         torch.from_numpy(cu).to(dev), len(lens), int(max(lens)), 1 / math.sqrt(128),
+                         out, kv4.KV4_OUT_F32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    rows = []
+    for b, n in enumerate(lens):
+        fixed = [0, 1, 15, 16, 31, 32, 127, 128, 129, 4095, 4096, 8191, 12000, n - 2, n - 1]
+        picks = set(t for t in fixed if 0 <= t < n)
+        picks |= set(int(t) for t in rng.integers(0, n, size=12 if n > 100 else n))
+        rows += [(b, t) for t in sorted(picks)]
+    for i in range(0, len(rows), 16):
+        chunk = rows[i:i + 16]
+        idx = [int(cu[b]) + t for b, t in chunk]
+        ks = [k[cu[b]:cu[b] + t + 1] for b, t in chunk]
+        vs = [v[cu[b]:cu[b] + t + 1] for b, t in chunk]
+        want = oracle.attend_dense(q[idx], ks, vs, 1 / math.sqrt(128))
+        err = H.check_output(got[idx], want, ATOL, RTOL)
+    H.log(f"  {len(rows)} sampled rows within the bar (last chunk max abs {err[0]:.2e})")

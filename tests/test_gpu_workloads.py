@@ -6,13 +6,13 @@ max_ctx = the longest sequence).
     output, against the oracle;
   * long context, batch 16 x 32,768: every sequence's output, bytes of a
     sample of sequences;
-  * Qwen3-8B shape, batch 256 (lognormal median 4k, max 16k): bytes and output
-    of sampled sequences (shortest, longest, median and random ones) computed
-    one by one by the oracle; for every other row, properties that hold at any
-    size (finite output inside the hull of the dequantized values);
-  * the integer decode path on the Qwen3-8B shape, batch 256: sampled
-    sequences against the oracle's integer path;
-  * the KV8 mode on the same batch: bytes and outputs of sampled sequences;
+  * Qwen3-8B shape, batch 256 (lognormal median 4k, max 16k): the output of
+    every (sequence, q head) row against the oracle, computed 32 sequences at a
+    time; bytes of sampled sequences (shortest, longest, median, random ones);
+  * the integer decode path on the same batch: every row against the oracle's
+    integer path;
+  * the KV8 mode on the same batch: every row's output, bytes of sampled
+    sequences;
   * 36 layers x 64 decode steps, batch 128 (contexts uniform 1k..12k): every
     step appends one token per sequence and layer and decodes; the output of
     every sequence against the oracle at layers {0, 17, 35} x steps {0, 31,
@@ -62,79 +62,129 @@ def _run(cfg_name, sample=None, byte_sample=None):
     return out, built
 
 
-def _run_int(cfg_name, sample):
-    """Integer decode path (KV4_FLAG_INT_PATH) on a full workload, sampled
-    sequences against the oracle's integer path: within 1e-4 plus the tie-flip
-    bound, and an rms far below the path's own error."""
-    from int8_mixed_precision_amd import kv4
-    from tests.test_gpu_parity import INT_ATOL
-    cfg = W.CONFIGS[cfg_name]
-    ctx = W.contexts(cfg)
-    n = ctx + 1
-    H.log(f"case {cfg_name} integer path: B={cfg.batch} sum(n)={int(n.sum())}")
-    sample = sorted(set(sample))
-    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                         seed=cfg.seed, flags=kv4.KV4_FLAG_INT_PATH)
-    _fill_garbage(built)
-    kept = H.build_streaming(built, cfg, 0, ctx, keep=sample)
-    q = W.queries(cfg, 0)
-    out = H.decode(built, 0, q, n).cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(out))
-    oc = oracle.MixedCache([kept[s][0] for s in sample], [kept[s][1] for s in sample], cfg.group)
-    want, bound = oracle.attend_int(q[sample], oc, cfg.sink, cfg.recent, 1 / math.sqrt(cfg.head_dim))
-    exact = oracle.attend_mixed(q[sample], oc, cfg.sink, cfg.recent, 1 / math.sqrt(cfg.head_dim))
-    err = np.abs(out[sample] - want)
-    assert (err - (INT_ATOL + bound)).max() <= 0
-    dev = float(np.sqrt(np.mean((out[sample] - want) ** 2)))
-    own = float(np.sqrt(np.mean((want - exact) ** 2)))
-    H.log(f"{cfg_name} integer path: {len(sample)} sequences, max |o - o_int| {err.max():.2e}, "
-          f"rms {dev:.2e}; path vs exact rms {own:.2e}")
-    assert dev <= 0.1 * own + 1e-6
-    return out
-
-
-def test_qwen3_8b_batch256_integer_path_sampled():
+def _q8b256_sample(seed):
+    """Shortest, longest and median sequences of the Qwen3-8B batch and a few
+    random ones (for byte comparisons)."""
     cfg = W.CONFIGS["q8b256"]
     ctx = W.contexts(cfg)
     order = np.argsort(ctx)
-    rng = np.random.default_rng(124)
-    sample = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    sample += [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]
-    _run_int("q8b256", sample)
+    rng = np.random.default_rng(seed)
+    return sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
+                      [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]))
 
 
-def test_qwen3_8b_batch256_kv8_sampled():
-    """KV8 mode on config 3's batch: bytes and outputs of sampled sequences
-    against the oracle's INT8 copies and its attention with every position
-    protected."""
-    from int8_mixed_precision_amd import kv4
-    from tests import layout as L
+def _all_rows(cfg, built, out, check_chunk, chunk=32):
+    """Regenerate every sequence's sources, 32 at a time, and hand each chunk
+    (sequence ids, keys, values) to check_chunk."""
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    for lo in range(0, cfg.batch, chunk):
+        seqs = list(range(lo, min(cfg.batch, lo + chunk)))
+        ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
+        check_chunk(seqs, ks, vs)
+
+
+def _build_q8b256(**kw):
     cfg = W.CONFIGS["q8b256"]
     ctx = W.contexts(cfg)
     n = ctx + 1
-    order = np.argsort(ctx)
-    rng = np.random.default_rng(125)
-    sample = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] +
-                        [int(s) for s in rng.choice(cfg.batch, size=5, replace=False)]))
-    H.log(f"case q8b256 KV8: B={cfg.batch} sum(n)={int(n.sum())}")
-    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                         kind=kv4.KV4_KIND_KV8)
+    H.log(f"case q8b256 {kw}: B={cfg.batch} sum(n)={int(n.sum())} max={int(n.max())}")
+    S, R = (0, 0) if kw.get("kind", 0) else (cfg.sink, cfg.recent)
+    built = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, S, R, n, seed=cfg.seed, **kw)
     _fill_garbage(built)
-    kept = H.build_streaming(built, cfg, 0, ctx, keep=sample)
+    H.build_streaming(built, cfg, 0, ctx, keep=())
     q = W.queries(cfg, 0)
     out = H.decode(built, 0, q, n).cpu().numpy()
     assert np.all(np.isfinite(out))
-    oc = oracle.MixedCache([kept[s][0] for s in sample], [kept[s][1] for s in sample], cfg.group)
-    want = oracle.attend_mixed(q[sample], oc, 0, int(n.max()), 1 / math.sqrt(cfg.head_dim))
-    err = H.check_output(out[sample], want, ATOL, RTOL)
-    H.log(f"q8b256 KV8: {len(sample)} sequences, max abs {err[0]:.2e} rel {err[1]:.2e}")
+    return cfg, n, q, built, out
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_batch256_all_rows():
+    """Every (sequence, q head) row of the benchmarked workload, in the
+    benchmark's launch configuration, against the oracle; bytes of sampled
+    sequences bit for bit."""
+    cfg, n, q, built, out = _build_q8b256()
+    pages, side = H.pools_host(built)
+    sm = 1 / math.sqrt(cfg.head_dim)
+    byte_seqs = set(_q8b256_sample(123))
+    worst = [0.0, 0.0]
+
+    def check(seqs, ks, vs):
+        oc = oracle.MixedCache(ks, vs, cfg.group)
+        want = oracle.attend_mixed(q[seqs], oc, cfg.sink, cfg.recent, sm)
+        err = H.check_output(out[seqs], want, ATOL, RTOL)
+        worst[0], worst[1] = max(worst[0], err[0]), max(worst[1], err[1])
+        idx = [i for i, s in enumerate(seqs) if s in byte_seqs]
+        if idx:
+            sub = oracle.MixedCache([ks[i] for i in idx], [vs[i] for i in idx], cfg.group)
+            _compare_bytes(built, pages, side, 0, sub, cfg.sink, cfg.recent, seqs=[seqs[i] for i in idx])
+        H.log(f"  sequences {seqs[0]}..{seqs[-1]}: max abs {err[0]:.2e} rel {err[1]:.2e}")
+
+    _all_rows(cfg, built, out, check)
+    H.log(f"q8b256: all {cfg.batch} x {cfg.q_heads} rows, max abs {worst[0]:.2e} rel {worst[1]:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_batch256_integer_path_all_rows():
+    """Integer decode path (KV4_FLAG_INT_PATH) on the benchmarked workload:
+    every row against the oracle's integer path within 1e-4 plus the tie-flip
+    bound, and an rms far below the path's own error."""
+    from int8_mixed_precision_amd import kv4
+    from tests.test_gpu_parity import INT_ATOL
+    cfg, n, q, built, out = _build_q8b256(flags=kv4.KV4_FLAG_INT_PATH)
+    out = out.astype(np.float64)
+    sm = 1 / math.sqrt(cfg.head_dim)
+    acc = dict(sq_dev=0.0, sq_own=0.0, cnt=0, worst=0.0)
+
+    def check(seqs, ks, vs):
+        oc = oracle.MixedCache(ks, vs, cfg.group)
+        want, bound = oracle.attend_int(q[seqs], oc, cfg.sink, cfg.recent, sm)
+        exact = oracle.attend_mixed(q[seqs], oc, cfg.sink, cfg.recent, sm)
+        err = np.abs(out[seqs] - want)
+        excess = err - (INT_ATOL + bound)
+        assert excess.max() <= 0, (seqs[0], float(excess.max()))
+        acc["sq_dev"] += float(np.sum((out[seqs] - want) ** 2))
+        acc["sq_own"] += float(np.sum((want - exact) ** 2))
+        acc["cnt"] += want.size
+        acc["worst"] = max(acc["worst"], float(err.max()))
+        H.log(f"  sequences {seqs[0]}..{seqs[-1]}: max |o - o_int| {err.max():.2e}")
+
+    _all_rows(cfg, built, out, check)
+    dev = math.sqrt(acc["sq_dev"] / acc["cnt"])
+    own = math.sqrt(acc["sq_own"] / acc["cnt"])
+    H.log(f"q8b256 integer path: all rows, max |o - o_int| {acc['worst']:.2e}, rms {dev:.2e}; "
+          f"path vs exact rms {own:.2e}")
+    assert dev <= 0.1 * own + 1e-6
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_batch256_kv8_all_rows():
+    """KV8 mode on the benchmarked batch: every row's output against the
+    oracle's attention with every position protected; bytes of sampled
+    sequences against its INT8 copies."""
+    from int8_mixed_precision_amd import kv4
+    from tests import layout as L
+    cfg, n, q, built, out = _build_q8b256(kind=kv4.KV4_KIND_KV8)
     pages, _ = H.pools_host(built)
-    for i, b in enumerate(sample):
-        got = L.gather_kv8(pages, layer=0, num_pages=built.desc.num_pages, Hkv=cfg.kv_heads,
-                           d=cfg.head_dim, block_tables=built.bt_host, slot=int(built.slots_host[b]),
-                           n=int(n[b]))
-        for name in ("k8", "v8", "k8s", "v8s"):
-            assert np.array_equal(got[name], getattr(oc, name)[oc.seq(i)]), (b, name)
+    sm = 1 / math.sqrt(cfg.head_dim)
+    byte_seqs = set(_q8b256_sample(125))
+
+    def check(seqs, ks, vs):
+        oc = oracle.MixedCache(ks, vs, cfg.group)
+        want = oracle.attend_mixed(q[seqs], oc, 0, int(n.max()), sm)
+        err = H.check_output(out[seqs], want, ATOL, RTOL)
+        for i, b in enumerate(seqs):
+            if b not in byte_seqs:
+                continue
+            got = L.gather_kv8(pages, layer=0, num_pages=built.desc.num_pages, Hkv=cfg.kv_heads,
+                               d=cfg.head_dim, block_tables=built.bt_host,
+                               slot=int(built.slots_host[b]), n=int(n[b]))
+            for name in ("k8", "v8", "k8s", "v8s"):
+                assert np.array_equal(got[name], getattr(oc, name)[oc.seq(i)]), (b, name)
+        H.log(f"  sequences {seqs[0]}..{seqs[-1]}: max abs {err[0]:.2e} rel {err[1]:.2e}")
+
+    _all_rows(cfg, built, out, check)
 
 
 def test_qwen3_4b_shape_full():
@@ -143,19 +193,6 @@ def test_qwen3_4b_shape_full():
 
 def test_long_context_full():
     _run("long", byte_sample=[0, 7, 15])
-
-
-def test_qwen3_8b_batch256_sampled():
-    cfg = W.CONFIGS["q8b256"]
-    ctx = W.contexts(cfg)
-    rng = np.random.default_rng(123)
-    order = np.argsort(ctx)
-    sample = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
-    sample += [int(s) for s in rng.choice(cfg.batch, size=9, replace=False)]
-    out, built = _run("q8b256", sample=sample)
-    # every row: a convex combination of dequantized values stays inside their
-    # per-channel range; |o| is bounded by the largest |v^| (<= ~6 for N(0,1))
-    assert np.abs(out).max() < 16.0
 
 
 def test_full36_decode_steps():

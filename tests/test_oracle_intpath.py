@@ -169,3 +169,79 @@ def test_brute_force_small_case():
         den = sum(p)
         want = np.array([float(x / den) for x in num])
         assert np.allclose(out[0, j], want, rtol=1e-12, atol=1e-13)
+
+
+def _two_token_tie_case():
+    """Two INT4 positions in one 8-position block, q = 0 (so both scores are
+    0 and p = 1 for both): token 0's values are 0..15 in every 32-channel group
+    (offset 0, step 1), token 1's values are 0, 0.5, .., 7.5 (offset 0, step
+    0.5).  Per value group w = p * Delta = (1, 0.5), sigma = 1/255 and
+    w / sigma = (255, 127.5): token 1's code sits exactly on a rounding tie."""
+    d = 128
+    v0 = np.tile(np.arange(16, dtype=np.float32), d // 16)
+    v1 = np.tile(np.arange(16, dtype=np.float32) * 0.5, d // 16)
+    k = np.zeros((2, 1, d), np.float32)
+    v = np.stack([v0, v1])[:, None, :]
+    return [k], [v]
+
+
+def test_tie_flip_bound_by_hand():
+    """The integer path's tie-flip bound (reading I-5) on a block built so
+    that one w / sigma lies on a tie: the bound of channel c is
+    sigma * code_1(c) / den = (1/255) * (c mod 16) / 2, and the output, with
+    u = (255, rint(127.5) = 128), is (c mod 16) * (1 + 128/255) / 2."""
+    ks, vs = _two_token_tie_case()
+    oc = oracle.MixedCache(ks, vs, 32)
+    q = np.zeros((1, 1, 128), np.float32)
+    out, bound = oracle.attend_int(q, oc, 0, 0, SCALE)
+    c = np.arange(128) % 16
+    assert np.allclose(bound[0, 0], c / 255.0 / 2.0, rtol=0, atol=1e-15)
+    assert np.allclose(out[0, 0], c * (1 + 128 / 255) / 2.0, rtol=0, atol=1e-13)
+
+
+def test_tie_flip_window_width():
+    """Just outside the 2^-6 window the bound is 0; a window wide enough to
+    reach the code counts it.  Token 1's step is the binary16 value after 0.5
+    (0.5 + 2^-11), so w / sigma = 127.5 + 255 * 2^-11 / 1 = 127.6245...: 0.12
+    from the tie."""
+    ks, vs = _two_token_tie_case()
+    vs[0][1, 0, :] *= np.float32(1.0 + 2.0 ** -10)          # step 0.5 -> 0.5 (1 + 2^-10)
+    oc = oracle.MixedCache(ks, vs, 32)
+    assert np.all(oc.v4d[1] == 0x3801)                      # binary16 0.5 + 2^-11
+    q = np.zeros((1, 1, 128), np.float32)
+    x = 255 * (0.5 + 2.0 ** -11)
+    assert abs(x - math.floor(x) - 0.5) > 2.0 ** -6
+    _, bound = oracle.attend_int(q, oc, 0, 0, SCALE)
+    assert np.all(bound == 0)
+    _, wide = oracle.attend_int(q, oc, 0, 0, SCALE, eps=0.2)
+    c = np.arange(128) % 16
+    assert np.allclose(wide[0, 0], c / 255.0 / 2.0, rtol=0, atol=1e-15)
+
+
+def test_negligible_block_rule():
+    """The kernels give all-zero 8-bit codes to a block whose largest w is at
+    most 2^-100 in their own scaled units; such a block's weight relative to
+    the leading position is below 2^-90.  The oracle keeps rint(255 w / max w)
+    for every block; this pins that the difference is far below any
+    tolerance: a block whose keys score about 150 units (in log base e) below
+    the leading position, with its value codes zeroed, changes the oracle's
+    output by less than 2^-90."""
+    d, n = 128, 24
+    rng = np.random.default_rng(77)
+    k = np.zeros((n, 1, d), np.float32)
+    k[:8, 0, :] = 1.0                                         # the leading block
+    k[8:16, 0, :] = -1.0                                      # the negligible block
+    k[16:, 0, :] = 0.5
+    v = _bf16(rng.standard_normal((n, 1, d)))
+    q = np.full((1, 1, d), 8.0, np.float32)
+    oc = oracle.MixedCache([k], [v], 32)
+    # the INT8 query is 127 everywhere with s_q = 8/127 and every key group is
+    # constant (step 0, offset k), so a position's score is sm_scale * 8 * 128 * k:
+    # with sm_scale = 10/128 the middle block sits 160 nats below the leading one
+    sm = 10.0 / 128
+    out, _ = oracle.attend_int(q, oc, 0, 0, sm)
+    oc.v4[8:16] = 0
+    out0, _ = oracle.attend_int(q, oc, 0, 0, sm)
+    diff = float(np.abs(out - out0).max())
+    assert diff < 2.0 ** -90
+    assert np.all(np.isfinite(out))
