@@ -13,7 +13,8 @@
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers unless stated otherwise; the
  *     library never allocates, frees or initialises device memory.  Pools and
- *     workspaces are owned by the caller.
+ *     workspaces are owned by the caller (the one exception is the static
+ *     workspace of kv4_decode_attn_noalloc, reserved with the code object).
  *   - Work is enqueued asynchronously on the given HIP stream; device-side
  *     faults surface at the caller's next synchronisation with that stream.
  *   - Arguments are validated on the host before anything is launched; on any
@@ -345,6 +346,31 @@ int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_b
                      const void* v_bf16, const int32_t* cu_seqlens, int batch, int total,
                      int max_seqlen, float sm_scale, void* out, int out_dtype,
                      kv4_stream_t stream);
+
+/*
+ * kv4_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the partition's records, header and pool
+ * counters live in a static device array of KV4_NOALLOC_SCRATCH_BYTES that the
+ * library reserves with its code object -- each GPU the library runs on holds
+ * its own copy until the process ends.  The call allocates and frees nothing;
+ * it looks the array's device address up once per device (hipGetSymbolAddress,
+ * on the first call with that device current).  Arguments, kernels and results
+ * are those of kv4_decode_attn (the output is bit-identical); what must start
+ * at zero (the pool counters) is cleared by a kernel in every call.  Every
+ * call on one GPU shares that GPU's array and leaves its contents behind, so
+ * calls that overlap in time on one GPU (different streams, threads or
+ * handles) race: order them.
+ * Errors: as kv4_decode_attn, plus KV4_ERR_CAPACITY when the batch needs more
+ * workspace than the array holds (kv4_decode_workspace_bytes > the limit;
+ * checked on the host, nothing launched) and KV4_ERR_HIP when the array's
+ * address cannot be obtained.
+ */
+#define KV4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kv4_decode_attn_noalloc(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                            const int32_t* slot_ids, const int32_t* block_tables, int batch,
+                            int max_ctx, float sm_scale, void* out, int out_dtype,
+                            kv4_stream_t stream);
 
 /* Free the host handle (the pools stay with the caller). NULL is accepted. */
 int kv4_cache_free(kv4_cache* cache);

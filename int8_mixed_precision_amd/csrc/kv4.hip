@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "kv4_append.hpp"
@@ -14,6 +15,13 @@
 #include "kv4_decode.hpp"
 #include "kv4_decode_mfma.hpp"
 #include "kv4_prefill.hpp"
+
+// Workspace of kv4_decode_attn_noalloc: device memory reserved with the code
+// object (every device that loads the library holds its own copy until the
+// process ends).  Host code never passes this name to a kernel: on the host it
+// is only a stand-in for the symbol, whose per-device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[KV4_NOALLOC_SCRATCH_BYTES];
 
 struct kv4_cache {
     kv4_cache_desc desc;
@@ -294,6 +302,34 @@ void launch_merge(const kv4::DecodeArgs& a, hipStream_t s)
     hipLaunchKernelGGL(kv4::merge_parts_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return KV4_ERR_HIP;
+    }
+    if (dev >= kMaxDevices) return KV4_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return KV4_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KV4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -442,6 +478,36 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
     int st = decode_args(cache, layer, q_bf16, seq_lens, slot_ids, block_tables, batch, max_ctx,
                          sm_scale, workspace, workspace_bytes_, true, a);
     if (st != KV4_OK || batch == 0) return st;
+    if (out == nullptr) return KV4_ERR_INVALID_ARG;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    launch_decode(a, s);
+    st = launch_status();
+    if (st != KV4_OK) return st;
+    launch_merge(a, s);
+    return launch_status();
+}
+
+int kv4_decode_attn_noalloc(kv4_cache* cache, int layer, const void* q_bf16, const int32_t* seq_lens,
+                            const int32_t* slot_ids, const int32_t* block_tables, int batch,
+                            int max_ctx, float sm_scale, void* out, int out_dtype,
+                            kv4_stream_t stream)
+{
+    if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
+    if (cache == nullptr || batch < 0 || max_ctx < 1) return KV4_ERR_INVALID_ARG;
+    size_t need = 0;
+    int st = kv4_decode_workspace_bytes(cache, batch, max_ctx, &need);
+    if (st != KV4_OK) return st;
+    if (need > (size_t)KV4_NOALLOC_SCRATCH_BYTES) return KV4_ERR_CAPACITY;
+    if (batch == 0) return KV4_OK;
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != KV4_OK) return st;
+    kv4::DecodeArgs a;
+    st = decode_args(cache, layer, q_bf16, seq_lens, slot_ids, block_tables, batch, max_ctx,
+                     sm_scale, ws, (size_t)KV4_NOALLOC_SCRATCH_BYTES, true, a);
+    if (st != KV4_OK) return st;
     if (out == nullptr) return KV4_ERR_INVALID_ARG;
     a.out = out;
     a.out_dtype = out_dtype;

@@ -63,6 +63,7 @@ def _load(path: str = LIB_PATH):
     L.kv4_decode_attn.argtypes = [P, i32, P, P, P, P, i32, i32, ctypes.c_float, P, i32, P, sz, P]
     L.kv4_decode_partials.argtypes = [P, i32, P, P, P, P, i32, i32, ctypes.c_float, P, sz, P]
     L.kv4_decode_merge.argtypes = [P, P, i32, i32, P, i32, P, sz, P]
+    L.kv4_decode_attn_noalloc.argtypes = [P, i32, P, P, P, P, i32, i32, ctypes.c_float, P, i32, P]
     L.kv4_cache_free.argtypes = [P]
     L.kv4_status_string.argtypes = [i32]
     L.kv4_status_string.restype = ctypes.c_char_p
@@ -70,7 +71,8 @@ def _load(path: str = LIB_PATH):
     L.kv4_prefill_attn.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.c_float, P, i32, P]
     for f in ("kv4_cache_required_bytes", "kv4_cache_create", "kv4_append",
               "kv4_decode_workspace_bytes", "kv4_decode_attn", "kv4_decode_partials",
-              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition", "kv4_prefill_attn"):
+              "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition", "kv4_prefill_attn",
+              "kv4_decode_attn_noalloc"):
         getattr(L, f).restype = i32
     return L
 
@@ -199,6 +201,26 @@ def kv4_decode_attn(cache, layer: int, q: torch.Tensor, seq_lens: torch.Tensor,
                                 _ptr(block_tables), int(batch), int(max_ctx), float(sm_scale),
                                 _ptr(out), int(out_dtype), _ptr(workspace), workspace.numel(),
                                 _stream(stream)), "kv4_decode_attn")
+
+
+KV4_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def kv4_decode_attn_noalloc(cache, layer: int, q: torch.Tensor, seq_lens: torch.Tensor,
+                            slot_ids: torch.Tensor, block_tables: torch.Tensor, batch: int,
+                            max_ctx: int, sm_scale: float, out: torch.Tensor, out_dtype: int,
+                            stream=None) -> None:
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    for name, t in (("seq_lens", seq_lens), ("slot_ids", slot_ids), ("block_tables", block_tables)):
+        _need(t, name, torch.int32, dev)
+    _need(out, "out", torch.float32 if out_dtype == KV4_OUT_F32 else torch.bfloat16, dev)
+    if q.dim() != 3 or q.shape[0] < batch or out.shape != q.shape:
+        raise ValueError("q and out must be [batch, Hq, d]")
+    _check(_lib.kv4_decode_attn_noalloc(cache, int(layer), _ptr(q), _ptr(seq_lens), _ptr(slot_ids),
+                                        _ptr(block_tables), int(batch), int(max_ctx),
+                                        float(sm_scale), _ptr(out), int(out_dtype),
+                                        _stream(stream)), "kv4_decode_attn_noalloc")
 
 
 def kv4_prefill_attn(cache, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
