@@ -57,18 +57,23 @@ def parse():
                     help="skip the integer decode path (KV4_FLAG_INT_PATH) over the same KV4 bytes")
     ap.add_argument("--prefill-reps", type=int, default=3,
                     help="timed prefill attentions over the populate histories (0 = skip)")
+    ap.add_argument("--only-kv4", action="store_true",
+                    help="time the KV4 decode only (no comparators, sub-records, populate, prefill or "
+                         "CPU baseline): the command the counter profiles run")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the sub-records (G = 128 rotated, Qwen3-4B shape, long context) and "
+                         "the read ceilings")
     ap.add_argument("--rotate", action="store_true",
                     help="store keys in the rotated basis (KV4_FLAG_ROTATE_K) in the KV4 cache")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_kv4_mfma_kernel_qwen3-8b_b256_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_kv4_mfma_kernel_qwen3-8b_b256_counters.json"))
     # summaries of rocprofv3 output (no GPU work): kernel durations from a
-    # --kernel-trace csv directory; HBM traffic from a FETCH_SIZE and a
-    # WRITE_SIZE --pmc csv directory of runs made with --copy-calibration
+    # --kernel-trace csv directory; counters and HBM traffic from --pmc csv
+    # directories
     ap.add_argument("--summarize-trace", metavar="DIR")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc output directories (one per counter pass)")
     ap.add_argument("--summary-out", metavar="FILE")
     ap.add_argument("--summary-cmd", default="", help="command that produced the profile")
     ap.add_argument("--summary-bench", metavar="JSON",
@@ -156,8 +161,6 @@ def append_bytes_bf16(n, cfg):
 
 DOMINANT = "decode_kv4_mfma_kernel"
 TP_NOTE = {"q8b256tp2": " (one GPU's share under two-way tensor parallelism)"}
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
-COPY_BYTES = 1 << 30
 
 
 def _csv_rows(d, suffix):
@@ -215,42 +218,276 @@ def summarize_trace(args):
     print(text)
 
 
-def summarize_pmc(args):
-    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch), each scaled by what the same counter reads for the
-    1 GiB device-to-device copies that --copy-calibration issues."""
-    out = {}
-    for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_pmc):
-        rows = [r for r in _csv_rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
-        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        dom = [float(r["Counter_Value"]) for r in rows if DOMINANT in r["Kernel_Name"]]
-        last_dom = max(int(r["Dispatch_Id"]) for r in rows if DOMINANT in r["Kernel_Name"])
-        # the calibration copies are the device copies issued after every decode
-        cal = [float(r["Counter_Value"]) for r in rows
-               if r["Kernel_Name"].startswith(COPY_KERNEL) and int(r["Dispatch_Id"]) > last_dom]
-        cal = [c for c in cal if cal and c >= 0.5 * max(cal)]     # the 1 GiB copies only
-        if not dom or not cal:
-            raise SystemExit(f"{counter}: {len(dom)} decode dispatches, {len(cal)} copy dispatches")
-        scale = COPY_BYTES / (np.median(cal) * 1024.0)
-        out[counter] = dict(kib_per_launch=float(np.mean(dom)), launches=len(dom),
-                            kib_spread=[float(np.min(dom)), float(np.max(dom))],
-                            copy_kib=float(np.median(cal)), copy_launches=len(cal), scale=scale,
-                            bytes_per_launch=float(np.mean(dom)) * 1024.0 * scale)
-    fetch, write = out["FETCH_SIZE"], out["WRITE_SIZE"]
-    total = fetch["bytes_per_launch"] + write["bytes_per_launch"]
-    res = dict(kernel=DOMINANT, kernel_source_hash=_kernel_hash(), command=args.summary_cmd,
-               fetch=fetch, write=write, bytes_per_launch=int(round(total)))
+def summarize_counters(args):
+    """Per-launch counters of the dominant kernel from rocprofv3 --pmc runs
+    (one directory per pass), averaged over its dispatches, and the HBM
+    traffic they give:
+      read bytes  = 32 TCC_EA0_RDREQ_32B + 64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B
+                    (the L2's read requests to memory by size);
+      write bytes = 64 TCC_EA0_WRREQ_64B + 32 (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B);
+    and the factor by which the FETCH_SIZE / WRITE_SIZE metrics of this
+    rocprofv3 build differ from those request-size sums."""
+    vals = {}
+    for d in args.summarize_counters:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if DOMINANT not in r["Kernel_Name"]:
+                continue
+            key = (r["Counter_Name"], int(r["Dispatch_Id"]))
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (name, _), v in vals.items():
+        per.setdefault(name, []).append(v)
+    mean = {k: float(np.mean(v)) for k, v in per.items()}
+    launches = {k: len(v) for k, v in per.items()}
+    out = dict(kernel=DOMINANT, kernel_source_hash=_kernel_hash(), commands=args.summary_cmd,
+               counters_per_launch=mean, launches=launches)
+    if all(k in mean for k in ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B")):
+        rd = 32 * mean["TCC_EA0_RDREQ_32B"] + 64 * mean["TCC_EA0_RDREQ_64B"] + 128 * mean["TCC_EA0_RDREQ_128B"]
+        out["read_bytes_per_launch"] = rd
+        if "FETCH_SIZE" in mean:
+            out["fetch_size_factor"] = rd / (mean["FETCH_SIZE"] * 1024.0)
+    if all(k in mean for k in ("TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")):
+        wr = 64 * mean["TCC_EA0_WRREQ_64B"] + 32 * (mean["TCC_EA0_WRREQ"] - mean["TCC_EA0_WRREQ_64B"])
+        out["write_bytes_per_launch"] = wr
+        if "WRITE_SIZE" in mean:
+            out["write_size_factor"] = wr / (mean["WRITE_SIZE"] * 1024.0)
+    if "read_bytes_per_launch" in out and "write_bytes_per_launch" in out:
+        out["bytes_per_launch"] = int(round(out["read_bytes_per_launch"] + out["write_bytes_per_launch"]))
+    if "TCC_HIT" in mean and "TCC_MISS" in mean:
+        out["l2_hit_rate"] = mean["TCC_HIT"] / max(1.0, mean["TCC_HIT"] + mean["TCC_MISS"])
     if args.summary_out:
-        json.dump(res, open(args.summary_out, "w"), indent=1)
-    print(json.dumps(res, indent=1))
+        json.dump(out, open(args.summary_out, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+class Timer:
+    """HIP events on the stream every launch goes to (torch's current stream)."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def build_caches(cfg, specs, H, W, kv4, dev, keep_first=0):
+    """Build every cache in `specs` ({name: make_cache kwargs}) from the same
+    seeded sources, 32 sequences at a time; return the caches, the step
+    tokens on the device, and the histories of the first `keep_first`
+    sequences (for the populate and prefill timings)."""
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    B = cfg.batch
+    caches = {name: H.make_cache(cfg.q_heads, cfg.kv_heads, kw.pop("group", cfg.group),
+                                 kw.pop("sink", cfg.sink), kw.pop("recent", cfg.recent), n,
+                                 seed=cfg.seed, device=str(dev), **kw)
+              for name, kw in ((k, dict(v)) for k, v in specs.items())}
+    step_k, step_v, first = [], [], None
+    for lo in range(0, B, 32):
+        seqs = list(range(lo, min(B, lo + 32)))
+        ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
+        if lo == 0 and keep_first:
+            first = [(ks[i][:int(ctx[s])], vs[i][:int(ctx[s])]) for i, s in enumerate(seqs[:keep_first])]
+        hist = [i for i, s in enumerate(seqs) if ctx[s] > 0]
+        for c in caches.values():
+            H.append_chunks(c, 0, [ks[i][:int(ctx[seqs[i]])] for i in hist],
+                            [vs[i][:int(ctx[seqs[i]])] for i in hist], [0] * len(hist),
+                            [seqs[i] for i in hist], device=str(dev))
+        for i, s in enumerate(seqs):
+            step_k.append(ks[i][int(ctx[s]):int(ctx[s]) + 1])
+            step_v.append(vs[i][int(ctx[s]):int(ctx[s]) + 1])
+        kv4_sync(dev)
+    knew = H.to_dev_bf16(np.concatenate(step_k, 0), str(dev))
+    vnew = H.to_dev_bf16(np.concatenate(step_v, 0), str(dev))
+    return caches, knew, vnew, first
+
+
+def kv4_sync(dev):
+    import torch
+    torch.cuda.synchronize(dev)
+
+
+def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=None,
+              clock_warm_s=0.0):
+    """`warmup` untimed steps, then `steps` timed steps of (append, partials,
+    merge) on cache c; every step re-appends the same token at the same
+    position (idempotent), so each does the full work on identical state.
+    `flush` (untimed, between steps) evicts the caches for workloads that fit
+    in them.  Returns per-step milliseconds of the three phases and the
+    output."""
+    dev = knew.device
+    B = len(n)
+    ctx = n - 1
+    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    ctx_d = torch.from_numpy(ctx.astype(np.int32)).to(dev)
+    n_d = torch.from_numpy(n.astype(np.int32)).to(dev)
+    max_ctx = int(n.max())
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+    out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    ws = c.cache.workspace(B, max_ctx)
+    st = tm.stream
+
+    def append():
+        kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B, B, st)
+
+    def partials():
+        kv4.kv4_decode_partials(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm, ws, st)
+
+    def merge():
+        kv4.kv4_decode_merge(c.cache.handle, n_d, B, max_ctx, out, kv4.KV4_OUT_F32, ws, st)
+
+    if clock_warm_s > 0:
+        # untimed: bring the clocks up before the first timed launch
+        t_end = time.perf_counter() + clock_warm_s
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                append(); partials(); merge()
+            torch.cuda.synchronize()
+    for _ in range(warmup):
+        if flush:
+            flush()
+        append(); partials(); merge()
+    torch.cuda.synchronize()
+    t = np.zeros((steps, 3))
+    evs = []
+    for i in range(steps):
+        if flush:
+            flush()
+        e0 = tm.ev(); append(); e1 = tm.ev(); partials(); e2 = tm.ev(); merge(); e3 = tm.ev()
+        evs.append((e0, e1, e2, e3))
+    torch.cuda.synchronize()
+    for i, (e0, e1, e2, e3) in enumerate(evs):
+        t[i] = (e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3))
+    whole = torch.empty_like(out)
+    kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm, whole,
+                        kv4.KV4_OUT_F32, ws, st)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert torch.equal(whole, out), "kv4_decode_attn differs from partials + merge"
+    waves, chunks = kv4.kv4_decode_partition(c.cache.handle)
+    ta, tp, tmg = t[:, 0], t[:, 1], t[:, 2]
+    td = tp + tmg
+    return dict(append_ms=float(ta.mean()), partials_ms=float(tp.mean()), merge_ms=float(tmg.mean()),
+                decode_ms=float(td.mean()), decode_ms_median=float(np.median(td)),
+                decode_ms_p10=float(np.percentile(td, 10)), decode_ms_p90=float(np.percentile(td, 90)),
+                partials_ms_median=float(np.median(tp)), waves=waves, pool_chunks=chunks)
+
+
+def read_ceiling(torch, dev, st, partial_bytes):
+    """The read ceilings of this GPU (libkv4_roof.so): a 4 GiB stream, and
+    random 2,560-byte blocks (one (page, kv head) block of the INT4 pool) in
+    the decode's own launch shape -- 4,096 one-wave workgroups, two blocks in
+    flight, nontemporal loads -- over as many bytes as the decode's tiles."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "int8_mixed_precision_amd", "libkv4_roof.so"))
+    lib.kv4_roof_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.kv4_roof_block_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    tm = Timer(torch, st)
+    sp = ctypes.c_void_p(st.cuda_stream)
+    res = {}
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = tm.ev(); assert fn() == 0; e1 = tm.ev()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms = timed(lambda: lib.kv4_roof_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 32 * cus,
+                                                ctypes.c_void_p(sink.data_ptr()), sp))
+    res["stream_gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    waves, blk = 16 * cus, 2560
+    per = max(2, int(partial_bytes // blk // waves) // 2 * 2)
+    nb = per * waves
+    ids = torch.from_numpy(np.random.default_rng(7).permutation(nb).astype(np.int32)).to(dev)
+    ms = timed(lambda: lib.kv4_roof_block_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                               ctypes.c_void_p(ids.data_ptr()), waves, per, blk,
+                                               ctypes.c_void_p(sink.data_ptr()), sp))
+    res["block2560_gbs"] = round(nb * blk / (ms * 1e-3) / 1e9, 1)
+    res["block2560_us"] = round(ms * 1e3, 1)
+    res["block2560_bytes"] = nb * blk
+    res["kernels"] = ("libkv4_roof.so: stream_read_kernel (4 GiB, 8 x 16 B loads in flight per lane), "
+                      f"block_read_kernel ({waves} one-wave workgroups x {per} random 2,560 B blocks, "
+                      "2 in flight); nontemporal loads")
+    del buf, ids
+    torch.cuda.empty_cache()
+    return res
+
+
+def sub_record(name, cfg, kv4c_kw, H, W, kv4, torch, dev, tm, args, flush_bytes=0, bf16=True):
+    """Decode-attention time, bandwidth and fraction of the HBM peak of one
+    more workload (KV4 cache, and the BF16 comparator for the ratio)."""
+    ctx = W.contexts(cfg)
+    n = ctx + 1
+    specs = {"kv4": dict(kv4c_kw)}
+    if bf16:
+        specs["bf16"] = dict(kind=kv4.KV4_KIND_BF16, sink=0, recent=0)
+    caches, knew, vnew, _ = build_caches(cfg, specs, H, W, kv4, dev)
+    q = H.to_dev_bf16(W.queries(cfg, 0), str(dev))
+    flush = None
+    if flush_bytes:
+        # reading 1 GiB of other data evicts the 256 MB Infinity Cache (MALL)
+        # with clean lines, so the timed decode neither hits it nor pays for
+        # writing dirty flush data back
+        scratch = torch.ones(flush_bytes // 4, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
+
+        def flush():
+            torch.amax(scratch, dim=0, out=sink)
+    res = {}
+    for k, c in caches.items():
+        res[k] = time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, args.steps, args.warmup, flush=flush)
+    g = kv4c_kw.get("group", cfg.group)
+    cg = W.scaled(cfg, group=g)
+    db = decode_bytes_kv4(n, cg)
+    pb = partial_bytes_kv4(n, cg)
+    r = res["kv4"]
+    out = {"workload": f"{cfg.name}: batch {cfg.batch}, {cfg.q_heads}q/{cfg.kv_heads}kv, group {g}, "
+                       f"S={cfg.sink}, R={cfg.recent}, sum n {int(n.sum())}, max n {int(n.max())}",
+           "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
+           "decode_attn_us_median": round(r["decode_ms_median"] * 1e3, 2),
+           "decode_partials_us": round(r["partials_ms"] * 1e3, 2),
+           "decode_merge_us": round(r["merge_ms"] * 1e3, 2),
+           "append_us": round(r["append_ms"] * 1e3, 2),
+           "decode_alg_bytes": db,
+           "decode_attn_gbs": round(db / (r["decode_ms"] * 1e-3) / 1e9, 1),
+           "decode_attn_frac_hbm_peak": round(db / (r["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "partials_frac_hbm_peak": round(pb / (r["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "layer_tokens_per_s": round(cfg.batch / ((r["append_ms"] + r["decode_ms"]) * 1e-3), 1)}
+    if flush_bytes:
+        out["cache_flush"] = f"{flush_bytes >> 20} MiB of other data read between steps (untimed)"
+    if "bf16" in res:
+        rb = res["bf16"]
+        out["bf16_decode_attn_us"] = round(rb["decode_ms"] * 1e3, 2)
+        out["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
+        out["speedup_vs_bf16_step"] = round((rb["append_ms"] + rb["decode_ms"]) /
+                                            (r["append_ms"] + r["decode_ms"]), 3)
+    del caches, knew, vnew, q
+    torch.cuda.empty_cache()
+    log(f"{name}: decode {out['decode_attn_us']} us, {out['decode_attn_gbs']} GB/s "
+        f"({100 * out['decode_attn_frac_hbm_peak']:.1f}% of peak)")
+    return out
 
 
 def main():
     args = parse()
     if args.summarize_trace:
         return summarize_trace(args)
-    if args.summarize_pmc:
-        return summarize_pmc(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 "
                                    "(the decode step shards by sequence or kv head with no "
@@ -259,9 +496,11 @@ def main():
 
     import torch
     from int8_mixed_precision_amd import kv4
+    from int8_mixed_precision_amd import paged as H
     from int8_mixed_precision_amd import workloads as W
-    from tests import gpu_harness as H
 
+    if args.config == "full36":
+        return run_full36(args, torch, kv4, H, W)
     cfg = W.CONFIGS[args.config]
     if args.group:
         cfg = W.scaled(cfg, group=args.group)
@@ -270,147 +509,67 @@ def main():
     B = cfg.batch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    tm = Timer(torch, stream)
     t0 = time.time()
     log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
 
-    kv4c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                        seed=cfg.seed, waves=args.waves, pool_chunks=args.pool_chunks,
-                        flags=kv4.KV4_FLAG_ROTATE_K if args.rotate else 0, device="cuda:0")
-    caches = [("kv4", kv4c)]
-    if not args.no_bf16:
-        bfc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                           kind=kv4.KV4_KIND_BF16, waves=args.waves,
-                           pool_chunks=args.pool_chunks, device="cuda:0")
-        caches.append(("bf16", bfc))
-    if not args.no_int_path:
-        ipc = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, n,
-                           seed=cfg.seed, waves=args.waves, pool_chunks=args.pool_chunks,
-                           flags=kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if args.rotate else 0),
-                           device="cuda:0")
-        caches.append(("int", ipc))
-    if not args.no_kv8:
-        k8c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, 0, 0, n, seed=cfg.seed,
-                           kind=kv4.KV4_KIND_KV8, waves=args.waves,
-                           pool_chunks=args.pool_chunks, device="cuda:0")
-        caches.append(("kv8", k8c))
-    # build every cache from the same sources, sequence chunk by chunk
-    step_k, step_v = [], []
-    pop = None
-    for lo in range(0, B, 32):
-        seqs = list(range(lo, min(B, lo + 32)))
-        ks, vs = W.all_kv_sources(cfg, 0, n, seqs=seqs, threads=16)
-        if lo == 0 and args.populate_reps > 0:
-            # the first chunk's histories, kept on the device for the populate timing
-            hist = np.array([int(ctx[s]) for s in seqs])
-            pcu = np.zeros(len(seqs) + 1, np.int32)
-            pcu[1:] = np.cumsum(hist)
-            pop = dict(hist=hist,
-                       k=H.to_dev_bf16(np.concatenate([ks[i][:hist[i]] for i in range(len(seqs))], 0), "cuda:0"),
-                       v=H.to_dev_bf16(np.concatenate([vs[i][:hist[i]] for i in range(len(seqs))], 0), "cuda:0"),
-                       cu=torch.from_numpy(pcu).to(dev),
-                       ctx0=torch.zeros(len(seqs), dtype=torch.int32, device=dev),
-                       slots=torch.from_numpy(kv4c.slots_host[seqs]).to(dev))
-        for _, c in caches:
-            H.append_chunks(c, 0, [ks[i][:int(ctx[s])] for i, s in enumerate(seqs)],
-                            [vs[i][:int(ctx[s])] for i, s in enumerate(seqs)], [0] * len(seqs),
-                            seqs, device="cuda:0")
-        for i, s in enumerate(seqs):
-            step_k.append(ks[i][int(ctx[s]):int(ctx[s]) + 1])
-            step_v.append(vs[i][int(ctx[s]):int(ctx[s]) + 1])
-        torch.cuda.synchronize()
-        log(f"built sequences {seqs[0]}..{seqs[-1]}")
-    knew = H.to_dev_bf16(np.concatenate(step_k, 0), "cuda:0")
-    vnew = H.to_dev_bf16(np.concatenate(step_v, 0), "cuda:0")
-    q = H.to_dev_bf16(W.queries(cfg, 0), "cuda:0")
-    cu = torch.arange(B + 1, dtype=torch.int32, device=dev)
-    ctx_d = torch.from_numpy(ctx.astype(np.int32)).to(dev)
-    n_d = torch.from_numpy(n.astype(np.int32)).to(dev)
-    max_ctx = int(n.max())
-    sm = 1.0 / math.sqrt(cfg.head_dim)
+    common = dict(waves=args.waves, pool_chunks=args.pool_chunks)
+    specs = {"kv4": dict(common, flags=kv4.KV4_FLAG_ROTATE_K if args.rotate else 0)}
+    if not args.only_kv4:
+        if not args.no_bf16:
+            specs["bf16"] = dict(common, kind=kv4.KV4_KIND_BF16, sink=0, recent=0)
+        if not args.no_int_path:
+            specs["int"] = dict(common, flags=kv4.KV4_FLAG_INT_PATH |
+                                (kv4.KV4_FLAG_ROTATE_K if args.rotate else 0))
+        if not args.no_kv8:
+            specs["kv8"] = dict(common, kind=kv4.KV4_KIND_KV8, sink=0, recent=0)
+        if not args.no_sub and cfg.name == "q8b256" and cfg.group == 32 and not args.rotate:
+            # the pages' default representation: head-wise groups, rotated keys
+            specs["g128_rot"] = dict(common, group=128, flags=kv4.KV4_FLAG_ROTATE_K)
+    keep = 32 if (args.populate_reps > 0 and not args.only_kv4) else 0
+    caches, knew, vnew, first = build_caches(cfg, specs, H, W, kv4, dev, keep_first=keep)
+    q = H.to_dev_bf16(W.queries(cfg, 0), str(dev))
     log(f"caches built in {time.time() - t0:.1f}s")
 
-    # every launch goes to torch's current stream, which the events record on
-    stream = torch.cuda.current_stream()
+    # the headline first, after an untimed clock warm-up; then the comparators
     results = {}
-    for name, c in caches:
-        out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
-        ws = c.cache.workspace(B, max_ctx)
-        waves, chunks = kv4.kv4_decode_partition(c.cache.handle)
-
-        def append():
-            kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B,
-                           B, stream)
-
-        def partials():
-            kv4.kv4_decode_partials(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B,
-                                    max_ctx, sm, ws, stream)
-
-        def merge():
-            kv4.kv4_decode_merge(c.cache.handle, n_d, B, max_ctx, out, kv4.KV4_OUT_F32, ws, stream)
-
-        for _ in range(args.warmup):
-            append()
-            partials()
-            merge()
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        for i in range(args.steps):
-            ev[i][0].record(stream)
-            append()
-            ev[i][1].record(stream)
-            partials()
-            ev[i][2].record(stream)
-            merge()
-            ev[i][3].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        t = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)]
-                      for i in range(args.steps)])
-        ta, tp, tm = t[:, 0], t[:, 1], t[:, 2]
-        td = tp + tm
-        assert torch.isfinite(out).all()
-        # the two phases are kv4_decode_attn exactly
-        whole = torch.empty_like(out)
-        kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm,
-                            whole, kv4.KV4_OUT_F32, ws, stream)
-        torch.cuda.synchronize()
-        assert torch.equal(whole, out), "kv4_decode_attn differs from partials + merge"
-        results[name] = dict(append_ms=float(ta.mean()), partials_ms=float(tp.mean()),
-                             merge_ms=float(tm.mean()), decode_ms=float(td.mean()),
-                             decode_ms_median=float(np.median(td)),
-                             decode_ms_p10=float(np.percentile(td, 10)),
-                             decode_ms_p90=float(np.percentile(td, 90)),
-                             wall_ms_per_step=wall * 1e3 / args.steps,
-                             waves=waves, pool_chunks=chunks)
-        log(f"{name}: append {ta.mean() * 1e3:.1f} us, partials {tp.mean() * 1e3:.1f} us, "
-            f"merge {tm.mean() * 1e3:.1f} us, decode {td.mean() * 1e3:.1f} us "
-            f"(median {np.median(td) * 1e3:.1f}), waves {waves}, pool chunks {chunks}")
+    for name, c in caches.items():
+        results[name] = time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, args.steps, args.warmup,
+                                  clock_warm_s=0.3 if name == "kv4" else 0.0)
+        r = results[name]
+        log(f"{name}: append {r['append_ms'] * 1e3:.1f} us, partials {r['partials_ms'] * 1e3:.1f} us, "
+            f"merge {r['merge_ms'] * 1e3:.1f} us, decode {r['decode_ms'] * 1e3:.1f} us "
+            f"(median {r['decode_ms_median'] * 1e3:.1f}), waves {r['waves']}, pool chunks {r['pool_chunks']}")
 
     # bulk populate: the first 32 sequences' histories re-appended whole (after
     # every decode timing: it rewrites ring entries the step token owns)
     populate = prefill = None
-    if pop is not None:
-        c = kv4c
-        T = int(pop["hist"].sum())
+    if first is not None:
+        c = caches["kv4"]
+        hist = np.array([k.shape[0] for k, _ in first])
+        pcu = np.zeros(len(first) + 1, np.int32)
+        pcu[1:] = np.cumsum(hist)
+        pk = H.to_dev_bf16(np.concatenate([k for k, _ in first], 0), str(dev))
+        pv = H.to_dev_bf16(np.concatenate([v for _, v in first], 0), str(dev))
+        cu = torch.from_numpy(pcu).to(dev)
+        ctx0 = torch.zeros(len(first), dtype=torch.int32, device=dev)
+        slots = torch.from_numpy(c.slots_host[:len(first)].copy()).to(dev)
+        T = int(hist.sum())
 
         def bulk():
-            kv4.kv4_append(c.cache.handle, 0, pop["k"], pop["v"], pop["cu"], pop["ctx0"],
-                           pop["slots"], c.block_tables, len(pop["hist"]), T, stream)
+            kv4.kv4_append(c.cache.handle, 0, pk, pv, cu, ctx0, slots, c.block_tables, len(first), T, stream)
 
         bulk()
         torch.cuda.synchronize()
-        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.populate_reps)]
-        for e0, e1 in pe:
-            e0.record(stream)
-            bulk()
-            e1.record(stream)
+        pe = []
+        for _ in range(args.populate_reps):
+            e0 = tm.ev(); bulk(); e1 = tm.ev()
+            pe.append((e0, e1))
         torch.cuda.synchronize()
         pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
-        pbytes = populate_bytes_kv4(pop["hist"], cfg)
-        populate = {"sequences": len(pop["hist"]), "tokens": T, "us": round(pms * 1e3, 2),
+        pbytes = populate_bytes_kv4(hist, cfg)
+        populate = {"sequences": len(hist), "tokens": T, "us": round(pms * 1e3, 2),
                     "alg_bytes": pbytes, "gbs": round(pbytes / (pms * 1e-3) / 1e9, 2),
                     "frac_hbm_peak": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "tokens_per_s": round(T / (pms * 1e-3), 1)}
@@ -421,38 +580,29 @@ def main():
             gen.manual_seed(cfg.seed)
             qp = torch.randn((T, cfg.q_heads, cfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
             po = torch.empty((T, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+            sm = 1.0 / math.sqrt(cfg.head_dim)
 
             def pre():
-                kv4.kv4_prefill_attn(c.cache.handle, qp, pop["k"], pop["v"], pop["cu"],
-                                     len(pop["hist"]), int(pop["hist"].max()), sm, po, kv4.KV4_OUT_F32,
-                                     stream)
+                kv4.kv4_prefill_attn(c.cache.handle, qp, pk, pv, cu, len(hist), int(hist.max()), sm, po,
+                                     kv4.KV4_OUT_F32, stream)
 
             pre()
             torch.cuda.synchronize()
-            fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.prefill_reps)]
-            for e0, e1 in fe:
-                e0.record(stream)
-                pre()
-                e1.record(stream)
+            fe = []
+            for _ in range(args.prefill_reps):
+                e0 = tm.ev(); pre(); e1 = tm.ev()
+                fe.append((e0, e1))
             torch.cuda.synchronize()
             fms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe]))
-            fl = prefill_flops(pop["hist"], cfg)
-            prefill = {"sequences": len(pop["hist"]), "tokens": T, "us": round(fms * 1e3, 2),
-                       "alg_flops": fl, "tflops": round(fl / (fms * 1e-3) / 1e12, 2),
+            fl = prefill_flops(hist, cfg)
+            prefill = {"sequences": len(hist), "tokens": T, "max_prompt": int(hist.max()),
+                       "us": round(fms * 1e3, 2), "alg_flops": fl, "tflops": round(fl / (fms * 1e-3) / 1e12, 2),
                        "frac_mfma_bf16_peak": round(fl / (fms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                        "tokens_per_s": round(T / (fms * 1e-3), 1)}
             log(f"prefill: {T} tokens in {fms * 1e3:.1f} us ({prefill['tflops']} TFLOP/s)")
             del qp, po
-        del pop
+        del pk, pv
 
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies")
 
     r = results["kv4"]
     db = decode_bytes_kv4(n, cfg)
@@ -526,7 +676,6 @@ def main():
         }
         line["speedup_vs_bf16_step"] = round(bstep / step_ms, 3)
         line["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
-
     if populate is not None:
         line["populate"] = populate
     if prefill is not None:
@@ -553,10 +702,169 @@ def main():
             "layer_tokens_per_s": round(B / ((r8["append_ms"] + r8["decode_ms"]) * 1e-3), 1),
         }
         line["speedup_vs_kv8_decode"] = round(r8["decode_ms"] / r["decode_ms"], 3)
+    if "g128_rot" in results:
+        rg = results["g128_rot"]
+        cg = W.scaled(cfg, group=128)
+        pg, dg = partial_bytes_kv4(n, cg), decode_bytes_kv4(n, cg)
+        line["g128_rot"] = {
+            "workload": "the same batch, head-wise INT4 groups (G = 128, 136 B per token and kv head) "
+                        "with keys in the rotated basis (KV4_FLAG_ROTATE_K): the pages' default",
+            "decode_attn_us": round(rg["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(rg["partials_ms"] * 1e3, 2),
+            "partials_alg_bytes": pg,
+            "partials_frac_hbm_peak": round(pg / (rg["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_attn_frac_hbm_peak": round(dg / (rg["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "append_us": round(rg["append_ms"] * 1e3, 2),
+        }
+        if "bf16" in results:
+            line["g128_rot"]["speedup_vs_bf16_decode"] = round(results["bf16"]["decode_ms"] / rg["decode_ms"], 3)
+    del caches, knew, vnew, q
+    torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
+    if not args.only_kv4 and not args.no_sub and cfg.name == "q8b256":
+        sub = {}
+        sub["q4b"] = sub_record("q4b", W.CONFIGS["q4b"], dict(common), H, W, kv4, torch, dev, tm, args,
+                                flush_bytes=1 << 30)
+        sub["long"] = sub_record("long", W.CONFIGS["long"], dict(common), H, W, kv4, torch, dev, tm, args)
+        line["sub_records"] = sub
+        f36 = measure_full36(args, torch, kv4, H, W, cpu_seconds=5.0)
+        sub["full36"] = {k: f36[k] for k in ("metric", "value", "unit", "ms_per_step", "config",
+                                             "step_ms_median_p10_p90", "step_gbs", "step_frac_hbm_peak",
+                                             "bf16_comparator", "speedup_vs_bf16_step", "cpu_baseline")
+                         if k in f36}
+        rc = read_ceiling(torch, dev, stream, pb)
+        rc["decode_partials_frac_of_block_ceiling"] = round(achieved / rc["block2560_gbs"], 4)
+        rc["decode_attn_frac_of_block_ceiling"] = round(decode_gbs / rc["block2560_gbs"], 4)
+        line["read_ceiling"] = rc
+        log(f"read ceiling: stream {rc['stream_gbs']} GB/s, random 2.5 KB blocks {rc['block2560_gbs']} GB/s")
+
+    if not args.no_cpu_baseline and not args.only_kv4:
         line["cpu_baseline"] = cpu_baseline(cfg, ctx, n, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def run_full36(args, torch, kv4, H, W):
+    line = measure_full36(args, torch, kv4, H, W, cpu_seconds=args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def measure_full36(args, torch, kv4, H, W, cpu_seconds):
+    """The full decode step of a Qwen3-8B-shaped model, attention only: 36
+    layers x (32 q / 8 kv heads), batch 128, contexts uniform 1k..12k, 64
+    consecutive steps; every step appends one token per sequence and layer
+    (crossing the recent window's demotion boundary) and decodes every layer.
+    KV4 and the BF16 comparator are built one at a time (about 40 GB and
+    126 GB resident).  tokens/s = batch / mean step time over the 64 steps
+    (all timed: each step changes the caches, so none is repeated)."""
+    cfg = W.CONFIGS["full36"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    tm = Timer(torch, stream)
+    ctx = W.contexts(cfg)
+    B, steps, Lyr, Hkv, d = cfg.batch, cfg.steps, cfg.layers, cfg.kv_heads, cfg.head_dim
+    total = ctx + steps
+    out_ch = W.outlier_channels(cfg)
+    sm = 1.0 / math.sqrt(d)
+    cu1 = torch.arange(B + 1, dtype=torch.int32, device=dev)
+    qs = torch.stack([torch.stack([W.queries_device(cfg, layer, st, dev) for st in range(steps)])
+                      for layer in range(Lyr)])                  # [L, steps, B, Hq, d] bf16
+    res = {}
+    for name, kind in (("kv4", kv4.KV4_KIND_MIXED), ("bf16", kv4.KV4_KIND_BF16)):
+        t0 = time.time()
+        S, R = (cfg.sink, cfg.recent) if kind == kv4.KV4_KIND_MIXED else (0, 0)
+        built = H.make_cache(cfg.q_heads, Hkv, cfg.group, S, R, total, layers=Lyr, kind=kind,
+                             seed=cfg.seed, device="cuda:0")
+        c = built.cache
+        step_k = torch.empty((Lyr, steps, B, Hkv, d), dtype=torch.bfloat16, device=dev)
+        step_v = torch.empty_like(step_k)
+        for layer in range(Lyr):
+            for lo in range(0, B, 16):
+                seqs = list(range(lo, min(B, lo + 16)))
+                ks, vs = [], []
+                for b in seqs:
+                    k, v = W.kv_sources_device(cfg, layer, b, int(total[b]), dev, out_ch)
+                    ks.append(k[:int(ctx[b])])
+                    vs.append(v[:int(ctx[b])])
+                    step_k[layer, :, b] = k[int(ctx[b]):]
+                    step_v[layer, :, b] = v[int(ctx[b]):]
+                cnt = np.array([int(ctx[b]) for b in seqs])
+                cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)).to(dev)
+                kv4.kv4_append(c.handle, layer, torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), cu,
+                               torch.zeros(len(seqs), dtype=torch.int32, device=dev),
+                               built.slots[lo:lo + len(seqs)].contiguous(), built.block_tables,
+                               len(seqs), int(cnt.sum()), stream)
+            torch.cuda.synchronize()
+        log(f"full36 {name}: {Lyr} layers built in {time.time() - t0:.1f}s")
+        befores = [torch.from_numpy((ctx + st).astype(np.int32)).to(dev) for st in range(steps)]
+        out = torch.empty((B, cfg.q_heads, d), dtype=torch.float32, device=dev)
+        ws = c.workspace(B, int(total.max()))
+        # untimed clock warm-up: decodes of layer 0 at the first step's lengths
+        # (decoding does not change the cache)
+        n0 = befores[0] + 1
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                kv4.kv4_decode_attn(c.handle, 0, qs[0, 0], n0, built.slots, built.block_tables, B,
+                                    int(ctx.max()) + 1, sm, out, kv4.KV4_OUT_F32, ws, stream)
+            torch.cuda.synchronize()
+        evs = []
+        for st in range(steps):
+            n_d = befores[st] + 1
+            max_ctx = int(ctx.max()) + st + 1
+            e0 = tm.ev()
+            for layer in range(Lyr):
+                kv4.kv4_append(c.handle, layer, step_k[layer, st], step_v[layer, st], cu1, befores[st],
+                               built.slots, built.block_tables, B, B, stream)
+                kv4.kv4_decode_attn(c.handle, layer, qs[layer, st], n_d, built.slots, built.block_tables,
+                                    B, max_ctx, sm, out, kv4.KV4_OUT_F32, ws, stream)
+            evs.append((e0, tm.ev()))
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        t = np.array([a.elapsed_time(b) for a, b in evs])
+        res[name] = dict(step_ms=float(t.mean()), step_ms_median=float(np.median(t)),
+                         step_ms_p10=float(np.percentile(t, 10)), step_ms_p90=float(np.percentile(t, 90)))
+        log(f"full36 {name}: step {t.mean():.3f} ms (median {np.median(t):.3f})")
+        del built, c, step_k, step_v, ws, out
+        torch.cuda.empty_cache()
+    r, rb = res["kv4"], res["bf16"]
+    # algorithmic bytes of a whole step: 36 layers of (append + decode) at the
+    # mean length over the 64 steps
+    nbar = ctx + (steps + 1) / 2.0
+    per_layer = decode_bytes_kv4(np.round(nbar).astype(np.int64), cfg) + append_bytes_kv4(nbar, cfg)
+    step_bytes = Lyr * per_layer
+    line = {
+        "metric": "36-layer attention-only decode tokens/s (KV4 vs BF16-KV), Qwen3-8B shape",
+        "value": round(B / (r["step_ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": 0,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V drawn on the device, 4 outlier K channels x10)",
+        "config": {"workload": "Qwen3-8B-shaped decode step, attention only: 36 layers x (32q/8kv heads, "
+                               "d=128), batch 128, contexts uniform 1k..12k, page 16, group 32, S=4, R=128, "
+                               "64 consecutive steps (append + decode per layer), each step timed",
+                   "global_batch": B, "layers": Lyr, "seq_len_mean_first_step": float(ctx.mean() + 1),
+                   "parallelism": "single GPU"},
+        "step_ms_median_p10_p90": [round(r["step_ms_median"], 4), round(r["step_ms_p10"], 4),
+                                   round(r["step_ms_p90"], 4)],
+        "step_alg_bytes": int(step_bytes),
+        "step_gbs": round(step_bytes / (r["step_ms"] * 1e-3) / 1e9, 1),
+        "step_frac_hbm_peak": round(step_bytes / (r["step_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bf16_comparator": {"step_ms": round(rb["step_ms"], 4),
+                            "tokens_per_s": round(B / (rb["step_ms"] * 1e-3), 1)},
+        "speedup_vs_bf16_step": round(rb["step_ms"] / r["step_ms"], 3),
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(W.scaled(cfg, layers=1, steps=1), ctx, ctx + 1, cpu_seconds)
+        # one layer-step of the sample, scaled to the whole batch, x 36 layers
+        per_seq_layer = cb["seconds"] / cb["sequences"]
+        cpu_step = per_seq_layer * B * Lyr
+        line["cpu_baseline"] = {"value": round(B / cpu_step, 3), "unit": "tokens/s", "cores": cb["cores"],
+                                "kind": "oracle",
+                                "sample": cb["sample"] + f"; one layer-step of {cb['sequences']} sequences "
+                                          f"scaled to {B} sequences x {Lyr} layers (x36 extrapolation)"}
+    return line
 
 
 def _kernel_hash():
@@ -603,7 +911,7 @@ def cpu_baseline(cfg, ctx, n, seconds):
             "kind": "oracle",
             "sample": f"first {k} of {cfg.batch} sequences ({int(sub.sum())} context tokens), "
                       f"one decode step (quantize new token + fp64 attention), {elapsed:.1f} s",
-            "seconds": round(elapsed, 2)}
+            "seconds": round(elapsed, 2), "sequences": k}
 
 
 if __name__ == "__main__":

@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "kv4.hip")
 LIB = os.path.join(HERE, "libkv4.so")
+# read-bandwidth ceilings (measurement aid, include/kv4_roof.h)
+ROOF_SRC = os.path.join(HERE, "csrc", "kv4_roof.hip")
+ROOF_LIB = os.path.join(HERE, "libkv4_roof.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIPFLAGS = [
@@ -33,18 +36,25 @@ HIPFLAGS = [
 
 
 def sources():
+    """Sources of the decode library (libkv4.so)."""
     csrc = os.path.join(HERE, "csrc")
     return [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
-            if f.endswith((".hip", ".hpp", ".h"))] + [os.path.join(ROOT, "include", "kv4.h")]
+            if f.endswith((".hip", ".hpp", ".h")) and f != "kv4_roof.hip"] + \
+        [os.path.join(ROOT, "include", "kv4.h")]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *HIPFLAGS, SRC, "-o", tmp]
+def _compile(src, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *HIPFLAGS, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SRC, LIB, verbose)
+    _compile(ROOF_SRC, ROOF_LIB, verbose)
     return LIB
 
 

@@ -74,32 +74,42 @@ def test_populate_and_append_bytes():
     assert bench.append_bytes_kv4(n, cfg) == len(n) * Hkv * (src + 160 + 260)
 
 
-def _counter_dir(tmp_path, name, counter, rows):
+def _counter_dir(tmp_path, name, rows):
     d = tmp_path / name
     d.mkdir()
     with open(d / "run_counter_collection.csv", "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for i, (kernel, value) in enumerate(rows):
-            w.writerow(dict(Dispatch_Id=i + 1, Kernel_Name=kernel, Counter_Name=counter,
-                            Counter_Value=value))
+        for disp, kernel, counter, value in rows:
+            w.writerow(dict(Dispatch_Id=disp, Kernel_Name=kernel, Counter_Name=counter, Counter_Value=value))
     return str(d)
 
 
-def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
+def test_counter_summary_bytes_from_request_sizes(tmp_path):
+    """Traffic from the L2's request counts by size, averaged over the dominant
+    kernel's dispatches (other kernels ignored), and the factor FETCH_SIZE /
+    WRITE_SIZE would need to match it."""
     dom = "void kv4::decode_kv4_mfma_kernel<32, false>(kv4::DecodeArgs)"
-    cp = bench.COPY_KERNEL + "(...)"
-    kib = bench.COPY_BYTES / 1024
-    # FETCH: the copies read twice their size as counted (scale 1/2); WRITE: as counted
-    fetch = _counter_dir(tmp_path, "f", "FETCH_SIZE",
-                         [(cp, 4.0), (dom, 1000.0), (dom, 1002.0), (cp, 2 * kib), (cp, 2 * kib), (cp, 3.0)])
-    write = _counter_dir(tmp_path, "w", "WRITE_SIZE",
-                         [(cp, 4.0), (dom, 10.0), (dom, 14.0), (cp, kib), (cp, kib)])
-    out = tmp_path / "t.json"
-    args = argparse.Namespace(summarize_pmc=[fetch, write], summary_cmd="cmd", summary_out=str(out))
-    bench.summarize_pmc(args)
+    other = "void kv4::merge_parts_kernel(kv4::DecodeArgs)"
+    rd = _counter_dir(tmp_path, "r", [
+        (1, dom, "TCC_EA0_RDREQ_32B", 10.0), (1, dom, "TCC_EA0_RDREQ_64B", 20.0),
+        (1, dom, "TCC_EA0_RDREQ_128B", 1000.0), (1, other, "TCC_EA0_RDREQ_128B", 5e9),
+        (2, dom, "TCC_EA0_RDREQ_32B", 12.0), (2, dom, "TCC_EA0_RDREQ_64B", 22.0),
+        (2, dom, "TCC_EA0_RDREQ_128B", 1002.0)])
+    fs = _counter_dir(tmp_path, "f", [(3, dom, "FETCH_SIZE", 64.0), (4, dom, "FETCH_SIZE", 64.0)])
+    wr = _counter_dir(tmp_path, "w", [
+        (5, dom, "TCC_EA0_WRREQ", 100.0), (5, dom, "TCC_EA0_WRREQ_64B", 60.0), (5, dom, "WRITE_SIZE", 4.0),
+        (5, dom, "TCC_HIT", 30.0), (5, dom, "TCC_MISS", 90.0)])
+    out = tmp_path / "c.json"
+    args = argparse.Namespace(summarize_counters=[rd, fs, wr], summary_cmd="cmd", summary_out=str(out))
+    bench.summarize_counters(args)
     res = json.load(open(out))
-    assert res["fetch"]["launches"] == 2 and res["fetch"]["copy_launches"] == 2
-    assert abs(res["fetch"]["scale"] - 0.5) < 1e-12 and abs(res["write"]["scale"] - 1.0) < 1e-12
-    assert res["bytes_per_launch"] == round(1001.0 * 1024 * 0.5 + 12.0 * 1024)
+    read = 32 * 11.0 + 64 * 21.0 + 128 * 1001.0
+    write = 64 * 60.0 + 32 * 40.0
+    assert res["read_bytes_per_launch"] == read and res["write_bytes_per_launch"] == write
+    assert res["bytes_per_launch"] == round(read + write)
+    assert abs(res["fetch_size_factor"] - read / (64.0 * 1024)) < 1e-12
+    assert abs(res["write_size_factor"] - write / (4.0 * 1024)) < 1e-12
+    assert abs(res["l2_hit_rate"] - 0.25) < 1e-12
+    assert res["launches"]["TCC_EA0_RDREQ_128B"] == 2
     assert res["kernel_source_hash"] == bench._kernel_hash()
