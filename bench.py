@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--only-kv4", action="store_true",
                     help="time the KV4 decode only (no comparators, sub-records, populate, prefill or "
                          "CPU baseline): the command the counter profiles run")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill attention over the first 32 histories of the workload "
+                         "as prompts (the command the prefill profiles run)")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the sub-records (G = 128 rotated, Qwen3-4B shape, long context) and "
                          "the read ceilings")
@@ -501,6 +504,8 @@ def main():
 
     if args.config == "full36":
         return run_full36(args, torch, kv4, H, W)
+    if args.prefill_only:
+        return run_prefill_only(args, torch, kv4, H, W)
     cfg = W.CONFIGS[args.config]
     if args.group:
         cfg = W.scaled(cfg, group=args.group)
@@ -576,31 +581,8 @@ def main():
         log(f"populate: {T} tokens in {pms * 1e3:.1f} us ({populate['gbs']} GB/s)")
         if args.prefill_reps > 0:
             # the same histories as prompts: causal BF16 attention (synthetic queries)
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(cfg.seed)
-            qp = torch.randn((T, cfg.q_heads, cfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
-            po = torch.empty((T, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
-            sm = 1.0 / math.sqrt(cfg.head_dim)
-
-            def pre():
-                kv4.kv4_prefill_attn(c.cache.handle, qp, pk, pv, cu, len(hist), int(hist.max()), sm, po,
-                                     kv4.KV4_OUT_F32, stream)
-
-            pre()
-            torch.cuda.synchronize()
-            fe = []
-            for _ in range(args.prefill_reps):
-                e0 = tm.ev(); pre(); e1 = tm.ev()
-                fe.append((e0, e1))
-            torch.cuda.synchronize()
-            fms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe]))
-            fl = prefill_flops(hist, cfg)
-            prefill = {"sequences": len(hist), "tokens": T, "max_prompt": int(hist.max()),
-                       "us": round(fms * 1e3, 2), "alg_flops": fl, "tflops": round(fl / (fms * 1e-3) / 1e12, 2),
-                       "frac_mfma_bf16_peak": round(fl / (fms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                       "tokens_per_s": round(T / (fms * 1e-3), 1)}
-            log(f"prefill: {T} tokens in {fms * 1e3:.1f} us ({prefill['tflops']} TFLOP/s)")
-            del qp, po
+            prefill = time_prefill(c, hist, pk, pv, cu, cfg, kv4, torch, tm, args.prefill_reps)
+            log(f"prefill: {T} tokens in {prefill['us']} us ({prefill['tflops']} TFLOP/s)")
         del pk, pv
 
 
@@ -741,6 +723,58 @@ def main():
     if not args.no_cpu_baseline and not args.only_kv4:
         line["cpu_baseline"] = cpu_baseline(cfg, ctx, n, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def time_prefill(c, hist, pk, pv, cu, cfg, kv4, torch, tm, reps):
+    """kv4_prefill_attn over the histories `hist` packed as prompts (synthetic
+    seeded queries), the mean of `reps` event-timed calls after one untimed."""
+    dev = pk.device
+    T = int(hist.sum())
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    qp = torch.randn((T, cfg.q_heads, cfg.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+    po = torch.empty((T, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    sm = 1.0 / math.sqrt(cfg.head_dim)
+
+    def pre():
+        kv4.kv4_prefill_attn(c.cache.handle, qp, pk, pv, cu, len(hist), int(hist.max()), sm, po,
+                             kv4.KV4_OUT_F32, tm.stream)
+
+    pre()
+    torch.cuda.synchronize()
+    fe = []
+    for _ in range(reps):
+        e0 = tm.ev(); pre(); e1 = tm.ev()
+        fe.append((e0, e1))
+    torch.cuda.synchronize()
+    fms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fe]))
+    fl = prefill_flops(hist, cfg)
+    return {"sequences": len(hist), "tokens": T, "max_prompt": int(hist.max()),
+            "us": round(fms * 1e3, 2), "alg_flops": fl, "tflops": round(fl / (fms * 1e-3) / 1e12, 2),
+            "frac_mfma_bf16_peak": round(fl / (fms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(T / (fms * 1e-3), 1)}
+
+
+def run_prefill_only(args, torch, kv4, H, W):
+    """The prefill timing alone: the first 32 histories of the workload as
+    prompts (the same inputs as the default line's prefill record)."""
+    cfg = W.CONFIGS[args.config]
+    ctx = W.contexts(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tm = Timer(torch, torch.cuda.current_stream())
+    seqs = list(range(min(32, cfg.batch)))
+    ks, vs = W.all_kv_sources(cfg, 0, ctx + 1, seqs=seqs, threads=16)
+    hist = np.array([int(ctx[s]) for s in seqs])
+    pk = H.to_dev_bf16(np.concatenate([ks[i][:hist[i]] for i in range(len(seqs))], 0), str(dev))
+    pv = H.to_dev_bf16(np.concatenate([vs[i][:hist[i]] for i in range(len(seqs))], 0), str(dev))
+    pcu = np.zeros(len(seqs) + 1, np.int32)
+    pcu[1:] = np.cumsum(hist)
+    cu = torch.from_numpy(pcu).to(dev)
+    c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, [16], device=str(dev))
+    rec = time_prefill(c, hist, pk, pv, cu, cfg, kv4, torch, tm, max(1, args.prefill_reps))
+    log(f"prefill: {rec['tokens']} tokens in {rec['us']} us ({rec['tflops']} TFLOP/s)")
+    print(json.dumps({"prefill": rec}), flush=True)
 
 
 def run_full36(args, torch, kv4, H, W):

@@ -277,7 +277,7 @@ int kv4_decode_attn(kv4_cache* cache, int layer, const void* q_bf16, const int32
  * 3 * ceil((S + R) / 32) tiles, the measured cost of its 32-entry
  * INT8 tiles) and the 32-token tiles of its INT4 region [S, max(S, n - R))
  * (tile t covers positions [32t, 32t + 32) clipped to the region); T4 tiles
- * and P protected parts in all, W' = min(W, ceil((T4 + U8 P) / 8)) waves in
+ * and P protected parts in all, W' = min(W, ceil((T4 + U8 P) / 20)) waves in
  * use.  The tile sequence is cut into shares:
  *   - a pool of the last Tp = floor(3 T4 / 16) tiles in Cd chunks, Cd the
  *     largest power of two <= the cache's pool chunk count with 2 Cd <= Tp
@@ -340,7 +340,8 @@ int kv4_decode_merge(kv4_cache* cache, const int32_t* seq_lens, int batch, int m
  * q head j reads kv head j / (Hq / Hkv).  Offsets are clamped to [0, total].
  * Errors: KV4_ERR_INVALID_ARG (null pointers, batch < 1, total < 0,
  * max_seqlen < 1, non-finite sm_scale, bad out_dtype), KV4_ERR_CAPACITY
- * (max_seqlen above 2^24), KV4_ERR_HIP.  total = 0 launches nothing.
+ * (max_seqlen above 2^23 or batch above 65,536), KV4_ERR_HIP.  total = 0
+ * launches nothing.
  */
 int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_bf16,
                      const void* v_bf16, const int32_t* cu_seqlens, int batch, int total,

@@ -35,7 +35,10 @@ namespace kv4 {
 
 constexpr int kPartPad = 4;      // floats after o[d] in a partial: z and padding
 constexpr int kTile = 32;        // tokens per INT4 / BF16 unit
-constexpr int kMinUnits = 8;     // least weight a wave is given (fewer waves otherwise)
+// Least weight (in INT4 tiles) a wave is given: fewer waves otherwise.  With
+// less work per wave the launch is dominated by the slowest waves (measured
+// at the Qwen3-4B batch-64 shape: 67 us at 4,096 waves, 51 us at 2,560).
+constexpr int kMinUnits = 20;
 constexpr int kMaxWaves = 1 << 16;
 constexpr int kPoolCounters = 8;         // atomic counters of the pool
 constexpr int kPoolStride = 64;          // uint32 between counters (256 bytes)

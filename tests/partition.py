@@ -2,7 +2,7 @@
 out on the host in plain Python integers, for the layout tests.  It mirrors the
 closed forms that kv4_decode_partials documents; nothing here runs on the GPU."""
 
-MIN_UNITS = 8
+MIN_UNITS = 20
 POOL_MIN = 8
 POOL_SIXTEENTHS = 3
 

@@ -235,7 +235,9 @@ def test_prefill_validation_no_launch():
     assert call(max_len=0) == kv4.KV4_ERR_INVALID_ARG
     assert call(scale=float("inf")) == kv4.KV4_ERR_INVALID_ARG
     assert call(dt=5) == kv4.KV4_ERR_INVALID_ARG
-    assert call(max_len=(1 << 24) + 1) == kv4.KV4_ERR_CAPACITY
+    assert call(max_len=(1 << 23) + 1) == kv4.KV4_ERR_CAPACITY     # grid z: 65,536 blocks of 128
+    assert call(max_len=1 << 23, total=0) == kv4.KV4_OK
+    assert call(batch=65537) == kv4.KV4_ERR_CAPACITY               # grid y: 65,536 sequences
     assert call(total=0) == kv4.KV4_OK                         # nothing to launch
     kv4.kv4_cache_free(h)
 

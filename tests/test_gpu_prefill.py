@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 ATOL, RTOL = 1e-3, 2e-3
 
 
-def _case(Hq, Hkv, lens, seed, out_dtype=kv4.KV4_OUT_F32):
+def _case(Hq, Hkv, lens, seed, out_dtype=kv4.KV4_OUT_F32, sm_scale=1 / math.sqrt(128)):
     rng = np.random.default_rng(seed)
     T = int(sum(lens))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -32,10 +32,10 @@ def _case(Hq, Hkv, lens, seed, out_dtype=kv4.KV4_OUT_F32):
     out = torch.empty((T, Hq, 128), dtype=torch.float32 if out_dtype == kv4.KV4_OUT_F32 else torch.bfloat16,
                       device=dev)
     kv4.kv4_prefill_attn(built.cache.handle, H.to_dev_bf16(q), H.to_dev_bf16(k), H.to_dev_bf16(v),
-                         torch.from_numpy(cu).to(dev), len(lens), int(max(lens)), 1 / math.sqrt(128),
+                         torch.from_numpy(cu).to(dev), len(lens), int(max(lens)), sm_scale,
                          out, out_dtype)
     torch.cuda.synchronize()
-    want = oracle.prefill_attn(q, k, v, cu, 1 / math.sqrt(128))
+    want = oracle.prefill_attn(q, k, v, cu, sm_scale)
     return out.float().cpu().numpy(), want
 
 
@@ -46,6 +46,16 @@ def test_prefill_matches_oracle(Hq, Hkv):
     out, want = _case(Hq, Hkv, lens, seed=200 + Hq + Hkv)
     err = H.check_output(out, want, ATOL, RTOL)
     H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
+
+
+def test_prefill_scales():
+    """A negative and a large softmax scale (the kernel takes the scale's sign
+    into the query operand and compares raw scores)."""
+    for sc in (-1 / math.sqrt(128), 4 / math.sqrt(128), 1e-3):
+        H.log(f"case prefill sm_scale {sc:.4g}")
+        out, want = _case(8, 2, [1, 33, 200, 700], seed=230, sm_scale=sc)
+        err = H.check_output(out, want, ATOL, RTOL)
+        H.log(f"  max abs {err[0]:.2e} row rel {err[1]:.2e}")
 
 
 def test_prefill_long_prompt_and_bf16_output():
