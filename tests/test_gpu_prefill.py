@@ -49,9 +49,10 @@ def test_prefill_matches_oracle(Hq, Hkv):
 
 
 def test_prefill_scales():
-    """A negative and a large softmax scale (the kernel takes the scale's sign
-    into the query operand and compares raw scores)."""
-    for sc in (-1 / math.sqrt(128), 4 / math.sqrt(128), 1e-3):
+    """A negative, a large, a small and a zero softmax scale (the kernel takes
+    the scale's sign into the query operand and compares raw scores; a zero
+    scale is the uniform average of every prefix)."""
+    for sc in (-1 / math.sqrt(128), 4 / math.sqrt(128), 1e-3, 0.0):
         H.log(f"case prefill sm_scale {sc:.4g}")
         out, want = _case(8, 2, [1, 33, 200, 700], seed=230, sm_scale=sc)
         err = H.check_output(out, want, ATOL, RTOL)
