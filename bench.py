@@ -4,7 +4,7 @@
 A step is one pass of the hot path over one batch: kv4_append of the batch's
 new token (INT4 pages + INT8 ring) followed by kv4_decode_attn (GQA attention
 over the ragged paged contexts, cut by a balanced partition over the GPU's
-waves, + the log-sum-exp merge).  The
+waves, + the log-sum-exp merge), each bracketed by HIP events.  The
 workload is the Qwen3-8B-shaped layer (32 q / 8 kv heads, d = 128) at batch
 256 with long-tail lognormal contexts (median 4k, max 16k), 16-token pages,
 INT4 group 32, S = 4, R = 128.  Inputs are seeded synthetic data, resident in
@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--summary-cmd", default="", help="command that produced the profile")
     ap.add_argument("--summary-bench", metavar="JSON",
                     help="bench line printed by the profiled run (live event timings)")
+    ap.add_argument("--summary-kernel", default="decode_kv4_mfma_kernel",
+                    help="kernel-name substring whose counters are summarised")
     return ap.parse_args()
 
 
@@ -198,11 +200,20 @@ def summarize_trace(args):
         k = k if len(k) <= 44 else k[:41] + "..."
         lines.append(f"{k:44s} {len(v):6d} {a.mean():10.2f} {np.median(a):10.2f} {a.min():10.2f} "
                      f"{a.max():10.2f} {100 * a.sum() * 1e3 / total:8.2f}")
-    if args.summary_bench:
+    if args.summary_bench and "prefill" in json.loads(open(args.summary_bench).read().strip().splitlines()[-1]) \
+            and "decode_attn_us" not in json.loads(open(args.summary_bench).read().strip().splitlines()[-1]):
+        p = json.loads(open(args.summary_bench).read().strip().splitlines()[-1])["prefill"]
+        lines += ["", "live HIP-event timing of the same run (mean over the timed calls):",
+                  f"  kv4_prefill_attn (prefill_attn_kernel): {p['us']} us for {p['tokens']} tokens in "
+                  f"{p['sequences']} prompts (longest {p['max_prompt']}): {p['tflops']} TFLOP/s "
+                  f"= {p['frac_mfma_bf16_peak']} of the bf16 matrix-core peak",
+                  "kernel counts include the warm-up call"]
+    elif args.summary_bench:
         b = json.loads(open(args.summary_bench).read().strip().splitlines()[-1])
         lines += ["", "live HIP-event timings of the same run (mean over the timed steps):",
-                  f"  kv4_decode_partials ({DOMINANT}): {b['decode_partials_us']} us",
-                  f"  kv4_decode_merge (merge_parts_kernel, incl. launch gap): {b['decode_merge_us']} us",
+                  f"  kv4_decode_attn (the whole call, partials + merge back to back): {b['decode_attn_us']} us",
+                  f"  kv4_decode_partials ({DOMINANT}) alone: {b['decode_partials_us']} us",
+                  f"  kv4_decode_merge (merge_parts_kernel) alone: {b['decode_merge_us']} us",
                   f"  kv4_append (append_kv4_kernel<32>): {b['append_us']} us"]
         if "bf16_comparator" in b:
             lines.append(f"  BF16 comparator partials (decode_bf16_mfma_kernel): "
@@ -231,9 +242,10 @@ def summarize_counters(args):
     and the factor by which the FETCH_SIZE / WRITE_SIZE metrics of this
     rocprofv3 build differ from those request-size sums."""
     vals = {}
+    kernel = args.summary_kernel
     for d in args.summarize_counters:
         for r in _csv_rows(d, "counter_collection.csv"):
-            if DOMINANT not in r["Kernel_Name"]:
+            if kernel not in r["Kernel_Name"]:
                 continue
             key = (r["Counter_Name"], int(r["Dispatch_Id"]))
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
@@ -242,7 +254,7 @@ def summarize_counters(args):
         per.setdefault(name, []).append(v)
     mean = {k: float(np.mean(v)) for k, v in per.items()}
     launches = {k: len(v) for k, v in per.items()}
-    out = dict(kernel=DOMINANT, kernel_source_hash=_kernel_hash(), commands=args.summary_cmd,
+    out = dict(kernel=kernel, kernel_source_hash=_kernel_hash(kernel), commands=args.summary_cmd,
                counters_per_launch=mean, launches=launches)
     if all(k in mean for k in ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B")):
         rd = 32 * mean["TCC_EA0_RDREQ_32B"] + 64 * mean["TCC_EA0_RDREQ_64B"] + 128 * mean["TCC_EA0_RDREQ_128B"]
@@ -314,12 +326,14 @@ def kv4_sync(dev):
 
 def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=None,
               clock_warm_s=0.0):
-    """`warmup` untimed steps, then `steps` timed steps of (append, partials,
-    merge) on cache c; every step re-appends the same token at the same
-    position (idempotent), so each does the full work on identical state.
-    `flush` (untimed, between steps) evicts the caches for workloads that fit
-    in them.  Returns per-step milliseconds of the three phases and the
-    output."""
+    """`warmup` untimed steps, then `steps` timed steps of (append,
+    kv4_decode_attn) on cache c, each bracketed by events (the append and the
+    attention call apart); then `steps` more with the two phases of the
+    attention (kv4_decode_partials, kv4_decode_merge) bracketed apart, for the
+    split.  Every step re-appends the same token at the same position
+    (idempotent), so each does the full work on identical state.  `flush`
+    (untimed, between steps) evicts the caches for workloads that fit in
+    them.  Returns per-step milliseconds."""
     dev = knew.device
     B = len(n)
     ctx = n - 1
@@ -329,11 +343,16 @@ def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=Non
     max_ctx = int(n.max())
     sm = 1.0 / math.sqrt(cfg.head_dim)
     out = torch.empty((B, cfg.q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    whole = torch.empty_like(out)
     ws = c.cache.workspace(B, max_ctx)
     st = tm.stream
 
     def append():
         kv4.kv4_append(c.cache.handle, 0, knew, vnew, cu, ctx_d, c.slots, c.block_tables, B, B, st)
+
+    def attn():
+        kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm, whole,
+                            kv4.KV4_OUT_F32, ws, st)
 
     def partials():
         kv4.kv4_decode_partials(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm, ws, st)
@@ -346,32 +365,35 @@ def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=Non
         t_end = time.perf_counter() + clock_warm_s
         while time.perf_counter() < t_end:
             for _ in range(8):
-                append(); partials(); merge()
+                append(); attn()
             torch.cuda.synchronize()
     for _ in range(warmup):
         if flush:
             flush()
-        append(); partials(); merge()
+        append(); attn()
     torch.cuda.synchronize()
-    t = np.zeros((steps, 3))
-    evs = []
-    for i in range(steps):
-        if flush:
-            flush()
-        e0 = tm.ev(); append(); e1 = tm.ev(); partials(); e2 = tm.ev(); merge(); e3 = tm.ev()
-        evs.append((e0, e1, e2, e3))
-    torch.cuda.synchronize()
-    for i, (e0, e1, e2, e3) in enumerate(evs):
-        t[i] = (e0.elapsed_time(e1), e1.elapsed_time(e2), e2.elapsed_time(e3))
-    whole = torch.empty_like(out)
-    kv4.kv4_decode_attn(c.cache.handle, 0, q, n_d, c.slots, c.block_tables, B, max_ctx, sm, whole,
-                        kv4.KV4_OUT_F32, ws, st)
+
+    def timed(phases):
+        evs = []
+        for i in range(steps):
+            if flush:
+                flush()
+            e = [tm.ev()]
+            for f in phases:
+                f()
+                e.append(tm.ev())
+            evs.append(e)
+        torch.cuda.synchronize()
+        return np.array([[e[k].elapsed_time(e[k + 1]) for k in range(len(e) - 1)] for e in evs])
+
+    t = timed((append, attn))                 # the step as a caller runs it
+    ph = timed((append, partials, merge))     # the attention's two phases apart
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
     assert torch.equal(whole, out), "kv4_decode_attn differs from partials + merge"
     waves, chunks = kv4.kv4_decode_partition(c.cache.handle)
-    ta, tp, tmg = t[:, 0], t[:, 1], t[:, 2]
-    td = tp + tmg
+    ta, td = t[:, 0], t[:, 1]
+    tp, tmg = ph[:, 1], ph[:, 2]
     return dict(append_ms=float(ta.mean()), partials_ms=float(tp.mean()), merge_ms=float(tmg.mean()),
                 decode_ms=float(td.mean()), decode_ms_median=float(np.median(td)),
                 decode_ms_p10=float(np.percentile(td, 10)), decode_ms_p90=float(np.percentile(td, 90)),
@@ -901,12 +923,20 @@ def measure_full36(args, torch, kv4, H, W, cpu_seconds):
     return line
 
 
-def _kernel_hash():
+def _kernel_hash(kernel=DOMINANT):
+    """Hash of what a kernel's code is made from: the headers that define it
+    and the compiler flags (so that an edit elsewhere in the library does not
+    retire the kernel's counters)."""
     import hashlib
     from int8_mixed_precision_amd import build as hb
+    csrc = os.path.join(ROOT, "int8_mixed_precision_amd", "csrc")
+    parts = (["kv4_common.hpp", "kv4_decode.hpp", "kv4_decode_mfma.hpp"] if "decode" in kernel else
+             ["kv4_common.hpp", "kv4_decode_mfma.hpp", "kv4_prefill.hpp"] if "prefill" in kernel else
+             [os.path.basename(f) for f in hb.sources() if f.startswith(csrc)])
     h = hashlib.sha256()
-    for f in hb.sources():
-        h.update(open(f, "rb").read())
+    for f in parts:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(" ".join(hb.HIPFLAGS).encode())
     return h.hexdigest()[:16]
 
 
