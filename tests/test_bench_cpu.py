@@ -101,7 +101,8 @@ def test_counter_summary_bytes_from_request_sizes(tmp_path):
         (5, dom, "TCC_EA0_WRREQ", 100.0), (5, dom, "TCC_EA0_WRREQ_64B", 60.0), (5, dom, "WRITE_SIZE", 4.0),
         (5, dom, "TCC_HIT", 30.0), (5, dom, "TCC_MISS", 90.0)])
     out = tmp_path / "c.json"
-    args = argparse.Namespace(summarize_counters=[rd, fs, wr], summary_cmd="cmd", summary_out=str(out))
+    args = argparse.Namespace(summarize_counters=[rd, fs, wr], summary_cmd="cmd", summary_out=str(out),
+                              summary_kernel="decode_kv4_mfma_kernel")
     bench.summarize_counters(args)
     res = json.load(open(out))
     read = 32 * 11.0 + 64 * 21.0 + 128 * 1001.0
