@@ -936,7 +936,7 @@ def _kernel_hash(kernel=DOMINANT):
     h = hashlib.sha256()
     for f in parts:
         h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(" ".join(hb.HIPFLAGS).encode())
+    h.update(" ".join(f for f in hb.HIPFLAGS if not os.path.isabs(f)).encode())   # not the include path
     return h.hexdigest()[:16]
 
 
