@@ -17,7 +17,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkv4.so")
+# KV4_LIB selects another build of the library (for example the host-side
+# sanitizer build of tests/sanitize_cpu.py)
+LIB_PATH = os.environ.get("KV4_LIB") or os.path.join(_HERE, "libkv4.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "kv4.h")
 
 KV4_OK = 0

@@ -26,6 +26,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kv4_oracle.c")
 _LIB = os.path.join(_HERE, "libkv4_oracle.so")
+# a separately built oracle library to load instead (for example the
+# sanitizer build of tests/sanitize_cpu.py); it is then not rebuilt here
+_LIB_OVERRIDE = os.environ.get("KV4_ORACLE_LIB", "")
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
           "-shared", "-fPIC", "-Wall", "-Wno-unknown-pragmas"]
@@ -46,8 +49,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build(force=False)                      # (re)builds when missing or older than the source
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            build(force=False)                  # (re)builds when missing or older than the source
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         L.orc_f32_to_f16.argtypes = [ctypes.c_float]
