@@ -155,7 +155,7 @@ def dequant_int8(codes, scale) -> np.ndarray:
 def wht(x) -> np.ndarray:
     """The fixed normalized Hadamard transform y = x H / sqrt(d) of vectors
     x[..., d] (KV4-RL Section 5.1; Appendix A.3), in binary32 in the order of
-    reading R-15: butterfly stages of span 1, 2, ..., d/2, then one product
+    reading R-10: butterfly stages of span 1, 2, ..., d/2, then one product
     with the binary32 value nearest 1/sqrt(d)."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     d = x.shape[-1]
@@ -190,7 +190,7 @@ class MixedCache:
         """``protect=(S, R)`` computes the INT8 copies only of positions that
         are protected at the stored length (others stay zero); the default
         computes them for every position, so any prefix can be attended.
-        ``rotate`` stores the keys in the rotated basis (R-15): both the INT4
+        ``rotate`` stores the keys in the rotated basis (R-10): both the INT4
         and the INT8 copy are computed from wht(k); values stay as they are."""
         self.G = G
         self.seq_lens = np.array([k.shape[0] for k in k_src], dtype=np.int32)

@@ -195,7 +195,7 @@ void orc_quant_int8(const float* x, int64_t nvec, int d, int8_t* codes, uint16_t
 }
 
 /* ------------------------------------------------------------------------ */
-/* R-15: the fixed normalized Hadamard transform of keys (after RoPE, before */
+/* R-10: the fixed normalized Hadamard transform of keys (after RoPE, before */
 /* quantization) and of queries (before attention), KV4-RL Section 5.1 and   */
 /* Appendix A.3 "Encoding and allocation"; scores are kept because HH^T = I  */
 /* (eq. 3.4).                                                                */
