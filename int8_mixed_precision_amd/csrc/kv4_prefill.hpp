@@ -40,28 +40,19 @@ struct PrefillArgs {
 //     threshold; only when some lane of the wave passes it are the four lanes
 //     of each column reduced (two row swaps) and the accumulators rescaled.
 //     The running sum is kept per lane and reduced once at the end.
-//   PV: O^T = V^T P^T on bf16 MFMA 16x16x32: A = V^T rows (channel 16 m + n16,
-//     keys 8 kb + [0, 8)) from LDS; B = P^T (keys 8 kb + [0, 8), query n16) as
-//     bf16 hi + lo (fp32-level accuracy).  The B operand of lane (n16, kb)
-//     holds keys that lanes (n16, 2 (kb % 2)) and (n16, 2 (kb % 2) + 1) computed
-//     in key block c = kb / 2: one v_permlane32_swap and one v_permlane16_swap
-//     per register pair move them (no LDS).  Lane l then holds query n16,
-//     channels 16 m + 4 kb + r in O[m][r]: the rescale and the final
-//     normalisation are in-lane, and each lane stores 16 contiguous bytes.
+//   PV: O^T = V^T P^T on bf16 MFMA 16x16x32, with the keys of the contraction
+//     in the order of the score layout: k-slots 8 kb + [0, 4) are keys 4 kb +
+//     [0, 4) and k-slots 8 kb + [4, 8) are keys 16 + 4 kb + [0, 4) (the order of
+//     a contraction's terms is free as long as both operands follow it).  B =
+//     P^T, so the B operand of lane (n16, kb) is exactly its own 8
+//     probabilities, as bf16 hi + lo (fp32-level accuracy): no lane exchange.
+//     A = V^T rows (channel 16 m + n16) from LDS, where the V^T columns are
+//     stored in that key order.  Lane l then holds query n16, channels 16 m +
+//     4 kb + r in O[m][r]: the rescale and the final normalisation are
+//     in-lane, and each lane stores 16 contiguous bytes.
 constexpr int kPrefillKeys = 32;
 constexpr int kPrefillRows = 2;
 constexpr int kPreQ = 4 * 16 * kPrefillRows;   // queries per workgroup
-
-// A pair of 32-bit registers after v_permlane32_swap then v_permlane16_swap:
-// with x0 from key block 0 and x1 from key block 1 of every lane, lane row kb
-// receives (row 2 (kb % 2) of block kb / 2, row 2 (kb % 2) + 1 of block kb / 2).
-__device__ __forceinline__ void gather_rows(uint32_t x0, uint32_t x1, uint32_t& lo, uint32_t& hi)
-{
-    const auto s = __builtin_amdgcn_permlane32_swap(x0, x1, false, false);
-    const auto t = __builtin_amdgcn_permlane16_swap(s[0], s[1], false, false);
-    lo = t[0];
-    hi = t[1];
-}
 
 // Maximum of three floats in one v_max3_f32.  fmaxf on a matrix-core result
 // costs an extra canonicalising v_max per operand (the compiler cannot tell
@@ -90,7 +81,7 @@ __device__ __forceinline__ uint4 ld16_rows(Page r, uint32_t off)
 template <int KT, int RB>
 __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
 {
-    static_assert(KT == 32, "the P^T row exchange is written for 32-key tiles");
+    static_assert(KT == 32, "the PV key order is written for 32-key tiles");
     constexpr int kPreK = KT, NC = KT / 16;                    // key blocks of a tile
     constexpr int kKs = kHeadDim + 16, kVt = KT + 16;          // row strides (bf16 elements)
     constexpr int QB = 4 * 16 * RB;                            // queries per workgroup
@@ -150,10 +141,13 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
     // through a buffer descriptor per tile: K key tid / 16 and 16 + tid / 16 at
     // channels 8 (tid % 16) ..; V keys 2 kp and 2 kp + 1 (kp = tid % 16) at
     // channels vch = 8 (tid / 16) .., so that each V^T store is one 32-bit word
-    // holding a key pair.  The descriptor's range ends with the tile's last
+    // holding a key pair, at column vcol: keys 4 j .. 4 j + 3 go to columns
+    // 8 j .. 8 j + 3 and keys 16 + 4 j .. 16 + 4 j + 3 to columns 8 j + 4 ..
+    // 8 j + 7 (the PV contraction's key order).  The descriptor's range ends with the tile's last
     // key inside the sequence: rows past it read as zero (those keys are
     // masked), and the lane offsets are the same for every tile.
     const int kp = tid & 15, vch = 8 * (tid >> 4);
+    const int vcol = kp < 8 ? 8 * (kp >> 1) + 2 * (kp & 1) : 8 * ((kp - 8) >> 1) + 4 + 2 * (kp & 1);
     const int64_t rowe = (int64_t)a.Hkv * d;                  // elements per token row
     const uint32_t rowb = (uint32_t)rowe * 2u;
     const uint16_t* kseq = a.k + (int64_t)t0 * rowe + (int64_t)h * d;
@@ -183,8 +177,8 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // channel vch + 2 e: low halves; vch + 2 e + 1: high halves
-            *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e][2 * kp]) = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e + 1][2 * kp]) =
+            *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e][vcol]) = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(&VT[buf][vch + 2 * e + 1][vcol]) =
                 __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
         }
     };
@@ -298,23 +292,17 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
             for (int rb = 0; rb < RB; ++rb) {
                 l_r[rb] += ((p[rb][0][0] + p[rb][0][1]) + (p[rb][0][2] + p[rb][0][3])) +
                            ((p[rb][1][0] + p[rb][1][1]) + (p[rb][1][2] + p[rb][1][3]));
-                // bf16 hi + lo of the key pairs (4 kb + 2 i, 4 kb + 2 i + 1) of
-                // each key block, then the row exchange into the B operand
-                uint32_t h2[NC][2], l2[NC][2];
+                // bf16 hi + lo of the key pairs (16 c + 4 kb + 2 i, .. + 1): k-slots
+                // 8 kb + 4 c + 2 i, 8 kb + 4 c + 2 i + 1 of the B operand
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) split_bf16(p[rb][c][2 * i], p[rb][c][2 * i + 1], h2[c][i], l2[c][i]);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    uint32_t a0, a1, b0, b1;
-                    gather_rows(h2[0][i], h2[1][i], a0, a1);
-                    gather_rows(l2[0][i], l2[1][i], b0, b1);
-                    phi[rb][i] = a0;
-                    phi[rb][2 + i] = a1;
-                    plo[rb][i] = b0;
-                    plo[rb][2 + i] = b1;
-                }
+                    for (int i = 0; i < 2; ++i) {
+                        uint32_t hw, lw;
+                        split_bf16(p[rb][c][2 * i], p[rb][c][2 * i + 1], hw, lw);
+                        phi[rb][2 * c + i] = hw;
+                        plo[rb][2 * c + i] = lw;
+                    }
             }
             // ---- PV (O^T += V^T P^T): every V operand used for the RB row blocks
 #pragma unroll
