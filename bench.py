@@ -38,7 +38,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0             # dense bf16 matrix-core peak of MI35
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=90,
+                    help="timed steps (reported also as three blocks of a third each)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="q8b256")
     ap.add_argument("--waves", type=int, default=0,
@@ -397,6 +398,7 @@ def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=Non
     return dict(append_ms=float(ta.mean()), partials_ms=float(tp.mean()), merge_ms=float(tmg.mean()),
                 decode_ms=float(td.mean()), decode_ms_median=float(np.median(td)),
                 decode_ms_p10=float(np.percentile(td, 10)), decode_ms_p90=float(np.percentile(td, 90)),
+                decode_ms_block_medians=[float(np.median(x)) for x in np.array_split(td, 3) if len(x)],
                 partials_ms_median=float(np.median(tp)), waves=waves, pool_chunks=chunks)
 
 
@@ -654,6 +656,8 @@ def main():
         "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
         "decode_partials_us": round(r["partials_ms"] * 1e3, 2),
         "decode_merge_us": round(r["merge_ms"] * 1e3, 2),
+        "decode_attn_us_block_medians": [round(x * 1e3, 2) for x in r["decode_ms_block_medians"]],
+        "decode_attn_median_over_mean": round(r["decode_ms_median"] / r["decode_ms"], 4),
         "decode_attn_us_median_p10_p90": [round(r["decode_ms_median"] * 1e3, 2),
                                           round(r["decode_ms_p10"] * 1e3, 2),
                                           round(r["decode_ms_p90"] * 1e3, 2)],
