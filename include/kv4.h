@@ -387,6 +387,40 @@ const char* kv4_status_string(int status);
  */
 int kv4_decode_partition(const kv4_cache* cache, int* waves, int* pool_chunks);
 
+/*
+ * Validating build (the library compiled with KV4_VALIDATE: libkv4_validate.so;
+ * a debugging aid, no passage of the pages behind it).  Before each append,
+ * decode and prefill launch, a check kernel on the same stream reads the
+ * device arrays as this header defines them and records every kind of
+ * violation it finds; the checked launches are unchanged (they clamp as
+ * described under "Conventions").  Kinds:
+ *   SEQ_LEN    a decode length outside [1, max_ctx], or a prefill sequence
+ *              longer than max_seqlen;
+ *   SLOT       a slot id outside [0, max_slots);
+ *   PAGE       a block-table entry outside [0, num_pages) for a page the call
+ *              reads or writes (pages of positions [0, n) for a decode, of the
+ *              new positions for an append);
+ *   ROWS       row offsets (cu_new, cu_seqlens) that are negative, decreasing,
+ *              past the total, or do not start at 0 and end at the total;
+ *   POSITION   ctx_before[b] < 0 or ctx_before[b] + new_b beyond the block
+ *              table's capacity (max_pages_per_seq * page_size);
+ *   DUPLICATE_WRITE  two sequences of one append writing the same page, or the
+ *              same slot's INT8 ring (pages below 2^20 and slots below 2^16
+ *              are tracked).
+ * kv4_validate_report stores the OR of the kinds recorded on the current
+ * device since the last report into *violations and clears them (synchronous;
+ * synchronise the streams that ran the checked calls first).  Errors:
+ * KV4_ERR_INVALID_ARG (null pointer), KV4_ERR_UNSUPPORTED (a library built
+ * without KV4_VALIDATE; *violations is set to 0), KV4_ERR_HIP.
+ */
+#define KV4_VIOLATION_SEQ_LEN          0x01u
+#define KV4_VIOLATION_SLOT             0x02u
+#define KV4_VIOLATION_PAGE             0x04u
+#define KV4_VIOLATION_ROWS             0x08u
+#define KV4_VIOLATION_POSITION         0x10u
+#define KV4_VIOLATION_DUPLICATE_WRITE  0x20u
+int kv4_validate_report(uint32_t* violations);
+
 #ifdef __cplusplus
 }
 #endif

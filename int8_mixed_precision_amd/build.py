@@ -16,6 +16,8 @@ LIB = os.path.join(HERE, "libkv4.so")
 # read-bandwidth ceilings (measurement aid, include/kv4_roof.h)
 ROOF_SRC = os.path.join(HERE, "csrc", "kv4_roof.hip")
 ROOF_LIB = os.path.join(HERE, "libkv4_roof.so")
+# the same library with the device-side checks of KV4_VALIDATE (include/kv4.h)
+VALIDATE_LIB = os.path.join(HERE, "libkv4_validate.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIPFLAGS = [
@@ -43,9 +45,9 @@ def sources():
         [os.path.join(ROOT, "include", "kv4.h")]
 
 
-def _compile(src, lib, verbose):
+def _compile(src, lib, verbose, extra=()):
     tmp = lib + ".tmp"
-    cmd = [HIPCC, *HIPFLAGS, src, "-o", tmp]
+    cmd = [HIPCC, *HIPFLAGS, *extra, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -53,8 +55,13 @@ def _compile(src, lib, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    _compile(SRC, LIB, verbose)
-    _compile(ROOF_SRC, ROOF_LIB, verbose)
+    """Compiles the library, its validating build and the read-ceiling
+    kernels (three independent hipcc runs, in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(SRC, LIB, ()), (SRC, VALIDATE_LIB, ("-DKV4_VALIDATE",)), (ROOF_SRC, ROOF_LIB, ())]
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        for f in [ex.submit(_compile, src, lib, verbose, extra) for src, lib, extra in jobs]:
+            f.result()
     return LIB
 
 

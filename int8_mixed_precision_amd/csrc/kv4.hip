@@ -15,6 +15,9 @@
 #include "kv4_decode.hpp"
 #include "kv4_decode_mfma.hpp"
 #include "kv4_prefill.hpp"
+#ifdef KV4_VALIDATE
+#include "kv4_validate.hpp"
+#endif
 
 // Workspace of kv4_decode_attn_noalloc: device memory reserved with the code
 // object (every device that loads the library holds its own copy until the
@@ -190,6 +193,9 @@ void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 
 void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
 {
+#ifdef KV4_VALIDATE
+    hipLaunchKernelGGL(kv4::validate_decode_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+#endif
     // the pool counters start every launch at zero (a kernel, not a memset, so
     // that the launch sequence can be captured in a graph)
     if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
@@ -397,6 +403,14 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     a.pages = cache->pages;
     a.side = cache->side;
     hipStream_t s = static_cast<hipStream_t>(stream);
+#ifdef KV4_VALIDATE
+    {
+        const int np = std::min(g.num_pages, kv4::kOwnPages), ns = std::min(g.max_slots, kv4::kOwnSlots);
+        hipLaunchKernelGGL(kv4::validate_clear_kernel, dim3((unsigned)std::min(1024, (std::max(np, ns) + 255) / 256)),
+                           dim3(256), 0, s, np, ns);
+        hipLaunchKernelGGL(kv4::validate_append_kernel, dim3((unsigned)batch), dim3(256), 0, s, a);
+    }
+#endif
     // parallelism along each sequence sized by the mean number of new tokens
     int64_t mean_new = ((int64_t)total_new + batch - 1) / batch;
     if (g.kind == KV4_KIND_MIXED) {
@@ -547,9 +561,32 @@ int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_b
     a.gqa = d.num_q_heads / d.num_kv_heads;
     a.scale2 = sm_scale * 1.4426950408889634f;
     dim3 grid((unsigned)a.Hq, (unsigned)batch, (unsigned)((max_seqlen + kv4::kPreQ - 1) / kv4::kPreQ));
+#ifdef KV4_VALIDATE
+    hipLaunchKernelGGL(kv4::validate_prefill_kernel, dim3((unsigned)std::min(1024, (batch + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
+#endif
     hipLaunchKernelGGL((kv4::prefill_attn_kernel<kv4::kPrefillKeys, kv4::kPrefillRows>), grid, dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);
     return launch_status();
+}
+
+int kv4_validate_report(uint32_t* violations)
+{
+    if (violations == nullptr) return KV4_ERR_INVALID_ARG;
+    *violations = 0;
+#ifdef KV4_VALIDATE
+    uint32_t v = 0;
+    const uint32_t zero = 0;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(kv4::g_violations), sizeof v, 0, hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpyToSymbol(HIP_SYMBOL(kv4::g_violations), &zero, sizeof zero, 0, hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        return KV4_ERR_HIP;
+    }
+    *violations = v;
+    return KV4_OK;
+#else
+    return KV4_ERR_UNSUPPORTED;
+#endif
 }
 
 int kv4_cache_free(kv4_cache* cache)

@@ -20,6 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # KV4_LIB selects another build of the library (for example the host-side
 # sanitizer build of tests/sanitize_cpu.py)
 LIB_PATH = os.environ.get("KV4_LIB") or os.path.join(_HERE, "libkv4.so")
+# the validating build (KV4_VALIDATE device-side checks; include/kv4.h)
+VALIDATE_LIB_PATH = os.path.join(_HERE, "libkv4_validate.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "kv4.h")
 
 KV4_OK = 0
@@ -35,6 +37,12 @@ KV4_FLAG_ROTATE_K = 0x1
 KV4_FLAG_INT_PATH = 0x2
 KV4_OUT_F32 = 0
 KV4_OUT_BF16 = 1
+KV4_VIOLATION_SEQ_LEN = 0x01
+KV4_VIOLATION_SLOT = 0x02
+KV4_VIOLATION_PAGE = 0x04
+KV4_VIOLATION_ROWS = 0x08
+KV4_VIOLATION_POSITION = 0x10
+KV4_VIOLATION_DUPLICATE_WRITE = 0x20
 
 
 class kv4_cache_desc(ctypes.Structure):
@@ -71,10 +79,11 @@ def _load(path: str = LIB_PATH):
     L.kv4_status_string.restype = ctypes.c_char_p
     L.kv4_decode_partition.argtypes = [P, pi32, pi32]
     L.kv4_prefill_attn.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.c_float, P, i32, P]
+    L.kv4_validate_report.argtypes = [ctypes.POINTER(ctypes.c_uint32)]
     for f in ("kv4_cache_required_bytes", "kv4_cache_create", "kv4_append",
               "kv4_decode_workspace_bytes", "kv4_decode_attn", "kv4_decode_partials",
               "kv4_decode_merge", "kv4_cache_free", "kv4_decode_partition", "kv4_prefill_attn",
-              "kv4_decode_attn_noalloc"):
+              "kv4_decode_attn_noalloc", "kv4_validate_report"):
         getattr(L, f).restype = i32
     return L
 
@@ -270,6 +279,16 @@ def kv4_decode_merge(cache, seq_lens: torch.Tensor, batch: int, max_ctx: int, ou
     _check(_lib.kv4_decode_merge(cache, _ptr(seq_lens), int(batch), int(max_ctx), _ptr(out),
                                  int(out_dtype), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "kv4_decode_merge")
+
+
+def kv4_validate_report(library=None) -> int:
+    """The violation kinds the validating build recorded on the current device
+    since the last report (and clears them); raises KV4Error with
+    KV4_ERR_UNSUPPORTED on a library built without KV4_VALIDATE."""
+    L = library if library is not None else _lib
+    v = ctypes.c_uint32(0)
+    _check(L.kv4_validate_report(ctypes.byref(v)), "kv4_validate_report")
+    return int(v.value)
 
 
 def kv4_cache_free(cache) -> None:

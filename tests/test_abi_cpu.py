@@ -40,6 +40,21 @@ def test_library_exports_every_declared_function():
         assert name in names
 
 
+def test_validating_build_exports_the_same_functions():
+    """libkv4_validate.so (KV4_VALIDATE) is the same ABI; only it records
+    violations, the product build reports KV4_ERR_UNSUPPORTED."""
+    assert os.path.exists(kv4.VALIDATE_LIB_PATH), "build() also builds the validating library"
+    V = kv4._load(kv4.VALIDATE_LIB_PATH)
+    for name in kv4.declared_functions():
+        assert hasattr(V, name), name
+    with pytest.raises(kv4.KV4Error) as e:
+        kv4.kv4_validate_report()
+    assert e.value.code == kv4.KV4_ERR_UNSUPPORTED
+    v = ctypes.c_uint32(7)
+    assert kv4.lib().kv4_validate_report(ctypes.byref(v)) == kv4.KV4_ERR_UNSUPPORTED and v.value == 0
+    assert V.kv4_validate_report(None) == kv4.KV4_ERR_INVALID_ARG
+
+
 def test_storage_sizes_match_pages():
     gold = _golden()
     for G, key in ((128, "bits_per_elem_g128"), (32, "bits_per_elem_g32")):
