@@ -54,6 +54,11 @@ def parse():
                     help="INT4 group size of the KV4 cache (0 = the config's, 32)")
     ap.add_argument("--populate-reps", type=int, default=5,
                     help="timed bulk appends of the first 32 sequences' histories (0 = skip)")
+    ap.add_argument("--no-valu", action="store_true",
+                    help="skip the vector-ALU decode of the same KV4 bytes (KV4_FLAG_VALU_DECODE)")
+    ap.add_argument("--valu-decode", action="store_true",
+                    help="run the KV4 cache's decode on the vector-ALU kernel (KV4_FLAG_VALU_DECODE; "
+                         "for profiling it)")
     ap.add_argument("--no-int-path", action="store_true",
                     help="skip the integer decode path (KV4_FLAG_INT_PATH) over the same KV4 bytes")
     ap.add_argument("--prefill-reps", type=int, default=3,
@@ -544,10 +549,14 @@ def main():
     log(f"config {cfg.name}: B={B} sum(n)={int(n.sum())} max n={int(n.max())}")
 
     common = dict(waves=args.waves, pool_chunks=args.pool_chunks)
-    specs = {"kv4": dict(common, flags=kv4.KV4_FLAG_ROTATE_K if args.rotate else 0)}
+    specs = {"kv4": dict(common, flags=(kv4.KV4_FLAG_ROTATE_K if args.rotate else 0) |
+                                       (kv4.KV4_FLAG_VALU_DECODE if args.valu_decode else 0))}
     if not args.only_kv4:
         if not args.no_bf16:
             specs["bf16"] = dict(common, kind=kv4.KV4_KIND_BF16, sink=0, recent=0)
+        if not args.no_valu and not args.valu_decode:
+            specs["valu"] = dict(common, flags=kv4.KV4_FLAG_VALU_DECODE |
+                                 (kv4.KV4_FLAG_ROTATE_K if args.rotate else 0))
         if not args.no_int_path:
             specs["int"] = dict(common, flags=kv4.KV4_FLAG_INT_PATH |
                                 (kv4.KV4_FLAG_ROTATE_K if args.rotate else 0))
@@ -620,7 +629,7 @@ def main():
     achieved = pb / (r["partials_ms"] * 1e-3) / 1e9
     traffic = None
     # the stored counters are those of the default workload (unrotated, group 32)
-    if (os.path.exists(args.traffic_json) and not args.rotate and cfg.group == 32
+    if (os.path.exists(args.traffic_json) and not args.rotate and not args.valu_decode and cfg.group == 32
             and cfg.name == "q8b256"):
         try:
             tj = json.load(open(args.traffic_json))
@@ -666,7 +675,8 @@ def main():
         "partials_alg_bytes": pb,
         "append_alg_bytes": ab,
         "layer_tokens_per_s": round(B / (step_ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "decode_kv4_mfma_kernel (kv4_decode_partials)",
+        "roofline": {"bound": "hbm", "kernel": ("decode_valu_kv4_kernel" if args.valu_decode else
+                                                "decode_kv4_mfma_kernel") + " (kv4_decode_partials)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": pb,
@@ -688,6 +698,18 @@ def main():
         line["populate"] = populate
     if prefill is not None:
         line["prefill"] = prefill
+    if "valu" in results:
+        rv = results["valu"]
+        line["valu_comparator"] = {
+            "kernel": "decode_valu_kv4_kernel<4> (KV4_FLAG_VALU_DECODE: the floating-point decode on the "
+                      "vector ALU at GQA 4, same KV4 bytes)",
+            "waves": rv["waves"],
+            "decode_attn_us": round(rv["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(rv["partials_ms"] * 1e3, 2),
+            "partials_gbs": round(pb / (rv["partials_ms"] * 1e-3) / 1e9, 2),
+            "partials_frac_hbm_peak": round(pb / (rv["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "matrix_core_speedup": round(rv["partials_ms"] / r["partials_ms"], 3),
+        }
     if "int" in results:
         ri = results["int"]
         line["int_path"] = {

@@ -127,6 +127,12 @@ extern "C" {
  * probability quantization).  Mixed kind only (KV4_ERR_UNSUPPORTED otherwise);
  * any q/kv head ratio of 1, 2, 4 or 8; the cache's bytes do not change. */
 #define KV4_FLAG_INT_PATH 0x2
+/* KV4_FLAG_VALU_DECODE: the decode runs on the vector-ALU kernels at every q/kv
+ * head ratio (otherwise ratio 4 runs on the matrix-core kernels), with the
+ * same partition, arithmetic definitions and tolerance.  A measurement point
+ * for the choice of the matrix core at ratio 4 (no passage of the pages behind
+ * it).  Mixed and BF16 kinds (KV4_ERR_UNSUPPORTED for KV8). */
+#define KV4_FLAG_VALU_DECODE 0x4
 
 /* Output dtypes of kv4_decode_attn. */
 #define KV4_OUT_F32  0
@@ -151,10 +157,11 @@ typedef struct kv4_cache_desc {
     int32_t flags;              /* KV4_FLAG_* */
     int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
                                    partition; 0 = 16 per compute unit of the
-                                   current device (with KV4_FLAG_INT_PATH and a
-                                   q/kv head ratio other than 4: as many per
-                                   compute unit as its vector-ALU kernel keeps
-                                   resident, at most 16), else 1 .. 65536 */
+                                   current device (when the decode runs on a
+                                   vector-ALU kernel -- a q/kv head ratio other
+                                   than 4, or KV4_FLAG_VALU_DECODE -- as many per
+                                   compute unit as that kernel keeps resident,
+                                   at most 16), else 1 .. 65536 */
     int32_t pool_chunks;        /* most chunks of the decode's dynamic pool: 0 = no
                                    pool (the default), else a power of two in
                                    8 .. 65536 */

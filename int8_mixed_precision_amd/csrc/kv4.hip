@@ -55,7 +55,7 @@ int validate_desc(const kv4_cache_desc* d)
     if (d->num_q_heads % d->num_kv_heads != 0) return KV4_ERR_INVALID_ARG;
     if (d->kind != KV4_KIND_MIXED && d->kind != KV4_KIND_BF16 && d->kind != KV4_KIND_KV8)
         return KV4_ERR_INVALID_ARG;
-    if (d->flags & ~(KV4_FLAG_ROTATE_K | KV4_FLAG_INT_PATH)) return KV4_ERR_INVALID_ARG;
+    if (d->flags & ~(KV4_FLAG_ROTATE_K | KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE)) return KV4_ERR_INVALID_ARG;
     if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
     int gqa = d->num_q_heads / d->num_kv_heads;
     if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
@@ -66,6 +66,8 @@ int validate_desc(const kv4_cache_desc* d)
     // the integer path reads the INT4 pages and the INT8 ring
     if ((d->flags & KV4_FLAG_INT_PATH) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
     if (d->kind == KV4_KIND_KV8 && d->num_q_heads != 4 * d->num_kv_heads) return KV4_ERR_UNSUPPORTED;
+    // KV8 pages are decoded on the matrix core only
+    if (d->kind == KV4_KIND_KV8 && (d->flags & KV4_FLAG_VALU_DECODE)) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
     if ((int64_t)d->max_pages_per_seq * kv4::kPage > INT32_MAX / 2) return KV4_ERR_CAPACITY;
     return KV4_OK;
@@ -88,42 +90,63 @@ int num_cus(kv4_cache* c)
     return c->num_cus > 0 ? c->num_cus : 256;
 }
 
-// Waves of the balanced decode partition: explicit, or 16 per compute unit
-// (4 one-wave workgroups per SIMD, the occupancy the decode kernel is built
-// for), so that every wave of the grid is resident at once.
-// The integer path's vector-ALU kernels hold more registers than the
-// matrix-core ones: as many waves per compute unit as the kernel keeps
-// resident (at most 16), so that the partition's waves still run at once.
-// 16 when the runtime cannot tell (no device).
-int int_path_waves_per_cu(int gqa)
+// Resident one-wave workgroups per compute unit of a vector-ALU decode kernel
+// (at most 16), from the HIP occupancy query; 16 when the runtime cannot tell.
+template <class K>
+int resident_waves(K kernel, std::atomic<int>& known)
 {
-    static std::atomic<int> known[9];
-    const int k = gqa == 1 ? 1 : gqa == 2 ? 2 : gqa == 4 ? 4 : 8;
-    int w = known[k].load(std::memory_order_relaxed);
+    int w = known.load(std::memory_order_relaxed);
     if (w > 0) return w;
     int nb = 0;
-    hipError_t e;
-    switch (k) {
-        case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<1>, 64, 0); break;
-        case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<2>, 64, 0); break;
-        case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<4>, 64, 0); break;
-        default: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kv4::decode_int_kv4_kernel<8>, 64, 0); break;
-    }
-    if (e != hipSuccess || nb <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 64, 0) != hipSuccess || nb <= 0) {
         (void)hipGetLastError();
         return 16;
     }
     w = std::min(nb, 16);
-    known[k].store(w, std::memory_order_relaxed);
+    known.store(w, std::memory_order_relaxed);
     return w;
 }
 
+int valu_waves_per_cu(const kv4_cache_desc& d, int gqa)
+{
+    static std::atomic<int> known[3][9];
+    const int k = gqa == 1 ? 1 : gqa == 2 ? 2 : gqa == 4 ? 4 : 8;
+    if (d.flags & KV4_FLAG_INT_PATH) {
+        switch (k) {
+            case 1: return resident_waves(kv4::decode_int_kv4_kernel<1>, known[0][1]);
+            case 2: return resident_waves(kv4::decode_int_kv4_kernel<2>, known[0][2]);
+            case 4: return resident_waves(kv4::decode_int_kv4_kernel<4>, known[0][4]);
+            default: return resident_waves(kv4::decode_int_kv4_kernel<8>, known[0][8]);
+        }
+    }
+    if (d.kind == KV4_KIND_MIXED) {
+        switch (k) {
+            case 1: return resident_waves(kv4::decode_valu_kv4_kernel<1>, known[1][1]);
+            case 2: return resident_waves(kv4::decode_valu_kv4_kernel<2>, known[1][2]);
+            case 4: return resident_waves(kv4::decode_valu_kv4_kernel<4>, known[1][4]);
+            default: return resident_waves(kv4::decode_valu_kv4_kernel<8>, known[1][8]);
+        }
+    }
+    switch (k) {
+        case 1: return resident_waves(kv4::decode_valu_bf16_kernel<1>, known[2][1]);
+        case 2: return resident_waves(kv4::decode_valu_bf16_kernel<2>, known[2][2]);
+        case 4: return resident_waves(kv4::decode_valu_bf16_kernel<4>, known[2][4]);
+        default: return resident_waves(kv4::decode_valu_bf16_kernel<8>, known[2][8]);
+    }
+}
+
+// Waves of the balanced decode partition: explicit, or 16 per compute unit
+// (4 one-wave workgroups per SIMD, the occupancy the matrix-core decode
+// kernels are built for), so that every wave of the grid is resident at once.
+// The vector-ALU kernels hold more registers: as many waves per compute unit
+// as the kernel keeps resident (at most 16), so that the partition's waves
+// still run at once.
 int decode_waves(const kv4_cache* c, int cus)
 {
     if (c->desc.num_waves > 0) return c->desc.num_waves;
-    // (the matrix-core integer kernels of GQA 4 keep 16 resident)
+    // (the matrix-core kernels of GQA 4 keep 16 resident)
     const int gqa = c->desc.num_q_heads / c->desc.num_kv_heads;
-    if ((c->desc.flags & KV4_FLAG_INT_PATH) && gqa != 4) return int_path_waves_per_cu(gqa) * cus;
+    if (gqa != 4 || (c->desc.flags & KV4_FLAG_VALU_DECODE)) return valu_waves_per_cu(c->desc, gqa) * cus;
     return 16 * cus;
 }
 
@@ -180,7 +203,8 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
-// Vector-ALU kernels, used for GQA group sizes other than 4.
+// Vector-ALU kernels, used for GQA group sizes other than 4 (and for 4 with
+// KV4_FLAG_VALU_DECODE).
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
@@ -201,7 +225,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
     if (a.g.intp) {
         dim3 grid((unsigned)a.waves);
-        if (a.g.gqa == 4) {
+        if (a.g.gqa == 4 && !a.g.valu) {
             switch (a.g.G) {
                 case 32:
                     if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<32, true>), grid, dim3(64), 0, s, a);
@@ -226,7 +250,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
         }
         return;
     }
-    if (a.g.gqa == 4) {
+    if (a.g.gqa == 4 && !a.g.valu) {
         dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {
             switch (a.g.G) {
@@ -253,6 +277,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     switch (a.g.gqa) {
         case 1: launch_decode_valu<1>(a, s); break;
         case 2: launch_decode_valu<2>(a, s); break;
+        case 4: launch_decode_valu<4>(a, s); break;
         default: launch_decode_valu<8>(a, s); break;
     }
 }

@@ -20,6 +20,7 @@ struct Geo {
     int kind;
     int rot;                 // 1: keys stored, and queries attended, in the rotated basis
     int intp;                // 1: decode takes the integer path (INT8 q, 8-bit P operand)
+    int valu;                // 1: decode on the vector-ALU kernels at every q/kv ratio
     int64_t pb;              // bytes per (page, kv head) block
     int64_t layer_pages;     // bytes of one layer of the page pool
     int64_t rb;              // bytes per (slot, kv head) ring block
@@ -88,6 +89,7 @@ inline Geo make_geo(const kv4_cache_desc& c)
     g.kind = c.kind;
     g.rot = (c.flags & KV4_FLAG_ROTATE_K) != 0;
     g.intp = (c.flags & KV4_FLAG_INT_PATH) != 0;
+    g.valu = (c.flags & KV4_FLAG_VALU_DECODE) != 0;
     g.S = c.kind == KV4_KIND_MIXED ? c.sink : 0;
     g.R = c.kind == KV4_KIND_MIXED ? c.recent : 0;
     g.SR = g.S + g.R;

@@ -35,6 +35,7 @@ KV4_KIND_BF16 = 1
 KV4_KIND_KV8 = 2
 KV4_FLAG_ROTATE_K = 0x1
 KV4_FLAG_INT_PATH = 0x2
+KV4_FLAG_VALU_DECODE = 0x4
 KV4_OUT_F32 = 0
 KV4_OUT_BF16 = 1
 KV4_VIOLATION_SEQ_LEN = 0x01

@@ -121,7 +121,11 @@ def test_invalid_descriptors():
         (dict(flags=kv4.KV4_FLAG_INT_PATH | kv4.KV4_FLAG_ROTATE_K), kv4.KV4_OK),
         (dict(flags=kv4.KV4_FLAG_INT_PATH, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
         (dict(flags=kv4.KV4_FLAG_INT_PATH, kind=kv4.KV4_KIND_KV8), kv4.KV4_ERR_UNSUPPORTED),
-        (dict(flags=0x4), kv4.KV4_ERR_INVALID_ARG),
+        (dict(flags=0x8), kv4.KV4_ERR_INVALID_ARG),
+        (dict(flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_OK),
+        (dict(flags=kv4.KV4_FLAG_VALU_DECODE, kind=kv4.KV4_KIND_BF16), kv4.KV4_OK),
+        (dict(flags=kv4.KV4_FLAG_VALU_DECODE | kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),
+        (dict(flags=kv4.KV4_FLAG_VALU_DECODE, kind=kv4.KV4_KIND_KV8), kv4.KV4_ERR_UNSUPPORTED),
     ]
     for change, code in cases:
         d = kv4.make_desc(**{**base, **change})

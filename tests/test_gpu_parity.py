@@ -62,7 +62,7 @@ def _compare_bytes(built, pages, side, layer, oc, S, R, seqs=None, n_of=None):
 
 
 def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_bytes=True,
-              garbage=True, pool_chunks=0, rotate=False):
+              garbage=True, pool_chunks=0, rotate=False, flags=0):
     """Build a cache for contexts ctx (history + one step token), decode, and
     compare with the oracle.  Returns (built, output, oracle cache).  With
     ``rotate`` the cache stores keys in the rotated basis (KV4_FLAG_ROTATE_K)
@@ -73,7 +73,7 @@ def _run_case(Hq, Hkv, G, S, R, ctx, seed, waves=0, layers=1, layer=0, check_byt
     ks, vs = W.all_kv_sources(cfg, layer, n)
     q = W.queries(cfg, layer)
     built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, pool_chunks=pool_chunks,
-                         flags=kv4.KV4_FLAG_ROTATE_K if rotate else 0, seed=seed)
+                         flags=flags | (kv4.KV4_FLAG_ROTATE_K if rotate else 0), seed=seed)
     if garbage:
         _fill_garbage(built)
     H.build_from_sources(built, layer, ks, vs, ctx)
@@ -405,6 +405,29 @@ def test_append_extreme_values(G):
     H.log(f"  bytes bit-exact; outputs within the derived bar, worst error {worst:.2e} of max|v^|")
 
 
+def test_valu_decode_at_gqa4():
+    """KV4_FLAG_VALU_DECODE: at q/kv ratio 4 the decode runs on the vector-ALU
+    kernels, against the same oracle as the matrix-core ones (floating-point
+    and integer paths, rotated keys, G = 32 and 128, edge lengths)."""
+    ctx = [0, 3, 4, 5, 19, 20, 21, 100, 257, 700, 2500]
+    for G, rotate in ((32, False), (128, False), (32, True)):
+        H.log(f"case vector-ALU decode at GQA 4, G={G} rotate={rotate}")
+        _run_case(8, 2, G, 4, 16, ctx, seed=140 + G, rotate=rotate, flags=kv4.KV4_FLAG_VALU_DECODE)
+    H.log("case vector-ALU decode at GQA 4, integer path")
+    _int_case(8, 2, 32, 4, 64, [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500], seed=150,
+              flags=kv4.KV4_FLAG_VALU_DECODE)
+    H.log("case vector-ALU decode at GQA 4, BF16 kind")
+    ctxb = np.array([0, 15, 16, 17, 300, 1000, 3000])
+    n = ctxb + 1
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=33, batch=len(ctxb), ctx_kind="fixed", ctx_fixed=tuple(ctxb))
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    q = W.queries(cfg, 0)
+    built = H.make_cache(8, 2, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, flags=kv4.KV4_FLAG_VALU_DECODE, seed=5)
+    H.build_from_sources(built, 0, ks, vs, ctxb)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
+
+
 def test_bf16_comparator():
     """BF16 kind: pages hold the bf16 values exactly; output matches the
     oracle's dense attention."""
@@ -499,7 +522,7 @@ INT_ATOL = 1e-4
 
 
 def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, layer=0, pool_chunks=0,
-              qscale=1.0):
+              qscale=1.0, flags=0):
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R,
                    seed=seed, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
     n = np.asarray(ctx, np.int64) + 1
@@ -507,7 +530,7 @@ def _int_case(Hq, Hkv, G, S, R, ctx, seed, rotate=False, waves=0, layers=1, laye
     q = W.queries(cfg, layer)
     if qscale != 1.0:
         q = W.to_bf16_values((q * qscale).astype(np.float32))
-    flags = kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if rotate else 0)
+    flags |= kv4.KV4_FLAG_INT_PATH | (kv4.KV4_FLAG_ROTATE_K if rotate else 0)
     built = H.make_cache(Hq, Hkv, G, S, R, n, layers=layers, waves=waves, flags=flags, seed=seed,
                          pool_chunks=pool_chunks)
     _fill_garbage(built)
