@@ -90,8 +90,15 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
     // grid (q head, sequence, query block) with the query blocks in reverse:
     // workgroups are dispatched x fastest, so the last (heaviest: the most
     // causal key tiles) query blocks of every sequence and head start first
-    // and the cheap early blocks fill the tail
-    const int b = blockIdx.y, j = blockIdx.x, qb = (int)gridDim.z - 1 - (int)blockIdx.z;
+    // and the cheap early blocks fill the tail.
+    // Workgroups go to the eight XCDs in turn, so with a multiple of 8 q heads
+    // every workgroup with x % 8 == c runs on XCD c.  x is taken as q head
+    // c Hq/8 + x/8: the q heads of a kv head (consecutive), which read the same
+    // K and V tiles, then share one XCD's L2 (at Hq = 32 and 8 kv heads, XCD c
+    // holds exactly the four q heads of kv head c).
+    const int xq = (int)blockIdx.x;
+    const int j = (a.Hq & 7) ? xq : (xq & 7) * (a.Hq >> 3) + (xq >> 3);
+    const int b = blockIdx.y, qb = (int)gridDim.z - 1 - (int)blockIdx.z;
     const int t0 = clampi(a.cu[b], 0, a.total);
     const int L = min(clampi(a.cu[b + 1], t0, a.total) - t0, a.max_len);
     if (QB * qb >= L) return;                             // uniform over the workgroup
