@@ -135,6 +135,32 @@ int valu_waves_per_cu(const kv4_cache_desc& d, int gqa)
     }
 }
 
+// Resident waves per compute unit of the ratio-8 matrix-core kernel of the
+// cache's group size and key basis.
+int mfma8_waves_per_cu(const kv4_cache_desc& d)
+{
+    static std::atomic<int> known[3][2];
+    const bool rot = (d.flags & KV4_FLAG_ROTATE_K) != 0;
+    switch (d.group_size) {
+        case 32:
+            return rot ? resident_waves(kv4::decode_kv4_mfma8_kernel<32, true>, known[0][1])
+                       : resident_waves(kv4::decode_kv4_mfma8_kernel<32, false>, known[0][0]);
+        case 64:
+            return rot ? resident_waves(kv4::decode_kv4_mfma8_kernel<64, true>, known[1][1])
+                       : resident_waves(kv4::decode_kv4_mfma8_kernel<64, false>, known[1][0]);
+        default:
+            return rot ? resident_waves(kv4::decode_kv4_mfma8_kernel<128, true>, known[2][1])
+                       : resident_waves(kv4::decode_kv4_mfma8_kernel<128, false>, known[2][0]);
+    }
+}
+
+// Whether the decode of a cache runs on the ratio-8 matrix-core kernel.
+bool uses_mfma8(const kv4_cache_desc& d)
+{
+    return d.num_q_heads == 8 * d.num_kv_heads && d.kind == KV4_KIND_MIXED &&
+           !(d.flags & (KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE));
+}
+
 // Waves of the balanced decode partition: explicit, or 16 per compute unit
 // (4 one-wave workgroups per SIMD, the occupancy the matrix-core decode
 // kernels are built for), so that every wave of the grid is resident at once.
@@ -144,9 +170,10 @@ int valu_waves_per_cu(const kv4_cache_desc& d, int gqa)
 int decode_waves(const kv4_cache* c, int cus)
 {
     if (c->desc.num_waves > 0) return c->desc.num_waves;
-    // (the matrix-core kernels of GQA 4 keep 16 resident)
+    // (the matrix-core kernels, q/kv ratios 1, 2 and 4, keep 16 resident)
     const int gqa = c->desc.num_q_heads / c->desc.num_kv_heads;
-    if (gqa != 4 || (c->desc.flags & KV4_FLAG_VALU_DECODE)) return valu_waves_per_cu(c->desc, gqa) * cus;
+    if (uses_mfma8(c->desc)) return mfma8_waves_per_cu(c->desc) * cus;
+    if (gqa > 4 || (c->desc.flags & KV4_FLAG_VALU_DECODE)) return valu_waves_per_cu(c->desc, gqa) * cus;
     return 16 * cus;
 }
 
@@ -203,8 +230,10 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
-// Vector-ALU kernels, used for GQA group sizes other than 4 (and for 4 with
-// KV4_FLAG_VALU_DECODE).
+// Vector-ALU kernels, used for q/kv ratio 8 of the integer path and the BF16
+// kind (and for every ratio with KV4_FLAG_VALU_DECODE).  Ratios 1 and 2 run on
+// the matrix-core kernels of ratio 4, whose rows past the ratio carry q = 0
+// and are not written; ratio 8 of the mixed kind on decode_kv4_mfma8_kernel.
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
@@ -225,7 +254,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     if (a.pool_chunks > 0) hipLaunchKernelGGL(kv4::pool_reset_kernel, dim3(1), dim3(64), 0, s, a.ctr);
     if (a.g.intp) {
         dim3 grid((unsigned)a.waves);
-        if (a.g.gqa == 4 && !a.g.valu) {
+        if (a.g.gqa <= 4 && !a.g.valu) {
             switch (a.g.G) {
                 case 32:
                     if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<32, true>), grid, dim3(64), 0, s, a);
@@ -250,7 +279,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
         }
         return;
     }
-    if (a.g.gqa == 4 && !a.g.valu) {
+    if (a.g.gqa <= 4 && !a.g.valu) {
         dim3 grid((unsigned)a.waves);
         if (a.g.kind == KV4_KIND_MIXED) {
             switch (a.g.G) {
@@ -271,6 +300,24 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
             hipLaunchKernelGGL(kv4::decode_kv8_mfma_kernel, grid, dim3(64), 0, s, a);
         } else {
             hipLaunchKernelGGL(kv4::decode_bf16_mfma_kernel, grid, dim3(64), 0, s, a);
+        }
+        return;
+    }
+    if (a.g.gqa == 8 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {
+        dim3 grid((unsigned)a.waves);
+        switch (a.g.G) {
+            case 32:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<32, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<32, false>), grid, dim3(64), 0, s, a);
+                break;
+            case 64:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<64, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<64, false>), grid, dim3(64), 0, s, a);
+                break;
+            default:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<128, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma8_kernel<128, false>), grid, dim3(64), 0, s, a);
+                break;
         }
         return;
     }

@@ -296,7 +296,10 @@ __device__ __forceinline__ uint2 split_f16(float x, float y)
     return make_uint2(hi, pack_f16(x - h2f(hi, 0), y - h2f(hi, 1)));
 }
 
-template <int G, bool ROT>
+// NH = 2 (q/kv ratio 8): the wave runs the tile's QK, softmax and PV for q
+// heads 0-3 and then 4-7 of the group on the same staged K/V tile, each half
+// with its own query operands, softmax state and accumulators.
+template <int G, bool ROT, int NH = 1>
 __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                               float* rec, Pace& pace)
 {
@@ -318,84 +321,101 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     // exact in fp16 (a power-of-two scale; a rotated query is rounded to its
     // 11 significant bits), and the k-slots facing codes stored at 16 times
     // their value get a further 2^-4.
-    u32x4_t aqv;                                 // scaled q of head jq on block gq (k-slot pairs)
-    u32x4_t aql = {0u, 0u, 0u, 0u};              // its low half (rotated queries only)
-    float sq_part;
-    int sc;                                      // scale exponent of head jq
-    {
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
-        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-        if constexpr (ROT) {
-            // query into the keys' basis: channel bits 3-4 are lane bits 4-5
-            // (kb), bits 5-6 lane bits 0-1 (gq)
-            wht_local(q);
-            wht_lanes(q, 16);
-            wht_lanes(q, 32);
-            wht_lanes(q, 1);
-            wht_lanes(q, 2);
-            wht_scale(q);
-        }
-        float amax = 0.f;
+    u32x4_t aqv[NH];                             // scaled q of head jq on block gq (k-slot pairs)
+    u32x4_t aql[NH];                             // its low half (rotated queries only)
+    float sqm[NH][NG];                           // m-term factors and score factor of head kb
+    float c2[NH];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
-        amax = fmaxf(amax, dpp<0xB1>(amax));                 // over the quad (blocks) ...
-        amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));       // ... and the rows: head jq
-        sc = 15 - __builtin_amdgcn_frexp_expf(amax);
-        // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen_k16() pairs codes
-        if constexpr (ROT) {
-            const uint2 s0 = split_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
-            const uint2 s1 = split_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
-            const uint2 s2 = split_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
-            const uint2 s3 = split_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
-            aqv = u32x4_t{s0.x, s1.x, s2.x, s3.x};
-            aql = u32x4_t{s0.y, s1.y, s2.y, s3.y};
-        } else {
-            aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
-            aqv[1] = pack_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
-            aqv[2] = pack_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
-            aqv[3] = pack_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+    for (int hf = 0; hf < NH; ++hf) {
+        float sq_part;
+        int sc;                                      // scale exponent of head jq
+        aql[hf] = u32x4_t{0u, 0u, 0u, 0u};
+        {
+            // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+            // layout) carry q = 0; their results are not written
+            const int jh = 4 * hf + jq;
+            const bool qreal = jh < g.gqa;
+            const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
+            uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
+            if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
+            float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                          bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+            if constexpr (ROT) {
+                // query into the keys' basis: channel bits 3-4 are lane bits 4-5
+                // (kb), bits 5-6 lane bits 0-1 (gq)
+                wht_local(q);
+                wht_lanes(q, 16);
+                wht_lanes(q, 32);
+                wht_lanes(q, 1);
+                wht_lanes(q, 2);
+                wht_scale(q);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
+            amax = fmaxf(amax, dpp<0xB1>(amax));                 // over the quad (blocks) ...
+            amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));       // ... and the rows: head jq
+            sc = 15 - __builtin_amdgcn_frexp_expf(amax);
+            // k-slot pairs (c, c + 4) of channels 32 gq + 8 kb + c, as widen_k16() pairs codes
+            if constexpr (ROT) {
+                const uint2 s0 = split_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
+                const uint2 s1 = split_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
+                const uint2 s2 = split_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
+                const uint2 s3 = split_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+                aqv[hf] = u32x4_t{s0.x, s1.x, s2.x, s3.x};
+                aql[hf] = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+            } else {
+                aqv[hf][0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[4], sc));
+                aqv[hf][1] = pack_f16(ldexpf(q[1], sc - 4), ldexpf(q[5], sc - 4));
+                aqv[hf][2] = pack_f16(ldexpf(q[2], sc), ldexpf(q[6], sc));
+                aqv[hf][3] = pack_f16(ldexpf(q[3], sc - 4), ldexpf(q[7], sc - 4));
+            }
+            // the sum of q as the matrix core sees it, so that the offset term
+            // m sum(q) matches the products
+            auto opsum = [&](const u32x4_t& o, int i, int j) {
+                return (h2f(o[i], 0) + h2f(o[i], 1)) + (h2f(o[j], 0) + h2f(o[j], 1));
+            };
+            float e0 = opsum(aqv[hf], 0, 2), e1 = opsum(aqv[hf], 1, 3);
+            if constexpr (ROT) {
+                e0 += opsum(aql[hf], 0, 2);
+                e1 += opsum(aql[hf], 1, 3);
+            }
+            sq_part = ldexpf(fmaf(16.0f, e1, e0), -sc);
         }
-        // the sum of q as the matrix core sees it, so that the offset term
-        // m sum(q) matches the products
-        auto opsum = [&](const u32x4_t& o, int i, int j) {
-            return (h2f(o[i], 0) + h2f(o[i], 1)) + (h2f(o[j], 0) + h2f(o[j], 1));
-        };
-        float e0 = opsum(aqv, 0, 2), e1 = opsum(aqv, 1, 3);
-        if constexpr (ROT) {
-            e0 += opsum(aql, 0, 2);
-            e1 += opsum(aql, 1, 3);
+        // sum of q over block gq of head jq (the four lanes of A row n16), then
+        // the sums of head kb over each block r, for this lane's D rows
+        const float sq_blk = rows_sum(sq_part);
+        float sqr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sqr[r] = __shfl(sq_blk, 4 * kb + r);
+        // D rows of this lane belong to head kb: its products come scaled by
+        // 2^(sc_kb - 24); the offset term is scaled alike and the score factor
+        // undoes it.
+        const int sc_d = __shfl(sc, 4 * kb) - 24;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            sqm[hf][gg] = 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if ((32 * r) / G == gg) sqm[hf][gg] += sqr[r];
+            sqm[hf][gg] = ldexpf(sqm[hf][gg], sc_d);
         }
-        sq_part = ldexpf(fmaf(16.0f, e1, e0), -sc);
+        c2[hf] = ldexpf(a.scale2, -sc_d);
     }
-    // sum of q over block gq of head jq (the four lanes of A row n16), then
-    // the sums of head kb over each block r, for this lane's D rows
-    const float sq_blk = rows_sum(sq_part);
-    float sqr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sqr[r] = __shfl(sq_blk, 4 * kb + r);
-    // D rows of this lane belong to head kb: its products come scaled by
-    // 2^(sc_kb - 24); the offset term is scaled alike and the score factor
-    // undoes it.
-    const int sc_d = __shfl(sc, 4 * kb) - 24;
-    float sqm[NG];
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-        sqm[gg] = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if ((32 * r) / G == gg) sqm[gg] += sqr[r];
-        sqm[gg] = ldexpf(sqm[gg], sc_d);
-    }
-    const float c2 = ldexpf(a.scale2, -sc_d);
 
-    // E[h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
-    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    float accm[NG];
+    // E[hf][h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
+    f32x4_t E[NH][2];
+    float accm[NH][NG];
+    float m_sh[NH], l_run[NH];                   // m_sh = m_ref - kPScale
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) accm[gg] = 0.f;
-    float m_sh = -INFINITY, l_run = 0.f;        // m_sh = m_ref - kPScale
+    for (int hf = 0; hf < NH; ++hf) {
+        E[hf][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        E[hf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) accm[hf][gg] = 0.f;
+        m_sh[hf] = -INFINITY;
+        l_run[hf] = 0.f;
+    }
 
     // fixed per-lane offsets inside a page block
     constexpr int MB = 128 * NG;                 // metadata bytes per page
@@ -422,7 +442,7 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
     };
     const bool upper = kb >> 1;                  // lanes 32-63: PV tokens and metadata chunk in page 2
 
-    __shared__ __attribute__((aligned(16))) float pbuf[4][32];
+    __shared__ __attribute__((aligned(16))) float pbuf[NH][4][32];
     __shared__ __attribute__((aligned(16))) uint8_t mbuf[2 * 512];
     __shared__ uint4 stage[4][64];               // K codes of both pages, V codes, per lane
 
@@ -461,142 +481,146 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             }
         }
 
-        // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
-        f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
-        const uint32_t k0w[4] = {kc0.x, kc0.y, kc0.z, kc0.w};
-        const uint32_t k1w[4] = {kc1.x, kc1.y, kc1.z, kc1.w};
+        // ---- per half of the q heads (one half below ratio 8): QK, softmax, PV
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            // block-diagonal A: only rows of block bb (lanes with lane % 4 == bb) carry q
-            const uint64_t rows = 0x1111111111111111ull << bb;
-            const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
-                               keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-            const u32x4_t B0 = widen_k16(k0w[bb]), B1 = widen_k16(k1w[bb]);
-            D0 = mfma_f16(A, B0, D0);
-            D1 = mfma_f16(A, B1, D1);
-            if constexpr (ROT) {
-                const u32x4_t Al = {keep_lanes(aql[0], rows), keep_lanes(aql[1], rows),
-                                    keep_lanes(aql[2], rows), keep_lanes(aql[3], rows)};
-                D0 = mfma_f16(Al, B0, D0);
-                D1 = mfma_f16(Al, B1, D1);
+        for (int hf = 0; hf < NH; ++hf) {
+            // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
+            f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
+            const uint32_t k0w[4] = {kc0.x, kc0.y, kc0.z, kc0.w};
+            const uint32_t k1w[4] = {kc1.x, kc1.y, kc1.z, kc1.w};
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                // block-diagonal A: only rows of block bb (lanes with lane % 4 == bb) carry q
+                const uint64_t rows = 0x1111111111111111ull << bb;
+                const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
+                                   keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
+                const u32x4_t B0 = widen_k16(k0w[bb]), B1 = widen_k16(k1w[bb]);
+                D0 = mfma_f16(A, B0, D0);
+                D1 = mfma_f16(A, B1, D1);
+                if constexpr (ROT) {
+                    const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
+                                        keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
+                    D0 = mfma_f16(Al, B0, D0);
+                    D1 = mfma_f16(Al, B1, D1);
+                }
             }
-        }
-        float x0 = 0.f, x1 = 0.f;
+            float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int gg = (32 * r) / G;
-            x0 = fmaf(h2f(kdm[0][gg], 0), D0[r], x0);
-            x1 = fmaf(h2f(kdm[1][gg], 0), D1[r], x1);
-        }
-#pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-            x0 = fmaf(h2f(kdm[0][gg], 1), sqm[gg], x0);
-            x1 = fmaf(h2f(kdm[1][gg], 1), sqm[gg], x1);
-        }
-        float s0 = x0 * c2, s1 = x1 * c2;
-        const int tok0 = 32 * tl + n16;
-        const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
-        const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
-        if constexpr (!full) {
-            s0 = ok0 ? s0 : -INFINITY;
-            s1 = ok1 ? s1 : -INFINITY;
-        }
-        const float mx = row16_max(fmaxf(s0, s1));
-
-        // ---- raise the reference maximum of head kb when the tile exceeds it
-        // by more than kSlack.  The branch is wave-uniform and rarely taken;
-        // lanes that do not grow scale by exactly 1.
-        {
-            const bool grow = mx > m_sh + (kPScale + kSlack);
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx - kPScale : m_sh;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
-                m_sh = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
-            }
-        }
-
-        // ---- probabilities of head kb for tokens n16 and 16 + n16
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
-        l_run += p0 + p1;
-        {
-            const uint8_t* v0p = &mbuf[m_vm];
-            const uint8_t* v1p = &mbuf[MB + m_vm];
-            uint32_t vm0[(NG + 1) / 2], vm1[(NG + 1) / 2];
-            if constexpr (NG == 4) {
-                const uint2 u0 = *reinterpret_cast<const uint2*>(v0p);
-                const uint2 u1 = *reinterpret_cast<const uint2*>(v1p);
-                vm0[0] = u0.x; vm0[1] = u0.y; vm1[0] = u1.x; vm1[1] = u1.y;
-            } else if constexpr (NG == 2) {
-                vm0[0] = *reinterpret_cast<const uint32_t*>(v0p);
-                vm1[0] = *reinterpret_cast<const uint32_t*>(v1p);
-            } else {
-                vm0[0] = *reinterpret_cast<const uint16_t*>(v0p);
-                vm1[0] = *reinterpret_cast<const uint16_t*>(v1p);
+            for (int r = 0; r < 4; ++r) {
+                const int gg = (32 * r) / G;
+                x0 = fmaf(h2f(kdm[0][gg], 0), D0[r], x0);
+                x1 = fmaf(h2f(kdm[1][gg], 0), D1[r], x1);
             }
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
-                if constexpr (full) {
-                    accm[gg] = fmaf(p0, h2f(vm0[gg >> 1], gg & 1), fmaf(p1, h2f(vm1[gg >> 1], gg & 1), accm[gg]));
-                } else {
-                    // never-written slots may hold NaN: select, do not multiply
-                    const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
-                    const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
-                    accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+                x0 = fmaf(h2f(kdm[0][gg], 1), sqm[hf][gg], x0);
+                x1 = fmaf(h2f(kdm[1][gg], 1), sqm[hf][gg], x1);
+            }
+            float s0 = x0 * c2[hf], s1 = x1 * c2[hf];
+            const int tok0 = 32 * tl + n16;
+            const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
+            const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
+            if constexpr (!full) {
+                s0 = ok0 ? s0 : -INFINITY;
+                s1 = ok1 ? s1 : -INFINITY;
+            }
+            const float mx = row16_max(fmaxf(s0, s1));
+
+            // ---- raise the reference maximum of head kb when the tile exceeds it
+            // by more than kSlack.  The branch is wave-uniform and rarely taken;
+            // lanes that do not grow scale by exactly 1.
+            {
+                const bool grow = mx > m_sh[hf] + (kPScale + kSlack);
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx - kPScale : m_sh[hf];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh[hf] - m_new) : 1.0f;
+                    m_sh[hf] = m_new;
+                    l_run[hf] *= alpha;
+#pragma unroll
+                    for (int gg = 0; gg < NG; ++gg) accm[hf][gg] *= alpha;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) E[hf][hh] *= alpha;
                 }
             }
-        }
-        // A work item is one wave (64-thread workgroup) and one wave's LDS
-        // accesses execute in issue order, so the reads below see these
-        // writes; the barrier only keeps the compiler from reordering them.
-        pbuf[kb][n16] = p0;
-        pbuf[kb][16 + n16] = p1;
-        __builtin_amdgcn_wave_barrier();
-        const float4 pa = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb]);
-        const float4 pb = *reinterpret_cast<const float4*>(&pbuf[jq][8 * kb + 4]);
-        const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vd]);
 
-        // ---- PV: A = w = p Delta_V of head jq, block gq, tokens 8 kb + e
-        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t vdw[4] = {vd.x, vd.y, vd.z, vd.w};
-        float wv[8];
+            // ---- probabilities of head kb for tokens n16 and 16 + n16
+            const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh[hf]);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh[hf]);
+            l_run[hf] += p0 + p1;
+            {
+                const uint8_t* v0p = &mbuf[m_vm];
+                const uint8_t* v1p = &mbuf[MB + m_vm];
+                uint32_t vm0[(NG + 1) / 2], vm1[(NG + 1) / 2];
+                if constexpr (NG == 4) {
+                    const uint2 u0 = *reinterpret_cast<const uint2*>(v0p);
+                    const uint2 u1 = *reinterpret_cast<const uint2*>(v1p);
+                    vm0[0] = u0.x; vm0[1] = u0.y; vm1[0] = u1.x; vm1[1] = u1.y;
+                } else if constexpr (NG == 2) {
+                    vm0[0] = *reinterpret_cast<const uint32_t*>(v0p);
+                    vm1[0] = *reinterpret_cast<const uint32_t*>(v1p);
+                } else {
+                    vm0[0] = *reinterpret_cast<const uint16_t*>(v0p);
+                    vm1[0] = *reinterpret_cast<const uint16_t*>(v1p);
+                }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wv[e] = fmaf(pr[e], h2f(vdw[e >> 1], e & 1), 0.0f);
-        if constexpr (!full) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tok = 32 * tl + 8 * kb + e;
-                wv[e] = (tok >= t_lo && tok < t_hi) ? wv[e] : 0.0f;
+                for (int gg = 0; gg < NG; ++gg) {
+                    if constexpr (full) {
+                        accm[hf][gg] = fmaf(p0, h2f(vm0[gg >> 1], gg & 1), fmaf(p1, h2f(vm1[gg >> 1], gg & 1), accm[hf][gg]));
+                    } else {
+                        // never-written slots may hold NaN: select, do not multiply
+                        const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
+                        const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
+                        accm[hf][gg] = fmaf(p0, v0, fmaf(p1, v1, accm[hf][gg]));
+                    }
+                }
             }
-        }
-        u32x4_t ahi, alo;
+            // A work item is one wave (64-thread workgroup) and one wave's LDS
+            // accesses execute in issue order, so the reads below see these
+            // writes; the barrier only keeps the compiler from reordering them.
+            pbuf[hf][kb][n16] = p0;
+            pbuf[hf][kb][16 + n16] = p1;
+            __builtin_amdgcn_wave_barrier();
+            const float4 pa = *reinterpret_cast<const float4*>(&pbuf[hf][jq][8 * kb]);
+            const float4 pb = *reinterpret_cast<const float4*>(&pbuf[hf][jq][8 * kb + 4]);
+            const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vd]);
+
+            // ---- PV: A = w = p Delta_V of head jq, block gq, tokens 8 kb + e
+            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            const uint32_t vdw[4] = {vd.x, vd.y, vd.z, vd.w};
+            float wv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hw, lw;
-            split_bf16(wv[i], wv[i + 4], hw, lw);
-            ahi[i] = hw;
-            alo[i] = lw;
-        }
-        const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
-        const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
+            for (int e = 0; e < 8; ++e) wv[e] = fmaf(pr[e], h2f(vdw[e >> 1], e & 1), 0.0f);
+            if constexpr (!full) {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            // rows of block blk only: each accumulator row gathers its own block
-            const uint64_t rows = 0x1111111111111111ull << blk;
-            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
-            const u32x4_t b0 = widen_v(vcw[2 * blk]), b1 = widen_v(vcw[2 * blk + 1]);
-            E[0] = mfma_bf16(bh, b0, E[0]);
-            E[1] = mfma_bf16(bh, b1, E[1]);
-            E[0] = mfma_bf16(bl, b0, E[0]);
-            E[1] = mfma_bf16(bl, b1, E[1]);
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = 32 * tl + 8 * kb + e;
+                    wv[e] = (tok >= t_lo && tok < t_hi) ? wv[e] : 0.0f;
+                }
+            }
+            u32x4_t ahi, alo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hw, lw;
+                split_bf16(wv[i], wv[i + 4], hw, lw);
+                ahi[i] = hw;
+                alo[i] = lw;
+            }
+            const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
+            const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                // rows of block blk only: each accumulator row gathers its own block
+                const uint64_t rows = 0x1111111111111111ull << blk;
+                const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                    keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+                const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                    keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+                const u32x4_t b0 = widen_v(vcw[2 * blk]), b1 = widen_v(vcw[2 * blk + 1]);
+                E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
+                E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+            }
         }
     };
 
@@ -630,18 +654,22 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
         if (tl < tile_end) advance(tl, std::false_type{});
     }
 
-    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
-    const float l = row16_sum(l_run);
+    // ---- epilogue: lane l holds head 4 hf + kb, channels 32 r + 16 h + n16 in E[hf][h][r]
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
-    const float inv = 1.0f / l;
-    float* dst = rec + kb * (g.d + kPartPad);
+    for (int hf = 0; hf < NH; ++hf) {
+        const float l = row16_sum(l_run[hf]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        dst[32 * r + n16] = (ldexpf(E[0][r], 133) + accm[(32 * r) / G]) * inv;
-        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) + accm[(32 * r) / G]) * inv;
+        for (int gg = 0; gg < NG; ++gg) accm[hf][gg] = row16_sum(accm[hf][gg]);
+        const float inv = 1.0f / l;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dst[32 * r + n16] = (ldexpf(E[hf][0][r], 133) + accm[hf][(32 * r) / G]) * inv;
+            dst[32 * r + 16 + n16] = (ldexpf(E[hf][1][r], 133) + accm[hf][(32 * r) / G]) * inv;
+        }
+        if (n16 == 0) dst[g.d] = m_sh[hf] + log2f(l);
     }
-    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
 // Four int8 codes per word (byte i = code i) -> bf16 or fp16 pairs whose bit
@@ -677,7 +705,9 @@ __device__ __forceinline__ u32x4_t widen_i8(uint32_t w0, uint32_t w1)
 //     block r's MFMAs keep the A rows of block r and cover channels 32 r +
 //     16 h + n16 in E[h][r].
 // ---------------------------------------------------------------------------
-template <bool ROT>
+// NH = 2 (q/kv ratio 8): q heads 0-3 and 4-7 of the group in turn on each
+// tile's loads, as in the INT4 item.
+template <bool ROT, int NH = 1>
 __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h, float* rec)
 {
     const Geo& g = a.g;
@@ -692,62 +722,79 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
     const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
     const uint16_t* vsc = ksc + g.SR32;
 
-    // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
-    u32x4_t aqv;
-    u32x4_t aql = {0u, 0u, 0u, 0u};              // low half of a rotated query
-    int sc;
-    {
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
-        float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-        if constexpr (ROT) {
-            // channel bits 3-4 are lane bits 0-1 (gq), bits 5-6 lane bits 4-5 (kb)
-            wht_local(q);
-            wht_lanes(q, 1);
-            wht_lanes(q, 2);
-            wht_lanes(q, 16);
-            wht_lanes(q, 32);
-            wht_scale(q);
-        }
-        float amax = 0.f;
+    u32x4_t aqv[NH];
+    u32x4_t aql[NH];                             // low half of a rotated query
+    f32x4_t dinit[NH];
+    float c2[NH];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
-        amax = fmaxf(amax, dpp<0xB1>(amax));
-        amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
-        sc = 15 - __builtin_amdgcn_frexp_expf(amax);
-        // k-slot pairs as widen_i8 pairs codes: (0, 2), (1, 3), (4, 6), (5, 7)
-        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+    for (int hf = 0; hf < NH; ++hf) {
+        aql[hf] = u32x4_t{0u, 0u, 0u, 0u};
+        // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
+        int sc;
+        {
+            // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+            // layout) carry q = 0; their results are not written
+            const int jh = 4 * hf + jq;
+            const bool qreal = jh < g.gqa;
+            const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
+            uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+            if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
+            float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                          bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
             if constexpr (ROT) {
-                const uint2 hl = split_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
-                aqv[i] = hl.x;
-                aql[i] = hl.y;
-            } else {
-                aqv[i] = pack_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
+                // channel bits 3-4 are lane bits 0-1 (gq), bits 5-6 lane bits 4-5 (kb)
+                wht_local(q);
+                wht_lanes(q, 1);
+                wht_lanes(q, 2);
+                wht_lanes(q, 16);
+                wht_lanes(q, 32);
+                wht_scale(q);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(q[c]));
+            amax = fmaxf(amax, dpp<0xB1>(amax));
+            amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
+            sc = 15 - __builtin_amdgcn_frexp_expf(amax);
+            // k-slot pairs as widen_i8 pairs codes: (0, 2), (1, 3), (4, 6), (5, 7)
+            constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (ROT) {
+                    const uint2 hl = split_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
+                    aqv[hf][i] = hl.x;
+                    aql[hf][i] = hl.y;
+                } else {
+                    aqv[hf][i] = pack_f16(ldexpf(q[pe[i][0]], sc), ldexpf(q[pe[i][1]], sc));
+                }
             }
         }
-    }
-    float qpart = 0.f;                           // the sum of exactly the operand used
+        float qpart = 0.f;                           // the sum of exactly the operand used
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
-        if constexpr (ROT) qpart += h2f(aql[i], 0) + h2f(aql[i], 1);
-    }
-    // sum of the operand over MFMA block gq's 32 k-slots (row n16), then per D
-    // row (head kb, block r): D starts at -128 * 2^-24 * that sum
-    const float qblk = rows_sum(qpart);
-    f32x4_t dinit;
+        for (int i = 0; i < 4; ++i) {
+            qpart += h2f(aqv[hf][i], 0) + h2f(aqv[hf][i], 1);
+            if constexpr (ROT) qpart += h2f(aql[hf][i], 0) + h2f(aql[hf][i], 1);
+        }
+        // sum of the operand over MFMA block gq's 32 k-slots (row n16), then per D
+        // row (head kb, block r): D starts at -128 * 2^-24 * that sum
+        const float qblk = rows_sum(qpart);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dinit[r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
-    const float c2 = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
+        for (int r = 0; r < 4; ++r) dinit[hf][r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
+        c2[hf] = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
+    }
 
-    // E[h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
-    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
-    float m_sh = -INFINITY, l_run = 0.f;
-    __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
+    // E[hf][h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
+    f32x4_t E[NH][2], W[NH];
+    float m_sh[NH], l_run[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        E[hf][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        E[hf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        W[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_sh[hf] = -INFINITY;
+        l_run[hf] = 0.f;
+    }
+    __shared__ __attribute__((aligned(16))) float pbuf8[NH][4][32];
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
 
     for (int e0 = 0; e0 < n8; e0 += 32) {
@@ -767,104 +814,111 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
         const float sk1 = half_bits_to_float(ksc[e0 + 16 + n16]);
         const uint4 svp = *reinterpret_cast<const uint4*>(vsc + e0 + 8 * kb);
 
-        // ---- QK
-        f32x4_t D0 = dinit, D1 = dinit;
-        const uint32_t kw0[8] = {k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w};
-        const uint32_t kw1[8] = {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w};
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const uint64_t rows = 0x1111111111111111ull << bb;
-            const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
-                               keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-            const u32x4_t B0 = widen_i8(kw0[2 * bb], kw0[2 * bb + 1]);
-            const u32x4_t B1 = widen_i8(kw1[2 * bb], kw1[2 * bb + 1]);
-            D0 = mfma_f16(A, B0, D0);
-            D1 = mfma_f16(A, B1, D1);
-            if constexpr (ROT) {
-                const u32x4_t Al = {keep_lanes(aql[0], rows), keep_lanes(aql[1], rows),
-                                    keep_lanes(aql[2], rows), keep_lanes(aql[3], rows)};
-                D0 = mfma_f16(Al, B0, D0);
-                D1 = mfma_f16(Al, B1, D1);
-            }
-        }
-        const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
-        float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
-        float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2;
-        s0 = ok0 ? s0 : -INFINITY;
-        s1 = ok1 ? s1 : -INFINITY;
-        const float mx = row16_max(fmaxf(s0, s1));
-        {
-            const bool grow = mx > m_sh + (kPScale + kSlack);
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx - kPScale : m_sh;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
-                m_sh = m_new;
-                l_run *= alpha;
+        for (int hf = 0; hf < NH; ++hf) {
+            // ---- QK
+            f32x4_t D0 = dinit[hf], D1 = dinit[hf];
+            const uint32_t kw0[8] = {k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w};
+            const uint32_t kw1[8] = {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w};
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
-                W *= alpha;
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint64_t rows = 0x1111111111111111ull << bb;
+                const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
+                                   keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
+                const u32x4_t B0 = widen_i8(kw0[2 * bb], kw0[2 * bb + 1]);
+                const u32x4_t B1 = widen_i8(kw1[2 * bb], kw1[2 * bb + 1]);
+                D0 = mfma_f16(A, B0, D0);
+                D1 = mfma_f16(A, B1, D1);
+                if constexpr (ROT) {
+                    const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
+                                        keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
+                    D0 = mfma_f16(Al, B0, D0);
+                    D1 = mfma_f16(Al, B1, D1);
+                }
             }
-        }
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
-        l_run += p0 + p1;
-        pbuf8[kb][n16] = p0;
-        pbuf8[kb][16 + n16] = p1;
-        __builtin_amdgcn_wave_barrier();
-        const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb]);
-        const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb + 4]);
+            const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
+            float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2[hf];
+            float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2[hf];
+            s0 = ok0 ? s0 : -INFINITY;
+            s1 = ok1 ? s1 : -INFINITY;
+            const float mx = row16_max(fmaxf(s0, s1));
+            {
+                const bool grow = mx > m_sh[hf] + (kPScale + kSlack);
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx - kPScale : m_sh[hf];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh[hf] - m_new) : 1.0f;
+                    m_sh[hf] = m_new;
+                    l_run[hf] *= alpha;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) E[hf][hh] *= alpha;
+                    W[hf] *= alpha;
+                }
+            }
+            const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh[hf]);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh[hf]);
+            l_run[hf] += p0 + p1;
+            pbuf8[hf][kb][n16] = p0;
+            pbuf8[hf][kb][16 + n16] = p1;
+            __builtin_amdgcn_wave_barrier();
+            const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb]);
+            const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb + 4]);
 
-        // ---- PV: w = p' s_V of head jq, entries e0 + 8 kb + e
-        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
-        float wv[8];
+            // ---- PV: w = p' s_V of head jq, entries e0 + 8 kb + e
+            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
+            float wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // entries past the end may hold garbage scales: select, do not multiply
-            const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
-            wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
-        }
-        u32x4_t ahi, alo;
-        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+            for (int e = 0; e < 8; ++e) {
+                // entries past the end may hold garbage scales: select, do not multiply
+                const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
+                wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
+            }
+            u32x4_t ahi, alo;
+            constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hw, lw;
-            split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
-            ahi[i] = hw;
-            alo[i] = lw;
-        }
-        const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hw, lw;
+                split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
+                ahi[i] = hw;
+                alo[i] = lw;
+            }
+            const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                     v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint64_t rows = 0x1111111111111111ull << blk;
-            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
-            const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
-            const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
-            E[0] = mfma_bf16(bh, b0, E[0]);
-            E[1] = mfma_bf16(bh, b1, E[1]);
-            E[0] = mfma_bf16(bl, b0, E[0]);
-            E[1] = mfma_bf16(bl, b1, E[1]);
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint64_t rows = 0x1111111111111111ull << blk;
+                const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                    keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+                const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                    keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+                const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
+                const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
+                E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
+                E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+            }
+            W[hf] = mfma_bf16(ahi, ones, W[hf]);
+            W[hf] = mfma_bf16(alo, ones, W[hf]);
         }
-        W = mfma_bf16(ahi, ones, W);
-        W = mfma_bf16(alo, ones, W);
         __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
+    // ---- epilogue: lane l holds head 4 hf + kb, channels 32 r + 16 h + n16 in E[hf][h][r]
     // (every block row of W carries the same sum; row 0 is used)
-    const float l = row16_sum(l_run);
-    const float inv = 1.0f / l;
-    float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        dst[32 * r + n16] = (ldexpf(E[0][r], 133) - 128.0f * W[0]) * inv;
-        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) - 128.0f * W[0]) * inv;
+    for (int hf = 0; hf < NH; ++hf) {
+        const float l = row16_sum(l_run[hf]);
+        const float inv = 1.0f / l;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dst[32 * r + n16] = (ldexpf(E[hf][0][r], 133) - 128.0f * W[hf][0]) * inv;
+            dst[32 * r + 16 + n16] = (ldexpf(E[hf][1][r], 133) - 128.0f * W[hf][0]) * inv;
+        }
+        if (n16 == 0) dst[g.d] = m_sh[hf] + log2f(l);
     }
-    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -899,8 +953,12 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
     u32x4_t aqv;
     int sc;
     {
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+        // layout) carry q = 0; their results are not written
+        const bool qreal = jq < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
                             bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
         float amax = 0.f;
@@ -1073,6 +1131,7 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
     // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
     const float l = row16_sum(l_run);
     const float inv = 1.0f / l;
+    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1103,13 +1162,16 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
     const uint8_t* hbase = a.pages + (int64_t)a.layer * g.layer_pages + (int64_t)h * g.pb;
     const int64_t page_stride = (int64_t)g.Hkv * g.pb;
 
-    const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
+    // columns of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+    // layout) carry q = 0; their results are not written
+    const bool qreal = jq < g.gqa;
+    const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
     u32x4_t bq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * i + 8 * kb);
         u32x4_t v = {u.x, u.y, u.z, u.w}, z = {0u, 0u, 0u, 0u};
-        bq[i] = gq == 0 ? v : z;
+        bq[i] = gq == 0 && qreal ? v : z;
     }
     const float c2 = a.scale2;
     f32x4_t O[8];
@@ -1195,6 +1257,7 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
     __syncthreads();
     const float lj = sh_l[kb];
     const float inv = 1.0f / lj;
+    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (O[s][0] + O[s][1]) * inv;
@@ -1211,6 +1274,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_kv4<G, ROT>(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// q/kv ratio 8 on the matrix core: the four-head layout twice per tile (q
+// heads 0-3, then 4-7) on one load of the tile.  The second half's operands
+// and softmax state need more registers: three waves per SIMD.
+template <int G, bool ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_kv4_mfma8_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT, 2>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_kv4<G, ROT, 2>(a, b, h, lo, hi, rec, pace);
                });
 }
 
@@ -1296,8 +1371,12 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
     float Qg[NG];                                // code sums of head kb per group
     float c2;                                    // score factor of head kb
     {
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
+        // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+        // layout) carry q = 0; their results are not written
+        const bool qreal = jq < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
+        if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
                       bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
         if constexpr (ROT) {
@@ -1561,6 +1640,7 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
 #pragma unroll
     for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
     const float inv = 1.0f / l;
+    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1594,8 +1674,12 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
     u32x4_t A1, A2;
     float c2;
     {
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * 4 + jq) * g.d;
-        const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
+        // layout) carry q = 0; their results are not written
+        const bool qreal = jq < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
+        if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
                       bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
         if constexpr (ROT) {
@@ -1724,6 +1808,7 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
     // (every block row of W carries the same sum; row 0 is used)
     const float l = row16_sum(l_run);
     const float inv = 1.0f / l;
+    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
     float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

@@ -199,6 +199,18 @@ def test_gqa_ratios(Hq, Hkv):
     _run_case(Hq, Hkv, 32, 4, 16, [0, 5, 19, 20, 21, 100, 257, 700], seed=Hq * 10 + Hkv)
 
 
+def test_ratio8_matrix_core():
+    """q/kv ratio 8 on the matrix core (two four-head halves per tile): group
+    sizes 32, 64 and 128, rotated keys, edge lengths around S + R, several
+    waves, and a 64 q / 8 kv layer with long contexts."""
+    edge = [0, 1, 3, 4, 5, 19, 20, 21, 67, 68, 69, 100, 257, 700, 2500]
+    for G, rotate, waves in ((32, False, 0), (64, False, 5), (128, False, 0), (32, True, 0), (128, True, 7)):
+        H.log(f"case ratio 8 Hq=16 Hkv=2 G={G} rotate={rotate} waves={waves}")
+        _run_case(16, 2, G, 4, 64, edge, seed=170 + G + rotate, rotate=rotate, waves=waves)
+    H.log("case ratio 8 Hq=64 Hkv=8 G=32, long contexts")
+    _run_case(64, 8, 32, 4, 128, [9000, 17, 4000, 131, 133], seed=178)
+
+
 def test_group_64_and_multi_layer():
     H.log("case G=64, 3 layers, layer 2")
     _run_case(8, 2, 64, 4, 32, [33, 150, 401], seed=77, layers=3, layer=2)
@@ -405,27 +417,34 @@ def test_append_extreme_values(G):
     H.log(f"  bytes bit-exact; outputs within the derived bar, worst error {worst:.2e} of max|v^|")
 
 
-def test_valu_decode_at_gqa4():
-    """KV4_FLAG_VALU_DECODE: at q/kv ratio 4 the decode runs on the vector-ALU
-    kernels, against the same oracle as the matrix-core ones (floating-point
-    and integer paths, rotated keys, G = 32 and 128, edge lengths)."""
+def test_valu_decode_flag():
+    """KV4_FLAG_VALU_DECODE: the decode runs on the vector-ALU kernels at every
+    q/kv ratio (without the flag the mixed kind runs on the matrix-core
+    kernels), against the same oracle (floating-point and integer paths,
+    rotated keys, G = 32 and 128, edge lengths, the BF16 kind)."""
     ctx = [0, 3, 4, 5, 19, 20, 21, 100, 257, 700, 2500]
-    for G, rotate in ((32, False), (128, False), (32, True)):
-        H.log(f"case vector-ALU decode at GQA 4, G={G} rotate={rotate}")
-        _run_case(8, 2, G, 4, 16, ctx, seed=140 + G, rotate=rotate, flags=kv4.KV4_FLAG_VALU_DECODE)
-    H.log("case vector-ALU decode at GQA 4, integer path")
-    _int_case(8, 2, 32, 4, 64, [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500], seed=150,
-              flags=kv4.KV4_FLAG_VALU_DECODE)
-    H.log("case vector-ALU decode at GQA 4, BF16 kind")
+    for Hq, Hkv, G, rotate in ((8, 2, 32, False), (8, 2, 128, False), (8, 2, 32, True), (4, 4, 32, False),
+                               (8, 4, 64, True), (16, 2, 32, False)):
+        H.log(f"case vector-ALU decode Hq={Hq} Hkv={Hkv} G={G} rotate={rotate}")
+        _run_case(Hq, Hkv, G, 4, 16, ctx, seed=140 + G + Hq + Hkv, rotate=rotate,
+                  flags=kv4.KV4_FLAG_VALU_DECODE)
+    ictx = [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500]
+    for Hq, Hkv in ((8, 2), (8, 8), (8, 4)):
+        H.log(f"case vector-ALU decode, integer path, Hq={Hq} Hkv={Hkv}")
+        _int_case(Hq, Hkv, 32, 4, 64, ictx, seed=150 + Hq + Hkv, flags=kv4.KV4_FLAG_VALU_DECODE)
     ctxb = np.array([0, 15, 16, 17, 300, 1000, 3000])
     n = ctxb + 1
-    cfg = W.scaled(W.CONFIGS["tiny"], seed=33, batch=len(ctxb), ctx_kind="fixed", ctx_fixed=tuple(ctxb))
-    ks, vs = W.all_kv_sources(cfg, 0, n)
-    q = W.queries(cfg, 0)
-    built = H.make_cache(8, 2, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, flags=kv4.KV4_FLAG_VALU_DECODE, seed=5)
-    H.build_from_sources(built, 0, ks, vs, ctxb)
-    out = H.decode(built, 0, q, n).cpu().numpy()
-    H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
+    for Hq, Hkv in ((8, 2), (8, 4)):
+        H.log(f"case vector-ALU decode, BF16 kind, Hq={Hq} Hkv={Hkv}")
+        cfg = W.scaled(W.CONFIGS["tiny"], seed=33, batch=len(ctxb), ctx_kind="fixed", ctx_fixed=tuple(ctxb),
+                       q_heads=Hq, kv_heads=Hkv)
+        ks, vs = W.all_kv_sources(cfg, 0, n)
+        q = W.queries(cfg, 0)
+        built = H.make_cache(Hq, Hkv, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, flags=kv4.KV4_FLAG_VALU_DECODE,
+                             seed=5)
+        H.build_from_sources(built, 0, ks, vs, ctxb)
+        out = H.decode(built, 0, q, n).cpu().numpy()
+        H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
 
 
 def test_bf16_comparator():
