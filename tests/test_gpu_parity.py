@@ -447,17 +447,19 @@ def test_valu_decode_flag():
         H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
 
 
-def test_bf16_comparator():
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 4), (4, 4)])
+def test_bf16_comparator(Hq, Hkv):
     """BF16 kind: pages hold the bf16 values exactly; output matches the
-    oracle's dense attention."""
-    Hq, Hkv = 8, 2
+    oracle's dense attention (q/kv ratios 4, 2 and 1, all on the matrix-core
+    kernel)."""
     ctx = np.array([0, 15, 16, 17, 300, 1000, 3000])
     n = ctx + 1
-    cfg = W.scaled(W.CONFIGS["tiny"], seed=31, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx))
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=31, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx),
+                   q_heads=Hq, kv_heads=Hkv)
     ks, vs = W.all_kv_sources(cfg, 0, n)
     q = W.queries(cfg, 0)
     for waves in (0, 3):
-        H.log(f"case bf16 comparator waves={waves}")
+        H.log(f"case bf16 comparator Hq={Hq} Hkv={Hkv} waves={waves}")
         built = H.make_cache(Hq, Hkv, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, waves=waves, seed=4)
         _fill_garbage(built)
         H.build_from_sources(built, 0, ks, vs, ctx)
