@@ -116,10 +116,10 @@ extern "C" {
  * Exception: a block whose largest w is at most 2^-100 gets u = 0 for all its
  * positions (its term sum_t p_t m^v_t stays).  w is measured in each kernel's
  * own units: with p_t = 2^(score_t - m_ref) against the running maximum m_ref
- * of the scores in the vector-ALU form (q/kv ratio 8, or any ratio with
- * KV4_FLAG_VALU_DECODE), and with p_t = 2^(score_t - m_ref + 48) against a
- * reference that trails the running maximum by at most 16 in the matrix-core
- * form (ratios 1, 2 and 4), scores in base 2.
+ * of the scores in the vector-ALU form (KV4_FLAG_VALU_DECODE), and with
+ * p_t = 2^(score_t - m_ref + 48) against a reference that trails the running
+ * maximum by at most 16 in the matrix-core form (every ratio otherwise),
+ * scores in base 2.
  * Either way the dropped terms sum to at most 8 * 15 * max w <= 120 * 2^-100
  * against a normaliser of at least 1 (vector ALU) or 2^32 (matrix core), so
  * every output differs from the rint rule by less than 2^-90; 255 / max w
@@ -129,9 +129,9 @@ extern "C" {
  * any q/kv head ratio of 1, 2, 4 or 8; the cache's bytes do not change. */
 #define KV4_FLAG_INT_PATH 0x2
 /* KV4_FLAG_VALU_DECODE: the decode runs on the vector-ALU kernels at every q/kv
- * head ratio (otherwise ratios 1, 2 and 4 run on the matrix-core kernels and
- * ratio 8 on the vector ALU), with the same partition, arithmetic definitions
- * and tolerance.  A measurement point for the choice of the matrix core (no
+ * head ratio (otherwise the mixed kind runs on the matrix-core kernels at every
+ * ratio, the BF16 kind at ratios 1, 2 and 4), with the same partition,
+ * arithmetic definitions and tolerance.  A measurement point for the choice of the matrix core (no
  * passage of the pages behind it).  Mixed and BF16 kinds (KV4_ERR_UNSUPPORTED
  * for KV8). */
 #define KV4_FLAG_VALU_DECODE 0x4
@@ -160,10 +160,11 @@ typedef struct kv4_cache_desc {
     int32_t num_waves;          /* waves (one-wave workgroups) of the balanced decode
                                    partition; 0 = 16 per compute unit of the
                                    current device (when the decode runs on a
-                                   vector-ALU kernel -- q/kv head ratio 8, or
-                                   KV4_FLAG_VALU_DECODE -- as many per compute
-                                   unit as that kernel keeps resident, at most
-                                   16), else 1 .. 65536 */
+                                   kernel that keeps fewer resident -- the
+                                   vector-ALU kernels, and the matrix-core
+                                   kernels of q/kv ratio 8 -- as many per
+                                   compute unit as that kernel keeps resident,
+                                   at most 16), else 1 .. 65536 */
     int32_t pool_chunks;        /* most chunks of the decode's dynamic pool: 0 = no
                                    pool (the default), else a power of two in
                                    8 .. 65536 */

@@ -136,11 +136,25 @@ int valu_waves_per_cu(const kv4_cache_desc& d, int gqa)
 }
 
 // Resident waves per compute unit of the ratio-8 matrix-core kernel of the
-// cache's group size and key basis.
+// cache's path, group size and key basis.
 int mfma8_waves_per_cu(const kv4_cache_desc& d)
 {
     static std::atomic<int> known[3][2];
+    static std::atomic<int> known_int[3][2];
     const bool rot = (d.flags & KV4_FLAG_ROTATE_K) != 0;
+    if (d.flags & KV4_FLAG_INT_PATH) {
+        switch (d.group_size) {
+            case 32:
+                return rot ? resident_waves(kv4::decode_int_mfma8_kernel<32, true>, known_int[0][1])
+                           : resident_waves(kv4::decode_int_mfma8_kernel<32, false>, known_int[0][0]);
+            case 64:
+                return rot ? resident_waves(kv4::decode_int_mfma8_kernel<64, true>, known_int[1][1])
+                           : resident_waves(kv4::decode_int_mfma8_kernel<64, false>, known_int[1][0]);
+            default:
+                return rot ? resident_waves(kv4::decode_int_mfma8_kernel<128, true>, known_int[2][1])
+                           : resident_waves(kv4::decode_int_mfma8_kernel<128, false>, known_int[2][0]);
+        }
+    }
     switch (d.group_size) {
         case 32:
             return rot ? resident_waves(kv4::decode_kv4_mfma8_kernel<32, true>, known[0][1])
@@ -154,11 +168,11 @@ int mfma8_waves_per_cu(const kv4_cache_desc& d)
     }
 }
 
-// Whether the decode of a cache runs on the ratio-8 matrix-core kernel.
+// Whether the decode of a cache runs on a ratio-8 matrix-core kernel.
 bool uses_mfma8(const kv4_cache_desc& d)
 {
     return d.num_q_heads == 8 * d.num_kv_heads && d.kind == KV4_KIND_MIXED &&
-           !(d.flags & (KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE));
+           !(d.flags & KV4_FLAG_VALU_DECODE);
 }
 
 // Waves of the balanced decode partition: explicit, or 16 per compute unit
@@ -230,10 +244,11 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
-// Vector-ALU kernels, used for q/kv ratio 8 of the integer path and the BF16
-// kind (and for every ratio with KV4_FLAG_VALU_DECODE).  Ratios 1 and 2 run on
-// the matrix-core kernels of ratio 4, whose rows past the ratio carry q = 0
-// and are not written; ratio 8 of the mixed kind on decode_kv4_mfma8_kernel.
+// Vector-ALU kernels, used for q/kv ratio 8 of the BF16 kind (and for every
+// ratio with KV4_FLAG_VALU_DECODE).  Ratios 1 and 2 run on the matrix-core
+// kernels of ratio 4, whose rows past the ratio carry q = 0 and are not
+// written; ratio 8 of the mixed kind on decode_kv4_mfma8_kernel and
+// decode_int_mfma8_kernel (two four-head halves per tile).
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
@@ -267,6 +282,23 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
                 default:
                     if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<128, true>), grid, dim3(64), 0, s, a);
                     else hipLaunchKernelGGL((kv4::decode_int_mfma_kernel<128, false>), grid, dim3(64), 0, s, a);
+                    break;
+            }
+            return;
+        }
+        if (a.g.gqa == 8 && !a.g.valu) {
+            switch (a.g.G) {
+                case 32:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<32, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<32, false>), grid, dim3(64), 0, s, a);
+                    break;
+                case 64:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<64, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<64, false>), grid, dim3(64), 0, s, a);
+                    break;
+                default:
+                    if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<128, true>), grid, dim3(64), 0, s, a);
+                    else hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<128, false>), grid, dim3(64), 0, s, a);
                     break;
             }
             return;

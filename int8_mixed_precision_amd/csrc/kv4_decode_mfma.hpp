@@ -1350,7 +1350,9 @@ __device__ __forceinline__ QCodes quant_q8(const float (&q)[8], float S, uint16_
     return r;
 }
 
-template <int G, bool ROT>
+// NH = 2 (q/kv ratio 8): q heads 0-3 and then 4-7 of the group on each staged
+// tile, as in mfma_item_kv4.
+template <int G, bool ROT, int NH = 1>
 __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                               float* rec, Pace& pace)
 {
@@ -1367,14 +1369,16 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
     const int64_t page_stride = (int64_t)g.Hkv * g.pb;
 
     // ---- INT8 query: head jq's codes on channels 32 gq + 8 kb + [0, 8)
-    u32x4_t A1, A2;                              // block-diagonal QK operands
-    float Qg[NG];                                // code sums of head kb per group
-    float c2;                                    // score factor of head kb
-    {
+    u32x4_t A1[NH], A2[NH];                      // block-diagonal QK operands
+    float Qg[NH][NG];                            // code sums of head kb per group
+    float c2[NH];                                // score factor of head kb
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
         // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
         // layout) carry q = 0; their results are not written
-        const bool qreal = jq < g.gqa;
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        const int jh = 4 * hf + jq;
+        const bool qreal = jh < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
         uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * gq + 8 * kb);
         if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -1397,23 +1401,30 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
         const uint16_t sb = plus_zero16(f32_to_f16_bits(__fdiv_rn(amax, 127.0f)));
         const float S = half_bits_to_float(sb);
         const QCodes qc = quant_q8(q, S, sb);
-        A1 = u32x4_t{gq == 0 ? qc.lo : 0u, gq == 0 ? qc.hi : 0u, gq == 1 ? qc.lo : 0u, gq == 1 ? qc.hi : 0u};
-        A2 = u32x4_t{gq == 2 ? qc.lo : 0u, gq == 2 ? qc.hi : 0u, gq == 3 ? qc.lo : 0u, gq == 3 ? qc.hi : 0u};
+        A1[hf] = u32x4_t{gq == 0 ? qc.lo : 0u, gq == 0 ? qc.hi : 0u, gq == 1 ? qc.lo : 0u, gq == 1 ? qc.hi : 0u};
+        A2[hf] = u32x4_t{gq == 2 ? qc.lo : 0u, gq == 2 ? qc.hi : 0u, gq == 3 ? qc.lo : 0u, gq == 3 ? qc.hi : 0u};
         // code sum of head jq over block gq (the four rows), then head kb's blocks
         const float qblk = rows_sum((float)qc.sum);          // integers below 2^13: exact
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) Qg[gg] = 0.f;
+        for (int gg = 0; gg < NG; ++gg) Qg[hf][gg] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Qg[(32 * r) / G] += __shfl(qblk, 4 * kb + r);
-        c2 = a.scale2 * __shfl(S, 4 * kb);
+        for (int r = 0; r < 4; ++r) Qg[hf][(32 * r) / G] += __shfl(qblk, 4 * kb + r);
+        c2[hf] = a.scale2 * __shfl(S, 4 * kb);
     }
 
-    // O[r][hh]: head kb, channel 32 r + 16 hh + n16
-    float O[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-    float accm[NG];
+    // O[hf][r][hh]: head 4 hf + kb, channel 32 r + 16 hh + n16
+    float O[NH][4][2];
+    float accm[NH][NG];
+    float m_sh[NH], l_run[NH];                   // m_sh = m_ref - kPScale
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) accm[gg] = 0.f;
-    float m_sh = -INFINITY, l_run = 0.f;        // m_sh = m_ref - kPScale
+    for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[hf][r][0] = O[hf][r][1] = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) accm[hf][gg] = 0.f;
+        m_sh[hf] = -INFINITY;
+        l_run[hf] = 0.f;
+    }
 
     constexpr int MB = 128 * NG;                 // metadata bytes per page
     Kv4Offs o;
@@ -1437,8 +1448,8 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
     };
     const bool upper = kb >> 1;
 
-    __shared__ __attribute__((aligned(16))) float pbuf[4][32];
-    __shared__ __attribute__((aligned(16))) float sbuf[4][4][4];     // [group][head][block]
+    __shared__ __attribute__((aligned(16))) float pbuf[NH][4][32];
+    __shared__ __attribute__((aligned(16))) float sbuf[NH][4][4][4]; // [half][group][head][block]
     __shared__ __attribute__((aligned(16))) uint8_t mbuf[2 * 512];
     __shared__ uint4 stage[4][64];
 
@@ -1474,138 +1485,142 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
             }
         }
 
-        // ---- QK: integer sums of head kb over block r, token n16 of page hh
-        const i32x4_t z = {0, 0, 0, 0};
-        i32x4_t D0 = mfma_i8_64(A1, u32x4_t{nib_lo(kc0.x), nib_hi(kc0.x), nib_lo(kc0.y), nib_hi(kc0.y)}, z);
-        D0 = mfma_i8_64(A2, u32x4_t{nib_lo(kc0.z), nib_hi(kc0.z), nib_lo(kc0.w), nib_hi(kc0.w)}, D0);
-        i32x4_t D1 = mfma_i8_64(A1, u32x4_t{nib_lo(kc1.x), nib_hi(kc1.x), nib_lo(kc1.y), nib_hi(kc1.y)}, z);
-        D1 = mfma_i8_64(A2, u32x4_t{nib_lo(kc1.z), nib_hi(kc1.z), nib_lo(kc1.w), nib_hi(kc1.w)}, D1);
-        float x0 = 0.f, x1 = 0.f;
+        // ---- per half of the q heads (one half below ratio 8)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int gg = (32 * r) / G;
-            x0 = fmaf(h2f(kdm[0][gg], 0), (float)D0[r], x0);
-            x1 = fmaf(h2f(kdm[1][gg], 0), (float)D1[r], x1);
-        }
+        for (int hf = 0; hf < NH; ++hf) {
+            // ---- QK: integer sums of head kb over block r, token n16 of page hh
+            const i32x4_t z = {0, 0, 0, 0};
+            i32x4_t D0 = mfma_i8_64(A1[hf], u32x4_t{nib_lo(kc0.x), nib_hi(kc0.x), nib_lo(kc0.y), nib_hi(kc0.y)}, z);
+            D0 = mfma_i8_64(A2[hf], u32x4_t{nib_lo(kc0.z), nib_hi(kc0.z), nib_lo(kc0.w), nib_hi(kc0.w)}, D0);
+            i32x4_t D1 = mfma_i8_64(A1[hf], u32x4_t{nib_lo(kc1.x), nib_hi(kc1.x), nib_lo(kc1.y), nib_hi(kc1.y)}, z);
+            D1 = mfma_i8_64(A2[hf], u32x4_t{nib_lo(kc1.z), nib_hi(kc1.z), nib_lo(kc1.w), nib_hi(kc1.w)}, D1);
+            float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-            x0 = fmaf(h2f(kdm[0][gg], 1), Qg[gg], x0);
-            x1 = fmaf(h2f(kdm[1][gg], 1), Qg[gg], x1);
-        }
-        float s0 = x0 * c2, s1 = x1 * c2;
-        const int tok0 = 32 * tl + n16;
-        const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
-        const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
-        if constexpr (!full) {
-            s0 = ok0 ? s0 : -INFINITY;
-            s1 = ok1 ? s1 : -INFINITY;
-        }
-        const float mx = row16_max(fmaxf(s0, s1));
-        {
-            const bool grow = mx > m_sh + (kPScale + kSlack);
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx - kPScale : m_sh;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
-                m_sh = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int gg = 0; gg < NG; ++gg) accm[gg] *= alpha;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    O[r][0] *= alpha;
-                    O[r][1] *= alpha;
-                }
-            }
-        }
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
-        l_run += p0 + p1;
-        {
-            const uint8_t* v0p = &mbuf[m_vm];
-            const uint8_t* v1p = &mbuf[MB + m_vm];
-            uint32_t vm0[(NG + 1) / 2], vm1[(NG + 1) / 2];
-            if constexpr (NG == 4) {
-                const uint2 u0 = *reinterpret_cast<const uint2*>(v0p);
-                const uint2 u1 = *reinterpret_cast<const uint2*>(v1p);
-                vm0[0] = u0.x; vm0[1] = u0.y; vm1[0] = u1.x; vm1[1] = u1.y;
-            } else if constexpr (NG == 2) {
-                vm0[0] = *reinterpret_cast<const uint32_t*>(v0p);
-                vm1[0] = *reinterpret_cast<const uint32_t*>(v1p);
-            } else {
-                vm0[0] = *reinterpret_cast<const uint16_t*>(v0p);
-                vm1[0] = *reinterpret_cast<const uint16_t*>(v1p);
+            for (int r = 0; r < 4; ++r) {
+                const int gg = (32 * r) / G;
+                x0 = fmaf(h2f(kdm[0][gg], 0), (float)D0[r], x0);
+                x1 = fmaf(h2f(kdm[1][gg], 0), (float)D1[r], x1);
             }
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
-                // never-written slots may hold NaN: select, do not multiply
-                const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
-                const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
-                accm[gg] = fmaf(p0, v0, fmaf(p1, v1, accm[gg]));
+                x0 = fmaf(h2f(kdm[0][gg], 1), Qg[hf][gg], x0);
+                x1 = fmaf(h2f(kdm[1][gg], 1), Qg[hf][gg], x1);
             }
-        }
-        pbuf[kb][n16] = p0;
-        pbuf[kb][16 + n16] = p1;
-        __builtin_amdgcn_wave_barrier();
-
-        // ---- 8-bit operand of (head jq, block gq, group kb): w = p' Delta_V of
-        // tokens 32 tl + 8 gq + e, its scale max w / 255 and codes
-        float sig = 0.f;
-        uint32_t ulo = 0u, uhi = 0u;
-        if (kb < NG) {
-            const float4 pa = *reinterpret_cast<const float4*>(&pbuf[jq][8 * gq]);
-            const float4 pb = *reinterpret_cast<const float4*>(&pbuf[jq][8 * gq + 4]);
-            const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vdu]);
-            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-            const uint32_t vdw[4] = {vd.x, vd.y, vd.z, vd.w};
-            float w[8], wmax = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = pr[e] * h2f(vdw[e >> 1], e & 1);
-                const int tok = 32 * tl + 8 * gq + e;
-                w[e] = (full || (tok >= t_lo && tok < t_hi)) ? x : 0.f;
-                wmax = fmaxf(wmax, w[e]);
+            float s0 = x0 * c2[hf], s1 = x1 * c2[hf];
+            const int tok0 = 32 * tl + n16;
+            const bool ok0 = full || (tok0 >= t_lo && tok0 < t_hi);
+            const bool ok1 = full || (tok0 + 16 >= t_lo && tok0 + 16 < t_hi);
+            if constexpr (!full) {
+                s0 = ok0 ? s0 : -INFINITY;
+                s1 = ok1 ? s1 : -INFINITY;
             }
-            const float rr = wmax > kTinyW ? __fdiv_rn(255.0f, wmax) : 0.f;
-            int uc[8];
+            const float mx = row16_max(fmaxf(s0, s1));
+            {
+                const bool grow = mx > m_sh[hf] + (kPScale + kSlack);
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx - kPScale : m_sh[hf];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh[hf] - m_new) : 1.0f;
+                    m_sh[hf] = m_new;
+                    l_run[hf] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) uc[e] = (int)fminf(rintf(w[e] * rr), 255.0f);
-            // the matrix core multiplies signed bytes: carry u - 128 (exact in
-            // [-128, 127]) and add 128 sum c back through the ones product
-            ulo = pack_i8x4(uc[0] - 128, uc[2] - 128, uc[4] - 128, uc[6] - 128);
-            uhi = pack_i8x4(uc[1] - 128, uc[3] - 128, uc[5] - 128, uc[7] - 128);
-            sig = wmax * (1.0f / 255.0f);
-        }
-        sbuf[kb][jq][gq] = sig;
-        uint32_t Alo[NG], Ahi[NG];
+                    for (int gg = 0; gg < NG; ++gg) accm[hf][gg] *= alpha;
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) {
-            const uint32_t sl = (uint32_t)__shfl((int)ulo, 16 * gg + n16);
-            const uint32_t sh = (uint32_t)__shfl((int)uhi, 16 * gg + n16);
-            Alo[gg] = kb == gq ? sl : 0u;
-            Ahi[gg] = kb == gq ? sh : 0u;
-        }
-        __builtin_amdgcn_wave_barrier();
-        float4 sg[NG];
+                    for (int r = 0; r < 4; ++r) {
+                        O[hf][r][0] *= alpha;
+                        O[hf][r][1] *= alpha;
+                    }
+                }
+            }
+            const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh[hf]);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh[hf]);
+            l_run[hf] += p0 + p1;
+            {
+                const uint8_t* v0p = &mbuf[m_vm];
+                const uint8_t* v1p = &mbuf[MB + m_vm];
+                uint32_t vm0[(NG + 1) / 2], vm1[(NG + 1) / 2];
+                if constexpr (NG == 4) {
+                    const uint2 u0 = *reinterpret_cast<const uint2*>(v0p);
+                    const uint2 u1 = *reinterpret_cast<const uint2*>(v1p);
+                    vm0[0] = u0.x; vm0[1] = u0.y; vm1[0] = u1.x; vm1[1] = u1.y;
+                } else if constexpr (NG == 2) {
+                    vm0[0] = *reinterpret_cast<const uint32_t*>(v0p);
+                    vm1[0] = *reinterpret_cast<const uint32_t*>(v1p);
+                } else {
+                    vm0[0] = *reinterpret_cast<const uint16_t*>(v0p);
+                    vm1[0] = *reinterpret_cast<const uint16_t*>(v1p);
+                }
 #pragma unroll
-        for (int gg = 0; gg < NG; ++gg) sg[gg] = *reinterpret_cast<const float4*>(&sbuf[gg][kb][0]);
+                for (int gg = 0; gg < NG; ++gg) {
+                    // never-written slots may hold NaN: select, do not multiply
+                    const float v0 = ok0 ? h2f(vm0[gg >> 1], gg & 1) : 0.f;
+                    const float v1 = ok1 ? h2f(vm1[gg >> 1], gg & 1) : 0.f;
+                    accm[hf][gg] = fmaf(p0, v0, fmaf(p1, v1, accm[hf][gg]));
+                }
+            }
+            pbuf[hf][kb][n16] = p0;
+            pbuf[hf][kb][16 + n16] = p1;
+            __builtin_amdgcn_wave_barrier();
 
-        // ---- PV: integer sums per 8-token block, sum u c = sum (u - 128) c +
-        // 128 sum c (the ones operand sums the codes of block kb), combined by
-        // the blocks' scales
-        const uint32_t ones = kb == gq ? 0x01010101u : 0u;
-        const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
-        const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
+            // ---- 8-bit operand of (head jq, block gq, group kb): w = p' Delta_V of
+            // tokens 32 tl + 8 gq + e, its scale max w / 255 and codes
+            float sig = 0.f;
+            uint32_t ulo = 0u, uhi = 0u;
+            if (kb < NG) {
+                const float4 pa = *reinterpret_cast<const float4*>(&pbuf[hf][jq][8 * gq]);
+                const float4 pb = *reinterpret_cast<const float4*>(&pbuf[hf][jq][8 * gq + 4]);
+                const uint4 vd = *reinterpret_cast<const uint4*>(&mbuf[m_vdu]);
+                const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+                const uint32_t vdw[4] = {vd.x, vd.y, vd.z, vd.w};
+                float w[8], wmax = 0.f;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int gg = (32 * blk) / G;
+                for (int e = 0; e < 8; ++e) {
+                    const float x = pr[e] * h2f(vdw[e >> 1], e & 1);
+                    const int tok = 32 * tl + 8 * gq + e;
+                    w[e] = (full || (tok >= t_lo && tok < t_hi)) ? x : 0.f;
+                    wmax = fmaxf(wmax, w[e]);
+                }
+                const float rr = wmax > kTinyW ? __fdiv_rn(255.0f, wmax) : 0.f;
+                int uc[8];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const uint32_t vw = vcw[2 * blk + hh];
-                const i32x4_t Dc = mfma_i8_32(ones, ones, nib_lo(vw), nib_hi(vw), z);
-                const i32x4_t Dp = mfma_i8_32(Alo[gg], Ahi[gg], nib_lo(vw), nib_hi(vw), z);
-                const float d0 = (float)(Dp[0] + 128 * Dc[0]), d1 = (float)(Dp[1] + 128 * Dc[1]);
-                const float d2 = (float)(Dp[2] + 128 * Dc[2]), d3 = (float)(Dp[3] + 128 * Dc[3]);
-                O[blk][hh] += (sg[gg].x * d0 + sg[gg].y * d1) + (sg[gg].z * d2 + sg[gg].w * d3);
+                for (int e = 0; e < 8; ++e) uc[e] = (int)fminf(rintf(w[e] * rr), 255.0f);
+                // the matrix core multiplies signed bytes: carry u - 128 (exact in
+                // [-128, 127]) and add 128 sum c back through the ones product
+                ulo = pack_i8x4(uc[0] - 128, uc[2] - 128, uc[4] - 128, uc[6] - 128);
+                uhi = pack_i8x4(uc[1] - 128, uc[3] - 128, uc[5] - 128, uc[7] - 128);
+                sig = wmax * (1.0f / 255.0f);
+            }
+            sbuf[hf][kb][jq][gq] = sig;
+            uint32_t Alo[NG], Ahi[NG];
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) {
+                const uint32_t sl = (uint32_t)__shfl((int)ulo, 16 * gg + n16);
+                const uint32_t sh = (uint32_t)__shfl((int)uhi, 16 * gg + n16);
+                Alo[gg] = kb == gq ? sl : 0u;
+                Ahi[gg] = kb == gq ? sh : 0u;
+            }
+            __builtin_amdgcn_wave_barrier();
+            float4 sg[NG];
+#pragma unroll
+            for (int gg = 0; gg < NG; ++gg) sg[gg] = *reinterpret_cast<const float4*>(&sbuf[hf][gg][kb][0]);
+
+            // ---- PV: integer sums per 8-token block, sum u c = sum (u - 128) c +
+            // 128 sum c (the ones operand sums the codes of block kb), combined by
+            // the blocks' scales
+            const uint32_t ones = kb == gq ? 0x01010101u : 0u;
+            const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
+            const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const int gg = (32 * blk) / G;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t vw = vcw[2 * blk + hh];
+                    const i32x4_t Dc = mfma_i8_32(ones, ones, nib_lo(vw), nib_hi(vw), z);
+                    const i32x4_t Dp = mfma_i8_32(Alo[gg], Ahi[gg], nib_lo(vw), nib_hi(vw), z);
+                    const float d0 = (float)(Dp[0] + 128 * Dc[0]), d1 = (float)(Dp[1] + 128 * Dc[1]);
+                    const float d2 = (float)(Dp[2] + 128 * Dc[2]), d3 = (float)(Dp[3] + 128 * Dc[3]);
+                    O[hf][blk][hh] += (sg[gg].x * d0 + sg[gg].y * d1) + (sg[gg].z * d2 + sg[gg].w * d3);
+                }
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -1636,18 +1651,21 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
         if (tl < tile_end) advance(tl, std::false_type{});
     }
 
-    const float l = row16_sum(l_run);
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) accm[gg] = row16_sum(accm[gg]);
-    const float inv = 1.0f / l;
-    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
-    float* dst = rec + kb * (g.d + kPartPad);
+    for (int hf = 0; hf < NH; ++hf) {
+        const float l = row16_sum(l_run[hf]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        dst[32 * r + n16] = (O[r][0] + accm[(32 * r) / G]) * inv;
-        dst[32 * r + 16 + n16] = (O[r][1] + accm[(32 * r) / G]) * inv;
+        for (int gg = 0; gg < NG; ++gg) accm[hf][gg] = row16_sum(accm[hf][gg]);
+        const float inv = 1.0f / l;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dst[32 * r + n16] = (O[hf][r][0] + accm[hf][(32 * r) / G]) * inv;
+            dst[32 * r + 16 + n16] = (O[hf][r][1] + accm[hf][(32 * r) / G]) * inv;
+        }
+        if (n16 == 0) dst[g.d] = m_sh[hf] + log2f(l);
     }
-    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
 // Protected part of the integer path: integer QK of the INT8 query against
@@ -1656,7 +1674,8 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
 // product that covers those bytes only; B = 16 key bytes of entry n16), then
 // the PV of mfma_prot_kv4: binary32-accurate products with the dequantized
 // INT8 values, no probability quantization.
-template <bool ROT>
+// NH = 2 (q/kv ratio 8): q heads 0-3 and then 4-7 on each tile's loads.
+template <bool ROT, int NH = 1>
 __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h, float* rec)
 {
     const Geo& g = a.g;
@@ -1671,13 +1690,15 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
     const uint16_t* ksc = reinterpret_cast<const uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
     const uint16_t* vsc = ksc + g.SR32;
 
-    u32x4_t A1, A2;
-    float c2;
-    {
+    u32x4_t A1[NH], A2[NH];
+    float c2[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
         // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
         // layout) carry q = 0; their results are not written
-        const bool qreal = jq < g.gqa;
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        const int jh = 4 * hf + jq;
+        const bool qreal = jh < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
         uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
         if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -1702,16 +1723,23 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
 #pragma unroll
         for (int i = 0; i < 8; ++i) c[i] = int8_code(q[i], S, sb);
         const uint32_t w0 = pack_i8x4(c[0], c[1], c[2], c[3]), w1 = pack_i8x4(c[4], c[5], c[6], c[7]);
-        A1 = u32x4_t{gq == 0 ? w0 : 0u, gq == 0 ? w1 : 0u, gq == 1 ? w0 : 0u, gq == 1 ? w1 : 0u};
-        A2 = u32x4_t{gq == 2 ? w0 : 0u, gq == 2 ? w1 : 0u, gq == 3 ? w0 : 0u, gq == 3 ? w1 : 0u};
-        c2 = a.scale2 * __shfl(S, 4 * kb);
+        A1[hf] = u32x4_t{gq == 0 ? w0 : 0u, gq == 0 ? w1 : 0u, gq == 1 ? w0 : 0u, gq == 1 ? w1 : 0u};
+        A2[hf] = u32x4_t{gq == 2 ? w0 : 0u, gq == 2 ? w1 : 0u, gq == 3 ? w0 : 0u, gq == 3 ? w1 : 0u};
+        c2[hf] = a.scale2 * __shfl(S, 4 * kb);
     }
 
-    // E[h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
-    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
-    float m_sh = -INFINITY, l_run = 0.f;
-    __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
+    // E[hf][h]: rows (head, block r), channels 32 r + 16 h + n16 (block-diagonal PV)
+    f32x4_t E[NH][2], W[NH];
+    float m_sh[NH], l_run[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        E[hf][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        E[hf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        W[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_sh[hf] = -INFINITY;
+        l_run[hf] = 0.f;
+    }
+    __shared__ __attribute__((aligned(16))) float pbuf8[NH][4][32];
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
 
     for (int e0 = 0; e0 < n8; e0 += 32) {
@@ -1731,100 +1759,118 @@ __device__ __forceinline__ void mfma_prot_int(const DecodeArgs& a, int b, int h,
         const float sk1 = half_bits_to_float(ksc[e0 + 16 + n16]);
         const uint4 svp = *reinterpret_cast<const uint4*>(vsc + e0 + 8 * kb);
 
-        // ---- QK: integer sums of head kb over sub-block r of each lane's 32 channels
-        const i32x4_t z = {0, 0, 0, 0};
-        i32x4_t D0 = mfma_i8_64(A1, u32x4_t{k00.x, k00.y, k00.z, k00.w}, z);
-        D0 = mfma_i8_64(A2, u32x4_t{k01.x, k01.y, k01.z, k01.w}, D0);
-        i32x4_t D1 = mfma_i8_64(A1, u32x4_t{k10.x, k10.y, k10.z, k10.w}, z);
-        D1 = mfma_i8_64(A2, u32x4_t{k11.x, k11.y, k11.z, k11.w}, D1);
-        const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
-        float s0 = (float)((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
-        float s1 = (float)((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2;
-        s0 = ok0 ? s0 : -INFINITY;
-        s1 = ok1 ? s1 : -INFINITY;
-        const float mx = row16_max(fmaxf(s0, s1));
-        {
-            const bool grow = mx > m_sh + (kPScale + kSlack);
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx - kPScale : m_sh;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
-                m_sh = m_new;
-                l_run *= alpha;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
-                W *= alpha;
+        for (int hf = 0; hf < NH; ++hf) {
+            // ---- QK: integer sums of head kb over sub-block r of each lane's 32 channels
+            const i32x4_t z = {0, 0, 0, 0};
+            i32x4_t D0 = mfma_i8_64(A1[hf], u32x4_t{k00.x, k00.y, k00.z, k00.w}, z);
+            D0 = mfma_i8_64(A2[hf], u32x4_t{k01.x, k01.y, k01.z, k01.w}, D0);
+            i32x4_t D1 = mfma_i8_64(A1[hf], u32x4_t{k10.x, k10.y, k10.z, k10.w}, z);
+            D1 = mfma_i8_64(A2[hf], u32x4_t{k11.x, k11.y, k11.z, k11.w}, D1);
+            const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
+            float s0 = (float)((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2[hf];
+            float s1 = (float)((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2[hf];
+            s0 = ok0 ? s0 : -INFINITY;
+            s1 = ok1 ? s1 : -INFINITY;
+            const float mx = row16_max(fmaxf(s0, s1));
+            {
+                const bool grow = mx > m_sh[hf] + (kPScale + kSlack);
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx - kPScale : m_sh[hf];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh[hf] - m_new) : 1.0f;
+                    m_sh[hf] = m_new;
+                    l_run[hf] *= alpha;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) E[hf][hh] *= alpha;
+                    W[hf] *= alpha;
+                }
             }
-        }
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
-        l_run += p0 + p1;
-        pbuf8[kb][n16] = p0;
-        pbuf8[kb][16 + n16] = p1;
-        __builtin_amdgcn_wave_barrier();
-        const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb]);
-        const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb + 4]);
+            const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh[hf]);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh[hf]);
+            l_run[hf] += p0 + p1;
+            pbuf8[hf][kb][n16] = p0;
+            pbuf8[hf][kb][16 + n16] = p1;
+            __builtin_amdgcn_wave_barrier();
+            const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb]);
+            const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb + 4]);
 
-        // ---- PV: w = p' s_V of head jq, entries e0 + 8 kb + e
-        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
-        float wv[8];
+            // ---- PV: w = p' s_V of head jq, entries e0 + 8 kb + e
+            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
+            float wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // entries past the end may hold garbage scales: select, do not multiply
-            const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
-            wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
-        }
-        u32x4_t ahi, alo;
-        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+            for (int e = 0; e < 8; ++e) {
+                // entries past the end may hold garbage scales: select, do not multiply
+                const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
+                wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
+            }
+            u32x4_t ahi, alo;
+            constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hw, lw;
-            split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
-            ahi[i] = hw;
-            alo[i] = lw;
-        }
-        const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hw, lw;
+                split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
+                ahi[i] = hw;
+                alo[i] = lw;
+            }
+            const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                     v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint64_t rows = 0x1111111111111111ull << blk;
-            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
-            const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
-            const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
-            E[0] = mfma_bf16(bh, b0, E[0]);
-            E[1] = mfma_bf16(bh, b1, E[1]);
-            E[0] = mfma_bf16(bl, b0, E[0]);
-            E[1] = mfma_bf16(bl, b1, E[1]);
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint64_t rows = 0x1111111111111111ull << blk;
+                const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
+                                    keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
+                const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
+                                    keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
+                const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
+                const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
+                E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
+                E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
+                E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+            }
+            W[hf] = mfma_bf16(ahi, ones, W[hf]);
+            W[hf] = mfma_bf16(alo, ones, W[hf]);
         }
-        W = mfma_bf16(ahi, ones, W);
-        W = mfma_bf16(alo, ones, W);
         __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
+    // ---- epilogue: lane l holds head 4 hf + kb, channels 32 r + 16 h + n16 in E[hf][h][r]
     // (every block row of W carries the same sum; row 0 is used)
-    const float l = row16_sum(l_run);
-    const float inv = 1.0f / l;
-    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
-    float* dst = rec + kb * (g.d + kPartPad);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        dst[32 * r + n16] = (ldexpf(E[0][r], 133) - 128.0f * W[0]) * inv;
-        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) - 128.0f * W[0]) * inv;
+    for (int hf = 0; hf < NH; ++hf) {
+        const float l = row16_sum(l_run[hf]);
+        const float inv = 1.0f / l;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dst[32 * r + n16] = (ldexpf(E[hf][0][r], 133) - 128.0f * W[hf][0]) * inv;
+            dst[32 * r + 16 + n16] = (ldexpf(E[hf][1][r], 133) - 128.0f * W[hf][0]) * inv;
+        }
+        if (n16 == 0) dst[g.d] = m_sh[hf] + log2f(l);
     }
-    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
-// Integer path, GQA 4.
+// Integer path, q/kv ratios 1, 2 and 4.
 template <int G, bool ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void decode_int_mfma_kernel(DecodeArgs a)
 {
     walk_units(a, [&](int b, int h) { mfma_prot_int<ROT>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_int<G, ROT>(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// Integer path, q/kv ratio 8: two four-head halves per tile.  The integer
+// operands of the second half need more registers than three waves per SIMD
+// leave without spilling inside the tile loop: two waves per SIMD.
+template <int G, bool ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_int_mfma8_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int b, int h) { mfma_prot_int<ROT, 2>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_int<G, ROT, 2>(a, b, h, lo, hi, rec, pace);
                });
 }
 

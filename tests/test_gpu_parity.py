@@ -202,13 +202,19 @@ def test_gqa_ratios(Hq, Hkv):
 def test_ratio8_matrix_core():
     """q/kv ratio 8 on the matrix core (two four-head halves per tile): group
     sizes 32, 64 and 128, rotated keys, edge lengths around S + R, several
-    waves, and a 64 q / 8 kv layer with long contexts."""
+    waves, and a 64 q / 8 kv layer with long contexts; the integer path too."""
     edge = [0, 1, 3, 4, 5, 19, 20, 21, 67, 68, 69, 100, 257, 700, 2500]
     for G, rotate, waves in ((32, False, 0), (64, False, 5), (128, False, 0), (32, True, 0), (128, True, 7)):
         H.log(f"case ratio 8 Hq=16 Hkv=2 G={G} rotate={rotate} waves={waves}")
         _run_case(16, 2, G, 4, 64, edge, seed=170 + G + rotate, rotate=rotate, waves=waves)
     H.log("case ratio 8 Hq=64 Hkv=8 G=32, long contexts")
     _run_case(64, 8, 32, 4, 128, [9000, 17, 4000, 131, 133], seed=178)
+    ictx = [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500]
+    for G, rotate in ((32, False), (64, True)):
+        H.log(f"case ratio 8, integer path, G={G} rotate={rotate}")
+        _int_case(16, 2, G, 4, 64, ictx, seed=180 + G + rotate, rotate=rotate)
+    H.log("case ratio 8, integer path, Hq=64 Hkv=8, long contexts")
+    _int_case(64, 8, 32, 4, 128, [9000, 17, 4000], seed=183)
 
 
 def test_group_64_and_multi_layer():
@@ -429,7 +435,7 @@ def test_valu_decode_flag():
         _run_case(Hq, Hkv, G, 4, 16, ctx, seed=140 + G + Hq + Hkv, rotate=rotate,
                   flags=kv4.KV4_FLAG_VALU_DECODE)
     ictx = [0, 3, 7, 8, 9, 40, 67, 68, 69, 300, 1000, 2500]
-    for Hq, Hkv in ((8, 2), (8, 8), (8, 4)):
+    for Hq, Hkv in ((8, 2), (8, 8), (8, 4), (16, 2)):
         H.log(f"case vector-ALU decode, integer path, Hq={Hq} Hkv={Hkv}")
         _int_case(Hq, Hkv, 32, 4, 64, ictx, seed=150 + Hq + Hkv, flags=kv4.KV4_FLAG_VALU_DECODE)
     ctxb = np.array([0, 15, 16, 17, 300, 1000, 3000])
@@ -588,7 +594,7 @@ def test_integer_path_edges_rotation_layers():
     H.log("case integer path, rotated keys, GQA 4 (matrix core)")
     _int_case(8, 2, 32, 4, 64, [0, 40, 67, 300, 1000, 2500], seed=131, rotate=True)
     _int_case(16, 4, 128, 16, 8, [3, 200, 1500], seed=136, rotate=True)
-    H.log("case integer path, rotated keys, GQA 2 and 8 (vector ALU)")
+    H.log("case integer path, rotated keys, GQA 2 and 8 (matrix core)")
     _int_case(8, 4, 32, 4, 64, [0, 67, 1000], seed=134, rotate=True)
     _int_case(16, 2, 64, 4, 64, [5, 300], seed=135, rotate=True)
     H.log("case integer path, 3 layers, layer 1, waves 7")
