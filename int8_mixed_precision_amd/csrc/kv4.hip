@@ -57,8 +57,18 @@ int validate_desc(const kv4_cache_desc* d)
         return KV4_ERR_INVALID_ARG;
     if (d->flags & ~(KV4_FLAG_ROTATE_K | KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE)) return KV4_ERR_INVALID_ARG;
     if (d->head_dim % d->group_size != 0) return KV4_ERR_INVALID_ARG;
-    int gqa = d->num_q_heads / d->num_kv_heads;
-    if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
+    // q/kv ratios: the matrix-core kernels take 1 .. 8 in halves of four q heads
+    // (rows of heads past the ratio carry q = 0), and 16 as four halves on the
+    // floating-point path of the mixed kind; the vector-ALU kernels take 1, 2,
+    // 4 and 8; the BF16 kind decodes ratios up to 4 on the matrix core and 8 on
+    // the vector ALU; KV8 (below) takes 4.
+    const int gqa = d->num_q_heads / d->num_kv_heads;
+    const bool pow2 = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8;
+    if (gqa > 8 && gqa != 16) return KV4_ERR_UNSUPPORTED;
+    if (gqa == 16 && (d->kind != KV4_KIND_MIXED || (d->flags & (KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE))))
+        return KV4_ERR_UNSUPPORTED;
+    if (!pow2 && gqa != 16 && (d->flags & KV4_FLAG_VALU_DECODE)) return KV4_ERR_UNSUPPORTED;
+    if (d->kind == KV4_KIND_BF16 && gqa > 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
     if (d->head_dim != kv4::kHeadDim || d->page_size != kv4::kPage) return KV4_ERR_UNSUPPORTED;
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
     // the rotation belongs to the quantized keys: the BF16 comparator has none
@@ -168,10 +178,29 @@ int mfma8_waves_per_cu(const kv4_cache_desc& d)
     }
 }
 
-// Whether the decode of a cache runs on a ratio-8 matrix-core kernel.
-bool uses_mfma8(const kv4_cache_desc& d)
+// Resident waves per compute unit of the ratio-16 matrix-core kernel.
+int mfma16_waves_per_cu(const kv4_cache_desc& d)
 {
-    return d.num_q_heads == 8 * d.num_kv_heads && d.kind == KV4_KIND_MIXED &&
+    static std::atomic<int> known[3][2];
+    const bool rot = (d.flags & KV4_FLAG_ROTATE_K) != 0;
+    switch (d.group_size) {
+        case 32:
+            return rot ? resident_waves(kv4::decode_kv4_mfma16_kernel<32, true>, known[0][1])
+                       : resident_waves(kv4::decode_kv4_mfma16_kernel<32, false>, known[0][0]);
+        case 64:
+            return rot ? resident_waves(kv4::decode_kv4_mfma16_kernel<64, true>, known[1][1])
+                       : resident_waves(kv4::decode_kv4_mfma16_kernel<64, false>, known[1][0]);
+        default:
+            return rot ? resident_waves(kv4::decode_kv4_mfma16_kernel<128, true>, known[2][1])
+                       : resident_waves(kv4::decode_kv4_mfma16_kernel<128, false>, known[2][0]);
+    }
+}
+
+// Whether the decode of a cache runs on a matrix-core kernel of two or more
+// four-head halves (mixed kind, q/kv ratio above 4).
+bool uses_halves(const kv4_cache_desc& d)
+{
+    return d.num_q_heads > 4 * d.num_kv_heads && d.kind == KV4_KIND_MIXED &&
            !(d.flags & KV4_FLAG_VALU_DECODE);
 }
 
@@ -186,7 +215,8 @@ int decode_waves(const kv4_cache* c, int cus)
     if (c->desc.num_waves > 0) return c->desc.num_waves;
     // (the matrix-core kernels, q/kv ratios 1, 2 and 4, keep 16 resident)
     const int gqa = c->desc.num_q_heads / c->desc.num_kv_heads;
-    if (uses_mfma8(c->desc)) return mfma8_waves_per_cu(c->desc) * cus;
+    if (uses_halves(c->desc))
+        return (gqa > 8 ? mfma16_waves_per_cu(c->desc) : mfma8_waves_per_cu(c->desc)) * cus;
     if (gqa > 4 || (c->desc.flags & KV4_FLAG_VALU_DECODE)) return valu_waves_per_cu(c->desc, gqa) * cus;
     return 16 * cus;
 }
@@ -244,11 +274,12 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
-// Vector-ALU kernels, used for q/kv ratio 8 of the BF16 kind (and for every
-// ratio with KV4_FLAG_VALU_DECODE).  Ratios 1 and 2 run on the matrix-core
-// kernels of ratio 4, whose rows past the ratio carry q = 0 and are not
-// written; ratio 8 of the mixed kind on decode_kv4_mfma8_kernel and
-// decode_int_mfma8_kernel (two four-head halves per tile).
+// Vector-ALU kernels, used for q/kv ratio 8 of the BF16 kind (and for ratios
+// 1, 2, 4 and 8 with KV4_FLAG_VALU_DECODE).  The matrix-core kernels run the
+// q heads of a kv head in halves of four (rows of heads past the ratio carry
+// q = 0 and are not written): one half for ratios up to 4, two for 5 to 8
+// (decode_kv4_mfma8_kernel, decode_int_mfma8_kernel), four for 16
+// (decode_kv4_mfma16_kernel).
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
 {
@@ -286,7 +317,7 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
             }
             return;
         }
-        if (a.g.gqa == 8 && !a.g.valu) {
+        if (a.g.gqa <= 8 && !a.g.valu) {
             switch (a.g.G) {
                 case 32:
                     if (a.g.rot) hipLaunchKernelGGL((kv4::decode_int_mfma8_kernel<32, true>), grid, dim3(64), 0, s, a);
@@ -335,7 +366,25 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
         }
         return;
     }
-    if (a.g.gqa == 8 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {
+    if (a.g.gqa == 16 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {
+        dim3 grid((unsigned)a.waves);
+        switch (a.g.G) {
+            case 32:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<32, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<32, false>), grid, dim3(64), 0, s, a);
+                break;
+            case 64:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<64, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<64, false>), grid, dim3(64), 0, s, a);
+                break;
+            default:
+                if (a.g.rot) hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<128, true>), grid, dim3(64), 0, s, a);
+                else hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<128, false>), grid, dim3(64), 0, s, a);
+                break;
+        }
+        return;
+    }
+    if (a.g.gqa <= 8 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {
         dim3 grid((unsigned)a.waves);
         switch (a.g.G) {
             case 32:

@@ -328,7 +328,7 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf) {
         float sq_part;
-        int sc;                                      // scale exponent of head jq
+        int sc;                                  // scale exponent of head jq
         aql[hf] = u32x4_t{0u, 0u, 0u, 0u};
         {
             // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
@@ -769,7 +769,7 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
                 }
             }
         }
-        float qpart = 0.f;                           // the sum of exactly the operand used
+        float qpart = 0.f;                       // the sum of exactly the operand used
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             qpart += h2f(aqv[hf][i], 0) + h2f(aqv[hf][i], 1);
@@ -1286,6 +1286,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
     walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT, 2>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_kv4<G, ROT, 2>(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// q/kv ratio 16: the four-head layout four times per tile, two waves per SIMD.
+template <int G, bool ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kv4_mfma16_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int b, int h) { mfma_prot_kv4<ROT, 4>(a, b, h, prot_ptr(a, b * a.g.Hkv + h)); },
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_kv4<G, ROT, 4>(a, b, h, lo, hi, rec, pace);
                });
 }
 

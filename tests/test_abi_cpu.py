@@ -111,7 +111,19 @@ def test_invalid_descriptors():
         (dict(pool_chunks=4), kv4.KV4_ERR_INVALID_ARG),        # below 8
         (dict(pool_chunks=24), kv4.KV4_ERR_INVALID_ARG),       # not a power of two
         (dict(pool_chunks=1 << 17), kv4.KV4_ERR_INVALID_ARG),
-        (dict(num_q_heads=48, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(num_q_heads=96, num_kv_heads=3), kv4.KV4_ERR_UNSUPPORTED),     # ratio 32
+        (dict(num_q_heads=80, num_kv_heads=8), kv4.KV4_ERR_UNSUPPORTED),     # ratio 10
+        (dict(num_q_heads=128, flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_ERR_UNSUPPORTED),   # 16
+        (dict(num_q_heads=128, flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(num_q_heads=128, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
+        (dict(num_q_heads=24, flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_ERR_UNSUPPORTED),  # 3
+        (dict(num_q_heads=40, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),  # ratio 5
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=24), kv4.KV4_ERR_UNSUPPORTED),     # GQA 3
+        (dict(num_q_heads=24), kv4.KV4_OK),                                    # ratio 3
+        (dict(num_q_heads=40), kv4.KV4_OK),                                    # 5 (Qwen3-14B)
+        (dict(num_q_heads=56, flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),       # 7
+        (dict(num_q_heads=128, flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_OK),      # 16
+        (dict(num_q_heads=24, kind=kv4.KV4_KIND_BF16), kv4.KV4_OK),            # 3
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
         (dict(kind=kv4.KV4_KIND_KV8), kv4.KV4_OK),
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_ERR_UNSUPPORTED),     # GQA 2

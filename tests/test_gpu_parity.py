@@ -217,6 +217,32 @@ def test_ratio8_matrix_core():
     _int_case(64, 8, 32, 4, 128, [9000, 17, 4000], seed=183)
 
 
+def test_other_ratios():
+    """q/kv ratios that are not powers of two, and 16: the matrix core runs the q
+    heads of a kv head in halves of four with the heads past the ratio padded
+    (3: one half, 5-7: two, 16: four), on the floating-point and integer paths
+    and the BF16 kind (ratio 3), against the oracle."""
+    edge = [0, 3, 19, 20, 21, 67, 68, 69, 300, 1000, 2500]
+    for Hq, Hkv, G, rotate in ((12, 4, 32, False), (40, 8, 32, False), (12, 2, 64, True), (14, 2, 128, False),
+                               (64, 4, 32, False), (32, 2, 128, True)):
+        H.log(f"case ratio {Hq // Hkv}: Hq={Hq} Hkv={Hkv} G={G} rotate={rotate}")
+        _run_case(Hq, Hkv, G, 4, 64, edge, seed=190 + Hq + Hkv + G, rotate=rotate)
+    for Hq, Hkv, G in ((12, 4, 32), (40, 8, 32), (14, 2, 64)):
+        H.log(f"case ratio {Hq // Hkv}, integer path: Hq={Hq} Hkv={Hkv} G={G}")
+        _int_case(Hq, Hkv, G, 4, 64, edge, seed=195 + Hq + Hkv + G)
+    H.log("case ratio 3, BF16 kind")
+    ctx = np.array([0, 15, 16, 17, 300, 1000, 3000])
+    n = ctx + 1
+    cfg = W.scaled(W.CONFIGS["tiny"], seed=37, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx),
+                   q_heads=12, kv_heads=4)
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    q = W.queries(cfg, 0)
+    built = H.make_cache(12, 4, 32, 0, 0, n, kind=kv4.KV4_KIND_BF16, seed=6)
+    H.build_from_sources(built, 0, ks, vs, ctx)
+    out = H.decode(built, 0, q, n).cpu().numpy()
+    H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
+
+
 def test_group_64_and_multi_layer():
     H.log("case G=64, 3 layers, layer 2")
     _run_case(8, 2, 64, 4, 32, [33, 150, 401], seed=77, layers=3, layer=2)

@@ -40,8 +40,9 @@ def _case(Hq, Hkv, lens, seed, out_dtype=kv4.KV4_OUT_F32, sm_scale=1 / math.sqrt
 
 
 # q head counts that are multiples of 8 take the XCD-grouped head order (at
-# 32/8 and 64/8 each XCD holds whole kv-head groups); 12/3 keeps the launch order
-@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8), (8, 8), (16, 2), (12, 3), (64, 8)])
+# 32/8, 64/8 and 40/8 each XCD holds whole kv-head groups); 12/3 keeps the
+# launch order; ratios 3, 5 and 16 as well as powers of two
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (32, 8), (8, 8), (16, 2), (12, 3), (64, 8), (40, 8), (64, 4)])
 def test_prefill_matches_oracle(Hq, Hkv):
     lens = [1, 15, 16, 17, 31, 32, 33, 100, 257, 600]
     H.log(f"case prefill Hq={Hq} Hkv={Hkv} lens={lens}")
