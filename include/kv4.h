@@ -128,10 +128,9 @@ extern "C" {
  * probability quantization).  Mixed kind only (KV4_ERR_UNSUPPORTED otherwise);
  * q/kv head ratios 1 to 8; the cache's bytes do not change. */
 #define KV4_FLAG_INT_PATH 0x2
-/* KV4_FLAG_VALU_DECODE: the decode runs on the vector-ALU kernels (otherwise the
- * mixed kind runs on the matrix-core kernels at every ratio, the BF16 kind at
- * ratios up to 4), with the same partition, arithmetic definitions and
- * tolerance.  A measurement point for the choice of the matrix core (no
+/* KV4_FLAG_VALU_DECODE: the decode runs on the vector-ALU kernels (otherwise on
+ * the matrix-core kernels at every ratio), with the same partition, arithmetic
+ * definitions and tolerance.  A measurement point for the choice of the matrix core (no
  * passage of the pages behind it).  Mixed and BF16 kinds at q/kv head ratios
  * 1, 2, 4 and 8 (KV4_ERR_UNSUPPORTED for KV8 and other ratios). */
 #define KV4_FLAG_VALU_DECODE 0x4
@@ -149,8 +148,8 @@ typedef struct kv4_cache_desc {
     int32_t num_kv_heads;       /* Hkv.  Hq / Hkv: 1 to 8 (the matrix core runs
                                    the q heads of a kv head in halves of four),
                                    or 16 for the mixed kind without
-                                   KV4_FLAG_INT_PATH; the BF16 kind 1 to 4 or
-                                   8; KV8 4.  Others: KV4_ERR_UNSUPPORTED */
+                                   KV4_FLAG_INT_PATH; KV8 4.  Others:
+                                   KV4_ERR_UNSUPPORTED */
     int32_t head_dim;           /* d; the library supports 128 */
     int32_t page_size;          /* tokens per page; the library supports 16 */
     int32_t group_size;         /* G, INT4 channels per (Delta, m) pair: 32, 64 or 128 */

@@ -60,15 +60,13 @@ int validate_desc(const kv4_cache_desc* d)
     // q/kv ratios: the matrix-core kernels take 1 .. 8 in halves of four q heads
     // (rows of heads past the ratio carry q = 0), and 16 as four halves on the
     // floating-point path of the mixed kind; the vector-ALU kernels take 1, 2,
-    // 4 and 8; the BF16 kind decodes ratios up to 4 on the matrix core and 8 on
-    // the vector ALU; KV8 (below) takes 4.
+    // 4 and 8; KV8 (below) takes 4.
     const int gqa = d->num_q_heads / d->num_kv_heads;
     const bool pow2 = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8;
     if (gqa > 8 && gqa != 16) return KV4_ERR_UNSUPPORTED;
     if (gqa == 16 && (d->kind != KV4_KIND_MIXED || (d->flags & (KV4_FLAG_INT_PATH | KV4_FLAG_VALU_DECODE))))
         return KV4_ERR_UNSUPPORTED;
     if (!pow2 && gqa != 16 && (d->flags & KV4_FLAG_VALU_DECODE)) return KV4_ERR_UNSUPPORTED;
-    if (d->kind == KV4_KIND_BF16 && gqa > 4 && gqa != 8) return KV4_ERR_UNSUPPORTED;
     if (d->head_dim != kv4::kHeadDim || d->page_size != kv4::kPage) return KV4_ERR_UNSUPPORTED;
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return KV4_ERR_UNSUPPORTED;
     // the rotation belongs to the quantized keys: the BF16 comparator has none
@@ -151,6 +149,8 @@ int mfma8_waves_per_cu(const kv4_cache_desc& d)
 {
     static std::atomic<int> known[3][2];
     static std::atomic<int> known_int[3][2];
+    static std::atomic<int> known_bf16;
+    if (d.kind == KV4_KIND_BF16) return resident_waves(kv4::decode_bf16_mfma8_kernel, known_bf16);
     const bool rot = (d.flags & KV4_FLAG_ROTATE_K) != 0;
     if (d.flags & KV4_FLAG_INT_PATH) {
         switch (d.group_size) {
@@ -197,10 +197,10 @@ int mfma16_waves_per_cu(const kv4_cache_desc& d)
 }
 
 // Whether the decode of a cache runs on a matrix-core kernel of two or more
-// four-head halves (mixed kind, q/kv ratio above 4).
+// four-head halves (mixed and BF16 kinds, q/kv ratio above 4).
 bool uses_halves(const kv4_cache_desc& d)
 {
-    return d.num_q_heads > 4 * d.num_kv_heads && d.kind == KV4_KIND_MIXED &&
+    return d.num_q_heads > 4 * d.num_kv_heads && d.kind != KV4_KIND_KV8 &&
            !(d.flags & KV4_FLAG_VALU_DECODE);
 }
 
@@ -274,11 +274,11 @@ int launch_status()
     return e == hipSuccess ? KV4_OK : KV4_ERR_HIP;
 }
 
-// Vector-ALU kernels, used for q/kv ratio 8 of the BF16 kind (and for ratios
-// 1, 2, 4 and 8 with KV4_FLAG_VALU_DECODE).  The matrix-core kernels run the
-// q heads of a kv head in halves of four (rows of heads past the ratio carry
-// q = 0 and are not written): one half for ratios up to 4, two for 5 to 8
-// (decode_kv4_mfma8_kernel, decode_int_mfma8_kernel), four for 16
+// Vector-ALU kernels, used with KV4_FLAG_VALU_DECODE (ratios 1, 2, 4 and 8).
+// The matrix-core kernels run the q heads of a kv head in halves of four (rows
+// of heads past the ratio carry q = 0 and are not written): one half for
+// ratios up to 4, two for 5 to 8 (decode_kv4_mfma8_kernel,
+// decode_int_mfma8_kernel, decode_bf16_mfma8_kernel), four for 16
 // (decode_kv4_mfma16_kernel).
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
@@ -382,6 +382,10 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
                 else hipLaunchKernelGGL((kv4::decode_kv4_mfma16_kernel<128, false>), grid, dim3(64), 0, s, a);
                 break;
         }
+        return;
+    }
+    if (a.g.gqa <= 8 && !a.g.valu && a.g.kind == KV4_KIND_BF16) {
+        hipLaunchKernelGGL(kv4::decode_bf16_mfma8_kernel, dim3((unsigned)a.waves), dim3(64), 0, s, a);
         return;
     }
     if (a.g.gqa <= 8 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {

@@ -1149,6 +1149,7 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
 //       parts 2-3 zero;
 //       columns = channels 16 s + n16; k = tokens 8 kb .. 8 kb + 7 in order.
 // ---------------------------------------------------------------------------
+template <int NH = 1>
 __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                                float* rec, Pace& pace)
 {
@@ -1164,20 +1165,27 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
 
     // columns of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
     // layout) carry q = 0; their results are not written
-    const bool qreal = jq < g.gqa;
-    const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
-    u32x4_t bq[4];
+    // (NH = 2: q heads 0-3 and 4-7 of the group as two halves on the same loads)
+    u32x4_t bq[NH][4];
+    f32x4_t O[NH][8];
+    float m_run[NH], l_run[NH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * i + 8 * kb);
-        u32x4_t v = {u.x, u.y, u.z, u.w}, z = {0u, 0u, 0u, 0u};
-        bq[i] = gq == 0 && qreal ? v : z;
+    for (int hf = 0; hf < NH; ++hf) {
+        const int jh = 4 * hf + jq;
+        const bool qreal = jh < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * i + 8 * kb);
+            u32x4_t v = {u.x, u.y, u.z, u.w}, z = {0u, 0u, 0u, 0u};
+            bq[hf][i] = gq == 0 && qreal ? v : z;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) O[hf][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run[hf] = -INFINITY;
+        l_run[hf] = 0.f;
     }
     const float c2 = a.scale2;
-    f32x4_t O[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) O[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
     const int rq = n16 >> 2, rr = n16 & 3;
     const int k_off0 = 2 * ((8 * (rq & 1) + rr) * g.d + 8 * kb);
     const int k_off1 = k_off0 + 2 * 4 * g.d;
@@ -1192,47 +1200,55 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
         const uint8_t* P1 = hbase + p1 * page_stride;
         const uint8_t* PK = (rq >> 1) ? P1 : P0;
         const uint8_t* PM = (kb >> 1) ? P1 : P0;
-        f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t D0[NH], D1[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) D0[hf] = D1[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             uint4 k0 = *reinterpret_cast<const uint4*>(PK + k_off0 + 64 * i);
             uint4 k1 = *reinterpret_cast<const uint4*>(PK + k_off1 + 64 * i);
-            D0 = mfma_bf16(u32x4_t{k0.x, k0.y, k0.z, k0.w}, bq[i], D0);
-            D1 = mfma_bf16(u32x4_t{k1.x, k1.y, k1.z, k1.w}, bq[i], D1);
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                D0[hf] = mfma_bf16(u32x4_t{k0.x, k0.y, k0.z, k0.w}, bq[hf][i], D0[hf]);
+                D1[hf] = mfma_bf16(u32x4_t{k1.x, k1.y, k1.z, k1.w}, bq[hf][i], D1[hf]);
+            }
         }
-        float sc[8], mx = -INFINITY;
         bool valid[8];
+        u32x4_t ap[NH];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int tok = ts + 8 * kb + e;
-            valid[e] = tok >= t_lo && tok < t_hi;
-            float s = quad_sum(e < 4 ? D0[e] : D1[e - 4]);
-            sc[e] = valid[e] ? s * c2 : -INFINITY;
-            mx = fmaxf(mx, sc[e]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        float pv[8], ps = 0.f;
+        for (int hf = 0; hf < NH; ++hf) {
+            float sc[8], mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pv[e] = valid[e] ? exp2f(sc[e] - m_new) : 0.f;
-            ps += pv[e];
-        }
-        l_run = fmaf(l_run, alpha, ps);
-        u32x4_t ap;
+            for (int e = 0; e < 8; ++e) {
+                const int tok = ts + 8 * kb + e;
+                valid[e] = tok >= t_lo && tok < t_hi;
+                float s = quad_sum(e < 4 ? D0[hf][e] : D1[hf][e - 4]);
+                sc[e] = valid[e] ? s * c2 : -INFINITY;
+                mx = fmaxf(mx, sc[e]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[hf], mx);
+            const float alpha = exp2f(m_run[hf] - m_new);
+            m_run[hf] = m_new;
+            float pv[8], ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hw, lw;
-            split_bf16(pv[2 * i], pv[2 * i + 1], hw, lw);
-            ap[i] = gq == 0 ? hw : (gq == 1 ? lw : 0u);
-        }
-        const float alpha_d = __shfl(alpha, 4 * kb);
-        if (__any(alpha_d != 1.0f)) {
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = valid[e] ? exp2f(sc[e] - m_new) : 0.f;
+                ps += pv[e];
+            }
+            l_run[hf] = fmaf(l_run[hf], alpha, ps);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) { O[s][0] *= alpha_d; O[s][1] *= alpha_d; }
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hw, lw;
+                split_bf16(pv[2 * i], pv[2 * i + 1], hw, lw);
+                ap[hf][i] = gq == 0 ? hw : (gq == 1 ? lw : 0u);
+            }
+            const float alpha_d = __shfl(alpha, 4 * kb);
+            if (__any(alpha_d != 1.0f)) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) { O[hf][s][0] *= alpha_d; O[hf][s][1] *= alpha_d; }
+            }
         }
         // values of tokens outside the item may be any bit pattern (NaN, Inf):
         // zero them in partial tiles, since 0 * NaN would reach the sum
@@ -1247,21 +1263,29 @@ __device__ __forceinline__ void mfma_item_bf16(const DecodeArgs& a, int b, int h
             uint4 v = ldg_stream(PM + v_off + 2 * 16 * s * kHalf);
             u32x4_t bv = {v.x, v.y, v.z, v.w};
             if (!full) bv &= vmask;
-            O[s] = mfma_bf16(ap, bv, O[s]);
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) O[hf][s] = mfma_bf16(ap[hf], bv, O[hf][s]);
         }
     }
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    __shared__ float sh_l[4], sh_m[4];
-    if (kb == 0 && gq == 0) { sh_l[jq] = l_run; sh_m[jq] = m_run; }
-    __syncthreads();
-    const float lj = sh_l[kb];
-    const float inv = 1.0f / lj;
-    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
-    float* dst = rec + kb * (g.d + kPartPad);
+    __shared__ float sh_l[NH][4], sh_m[NH][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (O[s][0] + O[s][1]) * inv;
-    if (n16 == 0) dst[g.d] = sh_m[kb] + log2f(lj);
+    for (int hf = 0; hf < NH; ++hf) {
+        float lr = l_run[hf];
+        lr += __shfl_xor(lr, 16);
+        lr += __shfl_xor(lr, 32);
+        if (kb == 0 && gq == 0) { sh_l[hf][jq] = lr; sh_m[hf][jq] = m_run[hf]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        const float lj = sh_l[hf][kb];
+        const float inv = 1.0f / lj;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) dst[16 * s + n16] = (O[hf][s][0] + O[hf][s][1]) * inv;
+        if (n16 == 0) dst[g.d] = sh_m[hf][kb] + log2f(lj);
+    }
 }
 
 // Grid = W one-wave workgroups, each walking its range of the balanced unit
@@ -1898,6 +1922,15 @@ __global__ __launch_bounds__(64) void decode_bf16_mfma_kernel(DecodeArgs a)
     walk_units(a, [&](int, int) {},
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_bf16(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// BF16 comparator, q/kv ratios 5 to 8: two four-head halves on each tile's loads.
+__global__ __launch_bounds__(64) void decode_bf16_mfma8_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int, int) {},
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_bf16<2>(a, b, h, lo, hi, rec, pace);
                });
 }
 

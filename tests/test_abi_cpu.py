@@ -117,7 +117,7 @@ def test_invalid_descriptors():
         (dict(num_q_heads=128, flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_ERR_UNSUPPORTED),
         (dict(num_q_heads=128, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
         (dict(num_q_heads=24, flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_ERR_UNSUPPORTED),  # 3
-        (dict(num_q_heads=40, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),  # ratio 5
+        (dict(num_q_heads=40, kind=kv4.KV4_KIND_BF16), kv4.KV4_OK),               # ratio 5
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=24), kv4.KV4_ERR_UNSUPPORTED),     # GQA 3
         (dict(num_q_heads=24), kv4.KV4_OK),                                    # ratio 3
         (dict(num_q_heads=40), kv4.KV4_OK),                                    # 5 (Qwen3-14B)

@@ -466,7 +466,7 @@ def test_valu_decode_flag():
         _int_case(Hq, Hkv, 32, 4, 64, ictx, seed=150 + Hq + Hkv, flags=kv4.KV4_FLAG_VALU_DECODE)
     ctxb = np.array([0, 15, 16, 17, 300, 1000, 3000])
     n = ctxb + 1
-    for Hq, Hkv in ((8, 2), (8, 4)):
+    for Hq, Hkv in ((8, 2), (8, 4), (16, 2)):
         H.log(f"case vector-ALU decode, BF16 kind, Hq={Hq} Hkv={Hkv}")
         cfg = W.scaled(W.CONFIGS["tiny"], seed=33, batch=len(ctxb), ctx_kind="fixed", ctx_fixed=tuple(ctxb),
                        q_heads=Hq, kv_heads=Hkv)
@@ -479,11 +479,11 @@ def test_valu_decode_flag():
         H.check_output(out, oracle.attend_dense(q, ks, vs, 1 / math.sqrt(128)), ATOL, RTOL)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 4), (4, 4)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 4), (4, 4), (16, 2), (10, 2)])
 def test_bf16_comparator(Hq, Hkv):
     """BF16 kind: pages hold the bf16 values exactly; output matches the
-    oracle's dense attention (q/kv ratios 4, 2 and 1, all on the matrix-core
-    kernel)."""
+    oracle's dense attention (q/kv ratios 4, 2, 1, 8 and 5, all on the
+    matrix core: one four-head half up to 4, two above)."""
     ctx = np.array([0, 15, 16, 17, 300, 1000, 3000])
     n = ctx + 1
     cfg = W.scaled(W.CONFIGS["tiny"], seed=31, batch=len(ctx), ctx_kind="fixed", ctx_fixed=tuple(ctx),
