@@ -60,7 +60,7 @@ int validate_desc(const kv4_cache_desc* d)
     // q/kv ratios: the matrix-core kernels take 1 .. 8 in halves of four q heads
     // (rows of heads past the ratio carry q = 0), and 16 as four halves on the
     // floating-point path of the mixed kind; the vector-ALU kernels take 1, 2,
-    // 4 and 8; KV8 (below) takes 4.
+    // 4 and 8; KV8 (below) takes 1 to 4.
     const int gqa = d->num_q_heads / d->num_kv_heads;
     const bool pow2 = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8;
     if (gqa > 8 && gqa != 16) return KV4_ERR_UNSUPPORTED;
@@ -73,7 +73,7 @@ int validate_desc(const kv4_cache_desc* d)
     if ((d->flags & KV4_FLAG_ROTATE_K) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
     // the integer path reads the INT4 pages and the INT8 ring
     if ((d->flags & KV4_FLAG_INT_PATH) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
-    if (d->kind == KV4_KIND_KV8 && d->num_q_heads != 4 * d->num_kv_heads) return KV4_ERR_UNSUPPORTED;
+    if (d->kind == KV4_KIND_KV8 && gqa > 4) return KV4_ERR_UNSUPPORTED;
     // KV8 pages are decoded on the matrix core only
     if (d->kind == KV4_KIND_KV8 && (d->flags & KV4_FLAG_VALU_DECODE)) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;

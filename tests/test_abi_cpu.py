@@ -118,7 +118,7 @@ def test_invalid_descriptors():
         (dict(num_q_heads=128, kind=kv4.KV4_KIND_BF16), kv4.KV4_ERR_UNSUPPORTED),
         (dict(num_q_heads=24, flags=kv4.KV4_FLAG_VALU_DECODE), kv4.KV4_ERR_UNSUPPORTED),  # 3
         (dict(num_q_heads=40, kind=kv4.KV4_KIND_BF16), kv4.KV4_OK),               # ratio 5
-        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=24), kv4.KV4_ERR_UNSUPPORTED),     # GQA 3
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=24), kv4.KV4_OK),                  # GQA 3
         (dict(num_q_heads=24), kv4.KV4_OK),                                    # ratio 3
         (dict(num_q_heads=40), kv4.KV4_OK),                                    # 5 (Qwen3-14B)
         (dict(num_q_heads=56, flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),       # 7
@@ -126,8 +126,9 @@ def test_invalid_descriptors():
         (dict(num_q_heads=24, kind=kv4.KV4_KIND_BF16), kv4.KV4_OK),            # 3
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
         (dict(kind=kv4.KV4_KIND_KV8), kv4.KV4_OK),
-        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_ERR_UNSUPPORTED),     # GQA 2
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_OK),                  # GQA 2
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=64), kv4.KV4_ERR_UNSUPPORTED),     # GQA 8
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=40), kv4.KV4_ERR_UNSUPPORTED),     # GQA 5
         (dict(kind=kv4.KV4_KIND_KV8, flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
         (dict(flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),
         (dict(flags=kv4.KV4_FLAG_INT_PATH | kv4.KV4_FLAG_ROTATE_K), kv4.KV4_OK),

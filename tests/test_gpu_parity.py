@@ -512,8 +512,8 @@ def test_bf16_comparator(Hq, Hkv):
 # position is protected (S = 0, R >= n).
 # ---------------------------------------------------------------------------
 
-def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0, pool_chunks=0):
-    Hq = 4 * Hkv
+def _kv8_case(Hkv, ctx, seed, waves=0, layers=1, layer=0, pool_chunks=0, ratio=4):
+    Hq = ratio * Hkv
     n = np.asarray(ctx, np.int64) + 1
     cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, seed=seed, batch=len(ctx),
                    ctx_kind="fixed", ctx_fixed=tuple(int(c) for c in ctx))
@@ -550,6 +550,14 @@ def test_kv8_kind(Hkv):
         H.log(f"case kv8 Hkv={Hkv} waves={waves}")
         o2 = _kv8_case(Hkv, ctx, seed=80 + Hkv, waves=waves)
         assert np.abs(o2 - out).max() <= 5e-5
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 3])
+def test_kv8_ratios(ratio):
+    """KV8 kind at q/kv ratios below 4 (the four-head matrix-core layout with
+    the heads past the ratio padded)."""
+    H.log(f"case kv8 ratio {ratio}")
+    _kv8_case(2, [0, 15, 16, 31, 32, 300, 1000, 2500], seed=90 + ratio, ratio=ratio)
 
 
 def test_kv8_layers_and_long_context():
