@@ -407,6 +407,52 @@ def time_step(c, cfg, n, knew, vnew, q, kv4, torch, tm, steps, warmup, flush=Non
                 partials_ms_median=float(np.median(tp)), waves=waves, pool_chunks=chunks)
 
 
+class _SharedPools:
+    """A second library handle over a built cache's pools with another q head
+    count (the pools depend on the kv heads only), in the shape time_step
+    expects of a cache."""
+
+    def __init__(self, built, num_q_heads, kv4, torch):
+        d = kv4.kv4_cache_desc.from_buffer_copy(built.desc)
+        d.num_q_heads = num_q_heads
+        self.desc, self.device, self._kv4, self._torch = d, built.cache.device, kv4, torch
+        self.handle = kv4.kv4_cache_create(d, built.cache.page_pool, built.cache.side_pool)
+        self._ws = None
+
+    def workspace(self, batch, max_ctx):
+        nb = self._kv4.kv4_decode_workspace_bytes(self.handle, batch, max_ctx)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = self._torch.empty(max(nb, 16), dtype=self._torch.uint8, device=self.device)
+        return self._ws
+
+    def close(self):
+        self._kv4.kv4_cache_free(self.handle)
+
+
+def ratio8_record(c, cfg, n, knew, vnew, H, W, kv4, torch, tm, args, dev):
+    """The same batch and pools decoded with 8 q heads per kv head (64 q / 8
+    kv: the Qwen3-32B head shape) on the matrix core (two four-head halves
+    per tile)."""
+    from types import SimpleNamespace
+    c8 = W.scaled(cfg, q_heads=8 * cfg.kv_heads)
+    q8 = H.to_dev_bf16(W.queries(c8, 0), str(dev))
+    sp = _SharedPools(c, c8.q_heads, kv4, torch)
+    try:
+        r = time_step(SimpleNamespace(cache=sp, slots=c.slots, block_tables=c.block_tables), c8, n, knew,
+                      vnew, q8, kv4, torch, tm, args.steps, args.warmup)
+    finally:
+        sp.close()
+    p8, d8 = partial_bytes_kv4(n, c8), decode_bytes_kv4(n, c8)
+    return {"workload": f"the same batch and pools with {c8.q_heads} q heads ({c8.q_heads}q/{c8.kv_heads}kv, "
+                        f"q/kv ratio 8: the Qwen3-32B head shape)",
+            "kernel": "decode_kv4_mfma8_kernel", "waves": r["waves"],
+            "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
+            "decode_partials_us": round(r["partials_ms"] * 1e3, 2),
+            "partials_alg_bytes": p8,
+            "partials_frac_hbm_peak": round(p8 / (r["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_attn_frac_hbm_peak": round(d8 / (r["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def read_ceiling(torch, dev, st, partial_bytes):
     """The read ceilings of this GPU (libkv4_roof.so): a 4 GiB stream, and
     random 2,560-byte blocks (one (page, kv head) block of the INT4 pool) in
@@ -580,6 +626,13 @@ def main():
             f"merge {r['merge_ms'] * 1e3:.1f} us, decode {r['decode_ms'] * 1e3:.1f} us "
             f"(median {r['decode_ms_median'] * 1e3:.1f}), waves {r['waves']}, pool chunks {r['pool_chunks']}")
 
+    ratio8 = None
+    if (not args.only_kv4 and not args.no_sub and cfg.name == "q8b256" and not args.rotate
+            and not args.valu_decode):
+        ratio8 = ratio8_record(caches["kv4"], cfg, n, knew, vnew, H, W, kv4, torch, tm, args, dev)
+        log(f"ratio 8: decode {ratio8['decode_attn_us']} us, partials {ratio8['decode_partials_us']} us "
+            f"({ratio8['partials_frac_hbm_peak']} of the HBM peak)")
+
     # bulk populate: the first 32 sequences' histories re-appended whole (after
     # every decode timing: it rewrites ring entries the step token owns)
     populate = prefill = None
@@ -694,6 +747,8 @@ def main():
         }
         line["speedup_vs_bf16_step"] = round(bstep / step_ms, 3)
         line["speedup_vs_bf16_decode"] = round(rb["decode_ms"] / r["decode_ms"], 3)
+    if ratio8 is not None:
+        line["ratio8"] = ratio8
     if populate is not None:
         line["populate"] = populate
     if prefill is not None:
