@@ -59,13 +59,16 @@ def _i32(vals, dev):
     return Guarded((len(vals),), torch.int32, torch.tensor(vals, dtype=torch.int32, device=dev), dev)
 
 
-@pytest.mark.parametrize("case", ["mixed_gqa4", "mixed_gqa2", "mixed_int_path", "kv8", "bf16"])
+@pytest.mark.parametrize("case", ["mixed_gqa4", "mixed_gqa2", "mixed_int_path", "kv8", "bf16", "mixed_gqa5",
+                                  "mixed_gqa8", "mixed_gqa16", "mixed_int_gqa8", "bf16_gqa8"])
 def test_out_of_range_device_values_stay_inside_buffers(case):
     dev = torch.device("cuda")
-    kind = {"kv8": kv4.KV4_KIND_KV8, "bf16": kv4.KV4_KIND_BF16}.get(case, kv4.KV4_KIND_MIXED)
+    kind = {"kv8": kv4.KV4_KIND_KV8, "bf16": kv4.KV4_KIND_BF16,
+            "bf16_gqa8": kv4.KV4_KIND_BF16}.get(case, kv4.KV4_KIND_MIXED)
     Hkv = 2
-    Hq = 4 if case == "mixed_gqa2" else 8
-    flags = kv4.KV4_FLAG_INT_PATH if case == "mixed_int_path" else 0
+    Hq = {"mixed_gqa2": 4, "mixed_gqa5": 10, "mixed_gqa8": 16, "mixed_gqa16": 32, "mixed_int_gqa8": 16,
+          "bf16_gqa8": 16}.get(case, 8)
+    flags = kv4.KV4_FLAG_INT_PATH if case in ("mixed_int_path", "mixed_int_gqa8") else 0
     S, R = (4, 16) if kind == kv4.KV4_KIND_MIXED else (0, 0)
     B, max_slots, max_pages, num_pages = 4, 5, 4, 16
     cap = max_pages * 16
