@@ -699,7 +699,8 @@ int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_b
         return KV4_ERR_INVALID_ARG;
     if (batch < 1 || total < 0 || max_seqlen < 1 || !std::isfinite(sm_scale)) return KV4_ERR_INVALID_ARG;
     if (out_dtype != KV4_OUT_F32 && out_dtype != KV4_OUT_BF16) return KV4_ERR_INVALID_ARG;
-    // grid (q heads, sequences, query blocks): y and z are limited to 65,536
+    // grid (q heads x 16 query blocks, sequences, groups of 16 query blocks): the
+    // sequences are limited to 65,536, and query positions to 65,536 blocks
     if (max_seqlen > 65536 * kv4::kPreQ || batch > 65536) return KV4_ERR_CAPACITY;
     if (total == 0) return KV4_OK;
     const kv4_cache_desc& d = cache->desc;
@@ -717,7 +718,8 @@ int kv4_prefill_attn(const kv4_cache* cache, const void* q_bf16, const void* k_b
     a.Hkv = d.num_kv_heads;
     a.gqa = d.num_q_heads / d.num_kv_heads;
     a.scale2 = sm_scale * 1.4426950408889634f;
-    dim3 grid((unsigned)a.Hq, (unsigned)batch, (unsigned)((max_seqlen + kv4::kPreQ - 1) / kv4::kPreQ));
+    constexpr int kGroupQ = kv4::kPreGroup * kv4::kPreQ;
+    dim3 grid((unsigned)(a.Hq * kv4::kPreGroup), (unsigned)batch, (unsigned)((max_seqlen + kGroupQ - 1) / kGroupQ));
 #ifdef KV4_VALIDATE
     hipLaunchKernelGGL(kv4::validate_prefill_kernel, dim3((unsigned)std::min(1024, (batch + 255) / 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a);

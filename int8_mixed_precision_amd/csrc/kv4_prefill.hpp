@@ -53,6 +53,7 @@ struct PrefillArgs {
 constexpr int kPrefillKeys = 32;
 constexpr int kPrefillRows = 2;
 constexpr int kPreQ = 4 * 16 * kPrefillRows;   // queries per workgroup
+constexpr int kPreGroup = 16;                  // query blocks dispatched together
 
 // Maximum of three floats in one v_max3_f32.  fmaxf on a matrix-core result
 // costs an extra canonicalising v_max per operand (the compiler cannot tell
@@ -87,18 +88,22 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a)
     constexpr int QB = 4 * 16 * RB;                            // queries per workgroup
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n16 = lane & 15, kb = lane >> 4;
-    // grid (q head, sequence, query block) with the query blocks in reverse:
-    // workgroups are dispatched x fastest, so the last (heaviest: the most
-    // causal key tiles) query blocks of every sequence and head start first
-    // and the cheap early blocks fill the tail.
+    // grid (q head x 16 query blocks of a group, sequence, group of query
+    // blocks), groups and blocks in reverse.  Workgroups are dispatched x
+    // fastest, so the 16 blocks of one group of one sequence run together (at
+    // Hq = 32 and two workgroups per CU, one group fills the GPU), all reading
+    // the same prefix of K and V, while the heaviest groups (the most causal
+    // key tiles) of every sequence start first and the cheap early ones fill
+    // the tail.
     // Workgroups go to the eight XCDs in turn, so with a multiple of 8 q heads
-    // every workgroup with x % 8 == c runs on XCD c.  x is taken as q head
-    // c Hq/8 + x/8: the q heads of a kv head (consecutive), which read the same
-    // K and V tiles, then share one XCD's L2 (at Hq = 32 and 8 kv heads, XCD c
-    // holds exactly the four q heads of kv head c).
-    const int xq = (int)blockIdx.x;
+    // every workgroup with x % 8 == c runs on XCD c.  x % Hq is taken as q head
+    // c Hq/8 + (x % Hq)/8: the q heads of a kv head (consecutive), which read
+    // the same K and V tiles, then share one XCD's L2 (at Hq = 32 and 8 kv
+    // heads, XCD c holds exactly the four q heads of kv head c).
+    const int xq = (int)blockIdx.x % a.Hq, qlow = (int)blockIdx.x / a.Hq;
     const int j = (a.Hq & 7) ? xq : (xq & 7) * (a.Hq >> 3) + (xq >> 3);
-    const int b = blockIdx.y, qb = (int)gridDim.z - 1 - (int)blockIdx.z;
+    const int b = blockIdx.y;
+    const int qb = kPreGroup * ((int)gridDim.z - 1 - (int)blockIdx.z) + kPreGroup - 1 - qlow;
     const int t0 = clampi(a.cu[b], 0, a.total);
     const int L = min(clampi(a.cu[b + 1], t0, a.total) - t0, a.max_len);
     if (QB * qb >= L) return;                             // uniform over the workgroup
