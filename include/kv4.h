@@ -193,9 +193,13 @@ int kv4_cache_required_bytes(const kv4_cache_desc* desc, size_t* page_pool_bytes
 /*
  * Create a handle over caller-owned pools.  page_pool / side_pool are device
  * buffers of at least the sizes kv4_cache_required_bytes returns (side_pool
- * may be NULL when that size is 0).  Pools need no initialisation: a position
- * is only ever read after the append that wrote it.  *out receives a host
- * object freed with kv4_cache_free.  No device work.
+ * may be NULL when that size is 0), 16-byte aligned (hipMalloc and torch
+ * allocations are): the kernels move 16-byte words.  Pools need no
+ * initialisation: a position is only ever read after the append that wrote
+ * it.  *out receives a host object freed with kv4_cache_free.  No device work.
+ * Errors: those of the description's checks (as kv4_cache_required_bytes),
+ * KV4_ERR_INVALID_ARG (a needed pool or out NULL, a pool not 16-byte
+ * aligned), KV4_ERR_CAPACITY (a pool smaller than required).
  */
 int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_pool_bytes,
                      void* side_pool, size_t side_pool_bytes, kv4_cache** out);

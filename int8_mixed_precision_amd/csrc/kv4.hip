@@ -520,6 +520,8 @@ int kv4_cache_create(const kv4_cache_desc* desc, void* page_pool, size_t page_po
     sizes(g, &need_pages, &need_side, nullptr);
     if (page_pool == nullptr) return KV4_ERR_INVALID_ARG;
     if (need_side > 0 && side_pool == nullptr) return KV4_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(page_pool) | reinterpret_cast<uintptr_t>(side_pool)) & 15u)
+        return KV4_ERR_INVALID_ARG;
     if (page_pool_bytes < need_pages || side_pool_bytes < need_side) return KV4_ERR_CAPACITY;
     kv4_cache* c = new (std::nothrow) kv4_cache;
     if (c == nullptr) return KV4_ERR_CAPACITY;

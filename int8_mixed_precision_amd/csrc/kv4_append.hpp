@@ -38,38 +38,66 @@ struct AppendArgs {
 
 // DPP move inside a 16-lane row (every lane active, every source in the row).
 template <int CTRL>
-__device__ __forceinline__ float row_mov(float x)
+__device__ __forceinline__ int row_mov(int x)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+    return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, true);
 }
+
+// Order-preserving integer key of a binary32 value: for non-NaN a and b,
+// a < b exactly when fkey(a) < fkey(b) as signed integers (-0 sorts just
+// below +0).  The reductions compare keys, which needs no canonicalisation of
+// the moved operands and lets each DPP move fuse into its min or max.
+__device__ __forceinline__ int fkey(float x)
+{
+    const int i = __float_as_int(x);
+    return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float fkey_value(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
 
 // Minimum and maximum over aligned groups of LANES (16, 32 or 64) lanes: quad
 // swaps and row rotations inside each 16-lane row, then the row swaps of
 // v_permlane16_swap / v_permlane32_swap.  Exact for any order.
 template <int LANES>
-__device__ __forceinline__ void group_minmax(float& lo, float& hi)
+__device__ __forceinline__ void group_minmax_keys(int& lo, int& hi)
 {
     static_assert(LANES == 16 || LANES == 32 || LANES == 64, "group of 16, 32 or 64 lanes");
-    lo = fminf(lo, row_mov<0xB1>(lo));          // quad_perm [1,0,3,2]
-    hi = fmaxf(hi, row_mov<0xB1>(hi));
-    lo = fminf(lo, row_mov<0x4E>(lo));          // quad_perm [2,3,0,1]
-    hi = fmaxf(hi, row_mov<0x4E>(hi));
-    lo = fminf(lo, row_mov<0x124>(lo));         // row_ror 4
-    hi = fmaxf(hi, row_mov<0x124>(hi));
-    lo = fminf(lo, row_mov<0x128>(lo));         // row_ror 8
-    hi = fmaxf(hi, row_mov<0x128>(hi));
+    lo = min(lo, row_mov<0xB1>(lo));            // quad_perm [1,0,3,2]
+    hi = max(hi, row_mov<0xB1>(hi));
+    lo = min(lo, row_mov<0x4E>(lo));            // quad_perm [2,3,0,1]
+    hi = max(hi, row_mov<0x4E>(hi));
+    lo = min(lo, row_mov<0x124>(lo));           // row_ror 4
+    hi = max(hi, row_mov<0x124>(hi));
+    lo = min(lo, row_mov<0x128>(lo));           // row_ror 8
+    hi = max(hi, row_mov<0x128>(hi));
     if constexpr (LANES >= 32) {
-        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
-        lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
-        hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+        auto a = __builtin_amdgcn_permlane16_swap((unsigned)lo, (unsigned)lo, false, false);
+        lo = min((int)a[0], (int)a[1]);
+        auto b = __builtin_amdgcn_permlane16_swap((unsigned)hi, (unsigned)hi, false, false);
+        hi = max((int)b[0], (int)b[1]);
     }
     if constexpr (LANES == 64) {
-        auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
-        lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
-        hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+        auto a = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)lo, false, false);
+        lo = min((int)a[0], (int)a[1]);
+        auto b = __builtin_amdgcn_permlane32_swap((unsigned)hi, (unsigned)hi, false, false);
+        hi = max((int)b[0], (int)b[1]);
     }
+}
+
+// Correctly rounded binary32 quotient a / B for a constant B (15 or 127) and
+// any a >= 0: q0 = a * RN(1/B), the residual a - B q0 taken exactly by an fma,
+// and one correction step q0 + residual * RN(1/B), rounded once (Markstein's
+// correction theorem: a correctly rounded reciprocal and a quotient within
+// one ulp give the correctly rounded quotient).  Checked against the binary64
+// quotient rounded to binary32 for every finite a >= 0, subnormals included,
+// for B = 15 and 127; a = +inf (an offset that overflowed binary16) gives +inf.
+template <int B>
+__device__ __forceinline__ float div_rn_const(float a)
+{
+    constexpr float y = 1.0f / (float)B;
+    const float q0 = __fmul_rn(a, y);
+    const float e = __builtin_fmaf(-(float)B, q0, a);
+    const float q = __builtin_fmaf(e, y, q0);
+    return a == __builtin_inff() ? a : q;
 }
 
 // INT4 parameters of a group whose values are spread over `lanes` consecutive
@@ -77,13 +105,14 @@ __device__ __forceinline__ void group_minmax(float& lo, float& hi)
 template <int LANES>
 __device__ __forceinline__ void int4_params(float x0, float x1, uint16_t& db, uint16_t& mb)
 {
-    float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
-    group_minmax<LANES>(lo, hi);
-    mb = plus_zero16(f32_to_f16_bits(lo));
+    const int k0 = fkey(x0), k1 = fkey(x1);
+    int lo = min(k0, k1), hi = max(k0, k1);
+    group_minmax_keys<LANES>(lo, hi);
+    mb = plus_zero16(f32_to_f16_bits(fkey_value(lo)));
     float mf = half_bits_to_float(mb);
-    float r = hi - mf;
+    float r = fkey_value(hi) - mf;
     db = 0;
-    if (r > 0.0f) db = plus_zero16(f32_to_f16_bits(__fdiv_rn(r, 15.0f)));
+    if (r > 0.0f) db = plus_zero16(f32_to_f16_bits(div_rn_const<15>(r)));
 }
 
 __device__ __forceinline__ uint32_t int4_code_exact(float x, double D, double M, uint16_t db)
@@ -112,14 +141,17 @@ __device__ __forceinline__ uint32_t int4_code_exact(float x, double D, double M,
 // nearest code; near a midpoint, or for non-finite operands, the binary64 test
 // above decides.
 // The binary32 candidate of int4_code, without a branch: the code, and
-// whether the binary64 test must decide instead.
+// whether the binary64 test must decide instead.  u - rint(u) is exact, so
+// |u - rint(u)| >= 1/2 - 2^-14 (or a NaN) marks u as within 2^-14 of a
+// half-integer; the test does not look at which half-integer, since taking the
+// binary64 decision where the binary32 one would also do is always correct.
 __device__ __forceinline__ uint32_t int4_code_fast(float x, float Df, float Mf, uint16_t db, bool& exact)
 {
     const float u = (x - Mf) * __builtin_amdgcn_rcpf(Df);
-    const float fl = floorf(u);
-    const bool near = fabsf(u - fl - 0.5f) < 0x1p-14f && fl >= 0.0f && fl <= 14.0f;
+    const float r = rintf(u);
+    const bool near = !(fabsf(u - r) < 0.5f - 0x1p-14f);
     exact = db != 0 && (near || !(fabsf(u) < 64.0f) || !(Df < 65536.0f));
-    return db == 0 ? 0u : (uint32_t)fminf(fmaxf(rintf(u), 0.0f), 15.0f);
+    return db == 0 ? 0u : (uint32_t)fminf(fmaxf(r, 0.0f), 15.0f);
 }
 
 __device__ __forceinline__ uint32_t int4_code(float x, float Df, float Mf, uint16_t db)
@@ -132,16 +164,228 @@ __device__ __forceinline__ uint32_t int4_code(float x, float Df, float Mf, uint1
 // Full-wave (64 lanes, 128 channels) INT8 scale.
 __device__ __forceinline__ uint16_t int8_scale(float x0, float x1)
 {
-    float a = fmaxf(fabsf(x0), fabsf(x1)), unused = a;
-    group_minmax<64>(unused, a);
-    return plus_zero16(f32_to_f16_bits(__fdiv_rn(a, 127.0f)));
+    // the key of a value >= 0 is its bit pattern
+    int a = max(__float_as_int(fabsf(x0)), __float_as_int(fabsf(x1))), unused = a;
+    group_minmax_keys<64>(unused, a);
+    return plus_zero16(f32_to_f16_bits(div_rn_const<127>(__int_as_float(a))));
 }
 
-// Tokens of a whole half page quantized side by side.  One at a time measured
-// fastest: at the bulk populate of 145,101 tokens, groups of 2, 4 and 8
-// overlap their dependency chains but hold more registers, and the fewer waves
-// per SIMD cost more (413 us for 1, 455 us for 2, 862 us for 8).
-constexpr int kAppendGroup = 1;
+// Partner value of lane ^ MASK (MASK = 1, 2 or 4: inside groups of 8 lanes),
+// through ds_swizzle's bit mode (and-mask 0x1F, xor-mask MASK), which leaves
+// the vector ALU free.
+template <int MASK>
+__device__ __forceinline__ float lane_xor(float x)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (MASK << 10) | 0x1F));
+}
+
+// Minimum and maximum of 16 values in IEEE minimum / maximum (no NaN in the
+// inputs; -0 below +0), three operands per instruction.
+__device__ __forceinline__ void minmax16(const float (&x)[16], float& lo, float& hi)
+{
+    lo = __builtin_elementwise_minimum(x[0], x[1]);
+    hi = __builtin_elementwise_maximum(x[0], x[1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) {
+        lo = __builtin_elementwise_minimum(__builtin_elementwise_minimum(lo, x[j]), x[j + 1]);
+        hi = __builtin_elementwise_maximum(__builtin_elementwise_maximum(hi, x[j]), x[j + 1]);
+    }
+}
+
+// INT4 parameters from a group's minimum and maximum (the rule of int4_params).
+__device__ __forceinline__ void int4_params_from(float lo, float hi, uint16_t& db, uint16_t& mb)
+{
+    mb = plus_zero16(f32_to_f16_bits(lo));
+    const float r = hi - half_bits_to_float(mb);
+    db = r > 0.0f ? plus_zero16(f32_to_f16_bits(div_rn_const<15>(r))) : (uint16_t)0;
+}
+
+// Codes of 16 values under (Delta, m); nibble k of word w[k / 8] is value k.
+// The binary32 decision of int4_code_fast with two simplifications that give
+// the same codes: a zero Delta takes the reciprocal 0 (u = 0, code 0), and
+// there is no test on |u| or Delta, because where |u| >= 64 (or Delta is
+// infinite and m finite, u = 0) the clamped nearest integer of u is already
+// the exact code.  Only the largest |u - rint(u)| of the 16 values is tested:
+// when it lies within 2^-14 of 1/2 (or is a NaN) each value is tested again
+// and the binary64 decision replaces the codes of those that need it.
+__device__ __forceinline__ void int4_codes16(const float (&x)[16], uint16_t db, uint16_t mb, uint32_t (&w)[2])
+{
+    const float D = half_bits_to_float(db), M = half_bits_to_float(mb);
+    const float rD = db != 0 ? __builtin_amdgcn_rcpf(D) : 0.0f;
+    constexpr float kMargin = 0.5f - 0x1p-14f;
+    float c[16], dev = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float u = (x[j] - M) * rD;
+        c[j] = rintf(u);
+        dev = __builtin_elementwise_maximum(dev, fabsf(u - c[j]));
+    }
+    if (!(dev < kMargin)) {                      // rare: near a midpoint
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float u = (x[j] - M) * rD;
+            if (!(fabsf(u - rintf(u)) < kMargin))
+                c[j] = (float)int4_code_exact(x[j], (double)D, (double)M, db);
+        }
+    }
+    // two codes per byte, 16 c1 + c0, converted and placed by v_cvt_pk_u8_f32
+    w[0] = w[1] = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float c0 = __builtin_amdgcn_fmed3f(c[2 * i], 0.0f, 15.0f);
+        const float c1 = __builtin_amdgcn_fmed3f(c[2 * i + 1], 0.0f, 15.0f);
+        w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c1, 16.0f, c0), i & 3, w[i >> 2]);
+    }
+}
+
+// A whole half page of new tokens (8 positions pos0 .. pos0 + 7, pos0 a
+// multiple of 8) for one kv head, one wave: lane 8 t + b holds channels
+// 16 b .. 16 b + 15 of token t, so a group's range, Delta and m are formed
+// from 16 values per lane (G / 16 lanes per group) and a token's K code row
+// is written as whole words.  The V code words, one per channel over the 8
+// tokens, take a byte transpose through LDS.  Positions protected at the new
+// length also get their INT8 side entries.
+template <int G>
+__device__ __forceinline__ void append_half_page(const AppendArgs& a, int64_t row, int h, uint8_t* pb,
+                                                 int pos0, int p1, uint8_t* ring)
+{
+    static_assert(G == 32 || G == 64 || G == 128, "group of 32, 64 or 128 channels");
+    constexpr int LB = G / 16;                   // lanes per group
+    __shared__ uint8_t vt[8][64];                // [b][token-pair byte j][t]
+    const Geo& g = a.g;
+    const int lane = threadIdx.x, t = lane >> 3, b = lane & 7;
+    const int64_t src = ((row + t) * g.Hkv + h) * g.d + 16 * b;
+    const uint4 kq0 = *reinterpret_cast<const uint4*>(a.k + src);
+    const uint4 kq1 = *reinterpret_cast<const uint4*>(a.k + src + 8);
+    const uint4 vq0 = *reinterpret_cast<const uint4*>(a.v + src);
+    const uint4 vq1 = *reinterpret_cast<const uint4*>(a.v + src + 8);
+    const uint32_t kw[8] = {kq0.x, kq0.y, kq0.z, kq0.w, kq1.x, kq1.y, kq1.z, kq1.w};
+    const uint32_t vw[8] = {vq0.x, vq0.y, vq0.z, vq0.w, vq1.x, vq1.y, vq1.z, vq1.w};
+    float kx[16], vx[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        kx[2 * i] = bf16_lo(kw[i]);
+        kx[2 * i + 1] = bf16_hi(kw[i]);
+        vx[2 * i] = bf16_lo(vw[i]);
+        vx[2 * i + 1] = bf16_hi(vw[i]);
+    }
+    if (g.rot) {
+        // channel bits 0-3 in the lane, bits 4-6 on lane bits 0-2: the
+        // stages in the order of the channel bits, as everywhere else
+        wht_local(kx);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = lane_xor<1>(kx[j]);
+            kx[j] = (b & 1) ? p - kx[j] : kx[j] + p;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = lane_xor<2>(kx[j]);
+            kx[j] = (b & 2) ? p - kx[j] : kx[j] + p;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = lane_xor<4>(kx[j]);
+            kx[j] = (b & 4) ? p - kx[j] : kx[j] + p;
+        }
+        wht_scale(kx);
+    }
+    // ---- INT4 parameters: the group's range over LB lanes
+    float klo, khi, vlo, vhi;
+    minmax16(kx, klo, khi);
+    minmax16(vx, vlo, vhi);
+    if constexpr (LB >= 2) {
+        klo = __builtin_elementwise_minimum(klo, lane_xor<1>(klo));
+        khi = __builtin_elementwise_maximum(khi, lane_xor<1>(khi));
+        vlo = __builtin_elementwise_minimum(vlo, lane_xor<1>(vlo));
+        vhi = __builtin_elementwise_maximum(vhi, lane_xor<1>(vhi));
+    }
+    if constexpr (LB >= 4) {
+        klo = __builtin_elementwise_minimum(klo, lane_xor<2>(klo));
+        khi = __builtin_elementwise_maximum(khi, lane_xor<2>(khi));
+        vlo = __builtin_elementwise_minimum(vlo, lane_xor<2>(vlo));
+        vhi = __builtin_elementwise_maximum(vhi, lane_xor<2>(vhi));
+    }
+    if constexpr (LB >= 8) {
+        klo = __builtin_elementwise_minimum(klo, lane_xor<4>(klo));
+        khi = __builtin_elementwise_maximum(khi, lane_xor<4>(khi));
+        vlo = __builtin_elementwise_minimum(vlo, lane_xor<4>(vlo));
+        vhi = __builtin_elementwise_maximum(vhi, lane_xor<4>(vhi));
+    }
+    uint16_t kdb, kmb, vdb, vmb;
+    int4_params_from(klo, khi, kdb, kmb);
+    int4_params_from(vlo, vhi, vdb, vmb);
+    uint32_t kc[2], vc[2];
+    int4_codes16(kx, kdb, kmb, kc);
+    int4_codes16(vx, vdb, vmb, vc);
+
+    const int tp = pos0 % kPage + t, grp = b / LB;
+    // K codes: words 2b and 2b + 1 of the token's row
+    uint32_t* krow = reinterpret_cast<uint32_t*>(pb + g.off_kc + tp * (g.d / 2));
+    krow[kpos(2 * b)] = kc[0];
+    krow[kpos(2 * b + 1)] = kc[1];
+    if (b % LB == 0) {
+        reinterpret_cast<uint32_t*>(pb + g.off_kdm)[tp * g.ng + grp] = (uint32_t)kdb | ((uint32_t)kmb << 16);
+        reinterpret_cast<uint16_t*>(pb + g.off_vd)[grp * kPage + tp] = vdb;
+        reinterpret_cast<uint16_t*>(pb + g.off_vm)[tp * g.ng + grp] = vmb;
+    }
+    // V codes: byte j of lane (t, b) holds channels 16 b + 2 j, + 1 of token
+    // t; after the transpose lane (t, b) holds byte t of every token, i.e.
+    // channels 16 b + 2 t and 16 b + 2 t + 1 for tokens 0..7, and unzips the
+    // nibbles into the two channels' code words.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vt[b][8 * j + t] = (uint8_t)(vc[j >> 2] >> (8 * (j & 3)));
+    __syncthreads();
+    const uint2 col = *reinterpret_cast<const uint2*>(&vt[b][8 * t]);
+    __syncthreads();                             // vt is free for the next half page
+    // byte t' = lo | hi << 4 (lo: channel 2t, hi: channel 2t + 1, token t')
+    const uint32_t x0 = col.x, x1 = col.y;
+    const uint32_t sel = 0x000F000Fu;
+    const uint32_t l0 = (x0 & sel) | ((x0 >> 4) & ~sel), l1 = (x1 & sel) | ((x1 >> 4) & ~sel);
+    const uint32_t h0 = ((x0 >> 4) & sel) | ((x0 >> 8) & ~sel), h1 = ((x1 >> 4) & sel) | ((x1 >> 8) & ~sel);
+    // bytes 0 and 2 of each hold two tokens' nibbles
+    const uint32_t lo_word = __builtin_amdgcn_perm(l1, l0, 0x06040200u);
+    const uint32_t hi_word = __builtin_amdgcn_perm(h1, h0, 0x06040200u);
+    uint32_t* vwords = reinterpret_cast<uint32_t*>(pb + g.off_vc) + ((pos0 / kHalf) & 1) * g.d;
+    vwords[vpos(16 * b + 2 * t)] = lo_word;
+    vwords[vpos(16 * b + 2 * t + 1)] = hi_word;
+
+    // ---- INT8 side entries of protected positions
+    if (ring != nullptr && (pos0 < g.S || pos0 + kHalf > p1 - g.R)) {
+        const int pos = pos0 + t;
+        float ka = 0.0f, va = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            ka = __builtin_elementwise_maximum(ka, fabsf(kx[j]));
+            va = __builtin_elementwise_maximum(va, fabsf(vx[j]));
+        }
+        ka = __builtin_elementwise_maximum(ka, lane_xor<1>(ka));
+        va = __builtin_elementwise_maximum(va, lane_xor<1>(va));
+        ka = __builtin_elementwise_maximum(ka, lane_xor<2>(ka));
+        va = __builtin_elementwise_maximum(va, lane_xor<2>(va));
+        ka = __builtin_elementwise_maximum(ka, lane_xor<4>(ka));
+        va = __builtin_elementwise_maximum(va, lane_xor<4>(va));
+        if (pos < g.S || pos >= p1 - g.R) {
+            const int e = pos < g.S ? pos : g.S + (pos - g.S) % g.R;
+            const uint16_t sk = plus_zero16(f32_to_f16_bits(div_rn_const<127>(ka)));
+            const uint16_t sv = plus_zero16(f32_to_f16_bits(div_rn_const<127>(va)));
+            const float Sk = half_bits_to_float(sk), Sv = half_bits_to_float(sv);
+            uint32_t kb[4] = {0u, 0u, 0u, 0u};
+            uint8_t* vr = ring + (int64_t)g.SR32 * g.d;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                kb[j >> 2] |= (uint32_t)(int8_code(kx[j], Sk, sk) & 0xFF) << (8 * (j & 3));
+                vr[ring_vbyte(e, 16 * b + j)] = (uint8_t)int8_code(vx[j], Sv, sv);
+            }
+            *reinterpret_cast<uint4*>(ring + (int64_t)e * g.d + 16 * b) = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+            if (b == 0) {
+                uint16_t* sc = reinterpret_cast<uint16_t*>(ring + (int64_t)2 * g.SR32 * g.d);
+                sc[e] = sk;
+                sc[g.SR32 + e] = sv;
+            }
+        }
+    }
+}
 
 // One wave per (sequence, kv head, 8-token half page) of new tokens; the wave
 // owns the half page's V code words, so read-modify-write of nibbles is
@@ -172,92 +416,11 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
         uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
         uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hp & 1) * g.d;
         const int q0 = vpos(2 * lane), q1 = vpos(2 * lane + 1);
-        // every token of the half page is loaded before the first is quantized
-        // (one load latency per half page in a bulk append)
-        uint32_t kkr[kHalf], vvr[kHalf];
-        if (t_hi - t_lo == kHalf && !(ring != nullptr && (t_lo < g.S || t_hi > p1 - g.R))) {
-            // A whole half page with no INT8 side entry (the bulk of a
-            // populate): no test per token, the binary64 decision only for
-            // the lanes that need it (after the binary32 codes of a group of
-            // kAppendGroup tokens), and the V code words written whole, with
-            // no read: the half page owns every nibble of them.
-#pragma unroll
-            for (int i = 0; i < kHalf; ++i) {
-                const int64_t src = ((int64_t)(row0 + (t_lo + i - p0)) * g.Hkv + h) * g.d;
-                kkr[i] = *reinterpret_cast<const uint32_t*>(a.k + src + 2 * lane);
-                vvr[i] = *reinterpret_cast<const uint32_t*>(a.v + src + 2 * lane);
-            }
-            uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-            for (int i0 = 0; i0 < kHalf; i0 += kAppendGroup) {
-                float kx[kAppendGroup][2], vx[kAppendGroup][2];
-#pragma unroll
-                for (int j = 0; j < kAppendGroup; ++j) {
-                    kx[j][0] = bf16_lo(kkr[i0 + j]);
-                    kx[j][1] = bf16_hi(kkr[i0 + j]);
-                    vx[j][0] = bf16_lo(vvr[i0 + j]);
-                    vx[j][1] = bf16_hi(vvr[i0 + j]);
-                    if (g.rot) {
-                        wht_local(kx[j]);
-#pragma unroll
-                        for (int m = 1; m < 64; m <<= 1) wht_lanes(kx[j], m);
-                        wht_scale(kx[j]);
-                    }
-                }
-                uint16_t kdb[kAppendGroup], kmb[kAppendGroup], vdb[kAppendGroup], vmb[kAppendGroup];
-#pragma unroll
-                for (int j = 0; j < kAppendGroup; ++j) {
-                    int4_params<LPG>(kx[j][0], kx[j][1], kdb[j], kmb[j]);
-                    int4_params<LPG>(vx[j][0], vx[j][1], vdb[j], vmb[j]);
-                }
-                uint32_t kc[kAppendGroup][2], vc[kAppendGroup][2];
-                bool any_exact = false;
-#pragma unroll
-                for (int j = 0; j < kAppendGroup; ++j) {
-                    const float KD = half_bits_to_float(kdb[j]), KM = half_bits_to_float(kmb[j]);
-                    const float VD = half_bits_to_float(vdb[j]), VM = half_bits_to_float(vmb[j]);
-                    bool e0, e1, e2, e3;
-                    kc[j][0] = int4_code_fast(kx[j][0], KD, KM, kdb[j], e0);
-                    kc[j][1] = int4_code_fast(kx[j][1], KD, KM, kdb[j], e1);
-                    vc[j][0] = int4_code_fast(vx[j][0], VD, VM, vdb[j], e2);
-                    vc[j][1] = int4_code_fast(vx[j][1], VD, VM, vdb[j], e3);
-                    any_exact |= e0 | e1 | e2 | e3;
-                }
-                if (__builtin_amdgcn_ballot_w64(any_exact)) {        // rare: near a midpoint
-#pragma unroll
-                    for (int j = 0; j < kAppendGroup; ++j) {
-                        const float KD = half_bits_to_float(kdb[j]), KM = half_bits_to_float(kmb[j]);
-                        const float VD = half_bits_to_float(vdb[j]), VM = half_bits_to_float(vmb[j]);
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            bool ek, ev;
-                            (void)int4_code_fast(kx[j][e], KD, KM, kdb[j], ek);
-                            (void)int4_code_fast(vx[j][e], VD, VM, vdb[j], ev);
-                            if (ek) kc[j][e] = int4_code_exact(kx[j][e], (double)KD, (double)KM, kdb[j]);
-                            if (ev) vc[j][e] = int4_code_exact(vx[j][e], (double)VD, (double)VM, vdb[j]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < kAppendGroup; ++j) {
-                    const int i = i0 + j, tp = (t_lo + i) % kPage;
-                    pb[g.off_kc + tp * (g.d / 2) + 4 * kpos(lane >> 2) + (lane & 3)] =
-                        (uint8_t)(kc[j][0] | (kc[j][1] << 4));
-                    w0 |= vc[j][0] << (4 * i);
-                    w1 |= vc[j][1] << (4 * i);
-                    if ((lane % LPG) == 0) {
-                        uint16_t* kdm = reinterpret_cast<uint16_t*>(pb + g.off_kdm) + tp * 2 * g.ng + 2 * grp;
-                        kdm[0] = kdb[j];
-                        kdm[1] = kmb[j];
-                        reinterpret_cast<uint16_t*>(pb + g.off_vd)[grp * kPage + tp] = vdb[j];
-                        reinterpret_cast<uint16_t*>(pb + g.off_vm)[tp * g.ng + grp] = vmb[j];
-                    }
-                }
-            }
-            vw[q0] = w0;
-            vw[q1] = w1;
+        if (t_hi - t_lo == kHalf) {
+            append_half_page<G>(a, (int64_t)row0 + (t_lo - p0), h, pb, t_lo, p1, ring);
             continue;
         }
+        uint32_t kkr[kHalf], vvr[kHalf];
         uint32_t w0 = vw[q0], w1 = vw[q1];
 #pragma unroll
         for (int i = 0; i < kHalf; ++i) {

@@ -173,6 +173,9 @@ def test_create_errors():
     assert L_.kv4_cache_create(ctypes.byref(d), f, pages, f, side - 1, ctypes.byref(h)) == kv4.KV4_ERR_CAPACITY
     assert L_.kv4_cache_create(ctypes.byref(d), f, pages, None, side, ctypes.byref(h)) == kv4.KV4_ERR_INVALID_ARG
     assert L_.kv4_cache_create(ctypes.byref(d), f, pages, f, side, None) == kv4.KV4_ERR_INVALID_ARG
+    odd = ctypes.c_void_p((1 << 20) + 8)                 # pools must be 16-byte aligned
+    assert L_.kv4_cache_create(ctypes.byref(d), odd, pages, f, side, ctypes.byref(h)) == kv4.KV4_ERR_INVALID_ARG
+    assert L_.kv4_cache_create(ctypes.byref(d), f, pages, odd, side, ctypes.byref(h)) == kv4.KV4_ERR_INVALID_ARG
     assert L_.kv4_cache_free(None) == kv4.KV4_OK
 
 
