@@ -245,8 +245,26 @@ __device__ __forceinline__ void int4_codes16(const float (&x)[16], uint16_t db, 
 // is written as whole words.  The V code words, one per channel over the 8
 // tokens, take a byte transpose through LDS.  Positions protected at the new
 // length also get their INT8 side entries.
+// The bf16 K and V of a whole half page in the layout of append_half_page:
+// lane 8t + b holds channels 16 b .. 16 b + 15 of token t (row `row` + t).
+struct HalfPageIn {
+    uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ HalfPageIn load_half_page(const AppendArgs& a, int64_t row, int h)
+{
+    const int lane = threadIdx.x, t = lane >> 3, b = lane & 7;
+    const int64_t src = ((row + t) * a.g.Hkv + h) * a.g.d + 16 * b;
+    HalfPageIn in;
+    in.k0 = *reinterpret_cast<const uint4*>(a.k + src);
+    in.k1 = *reinterpret_cast<const uint4*>(a.k + src + 8);
+    in.v0 = *reinterpret_cast<const uint4*>(a.v + src);
+    in.v1 = *reinterpret_cast<const uint4*>(a.v + src + 8);
+    return in;
+}
+
 template <int G>
-__device__ __forceinline__ void append_half_page(const AppendArgs& a, int64_t row, int h, uint8_t* pb,
+__device__ __forceinline__ void append_half_page(const AppendArgs& a, const HalfPageIn& in, uint8_t* pb,
                                                  int pos0, int p1, uint8_t* ring)
 {
     static_assert(G == 32 || G == 64 || G == 128, "group of 32, 64 or 128 channels");
@@ -254,13 +272,8 @@ __device__ __forceinline__ void append_half_page(const AppendArgs& a, int64_t ro
     __shared__ uint8_t vt[8][64];                // [b][token-pair byte j][t]
     const Geo& g = a.g;
     const int lane = threadIdx.x, t = lane >> 3, b = lane & 7;
-    const int64_t src = ((row + t) * g.Hkv + h) * g.d + 16 * b;
-    const uint4 kq0 = *reinterpret_cast<const uint4*>(a.k + src);
-    const uint4 kq1 = *reinterpret_cast<const uint4*>(a.k + src + 8);
-    const uint4 vq0 = *reinterpret_cast<const uint4*>(a.v + src);
-    const uint4 vq1 = *reinterpret_cast<const uint4*>(a.v + src + 8);
-    const uint32_t kw[8] = {kq0.x, kq0.y, kq0.z, kq0.w, kq1.x, kq1.y, kq1.z, kq1.w};
-    const uint32_t vw[8] = {vq0.x, vq0.y, vq0.z, vq0.w, vq1.x, vq1.y, vq1.z, vq1.w};
+    const uint32_t kw[8] = {in.k0.x, in.k0.y, in.k0.z, in.k0.w, in.k1.x, in.k1.y, in.k1.z, in.k1.w};
+    const uint32_t vw[8] = {in.v0.x, in.v0.y, in.v0.z, in.v0.w, in.v1.x, in.v1.y, in.v1.z, in.v1.w};
     float kx[16], vx[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -410,16 +423,40 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
                                    ((int64_t)slot * g.Hkv + h) * g.rb
                              : nullptr;
 
-    for (int hp = p0 / kHalf + blockIdx.x; hp <= (p1 - 1) / kHalf; hp += gridDim.x) {
-        int t_lo = max(hp * kHalf, p0), t_hi = min(hp * kHalf + kHalf, p1);
-        int page = clampi(bt[hp / 2], 0, g.num_pages - 1);
-        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)page * g.Hkv + h) * g.pb;
-        uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hp & 1) * g.d;
-        const int q0 = vpos(2 * lane), q1 = vpos(2 * lane + 1);
-        if (t_hi - t_lo == kHalf) {
-            append_half_page<G>(a, (int64_t)row0 + (t_lo - p0), h, pb, t_lo, p1, ring);
-            continue;
+    // whole half pages [f0, f1), strided over blockIdx.x; the next one's
+    // loads (and block-table entry) are in flight while this one is quantized
+    const int f0 = (p0 + kHalf - 1) / kHalf, f1 = p1 / kHalf;
+    int hp = f0 + (int)blockIdx.x;
+    HalfPageIn cur{}, nxt{};
+    int page = 0, page_n = 0;
+    if (hp < f1) {
+        cur = load_half_page(a, (int64_t)row0 + (hp * kHalf - p0), h);
+        page = bt[hp / 2];
+    }
+    while (hp < f1) {
+        const int hn = hp + (int)gridDim.x;
+        if (hn < f1) {
+            nxt = load_half_page(a, (int64_t)row0 + (hn * kHalf - p0), h);
+            page_n = bt[hn / 2];
         }
+        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages +
+                      ((int64_t)clampi(page, 0, g.num_pages - 1) * g.Hkv + h) * g.pb;
+        append_half_page<G>(a, cur, pb, hp * kHalf, p1, ring);
+        cur = nxt;
+        page = page_n;
+        hp = hn;
+    }
+    // the partial half pages: an unaligned start (wave 0) and end (the last wave)
+    const int head = (p0 % kHalf) ? p0 / kHalf : -1;
+    const int tail = (p1 % kHalf && p1 / kHalf != head) ? p1 / kHalf : -1;
+    for (int k = 0; k < 2; ++k) {
+        const int hpp = k == 0 ? (blockIdx.x == 0 ? head : -1) : (blockIdx.x == gridDim.x - 1 ? tail : -1);
+        if (hpp < 0) continue;
+        const int t_lo = max(hpp * kHalf, p0), t_hi = min(hpp * kHalf + kHalf, p1);
+        const int pg = clampi(bt[hpp / 2], 0, g.num_pages - 1);
+        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages + ((int64_t)pg * g.Hkv + h) * g.pb;
+        uint32_t* vw = reinterpret_cast<uint32_t*>(pb + g.off_vc) + (hpp & 1) * g.d;
+        const int q0 = vpos(2 * lane), q1 = vpos(2 * lane + 1);
         uint32_t kkr[kHalf], vvr[kHalf];
         uint32_t w0 = vw[q0], w1 = vw[q1];
 #pragma unroll
