@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prefill attention over the first 32 histories of the workload "
                          "as prompts (the command the prefill profiles run)")
+    ap.add_argument("--populate-only", action="store_true",
+                    help="time only the bulk populate of the first 32 histories of the workload (the "
+                         "command the append profiles run)")
     ap.add_argument("--no-sub", action="store_true",
                     help="skip the sub-records (G = 128 rotated, Qwen3-4B shape, long context) and "
                          "the read ceilings")
@@ -89,6 +92,8 @@ def parse():
                     help="bench line printed by the profiled run (live event timings)")
     ap.add_argument("--summary-kernel", default="decode_kv4_mfma_kernel",
                     help="kernel-name substring whose counters are summarised")
+    ap.add_argument("--summary-last", type=int, default=0,
+                    help="summarise only the last N dispatches of that kernel (0 = all)")
     return ap.parse_args()
 
 
@@ -206,8 +211,15 @@ def summarize_trace(args):
         k = k if len(k) <= 44 else k[:41] + "..."
         lines.append(f"{k:44s} {len(v):6d} {a.mean():10.2f} {np.median(a):10.2f} {a.min():10.2f} "
                      f"{a.max():10.2f} {100 * a.sum() * 1e3 / total:8.2f}")
-    if args.summary_bench and "prefill" in json.loads(open(args.summary_bench).read().strip().splitlines()[-1]) \
-            and "decode_attn_us" not in json.loads(open(args.summary_bench).read().strip().splitlines()[-1]):
+    bench_line = json.loads(open(args.summary_bench).read().strip().splitlines()[-1]) if args.summary_bench else {}
+    if "populate" in bench_line and "decode_attn_us" not in bench_line:
+        p = bench_line["populate"]
+        lines += ["", "live HIP-event timing of the same run (mean over the timed calls):",
+                  f"  kv4_append (append_kv4_kernel): {p['us']} us for {p['tokens']} tokens in "
+                  f"{p['sequences']} histories: {p['gbs']} GB/s of algorithmic bytes "
+                  f"= {p['frac_hbm_peak']} of the HBM peak",
+                  "kernel counts include the untimed call"]
+    elif args.summary_bench and "prefill" in bench_line and "decode_attn_us" not in bench_line:
         p = json.loads(open(args.summary_bench).read().strip().splitlines()[-1])["prefill"]
         lines += ["", "live HIP-event timing of the same run (mean over the timed calls):",
                   f"  kv4_prefill_attn (prefill_attn_kernel): {p['us']} us for {p['tokens']} tokens in "
@@ -250,13 +262,17 @@ def summarize_counters(args):
     vals = {}
     kernel = args.summary_kernel
     for d in args.summarize_counters:
-        for r in _csv_rows(d, "counter_collection.csv"):
-            if kernel not in r["Kernel_Name"]:
+        rows = [r for r in _csv_rows(d, "counter_collection.csv") if kernel in r["Kernel_Name"]]
+        keep = sorted({int(r["Dispatch_Id"]) for r in rows})
+        last = getattr(args, "summary_last", 0)
+        keep = set(keep[-last:] if last > 0 else keep)
+        for r in rows:
+            if int(r["Dispatch_Id"]) not in keep:
                 continue
-            key = (r["Counter_Name"], int(r["Dispatch_Id"]))
+            key = (r["Counter_Name"], d, int(r["Dispatch_Id"]))
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
     per = {}
-    for (name, _), v in vals.items():
+    for (name, _, _), v in vals.items():
         per.setdefault(name, []).append(v)
     mean = {k: float(np.mean(v)) for k, v in per.items()}
     launches = {k: len(v) for k, v in per.items()}
@@ -581,6 +597,8 @@ def main():
         return run_full36(args, torch, kv4, H, W)
     if args.prefill_only:
         return run_prefill_only(args, torch, kv4, H, W)
+    if args.populate_only:
+        return run_populate_only(args, torch, kv4, H, W)
     cfg = W.CONFIGS[args.config]
     if args.group:
         cfg = W.scaled(cfg, group=args.group)
@@ -644,27 +662,11 @@ def main():
         pk = H.to_dev_bf16(np.concatenate([k for k, _ in first], 0), str(dev))
         pv = H.to_dev_bf16(np.concatenate([v for _, v in first], 0), str(dev))
         cu = torch.from_numpy(pcu).to(dev)
-        ctx0 = torch.zeros(len(first), dtype=torch.int32, device=dev)
         slots = torch.from_numpy(c.slots_host[:len(first)].copy()).to(dev)
         T = int(hist.sum())
-
-        def bulk():
-            kv4.kv4_append(c.cache.handle, 0, pk, pv, cu, ctx0, slots, c.block_tables, len(first), T, stream)
-
-        bulk()
-        torch.cuda.synchronize()
-        pe = []
-        for _ in range(args.populate_reps):
-            e0 = tm.ev(); bulk(); e1 = tm.ev()
-            pe.append((e0, e1))
-        torch.cuda.synchronize()
-        pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
-        pbytes = populate_bytes_kv4(hist, cfg)
-        populate = {"sequences": len(hist), "tokens": T, "us": round(pms * 1e3, 2),
-                    "alg_bytes": pbytes, "gbs": round(pbytes / (pms * 1e-3) / 1e9, 2),
-                    "frac_hbm_peak": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "tokens_per_s": round(T / (pms * 1e-3), 1)}
-        log(f"populate: {T} tokens in {pms * 1e3:.1f} us ({populate['gbs']} GB/s)")
+        populate = time_populate(c.cache.handle, slots, c.block_tables, hist, pk, pv, cu, cfg, kv4, torch,
+                                 tm, args.populate_reps, stream)
+        log(f"populate: {T} tokens in {populate['us']} us ({populate['gbs']} GB/s)")
         if args.prefill_reps > 0:
             # the same histories as prompts: causal BF16 attention (synthetic queries)
             prefill = time_prefill(c, hist, pk, pv, cu, cfg, kv4, torch, tm, args.prefill_reps)
@@ -858,6 +860,58 @@ def time_prefill(c, hist, pk, pv, cu, cfg, kv4, torch, tm, reps):
             "tokens_per_s": round(T / (fms * 1e-3), 1)}
 
 
+def time_populate(handle, slots, block_tables, hist, pk, pv, cu, cfg, kv4, torch, tm, reps, stream):
+    """kv4_append of the histories `hist` (packed in pk, pv; offsets cu) into
+    the slots `slots` from position 0: the mean of `reps` event-timed calls
+    after one untimed."""
+    dev = pk.device
+    B = len(hist)
+    T = int(hist.sum())
+    ctx0 = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    def bulk():
+        kv4.kv4_append(handle, 0, pk, pv, cu, ctx0, slots, block_tables, B, T, stream)
+
+    bulk()
+    torch.cuda.synchronize()
+    pe = []
+    for _ in range(max(1, reps)):
+        e0 = tm.ev(); bulk(); e1 = tm.ev()
+        pe.append((e0, e1))
+    torch.cuda.synchronize()
+    pms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in pe]))
+    pbytes = populate_bytes_kv4(hist, cfg)
+    return {"sequences": B, "tokens": T, "us": round(pms * 1e3, 2),
+            "alg_bytes": pbytes, "gbs": round(pbytes / (pms * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(T / (pms * 1e-3), 1)}
+
+
+def run_populate_only(args, torch, kv4, H, W):
+    """The bulk populate timing alone: the first 32 histories of the workload
+    appended whole into a KV4 cache of the workload's shape (the same inputs
+    as the default line's populate record)."""
+    cfg = W.CONFIGS[args.config]
+    ctx = W.contexts(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    tm = Timer(torch, stream)
+    seqs = list(range(min(32, cfg.batch)))
+    ks, vs = W.all_kv_sources(cfg, 0, ctx + 1, seqs=seqs, threads=16)
+    hist = np.array([int(ctx[s]) for s in seqs])
+    pk = H.to_dev_bf16(np.concatenate([ks[i][:hist[i]] for i in range(len(seqs))], 0), str(dev))
+    pv = H.to_dev_bf16(np.concatenate([vs[i][:hist[i]] for i in range(len(seqs))], 0), str(dev))
+    pcu = np.zeros(len(seqs) + 1, np.int32)
+    pcu[1:] = np.cumsum(hist)
+    cu = torch.from_numpy(pcu).to(dev)
+    c = H.make_cache(cfg.q_heads, cfg.kv_heads, cfg.group, cfg.sink, cfg.recent, list(hist), device=str(dev))
+    rec = time_populate(c.cache.handle, c.slots, c.block_tables, hist, pk, pv, cu, cfg, kv4, torch, tm,
+                        args.populate_reps, stream)
+    log(f"populate: {rec['tokens']} tokens in {rec['us']} us ({rec['gbs']} GB/s)")
+    print(json.dumps({"populate": rec}), flush=True)
+
+
 def run_prefill_only(args, torch, kv4, H, W):
     """The prefill timing alone: the first 32 histories of the workload as
     prompts (the same inputs as the default line's prefill record)."""
@@ -1013,6 +1067,7 @@ def _kernel_hash(kernel=DOMINANT):
     csrc = os.path.join(ROOT, "int8_mixed_precision_amd", "csrc")
     parts = (["kv4_common.hpp", "kv4_decode.hpp", "kv4_decode_mfma.hpp"] if "decode" in kernel else
              ["kv4_common.hpp", "kv4_decode_mfma.hpp", "kv4_prefill.hpp"] if "prefill" in kernel else
+             ["kv4_common.hpp", "kv4_append.hpp"] if "append" in kernel else
              [os.path.basename(f) for f in hb.sources() if f.startswith(csrc)])
     h = hashlib.sha256()
     for f in parts:

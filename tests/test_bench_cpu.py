@@ -114,3 +114,18 @@ def test_counter_summary_bytes_from_request_sizes(tmp_path):
     assert abs(res["l2_hit_rate"] - 0.25) < 1e-12
     assert res["launches"]["TCC_EA0_RDREQ_128B"] == 2
     assert res["kernel_source_hash"] == bench._kernel_hash()
+
+
+def test_counter_summary_last_dispatches(tmp_path):
+    """--summary-last N keeps only the kernel's last N dispatches of each pass
+    (the timed calls after the cache build's own launches of the kernel)."""
+    k = "void kv4::append_kv4_kernel<32>(kv4::AppendArgs)"
+    d = _counter_dir(tmp_path, "a", [(1, k, "SQ_INSTS_VALU", 1e9), (7, k, "SQ_INSTS_VALU", 10.0),
+                                     (9, k, "SQ_INSTS_VALU", 30.0)])
+    out = tmp_path / "a.json"
+    args = argparse.Namespace(summarize_counters=[d], summary_cmd="cmd", summary_out=str(out),
+                              summary_kernel="append_kv4_kernel", summary_last=2)
+    bench.summarize_counters(args)
+    res = json.load(open(out))
+    assert res["counters_per_launch"]["SQ_INSTS_VALU"] == 20.0 and res["launches"]["SQ_INSTS_VALU"] == 2
+    assert res["kernel_source_hash"] == bench._kernel_hash("append_kv4_kernel")
