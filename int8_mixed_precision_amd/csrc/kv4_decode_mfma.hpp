@@ -481,35 +481,49 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
             }
         }
 
-        // ---- per half of the q heads (one half below ratio 8): QK, softmax, PV
+        // ---- QK, block by block: D_hh[r] = q_{kb,r} . c over block r, token
+        // n16 of page hh; each block's widened K codes serve every half of the
+        // q heads (one half below ratio 8)
+        f32x4_t D0[NH], D1[NH];
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) {
-            // ---- QK: D_hh[r] = q_{kb,r} . c over block r, token n16 of page hh
-            f32x4_t D0 = {0.f, 0.f, 0.f, 0.f}, D1 = D0;
+            D0[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            D1[hf] = D0[hf];
+        }
+        {
             const uint32_t k0w[4] = {kc0.x, kc0.y, kc0.z, kc0.w};
             const uint32_t k1w[4] = {kc1.x, kc1.y, kc1.z, kc1.w};
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 // block-diagonal A: only rows of block bb (lanes with lane % 4 == bb) carry q
                 const uint64_t rows = 0x1111111111111111ull << bb;
-                const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
-                                   keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
                 const u32x4_t B0 = widen_k16(k0w[bb]), B1 = widen_k16(k1w[bb]);
-                D0 = mfma_f16(A, B0, D0);
-                D1 = mfma_f16(A, B1, D1);
-                if constexpr (ROT) {
-                    const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
-                                        keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
-                    D0 = mfma_f16(Al, B0, D0);
-                    D1 = mfma_f16(Al, B1, D1);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
+                                       keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
+                    D0[hf] = mfma_f16(A, B0, D0[hf]);
+                    D1[hf] = mfma_f16(A, B1, D1[hf]);
+                    if constexpr (ROT) {
+                        const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
+                                            keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
+                        D0[hf] = mfma_f16(Al, B0, D0[hf]);
+                        D1[hf] = mfma_f16(Al, B1, D1[hf]);
+                    }
                 }
             }
+        }
+
+        // ---- per half: scores, softmax and the PV operand
+        u32x4_t ahi[NH], alo[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
             float x0 = 0.f, x1 = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int gg = (32 * r) / G;
-                x0 = fmaf(h2f(kdm[0][gg], 0), D0[r], x0);
-                x1 = fmaf(h2f(kdm[1][gg], 0), D1[r], x1);
+                x0 = fmaf(h2f(kdm[0][gg], 0), D0[hf][r], x0);
+                x1 = fmaf(h2f(kdm[1][gg], 0), D1[hf][r], x1);
             }
 #pragma unroll
             for (int gg = 0; gg < NG; ++gg) {
@@ -597,25 +611,29 @@ __device__ __forceinline__ void mfma_item_kv4(const DecodeArgs& a, int b, int h,
                     wv[e] = (tok >= t_lo && tok < t_hi) ? wv[e] : 0.0f;
                 }
             }
-            u32x4_t ahi, alo;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t hw, lw;
                 split_bf16(wv[i], wv[i + 4], hw, lw);
-                ahi[i] = hw;
-                alo[i] = lw;
+                ahi[hf][i] = hw;
+                alo[hf][i] = lw;
             }
-            const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
-            const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
+        }
+
+        // ---- PV, block by block; each block's widened V codes serve every half
+        const uint4 vc0 = stage[2][lane], vc1 = stage[3][lane];
+        const uint32_t vcw[8] = {vc0.x, vc0.y, vc0.z, vc0.w, vc1.x, vc1.y, vc1.z, vc1.w};
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                // rows of block blk only: each accumulator row gathers its own block
-                const uint64_t rows = 0x1111111111111111ull << blk;
-                const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                    keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-                const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                    keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
-                const u32x4_t b0 = widen_v(vcw[2 * blk]), b1 = widen_v(vcw[2 * blk + 1]);
+        for (int blk = 0; blk < 4; ++blk) {
+            // rows of block blk only: each accumulator row gathers its own block
+            const uint64_t rows = 0x1111111111111111ull << blk;
+            const u32x4_t b0 = widen_v(vcw[2 * blk]), b1 = widen_v(vcw[2 * blk + 1]);
+#pragma unroll
+            for (int hf = 0; hf < NH; ++hf) {
+                const u32x4_t bh = {keep_lanes(ahi[hf][0], rows), keep_lanes(ahi[hf][1], rows),
+                                    keep_lanes(ahi[hf][2], rows), keep_lanes(ahi[hf][3], rows)};
+                const u32x4_t bl = {keep_lanes(alo[hf][0], rows), keep_lanes(alo[hf][1], rows),
+                                    keep_lanes(alo[hf][2], rows), keep_lanes(alo[hf][3], rows)};
                 E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
                 E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
                 E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
@@ -814,31 +832,43 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
         const float sk1 = half_bits_to_float(ksc[e0 + 16 + n16]);
         const uint4 svp = *reinterpret_cast<const uint4*>(vsc + e0 + 8 * kb);
 
+        // ---- QK, block by block; each block's widened codes serve every half
+        f32x4_t D0[NH], D1[NH];
 #pragma unroll
         for (int hf = 0; hf < NH; ++hf) {
-            // ---- QK
-            f32x4_t D0 = dinit[hf], D1 = dinit[hf];
+            D0[hf] = dinit[hf];
+            D1[hf] = dinit[hf];
+        }
+        {
             const uint32_t kw0[8] = {k00.x, k00.y, k00.z, k00.w, k01.x, k01.y, k01.z, k01.w};
             const uint32_t kw1[8] = {k10.x, k10.y, k10.z, k10.w, k11.x, k11.y, k11.z, k11.w};
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const uint64_t rows = 0x1111111111111111ull << bb;
-                const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
-                                   keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
                 const u32x4_t B0 = widen_i8(kw0[2 * bb], kw0[2 * bb + 1]);
                 const u32x4_t B1 = widen_i8(kw1[2 * bb], kw1[2 * bb + 1]);
-                D0 = mfma_f16(A, B0, D0);
-                D1 = mfma_f16(A, B1, D1);
-                if constexpr (ROT) {
-                    const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
-                                        keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
-                    D0 = mfma_f16(Al, B0, D0);
-                    D1 = mfma_f16(Al, B1, D1);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
+                                       keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
+                    D0[hf] = mfma_f16(A, B0, D0[hf]);
+                    D1[hf] = mfma_f16(A, B1, D1[hf]);
+                    if constexpr (ROT) {
+                        const u32x4_t Al = {keep_lanes(aql[hf][0], rows), keep_lanes(aql[hf][1], rows),
+                                            keep_lanes(aql[hf][2], rows), keep_lanes(aql[hf][3], rows)};
+                        D0[hf] = mfma_f16(Al, B0, D0[hf]);
+                        D1[hf] = mfma_f16(Al, B1, D1[hf]);
+                    }
                 }
             }
+        }
+        // ---- per half: scores, softmax and the PV operand
+        u32x4_t ahi[NH], alo[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
             const bool ok0 = e0 + n16 < n8, ok1 = e0 + 16 + n16 < n8;
-            float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2[hf];
-            float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2[hf];
+            float s0 = ((D0[hf][0] + D0[hf][1]) + (D0[hf][2] + D0[hf][3])) * sk0 * c2[hf];
+            float s1 = ((D1[hf][0] + D1[hf][1]) + (D1[hf][2] + D1[hf][3])) * sk1 * c2[hf];
             s0 = ok0 ? s0 : -INFINITY;
             s1 = ok1 ? s1 : -INFINITY;
             const float mx = row16_max(fmaxf(s0, s1));
@@ -873,33 +903,38 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
                 const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
                 wv[e] = e0 + 8 * kb + e < n8 ? w : 0.0f;
             }
-            u32x4_t ahi, alo;
             constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t hw, lw;
                 split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
-                ahi[i] = hw;
-                alo[i] = lw;
+                ahi[hf][i] = hw;
+                alo[hf][i] = lw;
             }
+            W[hf] = mfma_bf16(ahi[hf], ones, W[hf]);
+            W[hf] = mfma_bf16(alo[hf], ones, W[hf]);
+        }
+        // ---- PV, block by block; each block's widened codes serve every half
+        {
             const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
                                      v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
                 const uint64_t rows = 0x1111111111111111ull << blk;
-                const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                    keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-                const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                    keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
                 const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
                 const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
-                E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
-                E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
-                E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
-                E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    const u32x4_t bh = {keep_lanes(ahi[hf][0], rows), keep_lanes(ahi[hf][1], rows),
+                                        keep_lanes(ahi[hf][2], rows), keep_lanes(ahi[hf][3], rows)};
+                    const u32x4_t bl = {keep_lanes(alo[hf][0], rows), keep_lanes(alo[hf][1], rows),
+                                        keep_lanes(alo[hf][2], rows), keep_lanes(alo[hf][3], rows)};
+                    E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
+                    E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
+                    E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
+                    E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+                }
             }
-            W[hf] = mfma_bf16(ahi, ones, W[hf]);
-            W[hf] = mfma_bf16(alo, ones, W[hf]);
         }
         __builtin_amdgcn_wave_barrier();
     }
