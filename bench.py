@@ -455,7 +455,7 @@ def ratio8_record(c, cfg, n, knew, vnew, H, W, kv4, torch, tm, args, dev):
     sp = _SharedPools(c, c8.q_heads, kv4, torch)
     try:
         r = time_step(SimpleNamespace(cache=sp, slots=c.slots, block_tables=c.block_tables), c8, n, knew,
-                      vnew, q8, kv4, torch, tm, args.steps, args.warmup)
+                      vnew, q8, kv4, torch, tm, args.steps, args.warmup, clock_warm_s=0.3)
     finally:
         sp.close()
     p8, d8 = partial_bytes_kv4(n, c8), decode_bytes_kv4(n, c8)
@@ -464,6 +464,7 @@ def ratio8_record(c, cfg, n, knew, vnew, H, W, kv4, torch, tm, args, dev):
             "kernel": "decode_kv4_mfma8_kernel", "waves": r["waves"],
             "decode_attn_us": round(r["decode_ms"] * 1e3, 2),
             "decode_partials_us": round(r["partials_ms"] * 1e3, 2),
+            "decode_merge_us": round(r["merge_ms"] * 1e3, 2),
             "partials_alg_bytes": p8,
             "partials_frac_hbm_peak": round(p8 / (r["partials_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "decode_attn_frac_hbm_peak": round(d8 / (r["decode_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
