@@ -238,13 +238,6 @@ __device__ __forceinline__ void int4_codes16(const float (&x)[16], uint16_t db, 
     }
 }
 
-// A whole half page of new tokens (8 positions pos0 .. pos0 + 7, pos0 a
-// multiple of 8) for one kv head, one wave: lane 8 t + b holds channels
-// 16 b .. 16 b + 15 of token t, so a group's range, Delta and m are formed
-// from 16 values per lane (G / 16 lanes per group) and a token's K code row
-// is written as whole words.  The V code words, one per channel over the 8
-// tokens, take a byte transpose through LDS.  Positions protected at the new
-// length also get their INT8 side entries.
 // The bf16 K and V of a whole half page in the layout of append_half_page:
 // lane 8t + b holds channels 16 b .. 16 b + 15 of token t (row `row` + t).
 struct HalfPageIn {
@@ -263,6 +256,13 @@ __device__ __forceinline__ HalfPageIn load_half_page(const AppendArgs& a, int64_
     return in;
 }
 
+// A whole half page of new tokens (8 positions pos0 .. pos0 + 7, pos0 a
+// multiple of 8) for one kv head, one wave: lane 8 t + b holds channels
+// 16 b .. 16 b + 15 of token t, so a group's range, Delta and m are formed
+// from 16 values per lane (G / 16 lanes per group) and a token's K code row
+// is written as whole words.  The V code words, one per channel over the 8
+// tokens, take a byte transpose through LDS.  Positions protected at the new
+// length also get their INT8 side entries.
 template <int G>
 __device__ __forceinline__ void append_half_page(const AppendArgs& a, const HalfPageIn& in, uint8_t* pb,
                                                  int pos0, int p1, uint8_t* ring)
@@ -400,9 +400,12 @@ __device__ __forceinline__ void append_half_page(const AppendArgs& a, const Half
     }
 }
 
-// One wave per (sequence, kv head, 8-token half page) of new tokens; the wave
-// owns the half page's V code words, so read-modify-write of nibbles is
-// race-free.  Grid: (x, Hkv, batch); half pages are strided over x.
+// Grid (x, Hkv, batch): the whole half pages of a sequence's new tokens are
+// strided over x (append_half_page); an unaligned first half page goes to
+// wave x = 0 and an unaligned last one to the last wave, which quantize its
+// tokens one at a time with lane l holding channels 2l, 2l + 1.  Each half
+// page belongs to one wave, which owns its V code words, so the
+// read-modify-write of a partial half page's nibbles is race-free.
 template <int G>
 __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
 {
