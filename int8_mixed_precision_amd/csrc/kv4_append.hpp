@@ -418,7 +418,11 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
     int p1 = min(p0 + (row1 - row0), cap);
     if (p1 <= p0) return;
     int slot = clampi(a.slot_ids[b], 0, g.max_slots - 1);
-    const int32_t* bt = a.block_tables + (int64_t)slot * g.max_pages;
+    // page ids through the scalar cache (the block table is read-only during
+    // the kernel), so that waiting for one never waits for the vector loads
+    // issued after it
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    const const_i32 bt = (const_i32)(a.block_tables + (int64_t)slot * g.max_pages);
     constexpr int LPG = G / 2;                 // lanes per group
     const int grp = (2 * lane) / G;
 
@@ -427,27 +431,29 @@ __global__ __launch_bounds__(64) void append_kv4_kernel(AppendArgs a)
                              : nullptr;
 
     // whole half pages [f0, f1), strided over blockIdx.x; the next one's
-    // loads (and block-table entry) are in flight while this one is quantized
+    // loads (and block-table entry) are in flight while this one is
+    // quantized.  The loads are unconditional (past the last half page the
+    // current one is read again, from the cache), so the wait for this half
+    // page's data never waits for the next one's.
     const int f0 = (p0 + kHalf - 1) / kHalf, f1 = p1 / kHalf;
     int hp = f0 + (int)blockIdx.x;
-    HalfPageIn cur{}, nxt{};
-    int page = 0, page_n = 0;
     if (hp < f1) {
-        cur = load_half_page(a, (int64_t)row0 + (hp * kHalf - p0), h);
-        page = bt[hp / 2];
-    }
-    while (hp < f1) {
-        const int hn = hp + (int)gridDim.x;
-        if (hn < f1) {
-            nxt = load_half_page(a, (int64_t)row0 + (hn * kHalf - p0), h);
-            page_n = bt[hn / 2];
+        HalfPageIn cur = load_half_page(a, (int64_t)row0 + (hp * kHalf - p0), h);
+        int page = bt[hp / 2];
+        for (;;) {
+            const int hn = hp + (int)gridDim.x;
+            const bool more = hn < f1;
+            const int hl = more ? hn : hp;
+            const HalfPageIn nxt = load_half_page(a, (int64_t)row0 + (hl * kHalf - p0), h);
+            const int page_n = bt[hl / 2];
+            uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages +
+                          ((int64_t)clampi(page, 0, g.num_pages - 1) * g.Hkv + h) * g.pb;
+            append_half_page<G>(a, cur, pb, hp * kHalf, p1, ring);
+            if (!more) break;
+            cur = nxt;
+            page = page_n;
+            hp = hn;
         }
-        uint8_t* pb = a.pages + (int64_t)a.layer * g.layer_pages +
-                      ((int64_t)clampi(page, 0, g.num_pages - 1) * g.Hkv + h) * g.pb;
-        append_half_page<G>(a, cur, pb, hp * kHalf, p1, ring);
-        cur = nxt;
-        page = page_n;
-        hp = hn;
     }
     // the partial half pages: an unaligned start (wave 0) and end (the last wave)
     const int head = (p0 % kHalf) ? p0 / kHalf : -1;
