@@ -285,15 +285,17 @@ __device__ __forceinline__ void append_half_page(const AppendArgs& a, const Half
     if (g.rot) {
         // channel bits 0-3 in the lane, bits 4-6 on lane bits 0-2: the
         // stages in the order of the channel bits, as everywhere else
+        // (the first two lane stages through DPP quad permutes: no LDS round
+        // trip in the chain of 16 dependent stages per value)
         wht_local(kx);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float p = lane_xor<1>(kx[j]);
+            const float p = __int_as_float(row_mov<0xB1>(__float_as_int(kx[j])));   // lane ^ 1
             kx[j] = (b & 1) ? p - kx[j] : kx[j] + p;
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const float p = lane_xor<2>(kx[j]);
+            const float p = __int_as_float(row_mov<0x4E>(__float_as_int(kx[j])));   // lane ^ 2
             kx[j] = (b & 2) ? p - kx[j] : kx[j] + p;
         }
 #pragma unroll
