@@ -573,7 +573,18 @@ int kv4_append(kv4_cache* cache, int layer, const void* k_bf16, const void* v_bf
     // parallelism along each sequence sized by the mean number of new tokens
     int64_t mean_new = ((int64_t)total_new + batch - 1) / batch;
     if (g.kind == KV4_KIND_MIXED) {
-        int gx = (int)std::min<int64_t>((mean_new + kv4::kHalf - 1) / kv4::kHalf + 1, 256);
+        // waves per (sequence, kv head): one per four half pages of the mean
+        // sequence, so that a wave quantizes several half pages with the next
+        // one's loads in flight, at most 128, but enough for about 6,144
+        // waves in all when the batch has few (sequence, kv head) pairs.
+        // Measured against one wave per half page up to 256: 190 against
+        // 197 us for the populate of 32 histories (145,101 tokens), 322
+        // against 408 us for 256 sequences of 1,024 tokens, and 46 against
+        // 52 us for one sequence of 32,768.
+        const int64_t pairs = (int64_t)batch * g.Hkv;
+        const int64_t cap = std::max<int64_t>(128, (6144 + pairs - 1) / pairs);
+        int gx = (int)std::min<int64_t>((mean_new + 4 * kv4::kHalf - 1) / (4 * kv4::kHalf) + 1,
+                                        std::min<int64_t>(cap, 4096));
         if (mean_new <= 1) gx = 1;
         dim3 grid(gx, g.Hkv, batch);
         switch (g.G) {
