@@ -1104,15 +1104,28 @@ __global__ __launch_bounds__(256) void merge_parts_kernel(DecodeArgs a)
             o1 = fmaf(wi, v[i].y, o1);
         }
     } else if (np <= 128) {
-        // log-normalisers of up to 128 parts in two registers, then the outputs
-        // in batches of 16 loads
+        // log-normalisers of up to 128 parts in two registers; the outputs of
+        // the first kFirst parts are loaded right after them (they do not
+        // depend on the weights), so the wait for the log-normalisers leaves
+        // those loads in flight; the rest in batches of 16 loads
+        constexpr int kFirst = 16;
         const float z0 = lane < np ? part_of(lane)[g.d] : -INFINITY;
         const float z1 = 64 + lane < np ? part_of(64 + lane)[g.d] : -INFINITY;
+        float2 v[kFirst];
+#pragma unroll
+        for (int u = 0; u < kFirst; ++u)
+            v[u] = *reinterpret_cast<const float2*>(part_of(min(u, np - 1)) + 2 * lane);
         const float zm = wave_max(fmaxf(z0, z1));
         const float w0 = lane < np ? exp2f(z0 - zm) : 0.f;
         const float w1 = 64 + lane < np ? exp2f(z1 - zm) : 0.f;
         W = wave_sum(w0 + w1);
-        for (int i = 0; i < np; i += kBatch)
+#pragma unroll
+        for (int u = 0; u < kFirst; ++u) {
+            const float wi = u < np ? __shfl(w0, u) : 0.f;
+            o0 = fmaf(wi, v[u].x, o0);
+            o1 = fmaf(wi, v[u].y, o1);
+        }
+        for (int i = kFirst; i < np; i += kBatch)
             gather(i, np, [&](int ii) { return ii < 64 ? __shfl(w0, ii) : __shfl(w1, ii - 64); });
     } else {
         float zmax = -INFINITY;
