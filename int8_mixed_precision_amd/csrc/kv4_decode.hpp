@@ -875,7 +875,7 @@ __device__ __forceinline__ void int_item_kv4(const DecodeArgs& a, int b, int h, 
                     off += ok[ee] ? p * Mv[ee] : 0.f;
                 }
                 int u[kHalf];
-                const float r = wmax > kTinyW ? __fdiv_rn(255.0f, wmax) : 0.f;
+                const float r = wmax > kTinyW ? 255.0f * __builtin_amdgcn_rcpf(wmax) : 0.f;
 #pragma unroll
                 for (int ee = 0; ee < kHalf; ++ee) u[ee] = (int)fminf(rintf(w[ee] * r), 255.0f);
                 const uint32_t ue = pack_i8x4(u[0], u[2], u[4], u[6]);

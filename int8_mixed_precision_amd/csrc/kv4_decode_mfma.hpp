@@ -1648,7 +1648,7 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
                     w[e] = (full || (tok >= t_lo && tok < t_hi)) ? x : 0.f;
                     wmax = fmaxf(wmax, w[e]);
                 }
-                const float rr = wmax > kTinyW ? __fdiv_rn(255.0f, wmax) : 0.f;
+                const float rr = wmax > kTinyW ? 255.0f * __builtin_amdgcn_rcpf(wmax) : 0.f;
                 int uc[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) uc[e] = (int)fminf(rintf(w[e] * rr), 255.0f);
