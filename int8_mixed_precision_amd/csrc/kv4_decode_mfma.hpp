@@ -1646,7 +1646,7 @@ __device__ __forceinline__ void mfma_item_int(const DecodeArgs& a, int b, int h,
                     const float x = pr[e] * h2f(vdw[e >> 1], e & 1);
                     const int tok = 32 * tl + 8 * gq + e;
                     w[e] = (full || (tok >= t_lo && tok < t_hi)) ? x : 0.f;
-                    wmax = fmaxf(wmax, w[e]);
+                    wmax = __builtin_elementwise_maximum(wmax, w[e]);   // no NaN: no canonicalising
                 }
                 const float rr = wmax > kTinyW ? 255.0f * __builtin_amdgcn_rcpf(wmax) : 0.f;
                 int uc[8];
