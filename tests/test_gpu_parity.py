@@ -302,6 +302,42 @@ def test_bulk_equals_token_by_token():
             assert np.array_equal(ga[k], gb[k]), (i, k)
 
 
+@pytest.mark.parametrize("G,rotate", [(32, False), (128, True)])
+def test_bulk_append_long_history_in_two_unaligned_parts(G, rotate):
+    """Bulk appends at the extremes of the launch's shape, bytes bit-exact
+    against the oracle (KV4-RL eq. 3.3; Appendix A.3 "Encoding and
+    allocation"): one 20,003-token history appended in two calls, the second
+    starting at position 4,003 (each call then has a partial first or last
+    half page beside hundreds of waves of whole ones, and the second rewrites
+    the whole side ring), and 64 short histories of 1 to 299 tokens in one
+    call (few whole half pages per sequence)."""
+    Hq, Hkv, S, R = 8, 2, 4, 128
+    flags = kv4.KV4_FLAG_ROTATE_K if rotate else 0
+    n = np.array([20003])
+    H.log(f"case bulk long history G={G} rotate={rotate}")
+    cfg = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R, seed=77,
+                   batch=1, ctx_kind="fixed", ctx_fixed=(int(n[0]),))
+    ks, vs = W.all_kv_sources(cfg, 0, n)
+    built = H.make_cache(Hq, Hkv, G, S, R, n, flags=flags, seed=77)
+    _fill_garbage(built)
+    cut = 4003
+    H.append_chunks(built, 0, [ks[0][:cut]], [vs[0][:cut]], [0])
+    H.append_chunks(built, 0, [ks[0][cut:]], [vs[0][cut:]], [cut])
+    pages, side = H.pools_host(built)
+    _compare_bytes(built, pages, side, 0, oracle.MixedCache(ks, vs, G, rotate=rotate), S, R)
+
+    n2 = np.random.default_rng(5).integers(1, 300, 64)
+    H.log(f"case bulk 64 short histories G={G} rotate={rotate}")
+    cfg2 = W.scaled(W.CONFIGS["tiny"], q_heads=Hq, kv_heads=Hkv, group=G, sink=S, recent=R, seed=78,
+                    batch=64, ctx_kind="fixed", ctx_fixed=tuple(int(x) for x in n2))
+    ks2, vs2 = W.all_kv_sources(cfg2, 0, n2)
+    b2 = H.make_cache(Hq, Hkv, G, S, R, n2, flags=flags, seed=78)
+    _fill_garbage(b2)
+    H.append_chunks(b2, 0, ks2, vs2, [0] * len(n2))
+    pages2, side2 = H.pools_host(b2)
+    _compare_bytes(b2, pages2, side2, 0, oracle.MixedCache(ks2, vs2, G, rotate=rotate), S, R)
+
+
 def test_decode_steps_cross_demotion_boundary():
     """64 consecutive steps of (append, decode) starting at n = S+R-32, so the
     cache goes from all-INT8 to mixed and positions are demoted every step;
