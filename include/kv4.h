@@ -148,7 +148,7 @@ typedef struct kv4_cache_desc {
     int32_t num_kv_heads;       /* Hkv.  Hq / Hkv: 1 to 8 (the matrix core runs
                                    the q heads of a kv head in halves of four),
                                    or 16 for the mixed kind without
-                                   KV4_FLAG_INT_PATH; KV8 1 to 4.  Others:
+                                   KV4_FLAG_INT_PATH; KV8 1 to 8.  Others:
                                    KV4_ERR_UNSUPPORTED */
     int32_t head_dim;           /* d; the library supports 128 */
     int32_t page_size;          /* tokens per page; the library supports 16 */

@@ -60,7 +60,7 @@ int validate_desc(const kv4_cache_desc* d)
     // q/kv ratios: the matrix-core kernels take 1 .. 8 in halves of four q heads
     // (rows of heads past the ratio carry q = 0), and 16 as four halves on the
     // floating-point path of the mixed kind; the vector-ALU kernels take 1, 2,
-    // 4 and 8; KV8 (below) takes 1 to 4.
+    // 4 and 8; KV8 (below) takes 1 to 8.
     const int gqa = d->num_q_heads / d->num_kv_heads;
     const bool pow2 = gqa == 1 || gqa == 2 || gqa == 4 || gqa == 8;
     if (gqa > 8 && gqa != 16) return KV4_ERR_UNSUPPORTED;
@@ -73,7 +73,7 @@ int validate_desc(const kv4_cache_desc* d)
     if ((d->flags & KV4_FLAG_ROTATE_K) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
     // the integer path reads the INT4 pages and the INT8 ring
     if ((d->flags & KV4_FLAG_INT_PATH) && d->kind != KV4_KIND_MIXED) return KV4_ERR_UNSUPPORTED;
-    if (d->kind == KV4_KIND_KV8 && gqa > 4) return KV4_ERR_UNSUPPORTED;
+    if (d->kind == KV4_KIND_KV8 && gqa > 8) return KV4_ERR_UNSUPPORTED;
     // KV8 pages are decoded on the matrix core only
     if (d->kind == KV4_KIND_KV8 && (d->flags & KV4_FLAG_VALU_DECODE)) return KV4_ERR_UNSUPPORTED;
     if ((int64_t)d->sink + d->recent > kMaxSinkRecent) return KV4_ERR_CAPACITY;
@@ -149,8 +149,9 @@ int mfma8_waves_per_cu(const kv4_cache_desc& d)
 {
     static std::atomic<int> known[3][2];
     static std::atomic<int> known_int[3][2];
-    static std::atomic<int> known_bf16;
+    static std::atomic<int> known_bf16, known_kv8;
     if (d.kind == KV4_KIND_BF16) return resident_waves(kv4::decode_bf16_mfma8_kernel, known_bf16);
+    if (d.kind == KV4_KIND_KV8) return resident_waves(kv4::decode_kv8_mfma8_kernel, known_kv8);
     const bool rot = (d.flags & KV4_FLAG_ROTATE_K) != 0;
     if (d.flags & KV4_FLAG_INT_PATH) {
         switch (d.group_size) {
@@ -197,11 +198,10 @@ int mfma16_waves_per_cu(const kv4_cache_desc& d)
 }
 
 // Whether the decode of a cache runs on a matrix-core kernel of two or more
-// four-head halves (mixed and BF16 kinds, q/kv ratio above 4).
+// four-head halves (q/kv ratio above 4).
 bool uses_halves(const kv4_cache_desc& d)
 {
-    return d.num_q_heads > 4 * d.num_kv_heads && d.kind != KV4_KIND_KV8 &&
-           !(d.flags & KV4_FLAG_VALU_DECODE);
+    return d.num_q_heads > 4 * d.num_kv_heads && !(d.flags & KV4_FLAG_VALU_DECODE);
 }
 
 // Waves of the balanced decode partition: explicit, or 16 per compute unit
@@ -278,7 +278,7 @@ int launch_status()
 // The matrix-core kernels run the q heads of a kv head in halves of four (rows
 // of heads past the ratio carry q = 0 and are not written): one half for
 // ratios up to 4, two for 5 to 8 (decode_kv4_mfma8_kernel,
-// decode_int_mfma8_kernel, decode_bf16_mfma8_kernel), four for 16
+// decode_int_mfma8_kernel, decode_bf16_mfma8_kernel, decode_kv8_mfma8_kernel), four for 16
 // (decode_kv4_mfma16_kernel).
 template <int GQA>
 void launch_decode_valu(const kv4::DecodeArgs& a, hipStream_t s)
@@ -386,6 +386,10 @@ void launch_decode(const kv4::DecodeArgs& a, hipStream_t s)
     }
     if (a.g.gqa <= 8 && !a.g.valu && a.g.kind == KV4_KIND_BF16) {
         hipLaunchKernelGGL(kv4::decode_bf16_mfma8_kernel, dim3((unsigned)a.waves), dim3(64), 0, s, a);
+        return;
+    }
+    if (a.g.gqa <= 8 && a.g.kind == KV4_KIND_KV8) {
+        hipLaunchKernelGGL(kv4::decode_kv8_mfma8_kernel, dim3((unsigned)a.waves), dim3(64), 0, s, a);
         return;
     }
     if (a.g.gqa <= 8 && !a.g.valu && a.g.kind == KV4_KIND_MIXED) {

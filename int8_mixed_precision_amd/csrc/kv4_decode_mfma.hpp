@@ -965,6 +965,7 @@ __device__ __forceinline__ void mfma_prot_kv4(const DecodeArgs& a, int b, int h,
 // registers and move to a per-wave LDS stage at the start of the tile, so the
 // next tile's loads are in flight during the compute.
 // ---------------------------------------------------------------------------
+template <int NH = 1>
 __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h, int t_lo, int t_hi,
                                               float* rec, Pace& pace)
 {
@@ -984,14 +985,19 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
         return hbase + (int64_t)p * page_stride;
     };
 
-    // ---- q of head jq, channels 32 kb + 8 gq + i, scaled by 2^sc into fp16
-    u32x4_t aqv;
-    int sc;
-    {
+    // ---- q of head 4 hf + jq, channels 32 kb + 8 gq + i, scaled by 2^sc into
+    // fp16, per half of the q heads (one half up to ratio 4)
+    u32x4_t aqv[NH];
+    f32x4_t dinit[NH];
+    float c2[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        int sc;
         // rows of heads past the q/kv ratio (GQA 1 and 2 run in the four-head
         // layout) carry q = 0; their results are not written
-        const bool qreal = jq < g.gqa;
-        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jq : 0)) * g.d;
+        const int jh = 4 * hf + jq;
+        const bool qreal = jh < g.gqa;
+        const uint16_t* qrow = a.q + ((int64_t)b * g.Hq + h * g.gqa + (qreal ? jh : 0)) * g.d;
         uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * kb + 8 * gq);
         if (!qreal) u = make_uint4(0u, 0u, 0u, 0u);
         const float q[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -1002,25 +1008,31 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
         amax = fmaxf(amax, dpp<0xB1>(amax));
         amax = rows_max(fmaxf(amax, dpp<0x4E>(amax)));
         sc = 15 - __builtin_amdgcn_frexp_expf(amax);
-        aqv[0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[2], sc));
-        aqv[1] = pack_f16(ldexpf(q[1], sc), ldexpf(q[3], sc));
-        aqv[2] = pack_f16(ldexpf(q[4], sc), ldexpf(q[6], sc));
-        aqv[3] = pack_f16(ldexpf(q[5], sc), ldexpf(q[7], sc));
+        aqv[hf][0] = pack_f16(ldexpf(q[0], sc), ldexpf(q[2], sc));
+        aqv[hf][1] = pack_f16(ldexpf(q[1], sc), ldexpf(q[3], sc));
+        aqv[hf][2] = pack_f16(ldexpf(q[4], sc), ldexpf(q[6], sc));
+        aqv[hf][3] = pack_f16(ldexpf(q[5], sc), ldexpf(q[7], sc));
+        float qpart = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qpart += h2f(aqv[hf][i], 0) + h2f(aqv[hf][i], 1);
+        const float qblk = rows_sum(qpart);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dinit[hf][r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
+        c2[hf] = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
     }
-    float qpart = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qpart += h2f(aqv[i], 0) + h2f(aqv[i], 1);
-    const float qblk = rows_sum(qpart);
-    f32x4_t dinit;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dinit[r] = -0x1p-17f * __shfl(qblk, 4 * kb + r);
-    const float c2 = ldexpf(a.scale2, 24 - __shfl(sc, 4 * kb));
 
-    f32x4_t E[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-    f32x4_t W = {0.f, 0.f, 0.f, 0.f};
-    float m_sh = -INFINITY, l_run = 0.f;
+    f32x4_t E[NH][2], W[NH];
+    float m_sh[NH], l_run[NH];
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+        E[hf][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        E[hf][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        W[hf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_sh[hf] = -INFINITY;
+        l_run[hf] = 0.f;
+    }
     __shared__ uint4 stage8[8][64];
-    __shared__ __attribute__((aligned(16))) float pbuf8[4][32];
+    __shared__ __attribute__((aligned(16))) float pbuf8[NH][4][32];
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0
 
     // landing registers of one tile
@@ -1075,8 +1087,13 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
         T0 = N0;
         T1 = N1;
 
-        // ---- QK
-        f32x4_t D0 = dinit, D1 = dinit;
+        // ---- QK, block by block; each block's widened codes serve every half
+        f32x4_t D0[NH], D1[NH];
+#pragma unroll
+        for (int hf = 0; hf < NH; ++hf) {
+            D0[hf] = dinit[hf];
+            D1[hf] = dinit[hf];
+        }
         {
             const uint4 k00 = stage8[0][lane], k01 = stage8[1][lane];
             const uint4 k10 = stage8[2][lane], k11 = stage8[3][lane];
@@ -1085,95 +1102,115 @@ __device__ __forceinline__ void mfma_item_kv8(const DecodeArgs& a, int b, int h,
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const uint64_t rows = 0x1111111111111111ull << bb;
-                const u32x4_t A = {keep_lanes(aqv[0], rows), keep_lanes(aqv[1], rows),
-                                   keep_lanes(aqv[2], rows), keep_lanes(aqv[3], rows)};
-                D0 = mfma_f16(A, widen_i8(kw0[2 * bb], kw0[2 * bb + 1]), D0);
-                D1 = mfma_f16(A, widen_i8(kw1[2 * bb], kw1[2 * bb + 1]), D1);
+                const u32x4_t B0 = widen_i8(kw0[2 * bb], kw0[2 * bb + 1]);
+                const u32x4_t B1 = widen_i8(kw1[2 * bb], kw1[2 * bb + 1]);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    const u32x4_t A = {keep_lanes(aqv[hf][0], rows), keep_lanes(aqv[hf][1], rows),
+                                       keep_lanes(aqv[hf][2], rows), keep_lanes(aqv[hf][3], rows)};
+                    D0[hf] = mfma_f16(A, B0, D0[hf]);
+                    D1[hf] = mfma_f16(A, B1, D1[hf]);
+                }
             }
         }
         const int tok0 = 32 * tl + n16;
         const bool ok0 = tok0 >= t_lo && tok0 < t_hi;
         const bool ok1 = tok0 + 16 >= t_lo && tok0 + 16 < t_hi;
-        float s0 = ((D0[0] + D0[1]) + (D0[2] + D0[3])) * sk0 * c2;
-        float s1 = ((D1[0] + D1[1]) + (D1[2] + D1[3])) * sk1 * c2;
-        s0 = ok0 ? s0 : -INFINITY;
-        s1 = ok1 ? s1 : -INFINITY;
-        const float mx = row16_max(fmaxf(s0, s1));
-        {
-            const bool grow = mx > m_sh + (kPScale + kSlack);
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float m_new = grow ? mx - kPScale : m_sh;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh - m_new) : 1.0f;
-                m_sh = m_new;
-                l_run *= alpha;
+
+        // ---- per half: scores, softmax and the PV operand
+        u32x4_t ahi[NH], alo[NH];
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) E[hh] *= alpha;
-                W *= alpha;
+        for (int hf = 0; hf < NH; ++hf) {
+            float s0 = ((D0[hf][0] + D0[hf][1]) + (D0[hf][2] + D0[hf][3])) * sk0 * c2[hf];
+            float s1 = ((D1[hf][0] + D1[hf][1]) + (D1[hf][2] + D1[hf][3])) * sk1 * c2[hf];
+            s0 = ok0 ? s0 : -INFINITY;
+            s1 = ok1 ? s1 : -INFINITY;
+            const float mx = row16_max(fmaxf(s0, s1));
+            {
+                const bool grow = mx > m_sh[hf] + (kPScale + kSlack);
+                if (__builtin_amdgcn_ballot_w64(grow)) {
+                    const float m_new = grow ? mx - kPScale : m_sh[hf];
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_sh[hf] - m_new) : 1.0f;
+                    m_sh[hf] = m_new;
+                    l_run[hf] *= alpha;
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) E[hf][hh] *= alpha;
+                    W[hf] *= alpha;
+                }
+            }
+            const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh[hf]);
+            const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh[hf]);
+            l_run[hf] += p0 + p1;
+            pbuf8[hf][kb][n16] = p0;
+            pbuf8[hf][kb][16 + n16] = p1;
+            __builtin_amdgcn_wave_barrier();
+            const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb]);
+            const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[hf][jq][8 * kb + 4]);
+
+            // ---- PV operand: w = p' s_V of head 4 hf + jq, tokens 32 tl + 8 kb + e
+            const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+            const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
+            float wv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // tokens outside the run may have garbage scales: select, do not multiply
+                const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
+                const int tok = 32 * tl + 8 * kb + e;
+                wv[e] = tok >= t_lo && tok < t_hi ? w : 0.0f;
+            }
+            constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hw, lw;
+                split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
+                ahi[hf][i] = hw;
+                alo[hf][i] = lw;
+            }
+            W[hf] = mfma_bf16(ahi[hf], ones, W[hf]);
+            W[hf] = mfma_bf16(alo[hf], ones, W[hf]);
+        }
+
+        // ---- PV, block by block; each block's widened codes serve every half
+        {
+            const uint4 v0 = stage8[4][lane], v1 = stage8[5][lane];
+            const uint4 v2 = stage8[6][lane], v3 = stage8[7][lane];
+            const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                     v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const uint64_t rows = 0x1111111111111111ull << blk;
+                const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
+                const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
+#pragma unroll
+                for (int hf = 0; hf < NH; ++hf) {
+                    const u32x4_t bh = {keep_lanes(ahi[hf][0], rows), keep_lanes(ahi[hf][1], rows),
+                                        keep_lanes(ahi[hf][2], rows), keep_lanes(ahi[hf][3], rows)};
+                    const u32x4_t bl = {keep_lanes(alo[hf][0], rows), keep_lanes(alo[hf][1], rows),
+                                        keep_lanes(alo[hf][2], rows), keep_lanes(alo[hf][3], rows)};
+                    E[hf][0] = mfma_bf16(bh, b0, E[hf][0]);
+                    E[hf][1] = mfma_bf16(bh, b1, E[hf][1]);
+                    E[hf][0] = mfma_bf16(bl, b0, E[hf][0]);
+                    E[hf][1] = mfma_bf16(bl, b1, E[hf][1]);
+                }
             }
         }
-        const float p0 = __builtin_amdgcn_exp2f(s0 - m_sh);
-        const float p1 = __builtin_amdgcn_exp2f(s1 - m_sh);
-        l_run += p0 + p1;
-        pbuf8[kb][n16] = p0;
-        pbuf8[kb][16 + n16] = p1;
-        __builtin_amdgcn_wave_barrier();
-        const float4 pa = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb]);
-        const float4 pb = *reinterpret_cast<const float4*>(&pbuf8[jq][8 * kb + 4]);
-
-        // ---- PV: w = p' s_V of head jq, tokens 32 tl + 8 kb + e
-        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-        const uint32_t svw[4] = {svp.x, svp.y, svp.z, svp.w};
-        float wv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // tokens outside the run may have garbage scales: select, do not multiply
-            const float w = fmaf(pr[e], h2f(svw[e >> 1], e & 1), 0.0f);
-            const int tok = 32 * tl + 8 * kb + e;
-            wv[e] = tok >= t_lo && tok < t_hi ? w : 0.0f;
-        }
-        u32x4_t ahi, alo;
-        constexpr int pe[4][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hw, lw;
-            split_bf16(wv[pe[i][0]], wv[pe[i][1]], hw, lw);
-            ahi[i] = hw;
-            alo[i] = lw;
-        }
-        const uint4 v0 = stage8[4][lane], v1 = stage8[5][lane];
-        const uint4 v2 = stage8[6][lane], v3 = stage8[7][lane];
-        const uint32_t vw[16] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                 v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const uint64_t rows = 0x1111111111111111ull << blk;
-            const u32x4_t bh = {keep_lanes(ahi[0], rows), keep_lanes(ahi[1], rows),
-                                keep_lanes(ahi[2], rows), keep_lanes(ahi[3], rows)};
-            const u32x4_t bl = {keep_lanes(alo[0], rows), keep_lanes(alo[1], rows),
-                                keep_lanes(alo[2], rows), keep_lanes(alo[3], rows)};
-            const u32x4_t b0 = widen_i8(vw[4 * blk], vw[4 * blk + 1]);
-            const u32x4_t b1 = widen_i8(vw[4 * blk + 2], vw[4 * blk + 3]);
-            E[0] = mfma_bf16(bh, b0, E[0]);
-            E[1] = mfma_bf16(bh, b1, E[1]);
-            E[0] = mfma_bf16(bl, b0, E[0]);
-            E[1] = mfma_bf16(bl, b1, E[1]);
-        }
-        W = mfma_bf16(ahi, ones, W);
-        W = mfma_bf16(alo, ones, W);
         __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- epilogue: lane l holds head kb, channels 32 r + 16 h + n16 in E[h][r]
-    const float l = row16_sum(l_run);
-    const float inv = 1.0f / l;
-    if (kb >= g.gqa) return;                     // a head past the q/kv ratio
-    float* dst = rec + kb * (g.d + kPartPad);
+    // ---- epilogue: lane l holds head 4 hf + kb, channels 32 r + 16 h + n16 in E[hf][h][r]
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        dst[32 * r + n16] = (ldexpf(E[0][r], 133) - 128.0f * W[0]) * inv;
-        dst[32 * r + 16 + n16] = (ldexpf(E[1][r], 133) - 128.0f * W[0]) * inv;
+    for (int hf = 0; hf < NH; ++hf) {
+        const float l = row16_sum(l_run[hf]);
+        const float inv = 1.0f / l;
+        if (4 * hf + kb >= g.gqa) continue;      // a head past the q/kv ratio
+        float* dst = rec + (4 * hf + kb) * (g.d + kPartPad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dst[32 * r + n16] = (ldexpf(E[hf][0][r], 133) - 128.0f * W[hf][0]) * inv;
+            dst[32 * r + 16 + n16] = (ldexpf(E[hf][1][r], 133) - 128.0f * W[hf][0]) * inv;
+        }
+        if (n16 == 0) dst[g.d] = m_sh[hf] + log2f(l);
     }
-    if (n16 == 0) dst[g.d] = m_sh + log2f(l);
 }
 
 // ---------------------------------------------------------------------------
@@ -1949,6 +1986,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4))) void de
     walk_units(a, [&](int, int) {},
                [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
                    mfma_item_kv8(a, b, h, lo, hi, rec, pace);
+               });
+}
+
+// KV8 kind, q/kv ratios 5 to 8: two four-head halves per staged tile.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_kv8_mfma8_kernel(DecodeArgs a)
+{
+    walk_units(a, [&](int, int) {},
+               [&](int b, int h, int lo, int hi, float* rec, Pace& pace) {
+                   mfma_item_kv8<2>(a, b, h, lo, hi, rec, pace);
                });
 }
 

@@ -127,8 +127,9 @@ def test_invalid_descriptors():
         (dict(sink=40000, recent=40000), kv4.KV4_ERR_CAPACITY),
         (dict(kind=kv4.KV4_KIND_KV8), kv4.KV4_OK),
         (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=16), kv4.KV4_OK),                  # GQA 2
-        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=64), kv4.KV4_ERR_UNSUPPORTED),     # GQA 8
-        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=40), kv4.KV4_ERR_UNSUPPORTED),     # GQA 5
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=64), kv4.KV4_OK),                  # GQA 8
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=40), kv4.KV4_OK),                  # GQA 5
+        (dict(kind=kv4.KV4_KIND_KV8, num_q_heads=128), kv4.KV4_ERR_UNSUPPORTED),    # GQA 16
         (dict(kind=kv4.KV4_KIND_KV8, flags=kv4.KV4_FLAG_ROTATE_K), kv4.KV4_ERR_UNSUPPORTED),
         (dict(flags=kv4.KV4_FLAG_INT_PATH), kv4.KV4_OK),
         (dict(flags=kv4.KV4_FLAG_INT_PATH | kv4.KV4_FLAG_ROTATE_K), kv4.KV4_OK),

@@ -588,10 +588,11 @@ def test_kv8_kind(Hkv):
         assert np.abs(o2 - out).max() <= 5e-5
 
 
-@pytest.mark.parametrize("ratio", [1, 2, 3])
+@pytest.mark.parametrize("ratio", [1, 2, 3, 5, 8])
 def test_kv8_ratios(ratio):
-    """KV8 kind at q/kv ratios below 4 (the four-head matrix-core layout with
-    the heads past the ratio padded)."""
+    """KV8 kind at q/kv ratios other than 4 (the four-head matrix-core layout
+    with the heads past the ratio padded; 5 and 8 in two four-head halves per
+    staged tile)."""
     H.log(f"case kv8 ratio {ratio}")
     _kv8_case(2, [0, 15, 16, 31, 32, 300, 1000, 2500], seed=90 + ratio, ratio=ratio)
 
